@@ -1,0 +1,279 @@
+"""Benchmark of the QSA hot path on one MI355X.
+
+One step = one prefill pass of the chosen workload: qsa_indexer_prefill
+(pooling, query prep, block scoring, top-512 select + expand) followed by
+qsa_sparse_prefill over the lists it produced.  Inputs are resident in HBM
+before the timed region.  The decode pair (qsa_indexer_decode +
+qsa_sparse_decode) on the paged workload is timed the same way and reported
+in the "decode" object of the same JSON line.
+
+Prints ONE JSON line.  The roofline object covers the dominant kernel
+(sparse prefill attention): algorithmic bytes per launch / its average
+duration measured with HIP events on the launch stream.  cpu_baseline times
+the CPU oracle on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse prefill tokens/s + decode seqs/s (topK 2051); % HBM roofline"
+PREFILL_WORKLOADS = (2, 3, 5)
+DECODE_WORKLOAD = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=PREFILL_WORKLOADS,
+                    help="prefill workload timed as the step (default: 2)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def dev(a, dtype=None):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def cfg_struct(Q, icfg):
+    return Q.indexer_config(icfg.num_heads, icfg.head_dim, icfg.rot_dim, icfg.compress_ratio, icfg.budget,
+                            icfg.rope_theta, icfg.rms_eps)
+
+
+def prefill_bench(args, Q, syn, torch):
+    inp = syn.workload(args.workload)
+    icfg = inp.icfg
+    e = 2
+    cfg = cfg_struct(Q, icfg)
+    q, k, v = dev(inp.q, inp.dtype), dev(inp.k, inp.dtype), dev(inp.v, inp.dtype)
+    iq, ik = dev(inp.idx_q, inp.dtype), dev(inp.idx_k, inp.dtype)
+    wq, wk, ctx = dev(inp.w_q), dev(inp.w_k), dev(inp.ctx)
+    o = torch.empty_like(q)
+    lists = torch.empty((inp.B, inp.S, icfg.top_k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(Q.qsa_indexer_prefill_workspace_bytes(cfg, inp.B, inp.S), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        Q.qsa_indexer_prefill(iq, ik, wq, wk, ctx, lists, ws, cfg, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        Q.qsa_sparse_prefill(q, k, v, o, lists, ctx, inp.scale, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    idx_ms = [a.elapsed_time(b) for a, b, _ in evs]
+    attn_ms = [b.elapsed_time(c) for _, b, c in evs]
+
+    live = int(sum(min(int(c), inp.S) for c in inp.ctx))
+    dead = inp.B * inp.S - live
+    n_entries = int((lists >= 0).sum().item())          # listed ids over all live rows
+    attn_bytes = (n_entries * inp.Hkv * 2 * inp.D * e + live * inp.Hq * inp.D * e * 2
+                  + live * icfg.top_k * 4 + dead * inp.Hq * inp.D * e)
+    attn_avg = float(np.mean(attn_ms)) * 1e-3
+    idx_avg = float(np.mean(idx_ms)) * 1e-3
+    achieved = attn_bytes / attn_avg / 1e9
+    res = {
+        "inp": inp, "live": live, "wall": wall,
+        "ms_per_step": wall / args.steps * 1e3,
+        "indexer_ms": idx_avg * 1e3, "attention_ms": attn_avg * 1e3,
+        "attn_bytes": attn_bytes, "achieved_gbs": achieved, "n_entries": n_entries,
+    }
+    del q, k, v, iq, ik, o, lists, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_bench(args, Q, syn, torch):
+    inp = syn.workload(DECODE_WORKLOAD)
+    icfg = inp.icfg
+    e = 2
+    cfg = cfg_struct(Q, icfg)
+    pool = dev(inp.pool, inp.dtype)
+    pt, ctx = dev(inp.page_table), dev(inp.ctx)
+    iq, ik, wq, wk = dev(inp.idx_q, inp.dtype), dev(inp.idx_k, inp.dtype), dev(inp.w_q), dev(inp.w_k)
+    q = dev(inp.q, inp.dtype)
+    o = torch.empty_like(q)
+    lists = torch.empty((inp.B, 1, inp.top_k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(Q.qsa_indexer_decode_workspace_bytes(cfg, inp.B, inp.max_pages), dtype=torch.uint8,
+                     device="cuda")
+    po = torch.empty(Q.qsa_sparse_decode_partial_o_elems(inp.B, inp.Hkv, inp.D), dtype=torch.float32, device="cuda")
+    ps = torch.empty(Q.qsa_sparse_decode_partial_stats_elems(inp.B, inp.Hkv), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros(Q.qsa_sparse_decode_counter_elems(inp.B, inp.Hkv), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        Q.qsa_indexer_decode(iq, ik, wq, wk, pool, pt, ctx, lists, ws, cfg, inp.D, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        Q.qsa_sparse_decode(q, o, pool, pt, lists, ctx, po, ps, cnt, inp.scale, head_dim=inp.D, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    steps = max(args.steps, 50)
+    for _ in range(max(args.warmup, 5)):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    idx_ms = float(np.median([a.elapsed_time(b) for a, b, _ in evs]))
+    attn_ms = float(np.median([b.elapsed_time(c) for _, b, c in evs]))
+    n_entries = int((lists >= 0).sum().item())
+    nblk = int(sum(int(c) // icfg.compress_ratio for c in inp.ctx))
+    attn_bytes = n_entries * inp.Hkv * 2 * inp.D * e + inp.B * (inp.Hq * inp.D * e * 2 + inp.top_k * 4)
+    idx_bytes = nblk * icfg.head_dim * e + inp.B * inp.top_k * 4
+    step_ms = idx_ms + attn_ms
+    out = {
+        "workload": syn.WORKLOADS[DECODE_WORKLOAD],
+        "value": inp.B / (step_ms * 1e-3),
+        "unit": "seqs/s",
+        "ms_per_step": step_ms,
+        "wall_ms_per_step": wall / steps * 1e3,
+        "indexer_ms": idx_ms,
+        "attention_ms": attn_ms,
+        "steps": steps,
+        "algorithmic_bytes_per_step": attn_bytes + idx_bytes,
+        "hbm_frac_step": (attn_bytes + idx_bytes) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "attention_gbs": attn_bytes / (attn_ms * 1e-3) / 1e9,
+        "splits": Q.qsa_sparse_decode_default_splits(inp.B, inp.Hkv, inp.top_k),
+    }
+    del pool
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(wl):
+    """The oracle, unchanged, on the same workload (single thread)."""
+    import qsa_synth as syn
+    from threadpoolctl import threadpool_limits
+
+    from oracle import qsa_oracle as O
+    inp = syn.workload(wl)
+    icfg = inp.icfg
+    if wl == 2:
+        rows = None
+        n_rows = inp.B * inp.S
+        sample = "all 4096 rows of the workload (indexer + attention)"
+    else:
+        rng = np.random.default_rng(7)
+        rows = [(b, int(t)) for b in range(inp.B) for t in rng.integers(0, min(int(inp.ctx[b]), inp.S), 256)]
+        n_rows = len(rows)
+        sample = f"{n_rows} random live rows (indexer + attention), extrapolated per row"
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        lists = O.indexer_prefill(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.ctx, icfg, inp.dtype, icfg.top_k,
+                                  rows=rows)
+        if rows is not None:
+            full = np.full((inp.B, inp.S, icfg.top_k), -1, dtype=np.int32)
+            for r, l in lists.items():
+                full[r] = l
+            lists = full
+        O.sparse_prefill(inp.q, inp.k, inp.v, lists, inp.ctx, inp.scale, inp.dtype, rows=rows)
+        dt = time.perf_counter() - t0
+    live_rows = n_rows if rows is not None else int(sum(min(int(c), inp.S) for c in inp.ctx))
+    return {"value": live_rows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": dt, "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the QSA hot path is single-GPU work here "
+              "(sharding is described, not built); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import qsa_synth as syn
+    import top_indexed_sparse_qsa_amd as Q
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    Q.load()
+    print(f"# bench: prefill workload {args.workload}", file=sys.stderr, flush=True)
+    pf = prefill_bench(args, Q, syn, torch)
+    print(f"# bench: prefill {pf['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+    dec = None
+    if not args.no_decode:
+        print("# bench: decode workload 4", file=sys.stderr, flush=True)
+        dec = decode_bench(args, Q, syn, torch)
+        print(f"# bench: decode {dec['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.empty(n // 2, dtype=torch.float16, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.workload)
+
+    inp = pf["inp"]
+    value = pf["live"] * args.steps / pf["wall"]
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {"workload": syn.WORKLOADS[args.workload], "batch": inp.B, "seq_len": inp.S,
+                   "live_tokens": pf["live"], "num_q_heads": inp.Hq, "num_kv_heads": inp.Hkv,
+                   "head_dim": inp.D, "top_k": inp.icfg.top_k, "parallelism": "none"},
+        "parts_ms": {"indexer_prefill": pf["indexer_ms"], "sparse_prefill": pf["attention_ms"]},
+        "roofline": {"bound": "hbm", "kernel": "sparse_prefill_kernel",
+                     "achieved": pf["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": pf["achieved_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": pf["attn_bytes"]},
+        "cpu_baseline": cpu,
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,254 @@
+/*
+ * libqsa -- QSA (Qwen Sparse Attention) hot path for AMD MI355X (gfx950).
+ *
+ * Four entry points, in the order a layer calls them:
+ *
+ *   prefill:  qsa_indexer_prefill  -> int32 index lists [B, S, top_k]
+ *             qsa_sparse_prefill   -> sparse GQA attention over the lists
+ *   decode:   qsa_indexer_decode   -> indexer state update in the pool tails
+ *                                     + lists [B, 1, top_k]
+ *             qsa_sparse_decode    -> split-K sparse attention over the pool
+ *
+ * Sources (pages cited by title and section):
+ *   [Runner] TensorRT-Edge-LLM "Cute Dsl Qsa Sparse Runner": structs
+ *            QsaSparsePrefillParams and QsaSparseDecodeParams, and the
+ *            runners' run() contract.
+ *   [Plugin] TensorRT-Edge-LLM "Qsa Attention Plugin": the class
+ *            description (indexer steps, decode B1/B2/B3), its Contract
+ *            paragraph and the "KV pool contract (widened rows)" paragraph.
+ *   [Atlas]  atlasinference "spark_model/layers/ops/qsa.rs": doc comments of
+ *            qsa_block_pool, qsa_qprep, qsa_score, qsa_score_rows.
+ *
+ * Conventions for every call
+ *   - All pointers are DEVICE pointers, except the params struct itself and
+ *     the config struct, which are read on the host during the call and may
+ *     be freed when it returns.  The caller owns every buffer.
+ *   - The library never allocates, frees or synchronises, keeps no state
+ *     between calls, and enqueues all work on `stream` (a hipStream_t; NULL
+ *     is the default stream).  Buffers must stay alive until that work ends.
+ *     Calls are reentrant and contain no host-device synchronisation, so they
+ *     may be captured in a HIP graph.
+ *   - Only host-visible arguments are validated.  On any validation failure
+ *     the call returns a non-QSA_OK status and enqueues nothing.  Device
+ *     contents (list validity, context lengths, page ids) are the caller's
+ *     contract; kernels still bound every device-supplied index they use for
+ *     an address, so a broken contract gives wrong values, never a fault.
+ *   - QSA_ERR_LAUNCH reports a HIP launch error seen right after enqueueing.
+ *   - 16-bit tensors are fp16 or bf16 as `dtype` says, contiguous, innermost
+ *     dimension last.  Q/K/V/O, pool, indexer input and partial_o base
+ *     pointers must be 16-byte aligned (QSA_ERR_BAD_SHAPE otherwise);
+ *     workspaces 256-byte aligned.
+ */
+#ifndef LIBQSA_H
+#define LIBQSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_PAGE_TOKENS 128   /* tokens per KV page [Runner: QsaSparseDecodeParams] */
+#define QSA_PARTIAL_ROWS 16   /* rows per split partial (the MFMA M tile) */
+#define QSA_MAX_SPLITS 16     /* largest decode split count this library plans */
+#define QSA_MAX_BLOCKS 32768  /* largest complete-block count one row may see */
+
+typedef enum { QSA_FP16 = 0, QSA_BF16 = 1 } qsa_dtype;
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_NULL_POINTER = 1,
+  QSA_ERR_BAD_SHAPE = 2,
+  QSA_ERR_UNSUPPORTED = 3,
+  QSA_ERR_WORKSPACE_TOO_SMALL = 4,
+  QSA_ERR_LAUNCH = 5
+} qsa_status;
+
+/* Indexer attributes [Plugin: constructor attributes indexerNumHeads,
+ * indexerHeadDim, indexerBudget, indexerCompressRatio, rmsNormEps; Atlas:
+ * the rot and theta arguments of qsa_block_pool / qsa_qprep].
+ * Supported: num_heads 1..4, head_dim 128, rot_dim even and <= head_dim,
+ * compress_ratio 1..8, budget >= 1, rms_eps >= 0, rope_theta > 0. */
+typedef struct {
+  int32_t num_heads;      /* indexer query heads Hi (one shared key head) */
+  int32_t head_dim;       /* indexer head dim hd */
+  int32_t rot_dim;        /* leading dims that RoPE rotates, pairs (i, i+rot/2) */
+  int32_t compress_ratio; /* tokens per block */
+  int32_t budget;         /* blocks kept per row */
+  float rope_theta;       /* RoPE base */
+  float rms_eps;          /* RMSNorm epsilon, inside the square root */
+} qsa_indexer_config;
+
+/* Sparse prefill [Runner: QsaSparsePrefillParams].
+ * q, o: [batch, seq_len, num_q_heads, head_dim]; k, v: [batch, seq_len,
+ * num_kv_heads, head_dim].  indices: int32 [batch, seq_len, top_k], per row
+ * distinct token ids < t+1, any order, -1 padded on the right; one list
+ * serves every head of the row.  The kernel applies no positional mask.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * context_lengths: int32 [batch]; rows t >= context_lengths[b] are written
+ * as +0.0 and ids >= context_lengths[b] are never read.  A live row whose
+ * list holds no usable id is +0.0.  A chunk of 32 slots that holds no id
+ * >= 0 ends the row's list.
+ * Supported: head_dim 64 or 128; num_q_heads a multiple of num_kv_heads with
+ * ratio 1..16; top_k >= 1. */
+typedef struct {
+  const void *q;
+  const void *k;
+  const void *v;
+  void *o;
+  const int32_t *indices;
+  const int32_t *context_lengths;
+  int32_t batch;
+  int32_t seq_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t top_k;
+  float attention_scale; /* multiplies q.k; not assumed to be 1/sqrt(D) */
+  qsa_dtype dtype;
+  void *stream;
+} qsa_sparse_prefill_params;
+
+/* Split-K sparse decode [Runner: QsaSparseDecodeParams].
+ * q, o: [batch, 1, num_q_heads, head_dim].
+ * kv_pool: [num_flat_pages, 128, num_kv_heads, pool_head_dim]; only columns
+ * [0, head_dim) of each row are read (the tail holds indexer state).
+ * page_table: int32 [batch, 2, max_pages_per_seq]; row 0 holds K page ids,
+ * row 1 V page ids already offset by num_flat_pages / 2.
+ * indices: int32 [batch, 1, top_k] as for prefill.
+ * context_lengths: int32 [batch], the TOTAL length including the new token.
+ * partial_o: fp32, qsa_sparse_decode_partial_o_elems() elements;
+ * partial_stats: fp32, qsa_sparse_decode_partial_stats_elems() elements;
+ * split_counters: int32, qsa_sparse_decode_counter_elems() elements, all
+ * ZERO before the first call on a buffer; every call leaves them zero.
+ * num_splits: 0 lets the library choose; otherwise 1..QSA_MAX_SPLITS.
+ * The result does not depend on which split finishes last: partials are
+ * merged in split order.  Concurrent calls must not share split_counters.
+ * Supported: as prefill, plus pool_head_dim >= head_dim. */
+typedef struct {
+  const void *q;
+  void *o;
+  const void *kv_pool;
+  const int32_t *page_table;
+  const int32_t *indices;
+  const int32_t *context_lengths;
+  float *partial_o;
+  float *partial_stats;
+  int32_t *split_counters;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t pool_head_dim;
+  int32_t num_flat_pages;   /* 2 * numPages (both planes) */
+  int32_t max_pages_per_seq;
+  int32_t top_k;
+  int32_t num_splits;
+  float attention_scale;
+  qsa_dtype dtype;
+  void *stream;
+} qsa_sparse_decode_params;
+
+/* Indexer, prefill [Plugin: fused step 2; Atlas: qsa_block_pool,
+ * qsa_qprep_rows, qsa_score_rows].
+ * idx_q: [batch, seq_len, num_heads, hd] raw indexer queries; idx_k:
+ * [batch, seq_len, hd] raw indexer keys (one key head); q_norm_w, k_norm_w:
+ * fp32 [hd] raw gains, applied as (1 + w).  context_lengths: int32 [batch].
+ * Output indices: int32 [batch, seq_len, top_k].  Row t keeps the `budget`
+ * highest-scoring of its floor((t+1)/ratio) complete blocks (all of them if
+ * there are no more than `budget`; equal scores favour the lower block),
+ * written in ascending block order as ratio consecutive ids each, then its
+ * causal tail ratio*floor((t+1)/ratio) .. t, then -1.  Rows t >=
+ * context_lengths[b] are all -1.  Scores are computed in fp32 from an exact
+ * two- (fp16) or three-piece (bf16) split of the fp32 queries; the pages
+ * call such scoring selection-equivalent, so a swap of blocks whose scores
+ * sit within fp32 rounding of the cut can differ from a float64 reference.
+ * workspace: device scratch of at least
+ * qsa_indexer_prefill_workspace_bytes() bytes, 256-byte aligned.
+ * Supported: top_k >= budget*ratio + ratio - 1; floor(seq_len/ratio) <=
+ * QSA_MAX_BLOCKS. */
+typedef struct {
+  const void *idx_q;
+  const void *idx_k;
+  const float *q_norm_w;
+  const float *k_norm_w;
+  const int32_t *context_lengths;
+  int32_t *indices;
+  void *workspace;
+  size_t workspace_bytes;
+  int32_t batch;
+  int32_t seq_len;
+  int32_t top_k;
+  qsa_indexer_config cfg;
+  qsa_dtype dtype;
+  void *stream;
+} qsa_indexer_prefill_params;
+
+/* Indexer, one decode step [Plugin: decode B1/B2/B3 and the KV pool
+ * contract].  The indexer state lives in columns [head_dim, head_dim + hd)
+ * of KV head 0 rows of kv_pool: block g's kbar in the V-row tail of token
+ * ratio*g; for the trailing incomplete block only, each token's raw index
+ * key in its K-row tail.  With p = context_lengths[b] - 1:
+ *   B1  prep the queries at position p; if the block of p stays incomplete
+ *       (context length not a multiple of ratio) store idx_k in the K-row
+ *       tail of token p, else pool the block from the raw tails of its first
+ *       ratio-1 tokens plus idx_k and store kbar in the V-row tail of its
+ *       first token;
+ *   B2  score the floor(ctx/ratio) blocks from the V-row tails;
+ *   B3  select and expand as in prefill, for row p.
+ * kv_pool is updated in place (only those tails); everything else in the
+ * pool is left bit-unchanged.  idx_q: [batch, 1, num_heads, hd]; idx_k:
+ * [batch, 1, hd]; indices out: int32 [batch, 1, top_k].  Page table and
+ * pool as for qsa_sparse_decode.  workspace: at least
+ * qsa_indexer_decode_workspace_bytes() bytes.
+ * Supported: pool_head_dim >= head_dim + cfg.head_dim;
+ * max_pages_per_seq*128/ratio <= QSA_MAX_BLOCKS. */
+typedef struct {
+  const void *idx_q;
+  const void *idx_k;
+  const float *q_norm_w;
+  const float *k_norm_w;
+  void *kv_pool;
+  const int32_t *page_table;
+  const int32_t *context_lengths;
+  int32_t *indices;
+  void *workspace;
+  size_t workspace_bytes;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t pool_head_dim;
+  int32_t num_flat_pages;
+  int32_t max_pages_per_seq;
+  int32_t top_k;
+  qsa_indexer_config cfg;
+  qsa_dtype dtype;
+  void *stream;
+} qsa_indexer_decode_params;
+
+qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p);
+qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p);
+qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p);
+qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p);
+
+/* Workspace sizes (bytes or elements); 0 when the arguments are invalid. */
+size_t qsa_indexer_prefill_workspace_bytes(const qsa_indexer_config *cfg, int32_t batch,
+                                           int32_t seq_len);
+size_t qsa_indexer_decode_workspace_bytes(const qsa_indexer_config *cfg, int32_t batch,
+                                          int32_t max_pages_per_seq);
+size_t qsa_sparse_decode_partial_o_elems(int32_t batch, int32_t num_kv_heads, int32_t head_dim);
+size_t qsa_sparse_decode_partial_stats_elems(int32_t batch, int32_t num_kv_heads);
+size_t qsa_sparse_decode_counter_elems(int32_t batch, int32_t num_kv_heads);
+
+/* Split count qsa_sparse_decode uses for these arguments (num_splits = 0). */
+int32_t qsa_sparse_decode_default_splits(int32_t batch, int32_t num_kv_heads, int32_t top_k);
+
+/* Static, never-NULL description of a status. */
+const char *qsa_status_string(qsa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBQSA_H */

@@ -138,7 +138,7 @@ def pool_blocks(k_raw: np.ndarray, first_block: int, w_k, icfg, dtype: str) -> n
     first_block: index g of the first block (sets the rope positions)."""
     r = icfg.compress_ratio
     n = k_raw.shape[0] // r
-    m = k_raw[: n * r].reshape(n, r, -1).sum(axis=1) / r
+    m = k_raw[: n * r].reshape(n, r, k_raw.shape[1]).sum(axis=1) / r
     y = rms_norm(m, widen(w_k, "fp32"), f32(icfg.rms_eps))
     pos = r * (first_block + np.arange(n))
     y = rope(y, pos, icfg.rot_dim, f32(icfg.rope_theta))
@@ -324,7 +324,7 @@ def sparse_decode(q, pool, page_table, indices, ctx, scale: float, D: int, dtype
 # Indexer, decode  [Plugin: decode B1/B2/B3 and the KV pool contract]
 # ---------------------------------------------------------------------------
 def indexer_decode(idx_q, idx_k, w_q, w_k, pool, page_table, ctx, icfg, D: int, dtype: str,
-                   top_k: int, seqs=None, page_tokens: int = 128):
+                   top_k: int, seqs=None, page_tokens: int = 128, return_scores: bool = False):
     """One decode step of the indexer for each sequence.
 
     The indexer state lives in columns [D, D+hd) of KV head 0 of pool rows:
@@ -340,13 +340,14 @@ def indexer_decode(idx_q, idx_k, w_q, w_k, pool, page_table, ctx, icfg, D: int, 
 
     The pool is not modified.  Returns (writes, lists): writes is a list of
     (flat_page, row, values[hd] storage) tail updates, lists is int32
-    [B,1,top_k] (seqs=None) or {b: int32 [top_k]}."""
+    [B,1,top_k] (seqs=None) or {b: int32 [top_k]}.  With return_scores, also
+    {b: float64 block scores}."""
     B = idx_k.shape[0]
     r = icfg.compress_ratio
     hd = icfg.head_dim
     tail = slice(D, D + hd)
     want = range(B) if seqs is None else [int(b) for b in seqs]
-    writes, lists = [], {}
+    writes, lists, all_scores = [], {}, {}
     for b in want:
         c = int(ctx[b])
         if c <= 0:
@@ -376,10 +377,11 @@ def indexer_decode(idx_q, idx_k, w_q, w_k, pool, page_table, ctx, icfg, D: int, 
                 kbar[g] = widen(pool[pg, row, 0, tail], dtype)
         qhat = prep_queries(widen(idx_q[b, 0], dtype), p, w_q, icfg)
         s = block_scores(qhat, kbar)
+        all_scores[b] = s
         lists[b] = expand_list(p, select_blocks(s, icfg.budget), icfg, top_k)
     if seqs is None:
         lists = np.stack([lists[b] for b in range(B)])[:, None, :]
-    return writes, lists
+    return (writes, lists, all_scores) if return_scores else (writes, lists)
 
 
 def apply_tail_writes(pool: np.ndarray, writes, D: int) -> None:

@@ -1,0 +1,159 @@
+"""Host-side tests of the C ABI: the library loads, exports every function the
+header declares, sizes workspaces by the documented formulas and rejects bad
+arguments with the documented status before any device work.
+
+The argument-rejection tests pass fake (never dereferenced) device addresses;
+each case is built to fail validation.  They run without a GPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_indexed_sparse_qsa_amd as Q
+from top_indexed_sparse_qsa_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libqsa.h")
+
+OK, NULLP, SHAPE, UNSUP, WS, LAUNCH = range(6)
+FAKE = 0x7F0000000000          # 256-byte aligned, never dereferenced
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(Q.EXPORTS)
+
+
+def test_library_exports_every_declared_function():
+    lib = Q.load()
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, f"libqsa.so lacks {missing}"
+
+
+def test_status_strings():
+    for s in range(6):
+        assert isinstance(Q.qsa_status_string(s), str) and Q.qsa_status_string(s)
+    assert Q.qsa_status_string(99) == "unknown status"
+
+
+def test_workspace_sizes_follow_layout():
+    cfg = Q.indexer_config()
+    a = lambda x: (x + 255) // 256 * 256
+    # prefill: fp32 queries | kbar | fp32 scores with a 16-rounded stride
+    B, S = 1, 32768
+    g = S // 4
+    assert Q.qsa_indexer_prefill_workspace_bytes(cfg, B, S) == \
+        a(B * S * 4 * 128 * 4) + a(B * g * 128 * 2) + a(B * S * g * 4)
+    B, S = 4, 16383
+    g = S // 4
+    st = (g + 15) // 16 * 16
+    assert Q.qsa_indexer_prefill_workspace_bytes(cfg, B, S) == \
+        a(B * S * 4 * 128 * 4) + a(B * g * 128 * 2) + a(B * S * st * 4)
+    assert Q.qsa_indexer_decode_workspace_bytes(cfg, 32, 512) == a(32 * 4 * 128 * 4) + a(32 * 16384 * 4)
+    assert Q.qsa_sparse_decode_partial_o_elems(32, 4, 128) == 32 * 4 * 16 * 16 * 128
+    assert Q.qsa_sparse_decode_partial_stats_elems(32, 4) == 32 * 4 * 16 * 2 * 16
+    assert Q.qsa_sparse_decode_counter_elems(32, 4) == 128
+    assert Q.qsa_indexer_prefill_workspace_bytes(Q.indexer_config(head_dim=64), 1, 10) == 0
+    assert Q.qsa_sparse_decode_partial_o_elems(0, 4, 128) == 0
+
+
+def test_default_split_plan():
+    assert Q.qsa_sparse_decode_default_splits(32, 4, 2051) == 16
+    assert Q.qsa_sparse_decode_default_splits(1, 1, 40) == 2       # never more splits than 32-slot chunks
+    assert Q.qsa_sparse_decode_default_splits(4096, 8, 2051) == 1
+    assert Q.qsa_sparse_decode_default_splits(0, 4, 2051) == 0
+
+
+@pytest.fixture
+def no_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("argument-rejection cases use fake device addresses; host-only test")
+
+
+def _prefill(**kw):
+    p = L.SparsePrefillParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 8, 2, 128, 16, 0.125, 0, None)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return Q.load().qsa_sparse_prefill(ctypes.byref(p))
+
+
+def _decode(**kw):
+    p = L.SparseDecodeParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             2, 32, 4, 128, 256, 16, 8, 2051, 0, 0.088, 0, None)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return Q.load().qsa_sparse_decode(ctypes.byref(p))
+
+
+def _iprefill(**kw):
+    cfg = kw.pop("cfg", Q.indexer_config())
+    p = L.IndexerPrefillParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 1, 4096, 2051, cfg, 0, None)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return Q.load().qsa_indexer_prefill(ctypes.byref(p))
+
+
+def _idecode(**kw):
+    cfg = kw.pop("cfg", Q.indexer_config())
+    p = L.IndexerDecodeParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                              2, 4, 128, 256, 16, 8, 2051, cfg, 0, None)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return Q.load().qsa_indexer_decode(ctypes.byref(p))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULLP), (dict(indices=None), NULLP), (dict(context_lengths=None), NULLP),
+    (dict(dtype=2), UNSUP), (dict(batch=0), SHAPE), (dict(seq_len=0), SHAPE), (dict(top_k=0), SHAPE),
+    (dict(num_q_heads=7), SHAPE), (dict(num_q_heads=34), UNSUP), (dict(head_dim=96), UNSUP),
+    (dict(num_kv_heads=0), SHAPE), (dict(q=FAKE + 8), SHAPE), (dict(attention_scale=float("inf")), SHAPE),
+])
+def test_sparse_prefill_rejects(no_gpu, kw, status):
+    assert _prefill(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(split_counters=None), NULLP), (dict(page_table=None), NULLP), (dict(partial_stats=None), NULLP),
+    (dict(dtype=-1), UNSUP), (dict(batch=0), SHAPE), (dict(num_flat_pages=0), SHAPE),
+    (dict(pool_head_dim=120), SHAPE), (dict(pool_head_dim=130), SHAPE), (dict(num_splits=17), SHAPE),
+    (dict(num_splits=-1), SHAPE), (dict(max_pages_per_seq=5000), UNSUP), (dict(num_q_heads=33), SHAPE),
+    (dict(kv_pool=FAKE + 4), SHAPE), (dict(head_dim=256), UNSUP),
+])
+def test_sparse_decode_rejects(no_gpu, kw, status):
+    assert _decode(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(workspace=None), NULLP), (dict(q_norm_w=None), NULLP),
+    (dict(cfg=Q.indexer_config(num_heads=5)), UNSUP), (dict(cfg=Q.indexer_config(head_dim=64)), UNSUP),
+    (dict(cfg=Q.indexer_config(rot_dim=63)), UNSUP), (dict(cfg=Q.indexer_config(compress_ratio=9)), UNSUP),
+    (dict(cfg=Q.indexer_config(budget=0)), SHAPE), (dict(cfg=Q.indexer_config(rms_eps=-1.0)), SHAPE),
+    (dict(top_k=2050), SHAPE), (dict(seq_len=4 * 32768 + 4), UNSUP), (dict(workspace_bytes=1000), WS),
+    (dict(workspace=FAKE + 16), SHAPE), (dict(dtype=3), UNSUP), (dict(batch=0), SHAPE),
+])
+def test_indexer_prefill_rejects(no_gpu, kw, status):
+    assert _iprefill(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv_pool=None), NULLP), (dict(indices=None), NULLP),
+    (dict(pool_head_dim=255), SHAPE), (dict(pool_head_dim=200), SHAPE), (dict(top_k=100), SHAPE),
+    (dict(max_pages_per_seq=2048), UNSUP), (dict(workspace_bytes=64), WS), (dict(num_kv_heads=0), SHAPE),
+    (dict(cfg=Q.indexer_config(num_heads=0)), UNSUP),
+])
+def test_indexer_decode_rejects(no_gpu, kw, status):
+    assert _idecode(**kw) == status
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_LIB", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libqsa.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        L.load()

@@ -1,0 +1,310 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases compare every row; the five named workloads run at full size in
+the launch configuration bench.py times and compare sampled rows (the oracle
+computes those one by one).  See qsa_testlib for the comparison rules.
+"""
+import numpy as np
+import pytest
+import torch
+
+import qsa_synth as syn
+import qsa_testlib as TL
+import top_indexed_sparse_qsa_amd as Q
+from oracle import qsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("a gpu test ran without a GPU")
+    Q.load()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# runners (HIP path through the C ABI)
+# ---------------------------------------------------------------------------
+def gpu_sparse_prefill(inp, indices):
+    q, k, v = TL.dev(inp.q, inp.dtype), TL.dev(inp.k, inp.dtype), TL.dev(inp.v, inp.dtype)
+    o = torch.full_like(q, float("nan"))
+    idx = indices if isinstance(indices, torch.Tensor) else TL.dev(indices)
+    Q.qsa_sparse_prefill(q, k, v, o, idx, TL.dev(inp.ctx), inp.scale)
+    torch.cuda.synchronize()
+    return o
+
+
+def gpu_indexer_prefill(inp, icfg, top_k):
+    cfg = TL.idx_cfg_struct(icfg)
+    nbytes = Q.qsa_indexer_prefill_workspace_bytes(cfg, inp.B, inp.S)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((inp.B, inp.S, top_k), -7, dtype=torch.int32, device="cuda")
+    Q.qsa_indexer_prefill(TL.dev(inp.idx_q, inp.dtype), TL.dev(inp.idx_k, inp.dtype), TL.dev(inp.w_q),
+                          TL.dev(inp.w_k), TL.dev(inp.ctx), out, ws, cfg)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def kbar_from_workspace(ws, inp, icfg):
+    """The kbar region of the prefill workspace: after the fp32 queries."""
+    qbytes = inp.B * inp.S * icfg.num_heads * icfg.head_dim * 4
+    off = (qbytes + 255) // 256 * 256
+    gmax = inp.S // icfg.compress_ratio
+    raw = ws[off:off + inp.B * gmax * icfg.head_dim * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+    return raw.reshape(inp.B, gmax, icfg.head_dim)       # storage bits; rows past the live blocks are unset
+
+
+def compare_lists(lists_gpu, inp, icfg, top_k, rows, what):
+    ref, scores = O.indexer_prefill(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.ctx, icfg, inp.dtype,
+                                    top_k, rows=rows, return_scores=True)
+    swaps, same = 0, []
+    for (b, t) in rows:
+        used = TL.check_list(lists_gpu[b, t], ref[(b, t)], scores.get((b, t)), t, icfg, what)
+        swaps += used
+        if not used:
+            same.append((b, t))
+    return ref, swaps, same
+
+
+# ---------------------------------------------------------------------------
+# sparse prefill on given lists
+# ---------------------------------------------------------------------------
+PREFILL_CASES = [
+    dict(B=2, S=300, Hq=8, Hkv=2, D=128, dtype="fp16", top_k=100, ctx=[300, 177]),
+    dict(B=1, S=200, Hq=16, Hkv=1, D=128, dtype="bf16", top_k=200, ctx=[200]),
+    dict(B=2, S=130, Hq=4, Hkv=4, D=64, dtype="bf16", top_k=40, ctx=[130, 1]),
+    dict(B=1, S=100, Hq=12, Hkv=4, D=128, dtype="fp16", top_k=2051, ctx=[100]),
+    dict(B=3, S=70, Hq=6, Hkv=2, D=64, dtype="fp16", top_k=33, ctx=[0, 70, 45]),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"B{c['B']}S{c['S']}Hq{c['Hq']}Hkv{c['Hkv']}"
+                         f"D{c['D']}{c['dtype']}k{c['top_k']}")
+def test_sparse_prefill_small_all_rows(case):
+    c = dict(case)
+    top_k = c.pop("top_k")
+    TL.log(f"sparse_prefill small {case}")
+    inp = syn.make_prefill(7, with_indexer=False, **c)
+    idx = syn.random_lists(np.random.default_rng(70), inp.B, inp.S, top_k, inp.ctx)
+    o = gpu_sparse_prefill(inp, idx)
+    ref = O.sparse_prefill(inp.q, inp.k, inp.v, idx, inp.ctx, inp.scale, inp.dtype)
+    got = TL.host_f64(o, inp.dtype)
+    for b in range(inp.B):
+        live = min(int(inp.ctx[b]), inp.S)
+        TL.check_attention(got[b, :live], ref[b, :live], inp.dtype, f"b={b}")
+        TL.check_zero_rows(o[b, live:], f"b={b}")
+
+
+def test_sparse_prefill_workload1():
+    inp = syn.workload(1)
+    TL.log("sparse_prefill workload 1")
+    o = gpu_sparse_prefill(inp, inp.indices)
+    ref = O.sparse_prefill(inp.q, inp.k, inp.v, inp.indices, inp.ctx, inp.scale, "fp16")
+    TL.check_attention(TL.host_f64(o, "fp16"), ref, "fp16", "workload 1")
+
+
+def test_sparse_prefill_permuted_lists_same_result():
+    inp = syn.make_prefill(8, B=1, S=160, Hq=8, Hkv=1, D=128, dtype="fp16", ctx=[160], with_indexer=False)
+    rng = np.random.default_rng(80)
+    idx = syn.random_lists(rng, 1, 160, 96, inp.ctx)
+    perm = idx.copy()
+    for t in range(160):
+        n = int((idx[0, t] >= 0).sum())
+        perm[0, t, :n] = rng.permutation(idx[0, t, :n])
+    a = TL.host_f64(gpu_sparse_prefill(inp, idx), "fp16")
+    p = TL.host_f64(gpu_sparse_prefill(inp, perm), "fp16")
+    ref = O.sparse_prefill(inp.q, inp.k, inp.v, idx, inp.ctx, inp.scale, "fp16")
+    TL.check_attention(a, ref, "fp16", "sorted")
+    TL.check_attention(p, ref, "fp16", "permuted")
+
+
+# ---------------------------------------------------------------------------
+# indexer prefill
+# ---------------------------------------------------------------------------
+INDEXER_SMALL = [
+    dict(B=2, S=400, dtype="fp16", ctx=[400, 233], icfg=dict(budget=8)),
+    dict(B=2, S=257, dtype="bf16", ctx=[257, 96], icfg=dict(budget=5)),
+    dict(B=1, S=130, dtype="fp16", ctx=[130], icfg=dict(budget=3, compress_ratio=2, rot_dim=32, num_heads=3)),
+    dict(B=1, S=3, dtype="bf16", ctx=[3], icfg=dict(budget=1)),
+]
+
+
+@pytest.mark.parametrize("case", INDEXER_SMALL, ids=lambda c: f"B{c['B']}S{c['S']}{c['dtype']}{c['icfg']}")
+def test_indexer_prefill_small_all_rows(case):
+    icfg = syn.IndexerCfg(**case["icfg"])
+    TL.log(f"indexer_prefill small {case}")
+    inp = syn.make_prefill(9, B=case["B"], S=case["S"], Hq=2, Hkv=1, D=64, dtype=case["dtype"], ctx=case["ctx"],
+                           icfg=icfg)
+    out, ws = gpu_indexer_prefill(inp, icfg, icfg.top_k)
+    lists = out.cpu().numpy()
+    rows = [(b, t) for b in range(inp.B) for t in range(inp.S)]
+    _, swaps, _ = compare_lists(lists, inp, icfg, icfg.top_k, rows, "indexer small")
+    TL.log(f"  boundary swaps used: {swaps}")
+    # kbar is computed in float64 and rounded once on both sides
+    kb = kbar_from_workspace(ws, inp, icfg)
+    for b in range(inp.B):
+        n = min(int(inp.ctx[b]), inp.S) // icfg.compress_ratio
+        ref = O.pool_blocks(O.widen(inp.idx_k[b, :n * icfg.compress_ratio], inp.dtype), 0, inp.w_k, icfg, inp.dtype)
+        got = kb[b, :n].view(np.float16) if inp.dtype == "fp16" else kb[b, :n]
+        assert np.array_equal(O.widen(got, inp.dtype), ref), "kbar differs from the oracle"
+
+
+def test_indexer_prefill_budget512_selective_rows():
+    icfg = syn.IndexerCfg()
+    TL.log("indexer_prefill S=2600 budget 512")
+    inp = syn.make_prefill(10, B=1, S=2600, Hq=2, Hkv=1, D=64, dtype="fp16", ctx=[2600])
+    out, _ = gpu_indexer_prefill(inp, icfg, icfg.top_k)
+    rows = [(0, t) for t in list(range(0, 64)) + list(range(2040, 2600))]
+    _, swaps, _ = compare_lists(out.cpu().numpy(), inp, icfg, icfg.top_k, rows, "S2600")
+    TL.log(f"  boundary swaps used: {swaps}")
+
+
+# ---------------------------------------------------------------------------
+# the prefill workloads at full size (bench launch configuration)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("wl", [2, 3, 5])
+def test_prefill_workload_full_size(wl):
+    TL.log(f"prefill workload {wl}: generating")
+    inp = syn.workload(wl)
+    icfg = inp.icfg
+    TL.log(f"prefill workload {wl}: indexer")
+    out, _ = gpu_indexer_prefill(inp, icfg, icfg.top_k)
+    TL.log(f"prefill workload {wl}: attention")
+    o = gpu_sparse_prefill(inp, out)
+    rng = np.random.default_rng(100 + wl)
+    rows = TL.sample_rows(inp.B, inp.S, inp.ctx, 24, rng)
+    TL.log(f"prefill workload {wl}: oracle on {len(rows)} rows")
+    lists = {r: out[r[0], r[1]].cpu().numpy() for r in rows}
+    ref_lists, swaps, same = compare_lists(lists, inp, icfg, icfg.top_k, rows, f"workload {wl}")
+    TL.log(f"  boundary swaps used: {swaps} of {len(rows)} rows")
+    # attention parity on rows whose lists agree (each side reads its own lists)
+    full = np.full((inp.B, inp.S, icfg.top_k), -1, dtype=np.int32)
+    for r in same:
+        full[r] = ref_lists[r]
+    ref_o = O.sparse_prefill(inp.q, inp.k, inp.v, full, inp.ctx, inp.scale, inp.dtype, rows=same)
+    for (b, t) in same:
+        live = min(int(inp.ctx[b]), inp.S)
+        if t < live:
+            TL.check_attention(TL.host_f64(o[b, t], inp.dtype), ref_o[(b, t)], inp.dtype,
+                               f"workload {wl} b={b} t={t}")
+    for b in range(inp.B):
+        live = min(int(inp.ctx[b]), inp.S)
+        TL.check_zero_rows(o[b, live:], f"workload {wl} b={b}")
+
+
+@pytest.mark.parametrize("wl", [2, 5])
+def test_sparse_prefill_structured_lists_full_size(wl):
+    TL.log(f"sparse prefill structured lists workload {wl}")
+    inp = syn.workload(wl)
+    rng = np.random.default_rng(200 + wl)
+    idx = TL.structured_lists(rng, inp.B, inp.S, inp.ctx, inp.icfg, inp.icfg.top_k)
+    o = gpu_sparse_prefill(inp, idx)
+    rows = TL.sample_rows(inp.B, inp.S, inp.ctx, 24, rng)
+    ref = O.sparse_prefill(inp.q, inp.k, inp.v, idx, inp.ctx, inp.scale, inp.dtype, rows=rows)
+    for (b, t) in rows:
+        TL.check_attention(TL.host_f64(o[b, t], inp.dtype), ref[(b, t)], inp.dtype, f"b={b} t={t}")
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def gpu_indexer_decode(inp, pool_dev):
+    icfg = inp.icfg
+    cfg = TL.idx_cfg_struct(icfg)
+    ws = torch.empty(Q.qsa_indexer_decode_workspace_bytes(cfg, inp.B, inp.max_pages), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((inp.B, 1, inp.top_k), -7, dtype=torch.int32, device="cuda")
+    Q.qsa_indexer_decode(TL.dev(inp.idx_q, inp.dtype), TL.dev(inp.idx_k, inp.dtype), TL.dev(inp.w_q),
+                         TL.dev(inp.w_k), pool_dev, TL.dev(inp.page_table), TL.dev(inp.ctx), out, ws, cfg,
+                         inp.D)
+    torch.cuda.synchronize()
+    return out
+
+
+class DecodeWs:
+    def __init__(self, inp):
+        self.po = torch.empty(Q.qsa_sparse_decode_partial_o_elems(inp.B, inp.Hkv, inp.D), dtype=torch.float32,
+                              device="cuda")
+        self.ps = torch.empty(Q.qsa_sparse_decode_partial_stats_elems(inp.B, inp.Hkv), dtype=torch.float32,
+                              device="cuda")
+        self.cnt = torch.zeros(Q.qsa_sparse_decode_counter_elems(inp.B, inp.Hkv), dtype=torch.int32,
+                               device="cuda")
+
+
+def gpu_sparse_decode(inp, pool_dev, lists_dev, ws, num_splits=0):
+    q = TL.dev(inp.q, inp.dtype)
+    o = torch.full_like(q, float("nan"))
+    Q.qsa_sparse_decode(q, o, pool_dev, TL.dev(inp.page_table), lists_dev, TL.dev(inp.ctx), ws.po, ws.ps, ws.cnt,
+                        inp.scale, head_dim=inp.D, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o
+
+
+def decode_parity(inp, what, splits=(0,)):
+    icfg = inp.icfg
+    pool_dev = TL.dev(inp.pool, inp.dtype)
+    TL.log(f"{what}: indexer decode")
+    lists_t = gpu_indexer_decode(inp, pool_dev)
+    writes, ref_lists, scores = O.indexer_decode(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.pool,
+                                                 inp.page_table, inp.ctx, icfg, inp.D, inp.dtype, inp.top_k,
+                                                 return_scores=True)
+    # owned tails bit-exact, everything else bit-unchanged
+    expect = TL.dev(inp.pool, inp.dtype)
+    for pg, row, vals in writes:
+        expect[pg, row, 0, inp.D:inp.D + vals.shape[0]] = TL.dev(vals, inp.dtype)
+    assert torch.equal(pool_dev.view(torch.int16), expect.view(torch.int16)), f"{what}: pool differs"
+    del expect
+    lists = lists_t.cpu().numpy()
+    swaps, same = 0, []
+    for b in range(inp.B):
+        c = int(inp.ctx[b])
+        if c <= 0:
+            assert np.all(lists[b, 0] == -1)
+            continue
+        used = TL.check_list(lists[b, 0], ref_lists[b, 0], scores[b], c - 1, icfg, f"{what} b={b}")
+        swaps += used
+        if not used:
+            same.append(b)
+    TL.log(f"  boundary swaps used: {swaps} of {inp.B}")
+    ref_o = O.sparse_decode(inp.q, inp.pool, inp.page_table, ref_lists, inp.ctx, inp.scale, inp.D, inp.dtype)
+    ws = DecodeWs(inp)
+    outs = []
+    for ns in splits:
+        TL.log(f"{what}: sparse decode num_splits={ns}")
+        o = gpu_sparse_decode(inp, pool_dev, lists_t, ws, ns)
+        got = TL.host_f64(o, inp.dtype)[:, 0]
+        for b in same:
+            TL.check_attention(got[b], ref_o[b], inp.dtype, f"{what} splits={ns} b={b}")
+        assert int(ws.cnt.abs().sum()) == 0, "split counters not reset"
+        outs.append(o)
+    return pool_dev, lists_t, ws, outs
+
+
+DECODE_SMALL = [
+    dict(B=6, Hq=32, Hkv=4, D=128, dtype="fp16", ctx=[1, 6, 2052, 3000, 4096, 8191], max_pages=64),
+    dict(B=5, Hq=64, Hkv=4, D=128, dtype="bf16", ctx=[2, 7, 2051, 5000, 2049], max_pages=40),
+    dict(B=3, Hq=8, Hkv=2, D=64, dtype="fp16", ctx=[0, 2200, 4100], max_pages=33),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SMALL, ids=lambda c: f"B{c['B']}Hq{c['Hq']}D{c['D']}{c['dtype']}")
+def test_decode_small(case):
+    TL.log(f"decode small {case}")
+    inp = syn.make_decode(11, **case)
+    decode_parity(inp, "decode small", splits=(0, 1, 3, 16))
+
+
+def test_decode_workload4_full_size_and_determinism():
+    TL.log("decode workload 4: generating")
+    inp = syn.workload(4)
+    pool_dev, lists_t, ws, outs = decode_parity(inp, "workload 4", splits=(0, 8))
+    ref_bits = outs[0].view(torch.int16).clone()
+    for i in range(10):
+        o = gpu_sparse_decode(inp, pool_dev, lists_t, ws, 0)
+        assert torch.equal(o.view(torch.int16), ref_bits), f"rerun {i} differs"
+    # the indexer step is idempotent: a second call rewrites the same tails and lists
+    again = gpu_indexer_decode(inp, pool_dev)
+    assert torch.equal(again, lists_t)

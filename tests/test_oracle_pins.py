@@ -276,6 +276,15 @@ def test_lists_closed_forms_full_budget():
             assert np.array_equal(lst[: t + 1], np.arange(t + 1))
 
 
+def test_rows_before_the_first_complete_block():
+    # S < ratio: no complete block exists; every row is its causal tail 0..t.
+    icfg = syn.IndexerCfg(budget=1)
+    inp = syn.make_prefill(23, B=1, S=3, Hq=1, Hkv=1, D=16, dtype="fp16", ctx=[3], icfg=icfg)
+    lists = O.indexer_prefill(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.ctx, icfg, "fp16", icfg.top_k)
+    assert lists[0].tolist() == [[0, -1, -1, -1, -1, -1, -1], [0, 1, -1, -1, -1, -1, -1],
+                                 [0, 1, 2, -1, -1, -1, -1]]
+
+
 def test_lists_bruteforce_small_budget():
     icfg = syn.IndexerCfg(budget=3, head_dim=16, rot_dim=8)
     inp = syn.make_prefill(22, B=2, S=60, Hq=2, Hkv=1, D=16, dtype="bf16", ctx=[60, 37], icfg=icfg)

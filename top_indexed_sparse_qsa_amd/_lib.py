@@ -1,0 +1,222 @@
+"""ctypes binding of libqsa (include/libqsa.h).
+
+Argument marshalling only: every step of the hot path runs in libqsa's HIP
+kernels.  Functions carry the C names, take torch tensors for device buffers
+and enqueue on the current HIP stream unless one is given.  A missing or
+unloadable libqsa.so raises immediately; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqsa.so")
+
+QSA_FP16, QSA_BF16 = 0, 1
+QSA_PAGE_TOKENS = 128
+QSA_PARTIAL_ROWS = 16
+QSA_MAX_SPLITS = 16
+QSA_MAX_BLOCKS = 32768
+
+STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL_POINTER", 2: "QSA_ERR_BAD_SHAPE", 3: "QSA_ERR_UNSUPPORTED",
+          4: "QSA_ERR_WORKSPACE_TOO_SMALL", 5: "QSA_ERR_LAUNCH"}
+
+EXPORTS = [
+    "qsa_indexer_prefill", "qsa_sparse_prefill", "qsa_indexer_decode", "qsa_sparse_decode",
+    "qsa_indexer_prefill_workspace_bytes", "qsa_indexer_decode_workspace_bytes",
+    "qsa_sparse_decode_partial_o_elems", "qsa_sparse_decode_partial_stats_elems",
+    "qsa_sparse_decode_counter_elems", "qsa_sparse_decode_default_splits", "qsa_status_string",
+]
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class QsaIndexerConfig(ctypes.Structure):
+    _fields_ = [("num_heads", _i32), ("head_dim", _i32), ("rot_dim", _i32), ("compress_ratio", _i32),
+                ("budget", _i32), ("rope_theta", _f32), ("rms_eps", _f32)]
+
+
+class SparsePrefillParams(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp), ("indices", _vp), ("context_lengths", _vp),
+                ("batch", _i32), ("seq_len", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
+                ("head_dim", _i32), ("top_k", _i32), ("attention_scale", _f32), ("dtype", ctypes.c_int),
+                ("stream", _vp)]
+
+
+class SparseDecodeParams(ctypes.Structure):
+    _fields_ = [("q", _vp), ("o", _vp), ("kv_pool", _vp), ("page_table", _vp), ("indices", _vp),
+                ("context_lengths", _vp), ("partial_o", _vp), ("partial_stats", _vp), ("split_counters", _vp),
+                ("batch", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
+                ("pool_head_dim", _i32), ("num_flat_pages", _i32), ("max_pages_per_seq", _i32),
+                ("top_k", _i32), ("num_splits", _i32), ("attention_scale", _f32), ("dtype", ctypes.c_int),
+                ("stream", _vp)]
+
+
+class IndexerPrefillParams(ctypes.Structure):
+    _fields_ = [("idx_q", _vp), ("idx_k", _vp), ("q_norm_w", _vp), ("k_norm_w", _vp),
+                ("context_lengths", _vp), ("indices", _vp), ("workspace", _vp), ("workspace_bytes", _sz),
+                ("batch", _i32), ("seq_len", _i32), ("top_k", _i32), ("cfg", QsaIndexerConfig),
+                ("dtype", ctypes.c_int), ("stream", _vp)]
+
+
+class IndexerDecodeParams(ctypes.Structure):
+    _fields_ = [("idx_q", _vp), ("idx_k", _vp), ("q_norm_w", _vp), ("k_norm_w", _vp), ("kv_pool", _vp),
+                ("page_table", _vp), ("context_lengths", _vp), ("indices", _vp), ("workspace", _vp),
+                ("workspace_bytes", _sz), ("batch", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
+                ("pool_head_dim", _i32), ("num_flat_pages", _i32), ("max_pages_per_seq", _i32),
+                ("top_k", _i32), ("cfg", QsaIndexerConfig), ("dtype", ctypes.c_int), ("stream", _vp)]
+
+
+class QsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+        self.status = status
+
+
+_LIB = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libqsa.so from the package directory (build it with
+    ``python -m top_indexed_sparse_qsa_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build libqsa first "
+                           "(python -m top_indexed_sparse_qsa_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, st in (("qsa_indexer_prefill", IndexerPrefillParams), ("qsa_sparse_prefill", SparsePrefillParams),
+                     ("qsa_indexer_decode", IndexerDecodeParams), ("qsa_sparse_decode", SparseDecodeParams)):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.POINTER(st)]
+        fn.restype = ctypes.c_int
+    lib.qsa_indexer_prefill_workspace_bytes.argtypes = [ctypes.POINTER(QsaIndexerConfig), _i32, _i32]
+    lib.qsa_indexer_prefill_workspace_bytes.restype = _sz
+    lib.qsa_indexer_decode_workspace_bytes.argtypes = [ctypes.POINTER(QsaIndexerConfig), _i32, _i32]
+    lib.qsa_indexer_decode_workspace_bytes.restype = _sz
+    lib.qsa_sparse_decode_partial_o_elems.argtypes = [_i32, _i32, _i32]
+    lib.qsa_sparse_decode_partial_o_elems.restype = _sz
+    lib.qsa_sparse_decode_partial_stats_elems.argtypes = [_i32, _i32]
+    lib.qsa_sparse_decode_partial_stats_elems.restype = _sz
+    lib.qsa_sparse_decode_counter_elems.argtypes = [_i32, _i32]
+    lib.qsa_sparse_decode_counter_elems.restype = _sz
+    lib.qsa_sparse_decode_default_splits.argtypes = [_i32, _i32, _i32]
+    lib.qsa_sparse_decode_default_splits.restype = _i32
+    lib.qsa_status_string.argtypes = [ctypes.c_int]
+    lib.qsa_status_string.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return QSA_FP16
+    if t.dtype == torch.bfloat16:
+        return QSA_BF16
+    raise TypeError(f"libqsa takes float16 or bfloat16 tensors, got {t.dtype}")
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, st: int) -> None:
+    if st != 0:
+        raise QsaError(fn, st)
+
+
+def indexer_config(num_heads=4, head_dim=128, rot_dim=64, compress_ratio=4, budget=512,
+                   rope_theta=1.0e6, rms_eps=1.0e-6) -> QsaIndexerConfig:
+    return QsaIndexerConfig(num_heads, head_dim, rot_dim, compress_ratio, budget, rope_theta, rms_eps)
+
+
+def qsa_status_string(status: int) -> str:
+    return load().qsa_status_string(status).decode()
+
+
+def qsa_indexer_prefill_workspace_bytes(cfg: QsaIndexerConfig, batch: int, seq_len: int) -> int:
+    return int(load().qsa_indexer_prefill_workspace_bytes(ctypes.byref(cfg), batch, seq_len))
+
+
+def qsa_indexer_decode_workspace_bytes(cfg: QsaIndexerConfig, batch: int, max_pages_per_seq: int) -> int:
+    return int(load().qsa_indexer_decode_workspace_bytes(ctypes.byref(cfg), batch, max_pages_per_seq))
+
+
+def qsa_sparse_decode_partial_o_elems(batch: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(load().qsa_sparse_decode_partial_o_elems(batch, num_kv_heads, head_dim))
+
+
+def qsa_sparse_decode_partial_stats_elems(batch: int, num_kv_heads: int) -> int:
+    return int(load().qsa_sparse_decode_partial_stats_elems(batch, num_kv_heads))
+
+
+def qsa_sparse_decode_counter_elems(batch: int, num_kv_heads: int) -> int:
+    return int(load().qsa_sparse_decode_counter_elems(batch, num_kv_heads))
+
+
+def qsa_sparse_decode_default_splits(batch: int, num_kv_heads: int, top_k: int) -> int:
+    return int(load().qsa_sparse_decode_default_splits(batch, num_kv_heads, top_k))
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def qsa_sparse_prefill(q, k, v, o, indices, context_lengths, attention_scale: float, stream=None) -> None:
+    """q, o [B,S,Hq,D]; k, v [B,S,Hkv,D]; indices int32 [B,S,top_k]; context_lengths int32 [B]."""
+    B, S, Hq, D = q.shape
+    p = SparsePrefillParams(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(indices), _ptr(context_lengths),
+                            B, S, Hq, k.shape[2], D, indices.shape[-1], float(attention_scale),
+                            _dtype_code(q), _stream(stream))
+    _check("qsa_sparse_prefill", load().qsa_sparse_prefill(ctypes.byref(p)))
+
+
+def qsa_sparse_decode(q, o, kv_pool, page_table, indices, context_lengths, partial_o, partial_stats,
+                      split_counters, attention_scale: float, head_dim: int | None = None,
+                      num_splits: int = 0, stream=None) -> None:
+    """q, o [B,1,Hq,D]; kv_pool [2*numPages,128,Hkv,poolHeadDim]; page_table int32 [B,2,maxPages]."""
+    B, _, Hq, D = q.shape
+    D = head_dim or D
+    p = SparseDecodeParams(_ptr(q), _ptr(o), _ptr(kv_pool), _ptr(page_table), _ptr(indices),
+                           _ptr(context_lengths), _ptr(partial_o), _ptr(partial_stats), _ptr(split_counters),
+                           B, Hq, kv_pool.shape[2], D, kv_pool.shape[3], kv_pool.shape[0],
+                           page_table.shape[-1], indices.shape[-1], num_splits, float(attention_scale),
+                           _dtype_code(q), _stream(stream))
+    _check("qsa_sparse_decode", load().qsa_sparse_decode(ctypes.byref(p)))
+
+
+def qsa_indexer_prefill(idx_q, idx_k, q_norm_w, k_norm_w, context_lengths, indices, workspace,
+                        cfg: QsaIndexerConfig, stream=None) -> None:
+    """idx_q [B,S,Hi,hd]; idx_k [B,S,hd]; q_norm_w/k_norm_w fp32 [hd]; indices int32 [B,S,top_k]."""
+    B, S = idx_k.shape[0], idx_k.shape[1]
+    p = IndexerPrefillParams(_ptr(idx_q), _ptr(idx_k), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(context_lengths),
+                             _ptr(indices), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             B, S, indices.shape[-1], cfg, _dtype_code(idx_q), _stream(stream))
+    _check("qsa_indexer_prefill", load().qsa_indexer_prefill(ctypes.byref(p)))
+
+
+def qsa_indexer_decode(idx_q, idx_k, q_norm_w, k_norm_w, kv_pool, page_table, context_lengths, indices,
+                       workspace, cfg: QsaIndexerConfig, head_dim: int, stream=None) -> None:
+    """idx_q [B,1,Hi,hd]; idx_k [B,1,hd]; kv_pool updated in place (head-0 tails only)."""
+    B = idx_k.shape[0]
+    p = IndexerDecodeParams(_ptr(idx_q), _ptr(idx_k), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(kv_pool),
+                            _ptr(page_table), _ptr(context_lengths), _ptr(indices), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), B, kv_pool.shape[2], head_dim,
+                            kv_pool.shape[3], kv_pool.shape[0], page_table.shape[-1], indices.shape[-1], cfg,
+                            _dtype_code(idx_q), _stream(stream))
+    _check("qsa_indexer_decode", load().qsa_indexer_decode(ctypes.byref(p)))

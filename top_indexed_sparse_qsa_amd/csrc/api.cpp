@@ -1,0 +1,346 @@
+// libqsa C ABI: argument validation, workspace layout, split planning and
+// kernel launches on the caller's stream.  Validation happens before any
+// HIP call, so a rejected call touches no device state.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "../../include/libqsa.h"
+#include "qsa_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+size_t round16(size_t x) { return (x + 15) / 16 * 16; }
+
+bool dtype_ok(qsa_dtype d) { return d == QSA_FP16 || d == QSA_BF16; }
+
+// Kernels read 16-byte vectors; every device base pointer must allow that.
+bool aligned16(const void *p) { return ((uintptr_t)p % 16) == 0; }
+template <class... P>
+bool all_aligned16(const P *...p) { return (aligned16(p) && ...); }
+
+qsa_status check_heads(int32_t hq, int32_t hkv, int32_t d) {
+  if (hq < 1 || hkv < 1) return QSA_ERR_BAD_SHAPE;
+  if (hq % hkv != 0) return QSA_ERR_BAD_SHAPE;
+  if (hq / hkv > 16) return QSA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return QSA_ERR_UNSUPPORTED;
+  return QSA_OK;
+}
+
+qsa_status check_cfg(const qsa_indexer_config &c) {
+  if (c.num_heads < 1 || c.num_heads > 4) return QSA_ERR_UNSUPPORTED;
+  if (c.head_dim != 128) return QSA_ERR_UNSUPPORTED;
+  if (c.rot_dim < 0 || c.rot_dim > c.head_dim || (c.rot_dim & 1)) return QSA_ERR_UNSUPPORTED;
+  if (c.compress_ratio < 1 || c.compress_ratio > 8) return QSA_ERR_UNSUPPORTED;
+  if (c.budget < 1) return QSA_ERR_BAD_SHAPE;
+  if (!(c.rope_theta > 0.f) || !(c.rms_eps >= 0.f) || !isfinite(c.rope_theta) || !isfinite(c.rms_eps))
+    return QSA_ERR_BAD_SHAPE;
+  return QSA_OK;
+}
+
+int64_t min_top_k(const qsa_indexer_config &c) {
+  return (int64_t)c.budget * c.compress_ratio + c.compress_ratio - 1;
+}
+
+// Prefill indexer workspace: fp32 queries | 16-bit kbar | fp32 score rows.
+struct PrefillWs {
+  size_t qhat, kbar, scores, total;
+  int gmax, stride;
+};
+PrefillWs prefill_ws(const qsa_indexer_config &c, int32_t B, int32_t S) {
+  PrefillWs w{};
+  w.gmax = S / c.compress_ratio;
+  w.stride = (int)round16((size_t)(w.gmax > 0 ? w.gmax : 1));
+  w.qhat = 0;
+  w.kbar = align_up((size_t)B * S * c.num_heads * c.head_dim * 4);
+  w.scores = w.kbar + align_up((size_t)B * (w.gmax > 0 ? w.gmax : 1) * c.head_dim * 2);
+  w.total = w.scores + align_up((size_t)B * S * w.stride * 4);
+  return w;
+}
+
+struct DecodeWs {
+  size_t qhat, scores, total;
+  int stride;
+};
+DecodeWs decode_ws(const qsa_indexer_config &c, int32_t B, int32_t max_pages) {
+  DecodeWs w{};
+  const size_t gmax = (size_t)max_pages * QSA_PAGE_TOKENS / c.compress_ratio;
+  w.stride = (int)round16(gmax > 0 ? gmax : 1);
+  w.qhat = 0;
+  w.scores = align_up((size_t)B * c.num_heads * c.head_dim * 4);
+  w.total = w.scores + align_up((size_t)B * w.stride * 4);
+  return w;
+}
+
+int default_splits(int32_t B, int32_t hkv, int32_t top_k) {
+  const int chunks = (top_k + 31) / 32;
+  const int pairs = B * hkv;
+  int want = (2048 + pairs - 1) / pairs;  // aim for ~2048 waves (8 per CU)
+  if (want > QSA_MAX_SPLITS) want = QSA_MAX_SPLITS;
+  if (want > chunks) want = chunks;
+  if (want < 1) want = 1;
+  return want;
+}
+
+qsa_status launched(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *qsa_status_string(qsa_status s) {
+  switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_NULL_POINTER: return "null pointer argument";
+    case QSA_ERR_BAD_SHAPE: return "invalid shape or size argument";
+    case QSA_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case QSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case QSA_ERR_LAUNCH: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t qsa_indexer_prefill_workspace_bytes(const qsa_indexer_config *cfg, int32_t batch, int32_t seq_len) {
+  if (!cfg || check_cfg(*cfg) != QSA_OK || batch < 1 || seq_len < 1) return 0;
+  return prefill_ws(*cfg, batch, seq_len).total;
+}
+
+size_t qsa_indexer_decode_workspace_bytes(const qsa_indexer_config *cfg, int32_t batch, int32_t max_pages) {
+  if (!cfg || check_cfg(*cfg) != QSA_OK || batch < 1 || max_pages < 1) return 0;
+  return decode_ws(*cfg, batch, max_pages).total;
+}
+
+size_t qsa_sparse_decode_partial_o_elems(int32_t batch, int32_t hkv, int32_t d) {
+  if (batch < 1 || hkv < 1 || d < 1) return 0;
+  return (size_t)batch * hkv * QSA_MAX_SPLITS * QSA_PARTIAL_ROWS * d;
+}
+
+size_t qsa_sparse_decode_partial_stats_elems(int32_t batch, int32_t hkv) {
+  if (batch < 1 || hkv < 1) return 0;
+  return (size_t)batch * hkv * QSA_MAX_SPLITS * 2 * QSA_PARTIAL_ROWS;
+}
+
+size_t qsa_sparse_decode_counter_elems(int32_t batch, int32_t hkv) {
+  if (batch < 1 || hkv < 1) return 0;
+  return (size_t)batch * hkv;
+}
+
+int32_t qsa_sparse_decode_default_splits(int32_t batch, int32_t hkv, int32_t top_k) {
+  if (batch < 1 || hkv < 1 || top_k < 1) return 0;
+  return default_splits(batch, hkv, top_k);
+}
+
+qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p) {
+  if (!p || !p->q || !p->k || !p->v || !p->o || !p->indices || !p->context_lengths) return QSA_ERR_NULL_POINTER;
+  if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
+  if (p->batch < 1 || p->seq_len < 1 || p->top_k < 1) return QSA_ERR_BAD_SHAPE;
+  if (qsa_status st = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim)) return st;
+  if (!all_aligned16(p->q, p->k, p->v, p->o)) return QSA_ERR_BAD_SHAPE;
+  if ((int64_t)p->batch * p->seq_len * p->num_kv_heads > (int64_t)INT32_MAX - 4) return QSA_ERR_UNSUPPORTED;
+  if (!isfinite(p->attention_scale)) return QSA_ERR_BAD_SHAPE;
+  qsa::PrefillAttnArgs a;
+  a.q = static_cast<const uint16_t *>(p->q);
+  a.k = static_cast<const uint16_t *>(p->k);
+  a.v = static_cast<const uint16_t *>(p->v);
+  a.o = static_cast<uint16_t *>(p->o);
+  a.indices = p->indices;
+  a.ctx = p->context_lengths;
+  a.B = p->batch;
+  a.S = p->seq_len;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads;
+  a.top_k = p->top_k;
+  a.sl2 = p->attention_scale * qsa::kLog2e;
+  return launched(qsa::launch_sparse_prefill(a, p->head_dim, (int)p->dtype, (hipStream_t)p->stream));
+}
+
+qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
+  if (!p || !p->q || !p->o || !p->kv_pool || !p->page_table || !p->indices || !p->context_lengths ||
+      !p->partial_o || !p->partial_stats || !p->split_counters)
+    return QSA_ERR_NULL_POINTER;
+  if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
+  if (p->batch < 1 || p->top_k < 1 || p->num_flat_pages < 1 || p->max_pages_per_seq < 1) return QSA_ERR_BAD_SHAPE;
+  if (qsa_status st = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim)) return st;
+  if (p->pool_head_dim < p->head_dim || (p->pool_head_dim % 8) != 0) return QSA_ERR_BAD_SHAPE;
+  if (!all_aligned16(p->q, p->o, p->kv_pool, p->partial_o)) return QSA_ERR_BAD_SHAPE;
+  if (p->max_pages_per_seq > 4096) return QSA_ERR_UNSUPPORTED;
+  if (p->num_splits < 0 || p->num_splits > QSA_MAX_SPLITS) return QSA_ERR_BAD_SHAPE;
+  if ((int64_t)p->batch * p->num_kv_heads * QSA_MAX_SPLITS > (int64_t)INT32_MAX) return QSA_ERR_UNSUPPORTED;
+  if (!isfinite(p->attention_scale)) return QSA_ERR_BAD_SHAPE;
+  int splits = p->num_splits ? p->num_splits : default_splits(p->batch, p->num_kv_heads, p->top_k);
+  const int chunks = (p->top_k + 31) / 32;
+  const int per = (chunks + splits - 1) / splits;
+  splits = (chunks + per - 1) / per;  // drop splits that would get no slots
+  qsa::DecodeAttnArgs a;
+  a.q = static_cast<const uint16_t *>(p->q);
+  a.o = static_cast<uint16_t *>(p->o);
+  a.pool = static_cast<const uint16_t *>(p->kv_pool);
+  a.pt = p->page_table;
+  a.indices = p->indices;
+  a.ctx = p->context_lengths;
+  a.part_o = p->partial_o;
+  a.part_stats = p->partial_stats;
+  a.counters = p->split_counters;
+  a.B = p->batch;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads;
+  a.PHD = p->pool_head_dim;
+  a.num_flat_pages = p->num_flat_pages;
+  a.max_pages = p->max_pages_per_seq;
+  a.top_k = p->top_k;
+  a.nsplits = splits;
+  a.split_slots = per * 32;
+  a.sl2 = p->attention_scale * qsa::kLog2e;
+  return launched(qsa::launch_sparse_decode(a, p->head_dim, (int)p->dtype, (hipStream_t)p->stream));
+}
+
+qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p) {
+  if (!p || !p->idx_q || !p->idx_k || !p->q_norm_w || !p->k_norm_w || !p->context_lengths || !p->indices ||
+      !p->workspace)
+    return QSA_ERR_NULL_POINTER;
+  if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
+  if (qsa_status st = check_cfg(p->cfg)) return st;
+  if (p->batch < 1 || p->seq_len < 1) return QSA_ERR_BAD_SHAPE;
+  if (p->top_k < min_top_k(p->cfg)) return QSA_ERR_BAD_SHAPE;
+  if (p->seq_len / p->cfg.compress_ratio > QSA_MAX_BLOCKS) return QSA_ERR_UNSUPPORTED;
+  if (!all_aligned16(p->idx_q, p->idx_k)) return QSA_ERR_BAD_SHAPE;
+  if ((int64_t)p->batch * p->seq_len > (int64_t)INT32_MAX / 2) return QSA_ERR_UNSUPPORTED;
+  if (((uintptr_t)p->workspace % kAlign) != 0) return QSA_ERR_BAD_SHAPE;
+  const PrefillWs w = prefill_ws(p->cfg, p->batch, p->seq_len);
+  if (p->workspace_bytes < w.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
+  char *ws = static_cast<char *>(p->workspace);
+  const hipStream_t s = (hipStream_t)p->stream;
+  const int dt = (int)p->dtype;
+
+  qsa::IdxPrepArgs pa;
+  pa.idx_q = static_cast<const uint16_t *>(p->idx_q);
+  pa.idx_k = static_cast<const uint16_t *>(p->idx_k);
+  pa.wq = p->q_norm_w;
+  pa.wk = p->k_norm_w;
+  pa.ctx = p->context_lengths;
+  pa.qhat = reinterpret_cast<float *>(ws + w.qhat);
+  pa.kbar = reinterpret_cast<uint16_t *>(ws + w.kbar);
+  pa.B = p->batch;
+  pa.S = p->seq_len;
+  pa.Hi = p->cfg.num_heads;
+  pa.hd = p->cfg.head_dim;
+  pa.rot = p->cfg.rot_dim;
+  pa.ratio = p->cfg.compress_ratio;
+  pa.Gmax = w.gmax;
+  pa.theta = (double)p->cfg.rope_theta;
+  pa.eps = (double)p->cfg.rms_eps;
+  pa.dt = dt;
+  if (qsa::launch_idx_prep(pa, s) != hipSuccess) return QSA_ERR_LAUNCH;
+
+  qsa::IdxScoreArgs sa;
+  sa.qhat = pa.qhat;
+  sa.kbar = pa.kbar;
+  sa.scores = reinterpret_cast<float *>(ws + w.scores);
+  sa.ctx = p->context_lengths;
+  sa.B = p->batch;
+  sa.S = p->seq_len;
+  sa.Hi = p->cfg.num_heads;
+  sa.Gmax = w.gmax;
+  sa.stride = w.stride;
+  sa.ratio = p->cfg.compress_ratio;
+  if (qsa::launch_idx_score(sa, dt, s) != hipSuccess) return QSA_ERR_LAUNCH;
+
+  qsa::IdxSelectArgs xa;
+  xa.scores = sa.scores;
+  xa.row_stride = w.stride;
+  xa.out = p->indices;
+  xa.ctx = p->context_lengths;
+  xa.B = p->batch;
+  xa.S = p->seq_len;
+  xa.top_k = p->top_k;
+  xa.budget = p->cfg.budget;
+  xa.ratio = p->cfg.compress_ratio;
+  xa.decode = 0;
+  xa.max_ctx = p->seq_len;
+  return launched(qsa::launch_idx_select(xa, w.gmax, s));
+}
+
+qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
+  if (!p || !p->idx_q || !p->idx_k || !p->q_norm_w || !p->k_norm_w || !p->kv_pool || !p->page_table ||
+      !p->context_lengths || !p->indices || !p->workspace)
+    return QSA_ERR_NULL_POINTER;
+  if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
+  if (qsa_status st = check_cfg(p->cfg)) return st;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->num_flat_pages < 1 || p->max_pages_per_seq < 1)
+    return QSA_ERR_BAD_SHAPE;
+  if (p->head_dim < 1 || p->pool_head_dim < p->head_dim + p->cfg.head_dim || (p->head_dim % 8) != 0 ||
+      (p->pool_head_dim % 8) != 0)
+    return QSA_ERR_BAD_SHAPE;
+  if (p->top_k < min_top_k(p->cfg)) return QSA_ERR_BAD_SHAPE;
+  if ((int64_t)p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio > QSA_MAX_BLOCKS)
+    return QSA_ERR_UNSUPPORTED;
+  if (!all_aligned16(p->idx_q, p->idx_k, p->kv_pool)) return QSA_ERR_BAD_SHAPE;
+  if (((uintptr_t)p->workspace % kAlign) != 0) return QSA_ERR_BAD_SHAPE;
+  const DecodeWs w = decode_ws(p->cfg, p->batch, p->max_pages_per_seq);
+  if (p->workspace_bytes < w.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
+  char *ws = static_cast<char *>(p->workspace);
+  const hipStream_t s = (hipStream_t)p->stream;
+  const int dt = (int)p->dtype;
+  const int gmax = p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio;
+
+  qsa::IdxDecPrepArgs pa;
+  pa.idx_q = static_cast<const uint16_t *>(p->idx_q);
+  pa.idx_k = static_cast<const uint16_t *>(p->idx_k);
+  pa.wq = p->q_norm_w;
+  pa.wk = p->k_norm_w;
+  pa.pool = static_cast<uint16_t *>(p->kv_pool);
+  pa.pt = p->page_table;
+  pa.ctx = p->context_lengths;
+  pa.qhat = reinterpret_cast<float *>(ws + w.qhat);
+  pa.B = p->batch;
+  pa.Hi = p->cfg.num_heads;
+  pa.hd = p->cfg.head_dim;
+  pa.rot = p->cfg.rot_dim;
+  pa.ratio = p->cfg.compress_ratio;
+  pa.Hkv = p->num_kv_heads;
+  pa.D = p->head_dim;
+  pa.PHD = p->pool_head_dim;
+  pa.num_flat_pages = p->num_flat_pages;
+  pa.max_pages = p->max_pages_per_seq;
+  pa.theta = (double)p->cfg.rope_theta;
+  pa.eps = (double)p->cfg.rms_eps;
+  pa.dt = dt;
+  if (qsa::launch_idx_dec_prep(pa, s) != hipSuccess) return QSA_ERR_LAUNCH;
+
+  qsa::IdxDecScoreArgs sa;
+  sa.qhat = pa.qhat;
+  sa.pool = pa.pool;
+  sa.pt = p->page_table;
+  sa.ctx = p->context_lengths;
+  sa.scores = reinterpret_cast<float *>(ws + w.scores);
+  sa.B = p->batch;
+  sa.Hi = p->cfg.num_heads;
+  sa.Hkv = p->num_kv_heads;
+  sa.D = p->head_dim;
+  sa.PHD = p->pool_head_dim;
+  sa.num_flat_pages = p->num_flat_pages;
+  sa.max_pages = p->max_pages_per_seq;
+  sa.ratio = p->cfg.compress_ratio;
+  sa.stride = w.stride;
+  sa.waves_per_seq = (gmax + 16 * qsa::kScoreTilesPerWave - 1) / (16 * qsa::kScoreTilesPerWave);
+  if (qsa::launch_idx_dec_score(sa, dt, s) != hipSuccess) return QSA_ERR_LAUNCH;
+
+  qsa::IdxSelectArgs xa;
+  xa.scores = sa.scores;
+  xa.row_stride = w.stride;
+  xa.out = p->indices;
+  xa.ctx = p->context_lengths;
+  xa.B = p->batch;
+  xa.S = 1;
+  xa.top_k = p->top_k;
+  xa.budget = p->cfg.budget;
+  xa.ratio = p->cfg.compress_ratio;
+  xa.decode = 1;
+  xa.max_ctx = p->max_pages_per_seq * QSA_PAGE_TOKENS;
+  return launched(qsa::launch_idx_select(xa, gmax, s));
+}
+
+}  // extern "C"

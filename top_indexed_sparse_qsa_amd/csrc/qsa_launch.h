@@ -1,0 +1,92 @@
+// Kernel argument blocks and host-side launchers (internal to libqsa).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct PrefillAttnArgs {
+  const uint16_t *q, *k, *v;
+  uint16_t *o;
+  const int32_t *indices, *ctx;
+  int B, S, Hq, Hkv, G, top_k;
+  float sl2;  // attention scale * log2(e)
+};
+
+struct DecodeAttnArgs {
+  const uint16_t *q;
+  uint16_t *o;
+  const uint16_t *pool;
+  const int32_t *pt, *indices, *ctx;
+  float *part_o, *part_stats;
+  int32_t *counters;
+  int B, Hq, Hkv, G, PHD, num_flat_pages, max_pages, top_k;
+  int nsplits, split_slots;  // split s covers list slots [s*split_slots, (s+1)*split_slots)
+  float sl2;
+};
+
+// Indexer: query prep + block pooling for prefill.
+struct IdxPrepArgs {
+  const uint16_t *idx_q, *idx_k;
+  const float *wq, *wk;
+  const int32_t *ctx;
+  float *qhat;      // [B,S,Hi,hd]
+  uint16_t *kbar;   // [B,Gmax,hd]
+  int B, S, Hi, hd, rot, ratio, Gmax;
+  double theta, eps;
+  int dt;
+};
+
+struct IdxScoreArgs {
+  const float *qhat;
+  const uint16_t *kbar;
+  float *scores;    // [B,S,stride]
+  const int32_t *ctx;
+  int B, S, Hi, Gmax, stride, ratio;
+};
+
+struct IdxSelectArgs {
+  const float *scores;
+  long long row_stride;
+  int32_t *out;
+  const int32_t *ctx;
+  int B, S;            // prefill: rows B*S; decode: rows B (S unused)
+  int top_k, budget, ratio;
+  int decode;          // 1: row of sequence b is position ctx[b]-1
+  int max_ctx;         // decode: clamp of ctx (max_pages * 128)
+};
+
+struct IdxDecPrepArgs {
+  const uint16_t *idx_q, *idx_k;
+  const float *wq, *wk;
+  uint16_t *pool;
+  const int32_t *pt, *ctx;
+  float *qhat;         // [B,Hi,hd]
+  int B, Hi, hd, rot, ratio, Hkv, D, PHD, num_flat_pages, max_pages;
+  double theta, eps;
+  int dt;
+};
+
+struct IdxDecScoreArgs {
+  const float *qhat;
+  const uint16_t *pool;
+  const int32_t *pt, *ctx;
+  float *scores;       // [B,stride]
+  int B, Hi, Hkv, D, PHD, num_flat_pages, max_pages, ratio, stride;
+  int waves_per_seq;
+};
+
+constexpr int kScoreTilesPerWave = 4;  // decode scoring: 4 tiles of 16 blocks per wave
+constexpr float kLog2e = 1.4426950408889634f;
+
+hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStream_t s);
+hipError_t launch_sparse_decode(const DecodeAttnArgs &a, int D, int dt, hipStream_t s);
+hipError_t launch_idx_prep(const IdxPrepArgs &a, hipStream_t s);
+hipError_t launch_idx_score(const IdxScoreArgs &a, int dt, hipStream_t s);
+hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s);
+hipError_t launch_idx_dec_prep(const IdxDecPrepArgs &a, hipStream_t s);
+hipError_t launch_idx_dec_score(const IdxDecScoreArgs &a, int dt, hipStream_t s);
+
+}  // namespace qsa
