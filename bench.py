@@ -130,7 +130,6 @@ def decode_bench(args, Q, syn, torch):
                      device="cuda")
     po = torch.empty(Q.qsa_sparse_decode_partial_o_elems(inp.B, inp.Hkv, inp.D), dtype=torch.float32, device="cuda")
     ps = torch.empty(Q.qsa_sparse_decode_partial_stats_elems(inp.B, inp.Hkv), dtype=torch.float32, device="cuda")
-    cnt = torch.zeros(Q.qsa_sparse_decode_counter_elems(inp.B, inp.Hkv), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -139,7 +138,7 @@ def decode_bench(args, Q, syn, torch):
         Q.qsa_indexer_decode(iq, ik, wq, wk, pool, pt, ctx, lists, ws, cfg, inp.D, stream=stream)
         if ev:
             ev[1].record(stream)
-        Q.qsa_sparse_decode(q, o, pool, pt, lists, ctx, po, ps, cnt, inp.scale, head_dim=inp.D, stream=stream)
+        Q.qsa_sparse_decode(q, o, pool, pt, lists, ctx, po, ps, inp.scale, head_dim=inp.D, stream=stream)
         if ev:
             ev[2].record(stream)
 

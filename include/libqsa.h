@@ -50,7 +50,7 @@ extern "C" {
 #endif
 
 #define QSA_PAGE_TOKENS 128   /* tokens per KV page [Runner: QsaSparseDecodeParams] */
-#define QSA_PARTIAL_ROWS 16   /* rows per split partial (the MFMA M tile) */
+#define QSA_PARTIAL_ROWS 16   /* rows per partial (the MFMA M tile) */
 #define QSA_MAX_SPLITS 16     /* largest decode split count this library plans */
 #define QSA_MAX_BLOCKS 32768  /* largest complete-block count one row may see */
 
@@ -118,14 +118,17 @@ typedef struct {
  * row 1 V page ids already offset by num_flat_pages / 2.
  * indices: int32 [batch, 1, top_k] as for prefill.
  * context_lengths: int32 [batch], the TOTAL length including the new token.
- * partial_o: fp32, qsa_sparse_decode_partial_o_elems() elements;
- * partial_stats: fp32, qsa_sparse_decode_partial_stats_elems() elements;
- * split_counters: int32, qsa_sparse_decode_counter_elems() elements, all
- * ZERO before the first call on a buffer; every call leaves them zero.
- * num_splits: 0 lets the library choose; otherwise 1..QSA_MAX_SPLITS.
- * The result does not depend on which split finishes last: partials are
- * merged in split order.  Concurrent calls must not share split_counters.
- * Supported: as prefill, plus pool_head_dim >= head_dim. */
+ * The list is cut into num_splits contiguous runs of 32-slot chunks (0 lets
+ * the library choose; otherwise 1..QSA_MAX_SPLITS), each run one online
+ * softmax.  Splits are merged in split order -- up to four inside a
+ * workgroup through LDS, the rest by a second small kernel -- so the result
+ * never depends on timing.  partial_o (fp32,
+ * qsa_sparse_decode_partial_o_elems()) and partial_stats (fp32,
+ * qsa_sparse_decode_partial_stats_elems()) hold the workgroup partials
+ * between the two kernels; they need no initial contents, and calls that
+ * overlap on the GPU must not share them.
+ * Supported: as prefill, plus pool_head_dim >= head_dim, a multiple of 8,
+ * and max_pages_per_seq <= 4096. */
 typedef struct {
   const void *q;
   void *o;
@@ -135,7 +138,6 @@ typedef struct {
   const int32_t *context_lengths;
   float *partial_o;
   float *partial_stats;
-  int32_t *split_counters;
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -239,7 +241,6 @@ size_t qsa_indexer_decode_workspace_bytes(const qsa_indexer_config *cfg, int32_t
                                           int32_t max_pages_per_seq);
 size_t qsa_sparse_decode_partial_o_elems(int32_t batch, int32_t num_kv_heads, int32_t head_dim);
 size_t qsa_sparse_decode_partial_stats_elems(int32_t batch, int32_t num_kv_heads);
-size_t qsa_sparse_decode_counter_elems(int32_t batch, int32_t num_kv_heads);
 
 /* Split count qsa_sparse_decode uses for these arguments (num_splits = 0). */
 int32_t qsa_sparse_decode_default_splits(int32_t batch, int32_t num_kv_heads, int32_t top_k);

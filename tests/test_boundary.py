@@ -56,9 +56,9 @@ def test_workspace_sizes_follow_layout():
     assert Q.qsa_indexer_prefill_workspace_bytes(cfg, B, S) == \
         a(B * S * 4 * 128 * 4) + a(B * g * 128 * 2) + a(B * S * st * 4)
     assert Q.qsa_indexer_decode_workspace_bytes(cfg, 32, 512) == a(32 * 4 * 128 * 4) + a(32 * 16384 * 4)
-    assert Q.qsa_sparse_decode_partial_o_elems(32, 4, 128) == 32 * 4 * 16 * 16 * 128
-    assert Q.qsa_sparse_decode_partial_stats_elems(32, 4) == 32 * 4 * 16 * 2 * 16
-    assert Q.qsa_sparse_decode_counter_elems(32, 4) == 128
+    # workgroup partials: at most QSA_MAX_SPLITS / 4 per (sequence, KV head)
+    assert Q.qsa_sparse_decode_partial_o_elems(32, 4, 128) == 32 * 4 * 4 * 16 * 128
+    assert Q.qsa_sparse_decode_partial_stats_elems(32, 4) == 32 * 4 * 4 * 2 * 16
     assert Q.qsa_indexer_prefill_workspace_bytes(Q.indexer_config(head_dim=64), 1, 10) == 0
     assert Q.qsa_sparse_decode_partial_o_elems(0, 4, 128) == 0
 
@@ -85,7 +85,7 @@ def _prefill(**kw):
 
 
 def _decode(**kw):
-    p = L.SparseDecodeParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    p = L.SparseDecodeParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                              2, 32, 4, 128, 256, 16, 8, 2051, 0, 0.088, 0, None)
     for k, v in kw.items():
         setattr(p, k, v)
@@ -120,7 +120,7 @@ def test_sparse_prefill_rejects(no_gpu, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(split_counters=None), NULLP), (dict(page_table=None), NULLP), (dict(partial_stats=None), NULLP),
+    (dict(partial_o=None), NULLP), (dict(page_table=None), NULLP), (dict(partial_stats=None), NULLP),
     (dict(dtype=-1), UNSUP), (dict(batch=0), SHAPE), (dict(num_flat_pages=0), SHAPE),
     (dict(pool_head_dim=120), SHAPE), (dict(pool_head_dim=130), SHAPE), (dict(num_splits=17), SHAPE),
     (dict(num_splits=-1), SHAPE), (dict(max_pages_per_seq=5000), UNSUP), (dict(num_q_heads=33), SHAPE),

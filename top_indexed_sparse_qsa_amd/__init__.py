@@ -24,7 +24,6 @@ from ._lib import (  # noqa: F401
     qsa_indexer_prefill,
     qsa_indexer_prefill_workspace_bytes,
     qsa_sparse_decode,
-    qsa_sparse_decode_counter_elems,
     qsa_sparse_decode_default_splits,
     qsa_sparse_decode_partial_o_elems,
     qsa_sparse_decode_partial_stats_elems,

@@ -26,7 +26,7 @@ EXPORTS = [
     "qsa_indexer_prefill", "qsa_sparse_prefill", "qsa_indexer_decode", "qsa_sparse_decode",
     "qsa_indexer_prefill_workspace_bytes", "qsa_indexer_decode_workspace_bytes",
     "qsa_sparse_decode_partial_o_elems", "qsa_sparse_decode_partial_stats_elems",
-    "qsa_sparse_decode_counter_elems", "qsa_sparse_decode_default_splits", "qsa_status_string",
+    "qsa_sparse_decode_default_splits", "qsa_status_string",
 ]
 
 _vp = ctypes.c_void_p
@@ -49,7 +49,7 @@ class SparsePrefillParams(ctypes.Structure):
 
 class SparseDecodeParams(ctypes.Structure):
     _fields_ = [("q", _vp), ("o", _vp), ("kv_pool", _vp), ("page_table", _vp), ("indices", _vp),
-                ("context_lengths", _vp), ("partial_o", _vp), ("partial_stats", _vp), ("split_counters", _vp),
+                ("context_lengths", _vp), ("partial_o", _vp), ("partial_stats", _vp),
                 ("batch", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
                 ("pool_head_dim", _i32), ("num_flat_pages", _i32), ("max_pages_per_seq", _i32),
                 ("top_k", _i32), ("num_splits", _i32), ("attention_scale", _f32), ("dtype", ctypes.c_int),
@@ -103,8 +103,6 @@ def load() -> ctypes.CDLL:
     lib.qsa_sparse_decode_partial_o_elems.restype = _sz
     lib.qsa_sparse_decode_partial_stats_elems.argtypes = [_i32, _i32]
     lib.qsa_sparse_decode_partial_stats_elems.restype = _sz
-    lib.qsa_sparse_decode_counter_elems.argtypes = [_i32, _i32]
-    lib.qsa_sparse_decode_counter_elems.restype = _sz
     lib.qsa_sparse_decode_default_splits.argtypes = [_i32, _i32, _i32]
     lib.qsa_sparse_decode_default_splits.restype = _i32
     lib.qsa_status_string.argtypes = [ctypes.c_int]
@@ -166,10 +164,6 @@ def qsa_sparse_decode_partial_stats_elems(batch: int, num_kv_heads: int) -> int:
     return int(load().qsa_sparse_decode_partial_stats_elems(batch, num_kv_heads))
 
 
-def qsa_sparse_decode_counter_elems(batch: int, num_kv_heads: int) -> int:
-    return int(load().qsa_sparse_decode_counter_elems(batch, num_kv_heads))
-
-
 def qsa_sparse_decode_default_splits(batch: int, num_kv_heads: int, top_k: int) -> int:
     return int(load().qsa_sparse_decode_default_splits(batch, num_kv_heads, top_k))
 
@@ -187,13 +181,13 @@ def qsa_sparse_prefill(q, k, v, o, indices, context_lengths, attention_scale: fl
 
 
 def qsa_sparse_decode(q, o, kv_pool, page_table, indices, context_lengths, partial_o, partial_stats,
-                      split_counters, attention_scale: float, head_dim: int | None = None,
-                      num_splits: int = 0, stream=None) -> None:
+                      attention_scale: float, head_dim: int | None = None, num_splits: int = 0,
+                      stream=None) -> None:
     """q, o [B,1,Hq,D]; kv_pool [2*numPages,128,Hkv,poolHeadDim]; page_table int32 [B,2,maxPages]."""
     B, _, Hq, D = q.shape
     D = head_dim or D
     p = SparseDecodeParams(_ptr(q), _ptr(o), _ptr(kv_pool), _ptr(page_table), _ptr(indices),
-                           _ptr(context_lengths), _ptr(partial_o), _ptr(partial_stats), _ptr(split_counters),
+                           _ptr(context_lengths), _ptr(partial_o), _ptr(partial_stats),
                            B, Hq, kv_pool.shape[2], D, kv_pool.shape[3], kv_pool.shape[0],
                            page_table.shape[-1], indices.shape[-1], num_splits, float(attention_scale),
                            _dtype_code(q), _stream(stream))

@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
-#include "../../include/libqsa.h"
+#include "libqsa.h"
 #include "qsa_launch.h"
 
 namespace {
@@ -113,17 +113,12 @@ size_t qsa_indexer_decode_workspace_bytes(const qsa_indexer_config *cfg, int32_t
 
 size_t qsa_sparse_decode_partial_o_elems(int32_t batch, int32_t hkv, int32_t d) {
   if (batch < 1 || hkv < 1 || d < 1) return 0;
-  return (size_t)batch * hkv * QSA_MAX_SPLITS * QSA_PARTIAL_ROWS * d;
+  return (size_t)batch * hkv * qsa::kDecMaxGroups * QSA_PARTIAL_ROWS * d;
 }
 
 size_t qsa_sparse_decode_partial_stats_elems(int32_t batch, int32_t hkv) {
   if (batch < 1 || hkv < 1) return 0;
-  return (size_t)batch * hkv * QSA_MAX_SPLITS * 2 * QSA_PARTIAL_ROWS;
-}
-
-size_t qsa_sparse_decode_counter_elems(int32_t batch, int32_t hkv) {
-  if (batch < 1 || hkv < 1) return 0;
-  return (size_t)batch * hkv;
+  return (size_t)batch * hkv * qsa::kDecMaxGroups * 2 * QSA_PARTIAL_ROWS;
 }
 
 int32_t qsa_sparse_decode_default_splits(int32_t batch, int32_t hkv, int32_t top_k) {
@@ -158,7 +153,7 @@ qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p) {
 
 qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
   if (!p || !p->q || !p->o || !p->kv_pool || !p->page_table || !p->indices || !p->context_lengths ||
-      !p->partial_o || !p->partial_stats || !p->split_counters)
+      !p->partial_o || !p->partial_stats)
     return QSA_ERR_NULL_POINTER;
   if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
   if (p->batch < 1 || p->top_k < 1 || p->num_flat_pages < 1 || p->max_pages_per_seq < 1) return QSA_ERR_BAD_SHAPE;
@@ -173,6 +168,8 @@ qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
   const int chunks = (p->top_k + 31) / 32;
   const int per = (chunks + splits - 1) / splits;
   splits = (chunks + per - 1) / per;  // drop splits that would get no slots
+  const int wpg = splits < 4 ? splits : 4;
+  const int ngroups = (splits + wpg - 1) / wpg;
   qsa::DecodeAttnArgs a;
   a.q = static_cast<const uint16_t *>(p->q);
   a.o = static_cast<uint16_t *>(p->o);
@@ -182,7 +179,6 @@ qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
   a.ctx = p->context_lengths;
   a.part_o = p->partial_o;
   a.part_stats = p->partial_stats;
-  a.counters = p->split_counters;
   a.B = p->batch;
   a.Hq = p->num_q_heads;
   a.Hkv = p->num_kv_heads;
@@ -193,6 +189,8 @@ qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
   a.top_k = p->top_k;
   a.nsplits = splits;
   a.split_slots = per * 32;
+  a.wpg = wpg;
+  a.ngroups = ngroups;
   a.sl2 = p->attention_scale * qsa::kLog2e;
   return launched(qsa::launch_sparse_decode(a, p->head_dim, (int)p->dtype, (hipStream_t)p->stream));
 }

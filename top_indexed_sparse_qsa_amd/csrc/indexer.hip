@@ -184,25 +184,34 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t score_key(float s) { return __float_as_uint(s) & 0x7fffffffu; }
 
-// Exclusive prefix count of `flag` over the 256 threads in thread order;
+// Exclusive prefix count of `flag` over the NT threads in thread order;
 // returns this thread's prefix and sets *total.
+template <int NT>
 __device__ __forceinline__ int block_scan_flag(bool flag, int *s_wave, int *total) {
+  constexpr int NW = NT / 64;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const unsigned long long m = __ballot(flag);
   const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
   __syncthreads();
   if (lane == 0) s_wave[wv] = __popcll(m);
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wv; ++w) before += s_wave[w];
-  *total = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = s_wave[w];
+    before += w < wv ? c : 0;
+    tot += c;
+  }
+  *total = tot;
   return before + in_wave;
 }
 
-__global__ __launch_bounds__(256) void idx_select_kernel(IdxSelectArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void idx_select_kernel(IdxSelectArgs a) {
+  constexpr int NW = NT / 64;
   extern __shared__ uint32_t s_key[];
   __shared__ uint32_t hist[256];
-  __shared__ int s_wave[4];
+  __shared__ int s_wave[NW > 4 ? NW : 4];
   __shared__ uint32_t s_digit, s_above;
   const int tid = threadIdx.x, lane = lane_id();
 
@@ -226,25 +235,49 @@ __global__ __launch_bounds__(256) void idx_select_kernel(IdxSelectArgs a) {
     srow = a.scores + ((size_t)b * a.S + t) * a.row_stride;
   }
   if (!live) {
-    for (int i = tid; i < a.top_k; i += 256) out[i] = -1;
+    for (int i = tid; i < a.top_k; i += NT) out[i] = -1;
     return;
   }
   const int r = a.ratio;
   const int nc = (t + 1) / r;
   if (nc <= a.budget) {  // every complete block is kept: the list is 0..t
-    for (int i = tid; i < a.top_k; i += 256) out[i] = i <= t ? i : -1;
+    for (int i = tid; i < a.top_k; i += NT) out[i] = i <= t ? i : -1;
     return;
   }
 
-  for (int i = tid; i < nc; i += 256) s_key[i] = score_key(srow[i]);
+  // Stage the row's keys in LDS.  Rows start 64-byte aligned; four float4
+  // loads per thread are in flight before the first LDS store.
+  {
+    const int n4 = nc >> 2;
+    const f32x4 *src4 = reinterpret_cast<const f32x4 *>(srow);
+    for (int base = 0; base < n4; base += 4 * NT) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i4 = base + u * NT + tid;
+        if (i4 < n4) v[u] = src4[i4];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i4 = base + u * NT + tid;
+        if (i4 < n4) {
+          s_key[4 * i4] = score_key(v[u][0]);
+          s_key[4 * i4 + 1] = score_key(v[u][1]);
+          s_key[4 * i4 + 2] = score_key(v[u][2]);
+          s_key[4 * i4 + 3] = score_key(v[u][3]);
+        }
+      }
+    }
+    for (int i = 4 * n4 + tid; i < nc; i += NT) s_key[i] = score_key(srow[i]);
+  }
   uint32_t prefix = 0, pmask = 0;
   uint32_t remaining = (uint32_t)a.budget;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    const int iters = (nc + 255) >> 8;
+    const int iters = (nc + NT - 1) / NT;
     for (int it = 0; it < iters; ++it) {
-      const int i = it * 256 + tid;
+      const int i = it * NT + tid;
       bool act = false;
       uint32_t dig = 0;
       if (i < nc) {
@@ -265,23 +298,25 @@ __global__ __launch_bounds__(256) void idx_select_kernel(IdxSelectArgs a) {
       if (act) atomicAdd(&hist[dig], 1u);
     }
     __syncthreads();
-    // Suffix counts over digits 255..0: thread j holds digit 255 - j.
-    const uint32_t c = hist[255 - tid];
+    // Suffix counts over digits 255..0: thread j < 256 holds digit 255 - j.
+    const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
     uint32_t incl = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t v = (uint32_t)__shfl_up((int)incl, o, 64);
       if (lane >= o) incl += v;
     }
-    if (lane == 63) s_wave[tid >> 6] = (int)incl;
+    if (tid < 256 && lane == 63) s_wave[tid >> 6] = (int)incl;
     __syncthreads();
-    uint32_t before = 0;
-    for (int w = 0; w < (tid >> 6); ++w) before += (uint32_t)s_wave[w];
-    incl += before;
-    const uint32_t excl = incl - c;
-    if (excl < remaining && incl >= remaining) {  // exactly one thread
-      s_digit = 255u - (uint32_t)tid;
-      s_above = excl;
+    if (tid < 256) {
+      uint32_t before = 0;
+      for (int w = 0; w < (tid >> 6); ++w) before += (uint32_t)s_wave[w];
+      incl += before;
+      const uint32_t excl = incl - c;
+      if (excl < remaining && incl >= remaining) {  // exactly one thread
+        s_digit = 255u - (uint32_t)tid;
+        s_above = excl;
+      }
     }
     __syncthreads();
     prefix |= s_digit << shift;
@@ -292,16 +327,16 @@ __global__ __launch_bounds__(256) void idx_select_kernel(IdxSelectArgs a) {
   const uint32_t T = prefix;
   const int need_eq = (int)remaining;          // keys equal to T still to take
   int eq_base = 0, sel_base = 0;
-  for (int base = 0; base < nc; base += 256) {
+  for (int base = 0; base < nc; base += NT) {
     const int g = base + tid;
     const uint32_t k = g < nc ? s_key[g] : 0u;
     const bool gt = g < nc && k > T;
     const bool eq = g < nc && k == T;
     int eq_tot;
-    const int eq_rank = eq_base + block_scan_flag(eq, s_wave, &eq_tot);
+    const int eq_rank = eq_base + block_scan_flag<NT>(eq, s_wave, &eq_tot);
     const bool sel = gt || (eq && eq_rank < need_eq);
     int sel_tot;
-    const int pos = sel_base + block_scan_flag(sel, s_wave, &sel_tot);
+    const int pos = sel_base + block_scan_flag<NT>(sel, s_wave, &sel_tot);
     if (sel)
       for (int j = 0; j < r; ++j) out[(size_t)r * pos + j] = r * g + j;
     eq_base += eq_tot;
@@ -309,7 +344,7 @@ __global__ __launch_bounds__(256) void idx_select_kernel(IdxSelectArgs a) {
   }
   const int head = r * a.budget;
   const int len = head + (t + 1) - r * nc;
-  for (int i = head + tid; i < a.top_k; i += 256) out[i] = i < len ? r * nc + (i - head) : -1;
+  for (int i = head + tid; i < a.top_k; i += NT) out[i] = i < len ? r * nc + (i - head) : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -446,7 +481,9 @@ hipError_t launch_idx_score(const IdxScoreArgs &a, int dt, hipStream_t s) {
 hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) {
   const unsigned rows = (unsigned)(a.decode ? a.B : (long long)a.B * a.S);
   const size_t lds = (size_t)(nc_max > 0 ? nc_max : 1) * sizeof(uint32_t);
-  hipLaunchKernelGGL(idx_select_kernel, dim3(rows), dim3(256), lds, s, a);
+  // Decode has one long row per sequence: a wide workgroup per row.
+  if (a.decode) hipLaunchKernelGGL(idx_select_kernel<1024>, dim3(rows), dim3(1024), lds, s, a);
+  else hipLaunchKernelGGL(idx_select_kernel<256>, dim3(rows), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

@@ -20,12 +20,14 @@ struct DecodeAttnArgs {
   uint16_t *o;
   const uint16_t *pool;
   const int32_t *pt, *indices, *ctx;
-  float *part_o, *part_stats;
-  int32_t *counters;
+  float *part_o, *part_stats;  // [pairs * kDecMaxGroups][16][D], [..][2][16]
   int B, Hq, Hkv, G, PHD, num_flat_pages, max_pages, top_k;
   int nsplits, split_slots;  // split s covers list slots [s*split_slots, (s+1)*split_slots)
+  int wpg, ngroups;          // splits (waves) per workgroup, workgroups per (sequence, KV head)
   float sl2;
 };
+
+constexpr int kDecMaxGroups = 4;  // QSA_MAX_SPLITS / waves per workgroup
 
 // Indexer: query prep + block pooling for prefill.
 struct IdxPrepArgs {

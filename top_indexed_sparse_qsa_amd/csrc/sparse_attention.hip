@@ -228,25 +228,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// One wave per (sequence, KV head, split).  Each split stores its unnormalised
-// accumulator and (max, sum) per head row; the last split to arrive (counter
-// after a release fence) merges all splits in split order, so the result does
-// not depend on arrival order, then resets the counter to zero.
+// Decode: one wave per (sequence, KV head, split); the waves of a workgroup
+// (up to four) take consecutive splits of the same (sequence, KV head),
+// share its page-table row in LDS, and merge their partial softmax states in
+// LDS in split order.  When a (sequence, KV head) needs more splits than one
+// workgroup holds, each workgroup stores its merged partial (unnormalised O,
+// running max, running sum) and a second small kernel merges the workgroup
+// partials, again in a fixed order.  The order never depends on timing, so
+// results are deterministic.  No cross-workgroup flags are used: on this
+// part each XCD has its own L2, and a kernel boundary is the cheap place to
+// make one workgroup's stores visible to another.
+constexpr int kDecWaves = 4;  // waves (splits) per workgroup
+
+template <int D>
+struct DecMergeLds {
+  static constexpr int RS = D + 4;  // padded row stride (floats)
+  float acc[kDecWaves][16 * RS];
+  float m[kDecWaves][16];
+  float l[kDecWaves][16];
+};
+
+// Lane (q, r) of wave w merges row r, dims [d0, d0 + D/16).
 template <int D, int DT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_decode_kernel(DecodeAttnArgs a) {
-  extern __shared__ int32_t s_pt[];  // [2][max_pages]
-  const int item = blockIdx.x;
-  const int split = item % a.nsplits;
-  const int rest = item / a.nsplits;
-  const int kvh = rest % a.Hkv;
-  const int b = rest / a.Hkv;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_decode_kernel(DecodeAttnArgs a) {
+  extern __shared__ __align__(16) unsigned char s_raw[];
+  DecMergeLds<D> &mg = *reinterpret_cast<DecMergeLds<D> *>(s_raw);
+  int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + sizeof(DecMergeLds<D>));  // [2][max_pages]
+  const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int group = blockIdx.x % a.ngroups;
+  const int pair = blockIdx.x / a.ngroups;
+  const int b = pair / a.Hkv, kvh = pair % a.Hkv;
+  const int split = group * a.wpg + wv;
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int ctx = min(max(a.ctx[b], 0), a.max_pages * 128);
   const int npages = (ctx + 127) >> 7;
   const int32_t *ptb = a.pt + (size_t)b * 2 * a.max_pages;
-  for (int i = lane; i < npages; i += 64) {
-    s_pt[i] = ptb[i];
-    s_pt[a.max_pages + i] = ptb[a.max_pages + i];
+  for (int i = threadIdx.x; i < 2 * npages; i += blockDim.x) {
+    const int row = i >= npages, j = i - row * npages;
+    s_pt[row * a.max_pages + j] = ptb[row * a.max_pages + j];
   }
   __syncthreads();
 
@@ -255,7 +274,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const int s0 = split * a.split_slots;
-  const int n_slots = min(a.top_k - s0, a.split_slots);
+  const int n_slots = split < a.nsplits ? min(a.top_k - s0, a.split_slots) : 0;
   if (ctx > 0 && n_slots > 0) {
     u32x4 qf[D / 32];
     load_q<D>(qf, a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
@@ -270,64 +289,103 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
   float l = l_run + shfl_xor_f(l_run, 16);
   l += shfl_xor_f(l, 32);
-
-  const int pair = b * a.Hkv + kvh;
-  const size_t slot0 = (size_t)pair * 16;  // QSA_MAX_SPLITS slots per pair
-  float *po = a.part_o + (slot0 + split) * 16 * D;
-  float *ps = a.part_stats + (slot0 + split) * 32;
   if (32 * q4 < D) {
+    float *dst = &mg.acc[wv][r16 * DecMergeLds<D>::RS + 32 * q4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      float *dst = po + (size_t)r16 * D + 32 * q4 + 8 * rr;
-      *reinterpret_cast<f32x4 *>(dst) = f32x4{acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]};
-      *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{acc[4][rr], acc[5][rr], acc[6][rr], acc[7][rr]};
+      *reinterpret_cast<f32x4 *>(dst + 8 * rr) = f32x4{acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]};
+      *reinterpret_cast<f32x4 *>(dst + 8 * rr + 4) = f32x4{acc[4][rr], acc[5][rr], acc[6][rr], acc[7][rr]};
     }
   }
   if (q4 == 0) {
-    ps[r16] = m_run;
-    ps[16 + r16] = l;
+    mg.m[wv][r16] = m_run;
+    mg.l[wv][r16] = l;
   }
-  __threadfence();
-  int last = 0;
-  if (lane == 0) last = (atomicAdd(&a.counters[pair], 1) == a.nsplits - 1);
-  last = __shfl(last, 0, 64);
-  if (!last) return;
-  __threadfence();
+  __syncthreads();
 
-  if (r16 < a.G && 32 * q4 < D) {
-    const float *pso = a.part_stats + slot0 * 32;
-    float M = -INFINITY;
-    for (int s = 0; s < a.nsplits; ++s) M = fmaxf(M, pso[s * 32 + r16]);
-    float L = 0.f;
-    float o[32];
+  // Merge the workgroup's splits in split order.  The head dims form 16
+  // slices of D/16; lane (q, r) of wave w takes row r and slices w*4+q,
+  // w*4+q + 4*nw, ...
+  constexpr int ND = D / 16;
+  float M = -INFINITY;
+  for (int w = 0; w < nw; ++w) M = fmaxf(M, mg.m[w][r16]);
+  float L = 0.f, sc[kDecWaves];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) o[j] = 0.f;
-    for (int s = 0; s < a.nsplits; ++s) {
-      const float ms = pso[s * 32 + r16];
-      const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      L += pso[s * 32 + 16 + r16] * w;
-      const float *src = a.part_o + ((slot0 + s) * 16 + r16) * D + 32 * q4;
+  for (int w = 0; w < kDecWaves; ++w) {
+    const float mw = w < nw ? mg.m[w][r16] : -INFINITY;
+    sc[w] = mw == -INFINITY ? 0.f : exp2f(mw - M);
+    L += w < nw ? mg.l[w][r16] * sc[w] : 0.f;
+  }
+  if (r16 >= a.G) return;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const size_t slot = (size_t)pair * kDecMaxGroups + group;
+  for (int sl = wv * 4 + q4; sl < 16; sl += 4 * nw) {
+    const int d0 = sl * ND;
+    float o[ND];
 #pragma unroll
-      for (int j = 0; j < 32; j += 4) {
-        f32x4 v = *reinterpret_cast<const f32x4 *>(src + j);
-        o[j] += v[0] * w;
-        o[j + 1] += v[1] * w;
-        o[j + 2] += v[2] * w;
-        o[j + 3] += v[3] * w;
-      }
+    for (int j = 0; j < ND; ++j) o[j] = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float *src = &mg.acc[w][r16 * DecMergeLds<D>::RS + d0];
+#pragma unroll
+      for (int j = 0; j < ND; ++j) o[j] += src[j] * sc[w];
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    uint16_t *dst = a.o + ((size_t)b * a.Hq + (size_t)kvh * a.G + r16) * D + 32 * q4;
+    if (a.ngroups == 1) {
+      uint16_t *out = a.o + ((size_t)b * a.Hq + (size_t)kvh * a.G + r16) * D + d0;
 #pragma unroll
-    for (int j = 0; j < 32; j += 8) {
-      u32x4 w;
+      for (int j = 0; j < ND; j += 2)
+        *reinterpret_cast<uint32_t *>(out + j) =
+            f32_to_bits<DT>(o[j] * inv) | (f32_to_bits<DT>(o[j + 1] * inv) << 16);
+    } else {
+      float *po = a.part_o + (slot * 16 + r16) * D + d0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        w[k] = f32_to_bits<DT>(o[j + 2 * k] * inv) | (f32_to_bits<DT>(o[j + 2 * k + 1] * inv) << 16);
-      st16(dst + j, w);
+      for (int j = 0; j < ND; j += 4) *reinterpret_cast<f32x4 *>(po + j) = f32x4{o[j], o[j + 1], o[j + 2], o[j + 3]};
     }
   }
-  if (lane == 0) __hip_atomic_store(&a.counters[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (a.ngroups > 1 && wv == 0 && q4 == 0) {
+    a.part_stats[slot * 32 + r16] = M;
+    a.part_stats[slot * 32 + 16 + r16] = L;
+  }
+}
+
+// Merges the workgroup partials of one (sequence, KV head) in group order.
+template <int D, int DT>
+__global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs a) {
+  const int pair = blockIdx.x;
+  const int b = pair / a.Hkv, kvh = pair % a.Hkv;
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
+  if (r16 >= a.G) return;
+  constexpr int NDL = D / 4;  // dims per lane
+  const int d0 = q4 * NDL;
+  const size_t slot0 = (size_t)pair * kDecMaxGroups;
+  float M = -INFINITY;
+  for (int g = 0; g < a.ngroups; ++g) M = fmaxf(M, a.part_stats[(slot0 + g) * 32 + r16]);
+  float L = 0.f, o[NDL];
+#pragma unroll
+  for (int j = 0; j < NDL; ++j) o[j] = 0.f;
+  for (int g = 0; g < a.ngroups; ++g) {
+    const float mg = a.part_stats[(slot0 + g) * 32 + r16];
+    const float sc = mg == -INFINITY ? 0.f : exp2f(mg - M);
+    L += a.part_stats[(slot0 + g) * 32 + 16 + r16] * sc;
+    const float *src = a.part_o + ((slot0 + g) * 16 + r16) * D + d0;
+#pragma unroll
+    for (int j = 0; j < NDL; j += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(src + j);
+      o[j] += v[0] * sc;
+      o[j + 1] += v[1] * sc;
+      o[j + 2] += v[2] * sc;
+      o[j + 3] += v[3] * sc;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t *out = a.o + ((size_t)b * a.Hq + (size_t)kvh * a.G + r16) * D + d0;
+#pragma unroll
+  for (int j = 0; j < NDL; j += 8) {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = f32_to_bits<DT>(o[j + 2 * k] * inv) | (f32_to_bits<DT>(o[j + 2 * k + 1] * inv) << 16);
+    st16(out + j, w);
+  }
 }
 
 template <int D, int DT>
@@ -345,9 +403,12 @@ hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStr
 
 template <int D, int DT>
 static hipError_t launch_decode_t(const DecodeAttnArgs &a, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.B * a.Hkv * a.nsplits);
-  const size_t lds = (size_t)2 * a.max_pages * sizeof(int32_t);
-  hipLaunchKernelGGL((sparse_decode_kernel<D, DT>), dim3(grid), dim3(64), lds, s, a);
+  const unsigned pairs = (unsigned)(a.B * a.Hkv);
+  const size_t lds = sizeof(DecMergeLds<D>) + (size_t)2 * a.max_pages * sizeof(int32_t);
+  hipLaunchKernelGGL((sparse_decode_kernel<D, DT>), dim3(pairs * a.ngroups), dim3(64 * a.wpg), lds, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ngroups == 1) return e;
+  hipLaunchKernelGGL((sparse_decode_merge_kernel<D, DT>), dim3(pairs), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
