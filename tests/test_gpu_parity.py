@@ -78,6 +78,9 @@ PREFILL_CASES = [
     dict(B=2, S=130, Hq=4, Hkv=4, D=64, dtype="bf16", top_k=40, ctx=[130, 1]),
     dict(B=1, S=100, Hq=12, Hkv=4, D=128, dtype="fp16", top_k=2051, ctx=[100]),
     dict(B=3, S=70, Hq=6, Hkv=2, D=64, dtype="fp16", top_k=33, ctx=[0, 70, 45]),
+    dict(B=2, S=90, Hq=12, Hkv=3, D=128, dtype="fp16", top_k=64, ctx=[90, 61]),
+    dict(B=1, S=50, Hq=16, Hkv=16, D=64, dtype="bf16", top_k=50, ctx=[50]),
+    dict(B=1, S=77, Hq=16, Hkv=8, D=128, dtype="bf16", top_k=70, ctx=[77]),
 ]
 
 

@@ -111,26 +111,55 @@ __device__ __forceinline__ void load8f(float (&x)[8], const float *p) {
   x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
 
-// Prefill scoring.  One wave per 4 consecutive rows: the MFMA M tile is
-// (row, head) with the head fastest, so each lane group ends with the four
-// head dots of one row and one block and sums their relus without any
-// cross-lane step.  Tiles of 16 blocks run up to the last row's complete
-// count; the kbar tile of the next step is fetched while this one computes.
+// Prefill scoring.  A workgroup takes 32 consecutive rows and one chunk of
+// kScoreChunk complete blocks; long row ranges are cut into several chunks
+// (chunks of the last rows are dispatched first).  The chunk's kbar rows are
+// staged once in LDS, 16-byte pieces XOR-swizzled by row so that MFMA
+// fragment reads are conflict-free; each wave then computes 8 rows against
+// the whole chunk.  The MFMA M tile is (row, head) with the head fastest, so
+// each 16-lane group ends with the four head dots of one row and one block
+// and sums their relus in-lane; a wave's two M tiles share every kbar
+// fragment.
 template <int DT>
 __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
   constexpr int NP = QSplit<DT>::NP;
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  const int T4 = (a.S + 3) >> 2;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= a.B * T4) return;
-  const int b = item % a.B;
-  const int t0 = 4 * (T4 - 1 - item / a.B);
+  __shared__ __align__(16) uint32_t s_kb[kScoreChunk * 64];  // kScoreChunk rows x 256 B
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15, wv = threadIdx.x >> 6;
+  const int T32 = (a.S + 31) >> 5;
+  const long long item = blockIdx.x;
+  const int b = (int)(item % a.B);
+  const long long rest = item / a.B;
+  const int ch = (int)(rest % a.nchunk);
+  const int tg = 32 * (T32 - 1 - (int)(rest / a.nchunk));
   const int live = min(a.ctx[b], a.S);
-  if (t0 >= live) return;
+  if (tg >= live) return;
+  const int nc_hi = (min(tg + 31, live - 1) + 1) / a.ratio;
+  const int g_lo = ch * kScoreChunk, g_hi = min(g_lo + kScoreChunk, nc_hi);
+  if (g_lo >= g_hi) return;
 
-  u32x4 qa[NP][4];
+  // stage kbar rows [g_lo, g_hi) (16 pieces of 16 B per row)
   {
-    const int t = t0 + (r16 >> 2), h = r16 & 3;
+    const uint16_t *src = a.kbar + ((size_t)b * a.Gmax + g_lo) * 128;
+    const int npiece = (g_hi - g_lo) * 16;
+    u32x4 v[kScoreChunk * 16 / 256];
+#pragma unroll
+    for (int u = 0; u < kScoreChunk * 16 / 256; ++u) {
+      const int i = threadIdx.x + 256 * u;
+      if (i < npiece) v[u] = ld16(src + 8 * i);
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreChunk * 16 / 256; ++u) {
+      const int i = threadIdx.x + 256 * u;
+      const int row = i >> 4, pc = i & 15;
+      if (i < npiece) *reinterpret_cast<u32x4 *>(&s_kb[row * 64 + 4 * (pc ^ (row & 15))]) = v[u];
+    }
+  }
+
+  const int t0 = tg + 8 * wv;
+  u32x4 qa[2][NP][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int t = t0 + 4 * m + (r16 >> 2), h = r16 & 3;
     const bool ok = t < live && h < a.Hi;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -142,58 +171,77 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
       u32x4 pieces[NP];
       split8<DT>(x, pieces);
 #pragma unroll
-      for (int p = 0; p < NP; ++p) qa[p][ks] = pieces[p];
+      for (int p = 0; p < NP; ++p) qa[m][p][ks] = pieces[p];
     }
   }
-  const int t_out = t0 + q4;
-  const int nc_out = t_out < live ? (t_out + 1) / a.ratio : 0;
-  const int nc_hi = (min(t0 + 3, live - 1) + 1) / a.ratio;
-  const uint16_t *kb0 = a.kbar + (size_t)b * a.Gmax * 128 + 8 * q4;
-  float *srow = a.scores + ((size_t)b * a.S + t_out) * a.stride;
-
-  auto load_tile = [&](int g0, u32x4 (&kb)[4]) {
-    const int g = min(g0 + r16, max(a.Gmax - 1, 0));
+  int nc_out[2];
+  float *srow[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kb[ks] = ld16(kb0 + (size_t)g * 128 + 32 * ks);
-  };
-  u32x4 cur[4], nxt[4];
-  if (nc_hi > 0) load_tile(0, cur);
-  for (int g0 = 0; g0 < nc_hi; g0 += 16) {
-    if (g0 + 16 < nc_hi) load_tile(g0 + 16, nxt);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < 2; ++m) {
+    const int t_out = t0 + 4 * m + q4;
+    nc_out[m] = t_out < live ? (t_out + 1) / a.ratio : 0;
+    srow[m] = a.scores + ((size_t)b * a.S + min(t_out, a.S - 1)) * a.stride;
+  }
+  __syncthreads();
+  const int nc_wave = t0 < live ? (min(t0 + 7, live - 1) + 1) / a.ratio : 0;
+  const int g_end = min(g_hi, nc_wave);
+  for (int g0 = g_lo; g0 < g_end; g0 += 16) {
+    const int lb = g0 - g_lo + r16;  // local kbar row; lb & 15 == r16
+    u32x4 kb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kb[ks] = *reinterpret_cast<const u32x4 *>(&s_kb[lb * 64 + 4 * ((4 * ks + q4) ^ r16)]);
+    // four independent accumulator chains (M tile x k-step parity), interleaved
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int p = 0; p < NP; ++p) acc = mfma16x16x32<DT>(qa[p][ks], cur[ks], acc);
-    const float s = fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) + fmaxf(acc[3], 0.f);
-    if (g0 + r16 < nc_out) srow[g0 + r16] = s;
+      for (int p = 0; p < NP; ++p)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) cur[ks] = nxt[ks];
+        for (int m = 0; m < 2; ++m) acc[m][ks & 1] = mfma16x16x32<DT>(qa[m][p][ks], kb[ks], acc[m][ks & 1]);
+    float sc[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const f32x4 d = acc[m][0] + acc[m][1];
+      sc[m] = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) + fmaxf(d[3], 0.f);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      if (g0 + r16 < nc_out[m]) srow[m][g0 + r16] = sc[m];
   }
 }
 
 // ---------------------------------------------------------------------------
-// Select + expand.  One workgroup (256 threads) per row.  Scores are
-// non-negative, so their fp32 bit patterns (sign cleared) order like the
-// values.  An MSB-first radix select (four 8-bit digits, LDS histograms with
-// wave-aggregated increments) finds the budget-th largest key T; the kept
-// set is every key > T plus the lowest-index keys == T until the budget is
-// met.  An ordered ballot scan then writes the kept blocks in ascending
-// order, each as ratio consecutive token ids, followed by the causal tail
-// and -1 padding.
+// Select + expand.  One workgroup per row (256 threads in prefill, 1024 for
+// the long decode rows).  Scores are non-negative, so their fp32 bit
+// patterns (sign cleared) order like the values.  An MSB-first radix select
+// over 8-bit digits (LDS histograms; each wave adds the count of its most
+// common digits with one increment) narrows the cut down to a bin: every key
+// above the bin is kept, and the lowest-index keys of the bin up to the
+// budget.  It stops as soon as the bin holds exactly the keys still needed.
+// Emission: thread j owns the contiguous key range [j*per, (j+1)*per) (per
+// odd, so LDS reads are conflict-free); two block-wide scans give each thread
+// the number of equal keys and of kept blocks before its range, and it writes
+// its kept blocks, in ascending order, as ratio consecutive token ids into an
+// LDS copy of the list that is then stored with the causal tail and -1
+// padding in one coalesced pass.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t score_key(float s) { return __float_as_uint(s) & 0x7fffffffu; }
 
-// Exclusive prefix count of `flag` over the NT threads in thread order;
-// returns this thread's prefix and sets *total.
+// Exclusive prefix sum of v over the NT threads in thread order; sets *total.
 template <int NT>
-__device__ __forceinline__ int block_scan_flag(bool flag, int *s_wave, int *total) {
+__device__ __forceinline__ int block_exscan(int v, int *s_wave, int *total) {
   constexpr int NW = NT / 64;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(flag);
-  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
   __syncthreads();
-  if (lane == 0) s_wave[wv] = __popcll(m);
+  if (lane == 63) s_wave[wv] = incl;
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
@@ -203,16 +251,16 @@ __device__ __forceinline__ int block_scan_flag(bool flag, int *s_wave, int *tota
     tot += c;
   }
   *total = tot;
-  return before + in_wave;
+  return before + incl - v;
 }
 
 template <int NT>
 __global__ __launch_bounds__(NT) void idx_select_kernel(IdxSelectArgs a) {
   constexpr int NW = NT / 64;
-  extern __shared__ uint32_t s_key[];
+  extern __shared__ uint32_t s_dyn[];      // keys [key_cap] | list [top_k]
   __shared__ uint32_t hist[256];
   __shared__ int s_wave[NW > 4 ? NW : 4];
-  __shared__ uint32_t s_digit, s_above;
+  __shared__ uint32_t s_digit, s_above, s_cnt;
   const int tid = threadIdx.x, lane = lane_id();
 
   int b, t, live;
@@ -244,8 +292,10 @@ __global__ __launch_bounds__(NT) void idx_select_kernel(IdxSelectArgs a) {
     for (int i = tid; i < a.top_k; i += NT) out[i] = i <= t ? i : -1;
     return;
   }
+  uint32_t *s_key = s_dyn;
+  int32_t *s_list = reinterpret_cast<int32_t *>(s_dyn + a.key_cap);
 
-  // Stage the row's keys in LDS.  Rows start 64-byte aligned; four float4
+  // Stage the row's keys in LDS: rows start 64-byte aligned; four float4
   // loads per thread are in flight before the first LDS store.
   {
     const int n4 = nc >> 2;
@@ -270,14 +320,13 @@ __global__ __launch_bounds__(NT) void idx_select_kernel(IdxSelectArgs a) {
     }
     for (int i = 4 * n4 + tid; i < nc; i += NT) s_key[i] = score_key(srow[i]);
   }
+
   uint32_t prefix = 0, pmask = 0;
   uint32_t remaining = (uint32_t)a.budget;
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    const int iters = (nc + NT - 1) / NT;
-    for (int it = 0; it < iters; ++it) {
-      const int i = it * NT + tid;
+    for (int i = tid; i < nc + NT - 1 - ((nc + NT - 1) % NT); i += NT) {
       bool act = false;
       uint32_t dig = 0;
       if (i < nc) {
@@ -285,7 +334,7 @@ __global__ __launch_bounds__(NT) void idx_select_kernel(IdxSelectArgs a) {
         act = (k & pmask) == prefix;
         dig = (k >> shift) & 255u;
       }
-      // Peel off the most common digit of the wave with one increment.
+      // Peel off the most common digits of the wave with one increment each.
       unsigned long long pend = __ballot(act);
       for (int rep = 0; rep < 4 && pend; ++rep) {
         const int leader = __ffsll((long long)pend) - 1;
@@ -316,35 +365,227 @@ __global__ __launch_bounds__(NT) void idx_select_kernel(IdxSelectArgs a) {
       if (excl < remaining && incl >= remaining) {  // exactly one thread
         s_digit = 255u - (uint32_t)tid;
         s_above = excl;
+        s_cnt = c;
       }
     }
     __syncthreads();
     prefix |= s_digit << shift;
     pmask |= 255u << shift;
     remaining -= s_above;
+    const bool resolved = s_cnt == remaining;  // the whole bin is kept
     __syncthreads();
+    if (resolved) break;
   }
-  const uint32_t T = prefix;
-  const int need_eq = (int)remaining;          // keys equal to T still to take
-  int eq_base = 0, sel_base = 0;
-  for (int base = 0; base < nc; base += NT) {
-    const int g = base + tid;
-    const uint32_t k = g < nc ? s_key[g] : 0u;
-    const bool gt = g < nc && k > T;
-    const bool eq = g < nc && k == T;
-    int eq_tot;
-    const int eq_rank = eq_base + block_scan_flag<NT>(eq, s_wave, &eq_tot);
-    const bool sel = gt || (eq && eq_rank < need_eq);
-    int sel_tot;
-    const int pos = sel_base + block_scan_flag<NT>(sel, s_wave, &sel_tot);
-    if (sel)
-      for (int j = 0; j < r; ++j) out[(size_t)r * pos + j] = r * g + j;
-    eq_base += eq_tot;
-    sel_base += sel_tot;
+
+  // Keys with (k & pmask) > prefix are kept; of those == prefix, the first
+  // `remaining` in index order.
+  const int per = ((nc + NT - 1) / NT) | 1;
+  const int lo = min(tid * per, nc), hi = min(lo + per, nc);
+  int n_gt = 0, n_eq = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t m = s_key[i] & pmask;
+    n_gt += m > prefix;
+    n_eq += m == prefix;
   }
+  int tot;
+  const int eq_before = block_exscan<NT>(n_eq, s_wave, &tot);
+  const int take_eq = min(n_eq, max(0, (int)remaining - eq_before));
+  const int sel_before = block_exscan<NT>(n_gt + take_eq, s_wave, &tot);
+  int pos = sel_before, eq_seen = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t m = s_key[i] & pmask;
+    bool keep = m > prefix;
+    if (m == prefix) {
+      keep = eq_seen < take_eq;
+      ++eq_seen;
+    }
+    if (keep) {
+      for (int j = 0; j < r; ++j) s_list[r * pos + j] = r * i + j;
+      ++pos;
+    }
+  }
+  __syncthreads();
   const int head = r * a.budget;
   const int len = head + (t + 1) - r * nc;
-  for (int i = head + tid; i < a.top_k; i += NT) out[i] = i < len ? r * nc + (i - head) : -1;
+  for (int i = tid; i < a.top_k; i += NT)
+    out[i] = i < head ? s_list[i] : (i < len ? r * nc + (i - head) : -1);
+}
+
+// ---------------------------------------------------------------------------
+// Select + expand, one wave per row (prefill rows with at most 64*KPL
+// complete blocks).  The row's keys live in registers: lane l holds keys
+// 256g + 4l + c (g < KPL/4, c < 4), loaded as float4s.  Histograms are per
+// wave in LDS and scanned with shuffles, so a row needs no workgroup barrier.
+// Emission walks the key groups in index order; wave-wide exclusive scans of
+// the per-lane counts place each kept block, and the list is assembled in
+// LDS and stored in one coalesced pass.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_exscan(int v, int *total) {
+  const int lane = lane_id();
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  *total = __shfl(incl, 63, 64);
+  return incl - v;
+}
+
+template <int KPL>
+__global__ __launch_bounds__(256) void idx_select_wave_kernel(IdxSelectArgs a) {
+  constexpr int NG = KPL / 4;
+  __shared__ uint32_t s_hist[4][256];
+  extern __shared__ int32_t s_lists[];  // [4][budget * ratio]
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  const int row = blockIdx.x * 4 + wv;
+  if (row >= a.B * a.S) return;
+  const int b = row % a.B;
+  const int t = a.S - 1 - row / a.B;  // longest rows first
+  const bool live = t < min(a.ctx[b], a.S);
+  int32_t *out = a.out + ((size_t)b * a.S + t) * a.top_k;
+  if (!live) {
+    for (int i = lane; i < a.top_k; i += 64) out[i] = -1;
+    return;
+  }
+  const int r = a.ratio;
+  const int nc = (t + 1) / r;
+  if (nc <= a.budget) {
+    for (int i = lane; i < a.top_k; i += 64) out[i] = i <= t ? i : -1;
+    return;
+  }
+  const float *srow = a.scores + ((size_t)b * a.S + t) * a.row_stride;
+  uint32_t key[KPL];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int i0 = 256 * g + 4 * lane;
+    if (i0 + 3 < nc) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + i0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[4 * g + c] = score_key(v[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[4 * g + c] = i0 + c < nc ? score_key(srow[i0 + c]) : 0u;
+    }
+  }
+  uint32_t *hist = s_hist[wv];
+  // All keys lie in [kmin, kmax] and share the bits above the highest bit
+  // where those two differ; the first 8-bit window starts there.
+  uint32_t kmax = 0, kmin = 0xffffffffu;
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (256 * g + 4 * lane + c < nc) {
+        kmax = max(kmax, key[4 * g + c]);
+        kmin = min(kmin, key[4 * g + c]);
+      }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+  }
+  const uint32_t diff = kmax ^ kmin;
+  int top = diff ? 31 - __clz((int)diff) : -1;       // highest differing bit
+  uint32_t pmask = top < 0 ? 0xffffffffu : (top >= 31 ? 0u : ~((2u << top) - 1u));
+  uint32_t prefix = kmax & pmask;
+  int remaining = a.budget;
+  while (top >= 0) {
+    const int w = min(8, top + 1), shift = top + 1 - w;
+    const uint32_t dmask = (1u << w) - 1u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (256 * g >= nc) break;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t k = key[4 * g + c];
+        const bool act = (256 * g + 4 * lane + c < nc) && (k & pmask) == prefix;
+        const uint32_t dig = (k >> shift) & dmask;
+        const unsigned long long pend = __ballot(act);
+        if (pend) {
+          // one increment for the first active lane's digit, the most common
+          const int leader = __ffsll((long long)pend) - 1;
+          const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)dig, leader);
+          const unsigned long long same = __ballot(act && dig == ld);
+          if (lane == leader) atomicAdd(&hist[ld], (uint32_t)__popcll(same));
+          if (act && dig != ld) atomicAdd(&hist[dig], 1u);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane l holds digits 255-4l .. 252-4l (descending)
+    uint32_t h[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = hist[255 - 4 * lane - j];
+    const int lsum = (int)(h[0] + h[1] + h[2] + h[3]);
+    int tot;
+    const int before = wave_exscan(lsum, &tot);  // keys with a digit above this lane's bins
+    int found = 0, dsel = 0, above = 0, cnt = 0;
+    int acc = before;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!found && acc < remaining && acc + (int)h[j] >= remaining) {
+        found = 1;
+        dsel = 255 - 4 * lane - j;
+        above = acc;
+        cnt = (int)h[j];
+      }
+      acc += (int)h[j];
+    }
+    const int src = __ffsll((long long)__ballot(found)) - 1;
+    dsel = __builtin_amdgcn_readlane(dsel, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    cnt = __builtin_amdgcn_readlane(cnt, src);
+    prefix |= (uint32_t)dsel << shift;
+    pmask |= dmask << shift;
+    remaining -= above;
+    __builtin_amdgcn_wave_barrier();
+    if (cnt == remaining) break;  // the whole bin is kept
+    top = shift - 1;
+  }
+
+  int32_t *lst = s_lists + wv * a.budget * r;
+  int kept = 0, eq_seen = 0;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (256 * g >= nc) break;
+    int gt_m = 0, eq_m = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool ok = 256 * g + 4 * lane + c < nc;
+      const uint32_t m = key[4 * g + c] & pmask;
+      gt_m |= (ok && m > prefix) << c;
+      eq_m |= (ok && m == prefix) << c;
+    }
+    int eq_tot;
+    int eq_rank = eq_seen + wave_exscan(__popc(eq_m), &eq_tot);
+    int keep_m = gt_m;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if ((eq_m >> c) & 1) {
+        if (eq_rank < remaining) keep_m |= 1 << c;
+        ++eq_rank;
+      }
+    int k_tot;
+    int pos = kept + wave_exscan(__popc(keep_m), &k_tot);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if ((keep_m >> c) & 1) {
+        const int blk = 256 * g + 4 * lane + c;
+        for (int j = 0; j < r; ++j) lst[r * pos + j] = r * blk + j;
+        ++pos;
+      }
+    kept += k_tot;
+    eq_seen += eq_tot;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int head = r * a.budget;
+  const int len = head + (t + 1) - r * nc;
+  for (int i = lane; i < a.top_k; i += 64)
+    out[i] = i < head ? lst[i] : (i < len ? r * nc + (i - head) : -1);
 }
 
 // ---------------------------------------------------------------------------
@@ -439,13 +680,19 @@ __global__ __launch_bounds__(256) void idx_dec_score_kernel(IdxDecScoreArgs a) {
     for (int ks = 0; ks < 4; ++ks) kb[tt][ks] = ld16(src + 32 * ks);
   }
   float *srow = a.scores + (size_t)b * a.stride;
+  f32x4 accs[TPW][2];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) accs[tt][0] = accs[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+        accs[tt][ks & 1] = mfma16x16x32<DT>(kb[tt][ks], qb[p][ks], accs[tt][ks & 1]);
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int p = 0; p < NP; ++p) acc = mfma16x16x32<DT>(kb[tt][ks], qb[p][ks], acc);
+    const f32x4 acc = accs[tt][0] + accs[tt][1];
     float v[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -470,20 +717,52 @@ hipError_t launch_idx_prep(const IdxPrepArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_idx_score(const IdxScoreArgs &a, int dt, hipStream_t s) {
-  const long long waves = (long long)a.B * ((a.S + 3) / 4);
-  const unsigned grid = (unsigned)((waves + 3) / 4);
+hipError_t launch_idx_score(const IdxScoreArgs &a_in, int dt, hipStream_t s) {
+  IdxScoreArgs a = a_in;
+  a.nchunk = (a.Gmax + kScoreChunk - 1) / kScoreChunk;
+  if (a.nchunk < 1) a.nchunk = 1;
+  const unsigned grid = (unsigned)((long long)a.B * ((a.S + 31) / 32) * a.nchunk);
   if (dt == DT_F16) hipLaunchKernelGGL(idx_score_kernel<DT_F16>, dim3(grid), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(idx_score_kernel<DT_BF16>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) {
+template <int KPL>
+static void launch_select_wave(const IdxSelectArgs &a, hipStream_t s) {
+  const unsigned grid = (unsigned)(((long long)a.B * a.S + 3) / 4);
+  const size_t lds = (size_t)4 * a.budget * a.ratio * sizeof(int32_t);
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&idx_select_wave_kernel<KPL>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(idx_select_wave_kernel<KPL>, dim3(grid), dim3(256), lds, s, a);
+}
+
+hipError_t launch_idx_select(const IdxSelectArgs &a_in, int nc_max, hipStream_t s) {
+  IdxSelectArgs a = a_in;
+  if (!a.decode && nc_max <= 64 * 128) {  // prefill rows fit in registers
+    if (nc_max <= 64 * 32) launch_select_wave<32>(a, s);
+    else if (nc_max <= 64 * 64) launch_select_wave<64>(a, s);
+    else launch_select_wave<128>(a, s);
+    return hipGetLastError();
+  }
   const unsigned rows = (unsigned)(a.decode ? a.B : (long long)a.B * a.S);
-  const size_t lds = (size_t)(nc_max > 0 ? nc_max : 1) * sizeof(uint32_t);
+  const int nt = a.decode ? 1024 : 256;
+  // keys padded to a whole number of (odd) per-thread ranges, then the list
+  const int per = ((nc_max + nt - 1) / nt) | 1;
+  a.key_cap = per * nt;
+  const size_t lds = ((size_t)a.key_cap + (size_t)a.budget * a.ratio) * sizeof(uint32_t);
   // Decode has one long row per sequence: a wide workgroup per row.
-  if (a.decode) hipLaunchKernelGGL(idx_select_kernel<1024>, dim3(rows), dim3(1024), lds, s, a);
-  else hipLaunchKernelGGL(idx_select_kernel<256>, dim3(rows), dim3(256), lds, s, a);
+  if (a.decode) {
+    if (lds > 65536)
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&idx_select_kernel<1024>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(idx_select_kernel<1024>, dim3(rows), dim3(1024), lds, s, a);
+  } else {
+    if (lds > 65536)
+      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&idx_select_kernel<256>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(idx_select_kernel<256>, dim3(rows), dim3(256), lds, s, a);
+  }
   return hipGetLastError();
 }
 

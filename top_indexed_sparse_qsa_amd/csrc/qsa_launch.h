@@ -47,7 +47,10 @@ struct IdxScoreArgs {
   float *scores;    // [B,S,stride]
   const int32_t *ctx;
   int B, S, Hi, Gmax, stride, ratio;
+  int nchunk;       // block chunks per 32-row group (set by the launcher)
 };
+
+constexpr int kScoreChunk = 128;  // kbar rows staged per prefill scoring workgroup
 
 struct IdxSelectArgs {
   const float *scores;
@@ -58,6 +61,7 @@ struct IdxSelectArgs {
   int top_k, budget, ratio;
   int decode;          // 1: row of sequence b is position ctx[b]-1
   int max_ctx;         // decode: clamp of ctx (max_pages * 128)
+  int key_cap;         // LDS key slots (set by the launcher)
 };
 
 struct IdxDecPrepArgs {

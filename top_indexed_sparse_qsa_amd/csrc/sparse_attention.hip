@@ -185,15 +185,48 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
     qf[ks] = (r16 < G) ? ld16(qhead0 + (size_t)r16 * D + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Row t of every sequence before row t-1: long lists are dispatched first.
+// Work order.  Rows are taken longest-first: row t of every sequence before
+// row t-1.  Workgroups are dispatched round-robin over the eight XCDs, each
+// with its own 4 MB L2.  When Hkv divides 8, workgroup w runs on XCD w % 8
+// and that XCD only ever processes KV head (w % 8) % Hkv: its gathers then
+// touch one KV head's rows instead of all of them, which raises the L2 hit
+// rate whenever K/V outgrow one L2 (every list walks its ids in ascending
+// order, so concurrent waves also touch nearby rows).  A workgroup's four
+// waves take four consecutive rows of that head.  Otherwise a workgroup
+// takes the Hkv heads of consecutive rows.
+__device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int &b, int &t, int &kvh) {
+  const int wave = threadIdx.x >> 6;
+  int rest;
+  if ((8 % a.Hkv) == 0) {
+    const int xcd = blockIdx.x & 7, n = blockIdx.x >> 3;
+    const int per_head = 8 / a.Hkv;  // XCDs sharing one KV head
+    kvh = xcd % a.Hkv;
+    rest = ((n * per_head + xcd / a.Hkv) << 2) + wave;
+    if (rest >= a.B * a.S) return false;
+  } else {
+    const int item = blockIdx.x * 4 + wave;
+    if (item >= a.B * a.S * a.Hkv) return false;
+    kvh = item % a.Hkv;
+    rest = item / a.Hkv;
+  }
+  b = rest % a.B;
+  t = a.S - 1 - rest / a.B;
+  return true;
+}
+
+static unsigned prefill_grid(const PrefillAttnArgs &a) {
+  if ((8 % a.Hkv) == 0) {
+    const long long quads = ((long long)a.B * a.S + 3) / 4;
+    const long long per_head = 8 / a.Hkv;
+    return (unsigned)(8 * ((quads + per_head - 1) / per_head));
+  }
+  return (unsigned)(((long long)a.B * a.S * a.Hkv + 3) / 4);
+}
+
 template <int D, int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(PrefillAttnArgs a) {
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= a.B * a.S * a.Hkv) return;
-  const int kvh = item % a.Hkv;
-  const int rest = item / a.Hkv;
-  const int b = rest % a.B;
-  const int t = a.S - 1 - rest / a.B;
+  int b, t, kvh;
+  if (!prefill_item(a, b, t, kvh)) return;
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int live = min(a.ctx[b], a.S);
   const size_t qo_off = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
@@ -390,9 +423,7 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
 
 template <int D, int DT>
 static hipError_t launch_prefill_t(const PrefillAttnArgs &a, hipStream_t s) {
-  const long long items = (long long)a.B * a.S * a.Hkv;
-  const unsigned grid = (unsigned)((items + 3) / 4);
-  hipLaunchKernelGGL((sparse_prefill_kernel<D, DT>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((sparse_prefill_kernel<D, DT>), dim3(prefill_grid(a)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
