@@ -29,6 +29,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_prefill_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "top_indexed_sparse_qsa_amd", "csrc", "sparse_attention.hip")
 METRIC = "sparse prefill tokens/s + decode seqs/s (topK 2051); % HBM roofline"
 PREFILL_WORKLOADS = (2, 3, 5)
 DECODE_WORKLOAD = 4
@@ -178,6 +180,27 @@ def decode_bench(args, Q, syn, torch):
     return out
 
 
+def measured_traffic(wl):
+    """HBM bytes per sparse_prefill launch from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, if it was taken on this kernel source."""
+    import hashlib
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                line = line.strip()
+                if line and not line.startswith("#") and "=" in line:
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        with open(KERNEL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("kernel_source_sha256") != sha:
+            return None
+        return int(kv[f"workload{wl}_fetch_bytes"]) + int(kv[f"workload{wl}_write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl):
     """The oracle, unchanged, on the same workload (single thread)."""
     import qsa_synth as syn
@@ -266,7 +289,7 @@ def main():
         "parts_ms": {"indexer_prefill": pf["indexer_ms"], "sparse_prefill": pf["attention_ms"]},
         "roofline": {"bound": "hbm", "kernel": "sparse_prefill_kernel",
                      "achieved": pf["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": pf["achieved_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": pf["achieved_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
                      "algorithmic_bytes_per_launch": pf["attn_bytes"]},
         "cpu_baseline": cpu,
         "decode": dec,

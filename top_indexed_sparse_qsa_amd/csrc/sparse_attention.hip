@@ -9,21 +9,22 @@
 // Work split: one wave per (query row, KV head) in prefill and per (sequence,
 // KV head, split) in decode.  The GQA head group of one KV head (up to 16
 // query heads) is the 16-wide MFMA tile.  Per chunk of 32 list slots a wave
-//   * gathers the 32 K rows straight into MFMA A-fragments (each lane reads
-//     16 contiguous bytes of one row; four lanes cover 64 bytes of a row),
-//   * gathers the 32 V rows with each 16-lane group reading whole rows
-//     (fully coalesced 256-byte rows for D = 128),
+//   * gathers the 32 K rows and the 32 V rows with each 16-lane group
+//     reading whole 256-byte rows (a row per 16 lanes is ~3x the L1
+//     throughput of spreading one load instruction over 16 rows), so lane
+//     (q, c) holds dims 8c..8c+7 of eight keys ("key slots") of K and of V,
+//   * writes its K rows to a per-wave LDS tile (16-byte pieces XOR-swizzled
+//     by row) and reads them back as MFMA A fragments, both conflict-free,
 //   * computes S^T = K Q^T (two 16-key tiles), so every lane ends up owning
-//     the scores of one query head m = lane % 16 for eight keys,
+//     the scores of one query head m = lane % 16 for its eight key slots,
 //   * runs the fp32 online softmax in the exp2 domain,
 //   * feeds those eight probabilities, unchanged in place, as the B operand
 //     of O^T += V^T P^T; the V^T A-operand is an in-register 8x8 transpose of
 //     16-bit values (v_perm) because a lane already holds eight keys x eight
 //     dims of V.  Output dim d = 8*row + e, so lane (q, m) accumulates the 32
 //     contiguous dims [32q, 32q+32) of head m.
-// No LDS is needed on the prefill path; decode stages its page-table row in
-// LDS.  The next chunk's gathers are in flight while the current one
-// computes, and ids run two chunks ahead.
+// The next chunk's gathers are in flight while the current one computes, and
+// ids run two chunks ahead.
 #include <math.h>
 
 #include "qsa_device.h"
@@ -34,7 +35,7 @@ namespace qsa {
 template <int D>
 struct Frag {
   static constexpr int NKS = D / 32;
-  u32x4 kf[2][NKS];  // K, A-operand layout, tiles of keys 0..15 and 16..31
+  u32x4 kf[8];       // K rows of the lane's eight key slots, dims 8c..8c+7
   u32x4 vf[8];       // V rows of the lane's eight key slots, dims 8c..8c+7
   uint32_t valid;    // bit i: key slot i of this lane is usable
 };
@@ -67,37 +68,46 @@ struct PagedKV {
 
 template <int D, int DT, class KV>
 __device__ __forceinline__ void issue_chunk(Frag<D> &f, int idv, const KV &kv, int q4, int r16) {
-  int kid0 = shfl_i(idv, r16), kid1 = shfl_i(idv, 16 + r16);
-  kid0 = ((unsigned)kid0 < (unsigned)kv.limit) ? kid0 : 0;
-  kid1 = ((unsigned)kid1 < (unsigned)kv.limit) ? kid1 : 0;
-  const uint16_t *k0 = kv.krow(kid0) + 8 * q4;
-  const uint16_t *k1 = kv.krow(kid1) + 8 * q4;
-#pragma unroll
-  for (int ks = 0; ks < Frag<D>::NKS; ++ks) {
-    f.kf[0][ks] = ld16(k0 + 32 * ks);
-    f.kf[1][ks] = ld16(k1 + 32 * ks);
-  }
   uint32_t valid = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int id = shfl_i(idv, slot_of(q4, i));
     bool ok = (unsigned)id < (unsigned)kv.limit;
     valid |= (uint32_t)ok << i;
-    if (D == 128 || r16 < D / 8) f.vf[i] = ld16(kv.vrow(ok ? id : 0) + 8 * r16);
-    else f.vf[i] = u32x4{0u, 0u, 0u, 0u};
+    const int sid = ok ? id : 0;
+    if (D == 128 || r16 < D / 8) {
+      f.kf[i] = ld16(kv.krow(sid) + 8 * r16);
+      f.vf[i] = ld16(kv.vrow(sid) + 8 * r16);
+    } else {
+      f.kf[i] = u32x4{0u, 0u, 0u, 0u};
+      f.vf[i] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
   f.valid = valid;
 }
 
+// Per-wave LDS tile for one chunk of K: 32 rows of 256 B, 16-byte pieces
+// XOR-swizzled by row so that both the row writes and the fragment reads are
+// free of bank conflicts.
 template <int D, int DT>
 __device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf)[D / 32], float sl2,
-                                              float &m_run, float &l_run, f32x4 (&acc)[8]) {
+                                              float &m_run, float &l_run, f32x4 (&acc)[8], u32x4 *ktile) {
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = slot_of(q4, i);
+    if (D == 128 || r16 < D / 8) ktile[row * 16 + (r16 ^ (row & 15))] = f.kf[i];
+  }
+  __builtin_amdgcn_wave_barrier();
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < Frag<D>::NKS; ++ks) {
-    s0 = mfma16x16x32<DT>(f.kf[0][ks], qf[ks], s0);
-    s1 = mfma16x16x32<DT>(f.kf[1][ks], qf[ks], s1);
+    const u32x4 k0 = ktile[r16 * 16 + ((4 * ks + q4) ^ r16)];
+    const u32x4 k1 = ktile[(16 + r16) * 16 + ((4 * ks + q4) ^ r16)];
+    s0 = mfma16x16x32<DT>(k0, qf[ks], s0);
+    s1 = mfma16x16x32<DT>(k1, qf[ks], s1);
   }
+  __builtin_amdgcn_wave_barrier();
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -140,7 +150,7 @@ __device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf
 template <int D, int DT, class KV>
 __device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV &kv,
                          const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
-                         f32x4 (&acc)[8]) {
+                         f32x4 (&acc)[8], u32x4 *ktile) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int nchunks = (n_slots + 31) >> 5;
   auto load_id = [&](int c) -> int {
@@ -163,7 +173,7 @@ __device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV
       issue_chunk<D, DT>(fb, id_b, kv, q4, r16);
       id_d = load_id(c + 3);
     }
-    consume_chunk<D, DT>(fa, qf, sl2, m_run, l_run, acc);
+    consume_chunk<D, DT>(fa, qf, sl2, m_run, l_run, acc, ktile);
     if (!b_ok) break;
     const bool c_ok = usable(id_c);
     int id_e = -1;
@@ -171,7 +181,7 @@ __device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV
       issue_chunk<D, DT>(fa, id_c, kv, q4, r16);
       id_e = load_id(c + 4);
     }
-    consume_chunk<D, DT>(fb, qf, sl2, m_run, l_run, acc);
+    consume_chunk<D, DT>(fb, qf, sl2, m_run, l_run, acc, ktile);
     if (!c_ok) break;
     id_b = id_d;
     id_c = id_e;
@@ -185,15 +195,15 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
     qf[ks] = (r16 < G) ? ld16(qhead0 + (size_t)r16 * D + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Work order.  Rows are taken longest-first: row t of every sequence before
-// row t-1.  Workgroups are dispatched round-robin over the eight XCDs, each
-// with its own 4 MB L2.  When Hkv divides 8, workgroup w runs on XCD w % 8
-// and that XCD only ever processes KV head (w % 8) % Hkv: its gathers then
-// touch one KV head's rows instead of all of them, which raises the L2 hit
-// rate whenever K/V outgrow one L2 (every list walks its ids in ascending
-// order, so concurrent waves also touch nearby rows).  A workgroup's four
-// waves take four consecutive rows of that head.  Otherwise a workgroup
-// takes the Hkv heads of consecutive rows.
+// Work order.  Sequences one after another, and within a sequence rows
+// longest-first (row t before row t-1).  Workgroups are dispatched
+// round-robin over the eight XCDs, each with its own 4 MB L2.  When Hkv
+// divides 8, workgroup w runs on XCD w % 8 and that XCD only ever processes
+// KV head (w % 8) % Hkv: its gathers then touch one KV head of one sequence
+// at a time, which keeps most gathers in L2 even when K/V outgrow it (every
+// list walks its ids in ascending order, so concurrent waves touch nearby
+// rows).  A workgroup's four waves take four consecutive rows of that head.
+// Otherwise a workgroup takes the Hkv heads of consecutive rows.
 __device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int &b, int &t, int &kvh) {
   const int wave = threadIdx.x >> 6;
   int rest;
@@ -209,8 +219,8 @@ __device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int &b, i
     kvh = item % a.Hkv;
     rest = item / a.Hkv;
   }
-  b = rest % a.B;
-  t = a.S - 1 - rest / a.B;
+  b = rest / a.S;
+  t = a.S - 1 - rest % a.S;
   return true;
 }
 
@@ -225,6 +235,8 @@ static unsigned prefill_grid(const PrefillAttnArgs &a) {
 
 template <int D, int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(PrefillAttnArgs a) {
+  __shared__ u32x4 s_ktile[4][32 * 16];
+  u32x4 *ktile = s_ktile[threadIdx.x >> 6];
   int b, t, kvh;
   if (!prefill_item(a, b, t, kvh)) return;
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
@@ -243,7 +255,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     kv.v = a.v + ((size_t)b * a.S * a.Hkv + kvh) * D;
     kv.row_stride = (size_t)a.Hkv * D;
     kv.limit = live;
-    run_list<D, DT>(a.indices + ((size_t)b * a.S + t) * a.top_k, a.top_k, kv, qf, a.sl2, m_run, l_run, acc);
+    run_list<D, DT>(a.indices + ((size_t)b * a.S + t) * a.top_k, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile);
   }
   float l = l_run + shfl_xor_f(l_run, 16);
   l += shfl_xor_f(l, 32);
@@ -273,12 +285,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // make one workgroup's stores visible to another.
 constexpr int kDecWaves = 4;  // waves (splits) per workgroup
 
+// The K tiles are dead once every wave has finished its list (a workgroup
+// barrier separates the two uses), so the merge scratch overlays them.
 template <int D>
-struct DecMergeLds {
+union DecMergeLds {
   static constexpr int RS = D + 4;  // padded row stride (floats)
-  float acc[kDecWaves][16 * RS];
-  float m[kDecWaves][16];
-  float l[kDecWaves][16];
+  struct {
+    float acc[kDecWaves][16 * RS];
+    float m[kDecWaves][16];
+    float l[kDecWaves][16];
+  };
+  u32x4 ktile[kDecWaves][32 * 16];
 };
 
 // Lane (q, r) of wave w merges row r, dims [d0, d0 + D/16).
@@ -318,8 +335,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     kv.row_stride = (size_t)a.Hkv * a.PHD;
     kv.num_flat_pages = a.num_flat_pages;
     kv.limit = ctx;
-    run_list<D, DT>(a.indices + (size_t)b * a.top_k + s0, n_slots, kv, qf, a.sl2, m_run, l_run, acc);
+    run_list<D, DT>(a.indices + (size_t)b * a.top_k + s0, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile[wv]);
   }
+  __syncthreads();  // every K tile is dead before the merge scratch is written
   float l = l_run + shfl_xor_f(l_run, 16);
   l += shfl_xor_f(l, 32);
   if (32 * q4 < D) {
