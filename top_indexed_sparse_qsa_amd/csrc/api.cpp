@@ -133,6 +133,8 @@ qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p) {
   if (qsa_status st = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim)) return st;
   if (!all_aligned16(p->q, p->k, p->v, p->o)) return QSA_ERR_BAD_SHAPE;
   if ((int64_t)p->batch * p->seq_len * p->num_kv_heads > (int64_t)INT32_MAX - 4) return QSA_ERR_UNSUPPORTED;
+  // one sequence's K (or V) is addressed with 32-bit byte offsets
+  if ((int64_t)p->seq_len * p->num_kv_heads * p->head_dim * 2 >= ((int64_t)1 << 32)) return QSA_ERR_UNSUPPORTED;
   if (!isfinite(p->attention_scale)) return QSA_ERR_BAD_SHAPE;
   qsa::PrefillAttnArgs a;
   a.q = static_cast<const uint16_t *>(p->q);

@@ -43,12 +43,18 @@ struct Frag {
 // Key slot i of lane group q: keys 4q+i (i < 4) and 16+4q+(i-4) (i >= 4).
 __device__ __forceinline__ int slot_of(int q4, int i) { return i < 4 ? 4 * q4 + i : 12 + 4 * q4 + i; }
 
+// Dense K/V of one sequence and KV head.  The bases are wave-uniform (scalar
+// registers) and a token's 16-byte piece is a 32-bit byte offset shared by
+// the K and V loads (the host keeps one sequence's K/V under 4 GiB).
 struct DenseKV {
-  const uint16_t *k, *v;  // row 0 of this sequence, this KV head
-  size_t row_stride;      // elements between consecutive tokens
+  const char *k, *v;      // row 0 of this sequence, this KV head
+  uint32_t row_bytes;     // bytes between consecutive tokens
   int limit;              // ids in [0, limit) are usable
-  __device__ const uint16_t *krow(int id) const { return k + (size_t)id * row_stride; }
-  __device__ const uint16_t *vrow(int id) const { return v + (size_t)id * row_stride; }
+  __device__ void load(int id, int r16, u32x4 &kd, u32x4 &vd) const {
+    const uint32_t off = (uint32_t)id * row_bytes + 16u * (uint32_t)r16;
+    kd = ld16(k + off);
+    vd = ld16(v + off);
+  }
 };
 
 struct PagedKV {
@@ -62,8 +68,10 @@ struct PagedKV {
     if ((unsigned)pg >= (unsigned)num_flat_pages) pg = 0;
     return pool + ((size_t)pg * 128 + (id & 127)) * row_stride;
   }
-  __device__ const uint16_t *krow(int id) const { return row(pk, id); }
-  __device__ const uint16_t *vrow(int id) const { return row(pv, id); }
+  __device__ void load(int id, int r16, u32x4 &kd, u32x4 &vd) const {
+    kd = ld16(row(pk, id) + 8 * r16);
+    vd = ld16(row(pv, id) + 8 * r16);
+  }
 };
 
 template <int D, int DT, class KV>
@@ -76,8 +84,7 @@ __device__ __forceinline__ void issue_chunk(Frag<D> &f, int idv, const KV &kv, i
     valid |= (uint32_t)ok << i;
     const int sid = ok ? id : 0;
     if (D == 128 || r16 < D / 8) {
-      f.kf[i] = ld16(kv.krow(sid) + 8 * r16);
-      f.vf[i] = ld16(kv.vrow(sid) + 8 * r16);
+      kv.load(sid, r16, f.kf[i], f.vf[i]);
     } else {
       f.kf[i] = u32x4{0u, 0u, 0u, 0u};
       f.vf[i] = u32x4{0u, 0u, 0u, 0u};
@@ -205,7 +212,7 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
 // rows).  A workgroup's four waves take four consecutive rows of that head.
 // Otherwise a workgroup takes the Hkv heads of consecutive rows.
 __device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int &b, int &t, int &kvh) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int rest;
   if ((8 % a.Hkv) == 0) {
     const int xcd = blockIdx.x & 7, n = blockIdx.x >> 3;
@@ -251,9 +258,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     u32x4 qf[D / 32];
     load_q<D>(qf, a.q + qo_off, a.G, q4, r16);
     DenseKV kv;
-    kv.k = a.k + ((size_t)b * a.S * a.Hkv + kvh) * D;
-    kv.v = a.v + ((size_t)b * a.S * a.Hkv + kvh) * D;
-    kv.row_stride = (size_t)a.Hkv * D;
+    kv.k = reinterpret_cast<const char *>(a.k + ((size_t)b * a.S * a.Hkv + kvh) * D);
+    kv.v = reinterpret_cast<const char *>(a.v + ((size_t)b * a.S * a.Hkv + kvh) * D);
+    kv.row_bytes = (uint32_t)(a.Hkv * D * 2);
     kv.limit = live;
     run_list<D, DT>(a.indices + ((size_t)b * a.S + t) * a.top_k, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile);
   }
