@@ -111,49 +111,36 @@ __device__ __forceinline__ void load8f(float (&x)[8], const float *p) {
   x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
 
-// Prefill scoring.  A workgroup takes 32 consecutive rows and one chunk of
-// kScoreChunk complete blocks; long row ranges are cut into several chunks
-// (chunks of the last rows are dispatched first).  The chunk's kbar rows are
-// staged once in LDS, 16-byte pieces XOR-swizzled by row so that MFMA
-// fragment reads are conflict-free; each wave then computes 8 rows against
-// the whole chunk.  The MFMA M tile is (row, head) with the head fastest, so
-// each 16-lane group ends with the four head dots of one row and one block
-// and sums their relus in-lane; a wave's two M tiles share every kbar
-// fragment.
+// Prefill scoring.  A workgroup takes 32 consecutive rows and a run of up to
+// kScoreChunksPerGroup chunks of kScoreChunk complete blocks (rows' queries
+// are loaded and split once per run); runs of the last rows are dispatched
+// first.  Per chunk the kbar rows are staged in LDS, 16-byte pieces
+// XOR-swizzled by row so that MFMA fragment reads are conflict-free; each wave
+// computes 8 rows against the chunk.  The MFMA M tile is (row, head) with the
+// head fastest, so each 16-lane group ends with the four head dots of one row
+// and one block and sums their relus in-lane; a wave's two M tiles share every
+// kbar fragment.  The chunk's 32 x kScoreChunk scores are assembled in LDS and
+// stored as whole 512-byte row segments.
 template <int DT>
 __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
   constexpr int NP = QSplit<DT>::NP;
-  __shared__ __align__(16) uint32_t s_kb[kScoreChunk * 64];  // kScoreChunk rows x 256 B
+  constexpr int CB = kScoreChunk;
+  __shared__ __align__(16) uint32_t s_kb[CB * 64];     // CB rows x 256 B
+  __shared__ __align__(16) float s_sc[32][CB + 4];    // scores of the chunk
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15, wv = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
   const int T32 = (a.S + 31) >> 5;
   const long long item = blockIdx.x;
   const int b = (int)(item % a.B);
   const long long rest = item / a.B;
-  const int ch = (int)(rest % a.nchunk);
+  const int run = (int)(rest % a.nchunk);
   const int tg = 32 * (T32 - 1 - (int)(rest / a.nchunk));
   const int live = min(a.ctx[b], a.S);
   if (tg >= live) return;
   const int nc_hi = (min(tg + 31, live - 1) + 1) / a.ratio;
-  const int g_lo = ch * kScoreChunk, g_hi = min(g_lo + kScoreChunk, nc_hi);
-  if (g_lo >= g_hi) return;
-
-  // stage kbar rows [g_lo, g_hi) (16 pieces of 16 B per row)
-  {
-    const uint16_t *src = a.kbar + ((size_t)b * a.Gmax + g_lo) * 128;
-    const int npiece = (g_hi - g_lo) * 16;
-    u32x4 v[kScoreChunk * 16 / 256];
-#pragma unroll
-    for (int u = 0; u < kScoreChunk * 16 / 256; ++u) {
-      const int i = threadIdx.x + 256 * u;
-      if (i < npiece) v[u] = ld16(src + 8 * i);
-    }
-#pragma unroll
-    for (int u = 0; u < kScoreChunk * 16 / 256; ++u) {
-      const int i = threadIdx.x + 256 * u;
-      const int row = i >> 4, pc = i & 15;
-      if (i < npiece) *reinterpret_cast<u32x4 *>(&s_kb[row * 64 + 4 * (pc ^ (row & 15))]) = v[u];
-    }
-  }
+  const int run_lo = run * kScoreChunksPerGroup * CB;
+  const int run_hi = min(run_lo + kScoreChunksPerGroup * CB, nc_hi);
+  if (run_lo >= run_hi) return;
 
   const int t0 = tg + 8 * wv;
   u32x4 qa[2][NP][4];
@@ -175,40 +162,71 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
     }
   }
   int nc_out[2];
-  float *srow[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int t_out = t0 + 4 * m + q4;
     nc_out[m] = t_out < live ? (t_out + 1) / a.ratio : 0;
-    srow[m] = a.scores + ((size_t)b * a.S + min(t_out, a.S - 1)) * a.stride;
   }
-  __syncthreads();
   const int nc_wave = t0 < live ? (min(t0 + 7, live - 1) + 1) / a.ratio : 0;
-  const int g_end = min(g_hi, nc_wave);
-  for (int g0 = g_lo; g0 < g_end; g0 += 16) {
-    const int lb = g0 - g_lo + r16;  // local kbar row; lb & 15 == r16
-    u32x4 kb[4];
+
+  for (int g_lo = run_lo; g_lo < run_hi; g_lo += CB) {
+    const int g_hi = min(g_lo + CB, run_hi);
+    // stage kbar rows [g_lo, g_hi)
+    {
+      const uint16_t *src = a.kbar + ((size_t)b * a.Gmax + g_lo) * 128;
+      const int npiece = (g_hi - g_lo) * 16;
+      u32x4 v[CB * 16 / 256];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kb[ks] = *reinterpret_cast<const u32x4 *>(&s_kb[lb * 64 + 4 * ((4 * ks + q4) ^ r16)]);
-    // four independent accumulator chains (M tile x k-step parity), interleaved
-    f32x4 acc[2][2];
+      for (int u = 0; u < CB * 16 / 256; ++u) {
+        const int i = tid + 256 * u;
+        if (i < npiece) v[u] = ld16(src + 8 * i);
+      }
+      __syncthreads();  // the previous chunk's LDS data is consumed
 #pragma unroll
-    for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m][ks & 1] = mfma16x16x32<DT>(qa[m][p][ks], kb[ks], acc[m][ks & 1]);
-    float sc[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const f32x4 d = acc[m][0] + acc[m][1];
-      sc[m] = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) + fmaxf(d[3], 0.f);
+      for (int u = 0; u < CB * 16 / 256; ++u) {
+        const int i = tid + 256 * u;
+        const int row = i >> 4, pc = i & 15;
+        if (i < npiece) *reinterpret_cast<u32x4 *>(&s_kb[row * 64 + 4 * (pc ^ (row & 15))]) = v[u];
+      }
+      __syncthreads();
     }
+    const int g_end = min(g_hi, nc_wave);
+    for (int g0 = g_lo; g0 < g_end; g0 += 16) {
+      const int lb = g0 - g_lo + r16;  // local kbar row; lb & 15 == r16
+      u32x4 kb[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-      if (g0 + r16 < nc_out[m]) srow[m][g0 + r16] = sc[m];
+      for (int ks = 0; ks < 4; ++ks) kb[ks] = *reinterpret_cast<const u32x4 *>(&s_kb[lb * 64 + 4 * ((4 * ks + q4) ^ r16)]);
+      // four independent accumulator chains (M tile x k-step parity), interleaved
+      f32x4 acc[2][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) acc[m][ks & 1] = mfma16x16x32<DT>(qa[m][p][ks], kb[ks], acc[m][ks & 1]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const f32x4 d = acc[m][0] + acc[m][1];
+        s_sc[8 * wv + 4 * m + q4][lb] = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) + fmaxf(d[3], 0.f);
+      }
+    }
+    __syncthreads();
+    // store the chunk's scores: 32 rows x (g_hi - g_lo) floats, 16 B per lane
+    const int width = g_hi - g_lo;            // multiple of 16 except at the causal edge
+    for (int i = tid; i < 32 * (CB / 4); i += 256) {
+      const int r = i / (CB / 4), c4 = 4 * (i % (CB / 4));
+      const int t = tg + r;
+      if (t >= live || c4 >= width) continue;
+      const int ncr = (t + 1) / a.ratio - g_lo;  // this row's blocks in the chunk
+      if (c4 >= ncr) continue;
+      float *dst = a.scores + ((size_t)b * a.S + t) * a.stride + g_lo + c4;
+      const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&s_sc[r][c4]);
+      if (c4 + 4 <= ncr) *reinterpret_cast<f32x4 *>(dst) = v4;
+      else
+        for (int j = 0; j < ncr - c4; ++j) dst[j] = v4[j];
+    }
   }
 }
 
@@ -719,7 +737,7 @@ hipError_t launch_idx_prep(const IdxPrepArgs &a, hipStream_t s) {
 
 hipError_t launch_idx_score(const IdxScoreArgs &a_in, int dt, hipStream_t s) {
   IdxScoreArgs a = a_in;
-  a.nchunk = (a.Gmax + kScoreChunk - 1) / kScoreChunk;
+  a.nchunk = (a.Gmax + kScoreChunk * kScoreChunksPerGroup - 1) / (kScoreChunk * kScoreChunksPerGroup);
   if (a.nchunk < 1) a.nchunk = 1;
   const unsigned grid = (unsigned)((long long)a.B * ((a.S + 31) / 32) * a.nchunk);
   if (dt == DT_F16) hipLaunchKernelGGL(idx_score_kernel<DT_F16>, dim3(grid), dim3(256), 0, s, a);

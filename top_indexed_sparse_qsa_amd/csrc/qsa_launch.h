@@ -47,10 +47,11 @@ struct IdxScoreArgs {
   float *scores;    // [B,S,stride]
   const int32_t *ctx;
   int B, S, Hi, Gmax, stride, ratio;
-  int nchunk;       // block chunks per 32-row group (set by the launcher)
+  int nchunk;       // chunk runs per 32-row group (set by the launcher)
 };
 
-constexpr int kScoreChunk = 128;  // kbar rows staged per prefill scoring workgroup
+constexpr int kScoreChunk = 128;           // kbar rows staged at a time in prefill scoring
+constexpr int kScoreChunksPerGroup = 8;    // chunks per prefill scoring workgroup
 
 struct IdxSelectArgs {
   const float *scores;
