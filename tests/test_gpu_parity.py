@@ -165,6 +165,87 @@ def test_indexer_prefill_budget512_selective_rows():
     TL.log(f"  boundary swaps used: {swaps}")
 
 
+def tie_classes(inp, icfg, classes):
+    """Give every token of block g the raw key of class g mod `classes`.  With
+    rot_dim 0 the pooled keys of one class are then identical, so a row's
+    scores tie exactly inside each class."""
+    r = icfg.compress_ratio
+    pats = inp.idx_k[0, :classes].copy()
+    inp.idx_k[:] = pats[(np.arange(inp.S) // r) % classes][None]
+
+
+def tie_expectation(t, class_score, classes, icfg):
+    """The one list the tie rule allows: classes by score, lower blocks first
+    inside the class that straddles the budget."""
+    r, budget = icfg.compress_ratio, icfg.budget
+    nc = (t + 1) // r
+    if nc <= budget:
+        return np.arange(t + 1)
+    blocks = np.arange(nc)
+    order = np.lexsort((blocks, -class_score[blocks % classes]))
+    keep = np.sort(order[:budget])
+    return np.concatenate([(keep[:, None] * r + np.arange(r)).ravel(), np.arange(r * nc, t + 1)])
+
+
+def check_tied_rows(lists, inp, icfg, classes, rows, what):
+    _, scores = O.indexer_prefill(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.ctx, icfg, inp.dtype, icfg.top_k,
+                                  rows=rows, return_scores=True)
+    checked = 0
+    for (b, t) in rows:
+        got = lists[b, t] if isinstance(lists, np.ndarray) else lists[(b, t)]
+        live = min(int(inp.ctx[b]), inp.S)
+        if t >= live:
+            assert np.all(got == -1), f"{what}: dead row {t}"
+            continue
+        sc = scores.get((b, t))
+        if sc is None or len(sc) == 0:
+            exp = np.arange(t + 1)
+        else:
+            cs = np.array([sc[c] for c in range(min(classes, len(sc)))])
+            # classes whose scores sit within 1e-3 of each other could swap by
+            # rounding: such rows are left out
+            if len(cs) > 1 and np.min(np.diff(np.sort(cs))) <= 1e-3 * max(np.max(cs), 1e-30):
+                continue
+            exp = tie_expectation(t, cs, len(cs), icfg)
+        n = len(exp)
+        assert np.array_equal(np.sort(got[:n]), np.sort(exp)), f"{what}: row {t} breaks the tie rule"
+        assert np.all(got[n:] == -1), f"{what}: row {t} padding"
+        checked += 1
+    assert checked >= len(rows) // 2, f"{what}: only {checked} rows had well separated classes"
+
+
+@pytest.mark.parametrize("classes", [1, 3])
+def test_indexer_prefill_exact_ties_wave_select(classes):
+    """Exact score ties at the cut: the lowest block indices win."""
+    icfg = syn.IndexerCfg(rot_dim=0)
+    TL.log(f"indexer_prefill ties classes={classes} S=3000")
+    inp = syn.make_prefill(12, B=2, S=3000, Hq=2, Hkv=1, D=64, dtype="fp16", ctx=[3000, 2100], icfg=icfg)
+    tie_classes(inp, icfg, classes)
+    out, _ = gpu_indexer_prefill(inp, icfg, icfg.top_k)
+    rows = [(b, t) for b in range(2) for t in list(range(2040, 2120)) + list(range(2900, 3000))]
+    check_tied_rows(out.cpu().numpy(), inp, icfg, classes, rows, f"ties{classes}")
+
+
+@pytest.mark.parametrize("classes", [0, 7])
+def test_indexer_prefill_long_rows_workgroup_select(classes):
+    """Rows with more than 8192 complete blocks take the workgroup select."""
+    icfg = syn.IndexerCfg(rot_dim=0) if classes else syn.IndexerCfg()
+    S = 33100
+    TL.log(f"indexer_prefill long rows S={S} classes={classes}")
+    inp = syn.make_prefill(13, B=1, S=S, Hq=2, Hkv=1, D=64, dtype="bf16", ctx=[S], icfg=icfg)
+    if classes:
+        tie_classes(inp, icfg, classes)
+    out, _ = gpu_indexer_prefill(inp, icfg, icfg.top_k)
+    rng = np.random.default_rng(13)
+    rows = sorted({(0, int(t)) for t in rng.integers(2048, S, 10)} | {(0, S - 1), (0, S - 4), (0, 32771)})
+    lists = {r: out[r[0], r[1]].cpu().numpy() for r in rows}
+    if classes:
+        check_tied_rows(lists, inp, icfg, classes, rows, "long ties")
+    else:
+        _, swaps, _ = compare_lists(lists, inp, icfg, icfg.top_k, rows, "long rows")
+        TL.log(f"  boundary swaps used: {swaps}")
+
+
 # ---------------------------------------------------------------------------
 # the prefill workloads at full size (bench launch configuration)
 # ---------------------------------------------------------------------------

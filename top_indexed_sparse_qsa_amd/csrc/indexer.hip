@@ -231,230 +231,60 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Select + expand.  One workgroup per row (256 threads in prefill, 1024 for
-// the long decode rows).  Scores are non-negative, so their fp32 bit
-// patterns (sign cleared) order like the values.  An MSB-first radix select
-// over 8-bit digits (LDS histograms; each wave adds the count of its most
-// common digits with one increment) narrows the cut down to a bin: every key
-// above the bin is kept, and the lowest-index keys of the bin up to the
-// budget.  It stops as soon as the bin holds exactly the keys still needed.
-// Emission: thread j owns the contiguous key range [j*per, (j+1)*per) (per
-// odd, so LDS reads are conflict-free); two block-wide scans give each thread
-// the number of equal keys and of kept blocks before its range, and it writes
-// its kept blocks, in ascending order, as ratio consecutive token ids into an
-// LDS copy of the list that is then stored with the causal tail and -1
-// padding in one coalesced pass.
+// Select + expand, shared pieces.  Scores are non-negative, so their fp32 bit
+// patterns (sign cleared) order like the values; an MSB-first radix select
+// over those keys narrows the cut down to one bin.  Every key above the bin
+// is kept, and of the bin's keys the lowest-index ones up to the budget.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t score_key(float s) { return __float_as_uint(s) & 0x7fffffffu; }
 
-// Exclusive prefix sum of v over the NT threads in thread order; sets *total.
-template <int NT>
-__device__ __forceinline__ int block_exscan(int v, int *s_wave, int *total) {
-  constexpr int NW = NT / 64;
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
-  __syncthreads();
-  if (lane == 63) s_wave[wv] = incl;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int c = s_wave[w];
-    before += w < wv ? c : 0;
-    tot += c;
-  }
-  *total = tot;
-  return before + incl - v;
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts inside
+// each 16-lane row, then the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
 }
 
-template <int NT>
-__global__ __launch_bounds__(NT) void idx_select_kernel(IdxSelectArgs a) {
-  constexpr int NW = NT / 64;
-  extern __shared__ uint32_t s_dyn[];      // keys [key_cap] | list [top_k]
-  __shared__ uint32_t hist[256];
-  __shared__ int s_wave[NW > 4 ? NW : 4];
-  __shared__ uint32_t s_digit, s_above, s_cnt;
-  const int tid = threadIdx.x, lane = lane_id();
+// Radix histograms: the first window has 2048 bins, later ones 256; four pad
+// words per 32 bins keep reads of consecutive bins by consecutive lanes free
+// of bank conflicts.
+constexpr int kSelBins = 2048;
+__device__ __forceinline__ int hpad(int d) { return d + ((d >> 5) << 2); }
+constexpr int kSelHistWords = 2048 + (2048 >> 3);
 
-  int b, t, live;
-  int32_t *out;
-  const float *srow;
-  if (a.decode) {
-    b = blockIdx.x;
-    const int c = min(a.ctx[b], a.max_ctx);
-    t = c - 1;
-    live = c > 0;
-    out = a.out + (size_t)b * a.top_k;
-    srow = a.scores + (size_t)b * a.row_stride;
-  } else {
-    // longest rows first
-    const int r = blockIdx.x;
-    b = r % a.B;
-    t = a.S - 1 - r / a.B;
-    live = t < min(a.ctx[b], a.S);
-    out = a.out + ((size_t)b * a.S + t) * a.top_k;
-    srow = a.scores + ((size_t)b * a.S + t) * a.row_stride;
-  }
-  if (!live) {
-    for (int i = tid; i < a.top_k; i += NT) out[i] = -1;
-    return;
-  }
-  const int r = a.ratio;
-  const int nc = (t + 1) / r;
-  if (nc <= a.budget) {  // every complete block is kept: the list is 0..t
-    for (int i = tid; i < a.top_k; i += NT) out[i] = i <= t ? i : -1;
-    return;
-  }
-  uint32_t *s_key = s_dyn;
-  int32_t *s_list = reinterpret_cast<int32_t *>(s_dyn + a.key_cap);
-
-  // Stage the row's keys in LDS: rows start 64-byte aligned; four float4
-  // loads per thread are in flight before the first LDS store.
-  {
-    const int n4 = nc >> 2;
-    const f32x4 *src4 = reinterpret_cast<const f32x4 *>(srow);
-    for (int base = 0; base < n4; base += 4 * NT) {
-      f32x4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i4 = base + u * NT + tid;
-        if (i4 < n4) v[u] = src4[i4];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i4 = base + u * NT + tid;
-        if (i4 < n4) {
-          s_key[4 * i4] = score_key(v[u][0]);
-          s_key[4 * i4 + 1] = score_key(v[u][1]);
-          s_key[4 * i4 + 2] = score_key(v[u][2]);
-          s_key[4 * i4 + 3] = score_key(v[u][3]);
-        }
-      }
-    }
-    for (int i = 4 * n4 + tid; i < nc; i += NT) s_key[i] = score_key(srow[i]);
-  }
-
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t remaining = (uint32_t)a.budget;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < nc + NT - 1 - ((nc + NT - 1) % NT); i += NT) {
-      bool act = false;
-      uint32_t dig = 0;
-      if (i < nc) {
-        const uint32_t k = s_key[i];
-        act = (k & pmask) == prefix;
-        dig = (k >> shift) & 255u;
-      }
-      // Peel off the most common digits of the wave with one increment each.
-      unsigned long long pend = __ballot(act);
-      for (int rep = 0; rep < 4 && pend; ++rep) {
-        const int leader = __ffsll((long long)pend) - 1;
-        const uint32_t ld = (uint32_t)__shfl((int)dig, leader, 64);
-        const unsigned long long same = __ballot(act && dig == ld);
-        if (lane == leader) atomicAdd(&hist[ld], (uint32_t)__popcll(same));
-        if (act && dig == ld) act = false;
-        pend &= ~same;
-      }
-      if (act) atomicAdd(&hist[dig], 1u);
-    }
-    __syncthreads();
-    // Suffix counts over digits 255..0: thread j < 256 holds digit 255 - j.
-    const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
-    uint32_t incl = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v = (uint32_t)__shfl_up((int)incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    if (tid < 256 && lane == 63) s_wave[tid >> 6] = (int)incl;
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t before = 0;
-      for (int w = 0; w < (tid >> 6); ++w) before += (uint32_t)s_wave[w];
-      incl += before;
-      const uint32_t excl = incl - c;
-      if (excl < remaining && incl >= remaining) {  // exactly one thread
-        s_digit = 255u - (uint32_t)tid;
-        s_above = excl;
-        s_cnt = c;
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    pmask |= 255u << shift;
-    remaining -= s_above;
-    const bool resolved = s_cnt == remaining;  // the whole bin is kept
-    __syncthreads();
-    if (resolved) break;
-  }
-
-  // Keys with (k & pmask) > prefix are kept; of those == prefix, the first
-  // `remaining` in index order.
-  const int per = ((nc + NT - 1) / NT) | 1;
-  const int lo = min(tid * per, nc), hi = min(lo + per, nc);
-  int n_gt = 0, n_eq = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t m = s_key[i] & pmask;
-    n_gt += m > prefix;
-    n_eq += m == prefix;
-  }
-  int tot;
-  const int eq_before = block_exscan<NT>(n_eq, s_wave, &tot);
-  const int take_eq = min(n_eq, max(0, (int)remaining - eq_before));
-  const int sel_before = block_exscan<NT>(n_gt + take_eq, s_wave, &tot);
-  int pos = sel_before, eq_seen = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t m = s_key[i] & pmask;
-    bool keep = m > prefix;
-    if (m == prefix) {
-      keep = eq_seen < take_eq;
-      ++eq_seen;
-    }
-    if (keep) {
-      for (int j = 0; j < r; ++j) s_list[r * pos + j] = r * i + j;
-      ++pos;
-    }
-  }
-  __syncthreads();
-  const int head = r * a.budget;
-  const int len = head + (t + 1) - r * nc;
-  for (int i = tid; i < a.top_k; i += NT)
-    out[i] = i < head ? s_list[i] : (i < len ? r * nc + (i - head) : -1);
-}
+// Radix window of a pass: the first takes 11 bits below the bits shared by
+// every key, later ones 8.
+__device__ __forceinline__ int sel_window(int pass, int top) { return min(pass == 0 ? 11 : 8, top + 1); }
 
 // ---------------------------------------------------------------------------
 // Select + expand, one wave per row (prefill rows with at most 64*KPL
 // complete blocks).  The row's keys live in registers: lane l holds keys
-// 256g + 4l + c (g < KPL/4, c < 4), loaded as float4s.  Histograms are per
-// wave in LDS and scanned with shuffles, so a row needs no workgroup barrier.
-// Emission walks the key groups in index order; wave-wide exclusive scans of
-// the per-lane counts place each kept block, and the list is assembled in
-// LDS and stored in one coalesced pass.
+// 256g + 4l + c (g < KPL/4, c < 4), loaded as float4s; slots past the row's
+// blocks hold 0xffffffff, which no radix prefix matches (real keys have bit
+// 31 clear).  All keys lie in [kmin, kmax] and share the bits above the
+// highest bit where those two differ; the first radix window (11 bits, 2048
+// bins) starts there, later windows take 8 bits.  Histograms are per wave in
+// LDS (plain atomic increments: the adaptive window spreads the digits; four
+// pad words per 32 bins keep the per-lane read-back free of bank conflicts).
+// The cut bin is found by a DPP scan of per-lane bin sums and a second DPP
+// scan inside the one lane range that holds it, so a row needs no workgroup
+// barrier.  The select stops as soon as the cut bin holds exactly the keys
+// still needed (the usual case); otherwise it refines until all 32 bits are
+// fixed and keeps the lowest-index keys among those equal to the cut.  Kept
+// blocks are placed in ascending order by one DPP scan per 256-block group
+// and staged in LDS (when the list fits), then the row is stored with its
+// causal tail and -1 padding in one coalesced pass.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int wave_exscan(int v, int *total) {
-  const int lane = lane_id();
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
-  *total = __shfl(incl, 63, 64);
-  return incl - v;
-}
 
-template <int KPL>
+template <int KPL, bool STAGE>
 __global__ __launch_bounds__(256) void idx_select_wave_kernel(IdxSelectArgs a) {
   constexpr int NG = KPL / 4;
-  __shared__ uint32_t s_hist[4][256];
-  extern __shared__ int32_t s_lists[];  // [4][budget * ratio]
+  extern __shared__ uint32_t s_dyn[];  // per wave: histogram, then the list
   const int wv = threadIdx.x >> 6, lane = lane_id();
   const int row = blockIdx.x * 4 + wv;
   if (row >= a.B * a.S) return;
@@ -472,6 +302,7 @@ __global__ __launch_bounds__(256) void idx_select_wave_kernel(IdxSelectArgs a) {
     for (int i = lane; i < a.top_k; i += 64) out[i] = i <= t ? i : -1;
     return;
   }
+  uint32_t *hist = s_dyn + wv * a.wave_words;
   const float *srow = a.scores + ((size_t)b * a.S + t) * a.row_stride;
   uint32_t key[KPL];
 #pragma unroll
@@ -483,89 +314,85 @@ __global__ __launch_bounds__(256) void idx_select_wave_kernel(IdxSelectArgs a) {
       for (int c = 0; c < 4; ++c) key[4 * g + c] = score_key(v[c]);
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) key[4 * g + c] = i0 + c < nc ? score_key(srow[i0 + c]) : 0u;
+      for (int c = 0; c < 4; ++c) key[4 * g + c] = i0 + c < nc ? score_key(srow[i0 + c]) : 0xffffffffu;
     }
   }
-  uint32_t *hist = s_hist[wv];
-  // All keys lie in [kmin, kmax] and share the bits above the highest bit
-  // where those two differ; the first 8-bit window starts there.
-  uint32_t kmax = 0, kmin = 0xffffffffu;
+  uint32_t kmax = 0, kmin = 0x7fffffffu;
 #pragma unroll
   for (int g = 0; g < NG; ++g)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (256 * g + 4 * lane + c < nc) {
-        kmax = max(kmax, key[4 * g + c]);
-        kmin = min(kmin, key[4 * g + c]);
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t k = key[4 * g + c];
+      if ((int)k >= 0) {
+        kmax = max(kmax, k);
+        kmin = min(kmin, k);
       }
+    }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
   }
   const uint32_t diff = kmax ^ kmin;
-  int top = diff ? 31 - __clz((int)diff) : -1;       // highest differing bit
-  uint32_t pmask = top < 0 ? 0xffffffffu : (top >= 31 ? 0u : ~((2u << top) - 1u));
+  int top = diff ? 31 - __clz((int)diff) : -1;  // highest differing bit (< 31)
+  uint32_t pmask = top < 0 ? 0xffffffffu : ~((2u << top) - 1u);
   uint32_t prefix = kmax & pmask;
   int remaining = a.budget;
-  while (top >= 0) {
-    const int w = min(8, top + 1), shift = top + 1 - w;
+  bool whole_bin = false;
+  for (int pass = 0; top >= 0; ++pass) {
+    const int w = sel_window(pass, top), shift = top + 1 - w;
     const uint32_t dmask = (1u << w) - 1u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
+    const int nb = 1 << w;
+    const int nvec = (hpad(nb - 1) + 4) >> 2;
+    for (int j = lane; j < nvec; j += 64) reinterpret_cast<u32x4 *>(hist)[j] = u32x4{0u, 0u, 0u, 0u};
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      if (256 * g >= nc) break;
+      if (256 * g < nc) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t k = key[4 * g + c];
-        const bool act = (256 * g + 4 * lane + c < nc) && (k & pmask) == prefix;
-        const uint32_t dig = (k >> shift) & dmask;
-        const unsigned long long pend = __ballot(act);
-        if (pend) {
-          // one increment for the first active lane's digit, the most common
-          const int leader = __ffsll((long long)pend) - 1;
-          const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)dig, leader);
-          const unsigned long long same = __ballot(act && dig == ld);
-          if (lane == leader) atomicAdd(&hist[ld], (uint32_t)__popcll(same));
-          if (act && dig != ld) atomicAdd(&hist[dig], 1u);
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t k = key[4 * g + c];
+          if ((k & pmask) == prefix) atomicAdd(&hist[hpad((int)((k >> shift) & dmask))], 1u);
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    // lane l holds digits 255-4l .. 252-4l (descending)
-    uint32_t h[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) h[j] = hist[255 - 4 * lane - j];
-    const int lsum = (int)(h[0] + h[1] + h[2] + h[3]);
-    int tot;
-    const int before = wave_exscan(lsum, &tot);  // keys with a digit above this lane's bins
-    int found = 0, dsel = 0, above = 0, cnt = 0;
-    int acc = before;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (!found && acc < remaining && acc + (int)h[j] >= remaining) {
-        found = 1;
-        dsel = 255 - 4 * lane - j;
-        above = acc;
-        cnt = (int)h[j];
+    // lane l sums bins [nb - per*(l+1), nb - per*l): lane 0 holds the top digits
+    const int per = (nb + 63) >> 6;
+    const int lo = nb - per * (lane + 1);
+    int lsum = 0;
+    if (per >= 4) {
+      for (int j = 0; j < per; j += 4) {
+        const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + hpad(lo + j));
+        lsum += (int)(h[0] + h[1] + h[2] + h[3]);
       }
-      acc += (int)h[j];
+    } else if (lo >= 0) {
+      for (int j = 0; j < per; ++j) lsum += (int)hist[hpad(lo + j)];
     }
-    const int src = __ffsll((long long)__ballot(found)) - 1;
-    dsel = __builtin_amdgcn_readlane(dsel, src);
-    above = __builtin_amdgcn_readlane(above, src);
-    cnt = __builtin_amdgcn_readlane(cnt, src);
+    const int incl = wave_incl_scan(lsum);
+    const int src = __ffsll((long long)__ballot(incl - lsum < remaining && incl >= remaining)) - 1;
+    const int above0 = __builtin_amdgcn_readlane(incl - lsum, src);
+    // inside lane src's range, top digit first
+    const int h = lane < per ? (int)hist[hpad(nb - 1 - (src * per + lane))] : 0;
+    const int incl2 = above0 + wave_incl_scan(h);
+    const int js = __ffsll((long long)__ballot(incl2 - h < remaining && incl2 >= remaining)) - 1;
+    const int dsel = nb - 1 - (src * per + js);
+    const int above = __builtin_amdgcn_readlane(incl2 - h, js);
+    const int cnt = __builtin_amdgcn_readlane(h, js);
     prefix |= (uint32_t)dsel << shift;
     pmask |= dmask << shift;
     remaining -= above;
     __builtin_amdgcn_wave_barrier();
-    if (cnt == remaining) break;  // the whole bin is kept
+    if (cnt == remaining) {  // the whole bin is kept
+      whole_bin = true;
+      break;
+    }
     top = shift - 1;
   }
 
-  int32_t *lst = s_lists + wv * a.budget * r;
+  // Keys with (k & pmask) > prefix are kept; of those == prefix, the first
+  // `remaining` in index order (all of them when whole_bin).
+  int32_t *lst = STAGE ? reinterpret_cast<int32_t *>(hist) : out;
   int kept = 0, eq_seen = 0;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -573,36 +400,248 @@ __global__ __launch_bounds__(256) void idx_select_wave_kernel(IdxSelectArgs a) {
     int gt_m = 0, eq_m = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bool ok = 256 * g + 4 * lane + c < nc;
-      const uint32_t m = key[4 * g + c] & pmask;
-      gt_m |= (ok && m > prefix) << c;
-      eq_m |= (ok && m == prefix) << c;
+      const uint32_t k = key[4 * g + c];
+      const uint32_t m = k & pmask;
+      gt_m |= ((int)k >= 0 && m > prefix) << c;
+      eq_m |= (m == prefix) << c;
     }
-    int eq_tot;
-    int eq_rank = eq_seen + wave_exscan(__popc(eq_m), &eq_tot);
     int keep_m = gt_m;
+    if (whole_bin) {
+      keep_m |= eq_m;
+    } else {
+      const int ec = __popc(eq_m);
+      const int eincl = wave_incl_scan(ec);
+      int eq_rank = eq_seen + eincl - ec;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if ((eq_m >> c) & 1) {
-        if (eq_rank < remaining) keep_m |= 1 << c;
-        ++eq_rank;
-      }
-    int k_tot;
-    int pos = kept + wave_exscan(__popc(keep_m), &k_tot);
+      for (int c = 0; c < 4; ++c)
+        if ((eq_m >> c) & 1) {
+          if (eq_rank < remaining) keep_m |= 1 << c;
+          ++eq_rank;
+        }
+      eq_seen += __builtin_amdgcn_readlane(eincl, 63);
+    }
+    const int kc = __popc(keep_m);
+    const int kincl = wave_incl_scan(kc);
+    int pos = kept + kincl - kc;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       if ((keep_m >> c) & 1) {
-        const int blk = 256 * g + 4 * lane + c;
-        for (int j = 0; j < r; ++j) lst[r * pos + j] = r * blk + j;
+        const int blk = r * (256 * g + 4 * lane + c);
+        if (STAGE && r == 4) {
+          *reinterpret_cast<int4 *>(lst + 4 * pos) = make_int4(blk, blk + 1, blk + 2, blk + 3);
+        } else {
+          for (int j = 0; j < r; ++j) lst[r * pos + j] = blk + j;
+        }
         ++pos;
       }
-    kept += k_tot;
-    eq_seen += eq_tot;
+    kept += __builtin_amdgcn_readlane(kincl, 63);
   }
   __builtin_amdgcn_wave_barrier();
   const int head = r * a.budget;
   const int len = head + (t + 1) - r * nc;
-  for (int i = lane; i < a.top_k; i += 64)
+  for (int i = (STAGE ? 0 : head) + lane; i < a.top_k; i += 64)
+    out[i] = i < head ? lst[i] : (i < len ? r * nc + (i - head) : -1);
+}
+
+// ---------------------------------------------------------------------------
+// Select + expand, one 1024-thread workgroup per row: decode rows (one per
+// sequence, up to 32768 blocks) and prefill rows too long for one wave.
+// Thread j holds the KPT keys of blocks [j*KPT, (j+1)*KPT) in registers, so
+// one workgroup scan of per-thread counts places kept blocks in ascending
+// order.  Passes as in the wave kernel, over one workgroup histogram: a
+// workgroup scan of per-thread bin sums names the thread whose range holds
+// the cut, and that thread walks its own bins.
+// ---------------------------------------------------------------------------
+constexpr int kSelWgThreads = 1024;
+
+// Exclusive prefix sum of v over the workgroup in thread order; s_wt holds
+// one int per wave and is free again on return.
+__device__ __forceinline__ int wg_exscan(int v, int *s_wt, int *total) {
+  constexpr int NW = kSelWgThreads / 64;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) s_wt[wv] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = s_wt[w];
+    before += w < wv ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+template <int KPT, bool STAGE>
+__global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
+  constexpr int NT = kSelWgThreads, NW = NT / 64;
+  extern __shared__ uint32_t s_dyn[];  // padded histogram | list
+  __shared__ int s_wt[NW];
+  __shared__ uint32_t s_red[2 * NW];
+  __shared__ int s_res[3];
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+
+  int b, t, live;
+  int32_t *out;
+  const float *srow;
+  if (a.decode) {
+    b = blockIdx.x;
+    const int c = min(a.ctx[b], a.max_ctx);
+    t = c - 1;
+    live = c > 0;
+    out = a.out + (size_t)b * a.top_k;
+    srow = a.scores + (size_t)b * a.row_stride;
+  } else {
+    const int rw = blockIdx.x;  // longest rows first
+    b = rw % a.B;
+    t = a.S - 1 - rw / a.B;
+    live = t < min(a.ctx[b], a.S);
+    out = a.out + ((size_t)b * a.S + t) * a.top_k;
+    srow = a.scores + ((size_t)b * a.S + t) * a.row_stride;
+  }
+  if (!live) {
+    for (int i = tid; i < a.top_k; i += NT) out[i] = -1;
+    return;
+  }
+  const int r = a.ratio;
+  const int nc = (t + 1) / r;
+  if (nc <= a.budget) {  // every complete block is kept: the list is 0..t
+    for (int i = tid; i < a.top_k; i += NT) out[i] = i <= t ? i : -1;
+    return;
+  }
+  uint32_t *hist = s_dyn;
+  int32_t *lst = STAGE ? reinterpret_cast<int32_t *>(s_dyn + kSelHistWords) : out;
+
+  uint32_t key[KPT];
+  const int i0 = tid * KPT;
+#pragma unroll
+  for (int j = 0; j < KPT; j += 4) {
+    const int i = i0 + j;
+    if (i + 3 < nc) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + i);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[j + c] = score_key(v[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[j + c] = i + c < nc ? score_key(srow[i + c]) : 0xffffffffu;
+    }
+  }
+  uint32_t kmax = 0, kmin = 0x7fffffffu;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if ((int)key[j] >= 0) {
+      kmax = max(kmax, key[j]);
+      kmin = min(kmin, key[j]);
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+  }
+  if (lane == 0) {
+    s_red[wv] = kmax;
+    s_red[NW + wv] = kmin;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    kmax = max(kmax, s_red[w]);
+    kmin = min(kmin, s_red[NW + w]);
+  }
+  const uint32_t diff = kmax ^ kmin;
+  int top = diff ? 31 - __clz((int)diff) : -1;  // highest differing bit (< 31)
+  uint32_t pmask = top < 0 ? 0xffffffffu : ~((2u << top) - 1u);
+  uint32_t prefix = kmax & pmask;
+  int remaining = a.budget;
+  bool whole_bin = false;
+  for (int pass = 0; top >= 0; ++pass) {
+    const int w = sel_window(pass, top), shift = top + 1 - w;
+    const uint32_t dmask = (1u << w) - 1u;
+    const int nb = 1 << w;
+    const int nvec = (hpad(nb - 1) + 4) >> 2;
+    for (int j = tid; j < nvec; j += NT) reinterpret_cast<u32x4 *>(hist)[j] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t k = key[j];
+      if ((k & pmask) == prefix) atomicAdd(&hist[hpad((int)((k >> shift) & dmask))], 1u);
+    }
+    __syncthreads();
+    // thread j sums bins [nb - per*(j+1), nb - per*j): thread 0 the top digits
+    const int per = nb > NT ? nb / NT : 1;
+    const int lo = nb - per * (tid + 1);
+    int lsum = 0;
+    if (lo >= 0)
+      for (int j = 0; j < per; ++j) lsum += (int)hist[hpad(lo + j)];
+    int tot;
+    const int excl = wg_exscan(lsum, s_wt, &tot);
+    if (lsum > 0 && excl < remaining && excl + lsum >= remaining) {  // exactly one thread
+      int acc = excl;
+      for (int j = per - 1; j >= 0; --j) {
+        const int h = (int)hist[hpad(lo + j)];
+        if (acc + h >= remaining) {
+          s_res[0] = lo + j;
+          s_res[1] = acc;
+          s_res[2] = h;
+          break;
+        }
+        acc += h;
+      }
+    }
+    __syncthreads();
+    const int dsel = __builtin_amdgcn_readfirstlane(s_res[0]);
+    const int above = __builtin_amdgcn_readfirstlane(s_res[1]);
+    const int cnt = __builtin_amdgcn_readfirstlane(s_res[2]);
+    prefix |= (uint32_t)dsel << shift;
+    pmask |= dmask << shift;
+    remaining -= above;
+    if (cnt == remaining) {  // the whole bin is kept
+      whole_bin = true;
+      break;
+    }
+    top = shift - 1;
+  }
+
+  // Keys with (k & pmask) > prefix are kept; of those == prefix, the first
+  // `remaining` in index order (all of them when whole_bin).
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t m = key[j] & pmask;
+    n_gt += (int)key[j] >= 0 && m > prefix;
+    n_eq += m == prefix;
+  }
+  int tot, take_eq = n_eq;
+  if (!whole_bin) {
+    const int eq_before = wg_exscan(n_eq, s_wt, &tot);
+    take_eq = min(n_eq, max(0, remaining - eq_before));
+  }
+  int pos = wg_exscan(n_gt + take_eq, s_wt, &tot);
+  int eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t m = key[j] & pmask;
+    bool keep = (int)key[j] >= 0 && m > prefix;
+    if (m == prefix) {
+      keep = eq_seen < take_eq;
+      ++eq_seen;
+    }
+    if (keep) {
+      const int blk = r * (i0 + j);
+      if (STAGE && r == 4) {
+        *reinterpret_cast<int4 *>(lst + 4 * pos) = make_int4(blk, blk + 1, blk + 2, blk + 3);
+      } else {
+        for (int q = 0; q < r; ++q) lst[r * pos + q] = blk + q;
+      }
+      ++pos;
+    }
+  }
+  __syncthreads();
+  const int head = r * a.budget;
+  const int len = head + (t + 1) - r * nc;
+  for (int i = (STAGE ? 0 : head) + tid; i < a.top_k; i += NT)
     out[i] = i < head ? lst[i] : (i < len ? r * nc + (i - head) : -1);
 }
 
@@ -746,41 +785,47 @@ hipError_t launch_idx_score(const IdxScoreArgs &a_in, int dt, hipStream_t s) {
 }
 
 template <int KPL>
-static void launch_select_wave(const IdxSelectArgs &a, hipStream_t s) {
+static void launch_select_wave(IdxSelectArgs a, hipStream_t s) {
   const unsigned grid = (unsigned)(((long long)a.B * a.S + 3) / 4);
-  const size_t lds = (size_t)4 * a.budget * a.ratio * sizeof(int32_t);
-  if (lds > 65536)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&idx_select_wave_kernel<KPL>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(idx_select_wave_kernel<KPL>, dim3(grid), dim3(256), lds, s, a);
+  // Lists of up to 8192 ids are staged in LDS (over the histogram), longer
+  // ones are written straight to the output.
+  const int list_words = (a.budget * a.ratio + 3) & ~3;
+  const bool stage = list_words <= 8192;
+  a.wave_words = stage ? max(kSelHistWords, list_words) : kSelHistWords;
+  const size_t lds = (size_t)4 * a.wave_words * sizeof(uint32_t);
+  const void *fn = stage ? reinterpret_cast<const void *>(&idx_select_wave_kernel<KPL, true>)
+                         : reinterpret_cast<const void *>(&idx_select_wave_kernel<KPL, false>);
+  if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (stage) hipLaunchKernelGGL((idx_select_wave_kernel<KPL, true>), dim3(grid), dim3(256), lds, s, a);
+  else hipLaunchKernelGGL((idx_select_wave_kernel<KPL, false>), dim3(grid), dim3(256), lds, s, a);
 }
 
-hipError_t launch_idx_select(const IdxSelectArgs &a_in, int nc_max, hipStream_t s) {
-  IdxSelectArgs a = a_in;
-  if (!a.decode && nc_max <= 64 * 128) {  // prefill rows fit in registers
+template <int KPT>
+static void launch_select_wg(IdxSelectArgs a, unsigned rows, hipStream_t s) {
+  const int list_words = (a.budget * a.ratio + 3) & ~3;
+  const bool stage = list_words <= 16384;
+  const size_t lds = (size_t)(kSelHistWords + (stage ? list_words : 0)) * sizeof(uint32_t);
+  const void *fn = stage ? reinterpret_cast<const void *>(&idx_select_wg_kernel<KPT, true>)
+                         : reinterpret_cast<const void *>(&idx_select_wg_kernel<KPT, false>);
+  if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (stage) hipLaunchKernelGGL((idx_select_wg_kernel<KPT, true>), dim3(rows), dim3(kSelWgThreads), lds, s, a);
+  else hipLaunchKernelGGL((idx_select_wg_kernel<KPT, false>), dim3(rows), dim3(kSelWgThreads), lds, s, a);
+}
+
+hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) {
+  if (!a.decode && nc_max <= 64 * 128) {  // prefill rows that fit one wave's registers
     if (nc_max <= 64 * 32) launch_select_wave<32>(a, s);
     else if (nc_max <= 64 * 64) launch_select_wave<64>(a, s);
     else launch_select_wave<128>(a, s);
     return hipGetLastError();
   }
+  // one workgroup per row; at most QSA_MAX_BLOCKS = 32 * 1024 blocks
   const unsigned rows = (unsigned)(a.decode ? a.B : (long long)a.B * a.S);
-  const int nt = a.decode ? 1024 : 256;
-  // keys padded to a whole number of (odd) per-thread ranges, then the list
-  const int per = ((nc_max + nt - 1) / nt) | 1;
-  a.key_cap = per * nt;
-  const size_t lds = ((size_t)a.key_cap + (size_t)a.budget * a.ratio) * sizeof(uint32_t);
-  // Decode has one long row per sequence: a wide workgroup per row.
-  if (a.decode) {
-    if (lds > 65536)
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&idx_select_kernel<1024>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(idx_select_kernel<1024>, dim3(rows), dim3(1024), lds, s, a);
-  } else {
-    if (lds > 65536)
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&idx_select_kernel<256>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(idx_select_kernel<256>, dim3(rows), dim3(256), lds, s, a);
-  }
+  const int kpt = (nc_max + kSelWgThreads - 1) / kSelWgThreads;
+  if (kpt <= 4) launch_select_wg<4>(a, rows, s);
+  else if (kpt <= 8) launch_select_wg<8>(a, rows, s);
+  else if (kpt <= 16) launch_select_wg<16>(a, rows, s);
+  else launch_select_wg<32>(a, rows, s);
   return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ struct IdxSelectArgs {
   int top_k, budget, ratio;
   int decode;          // 1: row of sequence b is position ctx[b]-1
   int max_ctx;         // decode: clamp of ctx (max_pages * 128)
-  int key_cap;         // LDS key slots (set by the launcher)
+  int wave_words;      // wave-per-row kernel: LDS words per wave (set by the launcher)
 };
 
 struct IdxDecPrepArgs {
