@@ -290,7 +290,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "sparse_prefill_kernel",
                      "achieved": pf["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf["achieved_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
-                     "algorithmic_bytes_per_launch": pf["attn_bytes"]},
+                     "algorithmic_bytes_per_call": pf["attn_bytes"]},
         "cpu_baseline": cpu,
         "decode": dec,
     }

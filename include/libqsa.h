@@ -105,7 +105,7 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t top_k;
-  float attention_scale; /* multiplies q.k; not assumed to be 1/sqrt(D) */
+  float attention_scale; /* multiplies q.k; finite and > 0, not assumed to be 1/sqrt(D) */
   qsa_dtype dtype;
   void *stream;
 } qsa_sparse_prefill_params;
@@ -147,7 +147,7 @@ typedef struct {
   int32_t max_pages_per_seq;
   int32_t top_k;
   int32_t num_splits;
-  float attention_scale;
+  float attention_scale;    /* finite and > 0 */
   qsa_dtype dtype;
   void *stream;
 } qsa_sparse_decode_params;

@@ -114,6 +114,7 @@ def _idecode(**kw):
     (dict(dtype=2), UNSUP), (dict(batch=0), SHAPE), (dict(seq_len=0), SHAPE), (dict(top_k=0), SHAPE),
     (dict(num_q_heads=7), SHAPE), (dict(num_q_heads=34), UNSUP), (dict(head_dim=96), UNSUP),
     (dict(num_kv_heads=0), SHAPE), (dict(q=FAKE + 8), SHAPE), (dict(attention_scale=float("inf")), SHAPE),
+    (dict(attention_scale=0.0), SHAPE), (dict(attention_scale=-0.125), SHAPE), (dict(attention_scale=float("nan")), SHAPE),
 ])
 def test_sparse_prefill_rejects(no_gpu, kw, status):
     assert _prefill(**kw) == status
@@ -124,7 +125,7 @@ def test_sparse_prefill_rejects(no_gpu, kw, status):
     (dict(dtype=-1), UNSUP), (dict(batch=0), SHAPE), (dict(num_flat_pages=0), SHAPE),
     (dict(pool_head_dim=120), SHAPE), (dict(pool_head_dim=130), SHAPE), (dict(num_splits=17), SHAPE),
     (dict(num_splits=-1), SHAPE), (dict(max_pages_per_seq=5000), UNSUP), (dict(num_q_heads=33), SHAPE),
-    (dict(kv_pool=FAKE + 4), SHAPE), (dict(head_dim=256), UNSUP),
+    (dict(kv_pool=FAKE + 4), SHAPE), (dict(head_dim=256), UNSUP), (dict(attention_scale=0.0), SHAPE),
 ])
 def test_sparse_decode_rejects(no_gpu, kw, status):
     assert _decode(**kw) == status

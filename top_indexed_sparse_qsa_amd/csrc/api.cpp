@@ -135,7 +135,7 @@ qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p) {
   if ((int64_t)p->batch * p->seq_len * p->num_kv_heads > (int64_t)INT32_MAX - 4) return QSA_ERR_UNSUPPORTED;
   // one sequence's K (or V) is addressed with 32-bit byte offsets
   if ((int64_t)p->seq_len * p->num_kv_heads * p->head_dim * 2 >= ((int64_t)1 << 32)) return QSA_ERR_UNSUPPORTED;
-  if (!isfinite(p->attention_scale)) return QSA_ERR_BAD_SHAPE;
+  if (!isfinite(p->attention_scale) || !(p->attention_scale > 0.f)) return QSA_ERR_BAD_SHAPE;
   qsa::PrefillAttnArgs a;
   a.q = static_cast<const uint16_t *>(p->q);
   a.k = static_cast<const uint16_t *>(p->k);
@@ -165,7 +165,7 @@ qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
   if (p->max_pages_per_seq > 4096) return QSA_ERR_UNSUPPORTED;
   if (p->num_splits < 0 || p->num_splits > QSA_MAX_SPLITS) return QSA_ERR_BAD_SHAPE;
   if ((int64_t)p->batch * p->num_kv_heads * QSA_MAX_SPLITS > (int64_t)INT32_MAX) return QSA_ERR_UNSUPPORTED;
-  if (!isfinite(p->attention_scale)) return QSA_ERR_BAD_SHAPE;
+  if (!isfinite(p->attention_scale) || !(p->attention_scale > 0.f)) return QSA_ERR_BAD_SHAPE;
   int splits = p->num_splits ? p->num_splits : default_splits(p->batch, p->num_kv_heads, p->top_k);
   const int chunks = (p->top_k + 31) / 32;
   const int per = (chunks + splits - 1) / splits;

@@ -48,17 +48,24 @@ __device__ __forceinline__ float bits_to_f32_t(uint32_t h) {
   else return __uint_as_float(h << 16);
 }
 
-// float -> 16-bit, round to nearest even.
+// float -> 16-bit, round to nearest even (gfx950 converts in one
+// instruction, two values at a time with pack2).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 template <int DT>
 __device__ __forceinline__ uint32_t f32_to_bits(float x) {
-  if constexpr (DT == DT_F16) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
-  } else {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-  }
+  if constexpr (DT == DT_F16) return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+  else return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Two floats -> two 16-bit values packed low | high << 16.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  if constexpr (DT == DT_F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ uint32_t f32_to_bits_rt(float x, int dt) {

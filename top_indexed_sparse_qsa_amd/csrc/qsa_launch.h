@@ -13,6 +13,7 @@ struct PrefillAttnArgs {
   const int32_t *indices, *ctx;
   int B, S, Hq, Hkv, G, top_k;
   float sl2;  // attention scale * log2(e)
+  int row0, nrows;  // this launch covers rows [row0, row0 + nrows) of the work order
 };
 
 struct DecodeAttnArgs {

@@ -38,6 +38,7 @@ struct Frag {
   u32x4 kf[8];       // K rows of the lane's eight key slots, dims 8c..8c+7
   u32x4 vf[8];       // V rows of the lane's eight key slots, dims 8c..8c+7
   uint32_t valid;    // bit i: key slot i of this lane is usable
+  bool full;         // every key slot of the wave is usable (wave-uniform)
 };
 
 // Key slot i of lane group q: keys 4q+i (i < 4) and 16+4q+(i-4) (i >= 4).
@@ -51,7 +52,8 @@ struct DenseKV {
   uint32_t row_bytes;     // bytes between consecutive tokens
   int limit;              // ids in [0, limit) are usable
   __device__ void load(int id, int r16, u32x4 &kd, u32x4 &vd) const {
-    const uint32_t off = (uint32_t)id * row_bytes + 16u * (uint32_t)r16;
+    // ids < 2^24 and row_bytes < 2^24: one full-rate 24-bit multiply
+    const uint32_t off = __umul24((uint32_t)id, row_bytes) + 16u * (uint32_t)r16;
     kd = ld16(k + off);
     vd = ld16(v + off);
   }
@@ -74,28 +76,62 @@ struct PagedKV {
   }
 };
 
+// Lanes l and l + 32 hold the id of list slot l % 32; invalid ids become 0
+// (a harmless row to load) and are masked by the validity bits.
 template <int D, int DT, class KV>
 __device__ __forceinline__ void issue_chunk(Frag<D> &f, int idv, const KV &kv, int q4, int r16) {
-  uint32_t valid = 0;
+  const bool ok = (unsigned)idv < (unsigned)kv.limit;
+  const int sidv = ok ? idv : 0;
+  const uint32_t bal = (uint32_t)__ballot(ok);  // bit s: list slot s is usable
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int id = shfl_i(idv, slot_of(q4, i));
-    bool ok = (unsigned)id < (unsigned)kv.limit;
-    valid |= (uint32_t)ok << i;
-    const int sid = ok ? id : 0;
+    const int id = shfl_i(sidv, slot_of(q4, i));
     if (D == 128 || r16 < D / 8) {
-      kv.load(sid, r16, f.kf[i], f.vf[i]);
+      kv.load(id, r16, f.kf[i], f.vf[i]);
     } else {
       f.kf[i] = u32x4{0u, 0u, 0u, 0u};
       f.vf[i] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  f.valid = valid;
+  // key slots 0-3 are list slots 4q.., 4-7 are 16+4q..
+  f.valid = ((bal >> (4 * q4)) & 0xfu) | (((bal >> (16 + 4 * q4)) & 0xfu) << 4);
+  f.full = bal == 0xffffffffu;
+}
+
+// Online-softmax bookkeeping.  m_run is the reference the probabilities are
+// taken against; it is raised only when a chunk's max exceeds it by more
+// than 2^kLazyLog2 (in the exp2 domain), so most chunks skip the rescale of
+// the accumulators, and a probability is at most 2^kLazyLog2.  The row sum
+// adds the same 16-bit rounded probabilities the PV product uses, two at a
+// time with packed dot products against (1, 1).
+constexpr float kLazyLog2 = 8.f;
+
+// Max with lane l ^ 16 / l ^ 32 by the gfx950 lane swaps (no LDS round
+// trip): one of the two swapped copies holds the partner, the other the
+// lane itself.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
+template <int DT>
+__device__ __forceinline__ float add_pair(uint32_t p2, float acc) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p2), __builtin_bit_cast(f16x2_t, 0x3C003C00u), acc,
+                                  false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p2),
+                                           __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
 }
 
 // Per-wave LDS tile for one chunk of K: 32 rows of 256 B, 16-byte pieces
 // XOR-swizzled by row so that both the row writes and the fragment reads are
-// free of bank conflicts.
+// free of bank conflicts.  sl2 (scale * log2 e) is positive, so the max of
+// the unscaled scores, times sl2, is the max of the scaled ones.
 template <int D, int DT>
 __device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf)[D / 32], float sl2,
                                               float &m_run, float &l_run, f32x4 (&acc)[8], u32x4 *ktile) {
@@ -118,30 +154,35 @@ __device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[i] = ((f.valid >> i) & 1u) ? s0[i] * sl2 : -INFINITY;
-    x[4 + i] = ((f.valid >> (4 + i)) & 1u) ? s1[i] * sl2 : -INFINITY;
+    x[i] = s0[i];
+    x[4 + i] = s1[i];
+  }
+  if (!f.full) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = ((f.valid >> i) & 1u) ? x[i] : -INFINITY;
   }
   float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  mx = fmaxf(mx, shfl_xor_f(mx, 16));
-  mx = fmaxf(mx, shfl_xor_f(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = exp2f(m_run - m_use);
-  uint32_t pb[4];
-  float psum = 0.f;
+  mx = max_xor16(mx);
+  mx = max_xor32(mx);
+  mx *= sl2;
+  if (wave_any(mx > m_run + kLazyLog2)) {
+    // m_new is finite on every lane: all heads see the same (>= 1) usable keys
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    m_run = m_new;
+  }
+  u32x4 bop;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t h0 = f32_to_bits<DT>(exp2f(x[2 * w] - m_use));
-    uint32_t h1 = f32_to_bits<DT>(exp2f(x[2 * w + 1] - m_use));
-    psum += bits_to_f32_t<DT>(h0) + bits_to_f32_t<DT>(h1);  // normalise by the rounded weights
-    pb[w] = h0 | (h1 << 16);
+    bop[w] = pack2<DT>(__builtin_amdgcn_exp2f(fmaf(x[2 * w], sl2, -m_run)),
+                       __builtin_amdgcn_exp2f(fmaf(x[2 * w + 1], sl2, -m_run)));
+    l_run = add_pair<DT>(bop[w], l_run);
   }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-  const u32x4 bop = {pb[0], pb[1], pb[2], pb[3]};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    acc[e] *= alpha;
     u32x4 a;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -219,13 +260,14 @@ __device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int &b, i
     const int per_head = 8 / a.Hkv;  // XCDs sharing one KV head
     kvh = xcd % a.Hkv;
     rest = ((n * per_head + xcd / a.Hkv) << 2) + wave;
-    if (rest >= a.B * a.S) return false;
+    if (rest >= a.nrows) return false;
   } else {
     const int item = blockIdx.x * 4 + wave;
-    if (item >= a.B * a.S * a.Hkv) return false;
+    if (item >= a.nrows * a.Hkv) return false;
     kvh = item % a.Hkv;
     rest = item / a.Hkv;
   }
+  rest += a.row0;
   b = rest / a.S;
   t = a.S - 1 - rest % a.S;
   return true;
@@ -233,11 +275,30 @@ __device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int &b, i
 
 static unsigned prefill_grid(const PrefillAttnArgs &a) {
   if ((8 % a.Hkv) == 0) {
-    const long long quads = ((long long)a.B * a.S + 3) / 4;
+    const long long quads = ((long long)a.nrows + 3) / 4;
     const long long per_head = 8 / a.Hkv;
     return (unsigned)(8 * ((quads + per_head - 1) / per_head));
   }
-  return (unsigned)(((long long)a.B * a.S * a.Hkv + 3) / 4);
+  return (unsigned)(((long long)a.nrows * a.Hkv + 3) / 4);
+}
+
+// Every list is walked in ascending id order, so waves that start together
+// touch nearby K/V rows at the same time and share them through L2.  When a
+// KV head's K/V is well past one XCD's L2, that sharing depends on the waves
+// staying in step, and they drift apart over successive generations of
+// workgroups; splitting the rows into launches of about kSyncWaves waves
+// starts every launch in step again.
+constexpr size_t kL2BytesPerXcd = 4u << 20;
+#ifndef QSA_PREFILL_SYNC_WAVES
+#define QSA_PREFILL_SYNC_WAVES 8192
+#endif
+constexpr int kSyncWaves = QSA_PREFILL_SYNC_WAVES;
+
+static int prefill_rows_per_launch(const PrefillAttnArgs &a, int D) {
+  const int total = a.B * a.S;
+  const size_t head_kv_bytes = (size_t)a.S * 2 * D * sizeof(uint16_t);
+  if (head_kv_bytes <= 2 * kL2BytesPerXcd) return total;
+  return max(64, kSyncWaves / a.Hkv);
 }
 
 template <int D, int DT>
@@ -274,7 +335,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       u32x4 w;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        w[j] = f32_to_bits<DT>(acc[2 * j][rr] * inv) | (f32_to_bits<DT>(acc[2 * j + 1][rr] * inv) << 16);
+        w[j] = pack2<DT>(acc[2 * j][rr] * inv, acc[2 * j + 1][rr] * inv);
       st16(dst + 8 * rr, w);
     }
   }
@@ -392,7 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int j = 0; j < ND; j += 2)
         *reinterpret_cast<uint32_t *>(out + j) =
-            f32_to_bits<DT>(o[j] * inv) | (f32_to_bits<DT>(o[j + 1] * inv) << 16);
+            pack2<DT>(o[j] * inv, o[j + 1] * inv);
     } else {
       float *po = a.part_o + (slot * 16 + r16) * D + d0;
 #pragma unroll
@@ -441,15 +502,23 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
     u32x4 w;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      w[k] = f32_to_bits<DT>(o[j + 2 * k] * inv) | (f32_to_bits<DT>(o[j + 2 * k + 1] * inv) << 16);
+      w[k] = pack2<DT>(o[j + 2 * k] * inv, o[j + 2 * k + 1] * inv);
     st16(out + j, w);
   }
 }
 
 template <int D, int DT>
 static hipError_t launch_prefill_t(const PrefillAttnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((sparse_prefill_kernel<D, DT>), dim3(prefill_grid(a)), dim3(256), 0, s, a);
-  return hipGetLastError();
+  const int total = a.B * a.S, per = prefill_rows_per_launch(a, D);
+  for (int r0 = 0; r0 < total; r0 += per) {
+    PrefillAttnArgs p = a;
+    p.row0 = r0;
+    p.nrows = min(per, total - r0);
+    hipLaunchKernelGGL((sparse_prefill_kernel<D, DT>), dim3(prefill_grid(p)), dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStream_t s) {
