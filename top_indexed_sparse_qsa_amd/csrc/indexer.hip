@@ -14,6 +14,8 @@
 // 1/sqrt(hd): a positive factor does not change which blocks win.
 #include <math.h>
 
+#include <algorithm>
+
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -21,64 +23,100 @@ namespace qsa {
 
 __device__ __forceinline__ double bits_to_f64(uint32_t h, int dt) { return (double)bits_to_f32(h, dt); }
 
-// Sum over the block (blockDim.x = 128 = two waves).
-__device__ __forceinline__ double block_sum128(double v, double *red) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  __syncthreads();
-  if (lane_id() == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return red[0] + red[1];
+// One 128-vector per wave: lane l holds dims l and l + 64.  RoPE pairs dims
+// (i, i + rot/2) and turns them by pos * theta^(-2i/rot); dims >= rot pass
+// through.  The frequencies come from a per-workgroup table, and the
+// cos/sin of one position serve every head at that position.
+struct Rope2 {
+  double c0, s0, c1, s1;  // rotation of dims lane and lane + 64
+};
+
+__device__ __forceinline__ void fill_freq(double *s_freq, int rot, double theta) {
+  for (int i = threadIdx.x; i < (rot >> 1); i += blockDim.x) s_freq[i] = pow(theta, (-2.0 * (double)i) / (double)rot);
 }
 
-// y = RoPE_pos(x / sqrt(mean(x^2) + eps) * (1 + w)) for one 128-vector held one
-// element per thread.  Pairs (i, i + rot/2), angle pos * theta^(-2i/rot).
-__device__ double norm_rope(double x, double w, double pos, int rot, double theta, double eps,
-                            double *sx, double *red) {
-  const int d = threadIdx.x;
-  const double ms = block_sum128(x * x, red) / 128.0;
-  const double y = x / sqrt(ms + eps) * (1.0 + w);
-  sx[d] = y;
-  __syncthreads();
-  const int half = rot >> 1;
-  double out = y;
-  if (d < rot) {
-    const int i = d < half ? d : d - half;
-    const double ang = pos * pow(theta, (-2.0 * (double)i) / (double)rot);
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    out = d < half ? y * cs - sx[d + half] * sn : y * cs + sx[d - half] * sn;
-  }
-  __syncthreads();
-  return out;
-}
-
-// grid: B*S query rows, then B*Gmax blocks; block: 128 threads (hd = 128).
-__global__ __launch_bounds__(128) void idx_prep_kernel(IdxPrepArgs a) {
-  __shared__ double sx[128];
-  __shared__ double red[2];
-  const int d = threadIdx.x;
-  const long long nrows = (long long)a.B * a.S;
-  const long long bid = blockIdx.x;
-  if (bid < nrows) {
-    const int b = (int)(bid / a.S), t = (int)(bid % a.S);
-    if (t >= min(a.ctx[b], a.S)) return;
-    const double w = (double)a.wq[d];
-    for (int h = 0; h < a.Hi; ++h) {
-      const size_t off = ((size_t)bid * a.Hi + h) * 128 + d;
-      const double x = bits_to_f64(a.idx_q[off], a.dt);
-      a.qhat[off] = (float)norm_rope(x, w, (double)t, a.rot, a.theta, a.eps, sx, red);
+__device__ __forceinline__ Rope2 rope_at(double pos, const double *s_freq, int rot) {
+  const int lane = lane_id(), half = rot >> 1;
+  Rope2 r{1.0, 0.0, 1.0, 0.0};
+  const int d0 = lane, d1 = lane + 64;
+  const int i0 = d0 < half ? d0 : d0 - half, i1 = d1 < half ? d1 : d1 - half;
+  if (d0 < rot) sincos(pos * s_freq[i0], &r.s0, &r.c0);
+  if (d1 < rot) {
+    if (d0 < rot && i1 == i0) {
+      r.c1 = r.c0;
+      r.s1 = r.s0;
+    } else {
+      sincos(pos * s_freq[i1], &r.s1, &r.c1);
     }
-  } else {
-    const long long k = bid - nrows;
-    const int b = (int)(k / a.Gmax), g = (int)(k % a.Gmax);
-    if (g >= min(a.ctx[b], a.S) / a.ratio) return;
-    double m = 0.0;
-    for (int j = 0; j < a.ratio; ++j)
-      m += bits_to_f64(a.idx_k[((size_t)b * a.S + (size_t)a.ratio * g + j) * 128 + d], a.dt);
-    m /= (double)a.ratio;
-    const double y = norm_rope(m, (double)a.wk[d], (double)a.ratio * g, a.rot, a.theta, a.eps, sx, red);
-    a.kbar[((size_t)b * a.Gmax + g) * 128 + d] = (uint16_t)f64_to_bits(y, a.dt);
+  }
+  return r;
+}
+
+// (o0, o1) = RoPE(x / sqrt(mean(x^2) + eps) * (1 + w)) for the lane's two dims.
+__device__ __forceinline__ void norm_rope2(double x0, double x1, double w0, double w1, double eps, int rot,
+                                           const Rope2 &r, double &o0, double &o1) {
+  double ss = x0 * x0 + x1 * x1;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  const double den = sqrt(ss / 128.0 + eps);
+  const double y0 = x0 / den * (1.0 + w0), y1 = x1 / den * (1.0 + w1);
+  const int lane = lane_id(), half = rot >> 1;
+  const int d0 = lane, d1 = lane + 64;
+  const int q0 = d0 < rot ? (d0 < half ? d0 + half : d0 - half) : d0;
+  const int q1 = d1 < rot ? (d1 < half ? d1 + half : d1 - half) : d1;
+  const double a0 = __shfl(y0, q0 & 63, 64), b0 = __shfl(y1, q0 & 63, 64);
+  const double a1 = __shfl(y0, q1 & 63, 64), b1 = __shfl(y1, q1 & 63, 64);
+  const double p0 = (q0 >> 6) ? b0 : a0, p1 = (q1 >> 6) ? b1 : a1;
+  o0 = d0 < rot ? (d0 < half ? y0 * r.c0 - p0 * r.s0 : y0 * r.c0 + p0 * r.s0) : y0;
+  o1 = d1 < rot ? (d1 < half ? y1 * r.c1 - p1 * r.s1 : y1 * r.c1 + p1 * r.s1) : y1;
+}
+
+// Items: B*S query rows, then B*Gmax blocks; a.per_wave consecutive items
+// per wave (up to kPrepItemsPerWave, fewer when that would leave the chip
+// short of waves), four waves per workgroup.
+constexpr int kPrepItemsPerWave = 4;
+
+__global__ __launch_bounds__(256) void idx_prep_kernel(IdxPrepArgs a) {
+  __shared__ double s_freq[64];
+  fill_freq(s_freq, a.rot, a.theta);
+  __syncthreads();
+  const int lane = lane_id();
+  const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long nrows = (long long)a.B * a.S, total = nrows + (long long)a.B * a.Gmax;
+  const double wq0 = a.wq[lane], wq1 = a.wq[lane + 64], wk0 = a.wk[lane], wk1 = a.wk[lane + 64];
+  for (int k = 0; k < a.per_wave; ++k) {
+    const long long item = wave * a.per_wave + k;
+    if (item >= total) break;
+    double o0, o1;
+    if (item < nrows) {
+      const int b = (int)(item / a.S), t = (int)(item % a.S);
+      if (t >= min(a.ctx[b], a.S)) continue;
+      const Rope2 r = rope_at((double)t, s_freq, a.rot);
+      for (int h = 0; h < a.Hi; ++h) {
+        const size_t off = ((size_t)item * a.Hi + h) * 128;
+        norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt), wq0, wq1,
+                   a.eps, a.rot, r, o0, o1);
+        a.qhat[off + lane] = (float)o0;
+        a.qhat[off + 64 + lane] = (float)o1;
+      }
+    } else {
+      const long long kk = item - nrows;
+      const int b = (int)(kk / a.Gmax), g = (int)(kk % a.Gmax);
+      if (g >= min(a.ctx[b], a.S) / a.ratio) continue;
+      double m0 = 0.0, m1 = 0.0;
+      for (int j = 0; j < a.ratio; ++j) {
+        const size_t off = ((size_t)b * a.S + (size_t)a.ratio * g + j) * 128;
+        m0 += bits_to_f64(a.idx_k[off + lane], a.dt);
+        m1 += bits_to_f64(a.idx_k[off + 64 + lane], a.dt);
+      }
+      m0 /= (double)a.ratio;
+      m1 /= (double)a.ratio;
+      const Rope2 r = rope_at((double)a.ratio * g, s_freq, a.rot);
+      norm_rope2(m0, m1, wk0, wk1, a.eps, a.rot, r, o0, o1);
+      const size_t ob = ((size_t)b * a.Gmax + g) * 128;
+      a.kbar[ob + lane] = (uint16_t)f64_to_bits(o0, a.dt);
+      a.kbar[ob + 64 + lane] = (uint16_t)f64_to_bits(o1, a.dt);
+    }
   }
 }
 
@@ -113,8 +151,8 @@ __device__ __forceinline__ void load8f(float (&x)[8], const float *p) {
 
 // Prefill scoring.  A workgroup takes 32 consecutive rows and a run of up to
 // kScoreChunksPerGroup chunks of kScoreChunk complete blocks (rows' queries
-// are loaded and split once per run); runs of the last rows are dispatched
-// first.  Per chunk the kbar rows are staged in LDS, 16-byte pieces
+// are loaded and split once per run; short prefills take shorter runs so the
+// grid still fills the chip); runs of the last rows are dispatched first.  Per chunk the kbar rows are staged in LDS, 16-byte pieces
 // XOR-swizzled by row so that MFMA fragment reads are conflict-free; each wave
 // computes 8 rows against the chunk.  The MFMA M tile is (row, head) with the
 // head fastest, so each 16-lane group ends with the four head dots of one row
@@ -138,8 +176,8 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
   const int live = min(a.ctx[b], a.S);
   if (tg >= live) return;
   const int nc_hi = (min(tg + 31, live - 1) + 1) / a.ratio;
-  const int run_lo = run * kScoreChunksPerGroup * CB;
-  const int run_hi = min(run_lo + kScoreChunksPerGroup * CB, nc_hi);
+  const int run_lo = run * a.run_chunks * CB;
+  const int run_hi = min(run_lo + a.run_chunks * CB, nc_hi);
   if (run_lo >= run_hi) return;
 
   const int t0 = tg + 8 * wv;
@@ -646,7 +684,7 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode B1: queries at p = ctx-1 and the tail update.  grid B, block 128.
+// Decode B1: queries at p = ctx-1 and the tail update.  One wave per sequence.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ long long pool_row_off(const int32_t *ptrow, int token, int max_pages,
                                                   int num_flat_pages, int Hkv, int PHD) {
@@ -657,40 +695,60 @@ __device__ __forceinline__ long long pool_row_off(const int32_t *ptrow, int toke
   return (((long long)pg * 128 + (token & 127)) * Hkv) * PHD;
 }
 
-__global__ __launch_bounds__(128) void idx_dec_prep_kernel(IdxDecPrepArgs a) {
-  __shared__ double sx[128];
-  __shared__ double red[2];
-  const int b = blockIdx.x, d = threadIdx.x;
+__global__ __launch_bounds__(64) void idx_dec_prep_kernel(IdxDecPrepArgs a) {
+  __shared__ double s_freq[64];
+  fill_freq(s_freq, a.rot, a.theta);
+  __syncthreads();
+  const int b = blockIdx.x, lane = lane_id();
   const int ctx = min(a.ctx[b], a.max_pages * 128);
   if (ctx <= 0) return;
   const int p = ctx - 1;
-  const double wq = (double)a.wq[d];
-  for (int h = 0; h < a.Hi; ++h) {
-    const size_t off = ((size_t)b * a.Hi + h) * 128 + d;
-    a.qhat[off] = (float)norm_rope(bits_to_f64(a.idx_q[off], a.dt), wq, (double)p, a.rot, a.theta, a.eps, sx, red);
+  double o0, o1;
+  {
+    const Rope2 r = rope_at((double)p, s_freq, a.rot);
+    const double wq0 = a.wq[lane], wq1 = a.wq[lane + 64];
+    for (int h = 0; h < a.Hi; ++h) {
+      const size_t off = ((size_t)b * a.Hi + h) * 128;
+      norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt), wq0, wq1,
+                 a.eps, a.rot, r, o0, o1);
+      a.qhat[off + lane] = (float)o0;
+      a.qhat[off + 64 + lane] = (float)o1;
+    }
   }
   const int32_t *ptk = a.pt + (size_t)b * 2 * a.max_pages;
   const int32_t *ptv = ptk + a.max_pages;
-  const uint16_t knew = a.idx_k[(size_t)b * 128 + d];
+  const uint16_t knew0 = a.idx_k[(size_t)b * 128 + lane], knew1 = a.idx_k[(size_t)b * 128 + 64 + lane];
   if (ctx % a.ratio != 0) {
     const long long o = pool_row_off(ptk, p, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
-    if (o >= 0) a.pool[o + a.D + d] = knew;
+    if (o >= 0) {
+      a.pool[o + a.D + lane] = knew0;
+      a.pool[o + a.D + 64 + lane] = knew1;
+    }
     return;
   }
   const int g = ctx / a.ratio - 1;
   const int base = a.ratio * g;
-  double m = 0.0;
+  double m0 = 0.0, m1 = 0.0;
   bool ok = true;
   for (int j = 0; j < a.ratio - 1; ++j) {
     const long long o = pool_row_off(ptk, base + j, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
     ok = ok && o >= 0;
-    if (o >= 0) m += bits_to_f64(a.pool[o + a.D + d], a.dt);
+    if (o >= 0) {
+      m0 += bits_to_f64(a.pool[o + a.D + lane], a.dt);
+      m1 += bits_to_f64(a.pool[o + a.D + 64 + lane], a.dt);
+    }
   }
-  m += bits_to_f64(knew, a.dt);
-  m /= (double)a.ratio;
-  const double y = norm_rope(m, (double)a.wk[d], (double)base, a.rot, a.theta, a.eps, sx, red);
+  m0 += bits_to_f64(knew0, a.dt);
+  m1 += bits_to_f64(knew1, a.dt);
+  m0 /= (double)a.ratio;
+  m1 /= (double)a.ratio;
+  const Rope2 r = rope_at((double)base, s_freq, a.rot);
+  norm_rope2(m0, m1, (double)a.wk[lane], (double)a.wk[lane + 64], a.eps, a.rot, r, o0, o1);
   const long long ov = pool_row_off(ptv, base, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
-  if (ok && ov >= 0) a.pool[ov + a.D + d] = (uint16_t)f64_to_bits(y, a.dt);
+  if (ok && ov >= 0) {
+    a.pool[ov + a.D + lane] = (uint16_t)f64_to_bits(o0, a.dt);
+    a.pool[ov + a.D + 64 + lane] = (uint16_t)f64_to_bits(o1, a.dt);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -768,17 +826,24 @@ __global__ __launch_bounds__(256) void idx_dec_score_kernel(IdxDecScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_idx_prep(const IdxPrepArgs &a, hipStream_t s) {
-  const long long nblk = (long long)a.B * a.S + (long long)a.B * a.Gmax;
-  hipLaunchKernelGGL(idx_prep_kernel, dim3((unsigned)nblk), dim3(128), 0, s, a);
+hipError_t launch_idx_prep(const IdxPrepArgs &a_in, hipStream_t s) {
+  IdxPrepArgs a = a_in;
+  const long long items = (long long)a.B * a.S + (long long)a.B * a.Gmax;
+  a.per_wave = (int)std::min<long long>(kPrepItemsPerWave, std::max<long long>(1, items / 8192));
+  const long long waves = (items + a.per_wave - 1) / a.per_wave;
+  hipLaunchKernelGGL(idx_prep_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_idx_score(const IdxScoreArgs &a_in, int dt, hipStream_t s) {
   IdxScoreArgs a = a_in;
-  a.nchunk = (a.Gmax + kScoreChunk * kScoreChunksPerGroup - 1) / (kScoreChunk * kScoreChunksPerGroup);
-  if (a.nchunk < 1) a.nchunk = 1;
-  const unsigned grid = (unsigned)((long long)a.B * ((a.S + 31) / 32) * a.nchunk);
+  const int chunks = max(1, (a.Gmax + kScoreChunk - 1) / kScoreChunk);
+  const long long groups = (long long)a.B * ((a.S + 31) / 32);
+  int run = kScoreChunksPerGroup;  // halve runs until ~2048 workgroups (8 waves per CU)
+  while (run > 1 && groups * ((chunks + run - 1) / run) < 2048) run >>= 1;
+  a.run_chunks = run;
+  a.nchunk = (chunks + run - 1) / run;
+  const unsigned grid = (unsigned)(groups * a.nchunk);
   if (dt == DT_F16) hipLaunchKernelGGL(idx_score_kernel<DT_F16>, dim3(grid), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(idx_score_kernel<DT_BF16>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -830,7 +895,7 @@ hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) 
 }
 
 hipError_t launch_idx_dec_prep(const IdxDecPrepArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(idx_dec_prep_kernel, dim3((unsigned)a.B), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(idx_dec_prep_kernel, dim3((unsigned)a.B), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

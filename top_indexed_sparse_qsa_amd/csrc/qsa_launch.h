@@ -40,6 +40,7 @@ struct IdxPrepArgs {
   int B, S, Hi, hd, rot, ratio, Gmax;
   double theta, eps;
   int dt;
+  int per_wave;     // items per wave (set by the launcher)
 };
 
 struct IdxScoreArgs {
@@ -49,10 +50,11 @@ struct IdxScoreArgs {
   const int32_t *ctx;
   int B, S, Hi, Gmax, stride, ratio;
   int nchunk;       // chunk runs per 32-row group (set by the launcher)
+  int run_chunks;   // chunks per run (set by the launcher)
 };
 
 constexpr int kScoreChunk = 128;           // kbar rows staged at a time in prefill scoring
-constexpr int kScoreChunksPerGroup = 8;    // chunks per prefill scoring workgroup
+constexpr int kScoreChunksPerGroup = 8;    // most chunks per prefill scoring workgroup
 
 struct IdxSelectArgs {
   const float *scores;
