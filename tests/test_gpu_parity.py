@@ -124,6 +124,66 @@ def test_sparse_prefill_permuted_lists_same_result():
     TL.check_attention(p, ref, "fp16", "permuted")
 
 
+def identity_lists(rng, B, S, ctx, top_k, mode):
+    """Lists whose heads are the identity (slot s holds id s), as every row
+    gets before the budget fills, plus variants that break the identity at
+    various points: "full" identity to min(t, top_k - 1); "tail" identity
+    for a row-dependent length, then other distinct ids in random order;
+    "mixed" identity rows next to random-order rows in some groups of four
+    consecutive rows (one workgroup's rows); "holes" identity with a
+    few -1 slots."""
+    out = np.full((B, S, top_k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(min(int(ctx[b]), S)):
+            n = min(t + 1, top_k)
+            # "mixed": two rows of every third group of four rows go random
+            odd_one = mode == "mixed" and ((S - 1 - t) // 4) % 3 == 1 and t % 2 == 0
+            if mode == "full" or (mode == "mixed" and not odd_one):
+                out[b, t, :n] = np.arange(n)
+            elif mode == "tail":
+                k = min(n, 40 + (t * 7) % 90)
+                rest = rng.permutation(np.arange(k, t + 1))[:n - k]
+                out[b, t, :k] = np.arange(k)
+                out[b, t, k:k + len(rest)] = rest
+            elif mode == "mixed":
+                out[b, t, :n] = rng.permutation(t + 1)[:n]
+            elif mode == "holes":
+                out[b, t, :n] = np.arange(n)
+                if n > 40:
+                    out[b, t, rng.integers(0, n, 3)] = -1
+    return out
+
+
+IDENTITY_CASES = [
+    dict(B=2, S=301, Hq=8, Hkv=2, D=128, dtype="fp16", top_k=300, ctx=[301, 170], mode="full"),
+    dict(B=1, S=400, Hq=16, Hkv=4, D=128, dtype="bf16", top_k=2051, ctx=[400], mode="tail"),
+    dict(B=2, S=200, Hq=8, Hkv=1, D=128, dtype="fp16", top_k=256, ctx=[200, 131], mode="mixed"),
+    dict(B=1, S=260, Hq=8, Hkv=1, D=64, dtype="bf16", top_k=260, ctx=[260], mode="full"),
+    dict(B=1, S=150, Hq=6, Hkv=3, D=128, dtype="fp16", top_k=150, ctx=[150], mode="full"),
+    dict(B=1, S=330, Hq=8, Hkv=2, D=128, dtype="fp16", top_k=330, ctx=[330], mode="holes"),
+    dict(B=1, S=90, Hq=8, Hkv=2, D=128, dtype="fp16", top_k=16, ctx=[90], mode="full"),
+]
+
+
+@pytest.mark.parametrize("case", IDENTITY_CASES, ids=lambda c: f"{c['mode']}-B{c['B']}S{c['S']}Hkv{c['Hkv']}"
+                         f"D{c['D']}{c['dtype']}k{c['top_k']}")
+def test_sparse_prefill_identity_prefix_lists_all_rows(case):
+    """Workgroups whose rows share an identity list head gather it once and
+    walk it together; every row must still match the oracle."""
+    TL.log(f"sparse_prefill identity lists {case}")
+    inp = syn.make_prefill(14, B=case["B"], S=case["S"], Hq=case["Hq"], Hkv=case["Hkv"], D=case["D"],
+                           dtype=case["dtype"], ctx=case["ctx"], with_indexer=False)
+    lists = identity_lists(np.random.default_rng(14), inp.B, inp.S, inp.ctx, case["top_k"], case["mode"])
+    o = gpu_sparse_prefill(inp, lists)
+    ref = O.sparse_prefill(inp.q, inp.k, inp.v, lists, inp.ctx, inp.scale, inp.dtype)
+    got = TL.host_f64(o, inp.dtype)
+    for b in range(inp.B):
+        live = min(int(inp.ctx[b]), inp.S)
+        for t in range(live):
+            TL.check_attention(got[b, t], ref[b, t], inp.dtype, f"b={b} t={t}")
+        TL.check_zero_rows(o[b, live:], f"b={b}")
+
+
 # ---------------------------------------------------------------------------
 # indexer prefill
 # ---------------------------------------------------------------------------

@@ -132,16 +132,13 @@ __device__ __forceinline__ float add_pair(uint32_t p2, float acc) {
 // XOR-swizzled by row so that both the row writes and the fragment reads are
 // free of bank conflicts.  sl2 (scale * log2 e) is positive, so the max of
 // the unscaled scores, times sl2, is the max of the scaled ones.
+// chunk_math: scores, online softmax and PV for one chunk whose K rows sit
+// in an LDS tile and whose V rows (the lane's eight key slots) are in vf.
 template <int D, int DT>
-__device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf)[D / 32], float sl2,
-                                              float &m_run, float &l_run, f32x4 (&acc)[8], u32x4 *ktile) {
+__device__ __forceinline__ void chunk_math(const u32x4 *ktile, const u32x4 (&vf)[8], uint32_t valid, bool full,
+                                           const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
+                                           f32x4 (&acc)[8]) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = slot_of(q4, i);
-    if (D == 128 || r16 < D / 8) ktile[row * 16 + (r16 ^ (row & 15))] = f.kf[i];
-  }
-  __builtin_amdgcn_wave_barrier();
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < Frag<D>::NKS; ++ks) {
@@ -157,9 +154,9 @@ __device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf
     x[i] = s0[i];
     x[4 + i] = s1[i];
   }
-  if (!f.full) {
+  if (!full) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = ((f.valid >> i) & 1u) ? x[i] : -INFINITY;
+    for (int i = 0; i < 8; ++i) x[i] = ((valid >> i) & 1u) ? x[i] : -INFINITY;
   }
   float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
   mx = max_xor16(mx);
@@ -186,19 +183,33 @@ __device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf
     u32x4 a;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t lo = u4_at(f.vf[2 * w], e >> 1), hi = u4_at(f.vf[2 * w + 1], e >> 1);
+      uint32_t lo = u4_at(vf[2 * w], e >> 1), hi = u4_at(vf[2 * w + 1], e >> 1);
       a[w] = (e & 1) ? pack_hi_hi(lo, hi) : pack_lo_lo(lo, hi);
     }
     acc[e] = mfma16x16x32<DT>(a, bop, acc[e]);
   }
 }
 
-// Runs the online softmax over list slots [0, n_slots).  Processing stops at
+template <int D, int DT>
+__device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf)[D / 32], float sl2,
+                                              float &m_run, float &l_run, f32x4 (&acc)[8], u32x4 *ktile) {
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = slot_of(q4, i);
+    if (D == 128 || r16 < D / 8) ktile[row * 16 + (r16 ^ (row & 15))] = f.kf[i];
+  }
+  __builtin_amdgcn_wave_barrier();
+  chunk_math<D, DT>(ktile, f.vf, f.valid, f.full, qf, sl2, m_run, l_run, acc);
+}
+
+// Runs the online softmax over list slots [32 * c0, n_slots), with chunk c0
+// (ids id_a, all usable or not) already issued into fa.  Processing stops at
 // the first 32-slot chunk that holds no usable id.
 template <int D, int DT, class KV>
-__device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV &kv,
-                         const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
-                         f32x4 (&acc)[8], u32x4 *ktile) {
+__device__ void run_chunks(const int32_t *__restrict__ list, int n_slots, const KV &kv,
+                           const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
+                           f32x4 (&acc)[8], u32x4 *ktile, int c0, Frag<D> &fa) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int nchunks = (n_slots + 31) >> 5;
   auto load_id = [&](int c) -> int {
@@ -207,13 +218,10 @@ __device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV
   };
   auto usable = [&](int idv) { return wave_any((unsigned)idv < (unsigned)kv.limit); };
 
-  Frag<D> fa, fb;
-  int id_a = load_id(0);
-  int id_b = load_id(1);
-  if (!usable(id_a)) return;
-  issue_chunk<D, DT>(fa, id_a, kv, q4, r16);
-  int id_c = load_id(2);
-  for (int c = 0;; c += 2) {
+  Frag<D> fb;
+  int id_b = load_id(c0 + 1);
+  int id_c = load_id(c0 + 2);
+  for (int c = c0;; c += 2) {
     // fa holds chunk c; id_b / id_c are the ids of chunks c+1 / c+2.
     const bool b_ok = usable(id_b);
     int id_d = -1;
@@ -236,11 +244,88 @@ __device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV
   }
 }
 
+// run_chunks from chunk c0, issuing that chunk first.
+template <int D, int DT, class KV>
+__device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV &kv,
+                         const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
+                         f32x4 (&acc)[8], u32x4 *ktile, int c0 = 0) {
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
+  const int s = (c0 << 5) + (lane & 31);
+  const int id_a = s < n_slots ? list[s] : -1;
+  if (!wave_any((unsigned)id_a < (unsigned)kv.limit)) return;
+  Frag<D> fa;
+  issue_chunk<D, DT>(fa, id_a, kv, q4, r16);
+  run_chunks<D, DT>(list, n_slots, kv, qf, sl2, m_run, l_run, acc, ktile, c0, fa);
+}
+
 template <int D>
 __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhead0, int G, int q4, int r16) {
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
     qf[ks] = (r16 < G) ? ld16(qhead0 + (size_t)r16 * D + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Shared chunks.  Rows whose lists start with the identity (list[s] = s:
+// every row before the budget fills holds its whole causal prefix) need the
+// same K/V rows chunk after chunk.  When the four waves of a workgroup hold
+// such rows of one sequence and KV head, they walk the common identity
+// prefix together: per 32-slot chunk each wave gathers 8 of the 32 K and V
+// rows into a double-buffered LDS tile (same swizzle as the per-wave tile),
+// one barrier publishes it, and every wave reads its K fragments and its V
+// key slots from LDS.  The rest of each list then runs on the wave's own
+// path from the first chunk that is not shared.
+template <int D>
+struct CoopStage {
+  u32x4 k[2], v[2];
+};
+
+// Wave wv gathers rows 8wv .. 8wv+7 of chunk c (ids 32c + row, clamped into
+// the live range; rows past a wave's own prefix are never shared chunks).
+template <int D>
+__device__ __forceinline__ void coop_issue(CoopStage<D> &st, int c, const DenseKV &kv, int wv, int lane) {
+  const int piece = lane & 15;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * wv + 4 * h + (lane >> 4);
+    const int id = min(32 * c + row, kv.limit - 1);
+    if (D == 128 || piece < D / 8) kv.load(id, piece, st.k[h], st.v[h]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void coop_store(const CoopStage<D> &st, u32x4 *kt, u32x4 *vt, int wv, int lane) {
+  const int piece = lane & 15;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * wv + 4 * h + (lane >> 4);
+    if (D == 128 || piece < D / 8) {
+      kt[row * 16 + (piece ^ (row & 15))] = st.k[h];
+      vt[row * 16 + (piece ^ (row & 15))] = st.v[h];
+    }
+  }
+}
+
+// Whole 32-slot chunks at the head of the list with list[s] = s < limit.
+__device__ __forceinline__ int identity_chunks(const int32_t *__restrict__ list, int n_slots, int limit) {
+  const int lane = lane_id();
+  int first_bad = min(n_slots, limit);
+  for (int base = 0; base < n_slots; base += 64 * 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sidx = base + 64 * u + lane;
+      v[u] = sidx < n_slots ? list[sidx] : sidx;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sidx = base + 64 * u + lane;
+      if (v[u] != sidx) first_bad = min(first_bad, sidx);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) first_bad = min(first_bad, __shfl_xor(first_bad, o, 64));
+    if (first_bad < base + 64 * 8) break;
+  }
+  return first_bad >> 5;
 }
 
 // Work order.  Sequences one after another, and within a sequence rows
@@ -304,27 +389,84 @@ static int prefill_rows_per_launch(const PrefillAttnArgs &a, int D) {
 template <int D, int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(PrefillAttnArgs a) {
   __shared__ u32x4 s_ktile[4][32 * 16];
-  u32x4 *ktile = s_ktile[threadIdx.x >> 6];
-  int b, t, kvh;
-  if (!prefill_item(a, b, t, kvh)) return;
+  __shared__ int s_key[4], s_pre[4];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  u32x4 *ktile = s_ktile[wv];
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  const int live = min(a.ctx[b], a.S);
-  const size_t qo_off = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
+  int b = 0, t = 0, kvh = 0;
+  const bool item = prefill_item(a, b, t, kvh);
+  const int live = item ? min(a.ctx[b], a.S) : 0;
+  const bool active = item && t < live;
+  const int32_t *list = a.indices + ((size_t)b * a.S + t) * a.top_k;
+  DenseKV kv;
+  kv.k = reinterpret_cast<const char *>(a.k + ((size_t)b * a.S * a.Hkv + kvh) * D);
+  kv.v = reinterpret_cast<const char *>(a.v + ((size_t)b * a.S * a.Hkv + kvh) * D);
+  kv.row_bytes = (uint32_t)(a.Hkv * D * 2);
+  kv.limit = live;
+
+  // The first chunk's gathers go out before the workgroup decides whether
+  // to share chunks: a workgroup shares only if all four waves hold live
+  // rows of one (sequence, KV head) whose first chunk is the identity.
+  const int s0 = lane & 31;
+  const int id0 = active && s0 < a.top_k ? list[s0] : -1;
+  const bool any0 = wave_any((unsigned)id0 < (unsigned)live);
+  const bool first_identity = active && a.top_k >= 32 && !wave_any(id0 != s0 || s0 >= live);
+  Frag<D> fa;
+  if (any0) issue_chunk<D, DT>(fa, id0, kv, q4, r16);
+  if (lane == 0) s_key[wv] = first_identity ? b * a.Hkv + kvh : -1 - wv;
+  __syncthreads();
+  const bool coop = s_key[0] >= 0 && s_key[0] == s_key[1] && s_key[0] == s_key[2] && s_key[0] == s_key[3];
 
   f32x4 acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  if (t < live) {
+  if (active) {
+    const size_t qo_q = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
     u32x4 qf[D / 32];
-    load_q<D>(qf, a.q + qo_off, a.G, q4, r16);
-    DenseKV kv;
-    kv.k = reinterpret_cast<const char *>(a.k + ((size_t)b * a.S * a.Hkv + kvh) * D);
-    kv.v = reinterpret_cast<const char *>(a.v + ((size_t)b * a.S * a.Hkv + kvh) * D);
-    kv.row_bytes = (uint32_t)(a.Hkv * D * 2);
-    kv.limit = live;
-    run_list<D, DT>(a.indices + ((size_t)b * a.S + t) * a.top_k, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile);
+    load_q<D>(qf, a.q + qo_q, a.G, q4, r16);
+    if (coop) {
+      int c0 = 0;
+      const int mine = identity_chunks(list, a.top_k, live);
+      if (lane == 0) s_pre[wv] = mine;
+      __syncthreads();
+      const int P = min(min(s_pre[0], s_pre[1]), min(s_pre[2], s_pre[3]));
+      // buffer j: K tile s_ktile[2j], V tile s_ktile[2j + 1].  Loads run two
+      // chunks ahead in two register stages (a wave's share is 2 + 2 rows).
+      CoopStage<D> sa, sb;
+      if (P > 0) {
+        coop_issue<D>(sa, 0, kv, wv, lane);
+        coop_store<D>(sa, s_ktile[0], s_ktile[1], wv, lane);
+        if (P > 1) coop_issue<D>(sa, 1, kv, wv, lane);
+        if (P > 2) coop_issue<D>(sb, 2, kv, wv, lane);
+      }
+      __syncthreads();
+      auto coop_chunk = [&](int c, CoopStage<D> &next) {
+        // buffer c & 1 holds chunk c; `next` holds chunk c + 1 in flight
+        const u32x4 *vsrc = s_ktile[2 * (c & 1) + 1];
+        u32x4 vf[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = slot_of(q4, i);
+          vf[i] = (D == 128 || r16 < D / 8) ? vsrc[row * 16 + (r16 ^ (row & 15))] : u32x4{0u, 0u, 0u, 0u};
+        }
+        chunk_math<D, DT>(s_ktile[2 * (c & 1)], vf, 0xffu, true, qf, a.sl2, m_run, l_run, acc);
+        if (c + 1 < P) coop_store<D>(next, s_ktile[2 * ((c + 1) & 1)], s_ktile[2 * ((c + 1) & 1) + 1], wv, lane);
+        if (c + 3 < P) coop_issue<D>(next, c + 3, kv, wv, lane);
+        __syncthreads();
+      };
+      for (int c = 0; c < P; c += 2) {
+        coop_chunk(c, sa);
+        if (c + 1 < P) coop_chunk(c + 1, sb);
+      }
+      c0 = P;
+      run_list<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, c0);
+    } else if (any0) {
+      run_chunks<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, 0, fa);
+    }
   }
+  if (!item) return;
+  const size_t qo_off = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
   float l = l_run + shfl_xor_f(l_run, 16);
   l += shfl_xor_f(l, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;
