@@ -204,12 +204,12 @@ __device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf
 }
 
 // Runs the online softmax over list slots [32 * c0, n_slots), with chunk c0
-// (ids id_a, all usable or not) already issued into fa.  Processing stops at
-// the first 32-slot chunk that holds no usable id.
+// already issued into fa and id_b holding the ids of chunk c0 + 1.
+// Processing stops at the first 32-slot chunk that holds no usable id.
 template <int D, int DT, class KV>
 __device__ void run_chunks(const int32_t *__restrict__ list, int n_slots, const KV &kv,
                            const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
-                           f32x4 (&acc)[8], u32x4 *ktile, int c0, Frag<D> &fa) {
+                           f32x4 (&acc)[8], u32x4 *ktile, int c0, Frag<D> &fa, int id_b) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int nchunks = (n_slots + 31) >> 5;
   auto load_id = [&](int c) -> int {
@@ -219,7 +219,6 @@ __device__ void run_chunks(const int32_t *__restrict__ list, int n_slots, const 
   auto usable = [&](int idv) { return wave_any((unsigned)idv < (unsigned)kv.limit); };
 
   Frag<D> fb;
-  int id_b = load_id(c0 + 1);
   int id_c = load_id(c0 + 2);
   for (int c = c0;; c += 2) {
     // fa holds chunk c; id_b / id_c are the ids of chunks c+1 / c+2.
@@ -252,10 +251,11 @@ __device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int s = (c0 << 5) + (lane & 31);
   const int id_a = s < n_slots ? list[s] : -1;
+  const int id_b = s + 32 < n_slots ? list[s + 32] : -1;
   if (!wave_any((unsigned)id_a < (unsigned)kv.limit)) return;
   Frag<D> fa;
   issue_chunk<D, DT>(fa, id_a, kv, q4, r16);
-  run_chunks<D, DT>(list, n_slots, kv, qf, sl2, m_run, l_run, acc, ktile, c0, fa);
+  run_chunks<D, DT>(list, n_slots, kv, qf, sl2, m_run, l_run, acc, ktile, c0, fa, id_b);
 }
 
 template <int D>
@@ -337,8 +337,7 @@ __device__ __forceinline__ int identity_chunks(const int32_t *__restrict__ list,
 // list walks its ids in ascending order, so concurrent waves touch nearby
 // rows).  A workgroup's four waves take four consecutive rows of that head.
 // Otherwise a workgroup takes the Hkv heads of consecutive rows.
-__device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int &b, int &t, int &kvh) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int wave, int &b, int &t, int &kvh) {
   int rest;
   if ((8 % a.Hkv) == 0) {
     const int xcd = blockIdx.x & 7, n = blockIdx.x >> 3;
@@ -386,7 +385,11 @@ static int prefill_rows_per_launch(const PrefillAttnArgs &a, int D) {
   return max(64, kSyncWaves / a.Hkv);
 }
 
-template <int D, int DT>
+// SHARE = false: every wave walks its own list.  SHARE = true (launched
+// only over rows t < top_k, where lists can be whole causal prefixes):
+// workgroups may share identity chunks.  Two kernels, because the sharing
+// code, even untaken, costs the plain walk registers and scheduling.
+template <int D, int DT, bool SHARE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(PrefillAttnArgs a) {
   __shared__ u32x4 s_ktile[4][32 * 16];
   __shared__ int s_key[4], s_pre[4];
@@ -394,7 +397,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   u32x4 *ktile = s_ktile[wv];
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   int b = 0, t = 0, kvh = 0;
-  const bool item = prefill_item(a, b, t, kvh);
+  const bool item = prefill_item(a, wv, b, t, kvh);
+  // Only a workgroup whose four rows are of one (sequence, KV head) and lie
+  // before top_k tries to share; the test depends on the workgroup alone, so
+  // all its waves agree.
+  bool try_share = SHARE;
+  for (int w = 0; SHARE && w < 4; ++w) {
+    int bw = 0, tw = 0, kw = 0;
+    const bool ok = prefill_item(a, w, bw, tw, kw);
+    try_share = try_share && ok && tw < a.top_k && bw == b && kw == kvh;
+  }
   const int live = item ? min(a.ctx[b], a.S) : 0;
   const bool active = item && t < live;
   const int32_t *list = a.indices + ((size_t)b * a.S + t) * a.top_k;
@@ -404,27 +416,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   kv.row_bytes = (uint32_t)(a.Hkv * D * 2);
   kv.limit = live;
 
-  // The first chunk's gathers go out before the workgroup decides whether
-  // to share chunks: a workgroup shares only if all four waves hold live
-  // rows of one (sequence, KV head) whose first chunk is the identity.
-  const int s0 = lane & 31;
-  const int id0 = active && s0 < a.top_k ? list[s0] : -1;
-  const bool any0 = wave_any((unsigned)id0 < (unsigned)live);
-  const bool first_identity = active && a.top_k >= 32 && !wave_any(id0 != s0 || s0 >= live);
-  Frag<D> fa;
-  if (any0) issue_chunk<D, DT>(fa, id0, kv, q4, r16);
-  if (lane == 0) s_key[wv] = first_identity ? b * a.Hkv + kvh : -1 - wv;
-  __syncthreads();
-  const bool coop = s_key[0] >= 0 && s_key[0] == s_key[1] && s_key[0] == s_key[2] && s_key[0] == s_key[3];
-
   f32x4 acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  if (active) {
-    const size_t qo_q = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
-    u32x4 qf[D / 32];
-    load_q<D>(qf, a.q + qo_q, a.G, q4, r16);
+  u32x4 qf[D / 32];
+  const size_t qo_off = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
+  if (!try_share) {
+    if (active) {
+      load_q<D>(qf, a.q + qo_off, a.G, q4, r16);
+      run_list<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile);
+    }
+  } else if constexpr (SHARE) {
+    // Q first (its loads must be older than the gathers, or the loop's waits
+    // on qf would also wait for the chunk in flight), then the first chunk's
+    // gathers, then the decision: the workgroup shares only if all four rows
+    // are live and their first chunks are the identity.
+    if (active) load_q<D>(qf, a.q + qo_off, a.G, q4, r16);
+    const int s0 = lane & 31;
+    const int id0 = active && s0 < a.top_k ? list[s0] : -1;
+    const int id1 = active && s0 + 32 < a.top_k ? list[s0 + 32] : -1;
+    const bool any0 = wave_any((unsigned)id0 < (unsigned)live);
+    Frag<D> fa;
+    if (any0) issue_chunk<D, DT>(fa, id0, kv, q4, r16);
+    const bool first_identity = active && a.top_k >= 32 && !wave_any(id0 != s0 || s0 >= live);
+    if (lane == 0) s_key[wv] = first_identity ? 1 : 0;
+    __syncthreads();
+    const bool coop = s_key[0] + s_key[1] + s_key[2] + s_key[3] == 4;
     if (coop) {
       int c0 = 0;
       const int mine = identity_chunks(list, a.top_k, live);
@@ -462,11 +480,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       c0 = P;
       run_list<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, c0);
     } else if (any0) {
-      run_chunks<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, 0, fa);
+      run_chunks<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, 0, fa, id1);
     }
   }
   if (!item) return;
-  const size_t qo_off = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
   float l = l_run + shfl_xor_f(l_run, 16);
   l += shfl_xor_f(l, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -651,13 +668,33 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
 
 template <int D, int DT>
 static hipError_t launch_prefill_t(const PrefillAttnArgs &a, hipStream_t s) {
-  const int total = a.B * a.S, per = prefill_rows_per_launch(a, D);
-  for (int r0 = 0; r0 < total; r0 += per) {
-    PrefillAttnArgs p = a;
-    p.row0 = r0;
-    p.nrows = min(per, total - r0);
-    hipLaunchKernelGGL((sparse_prefill_kernel<D, DT>), dim3(prefill_grid(p)), dim3(256), 0, s, p);
-    const hipError_t e = hipGetLastError();
+  // One launch of the sharing kernel over every row, unless the rows go out
+  // in several launches anyway (see prefill_rows_per_launch): then, per
+  // sequence, rows t >= top_k run on the plain kernel and rows t < top_k on
+  // the sharing kernel, each range in launches of at most `per` rows.  (A
+  // single launch keeps short prefix rows filling in behind long rows; the
+  // plain kernel is ~2-3 % faster on rows that never share.)
+  const int per = prefill_rows_per_launch(a, D);
+  const int plain = max(0, a.S - a.top_k);
+  auto run = [&](int r0, int n, bool share) -> hipError_t {
+    for (int o = 0; o < n; o += per) {
+      PrefillAttnArgs p = a;
+      p.row0 = r0 + o;
+      p.nrows = min(per, n - o);
+      if (share)
+        hipLaunchKernelGGL((sparse_prefill_kernel<D, DT, true>), dim3(prefill_grid(p)), dim3(256), 0, s, p);
+      else
+        hipLaunchKernelGGL((sparse_prefill_kernel<D, DT, false>), dim3(prefill_grid(p)), dim3(256), 0, s, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  if (a.top_k < 32) return run(0, a.B * a.S, false);  // no identity chunk fits
+  if (per >= a.B * a.S) return run(0, a.B * a.S, true);
+  for (int b = 0; b < a.B; ++b) {
+    hipError_t e = run(b * a.S, plain, false);
+    if (e == hipSuccess) e = run(b * a.S + plain, a.S - plain, true);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
