@@ -684,7 +684,7 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode B1: queries at p = ctx-1 and the tail update.  One wave per sequence.
+// Decode B1: queries at p = ctx-1 and the tail update.  One workgroup per sequence.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ long long pool_row_off(const int32_t *ptrow, int token, int max_pages,
                                                   int num_flat_pages, int Hkv, int PHD) {
@@ -695,26 +695,28 @@ __device__ __forceinline__ long long pool_row_off(const int32_t *ptrow, int toke
   return (((long long)pg * 128 + (token & 127)) * Hkv) * PHD;
 }
 
-__global__ __launch_bounds__(64) void idx_dec_prep_kernel(IdxDecPrepArgs a) {
+// Wave h < Hi prepares query head h; wave Hi updates the pool tail, so the
+// query and key chains run side by side.
+__global__ __launch_bounds__(320) void idx_dec_prep_kernel(IdxDecPrepArgs a) {
   __shared__ double s_freq[64];
   fill_freq(s_freq, a.rot, a.theta);
   __syncthreads();
   const int b = blockIdx.x, lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ctx = min(a.ctx[b], a.max_pages * 128);
   if (ctx <= 0) return;
   const int p = ctx - 1;
   double o0, o1;
-  {
+  if (wv < a.Hi) {
     const Rope2 r = rope_at((double)p, s_freq, a.rot);
-    const double wq0 = a.wq[lane], wq1 = a.wq[lane + 64];
-    for (int h = 0; h < a.Hi; ++h) {
-      const size_t off = ((size_t)b * a.Hi + h) * 128;
-      norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt), wq0, wq1,
-                 a.eps, a.rot, r, o0, o1);
-      a.qhat[off + lane] = (float)o0;
-      a.qhat[off + 64 + lane] = (float)o1;
-    }
+    const size_t off = ((size_t)b * a.Hi + wv) * 128;
+    norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
+               (double)a.wq[lane], (double)a.wq[lane + 64], a.eps, a.rot, r, o0, o1);
+    a.qhat[off + lane] = (float)o0;
+    a.qhat[off + 64 + lane] = (float)o1;
+    return;
   }
+  if (wv != a.Hi) return;
   const int32_t *ptk = a.pt + (size_t)b * 2 * a.max_pages;
   const int32_t *ptv = ptk + a.max_pages;
   const uint16_t knew0 = a.idx_k[(size_t)b * 128 + lane], knew1 = a.idx_k[(size_t)b * 128 + 64 + lane];
@@ -895,7 +897,7 @@ hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) 
 }
 
 hipError_t launch_idx_dec_prep(const IdxDecPrepArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(idx_dec_prep_kernel, dim3((unsigned)a.B), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(idx_dec_prep_kernel, dim3((unsigned)a.B), dim3(64 * (a.Hi + 1)), 0, s, a);
   return hipGetLastError();
 }
 
