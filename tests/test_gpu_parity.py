@@ -286,6 +286,30 @@ def test_indexer_prefill_exact_ties_wave_select(classes):
     check_tied_rows(out.cpu().numpy(), inp, icfg, classes, rows, f"ties{classes}")
 
 
+@pytest.mark.parametrize("classes", [0, 3])
+def test_indexer_prefill_two_wave_rows(classes):
+    """Rows of 4097..8192 complete blocks take the two-wave select (shorter
+    rows of the same call take the one-wave kernels); with a budget of 64 and
+    three tied classes the cut falls inside the best class, whose equal keys
+    sit in both waves."""
+    icfg = syn.IndexerCfg(budget=64, rot_dim=0) if classes else syn.IndexerCfg(budget=64)
+    S = 17000
+    TL.log(f"indexer_prefill two-wave rows S={S} classes={classes}")
+    inp = syn.make_prefill(15, B=1, S=S, Hq=2, Hkv=1, D=64, dtype="fp16", ctx=[S], icfg=icfg)
+    if classes:
+        tie_classes(inp, icfg, classes)
+    out, _ = gpu_indexer_prefill(inp, icfg, icfg.top_k)
+    rng = np.random.default_rng(15)
+    rows = sorted({(0, int(t)) for t in rng.integers(16387, S, 10)} | {(0, 16387), (0, 16386), (0, S - 1),
+                                                                         (0, 9000), (0, 300)})
+    lists = {r: out[r[0], r[1]].cpu().numpy() for r in rows}
+    if classes:
+        check_tied_rows(lists, inp, icfg, classes, rows, "two-wave ties")
+    else:
+        _, swaps, _ = compare_lists(lists, inp, icfg, icfg.top_k, rows, "two-wave rows")
+        TL.log(f"  boundary swaps used: {swaps}")
+
+
 @pytest.mark.parametrize("classes", [0, 7])
 def test_indexer_prefill_long_rows_workgroup_select(classes):
     """Rows with more than 8192 complete blocks take the workgroup select."""

@@ -65,7 +65,9 @@ struct IdxSelectArgs {
   int top_k, budget, ratio;
   int decode;          // 1: row of sequence b is position ctx[b]-1
   int max_ctx;         // decode: clamp of ctx (max_pages * 128)
-  int wave_words;      // wave-per-row kernel: LDS words per wave (set by the launcher)
+  int wave_words;      // per-row kernels: LDS words per row region (set by the launcher)
+  int list_words;      // two-wave kernel: LDS words of each wave's list (set by the launcher)
+  int row0, nrows;     // prefill: this launch covers rows [row0, row0 + nrows) (set by the launcher)
 };
 
 struct IdxDecPrepArgs {
