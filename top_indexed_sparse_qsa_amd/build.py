@@ -25,9 +25,9 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-# The attention kernels take finite inputs: without NaN semantics the
-# softmax max needs no quieting of MFMA results.
-EXTRA = {"sparse_attention.hip": ["-fno-honor-nans"]}
+# The kernels take finite inputs: without NaN semantics a max (softmax,
+# relu) needs no quieting of MFMA results.
+EXTRA = {"sparse_attention.hip": ["-fno-honor-nans"], "indexer.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

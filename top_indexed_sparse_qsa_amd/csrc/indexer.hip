@@ -199,72 +199,82 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
       for (int p = 0; p < NP; ++p) qa[m][p][ks] = pieces[p];
     }
   }
-  int nc_out[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int t_out = t0 + 4 * m + q4;
-    nc_out[m] = t_out < live ? (t_out + 1) / a.ratio : 0;
-  }
   const int nc_wave = t0 < live ? (min(t0 + 7, live - 1) + 1) / a.ratio : 0;
+  // score stores: thread tid owns columns 4 (tid % 32) .. +3 of rows tid / 32 + 8 j
+  static_assert(CB == 128, "store mapping assumes 32 float4 columns per chunk");
+  const int st_row0 = tid >> 5, st_c4 = 4 * (tid & 31);
+  int st_nc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = tg + st_row0 + 8 * j;
+    st_nc[j] = t < live ? (t + 1) / a.ratio : 0;
+  }
+  float *const st_base = a.scores + ((size_t)b * a.S + tg + st_row0) * a.stride;
 
+  // kbar rows of a chunk: global -> registers (issued a chunk ahead) -> LDS
+  constexpr int NV = CB * 16 / 256;  // 16-byte pieces per thread
+  u32x4 v[NV];
+  auto load_chunk = [&](int g_lo) {
+    const int npiece = (min(g_lo + CB, run_hi) - g_lo) * 16;
+    const uint16_t *src = a.kbar + ((size_t)b * a.Gmax + g_lo) * 128;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int i = tid + 256 * u;
+      if (i < npiece) v[u] = ld16(src + 8 * i);
+    }
+  };
+  auto stage_chunk = [&](int g_lo) {
+    const int npiece = (min(g_lo + CB, run_hi) - g_lo) * 16;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int i = tid + 256 * u;
+      const int row = i >> 4, pc = i & 15;
+      if (i < npiece) *reinterpret_cast<u32x4 *>(&s_kb[row * 64 + 4 * (pc ^ (row & 15))]) = v[u];
+    }
+  };
+  load_chunk(run_lo);
+  stage_chunk(run_lo);
+  __syncthreads();
   for (int g_lo = run_lo; g_lo < run_hi; g_lo += CB) {
     const int g_hi = min(g_lo + CB, run_hi);
-    // stage kbar rows [g_lo, g_hi)
-    {
-      const uint16_t *src = a.kbar + ((size_t)b * a.Gmax + g_lo) * 128;
-      const int npiece = (g_hi - g_lo) * 16;
-      u32x4 v[CB * 16 / 256];
-#pragma unroll
-      for (int u = 0; u < CB * 16 / 256; ++u) {
-        const int i = tid + 256 * u;
-        if (i < npiece) v[u] = ld16(src + 8 * i);
-      }
-      __syncthreads();  // the previous chunk's LDS data is consumed
-#pragma unroll
-      for (int u = 0; u < CB * 16 / 256; ++u) {
-        const int i = tid + 256 * u;
-        const int row = i >> 4, pc = i & 15;
-        if (i < npiece) *reinterpret_cast<u32x4 *>(&s_kb[row * 64 + 4 * (pc ^ (row & 15))]) = v[u];
-      }
-      __syncthreads();
-    }
+    const bool more = g_lo + CB < run_hi;
+    if (more) load_chunk(g_lo + CB);  // in flight during this chunk's MFMAs
     const int g_end = min(g_hi, nc_wave);
     for (int g0 = g_lo; g0 < g_end; g0 += 16) {
       const int lb = g0 - g_lo + r16;  // local kbar row; lb & 15 == r16
       u32x4 kb[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kb[ks] = *reinterpret_cast<const u32x4 *>(&s_kb[lb * 64 + 4 * ((4 * ks + q4) ^ r16)]);
-      // four independent accumulator chains (M tile x k-step parity), interleaved
-      f32x4 acc[2][2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // two independent accumulator chains (the M tiles), interleaved
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int p = 0; p < NP; ++p)
 #pragma unroll
-          for (int m = 0; m < 2; ++m) acc[m][ks & 1] = mfma16x16x32<DT>(qa[m][p][ks], kb[ks], acc[m][ks & 1]);
+          for (int m = 0; m < 2; ++m) acc[m] = mfma16x16x32<DT>(qa[m][p][ks], kb[ks], acc[m]);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const f32x4 d = acc[m][0] + acc[m][1];
+        const f32x4 d = acc[m];
         s_sc[8 * wv + 4 * m + q4][lb] = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) + fmaxf(d[3], 0.f);
       }
     }
-    __syncthreads();
-    // store the chunk's scores: 32 rows x (g_hi - g_lo) floats, 16 B per lane
-    const int width = g_hi - g_lo;            // multiple of 16 except at the causal edge
-    for (int i = tid; i < 32 * (CB / 4); i += 256) {
-      const int r = i / (CB / 4), c4 = 4 * (i % (CB / 4));
-      const int t = tg + r;
-      if (t >= live || c4 >= width) continue;
-      const int ncr = (t + 1) / a.ratio - g_lo;  // this row's blocks in the chunk
-      if (c4 >= ncr) continue;
-      float *dst = a.scores + ((size_t)b * a.S + t) * a.stride + g_lo + c4;
-      const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&s_sc[r][c4]);
-      if (c4 + 4 <= ncr) *reinterpret_cast<f32x4 *>(dst) = v4;
+    __syncthreads();  // this chunk's kbar is consumed and its scores are in LDS
+    // store the chunk's scores: 32 rows x (g_hi - g_lo) floats, 16 B per lane;
+    // thread tid writes columns c4 of rows tid / 32 + 8 j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = st_row0 + 8 * j;
+      const int ncr = st_nc[j] - g_lo;  // this row's blocks in the chunk (<= 0: none, or dead row)
+      if (st_c4 >= ncr) continue;
+      float *dst = st_base + (size_t)(8 * j) * a.stride + g_lo + st_c4;
+      const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&s_sc[r][st_c4]);
+      if (st_c4 + 4 <= ncr) *reinterpret_cast<f32x4 *>(dst) = v4;
       else
-        for (int j = 0; j < ncr - c4; ++j) dst[j] = v4[j];
+        for (int q = 0; q < ncr - st_c4; ++q) dst[q] = v4[q];
     }
+    if (more) stage_chunk(g_lo + CB);
+    __syncthreads();  // the next chunk's kbar is staged; the score tile is free
   }
 }
 
