@@ -303,7 +303,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // of bank conflicts.
 constexpr int kSelBins = 2048;
 __device__ __forceinline__ int hpad(int d) { return d + ((d >> 5) << 2); }
-constexpr int kSelHistWords = 2048 + (2048 >> 3);
+constexpr int kSelHistWords = kSelBins + (kSelBins >> 3);
 
 // Radix window of a pass: the first takes 11 bits below the bits shared by
 // every key, later ones 8.
@@ -556,10 +556,10 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
 
 // ---------------------------------------------------------------------------
 // Select + expand, one 1024-thread workgroup per row: decode rows (one per
-// sequence, up to 32768 blocks) and prefill rows too long for one wave.
-// Thread j holds the KPT keys of blocks [j*KPT, (j+1)*KPT) in registers, so
-// one workgroup scan of per-thread counts places kept blocks in ascending
-// order.  Passes as in the wave kernel, over one workgroup histogram: a
+// sequence, up to 32768 blocks) and prefill rows over 8192 blocks.  Thread
+// j holds the KPT keys of blocks [j*KPT, (j+1)*KPT) in registers, so one
+// workgroup scan of per-thread counts places kept blocks in ascending order.
+// Passes as in the per-row kernel, over one workgroup histogram: a
 // workgroup scan of per-thread bin sums names the thread whose range holds
 // the cut, and that thread walks its own bins.
 // ---------------------------------------------------------------------------
