@@ -64,7 +64,8 @@ def test_workspace_sizes_follow_layout():
 
 
 def test_default_split_plan():
-    assert Q.qsa_sparse_decode_default_splits(32, 4, 2051) == 16
+    assert Q.qsa_sparse_decode_default_splits(32, 4, 2051) == 8      # ~1024 waves
+    assert Q.qsa_sparse_decode_default_splits(8, 4, 2051) == 16
     assert Q.qsa_sparse_decode_default_splits(1, 1, 40) == 2       # never more splits than 32-slot chunks
     assert Q.qsa_sparse_decode_default_splits(4096, 8, 2051) == 1
     assert Q.qsa_sparse_decode_default_splits(0, 4, 2051) == 0
