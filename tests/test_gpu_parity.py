@@ -162,6 +162,7 @@ IDENTITY_CASES = [
     dict(B=1, S=150, Hq=6, Hkv=3, D=128, dtype="fp16", top_k=150, ctx=[150], mode="full"),
     dict(B=1, S=330, Hq=8, Hkv=2, D=128, dtype="fp16", top_k=330, ctx=[330], mode="holes"),
     dict(B=1, S=90, Hq=8, Hkv=2, D=128, dtype="fp16", top_k=16, ctx=[90], mode="full"),
+    dict(B=1, S=200, Hq=16, Hkv=1, D=128, dtype="bf16", top_k=200, ctx=[200], mode="full"),
 ]
 
 

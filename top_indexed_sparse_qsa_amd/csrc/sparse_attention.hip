@@ -328,6 +328,102 @@ __device__ __forceinline__ int identity_chunks(const int32_t *__restrict__ list,
   return first_bad >> 5;
 }
 
+// Packed sharing, for GQA groups of at most 8 heads: half of each 16-column
+// MFMA tile would be padding, so on the shared identity prefix a wave takes
+// two rows at once (column 8j + h = head h of row 2p + j) and every second
+// chunk: wave 2e + p takes rows 2p, 2p + 1 and chunks c = e (mod 2).  Chunk
+// pairs are staged together (wave w gathers pair rows 16w .. 16w + 15, one
+// pair ahead in registers).  At the end the two chunk-parity halves of each
+// row are merged through LDS (rescaled to the larger reference) into the
+// state of the row's own wave, which then walks the rest of its list.
+template <int D, int DT>
+__device__ void coop_packed(const PrefillAttnArgs &a, const DenseKV &kv, int b, int kvh, const int (&t_of)[4], int P,
+                            u32x4 (*s_tiles)[32 * 16], float *s_ml, float &m_run, float &l_run, f32x4 (&acc)[8]) {
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15, piece = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = wv & 1, e = wv >> 1;
+  u32x4 qp[D / 32];
+  {
+    const int rr = 2 * p + (r16 >> 3), h = r16 & 7;
+    const uint16_t *qh = a.q + (((size_t)b * a.S + t_of[rr]) * a.Hq + (size_t)kvh * a.G + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qp[ks] = h < a.G ? ld16(qh + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float pm = -INFINITY, pl = 0.f;
+  f32x4 pacc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) pacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 stk[4], stv[4];
+  auto issue = [&](int j) {  // pair j = chunks 2j, 2j + 1: ids 64 j + R, R < 64
+#pragma unroll
+    for (int h2 = 0; h2 < 4; ++h2) {
+      const int R = 16 * wv + 4 * h2 + (lane >> 4);
+      const int id = min(64 * j + R, kv.limit - 1);
+      if (D == 128 || piece < D / 8) kv.load(id, piece, stk[h2], stv[h2]);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int h2 = 0; h2 < 4; ++h2) {
+      const int R = 16 * wv + 4 * h2 + (lane >> 4);
+      const int half = R >> 5, row = R & 31;
+      if (D == 128 || piece < D / 8) {
+        s_tiles[2 * half][row * 16 + (piece ^ (row & 15))] = stk[h2];
+        s_tiles[2 * half + 1][row * 16 + (piece ^ (row & 15))] = stv[h2];
+      }
+    }
+  };
+  const int npairs = (P + 1) >> 1;
+  issue(0);
+  stage();
+  __syncthreads();
+  for (int j = 0; j < npairs; ++j) {
+    const bool more = j + 1 < npairs;
+    if (more) issue(j + 1);
+    if (2 * j + e < P) {
+      const u32x4 *vsrc = s_tiles[2 * e + 1];
+      u32x4 vf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = slot_of(q4, i);
+        vf[i] = (D == 128 || r16 < D / 8) ? vsrc[row * 16 + (r16 ^ (row & 15))] : u32x4{0u, 0u, 0u, 0u};
+      }
+      chunk_math<D, DT>(s_tiles[2 * e], vf, 0xffu, true, qp, a.sl2, pm, pl, pacc);
+    }
+    __syncthreads();  // the pair is consumed
+    if (more) stage();
+    __syncthreads();  // the next pair is staged
+  }
+  // merge: wave w's own row r = w sits in column 8 (r & 1) + h of waves
+  // (r >> 1) (even chunks) and 2 + (r >> 1) (odd chunks)
+  float *s_acc = reinterpret_cast<float *>(s_tiles);  // [wave][32][64]
+#pragma unroll
+  for (int k = 0; k < 32; ++k) s_acc[(wv * 32 + k) * 64 + lane] = pacc[k >> 2][k & 3];
+  s_ml[(wv * 2) * 64 + lane] = pm;
+  s_ml[(wv * 2 + 1) * 64 + lane] = pl;
+  __syncthreads();
+  const int h = r16;
+  if (h < a.G && h < 8) {
+    const int src = q4 * 16 + 8 * (wv & 1) + h;
+    const int w0 = wv >> 1, w1 = 2 + (wv >> 1);
+    const float mA = s_ml[(w0 * 2) * 64 + src], mB = s_ml[(w1 * 2) * 64 + src];
+    const float M = fmaxf(mA, mB);
+    const float sA = mA == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mA - M);
+    const float sB = mB == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mB - M);
+    m_run = M;
+    l_run = s_ml[(w0 * 2 + 1) * 64 + src] * sA + s_ml[(w1 * 2 + 1) * 64 + src] * sB;
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      acc[k >> 2][k & 3] = s_acc[(w0 * 32 + k) * 64 + src] * sA + s_acc[(w1 * 32 + k) * 64 + src] * sB;
+  } else {
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();  // the tiles are free again
+}
+
 // Work order.  Sequences one after another, and within a sequence rows
 // longest-first (row t before row t-1).  Workgroups are dispatched
 // round-robin over the eight XCDs, each with its own 4 MB L2.  When Hkv
@@ -393,6 +489,7 @@ template <int D, int DT, bool SHARE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(PrefillAttnArgs a) {
   __shared__ u32x4 s_ktile[4][32 * 16];
   __shared__ int s_key[4], s_pre[4];
+  __shared__ float s_ml[SHARE ? 4 * 2 * 64 : 1];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   u32x4 *ktile = s_ktile[wv];
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
@@ -402,10 +499,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // before top_k tries to share; the test depends on the workgroup alone, so
   // all its waves agree.
   bool try_share = SHARE;
+  int t_of[4] = {0, 0, 0, 0};
   for (int w = 0; SHARE && w < 4; ++w) {
-    int bw = 0, tw = 0, kw = 0;
-    const bool ok = prefill_item(a, w, bw, tw, kw);
-    try_share = try_share && ok && tw < a.top_k && bw == b && kw == kvh;
+    int bw = 0, kw = 0;
+    const bool ok = prefill_item(a, w, bw, t_of[w], kw);
+    try_share = try_share && ok && t_of[w] < a.top_k && bw == b && kw == kvh;
   }
   const int live = item ? min(a.ctx[b], a.S) : 0;
   const bool active = item && t < live;
@@ -449,6 +547,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (lane == 0) s_pre[wv] = mine;
       __syncthreads();
       const int P = min(min(s_pre[0], s_pre[1]), min(s_pre[2], s_pre[3]));
+      if (a.G <= 8 && P >= 2) {
+        coop_packed<D, DT>(a, kv, b, kvh, t_of, P, s_ktile, s_ml, m_run, l_run, acc);
+        run_list<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, P);
+      } else {
       // buffer j: K tile s_ktile[2j], V tile s_ktile[2j + 1].  Loads run two
       // chunks ahead in two register stages (a wave's share is 2 + 2 rows).
       CoopStage<D> sa, sb;
@@ -479,6 +581,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       c0 = P;
       run_list<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, c0);
+      }
     } else if (any0) {
       run_chunks<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, 0, fa, id1);
     }
