@@ -211,31 +211,32 @@ __device__ void run_chunks(const int32_t *__restrict__ list, int n_slots, const 
                            const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
                            f32x4 (&acc)[8], u32x4 *ktile, int c0, Frag<D> &fa, int id_b) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  const int nchunks = (n_slots + 31) >> 5;
-  auto load_id = [&](int c) -> int {
-    int s = (c << 5) + (lane & 31);
-    return (c < nchunks && s < n_slots) ? list[s] : -1;
-  };
+  // Every load here is unconditional: a load issued on one path only would
+  // make the compiler count the wait for the chunk being consumed as if
+  // nothing were in flight after it, so that each consume would also wait
+  // for the chunk just issued.  Past the end, ids read slot n_slots - 1 and
+  // chunks read key 0, and both are dropped.  A chunk's ids are loaded ahead
+  // of the gathers issued before its turn and kept raw (range-masked only
+  // when used): loads retire in order, so waiting on an id loaded after a
+  // chunk's gathers would wait for those gathers too.
+  auto load_id = [&](int c) -> int { return list[min((c << 5) + (lane & 31), n_slots - 1)]; };
+  auto in_list = [&](int c, int idv) -> int { return (c << 5) + (lane & 31) < n_slots ? idv : -1; };
   auto usable = [&](int idv) { return wave_any((unsigned)idv < (unsigned)kv.limit); };
 
   Frag<D> fb;
   int id_c = load_id(c0 + 2);
   for (int c = c0;; c += 2) {
-    // fa holds chunk c; id_b / id_c are the ids of chunks c+1 / c+2.
-    const bool b_ok = usable(id_b);
-    int id_d = -1;
-    if (b_ok) {
-      issue_chunk<D, DT>(fb, id_b, kv, q4, r16);
-      id_d = load_id(c + 3);
-    }
+    // fa holds chunk c; id_b / id_c are the raw ids of chunks c+1 / c+2.
+    const int ib = in_list(c + 1, id_b);
+    const bool b_ok = usable(ib);
+    const int id_d = load_id(c + 3);
+    issue_chunk<D, DT>(fb, ib, kv, q4, r16);
     consume_chunk<D, DT>(fa, qf, sl2, m_run, l_run, acc, ktile);
     if (!b_ok) break;
-    const bool c_ok = usable(id_c);
-    int id_e = -1;
-    if (c_ok) {
-      issue_chunk<D, DT>(fa, id_c, kv, q4, r16);
-      id_e = load_id(c + 4);
-    }
+    const int ic = in_list(c + 2, id_c);
+    const bool c_ok = usable(ic);
+    const int id_e = load_id(c + 4);
+    issue_chunk<D, DT>(fa, ic, kv, q4, r16);
     consume_chunk<D, DT>(fb, qf, sl2, m_run, l_run, acc, ktile);
     if (!c_ok) break;
     id_b = id_d;
