@@ -260,6 +260,10 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
       }
     }
     __syncthreads();  // this chunk's kbar is consumed and its scores are in LDS
+    // Stage the next chunk before storing this one's scores: the stage waits
+    // on vmcnt, which counts stores too, so with this chunk's stores still in
+    // flight it would wait for them as well.
+    if (more) stage_chunk(g_lo + CB);
     // store the chunk's scores: 32 rows x (g_hi - g_lo) floats, 16 B per lane;
     // thread tid writes columns c4 of rows tid / 32 + 8 j
 #pragma unroll
@@ -273,7 +277,6 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
       else
         for (int q = 0; q < ncr - st_c4; ++q) dst[q] = v4[q];
     }
-    if (more) stage_chunk(g_lo + CB);
     __syncthreads();  // the next chunk's kbar is staged; the score tile is free
   }
 }
