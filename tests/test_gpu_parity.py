@@ -163,14 +163,21 @@ IDENTITY_CASES = [
     dict(B=1, S=330, Hq=8, Hkv=2, D=128, dtype="fp16", top_k=330, ctx=[330], mode="holes"),
     dict(B=1, S=90, Hq=8, Hkv=2, D=128, dtype="fp16", top_k=16, ctx=[90], mode="full"),
     dict(B=1, S=200, Hq=16, Hkv=1, D=128, dtype="bf16", top_k=200, ctx=[200], mode="full"),
+    dict(B=1, S=520, Hq=16, Hkv=2, D=128, dtype="fp16", top_k=520, ctx=[515], mode="full"),
+    dict(B=1, S=100, Hq=10, Hkv=2, D=128, dtype="bf16", top_k=100, ctx=[100], mode="full"),
+    dict(B=2, S=120, Hq=12, Hkv=1, D=64, dtype="fp16", top_k=70, ctx=[120, 50], mode="full"),
 ]
 
 
 @pytest.mark.parametrize("case", IDENTITY_CASES, ids=lambda c: f"{c['mode']}-B{c['B']}S{c['S']}Hkv{c['Hkv']}"
                          f"D{c['D']}{c['dtype']}k{c['top_k']}")
 def test_sparse_prefill_identity_prefix_lists_all_rows(case):
-    """Workgroups whose rows share an identity list head gather it once and
-    walk it together; every row must still match the oracle."""
+    """Rows before the budget fills whose lists are their whole causal prefix
+    run as dense causal tiles (rows x heads packed as MFMA columns, K/V
+    staged once per tile), and a tile holding any other list falls back to
+    the list walk; every row must match the oracle either way (tiles with
+    ragged ends, rows past the live length, dead columns when G is not a
+    power of two, G below 4 without tiles)."""
     TL.log(f"sparse_prefill identity lists {case}")
     inp = syn.make_prefill(14, B=case["B"], S=case["S"], Hq=case["Hq"], Hkv=case["Hkv"], D=case["D"],
                            dtype=case["dtype"], ctx=case["ctx"], with_indexer=False)

@@ -132,38 +132,19 @@ __device__ __forceinline__ float add_pair(uint32_t p2, float acc) {
 // XOR-swizzled by row so that both the row writes and the fragment reads are
 // free of bank conflicts.  sl2 (scale * log2 e) is positive, so the max of
 // the unscaled scores, times sl2, is the max of the scaled ones.
-// chunk_math: scores, online softmax and PV for one chunk whose K rows sit
-// in an LDS tile and whose V rows (the lane's eight key slots) are in vf.
-template <int D, int DT>
-__device__ __forceinline__ void chunk_math(const u32x4 *ktile, const u32x4 (&vf)[8], uint32_t valid, bool full,
-                                           const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
-                                           f32x4 (&acc)[8]) {
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < Frag<D>::NKS; ++ks) {
-    const u32x4 k0 = ktile[r16 * 16 + ((4 * ks + q4) ^ r16)];
-    const u32x4 k1 = ktile[(16 + r16) * 16 + ((4 * ks + q4) ^ r16)];
-    s0 = mfma16x16x32<DT>(k0, qf[ks], s0);
-    s1 = mfma16x16x32<DT>(k1, qf[ks], s1);
-  }
-  __builtin_amdgcn_wave_barrier();
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = s0[i];
-    x[4 + i] = s1[i];
-  }
-  if (!full) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = ((valid >> i) & 1u) ? x[i] : -INFINITY;
-  }
+// Probabilities of one chunk for the lane's column: the column max over the
+// 32 scores (8 per lane, lanes l, l ^ 16, l ^ 32, l ^ 48), the lazy rescale,
+// exp2 and the 16-bit packing that is the B operand of the PV product.
+template <int DT>
+__device__ __forceinline__ u32x4 chunk_probs(const float (&x)[8], float sl2, float &m_run, float &l_run,
+                                             f32x4 (&acc)[8]) {
   float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
   mx = max_xor16(mx);
   mx = max_xor32(mx);
   mx *= sl2;
   if (wave_any(mx > m_run + kLazyLog2)) {
-    // m_new is finite on every lane: all heads see the same (>= 1) usable keys
+    // m_new is finite on every lane: every column sees >= 1 usable key by
+    // its first chunk
     const float m_new = fmaxf(m_run, mx);
     const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
@@ -178,16 +159,57 @@ __device__ __forceinline__ void chunk_math(const u32x4 *ktile, const u32x4 (&vf)
                        __builtin_amdgcn_exp2f(fmaf(x[2 * w + 1], sl2, -m_run)));
     l_run = add_pair<DT>(bop[w], l_run);
   }
+  return bop;
+}
+
+// A operand of the PV product for accumulator e: V^T built in registers
+// from the lane's eight key-slot pieces.
+__device__ __forceinline__ u32x4 v_operand(const u32x4 (&vf)[8], int e) {
+  u32x4 a;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    u32x4 a;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t lo = u4_at(vf[2 * w], e >> 1), hi = u4_at(vf[2 * w + 1], e >> 1);
-      a[w] = (e & 1) ? pack_hi_hi(lo, hi) : pack_lo_lo(lo, hi);
-    }
-    acc[e] = mfma16x16x32<DT>(a, bop, acc[e]);
+  for (int w = 0; w < 4; ++w) {
+    uint32_t lo = u4_at(vf[2 * w], e >> 1), hi = u4_at(vf[2 * w + 1], e >> 1);
+    a[w] = (e & 1) ? pack_hi_hi(lo, hi) : pack_lo_lo(lo, hi);
   }
+  return a;
+}
+
+// Scores of one chunk for one 16-column tile: S^T = K Q^T as two 16-key
+// tiles; x[i] is key slot slot_of(q4, i) of column r16.
+template <int D, int DT>
+__device__ __forceinline__ void chunk_scores(const u32x4 *ktile, const u32x4 (&qf)[D / 32], float (&x)[8]) {
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < Frag<D>::NKS; ++ks) {
+    const u32x4 k0 = ktile[r16 * 16 + ((4 * ks + q4) ^ r16)];
+    const u32x4 k1 = ktile[(16 + r16) * 16 + ((4 * ks + q4) ^ r16)];
+    s0 = mfma16x16x32<DT>(k0, qf[ks], s0);
+    s1 = mfma16x16x32<DT>(k1, qf[ks], s1);
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = s0[i];
+    x[4 + i] = s1[i];
+  }
+}
+
+// chunk_math: scores, online softmax and PV for one chunk whose K rows sit
+// in an LDS tile and whose V rows (the lane's eight key slots) are in vf.
+template <int D, int DT>
+__device__ __forceinline__ void chunk_math(const u32x4 *ktile, const u32x4 (&vf)[8], uint32_t valid, bool full,
+                                           const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
+                                           f32x4 (&acc)[8]) {
+  float x[8];
+  chunk_scores<D, DT>(ktile, qf, x);
+  if (!full) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = ((valid >> i) & 1u) ? x[i] : -INFINITY;
+  }
+  const u32x4 bop = chunk_probs<DT>(x, sl2, m_run, l_run, acc);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = mfma16x16x32<DT>(v_operand(vf, e), bop, acc[e]);
 }
 
 template <int D, int DT>
@@ -266,163 +288,215 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
     qf[ks] = (r16 < G) ? ld16(qhead0 + (size_t)r16 * D + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Shared chunks.  Rows whose lists start with the identity (list[s] = s:
-// every row before the budget fills holds its whole causal prefix) need the
-// same K/V rows chunk after chunk.  When the four waves of a workgroup hold
-// such rows of one sequence and KV head, they walk the common identity
-// prefix together: per 32-slot chunk each wave gathers 8 of the 32 K and V
-// rows into a double-buffered LDS tile (same swizzle as the per-wave tile),
-// one barrier publishes it, and every wave reads its K fragments and its V
-// key slots from LDS.  The rest of each list then runs on the wave's own
-// path from the first chunk that is not shared.
-template <int D>
-struct CoopStage {
-  u32x4 k[2], v[2];
+// Dense causal tiles.  Before the budget fills (t < top_k) a row's list can
+// be its whole causal prefix in ascending order, list[s] = s for s <= t (the
+// indexer emits exactly that there), and such rows are plain causal
+// attention.  A workgroup takes a tile of consecutive rows of one sequence
+// and KV head and packs their (row, head) pairs as the 128 columns of eight
+// 16-column MFMA tiles, two per wave (column r16 of a tile = head r16 % Gp of
+// row r16 / Gp, Gp = G rounded up to a power of two).  It walks the keys
+// once: every 32-key chunk of K and V is gathered once into a double-
+// buffered LDS tile (two chunks in flight in registers, one barrier per
+// chunk) and read by all four waves, with the causal mask applied on the
+// chunks that cross the diagonal.
+//
+// While it walks, the workgroup checks every live row's list: slots s <= t
+// must hold s, and the slots after t up to the end of the next chunk must
+// hold no usable id, so that the row's own list walk would stop exactly
+// where the identity ends.  A tile that fails the check recomputes its rows
+// on the list walk, one row per wave at a time: any list gets the list
+// walk's result, identity prefixes just get it faster.  (The kernel runs
+// that walk, so that its code exists once.)
+__host__ __device__ constexpr int tile_heads(int G) { return G <= 4 ? 4 : G <= 8 ? 8 : 16; }
+// rows per tile: eight 16-column tiles of 16 / Gp rows each (G >= 4 only:
+// the list check below covers at most 32 rows)
+__host__ __device__ constexpr int tile_rows_for(int G) { return 8 * (16 / tile_heads(G)); }
+
+struct TileStage {
+  u32x4 k[2], v[2];  // K and V rows srow and 16 + srow of the chunk, one piece each
+  int id[4];         // list slots 4 tid .. 4 tid + 3 of the tile's rows x 32 slots
 };
 
-// Wave wv gathers rows 8wv .. 8wv+7 of chunk c (ids 32c + row, clamped into
-// the live range; rows past a wave's own prefix are never shared chunks).
-template <int D>
-__device__ __forceinline__ void coop_issue(CoopStage<D> &st, int c, const DenseKV &kv, int wv, int lane) {
-  const int piece = lane & 15;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 8 * wv + 4 * h + (lane >> 4);
-    const int id = min(32 * c + row, kv.limit - 1);
-    if (D == 128 || piece < D / 8) kv.load(id, piece, st.k[h], st.v[h]);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void coop_store(const CoopStage<D> &st, u32x4 *kt, u32x4 *vt, int wv, int lane) {
-  const int piece = lane & 15;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 8 * wv + 4 * h + (lane >> 4);
-    if (D == 128 || piece < D / 8) {
-      kt[row * 16 + (piece ^ (row & 15))] = st.k[h];
-      vt[row * 16 + (piece ^ (row & 15))] = st.v[h];
-    }
-  }
-}
-
-// Whole 32-slot chunks at the head of the list with list[s] = s < limit.
-__device__ __forceinline__ int identity_chunks(const int32_t *__restrict__ list, int n_slots, int limit) {
-  const int lane = lane_id();
-  int first_bad = min(n_slots, limit);
-  for (int base = 0; base < n_slots; base += 64 * 8) {
-    int v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int sidx = base + 64 * u + lane;
-      v[u] = sidx < n_slots ? list[sidx] : sidx;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int sidx = base + 64 * u + lane;
-      if (v[u] != sidx) first_bad = min(first_bad, sidx);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) first_bad = min(first_bad, __shfl_xor(first_bad, o, 64));
-    if (first_bad < base + 64 * 8) break;
-  }
-  return first_bad >> 5;
-}
-
-// Packed sharing, for GQA groups of at most 8 heads: half of each 16-column
-// MFMA tile would be padding, so on the shared identity prefix a wave takes
-// two rows at once (column 8j + h = head h of row 2p + j) and every second
-// chunk: wave 2e + p takes rows 2p, 2p + 1 and chunks c = e (mod 2).  Chunk
-// pairs are staged together (wave w gathers pair rows 16w .. 16w + 15, one
-// pair ahead in registers).  At the end the two chunk-parity halves of each
-// row are merged through LDS (rescaled to the larger reference) into the
-// state of the row's own wave, which then walks the rest of its list.
+// Output of the lane's column: O = acc / l, or +0.0 for rows past the live
+// length (their accumulators may hold values, times 0 they could give -0.0).
+// dst points at the column's (row, head) output row.
 template <int D, int DT>
-__device__ void coop_packed(const PrefillAttnArgs &a, const DenseKV &kv, int b, int kvh, const int (&t_of)[4], int P,
-                            u32x4 (*s_tiles)[32 * 16], float *s_ml, float &m_run, float &l_run, f32x4 (&acc)[8]) {
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15, piece = lane & 15;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int p = wv & 1, e = wv >> 1;
-  u32x4 qp[D / 32];
-  {
-    const int rr = 2 * p + (r16 >> 3), h = r16 & 7;
-    const uint16_t *qh = a.q + (((size_t)b * a.S + t_of[rr]) * a.Hq + (size_t)kvh * a.G + h) * D;
+__device__ __forceinline__ void store_column(uint16_t *dst, const f32x4 (&acc)[8], float l_run, bool write,
+                                             bool zero) {
+  const int q4 = lane_id() >> 4;
+  float l = l_run + shfl_xor_f(l_run, 16);
+  l += shfl_xor_f(l, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (write && 32 * q4 < D) {
+    dst += 32 * q4;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) qp[ks] = h < a.G ? ld16(qh + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+    for (int rr = 0; rr < 4; ++rr) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = zero ? 0u : pack2<DT>(acc[2 * j][rr] * inv, acc[2 * j + 1][rr] * inv);
+      st16(dst + 8 * rr, w);
+    }
   }
-  float pm = -INFINITY, pl = 0.f;
-  f32x4 pacc[8];
+}
+
+// Returns false when the check failed; nothing is written then.
+template <int D, int DT>
+__device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x4 (*s_buf)[32 * 16],
+                           int *s_flag) {
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Gp = tile_heads(a.G), RP = 16 / Gp, R = 8 * RP;
+  const int live = min(a.ctx[b], a.S);
+  const int t_end = min(t0 + R, min(a.top_k, a.S));  // the tile's rows are [t0, t_end)
+  const int t_act = min(t_end, live);                 // of which [t0, t_act) are live
+  DenseKV kv;
+  kv.k = reinterpret_cast<const char *>(a.k + ((size_t)b * a.S * a.Hkv + kvh) * D);
+  kv.v = reinterpret_cast<const char *>(a.v + ((size_t)b * a.S * a.Hkv + kvh) * D);
+  kv.row_bytes = (uint32_t)(a.Hkv * D * 2);
+  kv.limit = live;
+
+  // columns: tile u of this wave holds rows t0 + (2 wv + u) RP + r16 / Gp
+  const int h = r16 & (Gp - 1);
+  int t_col[2];
+  bool col_live[2];
+  u32x4 qp[2][D / 32];
+  f32x4 acc[2][8];
+  float m_run[2], l_run[2];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) pacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 stk[4], stv[4];
-  auto issue = [&](int j) {  // pair j = chunks 2j, 2j + 1: ids 64 j + R, R < 64
+  for (int u = 0; u < 2; ++u) {
+    t_col[u] = t0 + (2 * wv + u) * RP + r16 / Gp;
+    col_live[u] = h < a.G && t_col[u] < t_act;
+    const uint16_t *qh = a.q + (((size_t)b * a.S + t_col[u]) * a.Hq + (size_t)kvh * a.G + h) * D;
 #pragma unroll
-    for (int h2 = 0; h2 < 4; ++h2) {
-      const int R = 16 * wv + 4 * h2 + (lane >> 4);
-      const int id = min(64 * j + R, kv.limit - 1);
-      if (D == 128 || piece < D / 8) kv.load(id, piece, stk[h2], stv[h2]);
-    }
-  };
-  auto stage = [&]() {
+    for (int ks = 0; ks < D / 32; ++ks)
+      qp[u][ks] = col_live[u] ? ld16(qh + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int h2 = 0; h2 < 4; ++h2) {
-      const int R = 16 * wv + 4 * h2 + (lane >> 4);
-      const int half = R >> 5, row = R & 31;
-      if (D == 128 || piece < D / 8) {
-        s_tiles[2 * half][row * 16 + (piece ^ (row & 15))] = stk[h2];
-        s_tiles[2 * half + 1][row * 16 + (piece ^ (row & 15))] = stv[h2];
+    for (int e = 0; e < 8; ++e) acc[u][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.f;
+  }
+
+  bool ok = true;
+  if (t_act > t0) {
+    const int nch = (t_act + 31) >> 5;  // chunks holding keys [0, t_act)
+    const int srow = tid >> 4, piece = tid & 15;
+    const int32_t *lists = a.indices + (size_t)b * a.S * a.top_k;
+    // Every load is unconditional (clamped addresses; what lies past the
+    // tile or the list is dropped): the waits then count exactly.
+    auto issue = [&](TileStage &st, int c) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int id = min(32 * c + 16 * hh + srow, t_act - 1);
+        if (D == 128 || piece < D / 8) kv.load(id, piece, st.k[hh], st.v[hh]);
       }
-    }
-  };
-  const int npairs = (P + 1) >> 1;
-  issue(0);
-  stage();
-  __syncthreads();
-  for (int j = 0; j < npairs; ++j) {
-    const bool more = j + 1 < npairs;
-    if (more) issue(j + 1);
-    if (2 * j + e < P) {
-      const u32x4 *vsrc = s_tiles[2 * e + 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = 4 * tid + j;
+        const int t = min(t0 + (idx >> 5), t_act - 1), sl = min(32 * c + (idx & 31), a.top_k - 1);
+        st.id[j] = lists[(size_t)t * a.top_k + sl];
+      }
+    };
+    auto store = [&](const TileStage &st, int c, int buf) {
+      u32x4 *kt = s_buf[2 * buf], *vt = s_buf[2 * buf + 1];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 16 * hh + srow;
+        if (D == 128 || piece < D / 8) {
+          kt[row * 16 + (piece ^ (row & 15))] = st.k[hh];
+          vt[row * 16 + (piece ^ (row & 15))] = st.v[hh];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = 4 * tid + j;
+        const int t = t0 + (idx >> 5), sl = 32 * c + (idx & 31);
+        if ((idx >> 5) < R && t < t_act && sl < a.top_k)
+          ok = ok && (sl <= t ? st.id[j] == sl : (unsigned)st.id[j] >= (unsigned)live);
+      }
+    };
+    auto compute = [&](int c, int buf) {
+      const u32x4 *kt = s_buf[2 * buf], *vt = s_buf[2 * buf + 1];
+      f32x4 s0[2], s1[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) s0[u] = s1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const u32x4 k0 = kt[r16 * 16 + ((4 * ks + q4) ^ r16)];
+        const u32x4 k1 = kt[(16 + r16) * 16 + ((4 * ks + q4) ^ r16)];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          s0[u] = mfma16x16x32<DT>(k0, qp[u][ks], s0[u]);
+          s1[u] = mfma16x16x32<DT>(k1, qp[u][ks], s1[u]);
+        }
+      }
       u32x4 vf[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = slot_of(q4, i);
-        vf[i] = (D == 128 || r16 < D / 8) ? vsrc[row * 16 + (r16 ^ (row & 15))] : u32x4{0u, 0u, 0u, 0u};
+        vf[i] = (D == 128 || r16 < D / 8) ? vt[row * 16 + (r16 ^ (row & 15))] : u32x4{0u, 0u, 0u, 0u};
       }
-      chunk_math<D, DT>(s_tiles[2 * e], vf, 0xffu, true, qp, a.sl2, pm, pl, pacc);
+      const bool full = 32 * c + 31 <= t0;  // every row of the tile sees the whole chunk
+      u32x4 bop[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = s0[u][i];
+          x[4 + i] = s1[u][i];
+        }
+        if (!full) {
+          // dead columns (zero Q) keep their keys: their scores stay finite
+          const int lim = col_live[u] ? t_col[u] : 0x7fffffff;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = 32 * c + slot_of(q4, i) <= lim ? x[i] : -INFINITY;
+        }
+        bop[u] = chunk_probs<DT>(x, a.sl2, m_run[u], l_run[u], acc[u]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const u32x4 av = v_operand(vf, e);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[u][e] = mfma16x16x32<DT>(av, bop[u], acc[u][e]);
+      }
+    };
+
+    // Chunks 0 .. nch are checked, 0 .. nch - 1 computed.  Buffer 0 holds
+    // even chunks, buffer 1 odd ones; a buffer is refilled only after the
+    // barrier that follows every wave's last read of it.
+    TileStage sa, sb;
+    issue(sa, 0);
+    issue(sb, 1);
+    store(sa, 0, 0);
+    issue(sa, 2);
+    __syncthreads();
+    for (int c = 0;; c += 2) {
+      // buffer 0: chunk c; in flight: sb = chunk c + 1, sa = chunk c + 2
+      if (c < nch) compute(c, 0);
+      if (c + 1 > nch) break;
+      store(sb, c + 1, 1);
+      issue(sb, c + 3);
+      __syncthreads();
+      if (c + 1 < nch) compute(c + 1, 1);
+      if (c + 2 > nch) break;
+      store(sa, c + 2, 0);
+      issue(sa, c + 4);
+      __syncthreads();
     }
-    __syncthreads();  // the pair is consumed
-    if (more) stage();
-    __syncthreads();  // the next pair is staged
   }
-  // merge: wave w's own row r = w sits in column 8 (r & 1) + h of waves
-  // (r >> 1) (even chunks) and 2 + (r >> 1) (odd chunks)
-  float *s_acc = reinterpret_cast<float *>(s_tiles);  // [wave][32][64]
+  const bool wave_bad = wave_any(!ok);  // all lanes vote (not inside the lane-0 branch)
+  if (lane == 0) s_flag[wv] = wave_bad ? 1 : 0;
+  __syncthreads();  // also: every wave is done with the LDS buffers
+  // uniform by construction; readfirstlane lets the compiler branch on it
+  // instead of running both sides under a lane mask
+  const bool fail = __builtin_amdgcn_readfirstlane(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) != 0;
+  if (fail) return false;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) s_acc[(wv * 32 + k) * 64 + lane] = pacc[k >> 2][k & 3];
-  s_ml[(wv * 2) * 64 + lane] = pm;
-  s_ml[(wv * 2 + 1) * 64 + lane] = pl;
-  __syncthreads();
-  const int h = r16;
-  if (h < a.G && h < 8) {
-    const int src = q4 * 16 + 8 * (wv & 1) + h;
-    const int w0 = wv >> 1, w1 = 2 + (wv >> 1);
-    const float mA = s_ml[(w0 * 2) * 64 + src], mB = s_ml[(w1 * 2) * 64 + src];
-    const float M = fmaxf(mA, mB);
-    const float sA = mA == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mA - M);
-    const float sB = mB == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mB - M);
-    m_run = M;
-    l_run = s_ml[(w0 * 2 + 1) * 64 + src] * sA + s_ml[(w1 * 2 + 1) * 64 + src] * sB;
-#pragma unroll
-    for (int k = 0; k < 32; ++k)
-      acc[k >> 2][k & 3] = s_acc[(w0 * 32 + k) * 64 + src] * sA + s_acc[(w1 * 32 + k) * 64 + src] * sB;
-  } else {
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 2; ++u) {
+    uint16_t *dst = a.o + (((size_t)b * a.S + t_col[u]) * a.Hq + (size_t)kvh * a.G + h) * D;
+    store_column<D, DT>(dst, acc[u], l_run[u], h < a.G && t_col[u] < t_end, !col_live[u]);
   }
-  __syncthreads();  // the tiles are free again
+  return true;
 }
 
 // Work order.  Sequences one after another, and within a sequence rows
@@ -433,17 +507,49 @@ __device__ void coop_packed(const PrefillAttnArgs &a, const DenseKV &kv, int b, 
 // at a time, which keeps most gathers in L2 even when K/V outgrow it (every
 // list walks its ids in ascending order, so concurrent waves touch nearby
 // rows).  A workgroup's four waves take four consecutive rows of that head.
-// Otherwise a workgroup takes the Hkv heads of consecutive rows.
-__device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int wave, int &b, int &t, int &kvh) {
-  int rest;
+// Otherwise a workgroup takes the Hkv heads of consecutive rows.  Tile
+// workgroups (dense_tile) come first in a launch, longest tiles first, with
+// the same XCD-to-head mapping; their count is a multiple of 8, so the row
+// workgroups after them keep theirs.
+__device__ __forceinline__ bool tile_item(const PrefillAttnArgs &a, int &b, int &kvh, int &t0) {
+  const int ntiles = a.tile_nb * a.tile_per_seq;
+  int k;
   if ((8 % a.Hkv) == 0) {
     const int xcd = blockIdx.x & 7, n = blockIdx.x >> 3;
+    kvh = xcd % a.Hkv;
+    k = n * (8 / a.Hkv) + xcd / a.Hkv;
+  } else {
+    kvh = blockIdx.x % a.Hkv;
+    k = blockIdx.x / a.Hkv;
+  }
+  if (k >= ntiles) return false;
+  b = a.tile_b0 + k % a.tile_nb;
+  t0 = (a.tile_per_seq - 1 - k / a.tile_nb) * a.tile_rows;
+  return true;
+}
+
+static int tile_grid(const PrefillAttnArgs &a) {
+  const long long ntiles = (long long)a.tile_nb * a.tile_per_seq;
+  long long g;
+  if ((8 % a.Hkv) == 0) {
+    const long long per_head = 8 / a.Hkv;
+    g = 8 * ((ntiles + per_head - 1) / per_head);
+  } else {
+    g = ntiles * a.Hkv;
+  }
+  return (int)((g + 7) / 8 * 8);
+}
+
+__device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int blk, int wave, int &b, int &t, int &kvh) {
+  int rest;
+  if ((8 % a.Hkv) == 0) {
+    const int xcd = blk & 7, n = blk >> 3;
     const int per_head = 8 / a.Hkv;  // XCDs sharing one KV head
     kvh = xcd % a.Hkv;
     rest = ((n * per_head + xcd / a.Hkv) << 2) + wave;
     if (rest >= a.nrows) return false;
   } else {
-    const int item = blockIdx.x * 4 + wave;
+    const int item = blk * 4 + wave;
     if (item >= a.nrows * a.Hkv) return false;
     kvh = item % a.Hkv;
     rest = item / a.Hkv;
@@ -482,126 +588,55 @@ static int prefill_rows_per_launch(const PrefillAttnArgs &a, int D) {
   return max(64, kSyncWaves / a.Hkv);
 }
 
-// SHARE = false: every wave walks its own list.  SHARE = true (launched
-// only over rows t < top_k, where lists can be whole causal prefixes):
-// workgroups may share identity chunks.  Two kernels, because the sharing
-// code, even untaken, costs the plain walk registers and scheduling.
-template <int D, int DT, bool SHARE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(PrefillAttnArgs a) {
-  __shared__ u32x4 s_ktile[4][32 * 16];
-  __shared__ int s_key[4], s_pre[4];
-  __shared__ float s_ml[SHARE ? 4 * 2 * 64 : 1];
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  u32x4 *ktile = s_ktile[wv];
+// One row (sequence b, position t, KV head kvh) on the list walk: Q of the
+// head group, the walk, the output (zeros past the live length).
+template <int D, int DT>
+__device__ __forceinline__ void walk_row(const PrefillAttnArgs &a, int b, int t, int kvh, u32x4 *ktile) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  int b = 0, t = 0, kvh = 0;
-  const bool item = prefill_item(a, wv, b, t, kvh);
-  // Only a workgroup whose four rows are of one (sequence, KV head) and lie
-  // before top_k tries to share; the test depends on the workgroup alone, so
-  // all its waves agree.
-  bool try_share = SHARE;
-  int t_of[4] = {0, 0, 0, 0};
-  for (int w = 0; SHARE && w < 4; ++w) {
-    int bw = 0, kw = 0;
-    const bool ok = prefill_item(a, w, bw, t_of[w], kw);
-    try_share = try_share && ok && t_of[w] < a.top_k && bw == b && kw == kvh;
-  }
-  const int live = item ? min(a.ctx[b], a.S) : 0;
-  const bool active = item && t < live;
-  const int32_t *list = a.indices + ((size_t)b * a.S + t) * a.top_k;
+  const int live = min(a.ctx[b], a.S);
   DenseKV kv;
   kv.k = reinterpret_cast<const char *>(a.k + ((size_t)b * a.S * a.Hkv + kvh) * D);
   kv.v = reinterpret_cast<const char *>(a.v + ((size_t)b * a.S * a.Hkv + kvh) * D);
   kv.row_bytes = (uint32_t)(a.Hkv * D * 2);
   kv.limit = live;
-
   f32x4 acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  u32x4 qf[D / 32];
   const size_t qo_off = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
-  if (!try_share) {
-    if (active) {
-      load_q<D>(qf, a.q + qo_off, a.G, q4, r16);
-      run_list<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile);
-    }
-  } else if constexpr (SHARE) {
-    // Q first (its loads must be older than the gathers, or the loop's waits
-    // on qf would also wait for the chunk in flight), then the first chunk's
-    // gathers, then the decision: the workgroup shares only if all four rows
-    // are live and their first chunks are the identity.
-    if (active) load_q<D>(qf, a.q + qo_off, a.G, q4, r16);
-    const int s0 = lane & 31;
-    const int id0 = active && s0 < a.top_k ? list[s0] : -1;
-    const int id1 = active && s0 + 32 < a.top_k ? list[s0 + 32] : -1;
-    const bool any0 = wave_any((unsigned)id0 < (unsigned)live);
-    Frag<D> fa;
-    if (any0) issue_chunk<D, DT>(fa, id0, kv, q4, r16);
-    const bool first_identity = active && a.top_k >= 32 && !wave_any(id0 != s0 || s0 >= live);
-    if (lane == 0) s_key[wv] = first_identity ? 1 : 0;
-    __syncthreads();
-    const bool coop = s_key[0] + s_key[1] + s_key[2] + s_key[3] == 4;
-    if (coop) {
-      int c0 = 0;
-      const int mine = identity_chunks(list, a.top_k, live);
-      if (lane == 0) s_pre[wv] = mine;
-      __syncthreads();
-      const int P = min(min(s_pre[0], s_pre[1]), min(s_pre[2], s_pre[3]));
-      if (a.G <= 8 && P >= 2) {
-        coop_packed<D, DT>(a, kv, b, kvh, t_of, P, s_ktile, s_ml, m_run, l_run, acc);
-        run_list<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, P);
-      } else {
-      // buffer j: K tile s_ktile[2j], V tile s_ktile[2j + 1].  Loads run two
-      // chunks ahead in two register stages (a wave's share is 2 + 2 rows).
-      CoopStage<D> sa, sb;
-      if (P > 0) {
-        coop_issue<D>(sa, 0, kv, wv, lane);
-        coop_store<D>(sa, s_ktile[0], s_ktile[1], wv, lane);
-        if (P > 1) coop_issue<D>(sa, 1, kv, wv, lane);
-        if (P > 2) coop_issue<D>(sb, 2, kv, wv, lane);
-      }
-      __syncthreads();
-      auto coop_chunk = [&](int c, CoopStage<D> &next) {
-        // buffer c & 1 holds chunk c; `next` holds chunk c + 1 in flight
-        const u32x4 *vsrc = s_ktile[2 * (c & 1) + 1];
-        u32x4 vf[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int row = slot_of(q4, i);
-          vf[i] = (D == 128 || r16 < D / 8) ? vsrc[row * 16 + (r16 ^ (row & 15))] : u32x4{0u, 0u, 0u, 0u};
-        }
-        chunk_math<D, DT>(s_ktile[2 * (c & 1)], vf, 0xffu, true, qf, a.sl2, m_run, l_run, acc);
-        if (c + 1 < P) coop_store<D>(next, s_ktile[2 * ((c + 1) & 1)], s_ktile[2 * ((c + 1) & 1) + 1], wv, lane);
-        if (c + 3 < P) coop_issue<D>(next, c + 3, kv, wv, lane);
-        __syncthreads();
-      };
-      for (int c = 0; c < P; c += 2) {
-        coop_chunk(c, sa);
-        if (c + 1 < P) coop_chunk(c + 1, sb);
-      }
-      c0 = P;
-      run_list<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, c0);
-      }
-    } else if (any0) {
-      run_chunks<D, DT>(list, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile, 0, fa, id1);
-    }
+  if (t < live) {
+    u32x4 qf[D / 32];
+    load_q<D>(qf, a.q + qo_off, a.G, q4, r16);
+    run_list<D, DT>(a.indices + ((size_t)b * a.S + t) * a.top_k, a.top_k, kv, qf, a.sl2, m_run, l_run, acc, ktile);
   }
-  if (!item) return;
-  float l = l_run + shfl_xor_f(l_run, 16);
-  l += shfl_xor_f(l, 32);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (r16 < a.G && 32 * q4 < D) {
-    uint16_t *dst = a.o + qo_off + (size_t)r16 * D + 32 * q4;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      u32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = pack2<DT>(acc[2 * j][rr] * inv, acc[2 * j + 1][rr] * inv);
-      st16(dst + 8 * rr, w);
+  store_column<D, DT>(a.o + qo_off + (size_t)r16 * D, acc, l_run, r16 < a.G, false);
+}
+
+// TILES = false: every wave walks its own list.  TILES = true: the launch
+// starts with dense_tile workgroups, and the row walk skips rows below
+// skip_below (the tiles hold them).  Two kernels, so that rows that never
+// meet a tile keep the leaner register allocation of the plain walk.
+template <int D, int DT, bool TILES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(PrefillAttnArgs a) {
+  __shared__ u32x4 s_ktile[4][32 * 16];
+  __shared__ int s_flag[4];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int blk = blockIdx.x;
+  if constexpr (TILES) {
+    if (blk < a.tile_blocks) {
+      int b = 0, kvh = 0, t0 = 0;
+      if (!tile_item(a, b, kvh, t0)) return;
+      if (dense_tile<D, DT>(a, b, kvh, t0, s_ktile, s_flag)) return;
+      // the tile failed its check: its rows go through the list walk
+      const int t_end = min(t0 + a.tile_rows, min(a.top_k, a.S));
+      for (int t = t0 + wv; t < t_end; t += 4) walk_row<D, DT>(a, b, t, kvh, s_ktile[wv]);
+      return;
     }
+    blk -= a.tile_blocks;
   }
+  int b = 0, t = 0, kvh = 0;
+  if (!prefill_item(a, blk, wv, b, t, kvh) || t < a.skip_below) return;
+  walk_row<D, DT>(a, b, t, kvh, s_ktile[wv]);
 }
 
 // Decode: one wave per (sequence, KV head, split); the waves of a workgroup
@@ -771,37 +806,67 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
 }
 
 template <int D, int DT>
-static hipError_t launch_prefill_t(const PrefillAttnArgs &a, hipStream_t s) {
-  // One launch of the sharing kernel over every row, unless the rows go out
-  // in several launches anyway (see prefill_rows_per_launch): then, per
-  // sequence, rows t >= top_k run on the plain kernel and rows t < top_k on
-  // the sharing kernel, each range in launches of at most `per` rows.  (A
-  // single launch keeps short prefix rows filling in behind long rows; the
-  // plain kernel is ~2-3 % faster on rows that never share.)
-  const int per = prefill_rows_per_launch(a, D);
-  const int plain = max(0, a.S - a.top_k);
-  auto run = [&](int r0, int n, bool share) -> hipError_t {
-    for (int o = 0; o < n; o += per) {
+static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
+  // Rows t < tk = min(top_k, S) of every sequence go to dense tiles (when
+  // G >= 4), the rest to the row walk.  One launch holds the tiles and all
+  // rows unless the rows go out in several launches anyway (see
+  // prefill_rows_per_launch).
+  PrefillAttnArgs a = a0;
+  const int tk = min(a.top_k, a.S);
+  const bool tiles = a.G >= 4;
+  a.tile_rows = tile_rows_for(a.G);
+  a.tile_per_seq = (tk + a.tile_rows - 1) / a.tile_rows;
+  a.tile_b0 = a.tile_nb = a.tile_blocks = 0;
+  a.skip_below = 0;
+  auto launch = [&](PrefillAttnArgs p, int b0, int nb) -> hipError_t {
+    p.tile_b0 = b0;
+    p.tile_nb = nb;
+    p.tile_blocks = nb > 0 ? tile_grid(p) : 0;
+    const unsigned grid = (unsigned)p.tile_blocks + (p.nrows > 0 ? prefill_grid(p) : 0u);
+    if (grid == 0) return hipSuccess;
+    if (nb > 0)
+      hipLaunchKernelGGL((sparse_prefill_kernel<D, DT, true>), dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((sparse_prefill_kernel<D, DT, false>), dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+  };
+  const int total = a.B * a.S, per = prefill_rows_per_launch(a, D);
+  if (!tiles) {
+    for (int o = 0; o < total; o += per) {
       PrefillAttnArgs p = a;
-      p.row0 = r0 + o;
-      p.nrows = min(per, n - o);
-      if (share)
-        hipLaunchKernelGGL((sparse_prefill_kernel<D, DT, true>), dim3(prefill_grid(p)), dim3(256), 0, s, p);
-      else
-        hipLaunchKernelGGL((sparse_prefill_kernel<D, DT, false>), dim3(prefill_grid(p)), dim3(256), 0, s, p);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      p.row0 = o;
+      p.nrows = min(per, total - o);
+      if (hipError_t e = launch(p, 0, 0)) return e;
     }
     return hipSuccess;
-  };
-  if (a.top_k < 32) return run(0, a.B * a.S, false);  // no identity chunk fits
-  if (per >= a.B * a.S) return run(0, a.B * a.S, true);
-  for (int b = 0; b < a.B; ++b) {
-    hipError_t e = run(b * a.S, plain, false);
-    if (e == hipSuccess) e = run(b * a.S + plain, a.S - plain, true);
-    if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  if (per >= total) {
+    PrefillAttnArgs p = a;
+    p.row0 = 0;
+    if (a.B == 1) {
+      p.nrows = a.S - tk;  // rows t >= tk come first in the work order
+    } else {
+      p.nrows = total;
+      p.skip_below = tk;
+    }
+    return launch(p, 0, a.B);
+  }
+  // Several launches: the row launches rely on their workgroups starting
+  // together (see prefill_rows_per_launch), and tiles in front of them would
+  // stagger those starts, so all sequences' tiles get a launch of their own
+  // after the rows.
+  const int n = a.S - tk;  // row-walk rows of a sequence: work order [b S, b S + n)
+  for (int b = 0; b < a.B; ++b) {
+    for (int o = 0; o < n; o += per) {
+      PrefillAttnArgs p = a;
+      p.row0 = b * a.S + o;
+      p.nrows = min(per, n - o);
+      if (hipError_t e = launch(p, 0, 0)) return e;
+    }
+  }
+  PrefillAttnArgs p = a;
+  p.row0 = p.nrows = 0;
+  return launch(p, 0, a.B);
 }
 
 hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStream_t s) {
