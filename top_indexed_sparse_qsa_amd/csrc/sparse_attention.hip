@@ -376,7 +376,7 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
     l_run[u] = 0.f;
   }
 
-  bool ok = true;
+  bool bad = false;
   if (t_act > t0) {
     const int nch = (t_act + 31) >> 5;  // chunks holding keys [0, t_act)
     const int srow = tid >> 4, piece = tid & 15;
@@ -406,12 +406,15 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
           vt[row * 16 + (piece ^ (row & 15))] = st.v[hh];
         }
       }
+      // branch-free (bitwise): a branch here would split the loop into
+      // blocks the scheduler cannot interleave
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int idx = 4 * tid + j;
-        const int t = t0 + (idx >> 5), sl = 32 * c + (idx & 31);
-        if ((idx >> 5) < R && t < t_act && sl < a.top_k)
-          ok = ok && (sl <= t ? st.id[j] == sl : (unsigned)st.id[j] >= (unsigned)live);
+        const int t = t0 + (idx >> 5), sl = 32 * c + (idx & 31), id = st.id[j];
+        const bool checked = ((idx >> 5) < R) & (t < t_act) & (sl < a.top_k);
+        const bool good = sl <= t ? id == sl : (unsigned)id >= (unsigned)live;
+        bad |= checked & !good;
       }
     };
     auto compute = [&](int c, int buf) {
@@ -484,7 +487,7 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
       __syncthreads();
     }
   }
-  const bool wave_bad = wave_any(!ok);  // all lanes vote (not inside the lane-0 branch)
+  const bool wave_bad = wave_any(bad);  // all lanes vote (not inside the lane-0 branch)
   if (lane == 0) s_flag[wv] = wave_bad ? 1 : 0;
   __syncthreads();  // also: every wave is done with the LDS buffers
   // uniform by construction; readfirstlane lets the compiler branch on it
