@@ -314,7 +314,7 @@ __host__ __device__ constexpr int tile_rows_for(int G) { return 8 * (16 / tile_h
 
 struct TileStage {
   u32x4 k[2], v[2];  // K and V rows srow and 16 + srow of the chunk, one piece each
-  int id[4];         // list slots 4 tid .. 4 tid + 3 of the tile's rows x 32 slots
+  int id[4];         // four list slots of one tile row (see my_list)
 };
 
 // Output of the lane's column: O = acc / l, or +0.0 for rows past the live
@@ -380,7 +380,13 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
   if (t_act > t0) {
     const int nch = (t_act + 31) >> 5;  // chunks holding keys [0, t_act)
     const int srow = tid >> 4, piece = tid & 15;
-    const int32_t *lists = a.indices + (size_t)b * a.S * a.top_k;
+    // the thread checks list slots 4 (tid & 7) .. + 3 of each chunk for row
+    // t0 + (tid >> 3): one 16-byte load per chunk (list rows are only 4-byte
+    // aligned, which global loads accept); the window is clamped into the
+    // row (top_k >= 32 with tiles), so it may re-read slots another thread
+    // checks, never slots past the row
+    const int32_t *my_list =
+        a.indices + ((size_t)b * a.S + min(t0 + (tid >> 3), t_act - 1)) * a.top_k;
     // Every load is unconditional (clamped addresses; what lies past the
     // tile or the list is dropped): the waits then count exactly.
     auto issue = [&](TileStage &st, int c) {
@@ -389,12 +395,10 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
         const int id = min(32 * c + 16 * hh + srow, t_act - 1);
         if (D == 128 || piece < D / 8) kv.load(id, piece, st.k[hh], st.v[hh]);
       }
+      typedef int i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+      const i32x4_a4 ids = *reinterpret_cast<const i32x4_a4 *>(my_list + min(32 * c + 4 * (tid & 7), a.top_k - 4));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = 4 * tid + j;
-        const int t = min(t0 + (idx >> 5), t_act - 1), sl = min(32 * c + (idx & 31), a.top_k - 1);
-        st.id[j] = lists[(size_t)t * a.top_k + sl];
-      }
+      for (int j = 0; j < 4; ++j) st.id[j] = ids[j];
     };
     auto store = [&](const TileStage &st, int c, int buf) {
       u32x4 *kt = s_buf[2 * buf], *vt = s_buf[2 * buf + 1];
@@ -408,13 +412,13 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
       }
       // branch-free (bitwise): a branch here would split the loop into
       // blocks the scheduler cannot interleave
+      const int t = t0 + (tid >> 3), sl0 = min(32 * c + 4 * (tid & 7), a.top_k - 4);
+      const bool row_checked = ((tid >> 3) < R) & (t < t_act) & (32 * c + 4 * (tid & 7) < a.top_k);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int idx = 4 * tid + j;
-        const int t = t0 + (idx >> 5), sl = 32 * c + (idx & 31), id = st.id[j];
-        const bool checked = ((idx >> 5) < R) & (t < t_act) & (sl < a.top_k);
+        const int sl = sl0 + j, id = st.id[j];
         const bool good = sl <= t ? id == sl : (unsigned)id >= (unsigned)live;
-        bad |= checked & !good;
+        bad |= row_checked & !good;
       }
     };
     auto compute = [&](int c, int buf) {
@@ -514,16 +518,16 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
 // workgroups (dense_tile) come first in a launch, longest tiles first, with
 // the same XCD-to-head mapping; their count is a multiple of 8, so the row
 // workgroups after them keep theirs.
-__device__ __forceinline__ bool tile_item(const PrefillAttnArgs &a, int &b, int &kvh, int &t0) {
+__device__ __forceinline__ bool tile_item(const PrefillAttnArgs &a, int blk, int &b, int &kvh, int &t0) {
   const int ntiles = a.tile_nb * a.tile_per_seq;
   int k;
   if ((8 % a.Hkv) == 0) {
-    const int xcd = blockIdx.x & 7, n = blockIdx.x >> 3;
+    const int xcd = blk & 7, n = blk >> 3;
     kvh = xcd % a.Hkv;
     k = n * (8 / a.Hkv) + xcd / a.Hkv;
   } else {
-    kvh = blockIdx.x % a.Hkv;
-    k = blockIdx.x / a.Hkv;
+    kvh = blk % a.Hkv;
+    k = blk / a.Hkv;
   }
   if (k >= ntiles) return false;
   b = a.tile_b0 + k % a.tile_nb;
@@ -628,7 +632,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if constexpr (TILES) {
     if (blk < a.tile_blocks) {
       int b = 0, kvh = 0, t0 = 0;
-      if (!tile_item(a, b, kvh, t0)) return;
+      if (!tile_item(a, blk, b, kvh, t0)) return;
       if (dense_tile<D, DT>(a, b, kvh, t0, s_ktile, s_flag)) return;
       // the tile failed its check: its rows go through the list walk
       const int t_end = min(t0 + a.tile_rows, min(a.top_k, a.S));
@@ -816,7 +820,7 @@ static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
   // prefill_rows_per_launch).
   PrefillAttnArgs a = a0;
   const int tk = min(a.top_k, a.S);
-  const bool tiles = a.G >= 4;
+  const bool tiles = a.G >= 4 && a.top_k >= 32;
   a.tile_rows = tile_rows_for(a.G);
   a.tile_per_seq = (tk + a.tile_rows - 1) / a.tile_rows;
   a.tile_b0 = a.tile_nb = a.tile_blocks = 0;
