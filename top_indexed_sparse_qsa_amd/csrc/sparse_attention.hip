@@ -135,7 +135,10 @@ __device__ __forceinline__ float add_pair(uint32_t p2, float acc) {
 // Probabilities of one chunk for the lane's column: the column max over the
 // 32 scores (8 per lane, lanes l, l ^ 16, l ^ 32, l ^ 48), the lazy rescale,
 // exp2 and the 16-bit packing that is the B operand of the PV product.
-template <int DT>
+// MAYBE_EMPTY: a column may have had no key yet (m_run = -inf, masked
+// scores -inf); its probabilities must then be exp2(-inf) = 0 rather than
+// exp2(-inf + inf).
+template <int DT, bool MAYBE_EMPTY = false>
 __device__ __forceinline__ u32x4 chunk_probs(const float (&x)[8], float sl2, float &m_run, float &l_run,
                                              f32x4 (&acc)[8]) {
   float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -143,8 +146,9 @@ __device__ __forceinline__ u32x4 chunk_probs(const float (&x)[8], float sl2, flo
   mx = max_xor32(mx);
   mx *= sl2;
   if (wave_any(mx > m_run + kLazyLog2)) {
-    // m_new is finite on every lane: every column sees >= 1 usable key by
-    // its first chunk
+    // m_new is finite on every lane of the list walk (every column sees >= 1
+    // usable key by its first chunk); a masked column with no key yet keeps
+    // -inf and alpha = 0 on its zero accumulators
     const float m_new = fmaxf(m_run, mx);
     const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
@@ -152,11 +156,12 @@ __device__ __forceinline__ u32x4 chunk_probs(const float (&x)[8], float sl2, flo
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
     m_run = m_new;
   }
+  const float m_ref = MAYBE_EMPTY && m_run == -INFINITY ? 0.f : m_run;
   u32x4 bop;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    bop[w] = pack2<DT>(__builtin_amdgcn_exp2f(fmaf(x[2 * w], sl2, -m_run)),
-                       __builtin_amdgcn_exp2f(fmaf(x[2 * w + 1], sl2, -m_run)));
+    bop[w] = pack2<DT>(__builtin_amdgcn_exp2f(fmaf(x[2 * w], sl2, -m_ref)),
+                       __builtin_amdgcn_exp2f(fmaf(x[2 * w + 1], sl2, -m_ref)));
     l_run = add_pair<DT>(bop[w], l_run);
   }
   return bop;
@@ -288,33 +293,40 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
     qf[ks] = (r16 < G) ? ld16(qhead0 + (size_t)r16 * D + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Dense causal tiles.  Before the budget fills (t < top_k) a row's list can
-// be its whole causal prefix in ascending order, list[s] = s for s <= t (the
-// indexer emits exactly that there), and such rows are plain causal
-// attention.  A workgroup takes a tile of consecutive rows of one sequence
-// and KV head and packs their (row, head) pairs as the 128 columns of eight
+// Tiles.  Where a row's list covers a large part of its causal prefix —
+// before the budget fills (t < top_k) it is the whole prefix, and at short
+// lengths it is half or more of it — walking all of the prefix densely with
+// a key mask is cheaper than gathering the listed rows: the gathers are
+// bound by on-chip gather throughput, the dense walk by MFMA and LDS.  A
+// tile workgroup takes 8 * 16 / Gp consecutive rows of one (sequence, KV
+// head) (Gp = G rounded up to a power of two, G >= 4: 16 rows at G = 8, 8 at
+// G = 16) and packs the (row, head) pairs as the 128 columns of eight
 // 16-column MFMA tiles, two per wave (column r16 of a tile = head r16 % Gp of
-// row r16 / Gp, Gp = G rounded up to a power of two).  It walks the keys
-// once: every 32-key chunk of K and V is gathered once into a double-
-// buffered LDS tile (two chunks in flight in registers, one barrier per
-// chunk) and read by all four waves, with the causal mask applied on the
-// chunks that cross the diagonal.
+// row r16 / Gp).
 //
-// While it walks, the workgroup checks every live row's list: slots s <= t
-// must hold s, and the slots after t up to the end of the next chunk must
-// hold no usable id, so that the row's own list walk would stop exactly
-// where the identity ends.  A tile that fails the check recomputes its rows
-// on the list walk, one row per wave at a time: any list gets the list
-// walk's result, identity prefixes just get it faster.  (The kernel runs
-// that walk, so that its code exists once.)
+// First the rows' lists become a key bitmask in LDS (one bit per key of
+// [0, t_act) per row, set by LDS atomic-or).  The mask reproduces exactly
+// the keys the list walk would use, or the tile gives up: an id repeated in
+// a list, a usable id at or past t_act (outside the causal range), or a
+// usable id after a 32-slot chunk with none (where the walk stops) sends the
+// tile's rows to the list walk, one row per wave at a time (the kernel runs
+// that walk, so its code exists once).
+//
+// Then the workgroup walks the keys once: every 32-key chunk of K and V is
+// gathered once into a double-buffered LDS tile (two chunks in flight in
+// registers, one barrier per chunk) and read by all four waves; the K and V
+// fragments serve both column tiles of a wave; a wave whose columns have no
+// key in a chunk skips it, and the mask is applied only where some column
+// misses a key.
 __host__ __device__ constexpr int tile_heads(int G) { return G <= 4 ? 4 : G <= 8 ? 8 : 16; }
-// rows per tile: eight 16-column tiles of 16 / Gp rows each (G >= 4 only:
-// the list check below covers at most 32 rows)
+// rows per tile: eight 16-column tiles of 16 / Gp rows each (G >= 4 only)
 __host__ __device__ constexpr int tile_rows_for(int G) { return 8 * (16 / tile_heads(G)); }
+// key-mask words of a tile workgroup (rows x 32-key chunks): 16 KB of LDS,
+// which bounds the tiled rows to t < 32 * kTileMaskWords / rows per tile
+constexpr int kTileMaskWords = 4096;
 
 struct TileStage {
   u32x4 k[2], v[2];  // K and V rows srow and 16 + srow of the chunk, one piece each
-  int id[4];         // four list slots of one tile row (see my_list)
 };
 
 // Output of the lane's column: O = acc / l, or +0.0 for rows past the live
@@ -339,68 +351,145 @@ __device__ __forceinline__ void store_column(uint16_t *dst, const f32x4 (&acc)[8
   }
 }
 
-// Returns false when the check failed; nothing is written then.
+// The key mask of the tile's live rows [t0, t_act): row r's words are
+// s_mask[r * W .. r * W + W).  Returns (on every lane of a wave that found
+// it) true when the lists need the walk.  Wave w builds rows w, w + 4, ...:
+// lane l reads slot quads l + 64 k of the row (16-byte loads; list rows are
+// only 4-byte aligned, which global loads accept), every load of a row
+// issued before any is used, and sets its usable ids' bits with
+// non-returning LDS or.  The walk's view is checked without atomics: the
+// 32-slot chunks holding usable ids must be a prefix of the row's chunks
+// (lanes 8m .. 8m + 7 hold one chunk; a ballot per load), no usable id may
+// lie at or past t_act, and after a barrier the row's mask must hold as many
+// bits as the row has usable ids (a repeated id sets one bit twice).
+__device__ __forceinline__ bool build_key_mask(const PrefillAttnArgs &a, int b, int t0, int t_act, int live, int W,
+                                               uint32_t *s_mask, int *s_cnt) {
+  typedef int i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+  const int lane = lane_id(), tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nr = t_act - t0;
+  const int nchunk = (a.top_k + 31) >> 5;  // 32-slot chunks of a list
+  const int nload = (nchunk + 7) >> 3;     // 64 quads = 8 chunks per load round
+  for (int i = tid; i < nr * W; i += 256) s_mask[i] = 0u;
+  __syncthreads();
+  bool bad = false;
+  for (int r = wv; r < nr; r += 4) {
+    int cnt = 0;  // usable ids of the row (wave-uniform)
+    const int32_t *row = a.indices + ((size_t)b * a.S + t0 + r) * a.top_k;
+    bool seen_empty = false;  // a chunk without usable ids came before
+    for (int k0 = 0; k0 < nload; k0 += 4) {
+      i32x4_a4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const i32x4_a4 *>(row + min(4 * (64 * (k0 + k) + lane), a.top_k - 4));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int q = 64 * (k0 + k) + lane;
+        const int s0 = min(4 * q, a.top_k - 4);  // slot of v[k].x
+        bool any = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sl = s0 + e, id = v[k][e];
+          // a slot counts once: only in the quad it belongs to (4q .. 4q+3)
+          const bool usable = (sl >= 4 * q) & (sl < a.top_k) & ((unsigned)id < (unsigned)live);
+          any |= usable;
+          cnt += __builtin_popcountll(__ballot(usable));
+          bad |= usable & (id >= t_act);
+          if (usable & (id < t_act)) __hip_atomic_fetch_or(&s_mask[r * W + (id >> 5)], 1u << (id & 31),
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        // chunks 8 (k0 + k) + m, m < 8: the used ones must be a prefix of
+        // the row's chunks (wave-uniform bookkeeping)
+        const uint64_t bal = __ballot(any);
+        uint32_t ub = 0;  // bit m: lanes 8m .. 8m + 7 hold a usable id
+#pragma unroll
+        for (int m = 0; m < 8; ++m) ub |= (uint32_t)(((bal >> (8 * m)) & 0xffull) != 0) << m;
+        const int here = min(8, nchunk - 8 * (k0 + k));  // chunks of the row in this round
+        if (here > 0) {
+          const uint32_t ex = (1u << here) - 1u;
+          bad |= ((ub & (ub + 1u)) != 0u) | (seen_empty & (ub != 0u));
+          seen_empty |= ub != ex;
+        }
+      }
+    }
+    if (lane == 0) s_cnt[r] = cnt;
+  }
+  __syncthreads();
+  for (int r = wv; r < nr; r += 4) {
+    int bits = 0;
+    for (int w = lane; w < W; w += 64) bits += __builtin_popcount(s_mask[r * W + w]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) bits += __shfl_xor(bits, o, 64);
+    bad |= bits != s_cnt[r];
+  }
+  return bad;
+}
+
+// Returns false when the tile's lists need the list walk; nothing is written then.
 template <int D, int DT>
-__device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x4 (*s_buf)[32 * 16],
-                           int *s_flag) {
+__device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x4 (*s_buf)[32 * 16],
+                          uint32_t *s_mask, int *s_cnt, int *s_flag) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Gp = tile_heads(a.G), RP = 16 / Gp, R = 8 * RP;
   const int live = min(a.ctx[b], a.S);
-  const int t_end = min(t0 + R, min(a.top_k, a.S));  // the tile's rows are [t0, t_end)
-  const int t_act = min(t_end, live);                 // of which [t0, t_act) are live
+  const int t_end = min(t0 + R, a.tile_below);  // the tile's rows are [t0, t_end)
+  const int t_act = min(t_end, live);           // of which [t0, t_act) are live
   DenseKV kv;
   kv.k = reinterpret_cast<const char *>(a.k + ((size_t)b * a.S * a.Hkv + kvh) * D);
   kv.v = reinterpret_cast<const char *>(a.v + ((size_t)b * a.S * a.Hkv + kvh) * D);
   kv.row_bytes = (uint32_t)(a.Hkv * D * 2);
   kv.limit = live;
 
-  // columns: tile u of this wave holds rows t0 + (2 wv + u) RP + r16 / Gp
+  // columns: tile u of this wave holds local row (2 wv + u) RP + r16 / Gp
   const int h = r16 & (Gp - 1);
-  int t_col[2];
+  int r_col[2];
   bool col_live[2];
   u32x4 qp[2][D / 32];
   f32x4 acc[2][8];
   float m_run[2], l_run[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    t_col[u] = t0 + (2 * wv + u) * RP + r16 / Gp;
-    col_live[u] = h < a.G && t_col[u] < t_act;
-    const uint16_t *qh = a.q + (((size_t)b * a.S + t_col[u]) * a.Hq + (size_t)kvh * a.G + h) * D;
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      qp[u][ks] = col_live[u] ? ld16(qh + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+    r_col[u] = (2 * wv + u) * RP + r16 / Gp;
+    col_live[u] = h < a.G && t0 + r_col[u] < t_act;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[u][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[u] = -INFINITY;
     l_run[u] = 0.f;
   }
 
-  bool bad = false;
+  bool fail = false;
   if (t_act > t0) {
-    const int nch = (t_act + 31) >> 5;  // chunks holding keys [0, t_act)
+    const int W = (t_act + 31) >> 5, nch = W;  // 32-key chunks of [0, t_act), mask words per row
+    const bool wave_bad = wave_any(build_key_mask(a, b, t0, t_act, live, W, s_mask, s_cnt));
+    if (lane == 0) s_flag[wv] = wave_bad ? 1 : 0;
+    __syncthreads();
+    // uniform by construction; readfirstlane lets the compiler branch on it
+    // instead of running both sides under a lane mask
+    fail = __builtin_amdgcn_readfirstlane(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) != 0;
+  }
+  if (!fail && t_act > t0) {
+    const int W = (t_act + 31) >> 5, nch = W;
+    // Q after the mask build, so that it does not stay live through it
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint16_t *qh = a.q + (((size_t)b * a.S + t0 + r_col[u]) * a.Hq + (size_t)kvh * a.G + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        qp[u][ks] = col_live[u] ? ld16(qh + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+    }
     const int srow = tid >> 4, piece = tid & 15;
-    // the thread checks list slots 4 (tid & 7) .. + 3 of each chunk for row
-    // t0 + (tid >> 3): one 16-byte load per chunk (list rows are only 4-byte
-    // aligned, which global loads accept); the window is clamped into the
-    // row (top_k >= 32 with tiles), so it may re-read slots another thread
-    // checks, never slots past the row
-    const int32_t *my_list =
-        a.indices + ((size_t)b * a.S + min(t0 + (tid >> 3), t_act - 1)) * a.top_k;
+    // dead columns (zero Q) get no key: with no key seen, a column's
+    // probabilities are 0 (chunk_probs<.., true>)
+    const uint32_t *mrow[2] = {s_mask + min(r_col[0], t_act - t0 - 1) * W, s_mask + min(r_col[1], t_act - t0 - 1) * W};
     // Every load is unconditional (clamped addresses; what lies past the
-    // tile or the list is dropped): the waits then count exactly.
+    // keys is dropped): the waits then count exactly.
     auto issue = [&](TileStage &st, int c) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int id = min(32 * c + 16 * hh + srow, t_act - 1);
         if (D == 128 || piece < D / 8) kv.load(id, piece, st.k[hh], st.v[hh]);
       }
-      typedef int i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-      const i32x4_a4 ids = *reinterpret_cast<const i32x4_a4 *>(my_list + min(32 * c + 4 * (tid & 7), a.top_k - 4));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st.id[j] = ids[j];
     };
-    auto store = [&](const TileStage &st, int c, int buf) {
+    auto store = [&](const TileStage &st, int buf) {
       u32x4 *kt = s_buf[2 * buf], *vt = s_buf[2 * buf + 1];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -410,18 +499,12 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
           vt[row * 16 + (piece ^ (row & 15))] = st.v[hh];
         }
       }
-      // branch-free (bitwise): a branch here would split the loop into
-      // blocks the scheduler cannot interleave
-      const int t = t0 + (tid >> 3), sl0 = min(32 * c + 4 * (tid & 7), a.top_k - 4);
-      const bool row_checked = ((tid >> 3) < R) & (t < t_act) & (32 * c + 4 * (tid & 7) < a.top_k);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int sl = sl0 + j, id = st.id[j];
-        const bool good = sl <= t ? id == sl : (unsigned)id >= (unsigned)live;
-        bad |= row_checked & !good;
-      }
     };
     auto compute = [&](int c, int buf) {
+      uint32_t word[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) word[u] = col_live[u] ? mrow[u][c] : 0u;
+      if (!wave_any((word[0] | word[1]) != 0u)) return;  // no column of this wave has a key here
       const u32x4 *kt = s_buf[2 * buf], *vt = s_buf[2 * buf + 1];
       f32x4 s0[2], s1[2];
 #pragma unroll
@@ -442,7 +525,7 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
         const int row = slot_of(q4, i);
         vf[i] = (D == 128 || r16 < D / 8) ? vt[row * 16 + (r16 ^ (row & 15))] : u32x4{0u, 0u, 0u, 0u};
       }
-      const bool full = 32 * c + 31 <= t0;  // every row of the tile sees the whole chunk
+      const bool full = !wave_any((word[0] & word[1]) != 0xffffffffu);  // every column sees every key
       u32x4 bop[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -453,12 +536,13 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
           x[4 + i] = s1[u][i];
         }
         if (!full) {
-          // dead columns (zero Q) keep their keys: their scores stay finite
-          const int lim = col_live[u] ? t_col[u] : 0x7fffffff;
+          // key slot slot_of(q4, i) = 4 q4 + i (i < 4), 12 + 4 q4 + i: shift
+          // once by 4 q4, then by constants
+          const uint32_t wq = word[u] >> (4 * q4);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = 32 * c + slot_of(q4, i) <= lim ? x[i] : -INFINITY;
+          for (int i = 0; i < 8; ++i) x[i] = (wq >> (i < 4 ? i : 12 + i)) & 1u ? x[i] : -INFINITY;
         }
-        bop[u] = chunk_probs<DT>(x, a.sl2, m_run[u], l_run[u], acc[u]);
+        bop[u] = chunk_probs<DT, true>(x, a.sl2, m_run[u], l_run[u], acc[u]);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -468,40 +552,34 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
       }
     };
 
-    // Chunks 0 .. nch are checked, 0 .. nch - 1 computed.  Buffer 0 holds
-    // even chunks, buffer 1 odd ones; a buffer is refilled only after the
-    // barrier that follows every wave's last read of it.
+    // Buffer 0 holds even chunks, buffer 1 odd ones; a buffer is refilled
+    // only after the barrier that follows every wave's last read of it.
     TileStage sa, sb;
     issue(sa, 0);
     issue(sb, 1);
-    store(sa, 0, 0);
+    store(sa, 0);
     issue(sa, 2);
     __syncthreads();
     for (int c = 0;; c += 2) {
       // buffer 0: chunk c; in flight: sb = chunk c + 1, sa = chunk c + 2
-      if (c < nch) compute(c, 0);
-      if (c + 1 > nch) break;
-      store(sb, c + 1, 1);
+      compute(c, 0);
+      if (c + 1 >= nch) break;
+      store(sb, 1);
       issue(sb, c + 3);
       __syncthreads();
-      if (c + 1 < nch) compute(c + 1, 1);
-      if (c + 2 > nch) break;
-      store(sa, c + 2, 0);
+      compute(c + 1, 1);
+      if (c + 2 >= nch) break;
+      store(sa, 0);
       issue(sa, c + 4);
       __syncthreads();
     }
   }
-  const bool wave_bad = wave_any(bad);  // all lanes vote (not inside the lane-0 branch)
-  if (lane == 0) s_flag[wv] = wave_bad ? 1 : 0;
-  __syncthreads();  // also: every wave is done with the LDS buffers
-  // uniform by construction; readfirstlane lets the compiler branch on it
-  // instead of running both sides under a lane mask
-  const bool fail = __builtin_amdgcn_readfirstlane(s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) != 0;
   if (fail) return false;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    uint16_t *dst = a.o + (((size_t)b * a.S + t_col[u]) * a.Hq + (size_t)kvh * a.G + h) * D;
-    store_column<D, DT>(dst, acc[u], l_run[u], h < a.G && t_col[u] < t_end, !col_live[u]);
+    const int t = t0 + r_col[u];
+    uint16_t *dst = a.o + (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G + h) * D;
+    store_column<D, DT>(dst, acc[u], l_run[u], h < a.G && t < t_end, !col_live[u]);
   }
   return true;
 }
@@ -515,7 +593,7 @@ __device__ bool dense_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32
 // list walks its ids in ascending order, so concurrent waves touch nearby
 // rows).  A workgroup's four waves take four consecutive rows of that head.
 // Otherwise a workgroup takes the Hkv heads of consecutive rows.  Tile
-// workgroups (dense_tile) come first in a launch, longest tiles first, with
+// workgroups (list_tile) come first in a launch, longest tiles first, with
 // the same XCD-to-head mapping; their count is a multiple of 8, so the row
 // workgroups after them keep theirs.
 __device__ __forceinline__ bool tile_item(const PrefillAttnArgs &a, int blk, int &b, int &kvh, int &t0) {
@@ -620,22 +698,23 @@ __device__ __forceinline__ void walk_row(const PrefillAttnArgs &a, int b, int t,
 }
 
 // TILES = false: every wave walks its own list.  TILES = true: the launch
-// starts with dense_tile workgroups, and the row walk skips rows below
+// starts with list_tile workgroups, and the row walk skips rows below
 // skip_below (the tiles hold them).  Two kernels, so that rows that never
 // meet a tile keep the leaner register allocation of the plain walk.
 template <int D, int DT, bool TILES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(PrefillAttnArgs a) {
   __shared__ u32x4 s_ktile[4][32 * 16];
-  __shared__ int s_flag[4];
+  __shared__ uint32_t s_mask[TILES ? kTileMaskWords : 1];
+  __shared__ int s_cnt[TILES ? 32 : 1], s_flag[4];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int blk = blockIdx.x;
   if constexpr (TILES) {
     if (blk < a.tile_blocks) {
       int b = 0, kvh = 0, t0 = 0;
       if (!tile_item(a, blk, b, kvh, t0)) return;
-      if (dense_tile<D, DT>(a, b, kvh, t0, s_ktile, s_flag)) return;
-      // the tile failed its check: its rows go through the list walk
-      const int t_end = min(t0 + a.tile_rows, min(a.top_k, a.S));
+      if (list_tile<D, DT>(a, b, kvh, t0, s_ktile, s_mask, s_cnt, s_flag)) return;
+      // the tile's lists need the walk
+      const int t_end = min(t0 + a.tile_rows, a.tile_below);
       for (int t = t0 + wv; t < t_end; t += 4) walk_row<D, DT>(a, b, t, kvh, s_ktile[wv]);
       return;
     }
@@ -812,16 +891,32 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
   }
 }
 
+// Tiles take rows t with t + 1 <= kTileRangeX2 / 2 * top_k * R / 16 (R rows
+// per tile).  At R = 16 a dense walk of a 32-key chunk costs a row ~1/2.6 of
+// what gathering 32 listed keys costs the list walk (workload 2: all 4096
+// rows as tiles 147 us, the 2045 rows t >= top_k on the walk 188 us for half
+// the row-keys); a tile's chunk costs the same for any R, so a row's share
+// scales with 1/R, while the walk's cost per row does not depend on G.
+#ifndef QSA_TILE_RANGE_X2
+#define QSA_TILE_RANGE_X2 5
+#endif
+constexpr int kTileRangeX2 = QSA_TILE_RANGE_X2;
+
 template <int D, int DT>
 static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
-  // Rows t < tk = min(top_k, S) of every sequence go to dense tiles (when
-  // G >= 4), the rest to the row walk.  One launch holds the tiles and all
-  // rows unless the rows go out in several launches anyway (see
-  // prefill_rows_per_launch).
+  // Rows t < tk of every sequence go to tiles (when G >= 4), the rest to the
+  // list walk: rows whose causal range is short enough next to the list
+  // (see kTileRangeX2) and whose key mask fits the tile's LDS.  One launch holds
+  // the tiles and all rows unless the rows go out in several launches anyway
+  // (see prefill_rows_per_launch).
   PrefillAttnArgs a = a0;
-  const int tk = min(a.top_k, a.S);
-  const bool tiles = a.G >= 4 && a.top_k >= 32;
   a.tile_rows = tile_rows_for(a.G);
+  long long tkl = (long long)kTileRangeX2 * a.top_k * a.tile_rows / 32;
+  if (tkl > a.S) tkl = a.S;
+  if (tkl > 32LL * kTileMaskWords / a.tile_rows) tkl = 32LL * kTileMaskWords / a.tile_rows;
+  const int tk = (int)tkl;
+  const bool tiles = a.G >= 4 && a.top_k >= 4;
+  a.tile_below = tk;
   a.tile_per_seq = (tk + a.tile_rows - 1) / a.tile_rows;
   a.tile_b0 = a.tile_nb = a.tile_blocks = 0;
   a.skip_below = 0;
