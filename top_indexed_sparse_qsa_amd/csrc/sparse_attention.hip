@@ -892,13 +892,16 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
 }
 
 // Tiles take rows t with t + 1 <= kTileRangeX2 / 2 * top_k * R / 16 (R rows
-// per tile).  At R = 16 a dense walk of a 32-key chunk costs a row ~1/2.6 of
+// per tile, kTileRangeX2 / 2 = 3.5).  At R = 16 a dense walk of a 32-key chunk costs a row ~1/2.6 of
 // what gathering 32 listed keys costs the list walk (workload 2: all 4096
 // rows as tiles 147 us, the 2045 rows t >= top_k on the walk 188 us for half
 // the row-keys); a tile's chunk costs the same for any R, so a row's share
-// scales with 1/R, while the walk's cost per row does not depend on G.
+// scales with 1/R, while the walk's cost per row does not depend on G.  The
+// break-even measured on whole calls sits higher than that ratio (rows near
+// it keep the walk's gathers off L2 for the other rows): 3.5 beat 1.5, 2.5
+// and 5 on workloads 3 and 5.
 #ifndef QSA_TILE_RANGE_X2
-#define QSA_TILE_RANGE_X2 5
+#define QSA_TILE_RANGE_X2 7
 #endif
 constexpr int kTileRangeX2 = QSA_TILE_RANGE_X2;
 
