@@ -14,10 +14,10 @@ struct PrefillAttnArgs {
   int B, S, Hq, Hkv, G, top_k;
   float sl2;  // attention scale * log2(e)
   int row0, nrows;  // this launch covers rows [row0, row0 + nrows) of the work order
-  // tiles of rows t < tile_below: the launch's first tile_blocks workgroups
-  // take the tiles of sequences [tile_b0, tile_b0 + tile_nb), tile_per_seq
-  // tiles of tile_rows rows each per sequence
-  int tile_blocks, tile_rows, tile_per_seq, tile_b0, tile_nb, tile_below;
+  // tiles of rows t < tile_below: a tile launch takes the tiles of
+  // sequences [tile_b0, tile_b0 + tile_nb), tile_per_seq tiles of tile_rows
+  // rows each per sequence
+  int tile_rows, tile_per_seq, tile_b0, tile_nb, tile_below;
   int skip_below;  // the row walk skips rows t < skip_below (held by tiles)
 };
 

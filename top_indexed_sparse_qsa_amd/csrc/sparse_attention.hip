@@ -319,8 +319,12 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
 // key in a chunk skips it, and the mask is applied only where some column
 // misses a key.
 __host__ __device__ constexpr int tile_heads(int G) { return G <= 4 ? 4 : G <= 8 ? 8 : 16; }
-// rows per tile: eight 16-column tiles of 16 / Gp rows each (G >= 4 only)
-__host__ __device__ constexpr int tile_rows_for(int G) { return 8 * (16 / tile_heads(G)); }
+// 16-column MFMA tiles per wave: one (147 VGPRs, three waves per SIMD),
+// except at Gp = 16 where a column tile is a single row and two per wave
+// (216 VGPRs, two waves per SIMD) keep eight rows per tile.
+__host__ __device__ constexpr int tile_nt(int G) { return tile_heads(G) == 16 ? 2 : 1; }
+// rows per tile: 4 * NT 16-column tiles of 16 / Gp rows each (G >= 4 only)
+__host__ __device__ constexpr int tile_rows_for(int G) { return 4 * tile_nt(G) * (16 / tile_heads(G)); }
 // key-mask words of a tile workgroup (rows x 32-key chunks): 16 KB of LDS,
 // which bounds the tiled rows to t < 32 * kTileMaskWords / rows per tile
 constexpr int kTileMaskWords = 4096;
@@ -424,12 +428,12 @@ __device__ __forceinline__ bool build_key_mask(const PrefillAttnArgs &a, int b, 
 }
 
 // Returns false when the tile's lists need the list walk; nothing is written then.
-template <int D, int DT>
+template <int D, int DT, int NT>
 __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x4 (*s_buf)[32 * 16],
                           uint32_t *s_mask, int *s_cnt, int *s_flag) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Gp = tile_heads(a.G), RP = 16 / Gp, R = 8 * RP;
+  const int Gp = tile_heads(a.G), RP = 16 / Gp, R = 4 * NT * RP;
   const int live = min(a.ctx[b], a.S);
   const int t_end = min(t0 + R, a.tile_below);  // the tile's rows are [t0, t_end)
   const int t_act = min(t_end, live);           // of which [t0, t_act) are live
@@ -441,14 +445,14 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
 
   // columns: tile u of this wave holds local row (2 wv + u) RP + r16 / Gp
   const int h = r16 & (Gp - 1);
-  int r_col[2];
-  bool col_live[2];
-  u32x4 qp[2][D / 32];
-  f32x4 acc[2][8];
-  float m_run[2], l_run[2];
+  int r_col[NT];
+  bool col_live[NT];
+  u32x4 qp[NT][D / 32];
+  f32x4 acc[NT][8];
+  float m_run[NT], l_run[NT];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    r_col[u] = (2 * wv + u) * RP + r16 / Gp;
+  for (int u = 0; u < NT; ++u) {
+    r_col[u] = (NT * wv + u) * RP + r16 / Gp;
     col_live[u] = h < a.G && t0 + r_col[u] < t_act;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[u][e] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -470,7 +474,7 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
     const int W = (t_act + 31) >> 5, nch = W;
     // Q after the mask build, so that it does not stay live through it
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NT; ++u) {
       const uint16_t *qh = a.q + (((size_t)b * a.S + t0 + r_col[u]) * a.Hq + (size_t)kvh * a.G + h) * D;
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
@@ -479,7 +483,9 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
     const int srow = tid >> 4, piece = tid & 15;
     // dead columns (zero Q) get no key: with no key seen, a column's
     // probabilities are 0 (chunk_probs<.., true>)
-    const uint32_t *mrow[2] = {s_mask + min(r_col[0], t_act - t0 - 1) * W, s_mask + min(r_col[1], t_act - t0 - 1) * W};
+    const uint32_t *mrow[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) mrow[u] = s_mask + min(r_col[u], t_act - t0 - 1) * W;
     // Every load is unconditional (clamped addresses; what lies past the
     // keys is dropped): the waits then count exactly.
     auto issue = [&](TileStage &st, int c) {
@@ -501,20 +507,26 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
       }
     };
     auto compute = [&](int c, int buf) {
-      uint32_t word[2];
+      uint32_t word[NT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) word[u] = col_live[u] ? mrow[u][c] : 0u;
-      if (!wave_any((word[0] | word[1]) != 0u)) return;  // no column of this wave has a key here
+      for (int u = 0; u < NT; ++u) word[u] = col_live[u] ? mrow[u][c] : 0u;
+      uint32_t any_w = 0u, all_w = 0xffffffffu;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        any_w |= word[u];
+        all_w &= word[u];
+      }
+      if (!wave_any(any_w != 0u)) return;  // no column of this wave has a key here
       const u32x4 *kt = s_buf[2 * buf], *vt = s_buf[2 * buf + 1];
-      f32x4 s0[2], s1[2];
+      f32x4 s0[NT], s1[NT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) s0[u] = s1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < NT; ++u) s0[u] = s1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
         const u32x4 k0 = kt[r16 * 16 + ((4 * ks + q4) ^ r16)];
         const u32x4 k1 = kt[(16 + r16) * 16 + ((4 * ks + q4) ^ r16)];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NT; ++u) {
           s0[u] = mfma16x16x32<DT>(k0, qp[u][ks], s0[u]);
           s1[u] = mfma16x16x32<DT>(k1, qp[u][ks], s1[u]);
         }
@@ -525,10 +537,10 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
         const int row = slot_of(q4, i);
         vf[i] = (D == 128 || r16 < D / 8) ? vt[row * 16 + (r16 ^ (row & 15))] : u32x4{0u, 0u, 0u, 0u};
       }
-      const bool full = !wave_any((word[0] & word[1]) != 0xffffffffu);  // every column sees every key
-      u32x4 bop[2];
+      const bool full = !wave_any(all_w != 0xffffffffu);  // every column sees every key
+      u32x4 bop[NT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NT; ++u) {
         float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -548,7 +560,7 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
       for (int e = 0; e < 8; ++e) {
         const u32x4 av = v_operand(vf, e);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) acc[u][e] = mfma16x16x32<DT>(av, bop[u], acc[u][e]);
+        for (int u = 0; u < NT; ++u) acc[u][e] = mfma16x16x32<DT>(av, bop[u], acc[u][e]);
       }
     };
 
@@ -576,7 +588,7 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
   }
   if (fail) return false;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NT; ++u) {
     const int t = t0 + r_col[u];
     uint16_t *dst = a.o + (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G + h) * D;
     store_column<D, DT>(dst, acc[u], l_run[u], h < a.G && t < t_end, !col_live[u]);
@@ -593,9 +605,8 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
 // list walks its ids in ascending order, so concurrent waves touch nearby
 // rows).  A workgroup's four waves take four consecutive rows of that head.
 // Otherwise a workgroup takes the Hkv heads of consecutive rows.  Tile
-// workgroups (list_tile) come first in a launch, longest tiles first, with
-// the same XCD-to-head mapping; their count is a multiple of 8, so the row
-// workgroups after them keep theirs.
+// workgroups (list_tile) go out longest tiles first, with the same
+// XCD-to-head mapping.
 __device__ __forceinline__ bool tile_item(const PrefillAttnArgs &a, int blk, int &b, int &kvh, int &t0) {
   const int ntiles = a.tile_nb * a.tile_per_seq;
   int k;
@@ -613,16 +624,13 @@ __device__ __forceinline__ bool tile_item(const PrefillAttnArgs &a, int blk, int
   return true;
 }
 
-static int tile_grid(const PrefillAttnArgs &a) {
+static unsigned tile_grid(const PrefillAttnArgs &a) {
   const long long ntiles = (long long)a.tile_nb * a.tile_per_seq;
-  long long g;
   if ((8 % a.Hkv) == 0) {
     const long long per_head = 8 / a.Hkv;
-    g = 8 * ((ntiles + per_head - 1) / per_head);
-  } else {
-    g = ntiles * a.Hkv;
+    return (unsigned)(8 * ((ntiles + per_head - 1) / per_head));
   }
-  return (int)((g + 7) / 8 * 8);
+  return (unsigned)(ntiles * a.Hkv);
 }
 
 __device__ __forceinline__ bool prefill_item(const PrefillAttnArgs &a, int blk, int wave, int &b, int &t, int &kvh) {
@@ -697,31 +705,97 @@ __device__ __forceinline__ void walk_row(const PrefillAttnArgs &a, int b, int t,
   store_column<D, DT>(a.o + qo_off + (size_t)r16 * D, acc, l_run, r16 < a.G, false);
 }
 
-// TILES = false: every wave walks its own list.  TILES = true: the launch
-// starts with list_tile workgroups, and the row walk skips rows below
-// skip_below (the tiles hold them).  Two kernels, so that rows that never
-// meet a tile keep the leaner register allocation of the plain walk.
-template <int D, int DT, bool TILES>
+// The list walk for rows [t0, t_end) of a tile whose lists the key mask
+// cannot represent (a repeated id, an id outside the causal range, ids
+// after the walk's stop): one row at a time, all four waves stage each
+// 32-slot chunk's K/V rows in LDS and wave 0 runs the online softmax over
+// the usable slots, stopping at the first chunk without one — the list
+// walk's result, at the tile's small register budget.  Rare (lists that
+// break the contract), so simple rather than fast.
+template <int D, int DT>
+__device__ void tile_walk_rows(const PrefillAttnArgs &a, int b, int kvh, int t0, int t_end, u32x4 (*s_buf)[32 * 16],
+                               int *s_slot) {
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int srow = tid >> 4, piece = tid & 15;
+  const int live = min(a.ctx[b], a.S);
+  DenseKV kv;
+  kv.k = reinterpret_cast<const char *>(a.k + ((size_t)b * a.S * a.Hkv + kvh) * D);
+  kv.v = reinterpret_cast<const char *>(a.v + ((size_t)b * a.S * a.Hkv + kvh) * D);
+  kv.row_bytes = (uint32_t)(a.Hkv * D * 2);
+  kv.limit = live;
+  u32x4 *kt = s_buf[0], *vt = s_buf[1];
+  for (int t = t0; t < t_end; ++t) {
+    const int32_t *list = a.indices + ((size_t)b * a.S + t) * a.top_k;
+    const size_t qo_off = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
+    f32x4 acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    u32x4 qf[D / 32];
+    load_q<D>(qf, a.q + qo_off, a.G, q4, r16);
+    for (int c = 0; t < live && 32 * c < a.top_k; ++c) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int slot = 16 * hh + srow, sl = 32 * c + slot;
+        const int id = sl < a.top_k ? list[sl] : -1;
+        const bool ok = (unsigned)id < (unsigned)live;
+        u32x4 kd, vd;
+        kv.load(ok ? id : 0, piece, kd, vd);
+        if (D == 128 || piece < D / 8) {
+          kt[slot * 16 + (piece ^ (slot & 15))] = kd;
+          vt[slot * 16 + (piece ^ (slot & 15))] = vd;
+        }
+        if (piece == 0) s_slot[slot] = ok ? 1 : 0;
+      }
+      __syncthreads();
+      const uint32_t word = (uint32_t)__ballot(s_slot[lane & 31] != 0);  // bit s: slot s usable
+      if (word == 0u) break;  // the walk stops at a chunk without usable ids (uniform)
+      if (wv == 0) {
+        float x[8];
+        chunk_scores<D, DT>(kt, qf, x);
+        const uint32_t wq = word >> (4 * q4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (wq >> (i < 4 ? i : 12 + i)) & 1u ? x[i] : -INFINITY;
+        const u32x4 bop = chunk_probs<DT, true>(x, a.sl2, m_run, l_run, acc);
+        u32x4 vf[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = slot_of(q4, i);
+          vf[i] = (D == 128 || r16 < D / 8) ? vt[row * 16 + (r16 ^ (row & 15))] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = mfma16x16x32<DT>(v_operand(vf, e), bop, acc[e]);
+      }
+      __syncthreads();  // the chunk's LDS is consumed
+    }
+    if (wv == 0) store_column<D, DT>(a.o + qo_off + (size_t)r16 * D, acc, l_run, r16 < a.G, false);
+    __syncthreads();
+  }
+}
+
+// Tile workgroups: one tile each (tile_item), with the register budget of
+// the tile alone (three waves per SIMD fit at NT = 1).
+template <int D, int DT, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, NT == 1 ? 3 : 2))) void
+sparse_prefill_tile_kernel(PrefillAttnArgs a) {
+  __shared__ u32x4 s_ktile[4][32 * 16];
+  __shared__ uint32_t s_mask[kTileMaskWords];
+  __shared__ int s_cnt[32], s_flag[4];
+  int b = 0, kvh = 0, t0 = 0;
+  if (!tile_item(a, blockIdx.x, b, kvh, t0)) return;
+  if (list_tile<D, DT, NT>(a, b, kvh, t0, s_ktile, s_mask, s_cnt, s_flag)) return;
+  tile_walk_rows<D, DT>(a, b, kvh, t0, min(t0 + a.tile_rows, a.tile_below), s_ktile, s_cnt);
+}
+
+// Row workgroups: every wave walks its own list; rows below skip_below
+// belong to tiles.
+template <int D, int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(PrefillAttnArgs a) {
   __shared__ u32x4 s_ktile[4][32 * 16];
-  __shared__ uint32_t s_mask[TILES ? kTileMaskWords : 1];
-  __shared__ int s_cnt[TILES ? 32 : 1], s_flag[4];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int blk = blockIdx.x;
-  if constexpr (TILES) {
-    if (blk < a.tile_blocks) {
-      int b = 0, kvh = 0, t0 = 0;
-      if (!tile_item(a, blk, b, kvh, t0)) return;
-      if (list_tile<D, DT>(a, b, kvh, t0, s_ktile, s_mask, s_cnt, s_flag)) return;
-      // the tile's lists need the walk
-      const int t_end = min(t0 + a.tile_rows, a.tile_below);
-      for (int t = t0 + wv; t < t_end; t += 4) walk_row<D, DT>(a, b, t, kvh, s_ktile[wv]);
-      return;
-    }
-    blk -= a.tile_blocks;
-  }
   int b = 0, t = 0, kvh = 0;
-  if (!prefill_item(a, blk, wv, b, t, kvh) || t < a.skip_below) return;
+  if (!prefill_item(a, blockIdx.x, wv, b, t, kvh) || t < a.skip_below) return;
   walk_row<D, DT>(a, b, t, kvh, s_ktile[wv]);
 }
 
@@ -909,43 +983,48 @@ template <int D, int DT>
 static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
   // Rows t < tk of every sequence go to tiles (when G >= 4), the rest to the
   // list walk: rows whose causal range is short enough next to the list
-  // (see kTileRangeX2) and whose key mask fits the tile's LDS.  One launch holds
-  // the tiles and all rows unless the rows go out in several launches anyway
-  // (see prefill_rows_per_launch).
+  // (see kTileRangeX2) and whose key mask fits the tile's LDS.  Tiles and
+  // rows have kernels of their own (their register budgets differ: three
+  // waves per SIMD for tiles, two for the walk).
   PrefillAttnArgs a = a0;
   a.tile_rows = tile_rows_for(a.G);
-  long long tkl = (long long)kTileRangeX2 * a.top_k * a.tile_rows / 32;
+  long long tkl = (long long)kTileRangeX2 * a.top_k * (16 / tile_heads(a.G)) / 4;
   if (tkl > a.S) tkl = a.S;
   if (tkl > 32LL * kTileMaskWords / a.tile_rows) tkl = 32LL * kTileMaskWords / a.tile_rows;
   const int tk = (int)tkl;
-  const bool tiles = a.G >= 4 && a.top_k >= 4;
+  const bool tiles_on = a.G >= 4 && a.top_k >= 4;
   a.tile_below = tk;
   a.tile_per_seq = (tk + a.tile_rows - 1) / a.tile_rows;
-  a.tile_b0 = a.tile_nb = a.tile_blocks = 0;
+  a.tile_b0 = a.tile_nb = 0;
   a.skip_below = 0;
-  auto launch = [&](PrefillAttnArgs p, int b0, int nb) -> hipError_t {
+  auto rows = [&](PrefillAttnArgs p) -> hipError_t {
+    if (p.nrows <= 0) return hipSuccess;
+    hipLaunchKernelGGL((sparse_prefill_kernel<D, DT>), dim3(prefill_grid(p)), dim3(256), 0, s, p);
+    return hipGetLastError();
+  };
+  auto tiles = [&](int b0, int nb) -> hipError_t {
+    PrefillAttnArgs p = a;
     p.tile_b0 = b0;
     p.tile_nb = nb;
-    p.tile_blocks = nb > 0 ? tile_grid(p) : 0;
-    const unsigned grid = (unsigned)p.tile_blocks + (p.nrows > 0 ? prefill_grid(p) : 0u);
-    if (grid == 0) return hipSuccess;
-    if (nb > 0)
-      hipLaunchKernelGGL((sparse_prefill_kernel<D, DT, true>), dim3(grid), dim3(256), 0, s, p);
+    if (p.tile_per_seq <= 0) return hipSuccess;
+    if (tile_nt(a.G) == 1)
+      hipLaunchKernelGGL((sparse_prefill_tile_kernel<D, DT, 1>), dim3(tile_grid(p)), dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((sparse_prefill_kernel<D, DT, false>), dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((sparse_prefill_tile_kernel<D, DT, 2>), dim3(tile_grid(p)), dim3(256), 0, s, p);
     return hipGetLastError();
   };
   const int total = a.B * a.S, per = prefill_rows_per_launch(a, D);
-  if (!tiles) {
+  if (!tiles_on) {
     for (int o = 0; o < total; o += per) {
       PrefillAttnArgs p = a;
       p.row0 = o;
       p.nrows = min(per, total - o);
-      if (hipError_t e = launch(p, 0, 0)) return e;
+      if (hipError_t e = rows(p)) return e;
     }
     return hipSuccess;
   }
   if (per >= total) {
+    if (hipError_t e = tiles(0, a.B)) return e;
     PrefillAttnArgs p = a;
     p.row0 = 0;
     if (a.B == 1) {
@@ -954,24 +1033,20 @@ static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
       p.nrows = total;
       p.skip_below = tk;
     }
-    return launch(p, 0, a.B);
+    return rows(p);
   }
-  // Several launches: the row launches rely on their workgroups starting
-  // together (see prefill_rows_per_launch), and tiles in front of them would
-  // stagger those starts, so all sequences' tiles get a launch of their own
-  // after the rows.
+  // Several row launches (each relies on its workgroups starting together,
+  // see prefill_rows_per_launch), then the tiles of every sequence.
   const int n = a.S - tk;  // row-walk rows of a sequence: work order [b S, b S + n)
   for (int b = 0; b < a.B; ++b) {
     for (int o = 0; o < n; o += per) {
       PrefillAttnArgs p = a;
       p.row0 = b * a.S + o;
       p.nrows = min(per, n - o);
-      if (hipError_t e = launch(p, 0, 0)) return e;
+      if (hipError_t e = rows(p)) return e;
     }
   }
-  PrefillAttnArgs p = a;
-  p.row0 = p.nrows = 0;
-  return launch(p, 0, a.B);
+  return tiles(0, a.B);
 }
 
 hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStream_t s) {
