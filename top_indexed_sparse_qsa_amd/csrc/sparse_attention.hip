@@ -359,27 +359,27 @@ __device__ __forceinline__ void store_column(uint16_t *dst, const f32x4 (&acc)[8
 // s_mask[r * W .. r * W + W).  Returns (on every lane of a wave that found
 // it) true when the lists need the walk.  Wave w builds rows w, w + 4, ...:
 // lane l reads slot quads l + 64 k of the row (16-byte loads; list rows are
-// only 4-byte aligned, which global loads accept), every load of a row
-// issued before any is used, and sets its usable ids' bits with
-// non-returning LDS or.  The walk's view is checked without atomics: the
-// 32-slot chunks holding usable ids must be a prefix of the row's chunks
-// (lanes 8m .. 8m + 7 hold one chunk; a ballot per load), no usable id may
-// lie at or past t_act, and after a barrier the row's mask must hold as many
-// bits as the row has usable ids (a repeated id sets one bit twice).
+// only 4-byte aligned, which global loads accept), four loads in flight, and
+// sets its usable ids' bits with non-returning LDS or (one per quad when its
+// ids share a 32-bit word, as the indexer's 4-key blocks do).  The walk's
+// view is checked without atomics: the 32-slot chunks holding usable ids
+// must be chunks 0 .. n-1 (their count equals the last one's index + 1;
+// lanes 8m .. 8m + 7 hold one chunk), no usable id may lie at or past t_act,
+// and after a barrier the row's mask must hold as many bits as the row has
+// usable ids (a repeated id sets one bit twice).
 __device__ __forceinline__ bool build_key_mask(const PrefillAttnArgs &a, int b, int t0, int t_act, int live, int W,
                                                uint32_t *s_mask, int *s_cnt) {
   typedef int i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
   const int lane = lane_id(), tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nr = t_act - t0;
-  const int nchunk = (a.top_k + 31) >> 5;  // 32-slot chunks of a list
-  const int nload = (nchunk + 7) >> 3;     // 64 quads = 8 chunks per load round
+  const int nload = (a.top_k + 255) >> 8;  // 64 quads = 8 chunks per load
   for (int i = tid; i < nr * W; i += 256) s_mask[i] = 0u;
   __syncthreads();
   bool bad = false;
   for (int r = wv; r < nr; r += 4) {
-    int cnt = 0;  // usable ids of the row (wave-uniform)
     const int32_t *row = a.indices + ((size_t)b * a.S + t0 + r) * a.top_k;
-    bool seen_empty = false;  // a chunk without usable ids came before
+    int cnt = 0;                      // this lane's usable ids
+    int used_chunks = 0, last = -1;   // wave-uniform
     for (int k0 = 0; k0 < nload; k0 += 4) {
       i32x4_a4 v[4];
 #pragma unroll
@@ -388,32 +388,48 @@ __device__ __forceinline__ bool build_key_mask(const PrefillAttnArgs &a, int b, 
       for (int k = 0; k < 4; ++k) {
         const int q = 64 * (k0 + k) + lane;
         const int s0 = min(4 * q, a.top_k - 4);  // slot of v[k].x
-        bool any = false;
+        bool u[4];
+        uint32_t bits = 0u;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int sl = s0 + e, id = v[k][e];
           // a slot counts once: only in the quad it belongs to (4q .. 4q+3)
-          const bool usable = (sl >= 4 * q) & (sl < a.top_k) & ((unsigned)id < (unsigned)live);
-          any |= usable;
-          cnt += __builtin_popcountll(__ballot(usable));
-          bad |= usable & (id >= t_act);
-          if (usable & (id < t_act)) __hip_atomic_fetch_or(&s_mask[r * W + (id >> 5)], 1u << (id & 31),
-                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          u[e] = (sl >= 4 * q) & (sl < a.top_k) & ((unsigned)id < (unsigned)live);
+          cnt += u[e] ? 1 : 0;
+          bad |= u[e] & (id >= t_act);
+          bits |= u[e] & (id < t_act) ? 1u << (id & 31) : 0u;
         }
-        // chunks 8 (k0 + k) + m, m < 8: the used ones must be a prefix of
-        // the row's chunks (wave-uniform bookkeeping)
-        const uint64_t bal = __ballot(any);
-        uint32_t ub = 0;  // bit m: lanes 8m .. 8m + 7 hold a usable id
+        const int id0 = v[k][0];
+        const bool one_word = ((!u[1]) | ((v[k][1] >> 5) == (id0 >> 5))) & ((!u[2]) | ((v[k][2] >> 5) == (id0 >> 5))) &
+                              ((!u[3]) | ((v[k][3] >> 5) == (id0 >> 5)));
+        if (u[0] & one_word) {
+          if (bits != 0u)
+            __hip_atomic_fetch_or(&s_mask[r * W + (id0 >> 5)], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) ub |= (uint32_t)(((bal >> (8 * m)) & 0xffull) != 0) << m;
-        const int here = min(8, nchunk - 8 * (k0 + k));  // chunks of the row in this round
-        if (here > 0) {
-          const uint32_t ex = (1u << here) - 1u;
-          bad |= ((ub & (ub + 1u)) != 0u) | (seen_empty & (ub != 0u));
-          seen_empty |= ub != ex;
+          for (int e = 0; e < 4; ++e) {
+            const int id = v[k][e];
+            if (u[e] & (id < t_act))
+              __hip_atomic_fetch_or(&s_mask[r * W + (id >> 5)], 1u << (id & 31), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+        }
+        // chunks 8 (k0 + k) + m: bit 8m of f is set when lanes 8m .. 8m + 7
+        // hold a usable id
+        uint64_t f = __ballot(u[0] | u[1] | u[2] | u[3]);
+        f |= f >> 4;
+        f |= f >> 2;
+        f |= f >> 1;
+        f &= 0x0101010101010101ull;
+        if (f != 0ull) {
+          used_chunks += __builtin_popcountll(f);
+          last = 8 * (k0 + k) + ((63 - __builtin_clzll(f)) >> 3);
         }
       }
     }
+    bad |= used_chunks != last + 1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
     if (lane == 0) s_cnt[r] = cnt;
   }
   __syncthreads();
