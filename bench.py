@@ -7,10 +7,12 @@ before the timed region.  The decode pair (qsa_indexer_decode +
 qsa_sparse_decode) on the paged workload is timed the same way and reported
 in the "decode" object of the same JSON line.
 
-Prints ONE JSON line.  The roofline object covers the dominant kernel
-(sparse prefill attention): algorithmic bytes per launch / its average
-duration measured with HIP events on the launch stream.  cpu_baseline times
-the CPU oracle on the same workload.
+Prints ONE JSON line.  The roofline object covers the dominant call
+(qsa_sparse_prefill: its tile and row kernels): algorithmic bytes per call /
+its average duration measured with HIP events on the launch stream, against
+HBM, and the algorithmic flops (QK^T and PV over the listed keys) against
+the dense fp16/bf16 MFMA peak.  cpu_baseline times the CPU oracle on the
+same workload.
 """
 from __future__ import annotations
 
@@ -29,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_prefill_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "top_indexed_sparse_qsa_amd", "csrc", "sparse_attention.hip")
 METRIC = "sparse prefill tokens/s + decode seqs/s (topK 2051); % HBM roofline"
@@ -106,11 +109,14 @@ def prefill_bench(args, Q, syn, torch):
     attn_avg = float(np.mean(attn_ms)) * 1e-3
     idx_avg = float(np.mean(idx_ms)) * 1e-3
     achieved = attn_bytes / attn_avg / 1e9
+    # QK^T and PV over the listed keys, per query head: 2 * D + 2 * D flops per id
+    attn_flops = n_entries * inp.Hq * inp.D * 4
     res = {
         "inp": inp, "live": live, "wall": wall,
         "ms_per_step": wall / args.steps * 1e3,
         "indexer_ms": idx_avg * 1e3, "attention_ms": attn_avg * 1e3,
         "attn_bytes": attn_bytes, "achieved_gbs": achieved, "n_entries": n_entries,
+        "attn_flops": attn_flops, "achieved_tflops": attn_flops / attn_avg / 1e12,
     }
     del q, k, v, iq, ik, o, lists, ws
     torch.cuda.empty_cache()
@@ -287,10 +293,13 @@ def main():
                    "live_tokens": pf["live"], "num_q_heads": inp.Hq, "num_kv_heads": inp.Hkv,
                    "head_dim": inp.D, "top_k": inp.icfg.top_k, "parallelism": "none"},
         "parts_ms": {"indexer_prefill": pf["indexer_ms"], "sparse_prefill": pf["attention_ms"]},
-        "roofline": {"bound": "hbm", "kernel": "sparse_prefill_kernel",
+        "roofline": {"bound": "hbm", "kernel": "qsa_sparse_prefill: sparse_prefill_tile_kernel + sparse_prefill_kernel",
                      "achieved": pf["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf["achieved_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
-                     "algorithmic_bytes_per_call": pf["attn_bytes"]},
+                     "algorithmic_bytes_per_call": pf["attn_bytes"],
+                     "mfma": {"achieved": pf["achieved_tflops"], "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": pf["achieved_tflops"] / MFMA_PEAK_TFLOPS,
+                              "algorithmic_flops_per_call": pf["attn_flops"]}},
         "cpu_baseline": cpu,
         "decode": dec,
     }
