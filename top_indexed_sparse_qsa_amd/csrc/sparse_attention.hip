@@ -333,6 +333,45 @@ struct TileStage {
   u32x4 k[2], v[2];  // K and V rows srow and 16 + srow of the chunk, one piece each
 };
 
+// LDS of a tile workgroup: K chunks with 16-byte pieces XOR-swizzled by row
+// (conflict-free row writes and fragment reads), V chunks row-major with
+// rows padded to 288 bytes, so that the transposing reads that build V^T
+// (lds_tr16) hit distinct banks and step through d by immediate offsets.
+constexpr int kTileVRowPieces = 18;
+struct TileLds {
+  u32x4 k[2][32 * 16];
+  u32x4 v[2][32 * kTileVRowPieces];
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+// gfx950 transposing LDS read of 16-bit elements: within each 16-lane group,
+// lane 4a + b gets element b of the 8-byte chunks addressed by lanes a,
+// a + 4, a + 8 and a + 12 of the group.
+__device__ __forceinline__ s16x4_t lds_tr16(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(p));
+}
+
+// Output of the lane's column from accumulators in the tile layout (acc[e][i]
+// holds output dim 16 e + 4 q4 + i): O = acc / l, or +0.0 for rows past the
+// live length.  dst points at the column's (row, head) output row.
+template <int D, int DT>
+__device__ __forceinline__ void store_column_tr(uint16_t *dst, const f32x4 (&acc)[8], float l_run, bool write,
+                                                bool zero) {
+  const int q4 = lane_id() >> 4;
+  float l = l_run + shfl_xor_f(l_run, 16);
+  l += shfl_xor_f(l, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (write) {
+#pragma unroll
+    for (int e = 0; e < D / 16; ++e) {
+      uint2 w;
+      w.x = zero ? 0u : pack2<DT>(acc[e][0] * inv, acc[e][1] * inv);
+      w.y = zero ? 0u : pack2<DT>(acc[e][2] * inv, acc[e][3] * inv);
+      *reinterpret_cast<uint2 *>(dst + 16 * e + 4 * q4) = w;
+    }
+  }
+}
+
 // Output of the lane's column: O = acc / l, or +0.0 for rows past the live
 // length (their accumulators may hold values, times 0 they could give -0.0).
 // dst points at the column's (row, head) output row.
@@ -445,8 +484,8 @@ __device__ __forceinline__ bool build_key_mask(const PrefillAttnArgs &a, int b, 
 
 // Returns false when the tile's lists need the list walk; nothing is written then.
 template <int D, int DT, int NT>
-__device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x4 (*s_buf)[32 * 16],
-                          uint32_t *s_mask, int *s_cnt, int *s_flag) {
+__device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, TileLds &L, uint32_t *s_mask, int *s_cnt,
+                          int *s_flag) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Gp = tile_heads(a.G), RP = 16 / Gp, R = 4 * NT * RP;
@@ -512,16 +551,22 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
       }
     };
     auto store = [&](const TileStage &st, int buf) {
-      u32x4 *kt = s_buf[2 * buf], *vt = s_buf[2 * buf + 1];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int row = 16 * hh + srow;
         if (D == 128 || piece < D / 8) {
-          kt[row * 16 + (piece ^ (row & 15))] = st.k[hh];
-          vt[row * 16 + (piece ^ (row & 15))] = st.v[hh];
+          L.k[buf][row * 16 + (piece ^ (row & 15))] = st.k[hh];
+          L.v[buf][row * kTileVRowPieces + piece] = st.v[hh];
         }
       }
     };
+    // V^T operand of accumulator e, two transposing reads: lane i = a + 4R of
+    // group q4 points at V[key slot 4 q4 + R][16 e + 4 a] (key slot
+    // 16 + 4 q4 + R for the second read), so lane j of the group gets
+    // V[key slots 4 q4 .. 4 q4 + 3][16 e + j]: MFMA A element (m = j,
+    // k = 8 q4 + i) is V[key slot slot_of(q4, i)][16 e + j], the key order of
+    // the P operand.  Accumulator e then holds output dims 16 e + 4 q4 + i.
+    const int v_lane = (4 * q4 + (r16 >> 2)) * (16 * kTileVRowPieces) + (r16 & 3) * 8;
     auto compute = [&](int c, int buf) {
       uint32_t word[NT];
 #pragma unroll
@@ -533,7 +578,7 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
         all_w &= word[u];
       }
       if (!wave_any(any_w != 0u)) return;  // no column of this wave has a key here
-      const u32x4 *kt = s_buf[2 * buf], *vt = s_buf[2 * buf + 1];
+      const u32x4 *kt = L.k[buf];
       f32x4 s0[NT], s1[NT];
 #pragma unroll
       for (int u = 0; u < NT; ++u) s0[u] = s1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -546,12 +591,6 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
           s0[u] = mfma16x16x32<DT>(k0, qp[u][ks], s0[u]);
           s1[u] = mfma16x16x32<DT>(k1, qp[u][ks], s1[u]);
         }
-      }
-      u32x4 vf[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = slot_of(q4, i);
-        vf[i] = (D == 128 || r16 < D / 8) ? vt[row * 16 + (r16 ^ (row & 15))] : u32x4{0u, 0u, 0u, 0u};
       }
       const bool full = !wave_any(all_w != 0xffffffffu);  // every column sees every key
       u32x4 bop[NT];
@@ -572,9 +611,14 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
         }
         bop[u] = chunk_probs<DT, true>(x, a.sl2, m_run[u], l_run[u], acc[u]);
       }
+      const char *vb = reinterpret_cast<const char *>(L.v[buf]) + v_lane;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const u32x4 av = v_operand(vf, e);
+      for (int e = 0; e < D / 16; ++e) {
+        const s16x4_t lo = lds_tr16(vb + 32 * e), hi = lds_tr16(vb + 16 * 16 * kTileVRowPieces + 32 * e);
+        const u32x4 av = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
 #pragma unroll
         for (int u = 0; u < NT; ++u) acc[u][e] = mfma16x16x32<DT>(av, bop[u], acc[u][e]);
       }
@@ -607,7 +651,7 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, u32x
   for (int u = 0; u < NT; ++u) {
     const int t = t0 + r_col[u];
     uint16_t *dst = a.o + (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G + h) * D;
-    store_column<D, DT>(dst, acc[u], l_run[u], h < a.G && t < t_end, !col_live[u]);
+    store_column_tr<D, DT>(dst, acc[u], l_run[u], h < a.G && t < t_end, !col_live[u]);
   }
   return true;
 }
@@ -729,8 +773,7 @@ __device__ __forceinline__ void walk_row(const PrefillAttnArgs &a, int b, int t,
 // walk's result, at the tile's small register budget.  Rare (lists that
 // break the contract), so simple rather than fast.
 template <int D, int DT>
-__device__ void tile_walk_rows(const PrefillAttnArgs &a, int b, int kvh, int t0, int t_end, u32x4 (*s_buf)[32 * 16],
-                               int *s_slot) {
+__device__ void tile_walk_rows(const PrefillAttnArgs &a, int b, int kvh, int t0, int t_end, TileLds &L, int *s_slot) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int srow = tid >> 4, piece = tid & 15;
@@ -740,7 +783,7 @@ __device__ void tile_walk_rows(const PrefillAttnArgs &a, int b, int kvh, int t0,
   kv.v = reinterpret_cast<const char *>(a.v + ((size_t)b * a.S * a.Hkv + kvh) * D);
   kv.row_bytes = (uint32_t)(a.Hkv * D * 2);
   kv.limit = live;
-  u32x4 *kt = s_buf[0], *vt = s_buf[1];
+  u32x4 *kt = L.k[0], *vt = L.v[0];  // 16-byte pieces XOR-swizzled by row, 16 per row
   for (int t = t0; t < t_end; ++t) {
     const int32_t *list = a.indices + ((size_t)b * a.S + t) * a.top_k;
     const size_t qo_off = (((size_t)b * a.S + t) * a.Hq + (size_t)kvh * a.G) * D;
@@ -795,13 +838,13 @@ __device__ void tile_walk_rows(const PrefillAttnArgs &a, int b, int kvh, int t0,
 template <int D, int DT, int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, NT == 1 ? 3 : 2))) void
 sparse_prefill_tile_kernel(PrefillAttnArgs a) {
-  __shared__ u32x4 s_ktile[4][32 * 16];
+  __shared__ TileLds s_tile;
   __shared__ uint32_t s_mask[kTileMaskWords];
   __shared__ int s_cnt[32], s_flag[4];
   int b = 0, kvh = 0, t0 = 0;
   if (!tile_item(a, blockIdx.x, b, kvh, t0)) return;
-  if (list_tile<D, DT, NT>(a, b, kvh, t0, s_ktile, s_mask, s_cnt, s_flag)) return;
-  tile_walk_rows<D, DT>(a, b, kvh, t0, min(t0 + a.tile_rows, a.tile_below), s_ktile, s_cnt);
+  if (list_tile<D, DT, NT>(a, b, kvh, t0, s_tile, s_mask, s_cnt, s_flag)) return;
+  tile_walk_rows<D, DT>(a, b, kvh, t0, min(t0 + a.tile_rows, a.tile_below), s_tile, s_cnt);
 }
 
 // Row workgroups: every wave walks its own list; rows below skip_below
