@@ -131,7 +131,8 @@ def identity_lists(rng, B, S, ctx, top_k, mode):
     for a row-dependent length, then other distinct ids in random order;
     "mixed" identity rows next to random-order rows in some groups of four
     consecutive rows (one workgroup's rows); "holes" identity with a
-    few -1 slots."""
+    few -1 slots; "dups" one id repeated in every fifth row; "future" a few
+    ids past t in free slots of every third row."""
     out = np.full((B, S, top_k), -1, dtype=np.int32)
     for b in range(B):
         for t in range(min(int(ctx[b]), S)):
@@ -151,6 +152,21 @@ def identity_lists(rng, B, S, ctx, top_k, mode):
                 out[b, t, :n] = np.arange(n)
                 if n > 40:
                     out[b, t, rng.integers(0, n, 3)] = -1
+            elif mode == "dups":
+                # the contract's ids are distinct; a repeated id counts twice
+                # on both sides (the list walk and the oracle)
+                out[b, t, :n] = np.arange(n)
+                if n > 8 and t % 5 == 0:
+                    j, j2 = rng.choice(n, 2, replace=False)
+                    out[b, t, j] = out[b, t, j2]
+            elif mode == "future":
+                # ids past t (outside the causal range) in free slots: both
+                # sides use them as listed
+                live = min(int(ctx[b]), S)
+                out[b, t, :n] = np.arange(n)
+                if t % 3 == 0 and n < top_k and t + 1 < live:
+                    extra = rng.choice(np.arange(t + 1, live), min(2, top_k - n, live - t - 1), replace=False)
+                    out[b, t, n:n + len(extra)] = extra
     return out
 
 
@@ -166,6 +182,9 @@ IDENTITY_CASES = [
     dict(B=1, S=520, Hq=16, Hkv=2, D=128, dtype="fp16", top_k=520, ctx=[515], mode="full"),
     dict(B=1, S=100, Hq=10, Hkv=2, D=128, dtype="bf16", top_k=100, ctx=[100], mode="full"),
     dict(B=2, S=120, Hq=12, Hkv=1, D=64, dtype="fp16", top_k=70, ctx=[120, 50], mode="full"),
+    dict(B=1, S=300, Hq=16, Hkv=2, D=128, dtype="fp16", top_k=300, ctx=[300], mode="dups"),
+    dict(B=1, S=300, Hq=16, Hkv=2, D=128, dtype="bf16", top_k=200, ctx=[280], mode="future"),
+    dict(B=1, S=260, Hq=16, Hkv=1, D=128, dtype="fp16", top_k=260, ctx=[260], mode="dups"),
 ]
 
 
