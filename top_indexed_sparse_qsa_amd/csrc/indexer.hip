@@ -25,14 +25,15 @@ __device__ __forceinline__ double bits_to_f64(uint32_t h, int dt) { return (doub
 
 // One 128-vector per wave: lane l holds dims l and l + 64.  RoPE pairs dims
 // (i, i + rot/2) and turns them by pos * theta^(-2i/rot); dims >= rot pass
-// through.  The frequencies come from a per-workgroup table, and the
-// cos/sin of one position serve every head at that position.
+// through.  The frequencies are computed once on the host (fp64 pow) and
+// passed with the kernel arguments, and the cos/sin of one position serve
+// every head at that position.
 struct Rope2 {
   double c0, s0, c1, s1;  // rotation of dims lane and lane + 64
 };
 
-__device__ __forceinline__ void fill_freq(double *s_freq, int rot, double theta) {
-  for (int i = threadIdx.x; i < (rot >> 1); i += blockDim.x) s_freq[i] = pow(theta, (-2.0 * (double)i) / (double)rot);
+static void fill_freq(double *freq, int rot, double theta) {
+  for (int i = 0; i < 64; ++i) freq[i] = i < (rot >> 1) ? pow(theta, (-2.0 * (double)i) / (double)rot) : 0.0;
 }
 
 __device__ __forceinline__ Rope2 rope_at(double pos, const double *s_freq, int rot) {
@@ -77,9 +78,7 @@ __device__ __forceinline__ void norm_rope2(double x0, double x1, double w0, doub
 constexpr int kPrepItemsPerWave = 4;
 
 __global__ __launch_bounds__(256) void idx_prep_kernel(IdxPrepArgs a) {
-  __shared__ double s_freq[64];
-  fill_freq(s_freq, a.rot, a.theta);
-  __syncthreads();
+  const double *s_freq = a.freq;
   const int lane = lane_id();
   const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long long nrows = (long long)a.B * a.S, total = nrows + (long long)a.B * a.Gmax;
@@ -774,9 +773,7 @@ __device__ __forceinline__ long long pool_row_off(const int32_t *ptrow, int toke
 // Wave h < Hi prepares query head h; wave Hi updates the pool tail, so the
 // query and key chains run side by side.
 __global__ __launch_bounds__(320) void idx_dec_prep_kernel(IdxDecPrepArgs a) {
-  __shared__ double s_freq[64];
-  fill_freq(s_freq, a.rot, a.theta);
-  __syncthreads();
+  const double *s_freq = a.freq;
   const int b = blockIdx.x, lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ctx = min(a.ctx[b], a.max_pages * 128);
@@ -906,6 +903,7 @@ __global__ __launch_bounds__(256) void idx_dec_score_kernel(IdxDecScoreArgs a) {
 // ---------------------------------------------------------------------------
 hipError_t launch_idx_prep(const IdxPrepArgs &a_in, hipStream_t s) {
   IdxPrepArgs a = a_in;
+  fill_freq(a.freq, a.rot, a.theta);
   const long long items = (long long)a.B * a.S + (long long)a.B * a.Gmax;
   a.per_wave = (int)std::min<long long>(kPrepItemsPerWave, std::max<long long>(1, items / 8192));
   const long long waves = (items + a.per_wave - 1) / a.per_wave;
@@ -1010,7 +1008,9 @@ hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_idx_dec_prep(const IdxDecPrepArgs &a, hipStream_t s) {
+hipError_t launch_idx_dec_prep(const IdxDecPrepArgs &a_in, hipStream_t s) {
+  IdxDecPrepArgs a = a_in;
+  fill_freq(a.freq, a.rot, a.theta);
   hipLaunchKernelGGL(idx_dec_prep_kernel, dim3((unsigned)a.B), dim3(64 * (a.Hi + 1)), 0, s, a);
   return hipGetLastError();
 }

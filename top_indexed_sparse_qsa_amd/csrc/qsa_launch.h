@@ -46,6 +46,7 @@ struct IdxPrepArgs {
   double theta, eps;
   int dt;
   int per_wave;     // items per wave (set by the launcher)
+  double freq[64];  // RoPE frequencies theta^(-2i/rot), i < rot/2 (set by the launcher)
 };
 
 struct IdxScoreArgs {
@@ -84,6 +85,7 @@ struct IdxDecPrepArgs {
   int B, Hi, hd, rot, ratio, Hkv, D, PHD, num_flat_pages, max_pages;
   double theta, eps;
   int dt;
+  double freq[64];  // RoPE frequencies theta^(-2i/rot), i < rot/2 (set by the launcher)
 };
 
 struct IdxDecScoreArgs {
