@@ -139,7 +139,7 @@ qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p) {
   // one sequence's K (or V) is addressed with 32-bit byte offsets
   if ((int64_t)p->seq_len * p->num_kv_heads * p->head_dim * 2 >= ((int64_t)1 << 32)) return QSA_ERR_UNSUPPORTED;
   if (!isfinite(p->attention_scale) || !(p->attention_scale > 0.f)) return QSA_ERR_BAD_SHAPE;
-  qsa::PrefillAttnArgs a;
+  qsa::PrefillAttnArgs a{};
   a.q = static_cast<const uint16_t *>(p->q);
   a.k = static_cast<const uint16_t *>(p->k);
   a.v = static_cast<const uint16_t *>(p->v);

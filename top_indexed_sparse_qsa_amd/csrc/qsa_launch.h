@@ -18,6 +18,9 @@ struct PrefillAttnArgs {
   // sequences [tile_b0, tile_b0 + tile_nb), tile_per_seq tiles of tile_rows
   // rows each per sequence
   int tile_rows, tile_per_seq, tile_b0, tile_nb, tile_below;
+  // the first tile_snake workgroups of each XCD (whole rows of tile_cus,
+  // its CU count) are taken in snake order (set by the launcher; 0: none)
+  int tile_cus, tile_snake;
   int skip_below;  // the row walk skips rows t < skip_below (held by tiles)
 };
 

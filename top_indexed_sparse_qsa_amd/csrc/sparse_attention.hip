@@ -305,11 +305,11 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
 // row r16 / Gp).
 //
 // First the rows' lists become a key bitmask in LDS (one bit per key of
-// [0, t_act) per row, set by LDS atomic-or).  The mask reproduces exactly
-// the keys the list walk would use, or the tile gives up: an id repeated in
-// a list, a usable id at or past t_act (outside the causal range), or a
-// usable id after a 32-slot chunk with none (where the walk stops) sends the
-// tile's rows to the list walk, one row per wave at a time (the kernel runs
+// [0, t_act) per row, set by LDS atomic-or), read like the walk reads them:
+// up to the first 32-slot chunk with no usable id.  The mask reproduces
+// exactly the keys the list walk would use, or the tile gives up: an id
+// repeated in a list or a key at or past t_act (outside the causal range)
+// sends the tile's rows to the list walk, one row per wave at a time (the kernel runs
 // that walk, so its code exists once).
 //
 // Then the workgroup walks the keys once: every 32-key chunk of K and V is
@@ -396,80 +396,111 @@ __device__ __forceinline__ void store_column(uint16_t *dst, const f32x4 (&acc)[8
 
 // The key mask of the tile's live rows [t0, t_act): row r's words are
 // s_mask[r * W .. r * W + W).  Returns (on every lane of a wave that found
-// it) true when the lists need the walk.  Wave w builds rows w, w + 4, ...:
-// lane l reads slot quads l + 64 k of the row (16-byte loads; list rows are
-// only 4-byte aligned, which global loads accept), four loads in flight, and
-// sets its usable ids' bits with non-returning LDS or (one per quad when its
-// ids share a 32-bit word, as the indexer's 4-key blocks do).  The walk's
-// view is checked without atomics: the 32-slot chunks holding usable ids
-// must be chunks 0 .. n-1 (their count equals the last one's index + 1;
-// lanes 8m .. 8m + 7 hold one chunk), no usable id may lie at or past t_act,
-// and after a barrier the row's mask must hold as many bits as the row has
-// usable ids (a repeated id sets one bit twice).
+// it) true when the lists need the walk.  Wave w builds rows w, w + 4, ...,
+// two rows at a time: lane l reads slot quads l + 64 k of each row (16-byte
+// loads; list rows are only 4-byte aligned, which global loads accept),
+// kBuildLoads loads per row in flight, and sets its usable ids' bits with
+// non-returning LDS or (one per quad when its ids share a 32-bit word, as
+// the indexer's 4-key blocks do).  A row is read in order up to its first
+// 32-slot chunk with no usable id (lanes 8m .. 8m + 7 of a load hold chunk
+// m of its 8), where the walk stops too: the ids before it are the row's
+// keys and nothing after it is read.  No key may lie at or past t_act, and
+// after a barrier the row's mask must hold as many bits as the row has keys
+// (a repeated id sets one bit twice).
+constexpr int kBuildLoads = 5;  // 2051 slots: two rounds
+
 __device__ __forceinline__ bool build_key_mask(const PrefillAttnArgs &a, int b, int t0, int t_act, int live, int W,
                                                uint32_t *s_mask, int *s_cnt) {
   typedef int i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
   const int lane = lane_id(), tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nr = t_act - t0;
   const int nload = (a.top_k + 255) >> 8;  // 64 quads = 8 chunks per load
+  const int nchunk = (a.top_k + 31) >> 5;
   for (int i = tid; i < nr * W; i += 256) s_mask[i] = 0u;
   __syncthreads();
   bool bad = false;
-  for (int r = wv; r < nr; r += 4) {
-    const int32_t *row = a.indices + ((size_t)b * a.S + t0 + r) * a.top_k;
-    int cnt = 0;                      // this lane's usable ids
-    int used_chunks = 0, last = -1;   // wave-uniform
-    for (int k0 = 0; k0 < nload; k0 += 4) {
-      i32x4_a4 v[4];
+  for (int r = wv; r < nr; r += 8) {
+    const int rr[2] = {r, min(r + 4, nr - 1)};
+    const int32_t *row[2];
+    int cnt[2] = {0, 0};            // this lane's keys per row
+    bool open[2] = {true, r + 4 < nr};  // still reading (wave-uniform)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const i32x4_a4 *>(row + min(4 * (64 * (k0 + k) + lane), a.top_k - 4));
+    for (int j = 0; j < 2; ++j) row[j] = a.indices + ((size_t)b * a.S + t0 + rr[j]) * a.top_k;
+    for (int k0 = 0; k0 < nload && (open[0] || open[1]); k0 += kBuildLoads) {
+      // both rows' loads are issued before either is used (clamped: what
+      // lies past the list or a closed row is dropped)
+      i32x4_a4 v[2][kBuildLoads];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int q = 64 * (k0 + k) + lane;
-        const int s0 = min(4 * q, a.top_k - 4);  // slot of v[k].x
-        bool u[4];
-        uint32_t bits = 0u;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int sl = s0 + e, id = v[k][e];
-          // a slot counts once: only in the quad it belongs to (4q .. 4q+3)
-          u[e] = (sl >= 4 * q) & (sl < a.top_k) & ((unsigned)id < (unsigned)live);
-          cnt += u[e] ? 1 : 0;
-          bad |= u[e] & (id >= t_act);
-          bits |= u[e] & (id < t_act) ? 1u << (id & 31) : 0u;
-        }
-        const int id0 = v[k][0];
-        const bool one_word = ((!u[1]) | ((v[k][1] >> 5) == (id0 >> 5))) & ((!u[2]) | ((v[k][2] >> 5) == (id0 >> 5))) &
-                              ((!u[3]) | ((v[k][3] >> 5) == (id0 >> 5)));
-        if (u[0] & one_word) {
-          if (bits != 0u)
-            __hip_atomic_fetch_or(&s_mask[r * W + (id0 >> 5)], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        } else {
+        for (int k = 0; k < kBuildLoads; ++k)
+          v[j][k] = *reinterpret_cast<const i32x4_a4 *>(row[j] + min(4 * (64 * (k0 + k) + lane), a.top_k - 4));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (!open[j]) continue;
+#pragma unroll
+        for (int k = 0; k < kBuildLoads; ++k) {
+          const int kk = k0 + k;
+          if (kk >= nload) break;
+          const int q = 64 * kk + lane;
+          const int s0 = min(4 * q, a.top_k - 4);  // slot of v[j][k].x
+          bool u[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int id = v[k][e];
-            if (u[e] & (id < t_act))
-              __hip_atomic_fetch_or(&s_mask[r * W + (id >> 5)], 1u << (id & 31), __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+            // a slot counts once: only in the quad it belongs to (4q .. 4q+3)
+            const int sl = s0 + e;
+            u[e] = (sl >= 4 * q) & (sl < a.top_k) & ((unsigned)v[j][k][e] < (unsigned)live);
           }
-        }
-        // chunks 8 (k0 + k) + m: bit 8m of f is set when lanes 8m .. 8m + 7
-        // hold a usable id
-        uint64_t f = __ballot(u[0] | u[1] | u[2] | u[3]);
-        f |= f >> 4;
-        f |= f >> 2;
-        f |= f >> 1;
-        f &= 0x0101010101010101ull;
-        if (f != 0ull) {
-          used_chunks += __builtin_popcountll(f);
-          last = 8 * (k0 + k) + ((63 - __builtin_clzll(f)) >> 3);
+          // bit 8m of f: chunk 8 kk + m holds a usable id
+          uint64_t f = __ballot(u[0] | u[1] | u[2] | u[3]);
+          f |= f >> 4;
+          f |= f >> 2;
+          f |= f >> 1;
+          const int nex = min(8, nchunk - 8 * kk);  // chunks of the list in this load
+          const uint64_t gap = ~f & 0x0101010101010101ull & (nex == 8 ? ~0ull : (1ull << (8 * nex)) - 1);
+          if (gap != 0ull) {
+            // the list ends before chunk 8 kk + m
+            const bool keep = lane < (__builtin_ctzll(gap) & ~7);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] &= keep;
+            open[j] = false;
+          }
+          uint32_t bits = 0u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int id = v[j][k][e];
+            cnt[j] += u[e] ? 1 : 0;
+            bad |= u[e] & (id >= t_act);
+            bits |= u[e] & (id < t_act) ? 1u << (id & 31) : 0u;
+          }
+          const int id0 = v[j][k][0];
+          const bool one_word = ((!u[1]) | ((v[j][k][1] >> 5) == (id0 >> 5))) &
+                                ((!u[2]) | ((v[j][k][2] >> 5) == (id0 >> 5))) &
+                                ((!u[3]) | ((v[j][k][3] >> 5) == (id0 >> 5)));
+          uint32_t *mrow = s_mask + rr[j] * W;
+          if (u[0] & one_word) {
+            if (bits != 0u) __hip_atomic_fetch_or(&mrow[id0 >> 5], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int id = v[j][k][e];
+              if (u[e] & (id < t_act))
+                __hip_atomic_fetch_or(&mrow[id >> 5], 1u << (id & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+          }
+          if (!open[j]) break;
         }
       }
     }
-    bad |= used_chunks != last + 1;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-    if (lane == 0) s_cnt[r] = cnt;
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cnt[j] += __shfl_xor(cnt[j], o, 64);
+    }
+    if (lane == 0) {
+      s_cnt[r] = cnt[0];
+      if (r + 4 < nr) s_cnt[r + 4] = cnt[1];
+    }
   }
   __syncthreads();
   for (int r = wv; r < nr; r += 4) {
@@ -605,9 +636,14 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, Tile
         if (!full) {
           // key slot slot_of(q4, i) = 4 q4 + i (i < 4), 12 + 4 q4 + i: shift
           // once by 4 q4, then by constants
-          const uint32_t wq = word[u] >> (4 * q4);
+          // and a signed one-bit extract is the select mask (0 or ~0):
+          // x or -inf is one bitwise select per score
+          const int wq = (int)(word[u] >> (4 * q4));
 #pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = (wq >> (i < 4 ? i : 12 + i)) & 1u ? x[i] : -INFINITY;
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe(wq, i < 4 ? i : 12 + i, 1);
+            x[i] = __uint_as_float((__float_as_uint(x[i]) & m) | (0xff800000u & ~m));
+          }
         }
         bop[u] = chunk_probs<DT, true>(x, a.sl2, m_run[u], l_run[u], acc[u]);
       }
@@ -666,12 +702,22 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, Tile
 // rows).  A workgroup's four waves take four consecutive rows of that head.
 // Otherwise a workgroup takes the Hkv heads of consecutive rows.  Tile
 // workgroups (list_tile) go out longest tiles first, with the same
-// XCD-to-head mapping.
+// XCD-to-head mapping, except that the workgroups which start together
+// take them in snake order: at launch an XCD hands its n-th workgroup to CU
+// n mod (its CU count) until every CU holds as many as fit, so in plain
+// order the CU with the longest tile also gets the longest of every later
+// round and finishes last; reversing every other round evens the CUs'
+// sums (the rest go out in order to whichever CU frees first).
 __device__ __forceinline__ bool tile_item(const PrefillAttnArgs &a, int blk, int &b, int &kvh, int &t0) {
   const int ntiles = a.tile_nb * a.tile_per_seq;
   int k;
   if ((8 % a.Hkv) == 0) {
-    const int xcd = blk & 7, n = blk >> 3;
+    const int xcd = blk & 7;
+    int n = blk >> 3;
+    if (n < a.tile_snake) {
+      const int round = n / a.tile_cus, c = n - round * a.tile_cus;
+      n = round * a.tile_cus + ((round & 1) ? a.tile_cus - 1 - c : c);
+    }
     kvh = xcd % a.Hkv;
     k = n * (8 / a.Hkv) + xcd / a.Hkv;
   } else {
@@ -1038,6 +1084,20 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
 #endif
 constexpr int kTileRangeX2 = QSA_TILE_RANGE_X2;
 
+// CUs per XCD of the current device (its CU count / 8), or 0 when that is
+// not a whole number; cached per device.
+static int xcd_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cache[dev] = (n > 0 && n % 8 == 0) ? n / 8 : -1;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
+}
+
 template <int D, int DT>
 static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
   // Rows t < tk of every sequence go to tiles (when G >= 4), the rest to the
@@ -1066,6 +1126,17 @@ static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
     p.tile_b0 = b0;
     p.tile_nb = nb;
     if (p.tile_per_seq <= 0) return hipSuccess;
+    // snake order over the workgroups that start together on an XCD: its
+    // CUs times the tile workgroups a CU holds (three at NT = 1: 4 waves at
+    // three per SIMD, ~51 KB of LDS each; two at NT = 2), in whole rows of
+    // CUs within the XCD's share of the grid
+    p.tile_cus = xcd_cus();
+    p.tile_snake = 0;
+    if (p.tile_cus > 0 && (8 % a.Hkv) == 0) {
+      const long long per_xcd = tile_grid(p) / 8;
+      const long long start = (long long)p.tile_cus * (tile_nt(a.G) == 1 ? 3 : 2);
+      p.tile_snake = (int)min(start, per_xcd / p.tile_cus * p.tile_cus);
+    }
     if (tile_nt(a.G) == 1)
       hipLaunchKernelGGL((sparse_prefill_tile_kernel<D, DT, 1>), dim3(tile_grid(p)), dim3(256), 0, s, p);
     else
