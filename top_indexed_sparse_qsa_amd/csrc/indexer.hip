@@ -151,7 +151,8 @@ __device__ __forceinline__ void load8f(float (&x)[8], const float *p) {
 // Prefill scoring.  A workgroup takes 32 consecutive rows and a run of up to
 // kScoreChunksPerGroup chunks of kScoreChunk complete blocks (rows' queries
 // are loaded and split once per run; short prefills take shorter runs so the
-// grid still fills the chip); runs of the last rows are dispatched first.  Per chunk the kbar rows are staged in LDS, 16-byte pieces
+// grid still fills the chip); runs of the last rows are dispatched first,
+// all runs of a row group on one XCD.  Per chunk the kbar rows are staged in LDS, 16-byte pieces
 // XOR-swizzled by row so that MFMA fragment reads are conflict-free; each wave
 // computes 8 rows against the chunk.  The MFMA M tile is (row, head) with the
 // head fastest, so each 16-lane group ends with the four head dots of one row
@@ -167,11 +168,17 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15, wv = threadIdx.x >> 6;
   const int tid = threadIdx.x;
   const int T32 = (a.S + 31) >> 5;
-  const long long item = blockIdx.x;
-  const int b = (int)(item % a.B);
-  const long long rest = item / a.B;
-  const int run = (int)(rest % a.nchunk);
-  const int tg = 32 * (T32 - 1 - (int)(rest / a.nchunk));
+  // Row group grp (= rows of sequence grp % B, last rows first) runs on XCD
+  // grp % 8 (workgroups go round-robin over the eight XCDs): its runs share
+  // the group's queries through that XCD's L2 instead of each XCD fetching
+  // them.
+  const int xcd = blockIdx.x & 7;
+  const long long n = blockIdx.x >> 3;
+  const int run = (int)(n % a.nchunk);
+  const long long grp = (n / a.nchunk) * 8 + xcd;
+  if (grp >= (long long)a.B * T32) return;
+  const int b = (int)(grp % a.B);
+  const int tg = 32 * (T32 - 1 - (int)(grp / a.B));
   const int live = min(a.ctx[b], a.S);
   if (tg >= live) return;
   const int nc_hi = (min(tg + 31, live - 1) + 1) / a.ratio;
@@ -919,7 +926,7 @@ hipError_t launch_idx_score(const IdxScoreArgs &a_in, int dt, hipStream_t s) {
   while (run > 1 && groups * ((chunks + run - 1) / run) < 2048) run >>= 1;
   a.run_chunks = run;
   a.nchunk = (chunks + run - 1) / run;
-  const unsigned grid = (unsigned)(groups * a.nchunk);
+  const unsigned grid = (unsigned)(8 * ((groups + 7) / 8) * a.nchunk);
   if (dt == DT_F16) hipLaunchKernelGGL(idx_score_kernel<DT_F16>, dim3(grid), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(idx_score_kernel<DT_BF16>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -471,7 +471,7 @@ __device__ __forceinline__ bool build_key_mask(const PrefillAttnArgs &a, int b, 
             const int id = v[j][k][e];
             cnt[j] += u[e] ? 1 : 0;
             bad |= u[e] & (id >= t_act);
-            bits |= u[e] & (id < t_act) ? 1u << (id & 31) : 0u;
+            bits |= (u[e] & (id < t_act)) ? 1u << (id & 31) : 0u;
           }
           const int id0 = v[j][k][0];
           const bool one_word = ((!u[1]) | ((v[j][k][1] >> 5) == (id0 >> 5))) &
