@@ -186,6 +186,29 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
   const int run_hi = min(run_lo + a.run_chunks * CB, nc_hi);
   if (run_lo >= run_hi) return;
 
+  // kbar rows of a chunk: global -> registers (issued a chunk ahead) -> LDS
+  constexpr int NV = CB * 16 / 256;  // 16-byte pieces per thread
+  u32x4 v[NV];
+  auto load_chunk = [&](int g_lo) {
+    const int npiece = (min(g_lo + CB, run_hi) - g_lo) * 16;
+    const uint16_t *src = a.kbar + ((size_t)b * a.Gmax + g_lo) * 128;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int i = tid + 256 * u;
+      if (i < npiece) v[u] = ld16(src + 8 * i);
+    }
+  };
+  auto stage_chunk = [&](int g_lo) {
+    const int npiece = (min(g_lo + CB, run_hi) - g_lo) * 16;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int i = tid + 256 * u;
+      const int row = i >> 4, pc = i & 15;
+      if (i < npiece) *reinterpret_cast<u32x4 *>(&s_kb[row * 64 + 4 * (pc ^ (row & 15))]) = v[u];
+    }
+  };
+  load_chunk(run_lo);  // in flight while the queries are loaded and split
+
   const int t0 = tg + 8 * wv;
   u32x4 qa[2][NP][4];
 #pragma unroll
@@ -217,28 +240,6 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
   }
   float *const st_base = a.scores + ((size_t)b * a.S + tg + st_row0) * a.stride;
 
-  // kbar rows of a chunk: global -> registers (issued a chunk ahead) -> LDS
-  constexpr int NV = CB * 16 / 256;  // 16-byte pieces per thread
-  u32x4 v[NV];
-  auto load_chunk = [&](int g_lo) {
-    const int npiece = (min(g_lo + CB, run_hi) - g_lo) * 16;
-    const uint16_t *src = a.kbar + ((size_t)b * a.Gmax + g_lo) * 128;
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int i = tid + 256 * u;
-      if (i < npiece) v[u] = ld16(src + 8 * i);
-    }
-  };
-  auto stage_chunk = [&](int g_lo) {
-    const int npiece = (min(g_lo + CB, run_hi) - g_lo) * 16;
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int i = tid + 256 * u;
-      const int row = i >> 4, pc = i & 15;
-      if (i < npiece) *reinterpret_cast<u32x4 *>(&s_kb[row * 64 + 4 * (pc ^ (row & 15))]) = v[u];
-    }
-  };
-  load_chunk(run_lo);
   stage_chunk(run_lo);
   __syncthreads();
   for (int g_lo = run_lo; g_lo < run_hi; g_lo += CB) {
