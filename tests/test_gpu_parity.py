@@ -37,6 +37,23 @@ def gpu_sparse_prefill(inp, indices):
     return o
 
 
+def check_rows_written(o, inp, what):
+    """Every live row, not only the sampled ones: written (the output starts
+    as NaN), finite, and no larger than its KV head's largest |v| (each
+    output row is a convex combination of V rows; 1 % for rounding)."""
+    v = TL.dev(inp.v, inp.dtype)
+    G = inp.Hq // inp.Hkv
+    for b in range(inp.B):
+        live = min(int(inp.ctx[b]), inp.S)
+        if live <= 0:
+            continue
+        ob = o[b, :live].float()
+        assert torch.isfinite(ob).all(), f"{what}: b={b} has unwritten or non-finite live rows"
+        vmax = v[b, :live].float().abs().amax(dim=(0, 2))  # [Hkv]
+        omax = ob.abs().view(live, inp.Hkv, G, inp.D).amax(dim=(0, 2, 3))
+        assert bool((omax <= vmax * 1.01).all()), f"{what}: b={b} output exceeds max |v|: {omax} vs {vmax}"
+
+
 def gpu_indexer_prefill(inp, icfg, top_k):
     cfg = TL.idx_cfg_struct(icfg)
     nbytes = Q.qsa_indexer_prefill_workspace_bytes(cfg, inp.B, inp.S)
@@ -388,6 +405,7 @@ def test_prefill_workload_full_size(wl):
     for b in range(inp.B):
         live = min(int(inp.ctx[b]), inp.S)
         TL.check_zero_rows(o[b, live:], f"workload {wl} b={b}")
+    check_rows_written(o, inp, f"workload {wl}")
 
 
 @pytest.mark.parametrize("wl", [2, 5])
@@ -401,6 +419,7 @@ def test_sparse_prefill_structured_lists_full_size(wl):
     ref = O.sparse_prefill(inp.q, inp.k, inp.v, idx, inp.ctx, inp.scale, inp.dtype, rows=rows)
     for (b, t) in rows:
         TL.check_attention(TL.host_f64(o[b, t], inp.dtype), ref[(b, t)], inp.dtype, f"b={b} t={t}")
+    check_rows_written(o, inp, f"structured lists workload {wl}")
 
 
 # ---------------------------------------------------------------------------
