@@ -186,10 +186,21 @@ def decode_bench(args, Q, syn, torch):
     return out
 
 
+def kernel_code_sha256(path=None):
+    """sha256 of the attention kernel source with its comments and blank
+    space removed, so that the counter figures survive comment edits but
+    not code changes."""
+    import hashlib
+    import re
+    with open(path or KERNEL_SRC) as f:
+        text = re.sub(r"//[^\n]*|/\*.*?\*/", "", f.read(), flags=re.S)
+    code = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()
+
+
 def measured_traffic(wl):
     """HBM bytes per sparse_prefill launch from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, if it was taken on this kernel source."""
-    import hashlib
+    FETCH_SIZE / WRITE_SIZE summary, if it was taken on this kernel code."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as f:
@@ -198,9 +209,7 @@ def measured_traffic(wl):
                 if line and not line.startswith("#") and "=" in line:
                     k, v = line.split("=", 1)
                     kv[k.strip()] = v.strip()
-        with open(KERNEL_SRC, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if kv.get("kernel_source_sha256") != sha:
+        if kv.get("kernel_code_sha256") != kernel_code_sha256():
             return None
         return int(kv[f"workload{wl}_fetch_bytes"]) + int(kv[f"workload{wl}_write_bytes"])
     except (OSError, KeyError, ValueError):

@@ -298,11 +298,11 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
 // lengths it is half or more of it — walking all of the prefix densely with
 // a key mask is cheaper than gathering the listed rows: the gathers are
 // bound by on-chip gather throughput, the dense walk by MFMA and LDS.  A
-// tile workgroup takes 8 * 16 / Gp consecutive rows of one (sequence, KV
-// head) (Gp = G rounded up to a power of two, G >= 4: 16 rows at G = 8, 8 at
-// G = 16) and packs the (row, head) pairs as the 128 columns of eight
-// 16-column MFMA tiles, two per wave (column r16 of a tile = head r16 % Gp of
-// row r16 / Gp).
+// tile workgroup takes 4 * NT * 16 / Gp consecutive rows of one (sequence,
+// KV head) (Gp = G rounded up to a power of two, G >= 4; NT 16-column MFMA
+// tiles per wave: 16 rows at G = 4, 8 at G = 8 and at G = 16) and packs the
+// (row, head) pairs as MFMA columns (column r16 of a tile = head r16 % Gp
+// of row r16 / Gp).
 //
 // First the rows' lists become a key bitmask in LDS (one bit per key of
 // [0, t_act) per row, set by LDS atomic-or), read like the walk reads them:
@@ -315,13 +315,13 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
 // Then the workgroup walks the keys once: every 32-key chunk of K and V is
 // gathered once into a double-buffered LDS tile (two chunks in flight in
 // registers, one barrier per chunk) and read by all four waves; the K and V
-// fragments serve both column tiles of a wave; a wave whose columns have no
+// fragments serve every column tile of a wave; a wave whose columns have no
 // key in a chunk skips it, and the mask is applied only where some column
 // misses a key.
 __host__ __device__ constexpr int tile_heads(int G) { return G <= 4 ? 4 : G <= 8 ? 8 : 16; }
-// 16-column MFMA tiles per wave: one (147 VGPRs, three waves per SIMD),
+// 16-column MFMA tiles per wave: one (132 VGPRs, three waves per SIMD),
 // except at Gp = 16 where a column tile is a single row and two per wave
-// (216 VGPRs, two waves per SIMD) keep eight rows per tile.
+// (186 VGPRs, two waves per SIMD) keep eight rows per tile.
 __host__ __device__ constexpr int tile_nt(int G) { return tile_heads(G) == 16 ? 2 : 1; }
 // rows per tile: 4 * NT 16-column tiles of 16 / Gp rows each (G >= 4 only)
 __host__ __device__ constexpr int tile_rows_for(int G) { return 4 * tile_nt(G) * (16 / tile_heads(G)); }
