@@ -159,3 +159,18 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libqsa.so"))
     with pytest.raises(RuntimeError, match="missing"):
         L.load()
+
+
+def test_bench_counter_figures_follow_kernel_code(tmp_path):
+    """The committed HBM counter figures apply while the attention kernel's
+    code is unchanged: a comment or whitespace edit keeps the key, a code
+    edit changes it."""
+    import bench
+    src = open(bench.KERNEL_SRC).read()
+    base = bench.kernel_code_sha256()
+    edited = tmp_path / "comments.hip"
+    edited.write_text("// a new comment\n" + src.replace("\n", "\n\n", 3) + "\n/* trailing */\n")
+    assert bench.kernel_code_sha256(str(edited)) == base
+    changed = tmp_path / "code.hip"
+    changed.write_text(src.replace("kTileRangeX2 = QSA_TILE_RANGE_X2", "kTileRangeX2 = QSA_TILE_RANGE_X2 + 1", 1))
+    assert bench.kernel_code_sha256(str(changed)) != base
