@@ -319,14 +319,17 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
 // key in a chunk skips it, and the mask is applied only where some column
 // misses a key.
 __host__ __device__ constexpr int tile_heads(int G) { return G <= 4 ? 4 : G <= 8 ? 8 : 16; }
-// 16-column MFMA tiles per wave: one (132 VGPRs, three waves per SIMD),
+// 16-column MFMA tiles per wave: one (128 VGPRs, four waves per SIMD),
 // except at Gp = 16 where a column tile is a single row and two per wave
 // (186 VGPRs, two waves per SIMD) keep eight rows per tile.
 __host__ __device__ constexpr int tile_nt(int G) { return tile_heads(G) == 16 ? 2 : 1; }
 // rows per tile: 4 * NT 16-column tiles of 16 / Gp rows each (G >= 4 only)
 __host__ __device__ constexpr int tile_rows_for(int G) { return 4 * tile_nt(G) * (16 / tile_heads(G)); }
-// key-mask words of a tile workgroup (rows x 32-key chunks): 16 KB of LDS,
-// which bounds the tiled rows to t < 32 * kTileMaskWords / rows per tile
+// key-mask words of a tile workgroup (rows x 32-key chunks of the tile
+// range), at most 16 KB of LDS, which bounds the tiled rows to
+// t < 32 * kTileMaskWords / rows per tile.  The launch sizes it to its tile
+// range: 4 KB at 4096 rows and eight rows per tile, so that with the 34 KB of
+// K/V staging four workgroups fit a CU's 160 KB.
 constexpr int kTileMaskWords = 4096;
 
 struct TileStage {
@@ -880,12 +883,13 @@ __device__ void tile_walk_rows(const PrefillAttnArgs &a, int b, int kvh, int t0,
 }
 
 // Tile workgroups: one tile each (tile_item), with the register budget of
-// the tile alone (three waves per SIMD fit at NT = 1).
+// the tile alone: four waves per SIMD at NT = 1, when the launch-sized key
+// mask leaves LDS for four workgroups per CU (three otherwise).
 template <int D, int DT, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 3 : 2, NT == 1 ? 3 : 2))) void
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 4 : 2, NT == 1 ? 4 : 2))) void
 sparse_prefill_tile_kernel(PrefillAttnArgs a) {
   __shared__ TileLds s_tile;
-  __shared__ uint32_t s_mask[kTileMaskWords];
+  extern __shared__ uint32_t s_mask[];  // tile_rows x ceil(tile_below / 32) words (launch-sized)
   __shared__ int s_cnt[32], s_flag[4];
   int b = 0, kvh = 0, t0 = 0;
   if (!tile_item(a, blockIdx.x, b, kvh, t0)) return;
@@ -1127,20 +1131,23 @@ static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
     p.tile_nb = nb;
     if (p.tile_per_seq <= 0) return hipSuccess;
     // snake order over the workgroups that start together on an XCD: its
-    // CUs times the tile workgroups a CU holds (three at NT = 1: 4 waves at
-    // three per SIMD, ~51 KB of LDS each; two at NT = 2), in whole rows of
-    // CUs within the XCD's share of the grid
+    // CUs times the tile workgroups a CU holds (at NT = 1 up to four, as
+    // many as the LDS allows; two at NT = 2, bound by registers), in whole
+    // rows of CUs within the XCD's share of the grid
+    const size_t mask_bytes = (size_t)p.tile_rows * ((p.tile_below + 31) / 32) * sizeof(uint32_t);
+    const size_t lds = sizeof(TileLds) + 36 * sizeof(int) + mask_bytes;
+    const int per_cu = tile_nt(a.G) == 1 ? (int)std::min<size_t>(4, (160 * 1024) / lds) : 2;
     p.tile_cus = xcd_cus();
     p.tile_snake = 0;
     if (p.tile_cus > 0 && (8 % a.Hkv) == 0) {
       const long long per_xcd = tile_grid(p) / 8;
-      const long long start = (long long)p.tile_cus * (tile_nt(a.G) == 1 ? 3 : 2);
+      const long long start = (long long)p.tile_cus * per_cu;
       p.tile_snake = (int)min(start, per_xcd / p.tile_cus * p.tile_cus);
     }
     if (tile_nt(a.G) == 1)
-      hipLaunchKernelGGL((sparse_prefill_tile_kernel<D, DT, 1>), dim3(tile_grid(p)), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((sparse_prefill_tile_kernel<D, DT, 1>), dim3(tile_grid(p)), dim3(256), mask_bytes, s, p);
     else
-      hipLaunchKernelGGL((sparse_prefill_tile_kernel<D, DT, 2>), dim3(tile_grid(p)), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((sparse_prefill_tile_kernel<D, DT, 2>), dim3(tile_grid(p)), dim3(256), mask_bytes, s, p);
     return hipGetLastError();
   };
   const int total = a.B * a.S, per = prefill_rows_per_launch(a, D);
