@@ -1003,16 +1003,20 @@ hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) 
   // 4097..8192 blocks: two waves of 64 keys per lane when both lists fit in
   // LDS (measured ~12 % faster than one wave of 128 on such rows; on shorter
   // rows the two-wave barriers cost more than the occupancy gains), else one
-  // wave of 128; 2049..4096: one wave of 64; the rest: one wave of 32.
+  // wave of 128; 2049..4096: one wave of 64; 1025..2048: one wave of 32; the
+  // rest: one wave of 16 (fewer registers, so a short prefill's rows all run
+  // at once).
   const int list_words = (a.budget * a.ratio + 3) & ~3;
   const int n_long = rows_from(64 * 64) - n_wg;
   const int n64 = rows_from(64 * 32) - n_wg - n_long;
-  const int n32 = (int)total - n_wg - n_long - n64;
+  const int n32 = rows_from(64 * 16) - n_wg - n_long - n64;
+  const int n16 = (int)total - n_wg - n_long - n64 - n32;
   launch_select_wg_for(a, nc_max, 0, (unsigned)n_wg, s);
   if (list_words <= 4096) launch_select_rows<64, 2>(a, n_wg, n_long, s);
   else launch_select_rows<128, 1>(a, n_wg, n_long, s);
   launch_select_rows<64, 1>(a, n_wg + n_long, n64, s);
   launch_select_rows<32, 1>(a, n_wg + n_long + n64, n32, s);
+  launch_select_rows<16, 1>(a, n_wg + n_long + n64 + n32, n16, s);
   return hipGetLastError();
 }
 
