@@ -168,8 +168,23 @@ typedef struct {
  * sit within fp32 rounding of the cut can differ from a float64 reference.
  * workspace: device scratch of at least
  * qsa_indexer_prefill_workspace_bytes() bytes, 256-byte aligned.
+ * Optional prefill -> decode handoff [Plugin: KV pool contract (widened
+ * rows)]: with kv_pool not NULL the call also leaves, for every sequence, the
+ * indexer state a decode step continues from, in the layout
+ * qsa_indexer_decode reads (pool and page table as for qsa_sparse_decode,
+ * num_kv_heads, head_dim, pool_head_dim, num_flat_pages and
+ * max_pages_per_seq describing them): with c = min(context_lengths[b],
+ * seq_len), the kbar of each complete block g < c/ratio (rounded to dtype,
+ * the value prefill scores with) in the V-row tail of token ratio*g, and the
+ * raw idx_k of each token of the trailing incomplete block ratio*(c/ratio)
+ * .. c-1 in its K-row tail.  Only those tails are written (tokens whose
+ * page-table entry is out of range are skipped); the rest of the pool is
+ * left bit-unchanged.  A qsa_indexer_decode step at context length c+1 then
+ * selects for row c as a prefill over c+1 tokens would.  With kv_pool NULL
+ * the handoff fields are ignored.
  * Supported: top_k >= budget*ratio + ratio - 1; floor(seq_len/ratio) <=
- * QSA_MAX_BLOCKS. */
+ * QSA_MAX_BLOCKS; with the handoff, pool_head_dim >= head_dim + cfg.head_dim,
+ * both multiples of 8. */
 typedef struct {
   const void *idx_q;
   const void *idx_k;
@@ -185,6 +200,14 @@ typedef struct {
   qsa_indexer_config cfg;
   qsa_dtype dtype;
   void *stream;
+  /* optional handoff (kv_pool NULL: none) */
+  void *kv_pool;
+  const int32_t *page_table;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t pool_head_dim;
+  int32_t num_flat_pages;
+  int32_t max_pages_per_seq;
 } qsa_indexer_prefill_params;
 
 /* Indexer, one decode step [Plugin: decode B1/B2/B3 and the KV pool

@@ -384,6 +384,36 @@ def indexer_decode(idx_q, idx_k, w_q, w_k, pool, page_table, ctx, icfg, D: int, 
     return (writes, lists, all_scores) if return_scores else (writes, lists)
 
 
+def prefill_state_writes(idx_k, w_k, ctx, page_table, icfg, D: int, dtype: str, page_tokens: int = 128):
+    """The indexer state a prefill of each sequence leaves in the pool tails
+    for decode to continue from [Plugin: "KV pool contract (widened rows)"]:
+    with c = the live length, block g < floor(c/ratio) keeps its kbar (the
+    value prefill scores with) in the V-row tail of token ratio*g, and each
+    token of the trailing incomplete block ratio*floor(c/ratio) .. c-1 keeps
+    its raw index key in its K-row tail.
+
+    idx_k [B,S,hd] raw storage; page_table [B,2,maxPages] (plane 1 pages
+    already offset by numPages).  Returns tail updates (flat_page, row,
+    values[hd] storage) in the form indexer_decode returns; pages past the
+    table or out of range are the caller's to avoid."""
+    B, S = idx_k.shape[0], idx_k.shape[1]
+    r = icfg.compress_ratio
+    writes = []
+    for b in range(B):
+        c = min(int(ctx[b]), S)
+        if c <= 0:
+            continue
+        nc = c // r
+        kbar = pool_blocks(widen(idx_k[b, : nc * r], dtype), 0, w_k, icfg, dtype)
+        for g in range(nc):
+            pg, row = pool_row(None, page_table, b, 1, r * g, page_tokens)
+            writes.append((pg, row, narrow(kbar[g], dtype)))
+        for j in range(nc * r, c):
+            pg, row = pool_row(None, page_table, b, 0, j, page_tokens)
+            writes.append((pg, row, idx_k[b, j].copy()))
+    return writes
+
+
 def apply_tail_writes(pool: np.ndarray, writes, D: int) -> None:
     """Apply indexer_decode's tail updates to a pool in place (head 0)."""
     for pg, row, vals in writes:

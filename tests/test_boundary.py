@@ -144,6 +144,20 @@ def test_indexer_prefill_rejects(no_gpu, kw, status):
     assert _iprefill(**kw) == status
 
 
+HANDOFF = dict(kv_pool=FAKE, page_table=FAKE, num_kv_heads=4, head_dim=128, pool_head_dim=256,
+               num_flat_pages=16, max_pages_per_seq=8)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_table=None), NULLP), (dict(num_kv_heads=0), SHAPE), (dict(num_flat_pages=0), SHAPE),
+    (dict(max_pages_per_seq=0), SHAPE), (dict(pool_head_dim=255), SHAPE), (dict(pool_head_dim=200), SHAPE),
+    (dict(head_dim=0), SHAPE), (dict(head_dim=100), SHAPE), (dict(kv_pool=FAKE + 4), SHAPE),
+])
+def test_indexer_prefill_handoff_rejects(no_gpu, kw, status):
+    """The optional pool handoff is checked like qsa_indexer_decode's pool."""
+    assert _iprefill(**{**HANDOFF, **kw}) == status
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(kv_pool=None), NULLP), (dict(indices=None), NULLP),
     (dict(pool_head_dim=255), SHAPE), (dict(pool_head_dim=200), SHAPE), (dict(top_k=100), SHAPE),

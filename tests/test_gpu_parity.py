@@ -497,6 +497,55 @@ def decode_parity(inp, what, splits=(0,)):
     return pool_dev, lists_t, ws, outs
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_indexer_prefill_handoff_then_decode_steps(dtype):
+    """qsa_indexer_prefill with the pool handoff leaves exactly the oracle's
+    tails and touches nothing else in the pool; qsa_indexer_decode steps that
+    continue from that state select for the following rows as the oracle's
+    prefill of the longer sequences does, and the pool ends with the oracle's
+    state (bit for bit)."""
+    icfg = syn.IndexerCfg(budget=8)
+    S, D, starts = 420, 64, np.array([300, 233], dtype=np.int32)
+    TL.log(f"indexer prefill handoff + decode steps {dtype}")
+    inp = syn.make_prefill(44, B=2, S=S, Hq=2, Hkv=1, D=D, dtype=dtype, ctx=[S, S], icfg=icfg)
+    dec = syn.make_decode(44, ctx=[S, S], B=2, Hq=8, Hkv=2, D=D, dtype=dtype, max_pages=8, icfg=icfg)
+    pool_dev, pt_dev = TL.dev(dec.pool, dtype), TL.dev(dec.page_table)
+    cfg = TL.idx_cfg_struct(icfg)
+    lists = torch.full((2, S, icfg.top_k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(Q.qsa_indexer_prefill_workspace_bytes(cfg, 2, S), dtype=torch.uint8, device="cuda")
+    Q.qsa_indexer_prefill(TL.dev(inp.idx_q, dtype), TL.dev(inp.idx_k, dtype), TL.dev(inp.w_q), TL.dev(inp.w_k),
+                          TL.dev(starts), lists, ws, cfg, kv_pool=pool_dev, page_table=pt_dev, head_dim=D)
+    torch.cuda.synchronize()
+    expect = dec.pool.copy()
+    O.apply_tail_writes(expect, O.prefill_state_writes(inp.idx_k, inp.w_k, starts, dec.page_table, icfg, D, dtype),
+                        D)
+    assert torch.equal(pool_dev.view(torch.int16), TL.dev(expect, dtype).view(torch.int16)), "handoff tails differ"
+    steps = 6
+    rows = [(b, int(starts[b]) + s) for b in range(2) for s in range(steps)]
+    ref, scores = O.indexer_prefill(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, np.array([S, S]), icfg, dtype,
+                                    icfg.top_k, rows=rows, return_scores=True)
+    wsd = torch.empty(Q.qsa_indexer_decode_workspace_bytes(cfg, 2, dec.max_pages), dtype=torch.uint8, device="cuda")
+    swaps = 0
+    for step in range(steps):
+        ctx = starts + step + 1
+        tok = ctx - 1
+        q1 = np.stack([inp.idx_q[b, tok[b]] for b in range(2)])[:, None]
+        k1 = np.stack([inp.idx_k[b, tok[b]] for b in range(2)])[:, None]
+        out = torch.full((2, 1, icfg.top_k), -7, dtype=torch.int32, device="cuda")
+        Q.qsa_indexer_decode(TL.dev(q1, dtype), TL.dev(k1, dtype), TL.dev(inp.w_q), TL.dev(inp.w_k), pool_dev, pt_dev,
+                             TL.dev(ctx.astype(np.int32)), out, wsd, cfg, D)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for b in range(2):
+            t = int(tok[b])
+            swaps += TL.check_list(got[b, 0], ref[(b, t)], scores[(b, t)], t, icfg, f"step {step} b={b}")
+        writes, _ = O.indexer_decode(q1, k1, inp.w_q, inp.w_k, expect, dec.page_table, ctx, icfg, D, dtype,
+                                     icfg.top_k)
+        O.apply_tail_writes(expect, writes, D)
+    TL.log(f"  boundary swaps used: {swaps}")
+    assert torch.equal(pool_dev.view(torch.int16), TL.dev(expect, dtype).view(torch.int16)), "pool after decode differs"
+
+
 DECODE_SMALL = [
     dict(B=6, Hq=32, Hkv=4, D=128, dtype="fp16", ctx=[1, 6, 2052, 3000, 4096, 8191], max_pages=64),
     dict(B=5, Hq=64, Hkv=4, D=128, dtype="bf16", ctx=[2, 7, 2051, 5000, 2049], max_pages=40),

@@ -440,6 +440,11 @@ def test_decode_indexer_continues_prefill_state(budget, S, ts):
         for s in range(r * (t // r), t):                     # raw keys of the open block
             pg, row = O.pool_row(pool, pt, 0, 0, s)
             pool[pg, row, 0, D:] = inp.idx_k[0, s]
+        # the oracle's prefill handoff over the first t tokens leaves exactly these tails
+        handoff = O.prefill_state_writes(inp.idx_k[:, :t], inp.w_k, np.array([t]), pt, icfg, D, "fp16")
+        pool_h = pool0.copy()
+        O.apply_tail_writes(pool_h, handoff, D)
+        assert np.array_equal(pool_h.view(np.uint16), pool.view(np.uint16))
         writes, lists = O.indexer_decode(inp.idx_q[:, t:t + 1], inp.idx_k[:, t:t + 1], inp.w_q,
                                          inp.w_k, pool, pt, np.array([c]), icfg, D, "fp16",
                                          icfg.top_k)
@@ -452,3 +457,41 @@ def test_decode_indexer_continues_prefill_state(budget, S, ts):
         else:
             assert (pg, row) == O.pool_row(pool, pt, 0, 1, r * (c // r - 1))
             assert np.array_equal(O.widen(vals, "fp16"), kbar[c // r - 1])
+
+
+def test_decode_steps_after_prefill_handoff_match_prefill_rows():
+    """Multi-step decode from the prefill handoff: after a prefill of c tokens,
+    decode steps at c+1, c+2, ... select for rows c, c+1, ... exactly as a
+    prefill over the longer sequence does, and the pool then holds the state
+    a prefill of the longer sequence would leave."""
+    icfg = syn.IndexerCfg(budget=5)
+    hd, D, r = icfg.head_dim, 16, icfg.compress_ratio
+    S = 90
+    inp = syn.make_prefill(43, B=2, S=S, Hq=2, Hkv=2, D=D, dtype="bf16", ctx=[S, S], icfg=icfg)
+    rng = np.random.default_rng(43)
+    pool, pt = _pool_from_dense(rng, inp.k[0], inp.v[0], D, hd)
+    pt = np.concatenate([pt, pt], axis=0)                # both sequences share the layout, own rows differ
+    pool = np.concatenate([pool, pool], axis=0)
+    npg = pool.shape[0] // 4
+    pt[1, 0] = np.where(pt[1, 0] >= 0, pt[1, 0] + 2 * npg, -1)
+    pt[1, 1] = np.where(pt[1, 1] >= 0, pt[1, 1] + 2 * npg, -1)
+    starts = [61, 70]                                    # prefill lengths: 1 and 2 tokens of an open block
+    pre = O.indexer_prefill(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.ctx, icfg, "bf16", icfg.top_k)
+    for b, c0 in enumerate(starts):
+        O.apply_tail_writes(pool, [w for w in O.prefill_state_writes(inp.idx_k[b:b + 1, :c0], inp.w_k,
+                                                                        np.array([c0]), pt[b:b + 1], icfg, D,
+                                                                        "bf16")], D)
+    for step in range(9):
+        ctx = np.array([c0 + step + 1 for c0 in starts])
+        tok = ctx - 1
+        q1 = np.stack([inp.idx_q[b, tok[b]] for b in range(2)])[:, None]
+        k1 = np.stack([inp.idx_k[b, tok[b]] for b in range(2)])[:, None]
+        writes, lists = O.indexer_decode(q1, k1, inp.w_q, inp.w_k, pool, pt, ctx, icfg, D, "bf16", icfg.top_k)
+        for b in range(2):
+            assert np.array_equal(lists[b, 0], pre[b, tok[b]]), (step, b)
+        O.apply_tail_writes(pool, writes, D)
+    for b, c0 in enumerate(starts):
+        c = c0 + 9
+        expect = O.prefill_state_writes(inp.idx_k[b:b + 1, :c], inp.w_k, np.array([c]), pt[b:b + 1], icfg, D, "bf16")
+        for pg, row, vals in expect:
+            assert np.array_equal(pool[pg, row, 0, D:].view(np.uint16), vals.view(np.uint16))

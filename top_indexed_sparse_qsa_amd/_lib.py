@@ -60,7 +60,9 @@ class IndexerPrefillParams(ctypes.Structure):
     _fields_ = [("idx_q", _vp), ("idx_k", _vp), ("q_norm_w", _vp), ("k_norm_w", _vp),
                 ("context_lengths", _vp), ("indices", _vp), ("workspace", _vp), ("workspace_bytes", _sz),
                 ("batch", _i32), ("seq_len", _i32), ("top_k", _i32), ("cfg", QsaIndexerConfig),
-                ("dtype", ctypes.c_int), ("stream", _vp)]
+                ("dtype", ctypes.c_int), ("stream", _vp),
+                ("kv_pool", _vp), ("page_table", _vp), ("num_kv_heads", _i32), ("head_dim", _i32),
+                ("pool_head_dim", _i32), ("num_flat_pages", _i32), ("max_pages_per_seq", _i32)]
 
 
 class IndexerDecodeParams(ctypes.Structure):
@@ -195,12 +197,20 @@ def qsa_sparse_decode(q, o, kv_pool, page_table, indices, context_lengths, parti
 
 
 def qsa_indexer_prefill(idx_q, idx_k, q_norm_w, k_norm_w, context_lengths, indices, workspace,
-                        cfg: QsaIndexerConfig, stream=None) -> None:
-    """idx_q [B,S,Hi,hd]; idx_k [B,S,hd]; q_norm_w/k_norm_w fp32 [hd]; indices int32 [B,S,top_k]."""
+                        cfg: QsaIndexerConfig, stream=None, kv_pool=None, page_table=None,
+                        head_dim: int | None = None) -> None:
+    """idx_q [B,S,Hi,hd]; idx_k [B,S,hd]; q_norm_w/k_norm_w fp32 [hd]; indices int32 [B,S,top_k].
+    Optional handoff: kv_pool [2*numPages,128,Hkv,poolHeadDim], page_table int32 [B,2,maxPages],
+    head_dim = the attention head dim (the tails start there)."""
     B, S = idx_k.shape[0], idx_k.shape[1]
     p = IndexerPrefillParams(_ptr(idx_q), _ptr(idx_k), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(context_lengths),
                              _ptr(indices), _ptr(workspace), workspace.numel() * workspace.element_size(),
                              B, S, indices.shape[-1], cfg, _dtype_code(idx_q), _stream(stream))
+    if kv_pool is not None:
+        p.kv_pool, p.page_table = _ptr(kv_pool), _ptr(page_table)
+        p.num_kv_heads, p.pool_head_dim, p.num_flat_pages = kv_pool.shape[2], kv_pool.shape[3], kv_pool.shape[0]
+        p.head_dim = int(head_dim) if head_dim is not None else 0
+        p.max_pages_per_seq = page_table.shape[-1] if page_table is not None else 0
     _check("qsa_indexer_prefill", load().qsa_indexer_prefill(ctypes.byref(p)))
 
 

@@ -212,6 +212,14 @@ qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p) {
   if (!all_aligned16(p->idx_q, p->idx_k)) return QSA_ERR_BAD_SHAPE;
   if ((int64_t)p->batch * p->seq_len > (int64_t)INT32_MAX / 2) return QSA_ERR_UNSUPPORTED;
   if (((uintptr_t)p->workspace % kAlign) != 0) return QSA_ERR_BAD_SHAPE;
+  if (p->kv_pool) {
+    if (!p->page_table) return QSA_ERR_NULL_POINTER;
+    if (p->num_kv_heads < 1 || p->num_flat_pages < 1 || p->max_pages_per_seq < 1) return QSA_ERR_BAD_SHAPE;
+    if (p->head_dim < 1 || p->pool_head_dim < p->head_dim + p->cfg.head_dim || (p->head_dim % 8) != 0 ||
+        (p->pool_head_dim % 8) != 0)
+      return QSA_ERR_BAD_SHAPE;
+    if (!all_aligned16(p->kv_pool)) return QSA_ERR_BAD_SHAPE;
+  }
   const PrefillWs w = prefill_ws(p->cfg, p->batch, p->seq_len);
   if (p->workspace_bytes < w.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
   char *ws = static_cast<char *>(p->workspace);
@@ -236,7 +244,15 @@ qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p) {
   pa.theta = (double)p->cfg.rope_theta;
   pa.eps = (double)p->cfg.rms_eps;
   pa.dt = dt;
+  pa.pool = static_cast<uint16_t *>(p->kv_pool);
+  pa.pt = p->kv_pool ? p->page_table : nullptr;
+  pa.Hkv = p->kv_pool ? p->num_kv_heads : 0;
+  pa.D = p->kv_pool ? p->head_dim : 0;
+  pa.PHD = p->kv_pool ? p->pool_head_dim : 0;
+  pa.num_flat_pages = p->kv_pool ? p->num_flat_pages : 0;
+  pa.max_pages = p->kv_pool ? p->max_pages_per_seq : 0;
   if (qsa::launch_idx_prep(pa, s) != hipSuccess) return QSA_ERR_LAUNCH;
+  if (qsa::launch_idx_handoff(pa, s) != hipSuccess) return QSA_ERR_LAUNCH;
 
   qsa::IdxScoreArgs sa;
   sa.qhat = pa.qhat;

@@ -72,6 +72,18 @@ __device__ __forceinline__ void norm_rope2(double x0, double x1, double w0, doub
   o1 = d1 < rot ? (d1 < half ? y1 * r.c1 - p1 * r.s1 : y1 * r.c1 + p1 * r.s1) : y1;
 }
 
+// Element offset of KV head 0 of `token`'s row in the paged pool (128 tokens
+// per page; ptrow is the sequence's K or V page-table row, V pages already
+// offset by numPages), or -1 when its page-table entry is out of range.
+__device__ __forceinline__ long long pool_row_off(const int32_t *ptrow, int token, int max_pages,
+                                                  int num_flat_pages, int Hkv, int PHD) {
+  const int pi = token >> 7;
+  if (token < 0 || pi >= max_pages) return -1;
+  const int pg = ptrow[pi];
+  if ((unsigned)pg >= (unsigned)num_flat_pages) return -1;
+  return (((long long)pg * 128 + (token & 127)) * Hkv) * PHD;
+}
+
 // Items: B*S query rows, then B*Gmax blocks; a.per_wave consecutive items
 // per wave (up to kPrepItemsPerWave, fewer when that would leave the chip
 // short of waves), four waves per workgroup.
@@ -116,6 +128,37 @@ __global__ __launch_bounds__(256) void idx_prep_kernel(IdxPrepArgs a) {
       a.kbar[ob + lane] = (uint16_t)f64_to_bits(o0, a.dt);
       a.kbar[ob + 64 + lane] = (uint16_t)f64_to_bits(o1, a.dt);
     }
+  }
+}
+
+// Prefill -> decode handoff: the indexer state a decode step continues from,
+// in the pool tails (columns [D, D + 128) of KV head 0 rows).  Wave item
+// (b, g), g < Gmax: block g's kbar, as pooled above, into the V-row tail of
+// token ratio*g when the block is complete; item (b, Gmax): the raw keys of
+// the trailing incomplete block into the K-row tails of its tokens.  Rows
+// whose page-table entry is out of range are skipped.
+__global__ __launch_bounds__(256) void idx_handoff_kernel(IdxPrepArgs a) {
+  const int lane = lane_id();
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (long long)a.B * (a.Gmax + 1)) return;
+  const int b = (int)(item / (a.Gmax + 1)), g = (int)(item % (a.Gmax + 1));
+  const int live = min(a.ctx[b], a.S), nc = live / a.ratio;
+  const int32_t *ptk = a.pt + (size_t)b * 2 * a.max_pages, *ptv = ptk + a.max_pages;
+  if (g < a.Gmax) {
+    if (g >= nc) return;
+    const long long o = pool_row_off(ptv, a.ratio * g, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
+    if (o < 0) return;
+    const uint16_t *kb = a.kbar + ((size_t)b * a.Gmax + g) * 128;
+    a.pool[o + a.D + lane] = kb[lane];
+    a.pool[o + a.D + 64 + lane] = kb[lane + 64];
+    return;
+  }
+  for (int t = nc * a.ratio; t < live; ++t) {
+    const long long o = pool_row_off(ptk, t, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
+    if (o < 0) continue;
+    const uint16_t *k = a.idx_k + ((size_t)b * a.S + t) * 128;
+    a.pool[o + a.D + lane] = k[lane];
+    a.pool[o + a.D + 64 + lane] = k[lane + 64];
   }
 }
 
@@ -769,14 +812,6 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
 // ---------------------------------------------------------------------------
 // Decode B1: queries at p = ctx-1 and the tail update.  One workgroup per sequence.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ long long pool_row_off(const int32_t *ptrow, int token, int max_pages,
-                                                  int num_flat_pages, int Hkv, int PHD) {
-  const int pi = token >> 7;
-  if (token < 0 || pi >= max_pages) return -1;
-  const int pg = ptrow[pi];
-  if ((unsigned)pg >= (unsigned)num_flat_pages) return -1;
-  return (((long long)pg * 128 + (token & 127)) * Hkv) * PHD;
-}
 
 // Wave h < Hi prepares query head h; wave Hi updates the pool tail, so the
 // query and key chains run side by side.
@@ -916,6 +951,13 @@ hipError_t launch_idx_prep(const IdxPrepArgs &a_in, hipStream_t s) {
   a.per_wave = (int)std::min<long long>(kPrepItemsPerWave, std::max<long long>(1, items / 8192));
   const long long waves = (items + a.per_wave - 1) / a.per_wave;
   hipLaunchKernelGGL(idx_prep_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_idx_handoff(const IdxPrepArgs &a, hipStream_t s) {
+  if (!a.pool) return hipSuccess;
+  const long long waves = (long long)a.B * (a.Gmax + 1);
+  hipLaunchKernelGGL(idx_handoff_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -50,6 +50,10 @@ struct IdxPrepArgs {
   int dt;
   int per_wave;     // items per wave (set by the launcher)
   double freq[64];  // RoPE frequencies theta^(-2i/rot), i < rot/2 (set by the launcher)
+  // prefill -> decode handoff into the pool tails (pool == nullptr: none)
+  uint16_t *pool;
+  const int32_t *pt;
+  int Hkv, D, PHD, num_flat_pages, max_pages;
 };
 
 struct IdxScoreArgs {
@@ -106,6 +110,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStream_t s);
 hipError_t launch_sparse_decode(const DecodeAttnArgs &a, int D, int dt, hipStream_t s);
 hipError_t launch_idx_prep(const IdxPrepArgs &a, hipStream_t s);
+// prefill -> decode handoff into the pool tails (no-op when a.pool is null)
+hipError_t launch_idx_handoff(const IdxPrepArgs &a, hipStream_t s);
 hipError_t launch_idx_score(const IdxScoreArgs &a, int dt, hipStream_t s);
 hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s);
 hipError_t launch_idx_dec_prep(const IdxDecPrepArgs &a, hipStream_t s);
