@@ -88,8 +88,9 @@ typedef struct {
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  * context_lengths: int32 [batch]; rows t >= context_lengths[b] are written
  * as +0.0 and ids >= context_lengths[b] are never read.  A live row whose
- * list holds no usable id is +0.0.  A chunk of 32 slots that holds no id
- * >= 0 ends the row's list.
+ * list holds no usable id (0 <= id < context_lengths[b]) is +0.0.  A chunk
+ * of 32 slots (slots 32c .. 32c+31) that holds no usable id ends the row's
+ * list: later slots are not read.
  * Supported: head_dim 64 or 128; num_q_heads a multiple of num_kv_heads with
  * ratio 1..16; top_k >= 1. */
 typedef struct {
