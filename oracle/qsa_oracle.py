@@ -25,7 +25,7 @@ pages are cited by title and section):
   relu(q_h . k_b) / sqrt(hd)) and qsa_score_rows (-inf beyond each row's
   complete block count).
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
 * RoPE rotates the first ``rot`` dims as pairs (i, i + rot/2) by angle
   pos * theta^(-2i/rot); dims at or past ``rot`` pass through.
 * RMSNorm is x / sqrt(mean(x^2) + eps) * (1 + w), mean over the head dim.
