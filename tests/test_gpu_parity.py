@@ -391,7 +391,7 @@ def test_prefill_workload_full_size(wl):
     rng = np.random.default_rng(100 + wl)
     # workload 2 (the headline one) row by row in full; the larger ones sampled
     rows = ([(b, t) for b in range(inp.B) for t in range(inp.S)] if wl == 2
-            else TL.sample_rows(inp.B, inp.S, inp.ctx, 24, rng))
+            else TL.sample_rows(inp.B, inp.S, inp.ctx, 128, rng))
     TL.log(f"prefill workload {wl}: oracle on {len(rows)} rows")
     out_np = out.cpu().numpy()
     lists = {r: out_np[r] for r in rows}
@@ -421,7 +421,7 @@ def test_sparse_prefill_structured_lists_full_size(wl):
     rng = np.random.default_rng(200 + wl)
     idx = TL.structured_lists(rng, inp.B, inp.S, inp.ctx, inp.icfg, inp.icfg.top_k)
     o = gpu_sparse_prefill(inp, idx)
-    rows = ([(0, t) for t in range(inp.S)] if wl == 2 else TL.sample_rows(inp.B, inp.S, inp.ctx, 24, rng))
+    rows = ([(0, t) for t in range(inp.S)] if wl == 2 else TL.sample_rows(inp.B, inp.S, inp.ctx, 128, rng))
     ref = O.sparse_prefill(inp.q, inp.k, inp.v, idx, inp.ctx, inp.scale, inp.dtype, rows=rows)
     for (b, t) in rows:
         TL.check_attention(TL.host_f64(o[b, t], inp.dtype), ref[(b, t)], inp.dtype, f"b={b} t={t}")
