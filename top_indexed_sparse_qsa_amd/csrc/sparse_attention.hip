@@ -25,6 +25,13 @@
 //     contiguous dims [32q, 32q+32) of head m.
 // The next chunk's gathers are in flight while the current one computes, and
 // ids run two chunks ahead.
+//
+// Prefill rows whose lists cover most of their causal prefix (all of them
+// before the budget fills) run as list tiles instead: a workgroup of four
+// waves takes several consecutive rows of one KV head, turns their lists
+// into a per-row key mask in LDS, and walks the keys of the prefix densely,
+// each 32-key chunk of K and V staged once in LDS for all its (row, head)
+// columns (see "Tiles" below).
 #include <math.h>
 
 #include "qsa_device.h"
