@@ -316,8 +316,8 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhea
 // up to the first 32-slot chunk with no usable id.  The mask reproduces
 // exactly the keys the list walk would use, or the tile gives up: an id
 // repeated in a list or a key at or past t_act (outside the causal range)
-// sends the tile's rows to the list walk, one row per wave at a time (the kernel runs
-// that walk, so its code exists once).
+// sends the tile's rows to a cooperative list walk, one row at a time (all
+// four waves stage each chunk; lists that break the contract only).
 //
 // Then the workgroup walks the keys once: every 32-key chunk of K and V is
 // gathered once into a double-buffered LDS tile (two chunks in flight in
@@ -822,8 +822,8 @@ __device__ __forceinline__ void walk_row(const PrefillAttnArgs &a, int b, int t,
 }
 
 // The list walk for rows [t0, t_end) of a tile whose lists the key mask
-// cannot represent (a repeated id, an id outside the causal range, ids
-// after the walk's stop): one row at a time, all four waves stage each
+// cannot represent (a repeated id, or a key at or past the tile's causal
+// range): one row at a time, all four waves stage each
 // 32-slot chunk's K/V rows in LDS and wave 0 runs the online softmax over
 // the usable slots, stopping at the first chunk without one — the list
 // walk's result, at the tile's small register budget.  Rare (lists that
