@@ -355,8 +355,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // words per 32 bins keep reads of consecutive bins by consecutive lanes free
 // of bank conflicts.
 constexpr int kSelBins = 2048;
-__device__ __forceinline__ int hpad(int d) { return d + ((d >> 5) << 2); }
+__host__ __device__ constexpr int hpad(int d) { return d + ((d >> 5) << 2); }
 constexpr int kSelHistWords = kSelBins + (kSelBins >> 3);
+constexpr int kSelOddVecs = (hpad(255) + 4) >> 2;  // a padded 256-bin histogram in 16-byte words
 
 // Radix window of a pass: the first takes 11 bits below the bits shared by
 // every key, later ones 8.
@@ -612,14 +613,16 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
 // sequence, up to 32768 blocks) and prefill rows over 8192 blocks.  Thread
 // j holds the KPT keys of blocks [j*KPT, (j+1)*KPT) in registers, so one
 // workgroup scan of per-thread counts places kept blocks in ascending order.
-// Passes as in the per-row kernel, over one workgroup histogram: a
-// workgroup scan of per-thread bin sums names the thread whose range holds
-// the cut, and that thread walks its own bins.
+// Passes as in the per-row kernel, over a workgroup histogram: a workgroup
+// scan of per-thread bin sums names the thread whose range holds the cut,
+// and that thread walks its own bins.  Two histograms alternate, so a pass
+// clears the next one's while it counts and takes three barriers.
 // ---------------------------------------------------------------------------
 constexpr int kSelWgThreads = 1024;
 
-// Exclusive prefix sum of v over the workgroup in thread order; s_wt holds
-// one int per wave and is free again on return.
+// Exclusive prefix sum of v over the workgroup in thread order, with one
+// barrier.  s_wt holds one int per wave and is read after that barrier, so
+// the caller puts another barrier between two calls.
 __device__ __forceinline__ int wg_exscan(int v, int *s_wt, int *total) {
   constexpr int NW = kSelWgThreads / 64;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -633,7 +636,6 @@ __device__ __forceinline__ int wg_exscan(int v, int *s_wt, int *total) {
     before += w < wv ? x : 0;
     all += x;
   }
-  __syncthreads();
   *total = all;
   return before + incl - v;
 }
@@ -642,6 +644,7 @@ template <int KPT, bool STAGE>
 __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
   constexpr int NT = kSelWgThreads, NW = NT / 64;
   extern __shared__ uint32_t s_dyn[];  // padded histogram | list
+  __shared__ u32x4 s_hodd[kSelOddVecs];  // histogram of the odd passes
   __shared__ int s_wt[NW];
   __shared__ uint32_t s_red[2 * NW];
   __shared__ int s_res[3];
@@ -675,8 +678,12 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
     for (int i = tid; i < a.top_k; i += NT) out[i] = i <= t ? i : -1;
     return;
   }
-  uint32_t *hist = s_dyn;
   int32_t *lst = STAGE ? reinterpret_cast<int32_t *>(s_dyn + kSelHistWords) : out;
+  // Pass p counts into s_dyn (even p) or s_hodd (odd p); both start cleared
+  // here, and pass p >= 1 clears the one pass p + 1 uses, which pass p - 1
+  // finished reading before its last barrier.
+  for (int j = tid; j < (kSelHistWords >> 2); j += NT) reinterpret_cast<u32x4 *>(s_dyn)[j] = u32x4{0u, 0u, 0u, 0u};
+  if (tid < kSelOddVecs) s_hodd[tid] = u32x4{0u, 0u, 0u, 0u};
 
   uint32_t key[KPT];
   const int i0 = tid * KPT;
@@ -719,19 +726,18 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
   uint32_t pmask = top < 0 ? 0xffffffffu : ~((2u << top) - 1u);
   uint32_t prefix = kmax & pmask;
   int remaining = a.budget;
-  bool whole_bin = false;
   for (int pass = 0; top >= 0; ++pass) {
     const int w = sel_window(pass, top), shift = top + 1 - w;
     const uint32_t dmask = (1u << w) - 1u;
     const int nb = 1 << w;
-    const int nvec = (hpad(nb - 1) + 4) >> 2;
-    for (int j = tid; j < nvec; j += NT) reinterpret_cast<u32x4 *>(hist)[j] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
+    uint32_t *hist = (pass & 1) ? reinterpret_cast<uint32_t *>(s_hodd) : s_dyn;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const uint32_t k = key[j];
       if ((k & pmask) == prefix) atomicAdd(&hist[hpad((int)((k >> shift) & dmask))], 1u);
     }
+    if (pass > 0 && tid < kSelOddVecs)  // later windows take at most 8 bits
+      ((pass & 1) ? reinterpret_cast<u32x4 *>(s_dyn) : s_hodd)[tid] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     // thread j sums bins [nb - per*(j+1), nb - per*j): thread 0 the top digits
     const int per = nb > NT ? nb / NT : 1;
@@ -761,15 +767,14 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
     prefix |= (uint32_t)dsel << shift;
     pmask |= dmask << shift;
     remaining -= above;
-    if (cnt == remaining) {  // the whole bin is kept
-      whole_bin = true;
-      break;
-    }
+    if (cnt == remaining) break;  // the whole bin is kept
     top = shift - 1;
   }
 
   // Keys with (k & pmask) > prefix are kept; of those == prefix, the first
-  // `remaining` in index order (all of them when whole_bin).
+  // `remaining` in index order (all of them when the loop kept a whole bin).
+  // Each pass's scan is followed by the s_res barrier, so this scan may
+  // reuse s_wt.
   int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -777,12 +782,15 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
     n_gt += (int)key[j] >= 0 && m > prefix;
     n_eq += m == prefix;
   }
-  int tot, take_eq = n_eq;
-  if (!whole_bin) {
-    const int eq_before = wg_exscan(n_eq, s_wt, &tot);
-    take_eq = min(n_eq, max(0, remaining - eq_before));
-  }
-  int pos = wg_exscan(n_gt + take_eq, s_wt, &tot);
+  // One scan of both counts (n_gt in the high half: fewer than budget < nc
+  // <= 32768 keys are above the cut, so neither half overflows).  The keys
+  // equal to the cut before this thread's take min(eq_before, remaining)
+  // slots, which is also right when the whole bin is kept.
+  int tot;
+  const int both = wg_exscan(n_eq | (n_gt << 16), s_wt, &tot);
+  const int eq_before = both & 0xffff;
+  const int take_eq = min(n_eq, max(0, remaining - eq_before));
+  int pos = (both >> 16) + min(eq_before, remaining);
   int eq_seen = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {

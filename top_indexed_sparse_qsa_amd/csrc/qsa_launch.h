@@ -104,7 +104,7 @@ struct IdxDecScoreArgs {
   int waves_per_seq;
 };
 
-constexpr int kScoreTilesPerWave = 2;  // decode scoring: 4 tiles of 16 blocks per wave
+constexpr int kScoreTilesPerWave = 2;  // decode scoring: tiles of 16 blocks per wave
 constexpr float kLog2e = 1.4426950408889634f;
 
 hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStream_t s);
