@@ -184,8 +184,8 @@ typedef struct {
  * selects for row c as a prefill over c+1 tokens would.  With kv_pool NULL
  * the handoff fields are ignored.
  * Supported: top_k >= budget*ratio + ratio - 1; floor(seq_len/ratio) <=
- * QSA_MAX_BLOCKS; with the handoff, pool_head_dim >= head_dim + cfg.head_dim,
- * both multiples of 8. */
+ * QSA_MAX_BLOCKS; batch*seq_len <= INT32_MAX/2; with the handoff,
+ * pool_head_dim >= head_dim + cfg.head_dim, both multiples of 8. */
 typedef struct {
   const void *idx_q;
   const void *idx_k;
@@ -229,7 +229,8 @@ typedef struct {
  * pool as for qsa_sparse_decode.  workspace: at least
  * qsa_indexer_decode_workspace_bytes() bytes.
  * Supported: pool_head_dim >= head_dim + cfg.head_dim;
- * max_pages_per_seq*128/ratio <= QSA_MAX_BLOCKS. */
+ * max_pages_per_seq*128/ratio <= QSA_MAX_BLOCKS, and batch times that
+ * <= INT32_MAX/2. */
 typedef struct {
   const void *idx_q;
   const void *idx_k;

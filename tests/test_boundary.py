@@ -162,7 +162,7 @@ def test_indexer_prefill_handoff_rejects(no_gpu, kw, status):
     (dict(kv_pool=None), NULLP), (dict(indices=None), NULLP),
     (dict(pool_head_dim=255), SHAPE), (dict(pool_head_dim=200), SHAPE), (dict(top_k=100), SHAPE),
     (dict(max_pages_per_seq=2048), UNSUP), (dict(workspace_bytes=64), WS), (dict(num_kv_heads=0), SHAPE),
-    (dict(cfg=Q.indexer_config(num_heads=0)), UNSUP),
+    (dict(cfg=Q.indexer_config(num_heads=0)), UNSUP), (dict(batch=1 << 23), UNSUP),
 ])
 def test_indexer_decode_rejects(no_gpu, kw, status):
     assert _idecode(**kw) == status

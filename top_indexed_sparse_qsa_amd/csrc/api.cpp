@@ -175,7 +175,7 @@ qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
   splits = (chunks + per - 1) / per;  // drop splits that would get no slots
   const int wpg = splits < 4 ? splits : 4;
   const int ngroups = (splits + wpg - 1) / wpg;
-  qsa::DecodeAttnArgs a;
+  qsa::DecodeAttnArgs a{};
   a.q = static_cast<const uint16_t *>(p->q);
   a.o = static_cast<uint16_t *>(p->o);
   a.pool = static_cast<const uint16_t *>(p->kv_pool);
@@ -226,7 +226,7 @@ qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p) {
   const hipStream_t s = (hipStream_t)p->stream;
   const int dt = (int)p->dtype;
 
-  qsa::IdxPrepArgs pa;
+  qsa::IdxPrepArgs pa{};
   pa.idx_q = static_cast<const uint16_t *>(p->idx_q);
   pa.idx_k = static_cast<const uint16_t *>(p->idx_k);
   pa.wq = p->q_norm_w;
@@ -254,7 +254,7 @@ qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p) {
   if (qsa::launch_idx_prep(pa, s) != hipSuccess) return QSA_ERR_LAUNCH;
   if (qsa::launch_idx_handoff(pa, s) != hipSuccess) return QSA_ERR_LAUNCH;
 
-  qsa::IdxScoreArgs sa;
+  qsa::IdxScoreArgs sa{};
   sa.qhat = pa.qhat;
   sa.kbar = pa.kbar;
   sa.scores = reinterpret_cast<float *>(ws + w.scores);
@@ -267,7 +267,7 @@ qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p) {
   sa.ratio = p->cfg.compress_ratio;
   if (qsa::launch_idx_score(sa, dt, s) != hipSuccess) return QSA_ERR_LAUNCH;
 
-  qsa::IdxSelectArgs xa;
+  qsa::IdxSelectArgs xa{};
   xa.scores = sa.scores;
   xa.row_stride = w.stride;
   xa.out = p->indices;
@@ -296,6 +296,9 @@ qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
   if (p->top_k < min_top_k(p->cfg)) return QSA_ERR_BAD_SHAPE;
   if ((int64_t)p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio > QSA_MAX_BLOCKS)
     return QSA_ERR_UNSUPPORTED;
+  // block indices across the batch (score rows, scoring waves) stay in int
+  if ((int64_t)p->batch * (p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio) > (int64_t)INT32_MAX / 2)
+    return QSA_ERR_UNSUPPORTED;
   if (!all_aligned16(p->idx_q, p->idx_k, p->kv_pool)) return QSA_ERR_BAD_SHAPE;
   if (((uintptr_t)p->workspace % kAlign) != 0) return QSA_ERR_BAD_SHAPE;
   const DecodeWs w = decode_ws(p->cfg, p->batch, p->max_pages_per_seq);
@@ -305,7 +308,7 @@ qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
   const int dt = (int)p->dtype;
   const int gmax = p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio;
 
-  qsa::IdxDecPrepArgs pa;
+  qsa::IdxDecPrepArgs pa{};
   pa.idx_q = static_cast<const uint16_t *>(p->idx_q);
   pa.idx_k = static_cast<const uint16_t *>(p->idx_k);
   pa.wq = p->q_norm_w;
@@ -329,7 +332,7 @@ qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
   pa.dt = dt;
   if (qsa::launch_idx_dec_prep(pa, s) != hipSuccess) return QSA_ERR_LAUNCH;
 
-  qsa::IdxDecScoreArgs sa;
+  qsa::IdxDecScoreArgs sa{};
   sa.qhat = pa.qhat;
   sa.pool = pa.pool;
   sa.pt = p->page_table;
@@ -347,7 +350,7 @@ qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
   sa.waves_per_seq = (gmax + 16 * qsa::kScoreTilesPerWave - 1) / (16 * qsa::kScoreTilesPerWave);
   if (qsa::launch_idx_dec_score(sa, dt, s) != hipSuccess) return QSA_ERR_LAUNCH;
 
-  qsa::IdxSelectArgs xa;
+  qsa::IdxSelectArgs xa{};
   xa.scores = sa.scores;
   xa.row_stride = w.stride;
   xa.out = p->indices;
