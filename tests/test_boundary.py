@@ -188,3 +188,35 @@ def test_bench_counter_figures_follow_kernel_code(tmp_path):
     changed = tmp_path / "code.hip"
     changed.write_text(src.replace("kTileRangeX2 = QSA_TILE_RANGE_X2", "kTileRangeX2 = QSA_TILE_RANGE_X2 + 1", 1))
     assert bench.kernel_code_sha256(str(changed)) != base
+
+
+def test_product_path_and_oracle_are_separate():
+    """The package (binding and HIP sources) never imports or includes the
+    oracle, and the oracle never imports the package or its sources: the two
+    share only the seeded input generator used by the tests."""
+    import ast
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "top_indexed_sparse_qsa_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            path = os.path.join(dirpath, f)
+            if f.endswith(".py"):
+                tree = ast.parse(open(path).read())
+                mods = [a.name for n in ast.walk(tree) if isinstance(n, ast.Import) for a in n.names]
+                mods += [n.module or "" for n in ast.walk(tree) if isinstance(n, ast.ImportFrom)]
+                assert not [m for m in mods if m.split(".")[0] in ("oracle", "qsa_oracle", "qsa_synth")], path
+            elif f.endswith((".hip", ".cpp", ".h")):
+                incs = re.findall(r'#include\s+[<"]([^>"]+)[>"]', open(path).read())
+                assert not [i for i in incs if "oracle" in i], path
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            tree = ast.parse(open(os.path.join(ROOT, "oracle", f)).read())
+            mods = [a.name for n in ast.walk(tree) if isinstance(n, ast.Import) for a in n.names]
+            mods += [n.module or "" for n in ast.walk(tree) if isinstance(n, ast.ImportFrom)]
+            assert not [m for m in mods if m.split(".")[0] in ("top_indexed_sparse_qsa_amd", "torch")], f
+    # importing the binding and loading the library pulls in no oracle module
+    code = ("import sys, top_indexed_sparse_qsa_amd as Q; Q.load(); "
+            "print(sorted(m for m in sys.modules if 'oracle' in m))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "[]", out.stdout
