@@ -774,14 +774,15 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
   // Keys with (k & pmask) > prefix are kept; of those == prefix, the first
   // `remaining` in index order (all of them when the loop kept a whole bin).
   // Each pass's scan is followed by the s_res barrier, so this scan may
-  // reuse s_wt.
-  int n_gt = 0, n_eq = 0;
+  // reuse s_wt.  Bit j of gt_bits / eq_bits: key j above / equal to the cut.
+  uint32_t gt_bits = 0u, eq_bits = 0u;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const uint32_t m = key[j] & pmask;
-    n_gt += (int)key[j] >= 0 && m > prefix;
-    n_eq += m == prefix;
+    gt_bits |= ((int)key[j] >= 0 && m > prefix) ? 1u << j : 0u;
+    eq_bits |= m == prefix ? 1u << j : 0u;
   }
+  const int n_gt = __builtin_popcount(gt_bits), n_eq = __builtin_popcount(eq_bits);
   // One scan of both counts (n_gt in the high half: fewer than budget < nc
   // <= 32768 keys are above the cut, so neither half overflows).  The keys
   // equal to the cut before this thread's take min(eq_before, remaining)
@@ -791,24 +792,23 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
   const int eq_before = both & 0xffff;
   const int take_eq = min(n_eq, max(0, remaining - eq_before));
   int pos = (both >> 16) + min(eq_before, remaining);
-  int eq_seen = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t m = key[j] & pmask;
-    bool keep = (int)key[j] >= 0 && m > prefix;
-    if (m == prefix) {
-      keep = eq_seen < take_eq;
-      ++eq_seen;
+  // kept keys: those above the cut and the lowest take_eq equal ones; the
+  // emission visits set bits only (a thread keeps few of its KPT keys)
+  uint32_t keep = gt_bits;
+  for (int e = 0; e < take_eq; ++e) {
+    keep |= eq_bits & (0u - eq_bits);
+    eq_bits &= eq_bits - 1u;
+  }
+  while (keep != 0u) {
+    const int j = __builtin_ctz(keep);
+    keep &= keep - 1u;
+    const int blk = r * (i0 + j);
+    if (STAGE && r == 4) {
+      *reinterpret_cast<int4 *>(lst + 4 * pos) = make_int4(blk, blk + 1, blk + 2, blk + 3);
+    } else {
+      for (int q = 0; q < r; ++q) lst[r * pos + q] = blk + q;
     }
-    if (keep) {
-      const int blk = r * (i0 + j);
-      if (STAGE && r == 4) {
-        *reinterpret_cast<int4 *>(lst + 4 * pos) = make_int4(blk, blk + 1, blk + 2, blk + 3);
-      } else {
-        for (int q = 0; q < r; ++q) lst[r * pos + q] = blk + q;
-      }
-      ++pos;
-    }
+    ++pos;
   }
   __syncthreads();
   const int head = r * a.budget;
