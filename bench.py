@@ -1,25 +1,43 @@
 """Benchmark of the QSA hot path on one MI355X.
 
-One step = one prefill pass of the chosen workload: qsa_indexer_prefill
+One step = one prefill pass of the headline workload (the long prefill,
+B=1 S=32768 Hq=32 Hkv=4 D=128 fp16 by default): qsa_indexer_prefill
 (pooling, query prep, block scoring, top-512 select + expand) followed by
 qsa_sparse_prefill over the lists it produced.  Inputs are resident in HBM
-before the timed region.  The decode pair (qsa_indexer_decode +
-qsa_sparse_decode) on the paged workload is timed the same way and reported
-in the "decode" object of the same JSON line.
+before the timed region.  ``value`` is live tokens per second over the wall
+clock of the timed steps.
 
-Prints ONE JSON line.  The roofline object covers the dominant call
-(qsa_sparse_prefill: its tile and row kernels): algorithmic bytes per call /
-its average duration measured with HIP events on the launch stream (timing-only
-events, created without the system-scope fence), against
-HBM, and the algorithmic flops (QK^T and PV over the listed keys) against
-the dense fp16/bf16 MFMA peak.  cpu_baseline times the CPU oracle on the
-same workload.
+The same JSON line carries, per workload, the same measurement for the other
+prefill workloads (``workloads``: the tiny fixed-list one runs attention
+only), and the decode pair (qsa_indexer_decode + qsa_sparse_decode) on the
+paged workload (``decode``, sequences per second over the wall clock).
+
+Rooflines.  Every ``frac`` is a fraction of a published peak that the
+quantity really can reach:
+* prefill attention: algorithmic flops (QK^T and PV over the listed keys)
+  per second against the dense fp16/bf16 MFMA peak.  The algorithmic bytes
+  (every listed K/V row counted once per row) exceed the HBM peak in rate,
+  because rows share K/V through the caches, so they are reported as a rate
+  of their own (``algorithmic_byte_rate_gbs``), not as a fraction; HBM is
+  priced with the bytes the counters saw (``traffic``, from the committed
+  rocprofv3 FETCH_SIZE / WRITE_SIZE figures, null once the kernel code has
+  changed since they were taken).
+* indexer: scoring flops against the MFMA peak.
+* decode: algorithmic bytes per step (distinct pool rows, far larger than
+  the caches) against HBM.
+Kernel durations are HIP-event averages on the launch stream over a loop of
+their own (timing-only events, created without the system-scope fence), so
+that the wall-clock loop carries no events.
+
+``cpu_baseline`` times the oracle, unchanged, on all host cores (one worker
+process per core, single-threaded BLAS each, over a bounded row sample); it
+runs before the GPU is touched.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
+import multiprocessing as mp
 import os
 import platform
 import sys
@@ -36,19 +54,24 @@ MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_prefill_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "top_indexed_sparse_qsa_amd", "csrc", "sparse_attention.hip")
 METRIC = "sparse prefill tokens/s + decode seqs/s (topK 2051); % HBM roofline"
-PREFILL_WORKLOADS = (2, 3, 5)
-TIMING_EVERY = 5  # prefill steps between timed (event-bracketed) steps
+PREFILL_WORKLOADS = (1, 2, 3, 5)
 DECODE_WORKLOAD = 4
+HEADLINE = 3
+MAX_CPU_WORKERS = 16  # the host share of one GPU on the box
+CPU_PREFILL_ROWS = 1536
+CPU_DECODE_SEQS = 32
+CPU_DECODE_REPS = 6
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=PREFILL_WORKLOADS,
-                    help="prefill workload timed as the step (default: 2)")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--headline", type=int, default=HEADLINE, choices=(2, 3, 5),
+                    help="prefill workload whose rate is `value` (default: 3)")
+    ap.add_argument("--workloads", default="1,2,3,4,5",
+                    help="comma list of workloads to run (4 = decode); the headline always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
@@ -108,6 +131,10 @@ class HipTimingEvents:
         self.made = []
 
 
+def note(msg):
+    print(f"# bench: {msg}", file=sys.stderr, flush=True)
+
+
 def dev(a, dtype=None):
     import torch
     if dtype == "bf16":
@@ -120,74 +147,115 @@ def cfg_struct(Q, icfg):
                             icfg.rope_theta, icfg.rms_eps)
 
 
-def prefill_bench(args, Q, syn, torch):
-    inp = syn.workload(args.workload)
-    icfg = inp.icfg
-    e = 2
-    cfg = cfg_struct(Q, icfg)
-    q, k, v = dev(inp.q, inp.dtype), dev(inp.k, inp.dtype), dev(inp.v, inp.dtype)
-    iq, ik = dev(inp.idx_q, inp.dtype), dev(inp.idx_k, inp.dtype)
-    wq, wk, ctx = dev(inp.w_q), dev(inp.w_k), dev(inp.ctx)
-    o = torch.empty_like(q)
-    lists = torch.empty((inp.B, inp.S, icfg.top_k), dtype=torch.int32, device="cuda")
-    ws = torch.empty(Q.qsa_indexer_prefill_workspace_bytes(cfg, inp.B, inp.S), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-    T = HipTimingEvents()
-
-    def step(ev=None):
-        if ev:
-            T.record(ev[0], stream)
-        Q.qsa_indexer_prefill(iq, ik, wq, wk, ctx, lists, ws, cfg, stream=stream)
-        if ev:
-            T.record(ev[1], stream)
-        Q.qsa_sparse_prefill(q, k, v, o, lists, ctx, inp.scale, stream=stream)
-        if ev:
-            T.record(ev[2], stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # Timing events on every TIMING_EVERY-th step of the timed region only:
-    # each recorded event still costs the kernels after it ~2 us, which the
-    # path itself does not have.
-    sampled = list(range(0, args.steps, TIMING_EVERY))
-    evs = {i: [T.create() for _ in range(3)] for i in sampled}
+def timed_loops(step, steps, warmup, stream, torch, n_marks):
+    """Wall clock of `steps` calls of step() (no events), then a second loop
+    of `steps` calls with timing events at the n_marks points step() offers;
+    returns (wall seconds, [per-interval average ms])."""
+    for _ in range(warmup):
+        step(None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs.get(i))
+    for _ in range(steps):
+        step(None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    idx_ms = [T.elapsed_ms(a, b) for a, b, _ in evs.values()]
-    attn_ms = [T.elapsed_ms(b, c) for _, b, c in evs.values()]
+    T = HipTimingEvents()
+    evs = [[T.create() for _ in range(n_marks)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(lambda k, i=i: T.record(evs[i][k], stream))
+    torch.cuda.synchronize()
+    parts = [float(np.mean([T.elapsed_ms(e[k], e[k + 1]) for e in evs])) for k in range(n_marks - 1)]
     T.destroy_all()
+    return wall, parts
 
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def prefill_bench(wl, inp, args, Q, torch):
+    e = 2
+    stream = torch.cuda.current_stream()
+    q, k, v = dev(inp.q, inp.dtype), dev(inp.k, inp.dtype), dev(inp.v, inp.dtype)
+    ctx = dev(inp.ctx)
+    o = torch.empty_like(q)
+    with_indexer = inp.indices is None
+    if with_indexer:
+        icfg = inp.icfg
+        top_k = icfg.top_k
+        cfg = cfg_struct(Q, icfg)
+        iq, ik = dev(inp.idx_q, inp.dtype), dev(inp.idx_k, inp.dtype)
+        wq, wk = dev(inp.w_q), dev(inp.w_k)
+        lists = torch.empty((inp.B, inp.S, top_k), dtype=torch.int32, device="cuda")
+        ws = torch.empty(Q.qsa_indexer_prefill_workspace_bytes(cfg, inp.B, inp.S), dtype=torch.uint8,
+                         device="cuda")
+    else:
+        top_k = inp.top_k
+        lists = dev(inp.indices)
+
+    def step(mark):
+        if mark:
+            mark(0)
+        if with_indexer:
+            Q.qsa_indexer_prefill(iq, ik, wq, wk, ctx, lists, ws, cfg, stream=stream)
+        if mark:
+            mark(1)
+        Q.qsa_sparse_prefill(q, k, v, o, lists, ctx, inp.scale, stream=stream)
+        if mark:
+            mark(2)
+
+    wall, (idx_ms, attn_ms) = timed_loops(step, args.steps, args.warmup, stream, torch, 3)
     live = int(sum(min(int(c), inp.S) for c in inp.ctx))
     dead = inp.B * inp.S - live
-    n_entries = int((lists >= 0).sum().item())          # listed ids over all live rows
+    n_entries = int((lists >= 0).sum().item())  # listed ids over all live rows
     attn_bytes = (n_entries * inp.Hkv * 2 * inp.D * e + live * inp.Hq * inp.D * e * 2
-                  + live * icfg.top_k * 4 + dead * inp.Hq * inp.D * e)
-    attn_avg = float(np.mean(attn_ms)) * 1e-3
-    idx_avg = float(np.mean(idx_ms)) * 1e-3
-    achieved = attn_bytes / attn_avg / 1e9
-    # QK^T and PV over the listed keys, per query head: 2 * D + 2 * D flops per id
-    attn_flops = n_entries * inp.Hq * inp.D * 4
-    res = {
-        "inp": inp, "live": live, "wall": wall,
-        "ms_per_step": wall / args.steps * 1e3,
-        "indexer_ms": idx_avg * 1e3, "attention_ms": attn_avg * 1e3,
-        "attn_bytes": attn_bytes, "achieved_gbs": achieved, "n_entries": n_entries,
-        "attn_flops": attn_flops, "achieved_tflops": attn_flops / attn_avg / 1e12,
+                  + live * top_k * 4 + dead * inp.Hq * inp.D * e)
+    attn_flops = n_entries * inp.Hq * inp.D * 4  # QK^T and PV per query head: 4 D flops per listed id
+    attn_s = attn_ms * 1e-3
+    traffic = measured_traffic(wl)
+    attention = {
+        "kernel": "qsa_sparse_prefill (sparse_prefill_kernel list walk + sparse_prefill_tile_kernel)",
+        "bound": "mfma", "achieved": attn_flops / attn_s / 1e12, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": attn_flops / attn_s / 1e12 / MFMA_PEAK_TFLOPS, "traffic": traffic,
+        "algorithmic_flops_per_call": attn_flops, "algorithmic_bytes_per_call": attn_bytes,
+        "algorithmic_byte_rate_gbs": attn_bytes / attn_s / 1e9,
+        "hbm_counter_gbs": traffic / attn_s / 1e9 if traffic else None,
+        "hbm_counter_frac": traffic / attn_s / 1e9 / HBM_PEAK_GBS if traffic else None,
+        "ms_per_call": attn_ms,
     }
-    del q, k, v, iq, ik, o, lists, ws
+    res = {
+        "workload": __import__("qsa_synth").WORKLOADS[wl],
+        "value": live * args.steps / wall, "unit": "tokens/s",
+        "ms_per_step": wall / args.steps * 1e3, "steps": args.steps,
+        "dtype": inp.dtype, "batch": inp.B, "seq_len": inp.S, "live_tokens": live,
+        "num_q_heads": inp.Hq, "num_kv_heads": inp.Hkv, "head_dim": inp.D, "top_k": top_k,
+        "attention_ms": attn_ms, "attention": attention,
+    }
+    if with_indexer:
+        icfg = inp.icfg
+        r = icfg.compress_ratio
+        pairs = sum(sum((t + 1) // r for t in range(min(int(c), inp.S))) for c in inp.ctx)
+        score_flops = pairs * icfg.num_heads * icfg.head_dim * 2
+        res["indexer_ms"] = idx_ms
+        res["indexer"] = {"kernel": "qsa_indexer_prefill (prep, MFMA scoring, radix select + expand)",
+                          "bound": "mfma", "achieved": score_flops / (idx_ms * 1e-3) / 1e12,
+                          "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": score_flops / (idx_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+                          "algorithmic_flops_per_call": score_flops}
+    else:
+        res["note"] = "fixed lists, attention only; a few microseconds per call: launch-bound, roofline not meaningful"
+    del q, k, v, o, lists
     torch.cuda.empty_cache()
     return res
 
 
-def decode_bench(args, Q, syn, torch):
-    inp = syn.workload(DECODE_WORKLOAD)
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def decode_bench(inp, args, Q, torch):
     icfg = inp.icfg
     e = 2
+    stream = torch.cuda.current_stream()
     cfg = cfg_struct(Q, icfg)
     pool = dev(inp.pool, inp.dtype)
     pt, ctx = dev(inp.page_table), dev(inp.ctx)
@@ -199,49 +267,43 @@ def decode_bench(args, Q, syn, torch):
                      device="cuda")
     po = torch.empty(Q.qsa_sparse_decode_partial_o_elems(inp.B, inp.Hkv, inp.D), dtype=torch.float32, device="cuda")
     ps = torch.empty(Q.qsa_sparse_decode_partial_stats_elems(inp.B, inp.Hkv), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    T = HipTimingEvents()
 
-    def step(ev=None):
-        if ev:
-            T.record(ev[0], stream)
+    def step(mark):
+        if mark:
+            mark(0)
         Q.qsa_indexer_decode(iq, ik, wq, wk, pool, pt, ctx, lists, ws, cfg, inp.D, stream=stream)
-        if ev:
-            T.record(ev[1], stream)
+        if mark:
+            mark(1)
         Q.qsa_sparse_decode(q, o, pool, pt, lists, ctx, po, ps, inp.scale, head_dim=inp.D, stream=stream)
-        if ev:
-            T.record(ev[2], stream)
+        if mark:
+            mark(2)
 
-    steps = max(args.steps, 50)
-    for _ in range(max(args.warmup, 5)):
-        step()
-    torch.cuda.synchronize()
-    evs = [[T.create() for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    idx_ms = float(np.median([T.elapsed_ms(a, b) for a, b, _ in evs]))
-    attn_ms = float(np.median([T.elapsed_ms(b, c) for _, b, c in evs]))
-    T.destroy_all()
+    wall, (idx_ms, attn_ms) = timed_loops(step, args.steps, args.warmup, stream, torch, 3)
     n_entries = int((lists >= 0).sum().item())
     nblk = int(sum(int(c) // icfg.compress_ratio for c in inp.ctx))
     attn_bytes = n_entries * inp.Hkv * 2 * inp.D * e + inp.B * (inp.Hq * inp.D * e * 2 + inp.top_k * 4)
     idx_bytes = nblk * icfg.head_dim * e + inp.B * inp.top_k * 4
-    step_ms = idx_ms + attn_ms
+    step_s = wall / args.steps
     out = {
-        "workload": syn.WORKLOADS[DECODE_WORKLOAD],
-        "value": inp.B / (step_ms * 1e-3),
+        "workload": __import__("qsa_synth").WORKLOADS[DECODE_WORKLOAD],
+        "value": inp.B / step_s,
         "unit": "seqs/s",
-        "ms_per_step": step_ms,
-        "wall_ms_per_step": wall / steps * 1e3,
+        "ms_per_step": step_s * 1e3,
+        "steps": args.steps,
         "indexer_ms": idx_ms,
         "attention_ms": attn_ms,
-        "steps": steps,
         "algorithmic_bytes_per_step": attn_bytes + idx_bytes,
-        "hbm_frac_step": (attn_bytes + idx_bytes) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "attention_gbs": attn_bytes / (attn_ms * 1e-3) / 1e9,
+        "roofline": {"kernel": "one decode step (qsa_indexer_decode + qsa_sparse_decode)", "bound": "hbm",
+                     "achieved": (attn_bytes + idx_bytes) / step_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (attn_bytes + idx_bytes) / step_s / 1e9 / HBM_PEAK_GBS},
+        "attention": {"kernel": "qsa_sparse_decode", "bound": "hbm",
+                      "achieved": attn_bytes / (attn_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": attn_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "algorithmic_bytes_per_call": attn_bytes},
+        "indexer": {"kernel": "qsa_indexer_decode", "bound": "hbm",
+                    "achieved": idx_bytes / (idx_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": idx_bytes / (idx_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "algorithmic_bytes_per_call": idx_bytes},
         "splits": Q.qsa_sparse_decode_default_splits(inp.B, inp.Hkv, inp.top_k),
     }
     del pool
@@ -249,6 +311,9 @@ def decode_bench(args, Q, syn, torch):
     return out
 
 
+# ---------------------------------------------------------------------------
+# HBM counter figures
+# ---------------------------------------------------------------------------
 def kernel_code_sha256(path=None):
     """sha256 of the attention kernel source with its comments and blank
     space removed, so that the counter figures survive comment edits but
@@ -262,7 +327,7 @@ def kernel_code_sha256(path=None):
 
 
 def measured_traffic(wl):
-    """HBM bytes per sparse_prefill launch from the committed rocprofv3
+    """HBM bytes per qsa_sparse_prefill call from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary, if it was taken on this kernel code."""
     try:
         kv = {}
@@ -279,102 +344,175 @@ def measured_traffic(wl):
         return None
 
 
-def cpu_baseline(wl):
-    """The oracle, unchanged, on the same workload (single thread)."""
-    import qsa_synth as syn
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on every host core (forked workers, before the GPU
+# is touched, so no worker holds the device)
+# ---------------------------------------------------------------------------
+_CPU = {}
+
+
+def _cpu_prefill_chunk(rows):
     from threadpoolctl import threadpool_limits
 
     from oracle import qsa_oracle as O
-    inp = syn.workload(wl)
+    inp = _CPU["prefill"]
     icfg = inp.icfg
-    if wl == 2:
-        rows = None
-        n_rows = inp.B * inp.S
-        sample = "all 4096 rows of the workload (indexer + attention)"
-    else:
-        rng = np.random.default_rng(7)
-        rows = [(b, int(t)) for b in range(inp.B) for t in rng.integers(0, min(int(inp.ctx[b]), inp.S), 256)]
-        n_rows = len(rows)
-        sample = f"{n_rows} random live rows (indexer + attention), extrapolated per row"
     with threadpool_limits(1):
-        t0 = time.perf_counter()
         lists = O.indexer_prefill(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.ctx, icfg, inp.dtype, icfg.top_k,
                                   rows=rows)
-        if rows is not None:
-            full = np.full((inp.B, inp.S, icfg.top_k), -1, dtype=np.int32)
-            for r, l in lists.items():
-                full[r] = l
-            lists = full
         O.sparse_prefill(inp.q, inp.k, inp.v, lists, inp.ctx, inp.scale, inp.dtype, rows=rows)
+    return len(rows)
+
+
+def _cpu_decode_chunk(seqs):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import qsa_oracle as O
+    inp = _CPU["decode"]
+    with threadpool_limits(1):
+        _, lists = O.indexer_decode(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.pool, inp.page_table, inp.ctx,
+                                    inp.icfg, inp.D, inp.dtype, inp.top_k, seqs=seqs)
+        full = np.full((inp.B, 1, inp.top_k), -1, dtype=np.int32)
+        for b, l in lists.items():
+            full[b, 0] = l
+        O.sparse_decode(inp.q, inp.pool, inp.page_table, full, inp.ctx, inp.scale, inp.D, inp.dtype, seqs=seqs)
+    return len(seqs)
+
+
+def _pool_run(fn, chunks, workers):
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        pool.map(abs, range(workers))  # workers up before the clock starts
+        t0 = time.perf_counter()
+        n = sum(pool.map(fn, chunks, chunksize=1))
         dt = time.perf_counter() - t0
-    live_rows = n_rows if rows is not None else int(sum(min(int(c), inp.S) for c in inp.ctx))
-    return {"value": live_rows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds": dt, "cpu": platform.processor() or platform.machine()}
+    return n, dt
 
 
+def cpu_workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, MAX_CPU_WORKERS))
+
+
+def cpu_baseline_prefill(inp, workers):
+    rng = np.random.default_rng(7)
+    live = [(b, int(t)) for b in range(inp.B) for t in range(min(int(inp.ctx[b]), inp.S))]
+    pick = rng.choice(len(live), min(CPU_PREFILL_ROWS, len(live)), replace=False)
+    rows = [live[i] for i in np.sort(pick)]
+    chunks = [rows[i::workers] for i in range(workers)]
+    _CPU["prefill"] = inp
+    n, dt = _pool_run(_cpu_prefill_chunk, [c for c in chunks if c], workers)
+    _CPU.pop("prefill")
+    return {"value": n / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{n} live rows drawn uniformly from the workload (indexer + attention per row), "
+                      f"rate = rows / wall time of {workers} single-threaded worker processes",
+            "seconds": dt, "cpu": platform.processor() or platform.machine()}
+
+
+def cpu_baseline_decode(inp, workers):
+    seqs = list(range(min(CPU_DECODE_SEQS, inp.B))) * CPU_DECODE_REPS
+    chunks = [seqs[i::workers] for i in range(workers)]
+    _CPU["decode"] = inp
+    n, dt = _pool_run(_cpu_decode_chunk, [c for c in chunks if c], workers)
+    _CPU.pop("decode")
+    return {"value": n / dt, "unit": "seqs/s", "cores": min(workers, n), "kind": "oracle",
+            "sample": f"all {min(CPU_DECODE_SEQS, inp.B)} sequences of one decode step, {CPU_DECODE_REPS} times "
+                      f"(indexer decode + sparse decode), spread over single-threaded worker processes",
+            "seconds": dt, "cpu": platform.processor() or platform.machine()}
+
+
+# ---------------------------------------------------------------------------
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the QSA hot path is single-GPU work here "
               "(sharding is described, not built); rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    import qsa_synth as syn
+
+    run = sorted({int(x) for x in args.workloads.split(",") if x.strip()} | {args.headline})
+    inputs = {}
+
+    def inp_of(wl):
+        if wl not in inputs:
+            note(f"generating workload {wl}")
+            inputs[wl] = syn.workload(wl)
+        return inputs[wl]
+
+    cpu, cpu_dec = None, None
+    if not args.no_cpu_baseline:
+        workers = cpu_workers()
+        note(f"cpu baseline (oracle), prefill workload {args.headline}, {workers} workers")
+        cpu = cpu_baseline_prefill(inp_of(args.headline), workers)
+        if DECODE_WORKLOAD in run:
+            note(f"cpu baseline (oracle), decode workload {DECODE_WORKLOAD}")
+            cpu_dec = cpu_baseline_decode(inp_of(DECODE_WORKLOAD), workers)
+
     import torch
 
-    import qsa_synth as syn
     import top_indexed_sparse_qsa_amd as Q
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     Q.load()
-    print(f"# bench: prefill workload {args.workload}", file=sys.stderr, flush=True)
-    pf = prefill_bench(args, Q, syn, torch)
-    print(f"# bench: prefill {pf['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
-    dec = None
-    if not args.no_decode:
-        print("# bench: decode workload 4", file=sys.stderr, flush=True)
-        dec = decode_bench(args, Q, syn, torch)
-        print(f"# bench: decode {dec['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+    results = {}
+    order = [args.headline] + [w for w in run if w != args.headline]
+    for wl in order:
+        inp = inp_of(wl)
+        note(f"workload {wl}")
+        if wl == DECODE_WORKLOAD:
+            results[wl] = decode_bench(inp, args, Q, torch)
+        else:
+            results[wl] = prefill_bench(wl, inp, args, Q, torch)
+        note(f"workload {wl}: {results[wl]['ms_per_step']:.4f} ms/step")
+        inputs.pop(wl, None)
+    copy_gbs = None
+    n = 1 << 30
+    a = torch.empty(n // 2, dtype=torch.float16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 10 / (time.perf_counter() - t0) / 1e9
     if args.calib_copy:
-        n = 1 << 30
-        a = torch.empty(n // 2, dtype=torch.float16, device="cuda").fill_(1.0)
-        b = torch.empty_like(a)
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
-        del a, b
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("# bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(args.workload)
+    del a, b
 
-    inp = pf["inp"]
-    value = pf["live"] * args.steps / pf["wall"]
+    head = results[args.headline]
+    dec = results.get(DECODE_WORKLOAD)
+    if dec is not None:
+        dec["cpu_baseline"] = cpu_dec
     line = {
         "metric": METRIC,
-        "value": value,
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": pf["ms_per_step"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": inp.dtype,
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": syn.WORKLOADS[args.workload], "batch": inp.B, "seq_len": inp.S,
-                   "live_tokens": pf["live"], "num_q_heads": inp.Hq, "num_kv_heads": inp.Hkv,
-                   "head_dim": inp.D, "top_k": inp.icfg.top_k, "parallelism": "none"},
-        "parts_ms": {"indexer_prefill": pf["indexer_ms"], "sparse_prefill": pf["attention_ms"],
-                     "timed_steps": len(range(0, args.steps, TIMING_EVERY))},
-        "roofline": {"bound": "hbm", "kernel": "qsa_sparse_prefill: sparse_prefill_tile_kernel + sparse_prefill_kernel",
-                     "achieved": pf["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": pf["achieved_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
-                     "algorithmic_bytes_per_call": pf["attn_bytes"],
-                     "mfma": {"achieved": pf["achieved_tflops"], "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": pf["achieved_tflops"] / MFMA_PEAK_TFLOPS,
-                              "algorithmic_flops_per_call": pf["attn_flops"]}},
+        "config": {"workload": head["workload"], "batch": head["batch"], "seq_len": head["seq_len"],
+                   "live_tokens": head["live_tokens"], "num_q_heads": head["num_q_heads"],
+                   "num_kv_heads": head["num_kv_heads"], "head_dim": head["head_dim"], "top_k": head["top_k"],
+                   "parallelism": "none"},
+        "parts_ms": {"indexer_prefill": head.get("indexer_ms"), "sparse_prefill": head["attention_ms"]},
+        "roofline": head["attention"],
         "cpu_baseline": cpu,
+        "workloads": {str(w): r for w, r in results.items() if w not in (args.headline, DECODE_WORKLOAD)},
         "decode": dec,
+        "hbm_copy_gbs": copy_gbs,
     }
     print(json.dumps(line), flush=True)
 
