@@ -92,7 +92,9 @@ typedef struct {
  * of 32 slots (slots 32c .. 32c+31) that holds no usable id ends the row's
  * list: later slots are not read.
  * Supported: head_dim 64 or 128; num_q_heads a multiple of num_kv_heads with
- * ratio 1..16; top_k >= 1. */
+ * ratio 1..16; top_k >= 1; seq_len < 2^24 and num_kv_heads * head_dim * 2 <
+ * 2^24 bytes (token offsets use a 24-bit multiply), and one sequence's K (or
+ * V) under 4 GiB; QSA_ERR_UNSUPPORTED otherwise. */
 typedef struct {
   const void *q;
   const void *k;
@@ -121,13 +123,17 @@ typedef struct {
  * context_lengths: int32 [batch], the TOTAL length including the new token.
  * The list is cut into num_splits contiguous runs of 32-slot chunks (0 lets
  * the library choose; otherwise 1..QSA_MAX_SPLITS), each run one online
- * softmax.  Splits are merged in split order -- up to four inside a
- * workgroup through LDS, the rest by a second small kernel -- so the result
- * never depends on timing.  partial_o (fp32,
- * qsa_sparse_decode_partial_o_elems()) and partial_stats (fp32,
- * qsa_sparse_decode_partial_stats_elems()) hold the workgroup partials
- * between the two kernels; they need no initial contents, and calls that
- * overlap on the GPU must not share them.
+ * softmax.  Up to eight splits of one (sequence, KV head) share a workgroup
+ * and are merged there in split order, so the library's own plan
+ * (num_splits = 0, never more than eight splits -- the pages' kMaxSplits)
+ * is a single launch that needs no workspace: partial_o and partial_stats
+ * may then be NULL.  An explicit num_splits above eight spreads a (sequence,
+ * KV head) over two workgroups whose partials (fp32, partial_o:
+ * qsa_sparse_decode_partial_o_elems(), partial_stats:
+ * qsa_sparse_decode_partial_stats_elems()) a second small kernel merges, in
+ * a fixed order.  Either way the result never depends on timing.  The
+ * partials need no initial contents; calls that overlap on the GPU must not
+ * share them.
  * Supported: as prefill, plus pool_head_dim >= head_dim, a multiple of 8,
  * and max_pages_per_seq <= 4096. */
 typedef struct {
@@ -227,7 +233,9 @@ typedef struct {
  * pool is left bit-unchanged.  idx_q: [batch, 1, num_heads, hd]; idx_k:
  * [batch, 1, hd]; indices out: int32 [batch, 1, top_k].  Page table and
  * pool as for qsa_sparse_decode.  workspace: at least
- * qsa_indexer_decode_workspace_bytes() bytes.
+ * qsa_indexer_decode_workspace_bytes() bytes (the fp32 score row of each
+ * sequence); it needs no initial contents, and calls that overlap on the
+ * GPU must not share it.  B1 and B2 run as one kernel, B3 as a second.
  * Supported: pool_head_dim >= head_dim + cfg.head_dim;
  * max_pages_per_seq*128/ratio <= QSA_MAX_BLOCKS, and batch times that
  * <= INT32_MAX/2. */

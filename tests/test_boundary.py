@@ -55,17 +55,19 @@ def test_workspace_sizes_follow_layout():
     st = (g + 15) // 16 * 16
     assert Q.qsa_indexer_prefill_workspace_bytes(cfg, B, S) == \
         a(B * S * 4 * 128 * 4) + a(B * g * 128 * 2) + a(B * S * st * 4)
-    assert Q.qsa_indexer_decode_workspace_bytes(cfg, 32, 512) == a(32 * 4 * 128 * 4) + a(32 * 16384 * 4)
-    # workgroup partials: at most QSA_MAX_SPLITS / 4 per (sequence, KV head)
-    assert Q.qsa_sparse_decode_partial_o_elems(32, 4, 128) == 32 * 4 * 4 * 16 * 128
-    assert Q.qsa_sparse_decode_partial_stats_elems(32, 4) == 32 * 4 * 4 * 2 * 16
+    # decode: one fp32 score row per sequence, stride 128 * max_pages / ratio rounded to 16
+    assert Q.qsa_indexer_decode_workspace_bytes(cfg, 32, 512) == a(32 * 16384 * 4)
+    assert Q.qsa_indexer_decode_workspace_bytes(cfg, 3, 33) == a(3 * 1056 * 4)
+    # workgroup partials: at most QSA_MAX_SPLITS / 8 per (sequence, KV head)
+    assert Q.qsa_sparse_decode_partial_o_elems(32, 4, 128) == 32 * 4 * 2 * 16 * 128
+    assert Q.qsa_sparse_decode_partial_stats_elems(32, 4) == 32 * 4 * 2 * 2 * 16
     assert Q.qsa_indexer_prefill_workspace_bytes(Q.indexer_config(head_dim=64), 1, 10) == 0
     assert Q.qsa_sparse_decode_partial_o_elems(0, 4, 128) == 0
 
 
 def test_default_split_plan():
     assert Q.qsa_sparse_decode_default_splits(32, 4, 2051) == 8      # ~1024 waves
-    assert Q.qsa_sparse_decode_default_splits(8, 4, 2051) == 16
+    assert Q.qsa_sparse_decode_default_splits(8, 4, 2051) == 8       # one 8-wave workgroup per pair at most
     assert Q.qsa_sparse_decode_default_splits(1, 1, 40) == 2       # never more splits than 32-slot chunks
     assert Q.qsa_sparse_decode_default_splits(4096, 8, 2051) == 1
     assert Q.qsa_sparse_decode_default_splits(0, 4, 2051) == 0
@@ -116,13 +118,17 @@ def _idecode(**kw):
     (dict(num_q_heads=7), SHAPE), (dict(num_q_heads=34), UNSUP), (dict(head_dim=96), UNSUP),
     (dict(num_kv_heads=0), SHAPE), (dict(q=FAKE + 8), SHAPE), (dict(attention_scale=float("inf")), SHAPE),
     (dict(attention_scale=0.0), SHAPE), (dict(attention_scale=-0.125), SHAPE), (dict(attention_scale=float("nan")), SHAPE),
+    # 24-bit token-row multiply: ids and row bytes below 2^24
+    (dict(seq_len=1 << 24, num_q_heads=1, num_kv_heads=1, head_dim=64), UNSUP),
+    (dict(num_q_heads=1 << 16, num_kv_heads=1 << 16, head_dim=128, seq_len=1), UNSUP),
 ])
 def test_sparse_prefill_rejects(no_gpu, kw, status):
     assert _prefill(**kw) == status
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(partial_o=None), NULLP), (dict(page_table=None), NULLP), (dict(partial_stats=None), NULLP),
+    (dict(partial_o=None, num_splits=9), NULLP), (dict(page_table=None), NULLP),
+    (dict(partial_stats=None, num_splits=16), NULLP), (dict(partial_o=FAKE + 4, num_splits=12), SHAPE),
     (dict(dtype=-1), UNSUP), (dict(batch=0), SHAPE), (dict(num_flat_pages=0), SHAPE),
     (dict(pool_head_dim=120), SHAPE), (dict(pool_head_dim=130), SHAPE), (dict(num_splits=17), SHAPE),
     (dict(num_splits=-1), SHAPE), (dict(max_pages_per_seq=5000), UNSUP), (dict(num_q_heads=33), SHAPE),
@@ -130,6 +136,14 @@ def test_sparse_prefill_rejects(no_gpu, kw, status):
 ])
 def test_sparse_decode_rejects(no_gpu, kw, status):
     assert _decode(**kw) == status
+
+
+def test_sparse_decode_partials_only_needed_past_one_workgroup(no_gpu):
+    """With the default plan (at most 8 splits, one workgroup per sequence and
+    KV head) the partial buffers are unused and may be NULL; validation of
+    the remaining arguments still runs first."""
+    assert _decode(partial_o=None, partial_stats=None, num_splits=8, batch=0) == SHAPE
+    assert _decode(partial_o=None, partial_stats=None, num_splits=0, head_dim=96) == UNSUP
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -566,6 +566,41 @@ def test_decode_small(case):
     decode_parity(inp, "decode small", splits=(0, 1, 2, 3, 4, 5, 8, 13, 16))
 
 
+def test_sparse_decode_largest_page_table():
+    """max_pages_per_seq = 4096, the largest the attention boundary accepts:
+    the page-table copy in LDS takes the workgroup past 64 KB of LDS.  Lists
+    come from the oracle's decode indexer (the indexer itself is limited to
+    QSA_MAX_BLOCKS blocks, i.e. 1024 pages at ratio 4)."""
+    inp = syn.make_decode(13, ctx=[300, 2052, 9001], B=3, Hq=16, Hkv=2, D=128, dtype="bf16", max_pages=4096)
+    _, ref_lists = O.indexer_decode(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.pool, inp.page_table, inp.ctx,
+                                    inp.icfg, inp.D, inp.dtype, inp.top_k)
+    pool_dev = TL.dev(inp.pool, inp.dtype)
+    ref_o = O.sparse_decode(inp.q, inp.pool, inp.page_table, ref_lists, inp.ctx, inp.scale, inp.D, inp.dtype)
+    ws = DecodeWs(inp)
+    for ns in (0, 3, 16):
+        o = gpu_sparse_decode(inp, pool_dev, TL.dev(ref_lists), ws, ns)
+        got = TL.host_f64(o, inp.dtype)[:, 0]
+        for b in range(inp.B):
+            TL.check_attention(got[b], ref_o[b], inp.dtype, f"max pages splits={ns} b={b}")
+
+
+def test_decode_default_plan_needs_no_partials():
+    """The library's own split plan is one workgroup per (sequence, KV head):
+    NULL partial buffers are accepted and the output equals the one computed
+    with them, bit for bit."""
+    inp = syn.make_decode(12, ctx=[2051, 2052, 9000, 3], B=4, Hq=32, Hkv=4, D=128, dtype="fp16", max_pages=80)
+    pool_dev = TL.dev(inp.pool, inp.dtype)
+    lists_t = gpu_indexer_decode(inp, pool_dev)
+    ws = DecodeWs(inp)
+    ref = gpu_sparse_decode(inp, pool_dev, lists_t, ws, 0)
+    q = TL.dev(inp.q, inp.dtype)
+    o = torch.full_like(q, float("nan"))
+    Q.qsa_sparse_decode(q, o, pool_dev, TL.dev(inp.page_table), lists_t, TL.dev(inp.ctx), None, None, inp.scale,
+                        head_dim=inp.D)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+
+
 def test_decode_workload4_full_size_and_determinism():
     TL.log("decode workload 4: generating")
     inp = syn.workload(4)

@@ -59,28 +59,29 @@ PrefillWs prefill_ws(const qsa_indexer_config &c, int32_t B, int32_t S) {
   return w;
 }
 
+// Decode indexer workspace: fp32 score rows, one per sequence.
 struct DecodeWs {
-  size_t qhat, scores, total;
+  size_t scores, total;
   int stride;
 };
 DecodeWs decode_ws(const qsa_indexer_config &c, int32_t B, int32_t max_pages) {
   DecodeWs w{};
   const size_t gmax = (size_t)max_pages * QSA_PAGE_TOKENS / c.compress_ratio;
   w.stride = (int)round16(gmax > 0 ? gmax : 1);
-  w.qhat = 0;
-  w.scores = align_up((size_t)B * c.num_heads * c.head_dim * 4);
-  w.total = w.scores + align_up((size_t)B * w.stride * 4);
+  w.scores = 0;
+  w.total = align_up((size_t)B * w.stride * 4);
   return w;
 }
 
 int default_splits(int32_t B, int32_t hkv, int32_t top_k) {
   const int chunks = (top_k + 31) / 32;
   const int pairs = B * hkv;
-  // aim for ~1024 waves: at 32 sequences x 4 KV heads, 8 splits measured
-  // 32.6 us per call against 36.9 us for 16 (fewer partials to merge, and the
-  // gathers already saturate the pool reads)
+  // aim for ~1024 waves, at most one workgroup of kDecWaves splits per
+  // (sequence, KV head) so that the call is a single launch: at 32 sequences
+  // x 4 KV heads, 8 splits in one 8-wave workgroup measured 27.6 us per call
+  // against 29.1 us as two 4-wave workgroups plus a merge launch
   int want = (1024 + pairs - 1) / pairs;
-  if (want > QSA_MAX_SPLITS) want = QSA_MAX_SPLITS;
+  if (want > qsa::kDecWaves) want = qsa::kDecWaves;
   if (want > chunks) want = chunks;
   if (want < 1) want = 1;
   return want;
@@ -136,8 +137,10 @@ qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p) {
   if (qsa_status st = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim)) return st;
   if (!all_aligned16(p->q, p->k, p->v, p->o)) return QSA_ERR_BAD_SHAPE;
   if ((int64_t)p->batch * p->seq_len * p->num_kv_heads > (int64_t)INT32_MAX - 4) return QSA_ERR_UNSUPPORTED;
-  // one sequence's K (or V) is addressed with 32-bit byte offsets
+  // one sequence's K (or V) is addressed with 32-bit byte offsets, a token's
+  // row as a 24-bit multiply of its id by the row bytes
   if ((int64_t)p->seq_len * p->num_kv_heads * p->head_dim * 2 >= ((int64_t)1 << 32)) return QSA_ERR_UNSUPPORTED;
+  if (p->seq_len >= (1 << 24) || (int64_t)p->num_kv_heads * p->head_dim * 2 >= (1 << 24)) return QSA_ERR_UNSUPPORTED;
   if (!isfinite(p->attention_scale) || !(p->attention_scale > 0.f)) return QSA_ERR_BAD_SHAPE;
   qsa::PrefillAttnArgs a{};
   a.q = static_cast<const uint16_t *>(p->q);
@@ -157,14 +160,13 @@ qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p) {
 }
 
 qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
-  if (!p || !p->q || !p->o || !p->kv_pool || !p->page_table || !p->indices || !p->context_lengths ||
-      !p->partial_o || !p->partial_stats)
+  if (!p || !p->q || !p->o || !p->kv_pool || !p->page_table || !p->indices || !p->context_lengths)
     return QSA_ERR_NULL_POINTER;
   if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
   if (p->batch < 1 || p->top_k < 1 || p->num_flat_pages < 1 || p->max_pages_per_seq < 1) return QSA_ERR_BAD_SHAPE;
   if (qsa_status st = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim)) return st;
   if (p->pool_head_dim < p->head_dim || (p->pool_head_dim % 8) != 0) return QSA_ERR_BAD_SHAPE;
-  if (!all_aligned16(p->q, p->o, p->kv_pool, p->partial_o)) return QSA_ERR_BAD_SHAPE;
+  if (!all_aligned16(p->q, p->o, p->kv_pool)) return QSA_ERR_BAD_SHAPE;
   if (p->max_pages_per_seq > 4096) return QSA_ERR_UNSUPPORTED;
   if (p->num_splits < 0 || p->num_splits > QSA_MAX_SPLITS) return QSA_ERR_BAD_SHAPE;
   if ((int64_t)p->batch * p->num_kv_heads * QSA_MAX_SPLITS > (int64_t)INT32_MAX) return QSA_ERR_UNSUPPORTED;
@@ -173,8 +175,12 @@ qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
   const int chunks = (p->top_k + 31) / 32;
   const int per = (chunks + splits - 1) / splits;
   splits = (chunks + per - 1) / per;  // drop splits that would get no slots
-  const int wpg = splits < 4 ? splits : 4;
+  const int wpg = splits < qsa::kDecWaves ? splits : qsa::kDecWaves;
   const int ngroups = (splits + wpg - 1) / wpg;
+  // more than one workgroup per (sequence, KV head): their partials meet in
+  // the caller's buffers
+  if (ngroups > 1 && (!p->partial_o || !p->partial_stats)) return QSA_ERR_NULL_POINTER;
+  if (ngroups > 1 && !aligned16(p->partial_o)) return QSA_ERR_BAD_SHAPE;
   qsa::DecodeAttnArgs a{};
   a.q = static_cast<const uint16_t *>(p->q);
   a.o = static_cast<uint16_t *>(p->o);
@@ -308,46 +314,30 @@ qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
   const int dt = (int)p->dtype;
   const int gmax = p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio;
 
-  qsa::IdxDecPrepArgs pa{};
-  pa.idx_q = static_cast<const uint16_t *>(p->idx_q);
-  pa.idx_k = static_cast<const uint16_t *>(p->idx_k);
-  pa.wq = p->q_norm_w;
-  pa.wk = p->k_norm_w;
-  pa.pool = static_cast<uint16_t *>(p->kv_pool);
-  pa.pt = p->page_table;
-  pa.ctx = p->context_lengths;
-  pa.qhat = reinterpret_cast<float *>(ws + w.qhat);
-  pa.B = p->batch;
-  pa.Hi = p->cfg.num_heads;
-  pa.hd = p->cfg.head_dim;
-  pa.rot = p->cfg.rot_dim;
-  pa.ratio = p->cfg.compress_ratio;
-  pa.Hkv = p->num_kv_heads;
-  pa.D = p->head_dim;
-  pa.PHD = p->pool_head_dim;
-  pa.num_flat_pages = p->num_flat_pages;
-  pa.max_pages = p->max_pages_per_seq;
-  pa.theta = (double)p->cfg.rope_theta;
-  pa.eps = (double)p->cfg.rms_eps;
-  pa.dt = dt;
-  if (qsa::launch_idx_dec_prep(pa, s) != hipSuccess) return QSA_ERR_LAUNCH;
-
   qsa::IdxDecScoreArgs sa{};
-  sa.qhat = pa.qhat;
-  sa.pool = pa.pool;
+  sa.idx_q = static_cast<const uint16_t *>(p->idx_q);
+  sa.idx_k = static_cast<const uint16_t *>(p->idx_k);
+  sa.wq = p->q_norm_w;
+  sa.wk = p->k_norm_w;
+  sa.pool = static_cast<uint16_t *>(p->kv_pool);
   sa.pt = p->page_table;
   sa.ctx = p->context_lengths;
   sa.scores = reinterpret_cast<float *>(ws + w.scores);
   sa.B = p->batch;
   sa.Hi = p->cfg.num_heads;
+  sa.hd = p->cfg.head_dim;
+  sa.rot = p->cfg.rot_dim;
+  sa.ratio = p->cfg.compress_ratio;
   sa.Hkv = p->num_kv_heads;
   sa.D = p->head_dim;
   sa.PHD = p->pool_head_dim;
   sa.num_flat_pages = p->num_flat_pages;
   sa.max_pages = p->max_pages_per_seq;
-  sa.ratio = p->cfg.compress_ratio;
   sa.stride = w.stride;
-  sa.waves_per_seq = (gmax + 16 * qsa::kScoreTilesPerWave - 1) / (16 * qsa::kScoreTilesPerWave);
+  sa.gmax = gmax;
+  sa.theta = (double)p->cfg.rope_theta;
+  sa.eps = (double)p->cfg.rms_eps;
+  sa.dt = dt;
   if (qsa::launch_idx_dec_score(sa, dt, s) != hipSuccess) return QSA_ERR_LAUNCH;
 
   qsa::IdxSelectArgs xa{};

@@ -818,98 +818,56 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode B1: queries at p = ctx-1 and the tail update.  One workgroup per sequence.
+// Decode B1 + B2 in one kernel.  A workgroup of four waves takes 128 blocks
+// (kDecScoreTiles tiles of 16 per wave) of one sequence, position
+// p = ctx - 1:
+//   * every wave issues the kbar tail loads of its blocks (V-row tails of
+//     tokens ratio*g) first, so that they are in flight during the rest;
+//   * wave h < Hi prepares query head h at p (fp64, one rounding to fp32)
+//     into LDS -- each workgroup does this for itself, which costs less
+//     than a launch of its own;
+//   * B1's pool update: when the context length closes a block (ctx mod
+//     ratio == 0), the workgroup holding that block pools it from the raw
+//     K-row tails of its first ratio-1 tokens plus the new key, stores kbar
+//     in the V-row tail of its first token and scores with that value (the
+//     tail it loaded is the stale one); otherwise the first workgroup of the
+//     sequence stores the new raw key in token p's K-row tail;
+//   * the MFMA scoring: A = kbar rows (rows = blocks), B = query pieces
+//     (columns = heads), the relus of the heads summed across lanes.
+// Nothing else reads or writes the tails this step touches.
 // ---------------------------------------------------------------------------
+constexpr int kDecScoreWaves = 4;
 
-// Wave h < Hi prepares query head h; wave Hi updates the pool tail, so the
-// query and key chains run side by side.
-__global__ __launch_bounds__(320) void idx_dec_prep_kernel(IdxDecPrepArgs a) {
-  const double *s_freq = a.freq;
-  const int b = blockIdx.x, lane = lane_id();
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ctx = min(a.ctx[b], a.max_pages * 128);
-  if (ctx <= 0) return;
-  const int p = ctx - 1;
-  double o0, o1;
-  if (wv < a.Hi) {
-    const Rope2 r = rope_at((double)p, s_freq, a.rot);
-    const size_t off = ((size_t)b * a.Hi + wv) * 128;
-    norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
-               (double)a.wq[lane], (double)a.wq[lane + 64], a.eps, a.rot, r, o0, o1);
-    a.qhat[off + lane] = (float)o0;
-    a.qhat[off + 64 + lane] = (float)o1;
-    return;
-  }
-  if (wv != a.Hi) return;
-  const int32_t *ptk = a.pt + (size_t)b * 2 * a.max_pages;
-  const int32_t *ptv = ptk + a.max_pages;
-  const uint16_t knew0 = a.idx_k[(size_t)b * 128 + lane], knew1 = a.idx_k[(size_t)b * 128 + 64 + lane];
-  if (ctx % a.ratio != 0) {
-    const long long o = pool_row_off(ptk, p, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
-    if (o >= 0) {
-      a.pool[o + a.D + lane] = knew0;
-      a.pool[o + a.D + 64 + lane] = knew1;
-    }
-    return;
-  }
-  const int g = ctx / a.ratio - 1;
-  const int base = a.ratio * g;
-  double m0 = 0.0, m1 = 0.0;
-  bool ok = true;
-  for (int j = 0; j < a.ratio - 1; ++j) {
-    const long long o = pool_row_off(ptk, base + j, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
-    ok = ok && o >= 0;
-    if (o >= 0) {
-      m0 += bits_to_f64(a.pool[o + a.D + lane], a.dt);
-      m1 += bits_to_f64(a.pool[o + a.D + 64 + lane], a.dt);
-    }
-  }
-  m0 += bits_to_f64(knew0, a.dt);
-  m1 += bits_to_f64(knew1, a.dt);
-  m0 /= (double)a.ratio;
-  m1 /= (double)a.ratio;
-  const Rope2 r = rope_at((double)base, s_freq, a.rot);
-  norm_rope2(m0, m1, (double)a.wk[lane], (double)a.wk[lane + 64], a.eps, a.rot, r, o0, o1);
-  const long long ov = pool_row_off(ptv, base, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
-  if (ok && ov >= 0) {
-    a.pool[ov + a.D + lane] = (uint16_t)f64_to_bits(o0, a.dt);
-    a.pool[ov + a.D + 64 + lane] = (uint16_t)f64_to_bits(o1, a.dt);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Decode B2: scores of blocks g < ctx/ratio from the V-row tails.  Each wave
-// takes kScoreTilesPerWave tiles of 16 blocks and issues all their tail
-// loads before the first MFMA.  A = kbar (rows = blocks), B = query pieces
-// (columns = heads); the relus of the heads are summed across lanes.
-// ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(256) void idx_dec_score_kernel(IdxDecScoreArgs a) {
   constexpr int NP = QSplit<DT>::NP;
   constexpr int TPW = kScoreTilesPerWave;
+  __shared__ __align__(16) float s_q[4][128];
+  __shared__ __align__(16) uint16_t s_kb[128];
+  const double *s_freq = a.freq;
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= a.B * a.waves_per_seq) return;
-  const int b = item / a.waves_per_seq, chunk = item % a.waves_per_seq;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.x / a.wg_per_seq, wg = blockIdx.x % a.wg_per_seq;
   const int ctx = min(a.ctx[b], a.max_pages * 128);
-  const int nc = ctx > 0 ? ctx / a.ratio : 0;
-  const int g_begin = chunk * TPW * 16;
-  if (g_begin >= nc) return;
-
-  u32x4 qb[NP][4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    float x[8];
-    if (r16 < a.Hi) load8f(x, a.qhat + ((size_t)b * a.Hi + r16) * 128 + 32 * ks + 8 * q4);
-    else
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
-    u32x4 pieces[NP];
-    split8<DT>(x, pieces);
-#pragma unroll
-    for (int p = 0; p < NP; ++p) qb[p][ks] = pieces[p];
+  if (ctx <= 0) return;
+  const int p = ctx - 1;
+  const int nc = ctx / a.ratio;
+  const int32_t *ptk = a.pt + (size_t)b * 2 * a.max_pages;
+  const int32_t *ptv = ptk + a.max_pages;
+  const bool closes = ctx % a.ratio == 0;
+  if (wg == 0 && !closes && wv == kDecScoreWaves - 1) {
+    // the new token's block stays open: its raw key goes to its K-row tail
+    const long long o = pool_row_off(ptk, p, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
+    if (o >= 0) {
+      a.pool[o + a.D + lane] = a.idx_k[(size_t)b * 128 + lane];
+      a.pool[o + a.D + 64 + lane] = a.idx_k[(size_t)b * 128 + 64 + lane];
+    }
   }
-  const int32_t *ptv = a.pt + (size_t)b * 2 * a.max_pages + a.max_pages;
+  const int wg_begin = wg * kDecScoreWaves * TPW * 16;
+  if (wg_begin >= nc) return;  // uniform over the workgroup
+  const int g_begin = wg_begin + wv * TPW * 16;
+
+  // kbar tail loads of this wave's blocks, issued before anything else
   u32x4 kb[TPW][4];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
@@ -920,6 +878,72 @@ __global__ __launch_bounds__(256) void idx_dec_score_kernel(IdxDecScoreArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kb[tt][ks] = ld16(src + 32 * ks);
   }
+
+  // query head wv at position p
+  if (wv < a.Hi) {
+    const Rope2 r = rope_at((double)p, s_freq, a.rot);
+    const size_t off = ((size_t)b * a.Hi + wv) * 128;
+    double o0, o1;
+    norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
+               (double)a.wq[lane], (double)a.wq[lane + 64], a.eps, a.rot, r, o0, o1);
+    s_q[wv][lane] = (float)o0;
+    s_q[wv][lane + 64] = (float)o1;
+  }
+  // the block this step completes, when this workgroup holds it
+  const int g_new = nc - 1;
+  const bool pool_new = closes && g_new >= wg_begin && g_new < wg_begin + kDecScoreWaves * TPW * 16;
+  if (pool_new && wv == (g_new - wg_begin) / (TPW * 16)) {
+    const int base = a.ratio * g_new;
+    double m0 = 0.0, m1 = 0.0;
+    bool ok = true;
+    for (int j = 0; j < a.ratio - 1; ++j) {
+      const long long o = pool_row_off(ptk, base + j, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
+      ok = ok && o >= 0;
+      if (o >= 0) {
+        m0 += bits_to_f64(a.pool[o + a.D + lane], a.dt);
+        m1 += bits_to_f64(a.pool[o + a.D + 64 + lane], a.dt);
+      }
+    }
+    m0 += bits_to_f64(a.idx_k[(size_t)b * 128 + lane], a.dt);
+    m1 += bits_to_f64(a.idx_k[(size_t)b * 128 + 64 + lane], a.dt);
+    m0 /= (double)a.ratio;
+    m1 /= (double)a.ratio;
+    const Rope2 r = rope_at((double)base, s_freq, a.rot);
+    double o0, o1;
+    norm_rope2(m0, m1, (double)a.wk[lane], (double)a.wk[lane + 64], a.eps, a.rot, r, o0, o1);
+    const uint16_t k0 = (uint16_t)f64_to_bits(o0, a.dt), k1 = (uint16_t)f64_to_bits(o1, a.dt);
+    s_kb[lane] = k0;
+    s_kb[lane + 64] = k1;
+    const long long ov = pool_row_off(ptv, base, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
+    if (ok && ov >= 0) {
+      a.pool[ov + a.D + lane] = k0;
+      a.pool[ov + a.D + 64 + lane] = k1;
+    }
+  }
+  __syncthreads();  // queries (and the new kbar) are in LDS
+  if (g_begin >= nc) return;
+  if (pool_new) {
+    // the lanes that hold block g_new score it with the value just pooled
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+      if (g_begin + tt * 16 + r16 == g_new)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[tt][ks] = *reinterpret_cast<const u32x4 *>(&s_kb[32 * ks + 8 * q4]);
+  }
+
+  u32x4 qb[NP][4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    float x[8];
+    if (r16 < a.Hi) load8f(x, &s_q[r16][32 * ks + 8 * q4]);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    u32x4 pieces[NP];
+    split8<DT>(x, pieces);
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) qb[pp][ks] = pieces[pp];
+  }
   float *srow = a.scores + (size_t)b * a.stride;
   f32x4 accs[TPW][2];
 #pragma unroll
@@ -927,20 +951,20 @@ __global__ __launch_bounds__(256) void idx_dec_score_kernel(IdxDecScoreArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt)
-        accs[tt][ks & 1] = mfma16x16x32<DT>(kb[tt][ks], qb[p][ks], accs[tt][ks & 1]);
+        accs[tt][ks & 1] = mfma16x16x32<DT>(kb[tt][ks], qb[pp][ks], accs[tt][ks & 1]);
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const f32x4 acc = accs[tt][0] + accs[tt][1];
     float v[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      float s = fmaxf(acc[rr], 0.f);
-      s += shfl_xor_f(s, 1);
-      s += shfl_xor_f(s, 2);
-      v[rr] = s;
+      float sc = fmaxf(acc[rr], 0.f);
+      sc += shfl_xor_f(sc, 1);
+      sc += shfl_xor_f(sc, 2);
+      v[rr] = sc;
     }
     const int g4 = g_begin + tt * 16 + 4 * q4;
     if (r16 == 0 && g4 < nc) {
@@ -1070,16 +1094,13 @@ hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_idx_dec_prep(const IdxDecPrepArgs &a_in, hipStream_t s) {
-  IdxDecPrepArgs a = a_in;
+hipError_t launch_idx_dec_score(const IdxDecScoreArgs &a_in, int dt, hipStream_t s) {
+  IdxDecScoreArgs a = a_in;
   fill_freq(a.freq, a.rot, a.theta);
-  hipLaunchKernelGGL(idx_dec_prep_kernel, dim3((unsigned)a.B), dim3(64 * (a.Hi + 1)), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_idx_dec_score(const IdxDecScoreArgs &a, int dt, hipStream_t s) {
-  const long long waves = (long long)a.B * a.waves_per_seq;
-  const unsigned grid = (unsigned)((waves + 3) / 4);
+  const int per_wg = kDecScoreWaves * kScoreTilesPerWave * 16;
+  a.wg_per_seq = (a.gmax + per_wg - 1) / per_wg;
+  if (a.wg_per_seq < 1) a.wg_per_seq = 1;  // the first workgroup also writes the open block's raw tail
+  const unsigned grid = (unsigned)((long long)a.B * a.wg_per_seq);
   if (dt == DT_F16) hipLaunchKernelGGL(idx_dec_score_kernel<DT_F16>, dim3(grid), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(idx_dec_score_kernel<DT_BF16>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();

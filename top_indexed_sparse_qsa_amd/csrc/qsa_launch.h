@@ -36,7 +36,13 @@ struct DecodeAttnArgs {
   float sl2;
 };
 
-constexpr int kDecMaxGroups = 4;  // QSA_MAX_SPLITS / waves per workgroup
+// Decode: waves (splits) per workgroup, merged in LDS; splits beyond that
+// go to further workgroups whose partials a second kernel merges.
+#ifndef QSA_DEC_WAVES
+#define QSA_DEC_WAVES 8
+#endif
+constexpr int kDecWaves = QSA_DEC_WAVES;
+constexpr int kDecMaxGroups = (16 + kDecWaves - 1) / kDecWaves;  // QSA_MAX_SPLITS / waves per workgroup
 
 // Indexer: query prep + block pooling for prefill.
 struct IdxPrepArgs {
@@ -83,25 +89,20 @@ struct IdxSelectArgs {
   int row0, nrows;     // prefill: this launch covers rows [row0, row0 + nrows) (set by the launcher)
 };
 
-struct IdxDecPrepArgs {
+// Indexer decode B1 + B2 (one kernel): query prep, the pool-tail update and
+// the block scores of one step.
+struct IdxDecScoreArgs {
   const uint16_t *idx_q, *idx_k;
   const float *wq, *wk;
   uint16_t *pool;
   const int32_t *pt, *ctx;
-  float *qhat;         // [B,Hi,hd]
-  int B, Hi, hd, rot, ratio, Hkv, D, PHD, num_flat_pages, max_pages;
+  float *scores;       // [B,stride]
+  int B, Hi, hd, rot, ratio, Hkv, D, PHD, num_flat_pages, max_pages, stride;
+  int gmax;            // blocks one sequence may hold (max_pages * 128 / ratio)
+  int wg_per_seq;      // set by the launcher
   double theta, eps;
   int dt;
-  double freq[64];  // RoPE frequencies theta^(-2i/rot), i < rot/2 (set by the launcher)
-};
-
-struct IdxDecScoreArgs {
-  const float *qhat;
-  const uint16_t *pool;
-  const int32_t *pt, *ctx;
-  float *scores;       // [B,stride]
-  int B, Hi, Hkv, D, PHD, num_flat_pages, max_pages, ratio, stride;
-  int waves_per_seq;
+  double freq[64];     // RoPE frequencies theta^(-2i/rot), i < rot/2 (set by the launcher)
 };
 
 constexpr int kScoreTilesPerWave = 2;  // decode scoring: tiles of 16 blocks per wave
@@ -114,7 +115,6 @@ hipError_t launch_idx_prep(const IdxPrepArgs &a, hipStream_t s);
 hipError_t launch_idx_handoff(const IdxPrepArgs &a, hipStream_t s);
 hipError_t launch_idx_score(const IdxScoreArgs &a, int dt, hipStream_t s);
 hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s);
-hipError_t launch_idx_dec_prep(const IdxDecPrepArgs &a, hipStream_t s);
 hipError_t launch_idx_dec_score(const IdxDecScoreArgs &a, int dt, hipStream_t s);
 
 }  // namespace qsa

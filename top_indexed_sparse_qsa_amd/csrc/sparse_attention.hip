@@ -925,7 +925,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // results are deterministic.  No cross-workgroup flags are used: on this
 // part each XCD has its own L2, and a kernel boundary is the cheap place to
 // make one workgroup's stores visible to another.
-constexpr int kDecWaves = 4;  // waves (splits) per workgroup
 
 // The K tiles are dead once every wave has finished its list (a workgroup
 // barrier separates the two uses), so the merge scratch overlays them.
@@ -942,7 +941,7 @@ union DecMergeLds {
 
 // Lane (q, r) of wave w merges row r, dims [d0, d0 + D/16).
 template <int D, int DT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_decode_kernel(DecodeAttnArgs a) {
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_decode_kernel(DecodeAttnArgs a) {
   extern __shared__ __align__(16) unsigned char s_raw[];
   DecMergeLds<D> &mg = *reinterpret_cast<DecMergeLds<D> *>(s_raw);
   int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + sizeof(DecMergeLds<D>));  // [2][max_pages]
@@ -1202,6 +1201,9 @@ template <int D, int DT>
 static hipError_t launch_decode_t(const DecodeAttnArgs &a, hipStream_t s) {
   const unsigned pairs = (unsigned)(a.B * a.Hkv);
   const size_t lds = sizeof(DecMergeLds<D>) + (size_t)2 * a.max_pages * sizeof(int32_t);
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_decode_kernel<D, DT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL((sparse_decode_kernel<D, DT>), dim3(pairs * a.ngroups), dim3(64 * a.wpg), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ngroups == 1) return e;
