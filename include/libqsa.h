@@ -53,6 +53,7 @@ extern "C" {
 #define QSA_PARTIAL_ROWS 16   /* rows per partial (the MFMA M tile) */
 #define QSA_MAX_SPLITS 16     /* largest decode split count this library plans */
 #define QSA_MAX_BLOCKS 32768  /* largest complete-block count one row may see */
+#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20) /* scratch of qsa_indexer_decode_noalloc, per GPU */
 
 typedef enum { QSA_FP16 = 0, QSA_BF16 = 1 } qsa_dtype;
 
@@ -266,6 +267,24 @@ qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p);
 qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p);
 qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p);
 qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p);
+
+/* Allocation-free qsa_indexer_decode, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same step as qsa_indexer_decode,
+ * except that its workspace comes from a scratch array libqsa keeps on each
+ * GPU it runs on (QSA_NOALLOC_SCRATCH_BYTES, held until the process ends);
+ * p->workspace and p->workspace_bytes are ignored.  The GPU is the current
+ * HIP device at the call, which must be the device of p->stream.  Returns
+ * QSA_ERR_WORKSPACE_TOO_SMALL when qsa_indexer_decode_workspace_bytes() for
+ * these arguments exceeds QSA_NOALLOC_SCRATCH_BYTES (e.g. batch 256 at
+ * max_pages_per_seq 512 and ratio 4 fits), and the statuses of
+ * qsa_indexer_decode otherwise; QSA_ERR_LAUNCH also when the scratch address
+ * cannot be looked up.  It calls no allocator.  Every call on one GPU uses
+ * that GPU's one array: calls that may overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  Together with
+ * qsa_sparse_decode on its default plan (NULL partials) a whole decode step
+ * allocates nothing. */
+qsa_status qsa_indexer_decode_noalloc(const qsa_indexer_decode_params *p);
 
 /* Workspace sizes (bytes or elements); 0 when the arguments are invalid. */
 size_t qsa_indexer_prefill_workspace_bytes(const qsa_indexer_config *cfg, int32_t batch,

@@ -182,6 +182,37 @@ def test_indexer_decode_rejects(no_gpu, kw, status):
     assert _idecode(**kw) == status
 
 
+def _idecode_noalloc(**kw):
+    cfg = kw.pop("cfg", Q.indexer_config())
+    p = L.IndexerDecodeParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                              2, 4, 128, 256, 16, 8, 2051, cfg, 0, None)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return Q.load().qsa_indexer_decode_noalloc(ctypes.byref(p))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv_pool=None), NULLP), (dict(indices=None), NULLP), (dict(top_k=100), SHAPE),
+    (dict(max_pages_per_seq=2048), UNSUP), (dict(cfg=Q.indexer_config(num_heads=0)), UNSUP),
+    # the scratch holds batch * stride fp32 scores: 16 MiB, e.g. 256 sequences
+    # of 512 pages; 257 of them do not fit
+    (dict(batch=257, max_pages_per_seq=512), WS), (dict(batch=129, max_pages_per_seq=1024), WS),
+])
+def test_indexer_decode_noalloc_rejects(no_gpu, kw, status):
+    """The allocation-free variant validates like qsa_indexer_decode, against
+    its fixed scratch size, before any HIP call (the caller's workspace
+    fields are ignored: here NULL and 0)."""
+    assert _idecode_noalloc(**kw) == status
+
+
+def test_noalloc_scratch_size_covers_the_decode_workload():
+    cfg = Q.indexer_config()
+    assert Q.qsa_indexer_decode_workspace_bytes(cfg, 256, 512) <= Q.QSA_NOALLOC_SCRATCH_BYTES
+    assert Q.qsa_indexer_decode_workspace_bytes(cfg, 257, 512) > Q.QSA_NOALLOC_SCRATCH_BYTES
+    hdr = open(HEADER).read()
+    assert re.search(r"#define QSA_NOALLOC_SCRATCH_BYTES \(16u << 20\)", hdr)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_LIB", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libqsa.so"))

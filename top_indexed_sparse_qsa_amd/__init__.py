@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     QSA_FP16,
     QSA_MAX_BLOCKS,
     QSA_MAX_SPLITS,
+    QSA_NOALLOC_SCRATCH_BYTES,
     QSA_PAGE_TOKENS,
     QSA_PARTIAL_ROWS,
     QsaError,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     indexer_config,
     load,
     qsa_indexer_decode,
+    qsa_indexer_decode_noalloc,
     qsa_indexer_decode_workspace_bytes,
     qsa_indexer_prefill,
     qsa_indexer_prefill_workspace_bytes,

@@ -18,12 +18,14 @@ QSA_PAGE_TOKENS = 128
 QSA_PARTIAL_ROWS = 16
 QSA_MAX_SPLITS = 16
 QSA_MAX_BLOCKS = 32768
+QSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL_POINTER", 2: "QSA_ERR_BAD_SHAPE", 3: "QSA_ERR_UNSUPPORTED",
           4: "QSA_ERR_WORKSPACE_TOO_SMALL", 5: "QSA_ERR_LAUNCH"}
 
 EXPORTS = [
     "qsa_indexer_prefill", "qsa_sparse_prefill", "qsa_indexer_decode", "qsa_sparse_decode",
+    "qsa_indexer_decode_noalloc",
     "qsa_indexer_prefill_workspace_bytes", "qsa_indexer_decode_workspace_bytes",
     "qsa_sparse_decode_partial_o_elems", "qsa_sparse_decode_partial_stats_elems",
     "qsa_sparse_decode_default_splits", "qsa_status_string",
@@ -93,7 +95,8 @@ def load() -> ctypes.CDLL:
                            "(python -m top_indexed_sparse_qsa_amd.build)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, st in (("qsa_indexer_prefill", IndexerPrefillParams), ("qsa_sparse_prefill", SparsePrefillParams),
-                     ("qsa_indexer_decode", IndexerDecodeParams), ("qsa_sparse_decode", SparseDecodeParams)):
+                     ("qsa_indexer_decode", IndexerDecodeParams), ("qsa_sparse_decode", SparseDecodeParams),
+                     ("qsa_indexer_decode_noalloc", IndexerDecodeParams)):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.POINTER(st)]
         fn.restype = ctypes.c_int
@@ -224,3 +227,15 @@ def qsa_indexer_decode(idx_q, idx_k, q_norm_w, k_norm_w, kv_pool, page_table, co
                             kv_pool.shape[3], kv_pool.shape[0], page_table.shape[-1], indices.shape[-1], cfg,
                             _dtype_code(idx_q), _stream(stream))
     _check("qsa_indexer_decode", load().qsa_indexer_decode(ctypes.byref(p)))
+
+
+def qsa_indexer_decode_noalloc(idx_q, idx_k, q_norm_w, k_norm_w, kv_pool, page_table, context_lengths, indices,
+                               cfg: QsaIndexerConfig, head_dim: int, stream=None) -> None:
+    """qsa_indexer_decode with the library's own per-GPU scratch instead of a
+    caller workspace (allocation-free; calls that overlap on one GPU race)."""
+    B = idx_k.shape[0]
+    p = IndexerDecodeParams(_ptr(idx_q), _ptr(idx_k), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(kv_pool),
+                            _ptr(page_table), _ptr(context_lengths), _ptr(indices), None, 0, B, kv_pool.shape[2],
+                            head_dim, kv_pool.shape[3], kv_pool.shape[0], page_table.shape[-1], indices.shape[-1],
+                            cfg, _dtype_code(idx_q), _stream(stream))
+    _check("qsa_indexer_decode_noalloc", load().qsa_indexer_decode_noalloc(ctypes.byref(p)))

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqsa.so")
-SOURCES = ["api.cpp", "indexer.hip", "sparse_attention.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "sparse_attention.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON = [

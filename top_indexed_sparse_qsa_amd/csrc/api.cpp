@@ -288,7 +288,11 @@ qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p) {
   return launched(qsa::launch_idx_select(xa, w.gmax, s));
 }
 
-qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
+}  // extern "C"
+
+// Host-visible argument checks of qsa_indexer_decode (shared with its
+// allocation-free variant, which checks with its scratch size).
+qsa_status qsa::check_indexer_decode(const qsa_indexer_decode_params *p) {
   if (!p || !p->idx_q || !p->idx_k || !p->q_norm_w || !p->k_norm_w || !p->kv_pool || !p->page_table ||
       !p->context_lengths || !p->indices || !p->workspace)
     return QSA_ERR_NULL_POINTER;
@@ -307,8 +311,15 @@ qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
     return QSA_ERR_UNSUPPORTED;
   if (!all_aligned16(p->idx_q, p->idx_k, p->kv_pool)) return QSA_ERR_BAD_SHAPE;
   if (((uintptr_t)p->workspace % kAlign) != 0) return QSA_ERR_BAD_SHAPE;
+  if (p->workspace_bytes < decode_ws(p->cfg, p->batch, p->max_pages_per_seq).total) return QSA_ERR_WORKSPACE_TOO_SMALL;
+  return QSA_OK;
+}
+
+extern "C" {
+
+qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
+  if (qsa_status st = qsa::check_indexer_decode(p)) return st;
   const DecodeWs w = decode_ws(p->cfg, p->batch, p->max_pages_per_seq);
-  if (p->workspace_bytes < w.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
   char *ws = static_cast<char *>(p->workspace);
   const hipStream_t s = (hipStream_t)p->stream;
   const int dt = (int)p->dtype;

@@ -5,7 +5,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "libqsa.h"
+
 namespace qsa {
+
+// Host-visible argument checks of qsa_indexer_decode (api.cpp).
+__attribute__((visibility("hidden"))) qsa_status check_indexer_decode(const qsa_indexer_decode_params *p);
 
 struct PrefillAttnArgs {
   const uint16_t *q, *k, *v;
