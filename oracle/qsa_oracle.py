@@ -18,6 +18,11 @@ pages are cited by title and section):
   QsaSparsePrefillParams (BSND layout, list contract, zero rows past the live
   length) and struct QsaSparseDecodeParams (paged pool, page table with V
   pages pre-offset by numPages, only columns [0, headDim) read).
+* [Plugin]  also its fused step 1 (packed-QKV split + per-head qk-norm with
+  gammas pre-folded to 1+w + partial RoPE + paged-KV write + dense K/V
+  mirrors; in decode the rope-append of the new token) and its KV pool
+  contract: the leading head_size elements of a pool row hold roped K / raw
+  V, the tail is the indexer's.
 * [Atlas]   atlasinference, "spark_model/layers/ops/qsa.rs": doc comments of
   qsa_block_pool (mean over ratio raw keys, then RMSNorm*(1+w), then rope at
   the block-start position), qsa_qprep (per head RMSNorm*(1+w) + partial rope
@@ -41,6 +46,13 @@ Readings where the pages leave a step open:
   in decode), the prepped queries to float32.
 * The 32-bit float parameters the boundary receives (eps, theta, attention
   scale) are used at their float32 values.
+* Front end: a packed QKV row holds the Hq query heads, then the Hkv key
+  heads, then the Hkv value heads, D each.  q-norm and k-norm are RMSNorm
+  over D with one gamma vector each (shared by the heads), received already
+  folded (gamma = 1 + w); RoPE as for the indexer.  Row t of sequence b sits
+  at position start[b] + t (start = 0 without past) and is live while that
+  position is below the sequence's total length; only live rows reach the
+  pool.  V passes through unchanged.
 
 Storage conventions: fp16 arrays are ``np.float16``; bf16 arrays are uint16
 bit patterns.
@@ -412,6 +424,67 @@ def prefill_state_writes(idx_k, w_k, ctx, page_table, icfg, D: int, dtype: str, 
             pg, row = pool_row(None, page_table, b, 0, j, page_tokens)
             writes.append((pg, row, idx_k[b, j].copy()))
     return writes
+
+
+# ---------------------------------------------------------------------------
+# Front end  [Plugin: fused step 1, KV pool contract]
+# ---------------------------------------------------------------------------
+def rms_norm_gamma(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean_d x_d^2 + eps) * gamma over the last axis; gamma is the
+    folded gain (1 + w)."""
+    ms = np.mean(np.square(x), axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def split_packed_qkv(qkv: np.ndarray, Hq: int, Hkv: int, D: int):
+    """[..., (Hq + 2 Hkv) D] -> q [..., Hq, D], k [..., Hkv, D], v [..., Hkv, D]."""
+    lead = qkv.shape[:-1]
+    assert qkv.shape[-1] == (Hq + 2 * Hkv) * D
+    q = qkv[..., : Hq * D].reshape(*lead, Hq, D)
+    k = qkv[..., Hq * D: (Hq + Hkv) * D].reshape(*lead, Hkv, D)
+    v = qkv[..., (Hq + Hkv) * D:].reshape(*lead, Hkv, D)
+    return q, k, v
+
+
+def front_end(qkv, q_gamma, k_gamma, ctx, Hq: int, Hkv: int, D: int, rot: int, theta: float, eps: float,
+              dtype: str, start=None, page_table=None, page_tokens: int = 128):
+    """Packed QKV -> (q, k, v, pool_writes).
+
+    qkv [B, S, (Hq+2Hkv) D] storage; q_gamma, k_gamma fp32 [D] (folded 1+w);
+    ctx [B] total lengths; start [B] past lengths or None (all 0).
+    q [B,S,Hq,D] and k [B,S,Hkv,D]: qk-norm then rope at the row's position,
+    rounded once to dtype; v [B,S,Hkv,D]: unchanged.  Every row is computed;
+    pool_writes, with a page table, lists for each live row (position <
+    ctx[b]) (flat_page, row, 'k' or 'v' plane, values [Hkv, D] storage), the
+    leading D columns of that token's K and V pool rows."""
+    B, S = qkv.shape[0], qkv.shape[1]
+    st = np.zeros(B, dtype=np.int64) if start is None else np.asarray(start, dtype=np.int64)
+    x = widen(qkv, dtype)
+    q_raw, k_raw, _ = split_packed_qkv(x, Hq, Hkv, D)
+    pos = st[:, None] + np.arange(S)[None, :]                         # [B, S]
+    eps32, theta32 = f32(eps), f32(theta)
+    q = rope(rms_norm_gamma(q_raw, widen(q_gamma, "fp32"), eps32), pos[..., None], rot, theta32)
+    k = rope(rms_norm_gamma(k_raw, widen(k_gamma, "fp32"), eps32), pos[..., None], rot, theta32)
+    q, k = round_to(q, dtype), round_to(k, dtype)
+    writes = []
+    if page_table is not None:
+        for b in range(B):
+            for t in range(S):
+                p = int(pos[b, t])
+                if p >= int(ctx[b]):
+                    continue
+                pk, row = pool_row(None, page_table, b, 0, p, page_tokens)
+                pv, _ = pool_row(None, page_table, b, 1, p, page_tokens)
+                writes.append((pk, row, "k", narrow(k[b, t], dtype)))
+                writes.append((pv, row, "v", np.asarray(qkv[b, t, (Hq + Hkv) * D:]).reshape(Hkv, D).copy()))
+    v = np.asarray(qkv)[..., (Hq + Hkv) * D:].reshape(B, S, Hkv, D).copy()   # raw V, storage unchanged
+    return narrow(q, dtype), narrow(k, dtype), v, writes
+
+
+def apply_front_end_writes(pool: np.ndarray, writes, D: int) -> None:
+    """Apply front_end's pool writes in place: columns [0, D) of every head."""
+    for pg, row, _, vals in writes:
+        pool[pg, row, :, :D] = vals
 
 
 def apply_tail_writes(pool: np.ndarray, writes, D: int) -> None:

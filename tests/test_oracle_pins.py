@@ -495,3 +495,108 @@ def test_decode_steps_after_prefill_handoff_match_prefill_rows():
         expect = O.prefill_state_writes(inp.idx_k[b:b + 1, :c], inp.w_k, np.array([c]), pt[b:b + 1], icfg, D, "bf16")
         for pg, row, vals in expect:
             assert np.array_equal(pool[pg, row, 0, D:].view(np.uint16), vals.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# front end [Plugin: fused step 1; KV pool contract]
+# ---------------------------------------------------------------------------
+def test_front_end_gamma_is_the_folded_one_plus_w():
+    """The front end's qk-norm takes the gain already folded (gamma = 1 + w);
+    it equals the indexer's RMSNorm*(1+w) on the same w, and gamma = 1 leaves
+    an output RMS of sqrt(ms / (ms + eps))."""
+    rng = np.random.default_rng(50)
+    x = rng.standard_normal((3, 128))
+    w = rng.standard_normal(128) * 0.1
+    eps = 1e-6
+    assert np.allclose(O.rms_norm_gamma(x, 1.0 + w, eps), O.rms_norm(x, w, eps), rtol=0, atol=1e-15)
+    y = O.rms_norm_gamma(x, np.ones(128), eps)
+    ms = np.mean(x * x, axis=1)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), np.sqrt(ms / (ms + eps)), rtol=1e-14)
+
+
+def test_front_end_packed_layout():
+    """A packed row is Q heads, then K heads, then V heads, D each."""
+    Hq, Hkv, D = 3, 2, 4
+    row = np.arange((Hq + 2 * Hkv) * D, dtype=np.float64)
+    q, k, v = O.split_packed_qkv(row, Hq, Hkv, D)
+    for h in range(Hq):
+        assert list(q[h]) == [h * D + d for d in range(D)]
+    for h in range(Hkv):
+        assert list(k[h]) == [(Hq + h) * D + d for d in range(D)]
+        assert list(v[h]) == [(Hq + Hkv + h) * D + d for d in range(D)]
+
+
+def test_front_end_position_zero_is_norm_times_gamma_hand_loop():
+    """At position 0 RoPE is the identity: q and k are x / sqrt(mean x^2 + eps)
+    * gamma, rounded once; written out with fsum loops.  V is the packed V
+    unchanged, bit for bit."""
+    rng = np.random.default_rng(51)
+    Hq, Hkv, D = 2, 1, 64
+    qkv = syn.normal(rng, (1, 1, (Hq + 2 * Hkv) * D), "fp16")
+    gq = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    gk = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    eps = 1e-6
+    q, k, v, _ = O.front_end(qkv, gq, gk, [1], Hq, Hkv, D, 32, 1e6, eps, "fp16")
+    x = qkv[0, 0].astype(np.float64)
+    e32 = float(np.float32(eps))
+    for h, (out, g, base) in enumerate([(q[0, 0, 0], gq, 0), (q[0, 0, 1], gq, D), (k[0, 0, 0], gk, Hq * D)]):
+        xs = x[base:base + D]
+        den = math.sqrt(math.fsum(t * t for t in xs) / D + e32)
+        want = np.array([xs[d] / den * float(g[d]) for d in range(D)]).astype(np.float16)
+        assert np.array_equal(out, want), f"head {h}"
+    assert np.array_equal(v[0, 0, 0], qkv[0, 0, (Hq + Hkv) * D:])
+
+
+def test_front_end_pool_matches_dense_mirrors_through_permuted_pages():
+    """The rows the front end writes to the paged pool (through a permuted
+    page table, V pages offset by numPages) are the rows of its dense K/V
+    mirrors: decode attention over the pool equals prefill attention over the
+    mirrors for the same list.  Tails (columns >= D) and dead rows are not
+    written."""
+    rng = np.random.default_rng(52)
+    B, S, Hq, Hkv, D, hd = 2, 300, 8, 2, 64, 32
+    ctx = np.array([300, 171], dtype=np.int32)
+    qkv = syn.normal(rng, (B, S, (Hq + 2 * Hkv) * D), "bf16")
+    gq = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    gk = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    pages = [3, 2]
+    perm = rng.permutation(sum(pages)).astype(np.int32)
+    npg = len(perm)
+    pt = np.full((B, 2, 4), -1, dtype=np.int32)
+    pt[0, 0, :3], pt[1, 0, :2] = perm[:3], perm[3:5]
+    pt[:, 1] = np.where(pt[:, 0] >= 0, pt[:, 0] + npg, -1)
+    q, k, v, writes = O.front_end(qkv, gq, gk, ctx, Hq, Hkv, D, 32, 1e6, 1e-6, "bf16", page_table=pt)
+    assert len(writes) == 2 * int(ctx.sum())
+    pool = syn.normal(rng, (2 * npg, 128, Hkv, D + hd), "bf16")
+    before = pool.copy()
+    O.apply_front_end_writes(pool, writes, D)
+    assert np.array_equal(pool[..., D:], before[..., D:]), "a tail changed"
+    for b in range(B):
+        t = int(ctx[b]) - 1
+        ids = np.sort(rng.choice(t + 1, min(t + 1, 40), replace=False)).astype(np.int32)
+        lst = np.full((B, 1, 64), -1, dtype=np.int32)
+        lst[b, 0, :ids.size] = ids
+        ql = q[:, t:t + 1]
+        dec = O.sparse_decode(ql, pool, pt, lst, ctx, 0.125, D, "bf16", seqs=[b])[b]
+        full = np.full((B, S, 64), -1, dtype=np.int32)
+        full[b, t, :ids.size] = ids
+        pre = O.sparse_prefill(q, k, v, full, ctx, 0.125, "bf16", rows=[(b, t)])[(b, t)]
+        assert np.allclose(dec, pre, rtol=0, atol=1e-12)
+
+
+def test_front_end_append_equals_prefill_row():
+    """Decode's rope-append of token p (one row, start = p) gives prefill row
+    p's q, k and pool rows bit for bit."""
+    rng = np.random.default_rng(53)
+    B, S, Hq, Hkv, D = 1, 70, 4, 1, 128
+    qkv = syn.normal(rng, (B, S, (Hq + 2 * Hkv) * D), "fp16")
+    g = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    pt = np.array([[[0], [1]]], dtype=np.int32)
+    q, k, v, w = O.front_end(qkv, g, g, [S], Hq, Hkv, D, 64, 1e6, 1e-6, "fp16", page_table=pt)
+    for p in (0, 1, 37, 69):
+        q1, k1, v1, w1 = O.front_end(qkv[:, p:p + 1], g, g, [p + 1], Hq, Hkv, D, 64, 1e6, 1e-6, "fp16",
+                                     start=[p], page_table=pt)
+        assert np.array_equal(q1[0, 0], q[0, p]) and np.array_equal(k1[0, 0], k[0, p])
+        assert np.array_equal(v1[0, 0], v[0, p])
+        want = [x for x in w if x[1] == p]
+        assert len(w1) == 2 and all(a[:3] == b_[:3] and np.array_equal(a[3], b_[3]) for a, b_ in zip(w1, want))
