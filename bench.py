@@ -73,6 +73,7 @@ def parse():
     ap.add_argument("--workloads", default="1,2,3,4,5",
                     help="comma list of workloads to run (4 = decode); the headline always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-front-end", action="store_true", help="skip the fused front end measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -312,6 +313,48 @@ def decode_bench(inp, args, Q, torch):
 
 
 # ---------------------------------------------------------------------------
+# front end (packed QKV -> Q, K/V mirrors, pool rows) at the long prefill's shape
+# ---------------------------------------------------------------------------
+FRONT_END_SHAPE = dict(B=1, S=32768, Hq=32, Hkv=4, D=128, dtype="fp16", ctx=[32768], rot=64)
+
+
+def front_end_bench(args, Q, torch, syn):
+    inp = syn.make_front_end(6, **FRONT_END_SHAPE)
+    stream = torch.cuda.current_stream()
+    qkv = dev(inp.qkv, inp.dtype)
+    gq, gk, ctx = dev(inp.q_gamma), dev(inp.k_gamma), dev(inp.ctx)
+    q = torch.empty((inp.B, inp.S, inp.Hq, inp.D), dtype=qkv.dtype, device="cuda")
+    k = torch.empty((inp.B, inp.S, inp.Hkv, inp.D), dtype=qkv.dtype, device="cuda")
+    v = torch.empty_like(k)
+    pool, pt = dev(inp.pool, inp.dtype), dev(inp.page_table)
+
+    def step(mark):
+        if mark:
+            mark(0)
+        Q.qsa_qkv_front_end(qkv, gq, gk, ctx, q, inp.Hq, inp.Hkv, inp.rot, 1.0e6, 1.0e-6, k_out=k, v_out=v,
+                            kv_pool=pool, page_table=pt, stream=stream)
+        if mark:
+            mark(1)
+
+    wall, (ms,) = timed_loops(step, args.steps, args.warmup, stream, torch, 2)
+    e = 2
+    rows = inp.B * inp.S
+    nbytes = rows * ((inp.Hq + 2 * inp.Hkv) * inp.D * e            # packed rows read
+                     + inp.Hq * inp.D * e + 2 * inp.Hkv * inp.D * e  # Q and the K/V mirrors written
+                     + 2 * inp.Hkv * inp.D * e)                      # pool K/V leading columns written
+    out = {"workload": "fused front end at the long prefill's shape: B=1 S=32768 Hq=32 Hkv=4 D=128 fp16 rot 64, "
+                       "packed QKV -> Q, dense K/V mirrors, paged pool rows",
+           "value": rows / (wall / args.steps), "unit": "tokens/s", "ms_per_step": wall / args.steps * 1e3,
+           "ms_per_call": ms,
+           "roofline": {"kernel": "front_end_kernel", "bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "algorithmic_bytes_per_call": nbytes}}
+    del qkv, q, k, v, pool
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 # HBM counter figures
 # ---------------------------------------------------------------------------
 def kernel_code_sha256(path=None):
@@ -469,6 +512,11 @@ def main():
             results[wl] = prefill_bench(wl, inp, args, Q, torch)
         note(f"workload {wl}: {results[wl]['ms_per_step']:.4f} ms/step")
         inputs.pop(wl, None)
+    fe = None
+    if not args.no_front_end:
+        note("front end")
+        fe = front_end_bench(args, Q, torch, syn)
+        note(f"front end: {fe['ms_per_call']:.4f} ms/call")
     copy_gbs = None
     n = 1 << 30
     a = torch.empty(n // 2, dtype=torch.float16, device="cuda").fill_(1.0)
@@ -512,6 +560,7 @@ def main():
         "cpu_baseline": cpu,
         "workloads": {str(w): r for w, r in results.items() if w not in (args.headline, DECODE_WORKLOAD)},
         "decode": dec,
+        "front_end": fe,
         "hbm_copy_gbs": copy_gbs,
     }
     print(json.dumps(line), flush=True)

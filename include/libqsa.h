@@ -263,6 +263,58 @@ typedef struct {
   void *stream;
 } qsa_indexer_decode_params;
 
+/* Fused front end [Plugin: fused step 1 -- packed-QKV split + per-head
+ * qk-norm (gammas pre-folded to 1+w) + partial RoPE + paged-KV write + dense
+ * K/V mirrors, and in decode the rope-append of the new token; "KV pool
+ * contract (widened rows)"].
+ * qkv: [batch, seq_len, (num_q_heads + 2*num_kv_heads) * head_dim], each row
+ * the query heads, then the key heads, then the value heads.  q_gamma,
+ * k_gamma: fp32 [head_dim], the gains already folded (1 + w), one vector for
+ * all query heads and one for all key heads.  Row t of sequence b sits at
+ * position start_positions[b] + t (start_positions NULL: t; decode passes
+ * the past lengths with seq_len 1) and is live while that position is below
+ * context_lengths[b] (the TOTAL length).
+ * Outputs, for every row: q_out [batch, seq_len, num_q_heads, head_dim] =
+ * RoPE(RMSNorm(q) * q_gamma) (eps inside the square root, mean over
+ * head_dim; the first rot_dim dims turn as pairs (i, i + rot_dim/2) by
+ * position * rope_theta^(-2i/rot_dim)), evaluated in fp64 and rounded once;
+ * k_out the same for the key heads with k_gamma; v_out the value heads
+ * unchanged.  k_out / v_out are the dense mirrors the prefill attention
+ * reads; both may be NULL (decode).  With kv_pool not NULL (pool and page
+ * table as for qsa_sparse_decode) each live row's K and V go to columns
+ * [0, head_dim) of its token's K-plane and V-plane rows; the tails
+ * [head_dim, pool_head_dim) and every other row stay bit-unchanged, and rows
+ * whose page-table entry is out of range are skipped.
+ * Supported: head_dim 64 or 128, rot_dim even and <= head_dim, num_q_heads
+ * and num_kv_heads >= 1, rope_theta > 0, rms_eps >= 0; with the pool,
+ * pool_head_dim >= head_dim, a multiple of 8. */
+typedef struct {
+  const void *qkv;
+  const float *q_gamma;
+  const float *k_gamma;
+  const int32_t *context_lengths;
+  const int32_t *start_positions;
+  void *q_out;
+  void *k_out;
+  void *v_out;
+  void *kv_pool;
+  const int32_t *page_table;
+  int32_t batch;
+  int32_t seq_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t rot_dim;
+  int32_t pool_head_dim;
+  int32_t num_flat_pages;
+  int32_t max_pages_per_seq;
+  float rope_theta;
+  float rms_eps;
+  qsa_dtype dtype;
+  void *stream;
+} qsa_front_end_params;
+
+qsa_status qsa_qkv_front_end(const qsa_front_end_params *p);
 qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p);
 qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p);
 qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p);

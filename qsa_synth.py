@@ -186,6 +186,53 @@ def make_decode(seed: int, ctx=None, B: int = 32, Hq: int = 32, Hkv: int = 4, D:
                         top_k=icfg.top_k, icfg=icfg)
 
 
+@dataclass
+class FrontEndInputs:
+    B: int
+    S: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    rot: int
+    ctx: np.ndarray            # int32 [B] total lengths
+    start: np.ndarray | None   # int32 [B] past lengths, or None
+    qkv: np.ndarray            # [B,S,(Hq+2Hkv)*D]
+    q_gamma: np.ndarray        # fp32 [D], 1 + N(0, 0.1^2)
+    k_gamma: np.ndarray
+    num_pages: int
+    max_pages: int
+    page_table: np.ndarray     # int32 [B,2,max_pages]
+    pool: np.ndarray           # [2*num_pages,128,Hkv,D+128]
+
+
+def make_front_end(seed: int, B: int, S: int, Hq: int, Hkv: int, D: int, dtype: str, ctx, rot: int,
+                   start=None, max_pages: int | None = None, tail: int = 128) -> FrontEndInputs:
+    """Packed QKV rows, folded gains 1 + N(0, 0.1^2), and a pool with a
+    seeded page permutation holding every position below ctx.  Draw order:
+    qkv, q gain, k gain, page permutation, pool."""
+    rng = np.random.default_rng(seed)
+    qkv = normal(rng, (B, S, (Hq + 2 * Hkv) * D), dtype)
+    q_gamma = (1.0 + norm_weights(rng, D)).astype(np.float32)
+    k_gamma = (1.0 + norm_weights(rng, D)).astype(np.float32)
+    ctx = np.asarray(ctx, dtype=np.int32).reshape(B)
+    pages_per = [(int(c) + PAGE_TOKENS - 1) // PAGE_TOKENS for c in ctx]
+    max_pages = max_pages or max(1, max(pages_per))
+    num_pages = max(1, sum(pages_per))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    pt = np.full((B, 2, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages_per):
+        pt[b, 0, :n] = perm[off:off + n]
+        pt[b, 1, :n] = perm[off:off + n] + num_pages
+        off += n
+    pool = normal(rng, (2 * num_pages, PAGE_TOKENS, Hkv, D + tail), dtype)
+    return FrontEndInputs(B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, rot=rot, ctx=ctx,
+                          start=None if start is None else np.asarray(start, dtype=np.int32).reshape(B),
+                          qkv=qkv, q_gamma=q_gamma, k_gamma=k_gamma, num_pages=num_pages, max_pages=max_pages,
+                          page_table=pt, pool=pool)
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.  Seed = workload number.
 # ---------------------------------------------------------------------------

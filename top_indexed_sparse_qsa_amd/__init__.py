@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     qsa_indexer_decode_workspace_bytes,
     qsa_indexer_prefill,
     qsa_indexer_prefill_workspace_bytes,
+    qsa_qkv_front_end,
     qsa_sparse_decode,
     qsa_sparse_decode_default_splits,
     qsa_sparse_decode_partial_o_elems,

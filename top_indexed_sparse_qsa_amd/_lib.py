@@ -25,7 +25,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL_POINTER", 2: "QSA_ERR_BAD_SHAPE", 3: "QS
 
 EXPORTS = [
     "qsa_indexer_prefill", "qsa_sparse_prefill", "qsa_indexer_decode", "qsa_sparse_decode",
-    "qsa_indexer_decode_noalloc",
+    "qsa_indexer_decode_noalloc", "qsa_qkv_front_end",
     "qsa_indexer_prefill_workspace_bytes", "qsa_indexer_decode_workspace_bytes",
     "qsa_sparse_decode_partial_o_elems", "qsa_sparse_decode_partial_stats_elems",
     "qsa_sparse_decode_default_splits", "qsa_status_string",
@@ -56,6 +56,15 @@ class SparseDecodeParams(ctypes.Structure):
                 ("pool_head_dim", _i32), ("num_flat_pages", _i32), ("max_pages_per_seq", _i32),
                 ("top_k", _i32), ("num_splits", _i32), ("attention_scale", _f32), ("dtype", ctypes.c_int),
                 ("stream", _vp)]
+
+
+class FrontEndParams(ctypes.Structure):
+    _fields_ = [("qkv", _vp), ("q_gamma", _vp), ("k_gamma", _vp), ("context_lengths", _vp),
+                ("start_positions", _vp), ("q_out", _vp), ("k_out", _vp), ("v_out", _vp), ("kv_pool", _vp),
+                ("page_table", _vp), ("batch", _i32), ("seq_len", _i32), ("num_q_heads", _i32),
+                ("num_kv_heads", _i32), ("head_dim", _i32), ("rot_dim", _i32), ("pool_head_dim", _i32),
+                ("num_flat_pages", _i32), ("max_pages_per_seq", _i32), ("rope_theta", _f32), ("rms_eps", _f32),
+                ("dtype", ctypes.c_int), ("stream", _vp)]
 
 
 class IndexerPrefillParams(ctypes.Structure):
@@ -96,7 +105,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     for name, st in (("qsa_indexer_prefill", IndexerPrefillParams), ("qsa_sparse_prefill", SparsePrefillParams),
                      ("qsa_indexer_decode", IndexerDecodeParams), ("qsa_sparse_decode", SparseDecodeParams),
-                     ("qsa_indexer_decode_noalloc", IndexerDecodeParams)):
+                     ("qsa_indexer_decode_noalloc", IndexerDecodeParams), ("qsa_qkv_front_end", FrontEndParams)):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.POINTER(st)]
         fn.restype = ctypes.c_int
@@ -239,3 +248,19 @@ def qsa_indexer_decode_noalloc(idx_q, idx_k, q_norm_w, k_norm_w, kv_pool, page_t
                             head_dim, kv_pool.shape[3], kv_pool.shape[0], page_table.shape[-1], indices.shape[-1],
                             cfg, _dtype_code(idx_q), _stream(stream))
     _check("qsa_indexer_decode_noalloc", load().qsa_indexer_decode_noalloc(ctypes.byref(p)))
+
+
+def qsa_qkv_front_end(qkv, q_gamma, k_gamma, context_lengths, q_out, num_q_heads: int, num_kv_heads: int,
+                      rot_dim: int, rope_theta: float = 1.0e6, rms_eps: float = 1.0e-6, k_out=None, v_out=None,
+                      start_positions=None, kv_pool=None, page_table=None, stream=None) -> None:
+    """qkv [B,S,(Hq+2Hkv)*D]; q_gamma/k_gamma fp32 [D] (folded 1+w); q_out [B,S,Hq,D]; optional mirrors
+    k_out/v_out [B,S,Hkv,D], start_positions int32 [B], pool [2*numPages,128,Hkv,poolHeadDim] + page table."""
+    B, S = qkv.shape[0], qkv.shape[1]
+    D = q_out.shape[-1]
+    p = FrontEndParams(_ptr(qkv), _ptr(q_gamma), _ptr(k_gamma), _ptr(context_lengths), _ptr(start_positions),
+                       _ptr(q_out), _ptr(k_out), _ptr(v_out), _ptr(kv_pool), _ptr(page_table), B, S, num_q_heads,
+                       num_kv_heads, D, rot_dim, kv_pool.shape[3] if kv_pool is not None else 0,
+                       kv_pool.shape[0] if kv_pool is not None else 0,
+                       page_table.shape[-1] if page_table is not None else 0, float(rope_theta), float(rms_eps),
+                       _dtype_code(qkv), _stream(stream))
+    _check("qsa_qkv_front_end", load().qsa_qkv_front_end(ctypes.byref(p)))

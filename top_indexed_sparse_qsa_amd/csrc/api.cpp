@@ -130,6 +130,49 @@ int32_t qsa_sparse_decode_default_splits(int32_t batch, int32_t hkv, int32_t top
   return default_splits(batch, hkv, top_k);
 }
 
+qsa_status qsa_qkv_front_end(const qsa_front_end_params *p) {
+  if (!p || !p->qkv || !p->q_gamma || !p->k_gamma || !p->context_lengths || !p->q_out) return QSA_ERR_NULL_POINTER;
+  if (!p->k_out != !p->v_out) return QSA_ERR_NULL_POINTER;  // both mirrors or neither
+  if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
+  if (p->batch < 1 || p->seq_len < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1) return QSA_ERR_BAD_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return QSA_ERR_UNSUPPORTED;
+  if (p->rot_dim < 0 || p->rot_dim > p->head_dim || (p->rot_dim & 1)) return QSA_ERR_UNSUPPORTED;
+  if (!(p->rope_theta > 0.f) || !isfinite(p->rope_theta) || !(p->rms_eps >= 0.f) || !isfinite(p->rms_eps))
+    return QSA_ERR_BAD_SHAPE;
+  if (!all_aligned16(p->qkv, p->q_out, p->k_out, p->v_out)) return QSA_ERR_BAD_SHAPE;
+  if ((int64_t)p->batch * p->seq_len * (p->num_q_heads + 2 * p->num_kv_heads) * p->head_dim > ((int64_t)1 << 40))
+    return QSA_ERR_UNSUPPORTED;
+  if (p->kv_pool) {
+    if (!p->page_table) return QSA_ERR_NULL_POINTER;
+    if (p->num_flat_pages < 1 || p->max_pages_per_seq < 1) return QSA_ERR_BAD_SHAPE;
+    if (p->pool_head_dim < p->head_dim || (p->pool_head_dim % 8) != 0) return QSA_ERR_BAD_SHAPE;
+    if (!all_aligned16(p->kv_pool)) return QSA_ERR_BAD_SHAPE;
+  }
+  qsa::FrontEndArgs a{};
+  a.qkv = static_cast<const uint16_t *>(p->qkv);
+  a.q_gamma = p->q_gamma;
+  a.k_gamma = p->k_gamma;
+  a.ctx = p->context_lengths;
+  a.start = p->start_positions;
+  a.q_out = static_cast<uint16_t *>(p->q_out);
+  a.k_out = static_cast<uint16_t *>(p->k_out);
+  a.v_out = static_cast<uint16_t *>(p->v_out);
+  a.pool = static_cast<uint16_t *>(p->kv_pool);
+  a.pt = p->kv_pool ? p->page_table : nullptr;
+  a.B = p->batch;
+  a.S = p->seq_len;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.rot = p->rot_dim;
+  a.PHD = p->kv_pool ? p->pool_head_dim : 0;
+  a.num_flat_pages = p->kv_pool ? p->num_flat_pages : 0;
+  a.max_pages = p->kv_pool ? p->max_pages_per_seq : 0;
+  a.theta = (double)p->rope_theta;
+  a.eps = (double)p->rms_eps;
+  a.dt = (int)p->dtype;
+  return launched(qsa::launch_front_end(a, p->head_dim, (hipStream_t)p->stream));
+}
+
 qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p) {
   if (!p || !p->q || !p->k || !p->v || !p->o || !p->indices || !p->context_lengths) return QSA_ERR_NULL_POINTER;
   if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;

@@ -836,10 +836,13 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
 //     (columns = heads), the relus of the heads summed across lanes.
 // Nothing else reads or writes the tails this step touches.
 // ---------------------------------------------------------------------------
-constexpr int kDecScoreWaves = 4;
+#ifndef QSA_DEC_SCORE_WAVES
+#define QSA_DEC_SCORE_WAVES 4
+#endif
+constexpr int kDecScoreWaves = QSA_DEC_SCORE_WAVES;
 
 template <int DT>
-__global__ __launch_bounds__(256) void idx_dec_score_kernel(IdxDecScoreArgs a) {
+__global__ __launch_bounds__(64 * kDecScoreWaves) void idx_dec_score_kernel(IdxDecScoreArgs a) {
   constexpr int NP = QSplit<DT>::NP;
   constexpr int TPW = kScoreTilesPerWave;
   __shared__ __align__(16) float s_q[4][128];
@@ -848,12 +851,19 @@ __global__ __launch_bounds__(256) void idx_dec_score_kernel(IdxDecScoreArgs a) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x / a.wg_per_seq, wg = blockIdx.x % a.wg_per_seq;
+  const int wg_begin = wg * kDecScoreWaves * TPW * 16;
+  const int g_begin = wg_begin + wv * TPW * 16;
+  const int32_t *ptk = a.pt + (size_t)b * 2 * a.max_pages;
+  const int32_t *ptv = ptk + a.max_pages;
+  // the page-table entries of this wave's blocks go out with the context
+  // length (one round trip before the tail loads instead of two)
+  int pte[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) pte[tt] = ptv[min((a.ratio * (g_begin + tt * 16 + r16)) >> 7, a.max_pages - 1)];
   const int ctx = min(a.ctx[b], a.max_pages * 128);
   if (ctx <= 0) return;
   const int p = ctx - 1;
   const int nc = ctx / a.ratio;
-  const int32_t *ptk = a.pt + (size_t)b * 2 * a.max_pages;
-  const int32_t *ptv = ptk + a.max_pages;
   const bool closes = ctx % a.ratio == 0;
   if (wg == 0 && !closes && wv == kDecScoreWaves - 1) {
     // the new token's block stays open: its raw key goes to its K-row tail
@@ -863,17 +873,17 @@ __global__ __launch_bounds__(256) void idx_dec_score_kernel(IdxDecScoreArgs a) {
       a.pool[o + a.D + 64 + lane] = a.idx_k[(size_t)b * 128 + 64 + lane];
     }
   }
-  const int wg_begin = wg * kDecScoreWaves * TPW * 16;
   if (wg_begin >= nc) return;  // uniform over the workgroup
-  const int g_begin = wg_begin + wv * TPW * 16;
 
   // kbar tail loads of this wave's blocks, issued before anything else
   u32x4 kb[TPW][4];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int g = g_begin + tt * 16 + r16;
-    long long o = g < nc ? pool_row_off(ptv, a.ratio * g, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD) : -1;
-    if (o < 0) o = 0;
+    const int tok = a.ratio * g;
+    long long o = 0;
+    if (g < nc && (tok >> 7) < a.max_pages && (unsigned)pte[tt] < (unsigned)a.num_flat_pages)
+      o = (((long long)pte[tt] * 128 + (tok & 127)) * a.Hkv) * a.PHD;
     const uint16_t *src = a.pool + o + a.D + 8 * q4;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kb[tt][ks] = ld16(src + 32 * ks);
@@ -1101,8 +1111,8 @@ hipError_t launch_idx_dec_score(const IdxDecScoreArgs &a_in, int dt, hipStream_t
   a.wg_per_seq = (a.gmax + per_wg - 1) / per_wg;
   if (a.wg_per_seq < 1) a.wg_per_seq = 1;  // the first workgroup also writes the open block's raw tail
   const unsigned grid = (unsigned)((long long)a.B * a.wg_per_seq);
-  if (dt == DT_F16) hipLaunchKernelGGL(idx_dec_score_kernel<DT_F16>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(idx_dec_score_kernel<DT_BF16>, dim3(grid), dim3(256), 0, s, a);
+  if (dt == DT_F16) hipLaunchKernelGGL(idx_dec_score_kernel<DT_F16>, dim3(grid), dim3(64 * kDecScoreWaves), 0, s, a);
+  else hipLaunchKernelGGL(idx_dec_score_kernel<DT_BF16>, dim3(grid), dim3(64 * kDecScoreWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -110,6 +110,22 @@ struct IdxDecScoreArgs {
   double freq[64];     // RoPE frequencies theta^(-2i/rot), i < rot/2 (set by the launcher)
 };
 
+// Fused front end (packed QKV -> Q, K/V mirrors, pool rows).
+struct FrontEndArgs {
+  const uint16_t *qkv;        // [B,S,(Hq+2Hkv)*D]
+  const float *q_gamma, *k_gamma;
+  const int32_t *ctx, *start;  // start may be null (all 0)
+  uint16_t *q_out, *k_out, *v_out;  // k_out / v_out may be null
+  uint16_t *pool;             // may be null
+  const int32_t *pt;
+  int B, S, Hq, Hkv, rot, PHD, num_flat_pages, max_pages;
+  double theta, eps;
+  int dt;
+  double freq[64];            // set by the launcher
+};
+
+hipError_t launch_front_end(const FrontEndArgs &a, int D, hipStream_t s);
+
 constexpr int kScoreTilesPerWave = 2;  // decode scoring: tiles of 16 blocks per wave
 constexpr float kLog2e = 1.4426950408889634f;
 

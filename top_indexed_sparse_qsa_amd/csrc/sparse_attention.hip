@@ -293,6 +293,19 @@ __device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV
   run_chunks<D, DT>(list, n_slots, kv, qf, sl2, m_run, l_run, acc, ktile, c0, fa, id_b);
 }
 
+// run_chunks over a list from slot 0, with the raw ids of its first two
+// chunks already loaded (slots past n_slots read as -1).
+template <int D, int DT, class KV>
+__device__ void run_list_ids(const int32_t *__restrict__ list, int n_slots, const KV &kv,
+                             const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
+                             f32x4 (&acc)[8], u32x4 *ktile, int id_a, int id_b) {
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
+  if (!wave_any((unsigned)id_a < (unsigned)kv.limit)) return;
+  Frag<D> fa;
+  issue_chunk<D, DT>(fa, id_a, kv, q4, r16);
+  run_chunks<D, DT>(list, n_slots, kv, qf, sl2, m_run, l_run, acc, ktile, 0, fa, id_b);
+}
+
 template <int D>
 __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhead0, int G, int q4, int r16) {
 #pragma unroll
@@ -951,24 +964,45 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   const int b = pair / a.Hkv, kvh = pair % a.Hkv;
   const int split = group * a.wpg + wv;
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  const int ctx = min(max(a.ctx[b], 0), a.max_pages * 128);
-  const int npages = (ctx + 127) >> 7;
-  const int32_t *ptb = a.pt + (size_t)b * 2 * a.max_pages;
-  for (int i = threadIdx.x; i < 2 * npages; i += blockDim.x) {
-    const int row = i >= npages, j = i - row * npages;
-    s_pt[row * a.max_pages + j] = ptb[row * a.max_pages + j];
+  // Everything the walk needs first is issued at once -- the first two
+  // chunks' ids, Q, the context length and both page-table rows (whole
+  // rows, so that the copy does not wait for the context length) -- so that
+  // one round trip precedes the first gathers.
+  const int s0 = split * a.split_slots;
+  const int n_slots = split < a.nsplits ? min(a.top_k - s0, a.split_slots) : 0;
+  const int32_t *list = a.indices + (size_t)b * a.top_k + s0;
+  const int sl = lane & 31;
+  const int id_a = sl < n_slots ? list[sl] : -1;
+  const int id_b = sl + 32 < n_slots ? list[sl + 32] : -1;
+  u32x4 qf[D / 32];
+  load_q<D>(qf, a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
+  const int ctx_in = a.ctx[b];
+  {
+    const int32_t *ptb = a.pt + (size_t)b * 2 * a.max_pages;  // rows 0 and 1 are contiguous
+    const int npt = 2 * a.max_pages;
+    constexpr int U = 4;
+    for (int i0 = threadIdx.x; i0 < npt; i0 += U * (int)blockDim.x) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * (int)blockDim.x;
+        v[u] = i < npt ? ptb[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * (int)blockDim.x;
+        if (i < npt) s_pt[i] = v[u];
+      }
+    }
   }
   __syncthreads();
+  const int ctx = min(max(ctx_in, 0), a.max_pages * 128);
 
   f32x4 acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  const int s0 = split * a.split_slots;
-  const int n_slots = split < a.nsplits ? min(a.top_k - s0, a.split_slots) : 0;
   if (ctx > 0 && n_slots > 0) {
-    u32x4 qf[D / 32];
-    load_q<D>(qf, a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
     PagedKV kv;
     kv.pool = a.pool + (size_t)kvh * a.PHD;
     kv.pk = s_pt;
@@ -976,7 +1010,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     kv.row_stride = (size_t)a.Hkv * a.PHD;
     kv.num_flat_pages = a.num_flat_pages;
     kv.limit = ctx;
-    run_list<D, DT>(a.indices + (size_t)b * a.top_k + s0, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile[wv]);
+    run_list_ids<D, DT>(list, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile[wv], id_a, id_b);
   }
   __syncthreads();  // every K tile is dead before the merge scratch is written
   float l = l_run + shfl_xor_f(l_run, 16);
