@@ -27,7 +27,13 @@
  *     between calls, and enqueues all work on `stream` (a hipStream_t; NULL
  *     is the default stream).  Buffers must stay alive until that work ends.
  *     Calls are reentrant and contain no host-device synchronisation, so they
- *     may be captured in a HIP graph.
+ *     may be captured in a HIP graph.  The only things the library holds are
+ *     read-only device properties it looks up once per device (the CU
+ *     count) and, on each GPU that runs it, the scratch of
+ *     qsa_indexer_decode_noalloc.
+ *   - Floating-point inputs must be finite (the kernels are built without
+ *     NaN/Inf semantics): a NaN or Inf in Q, K, V, the pool or the indexer
+ *     inputs gives unspecified output values, never a fault.
  *   - Only host-visible arguments are validated.  On any validation failure
  *     the call returns a non-QSA_OK status and enqueues nothing.  Device
  *     contents (list validity, context lengths, page ids) are the caller's
@@ -55,7 +61,15 @@ extern "C" {
 #define QSA_MAX_BLOCKS 32768  /* largest complete-block count one row may see */
 #define QSA_NOALLOC_SCRATCH_BYTES (16u << 20) /* scratch of qsa_indexer_decode_noalloc, per GPU */
 
-typedef enum { QSA_FP16 = 0, QSA_BF16 = 1 } qsa_dtype;
+/* The *_RANGE_MIN / *_RANGE_MAX members are not values to use: they give the
+ * enums the range of int32_t, so that any int a caller passes (an unknown
+ * dtype or status) is a valid value to test and reject. */
+typedef enum {
+  QSA_FP16 = 0,
+  QSA_BF16 = 1,
+  QSA_DTYPE_RANGE_MIN = -2147483647 - 1,
+  QSA_DTYPE_RANGE_MAX = 2147483647
+} qsa_dtype;
 
 typedef enum {
   QSA_OK = 0,
@@ -63,7 +77,9 @@ typedef enum {
   QSA_ERR_BAD_SHAPE = 2,
   QSA_ERR_UNSUPPORTED = 3,
   QSA_ERR_WORKSPACE_TOO_SMALL = 4,
-  QSA_ERR_LAUNCH = 5
+  QSA_ERR_LAUNCH = 5,
+  QSA_STATUS_RANGE_MIN = -2147483647 - 1,
+  QSA_STATUS_RANGE_MAX = 2147483647
 } qsa_status;
 
 /* Indexer attributes [Plugin: constructor attributes indexerNumHeads,

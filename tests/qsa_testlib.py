@@ -103,6 +103,62 @@ def check_list(got: np.ndarray, ref: np.ndarray, scores: np.ndarray | None, t: i
     return True
 
 
+def check_list_invariants_all_rows(lists: np.ndarray, ctx, icfg, what: str = "") -> int:
+    """Every row of an index-list array [B, S, top_k] against the closed forms
+    the method fixes, vectorised: |list(t)| = r*min(nc, budget) + (t+1) mod r,
+    -1 exactly on the right, the causal tail {r*nc .. t} present, the rest
+    whole aligned blocks of r ids below r*nc, all ids distinct and <= t; rows
+    at or past the live length all -1.  Returns the rows checked."""
+    r, budget = icfg.compress_ratio, icfg.budget
+    B, S, K = lists.shape
+    big = np.iinfo(np.int32).max
+    checked = 0
+    for b in range(B):
+        live = min(int(ctx[b]), S)
+        assert np.all(lists[b, live:] == -1), f"{what} b={b}: a row past the live length is not all -1"
+        if live == 0:
+            continue
+        L = lists[b, :live]
+        t = np.arange(live)
+        nc = (t + 1) // r
+        n_exp = r * np.minimum(nc, budget) + (t + 1) % r
+        valid = L >= 0
+        n = valid.sum(axis=1)
+        bad = np.nonzero(n != n_exp)[0]
+        assert bad.size == 0, f"{what} b={b}: row {bad[0]} has {n[bad[0]]} ids, expected {n_exp[bad[0]]}"
+        right = np.arange(K)[None, :] < n[:, None]
+        assert np.array_equal(valid, right), f"{what} b={b}: -1 not only on the right"
+        srt = np.sort(np.where(valid, L, big), axis=1)
+        # distinct
+        dup = (srt[:, 1:] == srt[:, :-1]) & (srt[:, 1:] != big)
+        assert not dup.any(), f"{what} b={b}: duplicate ids in row {np.nonzero(dup.any(1))[0][0]}"
+        # all ids <= t: the largest valid id is the last one of the sorted valid part
+        last = srt[np.arange(live), n - 1]
+        assert np.all(last <= t), f"{what} b={b}: an id past its row"
+        # the tail: the (t+1) mod r largest ids are r*nc .. t
+        tl = (t + 1) % r
+        for j in range(1, r):
+            rows = np.nonzero(tl >= j)[0]
+            if rows.size:
+                want = t[rows] - (j - 1)
+                got = srt[rows, n[rows] - j]
+                assert np.array_equal(got, want), f"{what} b={b}: wrong causal tail in row {rows[np.argmax(got != want)]}"
+        # the body: whole aligned blocks below r*nc
+        nb = n - tl                         # ids in whole blocks
+        col = np.arange(K)[None, :]
+        body = col < nb[:, None]
+        ids = np.where(body, srt, 0)
+        first = ids[:, ::r] if r > 1 else ids
+        assert np.all((first % r == 0) | ~body[:, ::r]), f"{what} b={b}: a block does not start at a multiple of r"
+        for j in range(1, r):
+            cj = ids[:, j::r][:, :first.shape[1]]
+            mask = body[:, j::r][:, :first.shape[1]]
+            assert np.all((cj == first[:, :cj.shape[1]] + j) | ~mask), f"{what} b={b}: ids are not whole blocks"
+        assert np.all(np.where(body, srt, -1) < (r * nc)[:, None]), f"{what} b={b}: a block reaches the tail"
+        checked += live
+    return checked
+
+
 def structured_lists(rng: np.random.Generator, B: int, S: int, ctx, icfg, top_k: int,
                      shuffle: bool = True) -> np.ndarray:
     """Lists with the shape the indexer produces -- min(nc, budget) whole

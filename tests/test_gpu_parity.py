@@ -392,8 +392,10 @@ def test_prefill_workload_full_size(wl):
     # workload 2 (the headline one) row by row in full; the larger ones sampled
     rows = ([(b, t) for b in range(inp.B) for t in range(inp.S)] if wl == 2
             else TL.sample_rows(inp.B, inp.S, inp.ctx, 128, rng))
-    TL.log(f"prefill workload {wl}: oracle on {len(rows)} rows")
     out_np = out.cpu().numpy()
+    n_rows = TL.check_list_invariants_all_rows(out_np, inp.ctx, icfg, f"workload {wl}")
+    TL.log(f"prefill workload {wl}: list invariants hold on all {n_rows} live rows")
+    TL.log(f"prefill workload {wl}: oracle on {len(rows)} rows")
     lists = {r: out_np[r] for r in rows}
     ref_lists, swaps, same = compare_lists(lists, inp, icfg, icfg.top_k, rows, f"workload {wl}")
     TL.log(f"  boundary swaps used: {swaps} of {len(rows)} rows")
@@ -414,7 +416,7 @@ def test_prefill_workload_full_size(wl):
     check_rows_written(o, inp, f"workload {wl}")
 
 
-@pytest.mark.parametrize("wl", [2, 5])
+@pytest.mark.parametrize("wl", [2, 3, 5])
 def test_sparse_prefill_structured_lists_full_size(wl):
     TL.log(f"sparse prefill structured lists workload {wl}")
     inp = syn.workload(wl)

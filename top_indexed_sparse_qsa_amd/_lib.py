@@ -11,7 +11,10 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqsa.so")
+# LIBQSA_PATH names another build of the same library (the host-sanitized
+# one the boundary tests run against); it is never a fallback: a missing
+# file still raises.
+LIB_PATH = os.environ.get("LIBQSA_PATH") or os.path.join(HERE, "libqsa.so")
 
 QSA_FP16, QSA_BF16 = 0, 1
 QSA_PAGE_TOKENS = 128

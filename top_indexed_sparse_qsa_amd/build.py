@@ -1,7 +1,9 @@
 """Builds libqsa.so in-tree with hipcc for gfx950.
 
 Each source compiles to an object in parallel, then one shared library is
-linked next to this file.  Run ``python -m top_indexed_sparse_qsa_amd.build``.
+linked next to this file.  Run ``python -m top_indexed_sparse_qsa_amd.build``;
+``--sanitize`` builds ``libqsa_san.so`` instead, with the host code under
+AddressSanitizer and UndefinedBehaviorSanitizer (for the boundary tests).
 """
 from __future__ import annotations
 
@@ -38,30 +40,48 @@ def _hipcc() -> str:
     return p
 
 
-def _compile(src: str, obj: str) -> None:
+# Host-side sanitizers (the device code is left as it is): the host layer's
+# argument checks, workspace arithmetic and launch planning run under
+# AddressSanitizer and UndefinedBehaviorSanitizer.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(HERE, "libqsa_san.so")
+
+
+def asan_runtime() -> str:
+    """Path of the shared ASan runtime the sanitized library needs preloaded."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else ""
+
+
+def _compile(src: str, obj: str, extra=()) -> None:
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out = SAN_LIB if sanitize else LIB
+    extra = SANITIZE if sanitize else []
     with tempfile.TemporaryDirectory(prefix="qsa_build_") as tmp:
         objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
         with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-            list(ex.map(_compile, SOURCES, objs))
-        out_tmp = LIB + ".tmp"
-        cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
+            list(ex.map(lambda so: _compile(*so, extra=extra), zip(SOURCES, objs)))
+        out_tmp = out + ".tmp"
+        link_extra = ["-shared-libasan", "-fsanitize=address,undefined"] if sanitize else []
+        cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", out_tmp]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-        os.replace(out_tmp, LIB)
+        os.replace(out_tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
     sys.exit(0)

@@ -101,6 +101,7 @@ const char *qsa_status_string(qsa_status s) {
     case QSA_ERR_UNSUPPORTED: return "configuration not supported by this build";
     case QSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case QSA_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: break;
   }
   return "unknown status";
 }

@@ -34,6 +34,8 @@
 // columns (see "Tiles" below).
 #include <math.h>
 
+#include <atomic>
+
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -1129,17 +1131,20 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
 constexpr int kTileRangeX2 = QSA_TILE_RANGE_X2;
 
 // CUs per XCD of the current device (its CU count / 8), or 0 when that is
-// not a whole number; cached per device.
+// not a whole number.  A read-only device property, looked up once per
+// device; concurrent first calls may both look it up and store the same value.
 static int xcd_cus() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-    cache[dev] = (n > 0 && n % 8 == 0) ? n / 8 : -1;
+    c = (n > 0 && n % 8 == 0) ? n / 8 : -1;
+    cache[dev].store(c, std::memory_order_relaxed);
   }
-  return cache[dev] > 0 ? cache[dev] : 0;
+  return c > 0 ? c : 0;
 }
 
 template <int D, int DT>
