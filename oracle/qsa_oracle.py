@@ -46,6 +46,14 @@ Readings where the pages leave a step open:
   in decode), the prepped queries to float32.
 * The 32-bit float parameters the boundary receives (eps, theta, attention
   scale) are used at their float32 values.
+* Chunked prefill: chunk row t of sequence b sits at position start[b] + t
+  and is live while that position is below the total length ctx[b]; its
+  list is the prefill list of that position (global token ids).  The
+  indexer state of the positions before the chunk is the one the pool tails
+  hold; a block the chunk completes is pooled from the stored raw keys of
+  its earlier tokens plus the chunk's keys; after the chunk the tails hold
+  what a prefill of length ctx[b] leaves.  Attention reads every key and
+  value, the chunk's own included, through the page table.
 * Front end: a packed QKV row holds the Hq query heads, then the Hkv key
   heads, then the Hkv value heads, D each.  q-norm and k-norm are RMSNorm
   over D with one gamma vector each (shared by the heads), received already
@@ -394,6 +402,79 @@ def indexer_decode(idx_q, idx_k, w_q, w_k, pool, page_table, ctx, icfg, D: int, 
     if seqs is None:
         lists = np.stack([lists[b] for b in range(B)])[:, None, :]
     return (writes, lists, all_scores) if return_scores else (writes, lists)
+
+
+def indexer_chunk(idx_q, idx_k, w_q, w_k, pool, page_table, start, ctx, icfg, D: int, dtype: str, top_k: int,
+                  page_tokens: int = 128, return_scores: bool = False):
+    """The indexer over a chunk of rows that continue the state in the pool
+    tails (decode is the chunk of one row).
+
+    idx_q [B,C,Hi,hd], idx_k [B,C,hd] raw storage of the chunk's tokens;
+    start [B] past lengths (positions of chunk row 0), ctx [B] total lengths.
+    Returns (writes, lists [B,C,top_k]) with writes the tail updates in
+    indexer_decode's form: the kbar of every block the chunk completes (V-row
+    tail of its first token) and the raw keys of the chunk's tokens in the
+    trailing incomplete block (their K-row tails).  The pool is not modified."""
+    B, C = idx_k.shape[0], idx_k.shape[1]
+    r, hd = icfg.compress_ratio, icfg.head_dim
+    tail = slice(D, D + hd)
+    writes = []
+    lists = np.full((B, C, top_k), -1, dtype=np.int32)
+    scores = {}
+    for b in range(B):
+        P, c = int(start[b]), int(ctx[b])
+        if c <= P:
+            continue
+        raw_of = lambda j: (widen(idx_k[b, j - P], dtype) if j >= P else
+                            widen(pool[pool_row(pool, page_table, b, 0, j, page_tokens) + (0,)][tail], dtype))
+        nc_all = c // r
+        kbar = np.empty((nc_all, hd), dtype=np.float64)
+        for g in range(nc_all):
+            if r * g + r <= P:           # complete before the chunk: its V-row tail holds kbar
+                pg, row = pool_row(pool, page_table, b, 1, r * g, page_tokens)
+                kbar[g] = widen(pool[pg, row, 0, tail], dtype)
+            else:                        # completed by the chunk: pool it
+                kbar[g] = pool_blocks(np.stack([raw_of(r * g + j) for j in range(r)]), g, w_k, icfg, dtype)[0]
+                pg, row = pool_row(pool, page_table, b, 1, r * g, page_tokens)
+                writes.append((pg, row, narrow(kbar[g], dtype)))
+        for j in range(max(P, r * nc_all), c):  # the chunk's tokens of the trailing incomplete block
+            pg, row = pool_row(pool, page_table, b, 0, j, page_tokens)
+            writes.append((pg, row, np.asarray(idx_k[b, j - P]).copy()))
+        for t in range(min(C, c - P)):
+            p = P + t
+            qhat = prep_queries(widen(idx_q[b, t], dtype), p, w_q, icfg)
+            s = block_scores(qhat, kbar[: (p + 1) // r])
+            lists[b, t] = expand_list(p, select_blocks(s, icfg.budget), icfg, top_k)
+            if return_scores:
+                scores[(b, t)] = s
+    return (writes, lists, scores) if return_scores else (writes, lists)
+
+
+def sparse_chunk(q, pool, page_table, indices, start, ctx, scale: float, D: int, dtype: str, page_tokens: int = 128):
+    """Sparse attention of chunk rows over the paged pool.  q [B,C,Hq,D];
+    indices [B,C,top_k]; row t of sequence b is live while start[b] + t <
+    ctx[b], other rows are +0.0.  Returns float64 [B,C,Hq,D]."""
+    B, C, Hq, _ = q.shape
+    Hkv = pool.shape[2]
+    G = Hq // Hkv
+    sc = f32(scale)
+    out = np.zeros((B, C, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for t in range(C):
+            if int(start[b]) + t >= int(ctx[b]):
+                continue
+            ids = indices[b, t]
+            ids = ids[ids >= 0]
+            if not ids.size:
+                continue
+            kp = page_table[b, 0, ids // page_tokens]
+            vp = page_table[b, 1, ids // page_tokens]
+            kr = widen(pool[kp, ids % page_tokens, :, :D], dtype)
+            vr = widen(pool[vp, ids % page_tokens, :, :D], dtype)
+            qr = widen(q[b, t], dtype)
+            for kv in range(Hkv):
+                out[b, t, kv * G:(kv + 1) * G] = attend(qr[kv * G:(kv + 1) * G], kr[:, kv], vr[:, kv], sc)
+    return out
 
 
 def prefill_state_writes(idx_k, w_k, ctx, page_table, icfg, D: int, dtype: str, page_tokens: int = 128):

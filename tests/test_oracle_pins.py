@@ -600,3 +600,87 @@ def test_front_end_append_equals_prefill_row():
         assert np.array_equal(v1[0, 0], v[0, p])
         want = [x for x in w if x[1] == p]
         assert len(w1) == 2 and all(a[:3] == b_[:3] and np.array_equal(a[3], b_[3]) for a, b_ in zip(w1, want))
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill [reading: a chunk row's list is the prefill list of its position]
+# ---------------------------------------------------------------------------
+def _paged_state(rng, B, N, D, Hkv, hd, dtype, k, v):
+    """A pool holding the K/V rows of positions < N of each sequence (columns
+    [0, D)) through a permuted page table, random tails elsewhere."""
+    pages = (N + 127) // 128
+    perm = rng.permutation(B * pages).astype(np.int32)
+    npg = B * pages
+    pt = np.full((B, 2, pages), -1, dtype=np.int32)
+    for b in range(B):
+        pt[b, 0] = perm[b * pages:(b + 1) * pages]
+        pt[b, 1] = pt[b, 0] + npg
+    pool = syn.normal(rng, (2 * npg, 128, Hkv, D + hd), dtype)
+    for b in range(B):
+        tok = np.arange(N)
+        pool[pt[b, 0, tok // 128], tok % 128, :, :D] = k[b, :N]
+        pool[pt[b, 1, tok // 128], tok % 128, :, :D] = v[b, :N]
+    return pool, pt
+
+
+@pytest.mark.parametrize("P,N", [(300, 377), (301, 390), (302, 303), (303, 420), (96, 100), (0, 70)])
+def test_chunk_equals_unchunked_prefill(P, N):
+    """Prefill of P tokens (its state handed to the pool tails), then one
+    chunk of the tokens P .. N-1: the chunk's lists are the prefill lists of
+    rows P .. N-1 of a one-shot prefill of N tokens, bit for bit; its tail
+    writes leave the state a prefill of N leaves; its attention over the pool
+    equals the prefill attention of those rows."""
+    icfg = syn.IndexerCfg(budget=8)
+    rng = np.random.default_rng(60 + P + N)
+    B, Hq, Hkv, D, dt = 2, 4, 2, 64, "fp16"
+    inp = syn.make_prefill(60, B=B, S=N, Hq=Hq, Hkv=Hkv, D=D, dtype=dt, ctx=[N, N], icfg=icfg)
+    ref = O.indexer_prefill(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.ctx, icfg, dt, icfg.top_k)
+    pool, pt = _paged_state(rng, B, N, D, Hkv, icfg.head_dim, dt, inp.k, inp.v)
+    start = np.array([P, P], dtype=np.int32)
+    O.apply_tail_writes(pool, O.prefill_state_writes(inp.idx_k, inp.w_k, start, pt, icfg, D, dt), D)
+    writes, lists = O.indexer_chunk(inp.idx_q[:, P:], inp.idx_k[:, P:], inp.w_q, inp.w_k, pool, pt, start, inp.ctx,
+                                    icfg, D, dt, icfg.top_k)
+    assert np.array_equal(lists, ref[:, P:])
+    after = pool.copy()
+    O.apply_tail_writes(after, writes, D)
+    want = pool.copy()
+    O.apply_tail_writes(want, O.prefill_state_writes(inp.idx_k, inp.w_k, inp.ctx, pt, icfg, D, dt), D)
+    # the state a decode continues from: V-row tails of complete blocks and K-row tails of the open block
+    r = icfg.compress_ratio
+    for b in range(B):
+        for g in range(N // r):
+            pg, row = O.pool_row(None, pt, b, 1, r * g)
+            assert np.array_equal(after[pg, row, 0, D:], want[pg, row, 0, D:]), f"kbar of block {g}"
+        for j in range(r * (N // r), N):
+            pg, row = O.pool_row(None, pt, b, 0, j)
+            assert np.array_equal(after[pg, row, 0, D:], want[pg, row, 0, D:]), f"raw tail of token {j}"
+    out = O.sparse_chunk(inp.q[:, P:], pool, pt, lists, start, inp.ctx, inp.scale, D, dt)
+    pre = O.sparse_prefill(inp.q, inp.k, inp.v, ref, inp.ctx, inp.scale, dt)
+    assert np.allclose(out, pre[:, P:], rtol=0, atol=1e-12)
+
+
+def test_chunk_of_one_row_is_a_decode_step():
+    inp = syn.make_decode(64, ctx=[2052, 9001, 7, 4096], B=4, Hq=8, Hkv=2, D=64, dtype="bf16", max_pages=80)
+    w1, l1 = O.indexer_decode(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.pool, inp.page_table, inp.ctx, inp.icfg,
+                              inp.D, inp.dtype, inp.top_k)
+    w2, l2 = O.indexer_chunk(inp.idx_q, inp.idx_k, inp.w_q, inp.w_k, inp.pool, inp.page_table, inp.ctx - 1, inp.ctx,
+                             inp.icfg, inp.D, inp.dtype, inp.top_k)
+    assert np.array_equal(l1, l2)
+    key = lambda w: sorted((int(p), int(r), tuple(v.view(np.uint16).tolist())) for p, r, v in w)
+    assert key(w1) == key(w2)
+
+
+def test_chunk_padding_rows():
+    """Chunk rows at or past the total length: lists all -1, output +0.0."""
+    icfg = syn.IndexerCfg(budget=4)
+    inp = syn.make_prefill(65, B=2, S=40, Hq=2, Hkv=1, D=64, dtype="fp16", ctx=[40, 40], icfg=icfg)
+    rng = np.random.default_rng(65)
+    pool, pt = _paged_state(rng, 2, 40, 64, 1, 128, "fp16", inp.k, inp.v)
+    start = np.array([20, 30], dtype=np.int32)
+    ctx = np.array([33, 30], dtype=np.int32)       # 13 live rows; none in the second sequence
+    O.apply_tail_writes(pool, O.prefill_state_writes(inp.idx_k, inp.w_k, start, pt, icfg, 64, "fp16"), 64)
+    _, lists = O.indexer_chunk(inp.idx_q[:, 20:], inp.idx_k[:, 20:], inp.w_q, inp.w_k, pool, pt, start, ctx, icfg,
+                               64, "fp16", icfg.top_k)
+    assert np.all(lists[0, 13:] == -1) and np.all(lists[1] == -1) and np.all(lists[0, :13, 0] >= 0)
+    out = O.sparse_chunk(inp.q[:, 20:], pool, pt, lists, start, ctx, inp.scale, 64, "fp16")
+    assert np.all(out[0, 13:] == 0) and np.all(out[1] == 0)
