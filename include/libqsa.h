@@ -336,6 +336,87 @@ qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p);
 qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p);
 qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p);
 
+/* Chunked prefill over the paged pool: a chunk of chunk_len new tokens per
+ * sequence continues a sequence whose earlier tokens are already in the pool
+ * (attention K/V in the leading columns, indexer state in the tails, as left
+ * by qsa_indexer_prefill's handoff, an earlier chunk or decode steps).  The
+ * pages' plugin rejects chunked prefill [Plugin: Contract]; this is our
+ * extension, with the list contract: chunk row t of sequence b sits at
+ * position start_positions[b] + t (start_positions = the past lengths) and
+ * is live while that position is below context_lengths[b] (the TOTAL length
+ * after the chunk); its list is exactly the prefill list of that position
+ * (top budget blocks of all complete blocks before it, expanded, plus its
+ * causal tail; global token ids, -1 padded), and rows that are not live are
+ * all -1 / +0.0.  Decode is the chunk of one row.
+ *
+ * qsa_indexer_chunk: idx_q [batch, chunk_len, num_heads, hd], idx_k [batch,
+ * chunk_len, hd] raw; indices out [batch, chunk_len, top_k].  It pools every
+ * block the chunk completes (the stored raw keys of its tokens before the
+ * chunk plus the chunk's keys) into that block's V-row tail, stores the raw
+ * keys of the chunk's tokens of the trailing incomplete block in their K-row
+ * tails, and leaves the rest of the pool bit-unchanged -- so the tails then
+ * hold what a prefill of context_lengths[b] tokens leaves.  workspace: at
+ * least qsa_indexer_chunk_workspace_bytes() bytes, 256-byte aligned (fp32
+ * queries, kbar of every block, fp32 score rows).  Pool, page table and
+ * sizes as for qsa_indexer_decode.
+ * qsa_sparse_chunk: q, o [batch, chunk_len, num_q_heads, head_dim]; the
+ * attention of every live row over its list, K/V read through the page
+ * table (the chunk's own tokens included: write them first, e.g. with
+ * qsa_qkv_front_end and start_positions); the split plan is the library's
+ * (one workgroup per row and KV head, no workspace).  Supported: as
+ * qsa_sparse_decode. */
+typedef struct {
+  const void *idx_q;
+  const void *idx_k;
+  const float *q_norm_w;
+  const float *k_norm_w;
+  void *kv_pool;
+  const int32_t *page_table;
+  const int32_t *start_positions;
+  const int32_t *context_lengths;
+  int32_t *indices;
+  void *workspace;
+  size_t workspace_bytes;
+  int32_t batch;
+  int32_t chunk_len;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t pool_head_dim;
+  int32_t num_flat_pages;
+  int32_t max_pages_per_seq;
+  int32_t top_k;
+  qsa_indexer_config cfg;
+  qsa_dtype dtype;
+  void *stream;
+} qsa_indexer_chunk_params;
+
+typedef struct {
+  const void *q;
+  void *o;
+  const void *kv_pool;
+  const int32_t *page_table;
+  const int32_t *indices;
+  const int32_t *start_positions;
+  const int32_t *context_lengths;
+  int32_t batch;
+  int32_t chunk_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t pool_head_dim;
+  int32_t num_flat_pages;
+  int32_t max_pages_per_seq;
+  int32_t top_k;
+  float attention_scale;
+  qsa_dtype dtype;
+  void *stream;
+} qsa_sparse_chunk_params;
+
+qsa_status qsa_indexer_chunk(const qsa_indexer_chunk_params *p);
+qsa_status qsa_sparse_chunk(const qsa_sparse_chunk_params *p);
+size_t qsa_indexer_chunk_workspace_bytes(const qsa_indexer_config *cfg, int32_t batch, int32_t chunk_len,
+                                         int32_t max_pages_per_seq);
+
 /* Allocation-free qsa_indexer_decode, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  The same step as qsa_indexer_decode,

@@ -103,12 +103,13 @@ def check_list(got: np.ndarray, ref: np.ndarray, scores: np.ndarray | None, t: i
     return True
 
 
-def check_list_invariants_all_rows(lists: np.ndarray, ctx, icfg, what: str = "") -> int:
+def check_list_invariants_all_rows(lists: np.ndarray, ctx, icfg, what: str = "", row0: int = 0) -> int:
     """Every row of an index-list array [B, S, top_k] against the closed forms
     the method fixes, vectorised: |list(t)| = r*min(nc, budget) + (t+1) mod r,
     -1 exactly on the right, the causal tail {r*nc .. t} present, the rest
     whole aligned blocks of r ids below r*nc, all ids distinct and <= t; rows
-    at or past the live length all -1.  Returns the rows checked."""
+    at or past the live length all -1.  Rows below row0 are not checked (a
+    chunk's rows start there).  Returns the rows checked."""
     r, budget = icfg.compress_ratio, icfg.budget
     B, S, K = lists.shape
     big = np.iinfo(np.int32).max
@@ -116,10 +117,10 @@ def check_list_invariants_all_rows(lists: np.ndarray, ctx, icfg, what: str = "")
     for b in range(B):
         live = min(int(ctx[b]), S)
         assert np.all(lists[b, live:] == -1), f"{what} b={b}: a row past the live length is not all -1"
-        if live == 0:
+        if live <= row0:
             continue
-        L = lists[b, :live]
-        t = np.arange(live)
+        L = lists[b, row0:live]
+        t = np.arange(row0, live)
         nc = (t + 1) // r
         n_exp = r * np.minimum(nc, budget) + (t + 1) % r
         valid = L >= 0
@@ -133,7 +134,7 @@ def check_list_invariants_all_rows(lists: np.ndarray, ctx, icfg, what: str = "")
         dup = (srt[:, 1:] == srt[:, :-1]) & (srt[:, 1:] != big)
         assert not dup.any(), f"{what} b={b}: duplicate ids in row {np.nonzero(dup.any(1))[0][0]}"
         # all ids <= t: the largest valid id is the last one of the sorted valid part
-        last = srt[np.arange(live), n - 1]
+        last = srt[np.arange(t.size), n - 1]
         assert np.all(last <= t), f"{what} b={b}: an id past its row"
         # the tail: the (t+1) mod r largest ids are r*nc .. t
         tl = (t + 1) % r
@@ -155,7 +156,7 @@ def check_list_invariants_all_rows(lists: np.ndarray, ctx, icfg, what: str = "")
             mask = body[:, j::r][:, :first.shape[1]]
             assert np.all((cj == first[:, :cj.shape[1]] + j) | ~mask), f"{what} b={b}: ids are not whole blocks"
         assert np.all(np.where(body, srt, -1) < (r * nc)[:, None]), f"{what} b={b}: a block reaches the tail"
-        checked += live
+        checked += t.size
     return checked
 
 

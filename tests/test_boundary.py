@@ -265,3 +265,68 @@ def test_product_path_and_oracle_are_separate():
             "print(sorted(m for m in sys.modules if 'oracle' in m))")
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, check=True)
     assert out.stdout.strip() == "[]", out.stdout
+
+
+def _front(**kw):
+    p = L.FrontEndParams(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None,
+                         1, 64, 8, 2, 128, 64, 0, 0, 0, 1.0e6, 1.0e-6, 0, None)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return Q.load().qsa_qkv_front_end(ctypes.byref(p))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=None), NULLP), (dict(q_out=None), NULLP), (dict(k_out=None), NULLP), (dict(q_gamma=None), NULLP),
+    (dict(dtype=5), UNSUP), (dict(batch=0), SHAPE), (dict(num_kv_heads=0), SHAPE), (dict(head_dim=96), UNSUP),
+    (dict(rot_dim=130), UNSUP), (dict(rot_dim=33), UNSUP), (dict(rope_theta=0.0), SHAPE), (dict(rms_eps=-1.0), SHAPE),
+    (dict(q_out=FAKE + 2), SHAPE), (dict(kv_pool=FAKE), NULLP),
+    (dict(kv_pool=FAKE, page_table=FAKE, num_flat_pages=4, max_pages_per_seq=2, pool_head_dim=100), SHAPE),
+    (dict(kv_pool=FAKE, page_table=FAKE, num_flat_pages=0, max_pages_per_seq=2, pool_head_dim=256), SHAPE),
+])
+def test_front_end_rejects(no_gpu, kw, status):
+    assert _front(**kw) == status
+
+
+def _ichunk(**kw):
+    cfg = kw.pop("cfg", Q.indexer_config())
+    p = L.IndexerChunkParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                             2, 64, 4, 128, 256, 16, 8, 2051, cfg, 0, None)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return Q.load().qsa_indexer_chunk(ctypes.byref(p))
+
+
+def _schunk(**kw):
+    p = L.SparseChunkParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 32, 4, 128, 256, 16, 8, 2051, 0.088, 0, None)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return Q.load().qsa_sparse_chunk(ctypes.byref(p))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(start_positions=None), NULLP), (dict(kv_pool=None), NULLP), (dict(workspace=None), NULLP),
+    (dict(chunk_len=0), SHAPE), (dict(top_k=2050), SHAPE), (dict(pool_head_dim=200), SHAPE),
+    (dict(max_pages_per_seq=2048), UNSUP), (dict(workspace_bytes=100), WS), (dict(workspace=FAKE + 8), SHAPE),
+    (dict(cfg=Q.indexer_config(compress_ratio=0)), UNSUP),
+])
+def test_indexer_chunk_rejects(no_gpu, kw, status):
+    assert _ichunk(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(start_positions=None), NULLP), (dict(indices=None), NULLP), (dict(chunk_len=0), SHAPE),
+    (dict(num_q_heads=33), SHAPE), (dict(head_dim=96), UNSUP), (dict(max_pages_per_seq=5000), UNSUP),
+    (dict(attention_scale=-1.0), SHAPE), (dict(q=FAKE + 4), SHAPE), (dict(pool_head_dim=120), SHAPE),
+])
+def test_sparse_chunk_rejects(no_gpu, kw, status):
+    assert _schunk(**kw) == status
+
+
+def test_chunk_workspace_follows_layout():
+    cfg = Q.indexer_config()
+    a = lambda x: (x + 255) // 256 * 256
+    B, C, mp = 2, 100, 20
+    g = mp * 128 // 4
+    assert Q.qsa_indexer_chunk_workspace_bytes(cfg, B, C, mp) == a(B * C * 4 * 128 * 4) + a(B * g * 128 * 2) + \
+        a(B * C * g * 4)
+    assert Q.qsa_indexer_chunk_workspace_bytes(cfg, 0, C, mp) == 0

@@ -20,12 +20,15 @@ from ._lib import (  # noqa: F401
     QsaIndexerConfig,
     indexer_config,
     load,
+    qsa_indexer_chunk,
+    qsa_indexer_chunk_workspace_bytes,
     qsa_indexer_decode,
     qsa_indexer_decode_noalloc,
     qsa_indexer_decode_workspace_bytes,
     qsa_indexer_prefill,
     qsa_indexer_prefill_workspace_bytes,
     qsa_qkv_front_end,
+    qsa_sparse_chunk,
     qsa_sparse_decode,
     qsa_sparse_decode_default_splits,
     qsa_sparse_decode_partial_o_elems,

@@ -28,7 +28,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL_POINTER", 2: "QSA_ERR_BAD_SHAPE", 3: "QS
 
 EXPORTS = [
     "qsa_indexer_prefill", "qsa_sparse_prefill", "qsa_indexer_decode", "qsa_sparse_decode",
-    "qsa_indexer_decode_noalloc", "qsa_qkv_front_end",
+    "qsa_indexer_decode_noalloc", "qsa_qkv_front_end", "qsa_indexer_chunk", "qsa_sparse_chunk",
+    "qsa_indexer_chunk_workspace_bytes",
     "qsa_indexer_prefill_workspace_bytes", "qsa_indexer_decode_workspace_bytes",
     "qsa_sparse_decode_partial_o_elems", "qsa_sparse_decode_partial_stats_elems",
     "qsa_sparse_decode_default_splits", "qsa_status_string",
@@ -87,6 +88,23 @@ class IndexerDecodeParams(ctypes.Structure):
                 ("top_k", _i32), ("cfg", QsaIndexerConfig), ("dtype", ctypes.c_int), ("stream", _vp)]
 
 
+class IndexerChunkParams(ctypes.Structure):
+    _fields_ = [("idx_q", _vp), ("idx_k", _vp), ("q_norm_w", _vp), ("k_norm_w", _vp), ("kv_pool", _vp),
+                ("page_table", _vp), ("start_positions", _vp), ("context_lengths", _vp), ("indices", _vp),
+                ("workspace", _vp), ("workspace_bytes", _sz), ("batch", _i32), ("chunk_len", _i32),
+                ("num_kv_heads", _i32), ("head_dim", _i32), ("pool_head_dim", _i32), ("num_flat_pages", _i32),
+                ("max_pages_per_seq", _i32), ("top_k", _i32), ("cfg", QsaIndexerConfig), ("dtype", ctypes.c_int),
+                ("stream", _vp)]
+
+
+class SparseChunkParams(ctypes.Structure):
+    _fields_ = [("q", _vp), ("o", _vp), ("kv_pool", _vp), ("page_table", _vp), ("indices", _vp),
+                ("start_positions", _vp), ("context_lengths", _vp), ("batch", _i32), ("chunk_len", _i32),
+                ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32), ("pool_head_dim", _i32),
+                ("num_flat_pages", _i32), ("max_pages_per_seq", _i32), ("top_k", _i32), ("attention_scale", _f32),
+                ("dtype", ctypes.c_int), ("stream", _vp)]
+
+
 class QsaError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} returned {STATUS.get(status, status)}")
@@ -108,7 +126,8 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     for name, st in (("qsa_indexer_prefill", IndexerPrefillParams), ("qsa_sparse_prefill", SparsePrefillParams),
                      ("qsa_indexer_decode", IndexerDecodeParams), ("qsa_sparse_decode", SparseDecodeParams),
-                     ("qsa_indexer_decode_noalloc", IndexerDecodeParams), ("qsa_qkv_front_end", FrontEndParams)):
+                     ("qsa_indexer_decode_noalloc", IndexerDecodeParams), ("qsa_qkv_front_end", FrontEndParams),
+                     ("qsa_indexer_chunk", IndexerChunkParams), ("qsa_sparse_chunk", SparseChunkParams)):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.POINTER(st)]
         fn.restype = ctypes.c_int
@@ -116,6 +135,8 @@ def load() -> ctypes.CDLL:
     lib.qsa_indexer_prefill_workspace_bytes.restype = _sz
     lib.qsa_indexer_decode_workspace_bytes.argtypes = [ctypes.POINTER(QsaIndexerConfig), _i32, _i32]
     lib.qsa_indexer_decode_workspace_bytes.restype = _sz
+    lib.qsa_indexer_chunk_workspace_bytes.argtypes = [ctypes.POINTER(QsaIndexerConfig), _i32, _i32, _i32]
+    lib.qsa_indexer_chunk_workspace_bytes.restype = _sz
     lib.qsa_sparse_decode_partial_o_elems.argtypes = [_i32, _i32, _i32]
     lib.qsa_sparse_decode_partial_o_elems.restype = _sz
     lib.qsa_sparse_decode_partial_stats_elems.argtypes = [_i32, _i32]
@@ -267,3 +288,32 @@ def qsa_qkv_front_end(qkv, q_gamma, k_gamma, context_lengths, q_out, num_q_heads
                        page_table.shape[-1] if page_table is not None else 0, float(rope_theta), float(rms_eps),
                        _dtype_code(qkv), _stream(stream))
     _check("qsa_qkv_front_end", load().qsa_qkv_front_end(ctypes.byref(p)))
+
+
+def qsa_indexer_chunk_workspace_bytes(cfg: QsaIndexerConfig, batch: int, chunk_len: int, max_pages_per_seq: int) -> int:
+    return int(load().qsa_indexer_chunk_workspace_bytes(ctypes.byref(cfg), batch, chunk_len, max_pages_per_seq))
+
+
+def qsa_indexer_chunk(idx_q, idx_k, q_norm_w, k_norm_w, kv_pool, page_table, start_positions, context_lengths,
+                      indices, workspace, cfg: QsaIndexerConfig, head_dim: int, stream=None) -> None:
+    """idx_q [B,C,Hi,hd]; idx_k [B,C,hd]; start_positions / context_lengths int32 [B] (past / total lengths);
+    indices int32 [B,C,top_k]; kv_pool updated in place (head-0 tails only)."""
+    B, C = idx_k.shape[0], idx_k.shape[1]
+    p = IndexerChunkParams(_ptr(idx_q), _ptr(idx_k), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(kv_pool), _ptr(page_table),
+                           _ptr(start_positions), _ptr(context_lengths), _ptr(indices), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), B, C, kv_pool.shape[2], head_dim,
+                           kv_pool.shape[3], kv_pool.shape[0], page_table.shape[-1], indices.shape[-1], cfg,
+                           _dtype_code(idx_q), _stream(stream))
+    _check("qsa_indexer_chunk", load().qsa_indexer_chunk(ctypes.byref(p)))
+
+
+def qsa_sparse_chunk(q, o, kv_pool, page_table, indices, start_positions, context_lengths, attention_scale: float,
+                     head_dim: int | None = None, stream=None) -> None:
+    """q, o [B,C,Hq,D]; indices int32 [B,C,top_k]; K/V of every position read through the page table."""
+    B, C, Hq, D = q.shape
+    D = head_dim or D
+    p = SparseChunkParams(_ptr(q), _ptr(o), _ptr(kv_pool), _ptr(page_table), _ptr(indices), _ptr(start_positions),
+                          _ptr(context_lengths), B, C, Hq, kv_pool.shape[2], D, kv_pool.shape[3], kv_pool.shape[0],
+                          page_table.shape[-1], indices.shape[-1], float(attention_scale), _dtype_code(q),
+                          _stream(stream))
+    _check("qsa_sparse_chunk", load().qsa_sparse_chunk(ctypes.byref(p)))

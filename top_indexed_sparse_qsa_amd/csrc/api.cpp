@@ -73,6 +73,33 @@ DecodeWs decode_ws(const qsa_indexer_config &c, int32_t B, int32_t max_pages) {
   return w;
 }
 
+// Chunk indexer workspace: fp32 queries | 16-bit kbar of every block a
+// sequence may hold | fp32 score rows.
+struct ChunkWs {
+  size_t qhat, kbar, scores, total;
+  int gmax, stride;
+};
+ChunkWs chunk_ws(const qsa_indexer_config &c, int32_t B, int32_t C, int32_t max_pages) {
+  ChunkWs w{};
+  w.gmax = max_pages * QSA_PAGE_TOKENS / c.compress_ratio;
+  w.stride = (int)round16((size_t)(w.gmax > 0 ? w.gmax : 1));
+  w.qhat = 0;
+  w.kbar = align_up((size_t)B * C * c.num_heads * c.head_dim * 4);
+  w.scores = w.kbar + align_up((size_t)B * w.gmax * c.head_dim * 2);
+  w.total = w.scores + align_up((size_t)B * C * w.stride * 4);
+  return w;
+}
+
+int default_splits_rows(int64_t rows, int32_t hkv, int32_t top_k) {
+  const int chunks = (top_k + 31) / 32;
+  const int64_t pairs = rows * hkv;
+  int64_t want = (1024 + pairs - 1) / pairs;
+  if (want > qsa::kDecWaves) want = qsa::kDecWaves;
+  if (want > chunks) want = chunks;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
 int default_splits(int32_t B, int32_t hkv, int32_t top_k) {
   const int chunks = (top_k + 31) / 32;
   const int pairs = B * hkv;
@@ -235,6 +262,8 @@ qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
   a.part_o = p->partial_o;
   a.part_stats = p->partial_stats;
   a.B = p->batch;
+  a.C = 1;
+  a.start = nullptr;
   a.Hq = p->num_q_heads;
   a.Hkv = p->num_kv_heads;
   a.G = p->num_q_heads / p->num_kv_heads;
@@ -248,6 +277,139 @@ qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
   a.ngroups = ngroups;
   a.sl2 = p->attention_scale * qsa::kLog2e;
   return launched(qsa::launch_sparse_decode(a, p->head_dim, (int)p->dtype, (hipStream_t)p->stream));
+}
+
+size_t qsa_indexer_chunk_workspace_bytes(const qsa_indexer_config *cfg, int32_t batch, int32_t chunk_len,
+                                          int32_t max_pages) {
+  if (!cfg || check_cfg(*cfg) != QSA_OK || batch < 1 || chunk_len < 1 || max_pages < 1) return 0;
+  return chunk_ws(*cfg, batch, chunk_len, max_pages).total;
+}
+
+qsa_status qsa_sparse_chunk(const qsa_sparse_chunk_params *p) {
+  if (!p || !p->q || !p->o || !p->kv_pool || !p->page_table || !p->indices || !p->context_lengths ||
+      !p->start_positions)
+    return QSA_ERR_NULL_POINTER;
+  if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
+  if (p->batch < 1 || p->chunk_len < 1 || p->top_k < 1 || p->num_flat_pages < 1 || p->max_pages_per_seq < 1)
+    return QSA_ERR_BAD_SHAPE;
+  if (qsa_status st = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim)) return st;
+  if (p->pool_head_dim < p->head_dim || (p->pool_head_dim % 8) != 0) return QSA_ERR_BAD_SHAPE;
+  if (!all_aligned16(p->q, p->o, p->kv_pool)) return QSA_ERR_BAD_SHAPE;
+  if (p->max_pages_per_seq > 4096) return QSA_ERR_UNSUPPORTED;
+  if ((int64_t)p->batch * p->chunk_len * p->num_kv_heads > (int64_t)INT32_MAX / 2) return QSA_ERR_UNSUPPORTED;
+  if (!isfinite(p->attention_scale) || !(p->attention_scale > 0.f)) return QSA_ERR_BAD_SHAPE;
+  int splits = default_splits_rows((int64_t)p->batch * p->chunk_len, p->num_kv_heads, p->top_k);
+  const int chunks = (p->top_k + 31) / 32;
+  const int per = (chunks + splits - 1) / splits;
+  splits = (chunks + per - 1) / per;
+  qsa::DecodeAttnArgs a{};
+  a.q = static_cast<const uint16_t *>(p->q);
+  a.o = static_cast<uint16_t *>(p->o);
+  a.pool = static_cast<const uint16_t *>(p->kv_pool);
+  a.pt = p->page_table;
+  a.indices = p->indices;
+  a.ctx = p->context_lengths;
+  a.part_o = nullptr;
+  a.part_stats = nullptr;
+  a.B = p->batch;
+  a.C = p->chunk_len;
+  a.start = p->start_positions;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads;
+  a.PHD = p->pool_head_dim;
+  a.num_flat_pages = p->num_flat_pages;
+  a.max_pages = p->max_pages_per_seq;
+  a.top_k = p->top_k;
+  a.nsplits = splits;
+  a.split_slots = per * 32;
+  a.wpg = splits;  // at most kDecWaves: one workgroup per (row, KV head)
+  a.ngroups = 1;
+  a.sl2 = p->attention_scale * qsa::kLog2e;
+  return launched(qsa::launch_sparse_decode(a, p->head_dim, (int)p->dtype, (hipStream_t)p->stream));
+}
+
+qsa_status qsa_indexer_chunk(const qsa_indexer_chunk_params *p) {
+  if (!p || !p->idx_q || !p->idx_k || !p->q_norm_w || !p->k_norm_w || !p->kv_pool || !p->page_table ||
+      !p->context_lengths || !p->start_positions || !p->indices || !p->workspace)
+    return QSA_ERR_NULL_POINTER;
+  if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
+  if (qsa_status st = check_cfg(p->cfg)) return st;
+  if (p->batch < 1 || p->chunk_len < 1 || p->num_kv_heads < 1 || p->num_flat_pages < 1 || p->max_pages_per_seq < 1)
+    return QSA_ERR_BAD_SHAPE;
+  if (p->head_dim < 1 || p->pool_head_dim < p->head_dim + p->cfg.head_dim || (p->head_dim % 8) != 0 ||
+      (p->pool_head_dim % 8) != 0)
+    return QSA_ERR_BAD_SHAPE;
+  if (p->top_k < min_top_k(p->cfg)) return QSA_ERR_BAD_SHAPE;
+  if ((int64_t)p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio > QSA_MAX_BLOCKS)
+    return QSA_ERR_UNSUPPORTED;
+  const int gmax = p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio;
+  if ((int64_t)p->batch * ((int64_t)p->chunk_len + gmax + 1) > (int64_t)INT32_MAX / 2) return QSA_ERR_UNSUPPORTED;
+  if ((int64_t)p->batch * p->chunk_len > (int64_t)INT32_MAX / 2) return QSA_ERR_UNSUPPORTED;
+  if (!all_aligned16(p->idx_q, p->idx_k, p->kv_pool)) return QSA_ERR_BAD_SHAPE;
+  if (((uintptr_t)p->workspace % kAlign) != 0) return QSA_ERR_BAD_SHAPE;
+  const ChunkWs w = chunk_ws(p->cfg, p->batch, p->chunk_len, p->max_pages_per_seq);
+  if (p->workspace_bytes < w.total) return QSA_ERR_WORKSPACE_TOO_SMALL;
+  char *ws = static_cast<char *>(p->workspace);
+  const hipStream_t s = (hipStream_t)p->stream;
+  const int dt = (int)p->dtype;
+
+  qsa::IdxChunkPrepArgs pa{};
+  pa.idx_q = static_cast<const uint16_t *>(p->idx_q);
+  pa.idx_k = static_cast<const uint16_t *>(p->idx_k);
+  pa.wq = p->q_norm_w;
+  pa.wk = p->k_norm_w;
+  pa.pool = static_cast<uint16_t *>(p->kv_pool);
+  pa.pt = p->page_table;
+  pa.ctx = p->context_lengths;
+  pa.start = p->start_positions;
+  pa.qhat = reinterpret_cast<float *>(ws + w.qhat);
+  pa.kbar = reinterpret_cast<uint16_t *>(ws + w.kbar);
+  pa.B = p->batch;
+  pa.C = p->chunk_len;
+  pa.Hi = p->cfg.num_heads;
+  pa.hd = p->cfg.head_dim;
+  pa.rot = p->cfg.rot_dim;
+  pa.ratio = p->cfg.compress_ratio;
+  pa.Hkv = p->num_kv_heads;
+  pa.D = p->head_dim;
+  pa.PHD = p->pool_head_dim;
+  pa.num_flat_pages = p->num_flat_pages;
+  pa.max_pages = p->max_pages_per_seq;
+  pa.Gmax = w.gmax;
+  pa.theta = (double)p->cfg.rope_theta;
+  pa.eps = (double)p->cfg.rms_eps;
+  pa.dt = dt;
+  if (qsa::launch_idx_chunk_prep(pa, s) != hipSuccess) return QSA_ERR_LAUNCH;
+
+  qsa::IdxScoreArgs sa{};
+  sa.qhat = pa.qhat;
+  sa.kbar = pa.kbar;
+  sa.scores = reinterpret_cast<float *>(ws + w.scores);
+  sa.ctx = p->context_lengths;
+  sa.start = p->start_positions;
+  sa.B = p->batch;
+  sa.S = p->chunk_len;
+  sa.Hi = p->cfg.num_heads;
+  sa.Gmax = w.gmax;
+  sa.stride = w.stride;
+  sa.ratio = p->cfg.compress_ratio;
+  if (qsa::launch_idx_score(sa, dt, s) != hipSuccess) return QSA_ERR_LAUNCH;
+
+  qsa::IdxSelectArgs xa{};
+  xa.scores = sa.scores;
+  xa.row_stride = w.stride;
+  xa.out = p->indices;
+  xa.ctx = p->context_lengths;
+  xa.start = p->start_positions;
+  xa.B = p->batch;
+  xa.S = p->chunk_len;
+  xa.top_k = p->top_k;
+  xa.budget = p->cfg.budget;
+  xa.ratio = p->cfg.compress_ratio;
+  xa.decode = 0;
+  xa.max_ctx = p->max_pages_per_seq * QSA_PAGE_TOKENS;
+  return launched(qsa::launch_idx_select(xa, gmax, s));
 }
 
 qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p) {

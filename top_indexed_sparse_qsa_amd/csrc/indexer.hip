@@ -162,6 +162,98 @@ __global__ __launch_bounds__(256) void idx_handoff_kernel(IdxPrepArgs a) {
   }
 }
 
+// Chunked prefill, step 1: the indexer state the chunk's rows score against.
+// Chunk row t of sequence b sits at position start[b] + t.  Wave items:
+//   * (b, t), t < C: the queries of a live row at its position -> qhat;
+//   * (b, g), g < Gmax: every complete block g < ctx/ratio into the dense
+//     kbar workspace -- copied from its V-row tail when it was complete
+//     before the chunk, else pooled from the raw keys of its tokens (the
+//     stored K-row tails of tokens before the chunk, the chunk's idx_k for
+//     the rest) and also stored in its V-row tail;
+//   * (b, Gmax): the chunk's tokens of the trailing incomplete block -> their
+//     raw keys into their K-row tails.
+// The tails these items read (V rows of blocks complete before the chunk, K
+// rows of tokens before it) and those they write are disjoint.
+__global__ __launch_bounds__(256) void idx_chunk_prep_kernel(IdxChunkPrepArgs a) {
+  const double *s_freq = a.freq;
+  const int lane = lane_id();
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long per_seq = (long long)a.C + a.Gmax + 1;
+  if (item >= (long long)a.B * per_seq) return;
+  const int b = (int)(item / per_seq), k = (int)(item % per_seq);
+  const int P = a.start[b];
+  if (P < 0) return;
+  // positions past the chunk have no keys here (a total length past
+  // start + C breaks the contract): they are treated as absent
+  const int ctx = (int)min((long long)min(a.ctx[b], a.max_pages * 128), (long long)P + a.C);
+  if (ctx <= P) return;
+  const int32_t *ptk = a.pt + (size_t)b * 2 * a.max_pages, *ptv = ptk + a.max_pages;
+  const int r = a.ratio;
+  double o0, o1;
+  if (k < a.C) {  // queries of row k
+    const int pos = P + k;
+    if (pos >= ctx) return;
+    const Rope2 rp = rope_at((double)pos, s_freq, a.rot);
+    for (int h = 0; h < a.Hi; ++h) {
+      const size_t off = (((size_t)b * a.C + k) * a.Hi + h) * 128;
+      norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
+                 (double)a.wq[lane], (double)a.wq[lane + 64], a.eps, a.rot, rp, o0, o1);
+      a.qhat[off + lane] = (float)o0;
+      a.qhat[off + 64 + lane] = (float)o1;
+    }
+    return;
+  }
+  const int nc = ctx / r;
+  if (k < a.C + a.Gmax) {  // block g
+    const int g = k - a.C;
+    if (g >= nc) return;
+    uint16_t *kb = a.kbar + ((size_t)b * a.Gmax + g) * 128;
+    const long long ov = pool_row_off(ptv, r * g, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
+    if (r * g + r <= P) {  // complete before the chunk: its tail holds kbar
+      kb[lane] = ov >= 0 ? a.pool[ov + a.D + lane] : 0;
+      kb[lane + 64] = ov >= 0 ? a.pool[ov + a.D + 64 + lane] : 0;
+      return;
+    }
+    double m0 = 0.0, m1 = 0.0;
+    bool ok = true;
+    for (int j = 0; j < r; ++j) {
+      const int tok = r * g + j;
+      if (tok < P) {
+        const long long o = pool_row_off(ptk, tok, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
+        ok = ok && o >= 0;
+        if (o >= 0) {
+          m0 += bits_to_f64(a.pool[o + a.D + lane], a.dt);
+          m1 += bits_to_f64(a.pool[o + a.D + 64 + lane], a.dt);
+        }
+      } else {
+        const size_t off = ((size_t)b * a.C + (tok - P)) * 128;
+        m0 += bits_to_f64(a.idx_k[off + lane], a.dt);
+        m1 += bits_to_f64(a.idx_k[off + 64 + lane], a.dt);
+      }
+    }
+    m0 /= (double)r;
+    m1 /= (double)r;
+    const Rope2 rp = rope_at((double)(r * g), s_freq, a.rot);
+    norm_rope2(m0, m1, (double)a.wk[lane], (double)a.wk[lane + 64], a.eps, a.rot, rp, o0, o1);
+    const uint16_t k0 = (uint16_t)f64_to_bits(o0, a.dt), k1 = (uint16_t)f64_to_bits(o1, a.dt);
+    kb[lane] = k0;
+    kb[lane + 64] = k1;
+    if (ok && ov >= 0) {
+      a.pool[ov + a.D + lane] = k0;
+      a.pool[ov + a.D + 64 + lane] = k1;
+    }
+    return;
+  }
+  // the chunk's tokens of the trailing incomplete block
+  for (int tok = max(P, r * nc); tok < ctx; ++tok) {
+    const long long o = pool_row_off(ptk, tok, a.max_pages, a.num_flat_pages, a.Hkv, a.PHD);
+    if (o < 0) continue;
+    const uint16_t *src = a.idx_k + ((size_t)b * a.C + (tok - P)) * 128;
+    a.pool[o + a.D + lane] = src[lane];
+    a.pool[o + a.D + 64 + lane] = src[lane + 64];
+  }
+}
+
 // fp32 -> exact sum of NP 16-bit pieces (two fp16 or three bf16).
 template <int DT>
 struct QSplit {
@@ -222,9 +314,13 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
   if (grp >= (long long)a.B * T32) return;
   const int b = (int)(grp % a.B);
   const int tg = 32 * (T32 - 1 - (int)(grp / a.B));
-  const int live = min(a.ctx[b], a.S);
+  // row t sits at position off + t; rows [0, live) are live
+  const int off = a.start ? a.start[b] : 0;
+  // positions stay below Gmax * ratio, the blocks the kbar rows hold
+  const int lim = a.start ? min(a.ctx[b], a.Gmax * a.ratio) : a.ctx[b];
+  const int live = max(0, min(lim - off, a.S));
   if (tg >= live) return;
-  const int nc_hi = (min(tg + 31, live - 1) + 1) / a.ratio;
+  const int nc_hi = (off + min(tg + 31, live - 1) + 1) / a.ratio;
   const int run_lo = run * a.run_chunks * CB;
   const int run_hi = min(run_lo + a.run_chunks * CB, nc_hi);
   if (run_lo >= run_hi) return;
@@ -271,7 +367,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
       for (int p = 0; p < NP; ++p) qa[m][p][ks] = pieces[p];
     }
   }
-  const int nc_wave = t0 < live ? (min(t0 + 7, live - 1) + 1) / a.ratio : 0;
+  const int nc_wave = t0 < live ? (off + min(t0 + 7, live - 1) + 1) / a.ratio : 0;
   // score stores: thread tid owns columns 4 (tid % 32) .. +3 of rows tid / 32 + 8 j
   static_assert(CB == 128, "store mapping assumes 32 float4 columns per chunk");
   const int st_row0 = tid >> 5, st_c4 = 4 * (tid & 31);
@@ -279,7 +375,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = tg + st_row0 + 8 * j;
-    st_nc[j] = t < live ? (t + 1) / a.ratio : 0;
+    st_nc[j] = t < live ? (off + t + 1) / a.ratio : 0;
   }
   float *const st_base = a.scores + ((size_t)b * a.S + tg + st_row0) * a.stride;
 
@@ -663,10 +759,12 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
   } else {
     const int rw = a.row0 + blockIdx.x;  // longest rows first
     b = rw % a.B;
-    t = a.S - 1 - rw / a.B;
-    live = t < min(a.ctx[b], a.S);
-    out = a.out + ((size_t)b * a.S + t) * a.top_k;
-    srow = a.scores + ((size_t)b * a.S + t) * a.row_stride;
+    const int tl = a.S - 1 - rw / a.B;   // the row; its position is off + tl
+    const int off = a.start ? a.start[b] : 0;
+    t = off + tl;
+    live = t >= 0 && t < min(a.ctx[b], a.max_ctx);
+    out = a.out + ((size_t)b * a.S + tl) * a.top_k;
+    srow = a.scores + ((size_t)b * a.S + tl) * a.row_stride;
   }
   if (!live) {
     for (int i = tid; i < a.top_k; i += NT) out[i] = -1;
@@ -1075,6 +1173,12 @@ hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) 
     launch_select_wg_for(a, nc_max, 0, (unsigned)a.B, s);
     return hipGetLastError();
   }
+  if (a.start) {
+    // chunk rows: their positions are device data, so the rows cannot be
+    // sorted into length classes on the host; one workgroup each
+    launch_select_wg_for(a, nc_max, 0, (unsigned)((long long)a.B * a.S), s);
+    return hipGetLastError();
+  }
   // Prefill rows go longest first (row = (S - 1 - t) * B + b), so rows whose
   // complete-block count nc = (t + 1) / ratio exceeds K are the first
   // rows_from(K) rows.  Each length class gets the kernel that fits it.
@@ -1101,6 +1205,14 @@ hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) 
   launch_select_rows<64, 1>(a, n_wg + n_long, n64, s);
   launch_select_rows<32, 1>(a, n_wg + n_long + n64, n32, s);
   launch_select_rows<16, 1>(a, n_wg + n_long + n64 + n32, n16, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_idx_chunk_prep(const IdxChunkPrepArgs &a_in, hipStream_t s) {
+  IdxChunkPrepArgs a = a_in;
+  fill_freq(a.freq, a.rot, a.theta);
+  const long long waves = (long long)a.B * ((long long)a.C + a.Gmax + 1);
+  hipLaunchKernelGGL(idx_chunk_prep_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -36,6 +36,10 @@ struct DecodeAttnArgs {
   const int32_t *pt, *indices, *ctx;
   float *part_o, *part_stats;  // [pairs * kDecMaxGroups][16][D], [..][2][16]
   int B, Hq, Hkv, G, PHD, num_flat_pages, max_pages, top_k;
+  // rows per sequence: 1 in decode (live when ctx > 0); C for a chunk, whose
+  // row r of sequence b is live when start[b] + r < ctx[b]
+  int C;
+  const int32_t *start;
   int nsplits, split_slots;  // split s covers list slots [s*split_slots, (s+1)*split_slots)
   int wpg, ngroups;          // splits (waves) per workgroup, workgroups per (sequence, KV head)
   float sl2;
@@ -72,6 +76,7 @@ struct IdxScoreArgs {
   const uint16_t *kbar;
   float *scores;    // [B,S,stride]
   const int32_t *ctx;
+  const int32_t *start;  // row t of sequence b sits at position start[b] + t (null: t)
   int B, S, Hi, Gmax, stride, ratio;
   int nchunk;       // chunk runs per 32-row group (set by the launcher)
   int run_chunks;   // chunks per run (set by the launcher)
@@ -85,6 +90,7 @@ struct IdxSelectArgs {
   long long row_stride;
   int32_t *out;
   const int32_t *ctx;
+  const int32_t *start;  // prefill rows: row t of sequence b sits at position start[b] + t (null: t)
   int B, S;            // prefill: rows B*S; decode: rows B (S unused)
   int top_k, budget, ratio;
   int decode;          // 1: row of sequence b is position ctx[b]-1
@@ -109,6 +115,23 @@ struct IdxDecScoreArgs {
   int dt;
   double freq[64];     // RoPE frequencies theta^(-2i/rot), i < rot/2 (set by the launcher)
 };
+
+// Chunked prefill, indexer step 1 (queries, kbar of every complete block,
+// the chunk's tail writes).
+struct IdxChunkPrepArgs {
+  const uint16_t *idx_q, *idx_k;   // [B,C,Hi,hd], [B,C,hd]
+  const float *wq, *wk;
+  uint16_t *pool;
+  const int32_t *pt, *ctx, *start;
+  float *qhat;                     // [B,C,Hi,hd]
+  uint16_t *kbar;                  // [B,Gmax,hd]
+  int B, C, Hi, hd, rot, ratio, Hkv, D, PHD, num_flat_pages, max_pages, Gmax;
+  double theta, eps;
+  int dt;
+  double freq[64];                 // set by the launcher
+};
+
+hipError_t launch_idx_chunk_prep(const IdxChunkPrepArgs &a, hipStream_t s);
 
 // Fused front end (packed QKV -> Q, K/V mirrors, pool rows).
 struct FrontEndArgs {

@@ -962,8 +962,9 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + sizeof(DecMergeLds<D>));  // [2][max_pages]
   const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int group = blockIdx.x % a.ngroups;
-  const int pair = blockIdx.x / a.ngroups;
-  const int b = pair / a.Hkv, kvh = pair % a.Hkv;
+  const int pair = blockIdx.x / a.ngroups;  // (query row, KV head)
+  const int br = pair / a.Hkv, kvh = pair % a.Hkv;
+  const int b = br / a.C, row = br % a.C;
   const int split = group * a.wpg + wv;
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   // Everything the walk needs first is issued at once -- the first two
@@ -972,13 +973,14 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   // one round trip precedes the first gathers.
   const int s0 = split * a.split_slots;
   const int n_slots = split < a.nsplits ? min(a.top_k - s0, a.split_slots) : 0;
-  const int32_t *list = a.indices + (size_t)b * a.top_k + s0;
+  const int32_t *list = a.indices + (size_t)br * a.top_k + s0;
   const int sl = lane & 31;
   const int id_a = sl < n_slots ? list[sl] : -1;
   const int id_b = sl + 32 < n_slots ? list[sl + 32] : -1;
   u32x4 qf[D / 32];
-  load_q<D>(qf, a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
+  load_q<D>(qf, a.q + ((size_t)br * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
   const int ctx_in = a.ctx[b];
+  const int pos = a.start ? a.start[b] + row : ctx_in - 1;  // the row's position
   {
     const int32_t *ptb = a.pt + (size_t)b * 2 * a.max_pages;  // rows 0 and 1 are contiguous
     const int npt = 2 * a.max_pages;
@@ -1004,7 +1006,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  if (ctx > 0 && n_slots > 0) {
+  if (ctx > 0 && n_slots > 0 && pos >= 0 && pos < ctx_in) {
     PagedKV kv;
     kv.pool = a.pool + (size_t)kvh * a.PHD;
     kv.pk = s_pt;
@@ -1058,7 +1060,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       for (int j = 0; j < ND; ++j) o[j] += src[j] * sc[w];
     }
     if (a.ngroups == 1) {
-      uint16_t *out = a.o + ((size_t)b * a.Hq + (size_t)kvh * a.G + r16) * D + d0;
+      uint16_t *out = a.o + ((size_t)br * a.Hq + (size_t)kvh * a.G + r16) * D + d0;
 #pragma unroll
       for (int j = 0; j < ND; j += 2)
         *reinterpret_cast<uint32_t *>(out + j) =
@@ -1078,8 +1080,8 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 // Merges the workgroup partials of one (sequence, KV head) in group order.
 template <int D, int DT>
 __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs a) {
-  const int pair = blockIdx.x;
-  const int b = pair / a.Hkv, kvh = pair % a.Hkv;
+  const int pair = blockIdx.x;  // (query row, KV head)
+  const int br = pair / a.Hkv, kvh = pair % a.Hkv;
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   if (r16 >= a.G) return;
   constexpr int NDL = D / 4;  // dims per lane
@@ -1105,7 +1107,7 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t *out = a.o + ((size_t)b * a.Hq + (size_t)kvh * a.G + r16) * D + d0;
+  uint16_t *out = a.o + ((size_t)br * a.Hq + (size_t)kvh * a.G + r16) * D + d0;
 #pragma unroll
   for (int j = 0; j < NDL; j += 8) {
     u32x4 w;
@@ -1238,7 +1240,7 @@ hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStr
 
 template <int D, int DT>
 static hipError_t launch_decode_t(const DecodeAttnArgs &a, hipStream_t s) {
-  const unsigned pairs = (unsigned)(a.B * a.Hkv);
+  const unsigned pairs = (unsigned)((long long)a.B * a.C * a.Hkv);
   const size_t lds = sizeof(DecMergeLds<D>) + (size_t)2 * a.max_pages * sizeof(int32_t);
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_decode_kernel<D, DT>),
