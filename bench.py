@@ -74,6 +74,7 @@ def parse():
                     help="comma list of workloads to run (4 = decode); the headline always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-front-end", action="store_true", help="skip the fused front end measurement")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -355,6 +356,78 @@ def front_end_bench(args, Q, torch, syn):
 
 
 # ---------------------------------------------------------------------------
+# chunked prefill: the long prefill's last 2048 tokens as one chunk over the
+# paged pool (the earlier 30720 tokens' K/V and indexer state already there)
+# ---------------------------------------------------------------------------
+CHUNK_PAST, CHUNK_LEN = 30720, 2048
+
+
+def chunk_bench(inp, args, Q, torch, syn):
+    icfg = inp.icfg
+    e = 2
+    stream = torch.cuda.current_stream()
+    B, S, P, C = inp.B, inp.S, CHUNK_PAST, CHUNK_LEN
+    pages = (S + 127) // 128
+    rng = np.random.default_rng(8)
+    perm = rng.permutation(B * pages).astype(np.int32)
+    pt = np.full((B, 2, pages), -1, dtype=np.int32)
+    for b in range(B):
+        pt[b, 0] = perm[b * pages:(b + 1) * pages]
+        pt[b, 1] = pt[b, 0] + B * pages
+    ptd = dev(pt)
+    # the pool: K/V of every position (leading columns) and the indexer state
+    # of the first P tokens in the tails, laid down by the library itself
+    pool = torch.zeros((2 * B * pages, 128, inp.Hkv, inp.D + icfg.head_dim), dtype=torch.float16, device="cuda")
+    kd, vd = dev(inp.k, inp.dtype), dev(inp.v, inp.dtype)
+    tok = torch.arange(S, device="cuda")
+    for b in range(B):
+        pool[ptd[b, 0, tok // 128].long(), tok % 128, :, :inp.D] = kd[b]
+        pool[ptd[b, 1, tok // 128].long(), tok % 128, :, :inp.D] = vd[b]
+    del kd, vd
+    cfg = cfg_struct(Q, icfg)
+    start = dev(np.full(B, P, dtype=np.int32))
+    ctx = dev(np.full(B, S, dtype=np.int32))
+    iq_all, ik_all = dev(inp.idx_q, inp.dtype), dev(inp.idx_k, inp.dtype)
+    wq, wk = dev(inp.w_q), dev(inp.w_k)
+    wsp = torch.empty(Q.qsa_indexer_prefill_workspace_bytes(cfg, B, P), dtype=torch.uint8, device="cuda")
+    lp = torch.empty((B, P, icfg.top_k), dtype=torch.int32, device="cuda")
+    Q.qsa_indexer_prefill(iq_all[:, :P].contiguous(), ik_all[:, :P].contiguous(), wq, wk, start, lp, wsp, cfg,
+                          stream=stream, kv_pool=pool, page_table=ptd, head_dim=inp.D)
+    torch.cuda.synchronize()
+    del wsp, lp
+    iq, ik = iq_all[:, P:].contiguous(), ik_all[:, P:].contiguous()
+    q = dev(np.ascontiguousarray(inp.q[:, P:]), inp.dtype)
+    o = torch.empty_like(q)
+    lists = torch.empty((B, C, icfg.top_k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(Q.qsa_indexer_chunk_workspace_bytes(cfg, B, C, pages), dtype=torch.uint8, device="cuda")
+
+    def step(mark):
+        if mark:
+            mark(0)
+        Q.qsa_indexer_chunk(iq, ik, wq, wk, pool, ptd, start, ctx, lists, ws, cfg, inp.D, stream=stream)
+        if mark:
+            mark(1)
+        Q.qsa_sparse_chunk(q, o, pool, ptd, lists, start, ctx, inp.scale, head_dim=inp.D, stream=stream)
+        if mark:
+            mark(2)
+
+    wall, (idx_ms, attn_ms) = timed_loops(step, args.steps, args.warmup, stream, torch, 3)
+    n_entries = int((lists >= 0).sum().item())
+    attn_flops = n_entries * inp.Hq * inp.D * 4
+    out = {"workload": f"chunked prefill over the paged pool: the last {C} tokens of the long prefill (B=1 "
+                       f"S=32768 Hq=32 Hkv=4 D=128 fp16) after {P} prefilled ones, topK 2051",
+           "value": B * C / (wall / args.steps), "unit": "tokens/s", "ms_per_step": wall / args.steps * 1e3,
+           "indexer_ms": idx_ms, "attention_ms": attn_ms,
+           "attention": {"kernel": "qsa_sparse_chunk", "bound": "mfma",
+                         "achieved": attn_flops / (attn_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": attn_flops / (attn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+                         "algorithmic_flops_per_call": attn_flops}}
+    del pool, q, o, lists, ws, iq_all, ik_all
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 # HBM counter figures
 # ---------------------------------------------------------------------------
 def kernel_code_sha256(path=None):
@@ -502,6 +575,7 @@ def main():
         sys.exit(2)
     Q.load()
     results = {}
+    chunk = None
     order = [args.headline] + [w for w in run if w != args.headline]
     for wl in order:
         inp = inp_of(wl)
@@ -511,6 +585,10 @@ def main():
         else:
             results[wl] = prefill_bench(wl, inp, args, Q, torch)
         note(f"workload {wl}: {results[wl]['ms_per_step']:.4f} ms/step")
+        if wl == 3 and not args.no_chunk:
+            note("chunked prefill")
+            chunk = chunk_bench(inp, args, Q, torch, syn)
+            note(f"chunked prefill: {chunk['ms_per_step']:.4f} ms/step")
         inputs.pop(wl, None)
     fe = None
     if not args.no_front_end:
@@ -561,6 +639,7 @@ def main():
         "workloads": {str(w): r for w, r in results.items() if w not in (args.headline, DECODE_WORKLOAD)},
         "decode": dec,
         "front_end": fe,
+        "chunk": chunk,
         "hbm_copy_gbs": copy_gbs,
     }
     print(json.dumps(line), flush=True)

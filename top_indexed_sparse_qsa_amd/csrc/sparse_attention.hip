@@ -941,26 +941,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // part each XCD has its own L2, and a kernel boundary is the cheap place to
 // make one workgroup's stores visible to another.
 
-// The K tiles are dead once every wave has finished its list (a workgroup
-// barrier separates the two uses), so the merge scratch overlays them.
+// LDS of a decode workgroup of nw waves, sized to nw: per wave a K tile
+// (32 rows of 256 B) during the walk; once every wave has finished its list
+// (a workgroup barrier separates the two uses) the merge scratch -- per wave
+// 16 rows of D + 4 floats of O, then the running max and sum of each row --
+// overlays the K tiles.  The page-table rows follow.
 template <int D>
-union DecMergeLds {
+struct DecLds {
   static constexpr int RS = D + 4;  // padded row stride (floats)
-  struct {
-    float acc[kDecWaves][16 * RS];
-    float m[kDecWaves][16];
-    float l[kDecWaves][16];
-  };
-  u32x4 ktile[kDecWaves][32 * 16];
+  static constexpr size_t kTile = 32 * 16 * sizeof(u32x4);
+  static constexpr size_t kMerge = (16 * RS + 2 * 16) * sizeof(float);
+  static constexpr size_t per_wave = kTile > kMerge ? kTile : kMerge;
+  static __host__ __device__ size_t bytes(int nw) { return per_wave * nw; }
+  unsigned char *base;
+  int nw;
+  __device__ u32x4 *ktile(int w) const { return reinterpret_cast<u32x4 *>(base + kTile * w); }
+  __device__ float *acc(int w) const { return reinterpret_cast<float *>(base) + (size_t)16 * RS * w; }
+  __device__ float *m(int w) const { return reinterpret_cast<float *>(base) + (size_t)16 * RS * nw + 16 * w; }
+  __device__ float *l(int w) const { return m(nw) + 16 * w; }
 };
 
 // Lane (q, r) of wave w merges row r, dims [d0, d0 + D/16).
 template <int D, int DT>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_decode_kernel(DecodeAttnArgs a) {
   extern __shared__ __align__(16) unsigned char s_raw[];
-  DecMergeLds<D> &mg = *reinterpret_cast<DecMergeLds<D> *>(s_raw);
-  int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + sizeof(DecMergeLds<D>));  // [2][max_pages]
   const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const DecLds<D> mg{s_raw, nw};
+  int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + DecLds<D>::bytes(nw));  // [2][max_pages]
   const int group = blockIdx.x % a.ngroups;
   const int pair = blockIdx.x / a.ngroups;  // (query row, KV head)
   const int br = pair / a.Hkv, kvh = pair % a.Hkv;
@@ -1014,13 +1021,13 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     kv.row_stride = (size_t)a.Hkv * a.PHD;
     kv.num_flat_pages = a.num_flat_pages;
     kv.limit = ctx;
-    run_list_ids<D, DT>(list, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile[wv], id_a, id_b);
+    run_list_ids<D, DT>(list, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile(wv), id_a, id_b);
   }
   __syncthreads();  // every K tile is dead before the merge scratch is written
   float l = l_run + shfl_xor_f(l_run, 16);
   l += shfl_xor_f(l, 32);
   if (32 * q4 < D) {
-    float *dst = &mg.acc[wv][r16 * DecMergeLds<D>::RS + 32 * q4];
+    float *dst = mg.acc(wv) + r16 * DecLds<D>::RS + 32 * q4;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       *reinterpret_cast<f32x4 *>(dst + 8 * rr) = f32x4{acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]};
@@ -1028,8 +1035,8 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     }
   }
   if (q4 == 0) {
-    mg.m[wv][r16] = m_run;
-    mg.l[wv][r16] = l;
+    mg.m(wv)[r16] = m_run;
+    mg.l(wv)[r16] = l;
   }
   __syncthreads();
 
@@ -1038,13 +1045,13 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   // w*4+q + 4*nw, ...
   constexpr int ND = D / 16;
   float M = -INFINITY;
-  for (int w = 0; w < nw; ++w) M = fmaxf(M, mg.m[w][r16]);
+  for (int w = 0; w < nw; ++w) M = fmaxf(M, mg.m(w)[r16]);
   float L = 0.f, sc[kDecWaves];
 #pragma unroll
   for (int w = 0; w < kDecWaves; ++w) {
-    const float mw = w < nw ? mg.m[w][r16] : -INFINITY;
+    const float mw = w < nw ? mg.m(w)[r16] : -INFINITY;
     sc[w] = mw == -INFINITY ? 0.f : exp2f(mw - M);
-    L += w < nw ? mg.l[w][r16] * sc[w] : 0.f;
+    L += w < nw ? mg.l(w)[r16] * sc[w] : 0.f;
   }
   if (r16 >= a.G) return;
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -1055,7 +1062,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int j = 0; j < ND; ++j) o[j] = 0.f;
     for (int w = 0; w < nw; ++w) {
-      const float *src = &mg.acc[w][r16 * DecMergeLds<D>::RS + d0];
+      const float *src = mg.acc(w) + r16 * DecLds<D>::RS + d0;
 #pragma unroll
       for (int j = 0; j < ND; ++j) o[j] += src[j] * sc[w];
     }
@@ -1241,7 +1248,7 @@ hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStr
 template <int D, int DT>
 static hipError_t launch_decode_t(const DecodeAttnArgs &a, hipStream_t s) {
   const unsigned pairs = (unsigned)((long long)a.B * a.C * a.Hkv);
-  const size_t lds = sizeof(DecMergeLds<D>) + (size_t)2 * a.max_pages * sizeof(int32_t);
+  const size_t lds = DecLds<D>::bytes(a.wpg) + (size_t)2 * a.max_pages * sizeof(int32_t);
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_decode_kernel<D, DT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
