@@ -517,9 +517,11 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   }
   uint32_t *region = s_dyn + (NW == 1 ? wv : 0) * a.wave_words;
   uint32_t *hist = region;
-  // one wave: the list overlays the histogram; two waves: [hist | list0 | list1]
-  int32_t *lst0 = reinterpret_cast<int32_t *>(region + (NW == 1 ? 0 : kSelHistWords));
-  int32_t *lst = STAGE ? lst0 + h * a.list_words : out;
+  // Staged lists hold the kept block indices (16 bits: blocks < QSA_MAX_BLOCKS),
+  // a.list_words words per wave.  One wave: the list overlays the histogram;
+  // two waves: [hist | list0 | list1].  Unstaged: expanded ids go straight out.
+  uint16_t *lb0 = reinterpret_cast<uint16_t *>(region + (NW == 1 ? 0 : kSelHistWords));
+  uint16_t *lb = lb0 + 2 * h * a.list_words;
   const float *srow = a.scores + ((size_t)b * a.S + t) * a.row_stride;
   const int base_i = h * SPAN;
   uint32_t key[KPL];
@@ -682,11 +684,11 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         if (kc[c]) {
-          const int blk = r * (base_i + 256 * g + 4 * lane + c);
-          if (STAGE && r == 4) {
-            *reinterpret_cast<int4 *>(lst + 4 * pos) = make_int4(blk, blk + 1, blk + 2, blk + 3);
+          const int g_blk = base_i + 256 * g + 4 * lane + c;
+          if constexpr (STAGE) {
+            lb[pos] = (uint16_t)g_blk;
           } else {
-            for (int j = 0; j < r; ++j) lst[r * pos + j] = blk + j;
+            for (int j = 0; j < r; ++j) out[r * pos + j] = r * g_blk + j;
           }
           ++pos;
         }
@@ -699,9 +701,19 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   row_sync<NW>();
   const int head = r * a.budget;
   const int len = head + (t + 1) - r * nc;
-  const int k0 = NW == 2 ? r * s_x[0][2] : head;  // ids in the first wave's list
-  for (int i = (STAGE ? 0 : head) + tid; i < a.top_k; i += nthr)
-    out[i] = i < head ? (i < k0 ? lst0[i] : lst0[a.list_words + i - k0]) : (i < len ? r * nc + (i - head) : -1);
+  const int kb0 = NW == 2 ? s_x[0][2] : a.budget;  // blocks in the first wave's list
+  const uint16_t *lb1 = lb0 + 2 * a.list_words;
+  for (int i = (STAGE ? 0 : head) + tid; i < a.top_k; i += nthr) {
+    int v;
+    if (i < head) {  // staged: kept block j = i / r, expanded
+      const int j = r == 4 ? i >> 2 : i / r;
+      const int blk = j < kb0 ? lb0[j] : lb1[j - kb0];
+      v = r * blk + (i - r * j);
+    } else {
+      v = i < len ? r * nc + (i - head) : -1;
+    }
+    out[i] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1120,13 +1132,14 @@ static void launch_select_rows(IdxSelectArgs a, int row0, int nrows, hipStream_t
   if (nrows <= 0) return;
   a.row0 = row0;
   a.nrows = nrows;
-  const int list_words = (a.budget * a.ratio + 3) & ~3;
+  // a staged list: the kept block indices, 16 bits each, in whole 4-byte words
+  const int list_words = ((a.budget + 1) / 2 + 3) & ~3;
   bool stage;
   unsigned grid, block;
-  if (NW == 1) {  // lists up to 8192 ids staged over the histogram, longer ones written straight out
-    stage = list_words <= 8192;
+  if (NW == 1) {  // lists staged over the histogram when they fit, else written straight out
+    stage = list_words <= kSelHistWords;
     a.list_words = list_words;
-    a.wave_words = stage ? max(kSelHistWords, list_words) : kSelHistWords;
+    a.wave_words = kSelHistWords;
     grid = (unsigned)((nrows + 3) / 4);
     block = 256;
   } else {        // the launcher only picks two waves when both lists fit
@@ -1194,7 +1207,7 @@ hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) 
   // wave of 128; 2049..4096: one wave of 64; 1025..2048: one wave of 32; the
   // rest: one wave of 16 (fewer registers, so a short prefill's rows all run
   // at once).
-  const int list_words = (a.budget * a.ratio + 3) & ~3;
+  const int list_words = (a.budget * a.ratio + 3) & ~3;  // expanded ids of one list
   const int n_long = rows_from(64 * 64) - n_wg;
   const int n64 = rows_from(64 * 32) - n_wg - n_long;
   const int n32 = rows_from(64 * 16) - n_wg - n_long - n64;
