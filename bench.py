@@ -75,6 +75,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-front-end", action="store_true", help="skip the fused front end measurement")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill measurement")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip measuring the part's ceilings")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -428,6 +429,80 @@ def chunk_bench(inp, args, Q, torch, syn):
 
 
 # ---------------------------------------------------------------------------
+# measured ceilings of this part (libqsa_ceilings.so, measurement only)
+# ---------------------------------------------------------------------------
+CEIL_LIB = os.path.join(ROOT, "top_indexed_sparse_qsa_amd", "libqsa_ceilings.so")
+
+
+def measure_ceilings(torch):
+    """HBM streaming read and random 256-byte row gathers from HBM (a 4 GiB
+    buffer) and from L2 (a 2 MiB one, resident), each the median of 5 timed
+    launches.  (MFMA fractions stay against the published dense peak.)"""
+    import ctypes
+    if not os.path.exists(CEIL_LIB):
+        return None
+    lib = ctypes.CDLL(CEIL_LIB)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.qsa_ceiling_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.qsa_ceiling_gather_rows.argtypes = [vp, sz, i32, i32, ctypes.c_uint, vp, vp]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    T = HipTimingEvents()
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def med(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(T.create(), T.create()) for _ in range(reps)]
+        for a, b in ev:
+            T.record(a, stream)
+            rc = fn()
+            T.record(b, stream)
+            if rc != 0:
+                raise RuntimeError(f"ceiling kernel failed with {rc}")
+        torch.cuda.synchronize()
+        return float(np.median([T.elapsed_ms(a, b) for a, b in ev])) * 1e-3
+
+    big = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+    s_stream = med(lambda: lib.qsa_ceiling_stream_read(big.data_ptr(), big.numel(), out.data_ptr(), 1024, sp))
+    waves, batches = 16384, 8
+    s_gather = med(lambda: lib.qsa_ceiling_gather_rows(big.data_ptr(), big.numel(), waves, batches, 7,
+                                                        out.data_ptr(), sp))
+    del big
+    small = torch.ones(2 << 20, dtype=torch.uint8, device="cuda")
+    s_l2 = med(lambda: lib.qsa_ceiling_gather_rows(small.data_ptr(), small.numel(), waves, 4 * batches, 7,
+                                                    out.data_ptr(), sp))
+    del small
+    T.destroy_all()
+    torch.cuda.empty_cache()
+    return {"hbm_stream_read_gbs": (4 << 30) / s_stream / 1e9,
+            "hbm_gather_256B_gbs": waves * batches * 64 * 256 / s_gather / 1e9,
+            "l2_gather_256B_gbs": waves * 4 * batches * 64 * 256 / s_l2 / 1e9,
+            "note": "measured on this GPU in this run: a streaming read of 4 GiB; random 256-byte rows gathered "
+                    "16 to a wave from a 4 GiB buffer (HBM) and from a 2 MiB one (L2-resident)"}
+
+
+def attach_ceiling_fracs(line, ceil):
+    """Each roofline object also gives its fraction of the matching measured
+    ceiling (the published-peak fraction stays in `frac`)."""
+    if not ceil:
+        return
+    def prefill(att):
+        att["frac_of_measured_l2_gather"] = att["algorithmic_byte_rate_gbs"] / ceil["l2_gather_256B_gbs"]
+    prefill(line["roofline"])
+    for w in line["workloads"].values():
+        if "algorithmic_byte_rate_gbs" in w["attention"]:
+            prefill(w["attention"])
+    dec = line.get("decode")
+    if dec:
+        for k in ("roofline", "attention", "indexer"):
+            dec[k]["frac_of_measured_hbm_gather"] = dec[k]["achieved"] / ceil["hbm_gather_256B_gbs"]
+    fe = line.get("front_end")
+    if fe:
+        fe["roofline"]["frac_of_measured_hbm_stream"] = fe["roofline"]["achieved"] / ceil["hbm_stream_read_gbs"]
+
+
+# ---------------------------------------------------------------------------
 # HBM counter figures
 # ---------------------------------------------------------------------------
 def kernel_code_sha256(path=None):
@@ -595,6 +670,10 @@ def main():
         note("front end")
         fe = front_end_bench(args, Q, torch, syn)
         note(f"front end: {fe['ms_per_call']:.4f} ms/call")
+    ceil = None
+    if not args.no_ceilings:
+        note("measured ceilings")
+        ceil = measure_ceilings(torch)
     copy_gbs = None
     n = 1 << 30
     a = torch.empty(n // 2, dtype=torch.float16, device="cuda").fill_(1.0)
@@ -641,7 +720,9 @@ def main():
         "front_end": fe,
         "chunk": chunk,
         "hbm_copy_gbs": copy_gbs,
+        "ceilings": ceil,
     }
+    attach_ceiling_fracs(line, ceil)
     print(json.dumps(line), flush=True)
 
 

@@ -46,6 +46,9 @@ def _hipcc() -> str:
 SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 SAN_LIB = os.path.join(HERE, "libqsa_san.so")
+# measurement-only kernels (the part's own ceilings), a library of their own
+CEIL_SRC = "ceilings.hip"
+CEIL_LIB = os.path.join(HERE, "libqsa_ceilings.so")
 
 
 def asan_runtime() -> str:
@@ -77,6 +80,12 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
         os.replace(out_tmp, out)
+    if not sanitize:
+        r = subprocess.run([_hipcc(), *COMMON, "-x", "hip", "-shared", os.path.join(CSRC, CEIL_SRC), "-o",
+                            CEIL_LIB + ".tmp"], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {CEIL_SRC}:\n{r.stdout}\n{r.stderr}")
+        os.replace(CEIL_LIB + ".tmp", CEIL_LIB)
     if verbose:
         print(f"built {out}")
     return out
