@@ -1,13 +1,19 @@
 /*
  * libqsa -- QSA (Qwen Sparse Attention) hot path for AMD MI355X (gfx950).
  *
- * Four entry points, in the order a layer calls them:
+ * Entry points, in the order a layer calls them:
  *
- *   prefill:  qsa_indexer_prefill  -> int32 index lists [B, S, top_k]
- *             qsa_sparse_prefill   -> sparse GQA attention over the lists
- *   decode:   qsa_indexer_decode   -> indexer state update in the pool tails
+ *   front end: qsa_qkv_front_end   -> packed QKV split, qk-norm, partial RoPE,
+ *                                     paged K/V write + dense K/V mirrors
+ *   prefill:   qsa_indexer_prefill -> int32 index lists [B, S, top_k]
+ *              qsa_sparse_prefill  -> sparse GQA attention over the lists
+ *   decode:    qsa_indexer_decode  -> indexer state update in the pool tails
  *                                     + lists [B, 1, top_k]
- *             qsa_sparse_decode    -> split-K sparse attention over the pool
+ *              qsa_sparse_decode   -> split-K sparse attention over the pool
+ *              qsa_decode_step     -> both, the select fused into the
+ *                                     attention kernel
+ *   chunked prefill over the pool: qsa_indexer_chunk, qsa_sparse_chunk
+ *   allocation-free decode indexer: qsa_indexer_decode_noalloc
  *
  * Sources (pages cited by title and section):
  *   [Runner] TensorRT-Edge-LLM "Cute Dsl Qsa Sparse Runner": structs
@@ -335,6 +341,25 @@ qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p);
 qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p);
 qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p);
 qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p);
+
+/* One whole decode step: qsa_indexer_decode(indexer) and then
+ * qsa_sparse_decode(attention) over the lists it makes, as the plugin's
+ * decode runs B1, B2, B3 and the sparse decode in one enqueue [Plugin: class
+ * description, decode B1/B2/B3].  The results are those of the two calls in
+ * that order, bit for bit: the pool tails, the lists in indexer->indices and
+ * attention->o.  The two structs must describe the same step:
+ * attention->indices == indexer->indices, and the same context_lengths,
+ * kv_pool, page_table, batch, num_kv_heads, head_dim, pool_head_dim,
+ * num_flat_pages, max_pages_per_seq, top_k, dtype and stream, else
+ * QSA_ERR_BAD_SHAPE; each struct is validated as its own call would be.
+ * Work: B1 + B2 in one kernel, then B3 and the attention in a second (one
+ * workgroup per (sequence, KV head) selects from the score rows and walks
+ * the list from LDS; the KV head 0 workgroup also stores the list), when
+ * max_pages_per_seq*128/ratio <= 16384 and the split plan puts all splits of
+ * a (sequence, KV head) in one workgroup (num_splits <= 8); otherwise the
+ * two calls' own kernels.  The indexer workspace is used as by
+ * qsa_indexer_decode. */
+qsa_status qsa_decode_step(const qsa_indexer_decode_params *indexer, const qsa_sparse_decode_params *attention);
 
 /* Chunked prefill over the paged pool: a chunk of chunk_len new tokens per
  * sequence continues a sequence whose earlier tokens are already in the pool

@@ -182,6 +182,41 @@ def test_indexer_decode_rejects(no_gpu, kw, status):
     assert _idecode(**kw) == status
 
 
+def _step(ikw=None, akw=None, drop=None):
+    """qsa_decode_step on a matching pair of structs, then edited."""
+    cfg = Q.indexer_config()
+    ip = L.IndexerDecodeParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                               2, 4, 128, 256, 16, 8, 2051, cfg, 0, None)
+    ap = L.SparseDecodeParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              2, 32, 4, 128, 256, 16, 8, 2051, 0, 0.088, 0, None)
+    for k, v in (ikw or {}).items():
+        setattr(ip, k, v)
+    for k, v in (akw or {}).items():
+        setattr(ap, k, v)
+    return Q.load().qsa_decode_step(None if drop == "i" else ctypes.byref(ip),
+                                    None if drop == "a" else ctypes.byref(ap))
+
+
+@pytest.mark.parametrize("ikw,akw,status", [
+    # each half is validated as its own call would be
+    (dict(workspace_bytes=64), {}, WS), (dict(kv_pool=None), {}, NULLP), ({}, dict(num_splits=17), SHAPE),
+    ({}, dict(q=None), NULLP), ({}, dict(head_dim=96), UNSUP),
+    # and both must describe the same step
+    ({}, dict(indices=FAKE + 256), SHAPE), ({}, dict(context_lengths=FAKE + 256), SHAPE),
+    ({}, dict(kv_pool=FAKE + 256), SHAPE), ({}, dict(page_table=FAKE + 256), SHAPE),
+    ({}, dict(batch=3), SHAPE), ({}, dict(num_kv_heads=2), SHAPE), ({}, dict(top_k=2052), SHAPE),
+    ({}, dict(dtype=1), SHAPE), ({}, dict(stream=1), SHAPE), ({}, dict(max_pages_per_seq=4), SHAPE),
+    ({}, dict(num_flat_pages=17), SHAPE), (dict(pool_head_dim=264), dict(pool_head_dim=264, head_dim=64), SHAPE),
+])
+def test_decode_step_rejects(no_gpu, ikw, akw, status):
+    assert _step(ikw, akw) == status
+
+
+def test_decode_step_null_structs(no_gpu):
+    assert _step(drop="i") == NULLP
+    assert _step(drop="a") == NULLP
+
+
 def _idecode_noalloc(**kw):
     cfg = kw.pop("cfg", Q.indexer_config())
     p = L.IndexerDecodeParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,

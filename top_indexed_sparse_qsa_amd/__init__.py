@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     QsaIndexerConfig,
     indexer_config,
     load,
+    qsa_decode_step,
     qsa_indexer_chunk,
     qsa_indexer_chunk_workspace_bytes,
     qsa_indexer_decode,

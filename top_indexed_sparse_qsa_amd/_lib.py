@@ -28,7 +28,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL_POINTER", 2: "QSA_ERR_BAD_SHAPE", 3: "QS
 
 EXPORTS = [
     "qsa_indexer_prefill", "qsa_sparse_prefill", "qsa_indexer_decode", "qsa_sparse_decode",
-    "qsa_indexer_decode_noalloc", "qsa_qkv_front_end", "qsa_indexer_chunk", "qsa_sparse_chunk",
+    "qsa_decode_step", "qsa_indexer_decode_noalloc", "qsa_qkv_front_end", "qsa_indexer_chunk", "qsa_sparse_chunk",
     "qsa_indexer_chunk_workspace_bytes",
     "qsa_indexer_prefill_workspace_bytes", "qsa_indexer_decode_workspace_bytes",
     "qsa_sparse_decode_partial_o_elems", "qsa_sparse_decode_partial_stats_elems",
@@ -131,6 +131,8 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.POINTER(st)]
         fn.restype = ctypes.c_int
+    lib.qsa_decode_step.argtypes = [ctypes.POINTER(IndexerDecodeParams), ctypes.POINTER(SparseDecodeParams)]
+    lib.qsa_decode_step.restype = ctypes.c_int
     lib.qsa_indexer_prefill_workspace_bytes.argtypes = [ctypes.POINTER(QsaIndexerConfig), _i32, _i32]
     lib.qsa_indexer_prefill_workspace_bytes.restype = _sz
     lib.qsa_indexer_decode_workspace_bytes.argtypes = [ctypes.POINTER(QsaIndexerConfig), _i32, _i32]
@@ -260,6 +262,28 @@ def qsa_indexer_decode(idx_q, idx_k, q_norm_w, k_norm_w, kv_pool, page_table, co
                             kv_pool.shape[3], kv_pool.shape[0], page_table.shape[-1], indices.shape[-1], cfg,
                             _dtype_code(idx_q), _stream(stream))
     _check("qsa_indexer_decode", load().qsa_indexer_decode(ctypes.byref(p)))
+
+
+def qsa_decode_step(idx_q, idx_k, q_norm_w, k_norm_w, q, o, kv_pool, page_table, context_lengths, indices,
+                    workspace, cfg: QsaIndexerConfig, attention_scale: float, partial_o=None, partial_stats=None,
+                    head_dim: int | None = None, num_splits: int = 0, stream=None) -> None:
+    """One decode step: qsa_indexer_decode then qsa_sparse_decode over its lists, in one call.
+    idx_q [B,1,Hi,hd]; idx_k [B,1,hd]; q, o [B,1,Hq,D]; kv_pool [2*numPages,128,Hkv,poolHeadDim]
+    (tails updated in place); page_table int32 [B,2,maxPages]; indices int32 [B,1,top_k] (written)."""
+    B, _, Hq, D = q.shape
+    D = head_dim or D
+    st = _stream(stream)
+    ip = IndexerDecodeParams(_ptr(idx_q), _ptr(idx_k), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(kv_pool),
+                             _ptr(page_table), _ptr(context_lengths), _ptr(indices), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), B, kv_pool.shape[2], D,
+                             kv_pool.shape[3], kv_pool.shape[0], page_table.shape[-1], indices.shape[-1], cfg,
+                             _dtype_code(idx_q), st)
+    ap = SparseDecodeParams(_ptr(q), _ptr(o), _ptr(kv_pool), _ptr(page_table), _ptr(indices),
+                            _ptr(context_lengths), _ptr(partial_o), _ptr(partial_stats),
+                            B, Hq, kv_pool.shape[2], D, kv_pool.shape[3], kv_pool.shape[0],
+                            page_table.shape[-1], indices.shape[-1], num_splits, float(attention_scale),
+                            _dtype_code(q), st)
+    _check("qsa_decode_step", load().qsa_decode_step(ctypes.byref(ip), ctypes.byref(ap)))
 
 
 def qsa_indexer_decode_noalloc(idx_q, idx_k, q_norm_w, k_norm_w, kv_pool, page_table, context_lengths, indices,

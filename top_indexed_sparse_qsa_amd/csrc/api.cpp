@@ -116,6 +116,56 @@ int default_splits(int32_t B, int32_t hkv, int32_t top_k) {
 
 qsa_status launched(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
 
+// Validates a sparse decode call and fills the kernel arguments.
+qsa_status decode_attn_args(const qsa_sparse_decode_params *p, qsa::DecodeAttnArgs &a) {
+  if (!p || !p->q || !p->o || !p->kv_pool || !p->page_table || !p->indices || !p->context_lengths)
+    return QSA_ERR_NULL_POINTER;
+  if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
+  if (p->batch < 1 || p->top_k < 1 || p->num_flat_pages < 1 || p->max_pages_per_seq < 1) return QSA_ERR_BAD_SHAPE;
+  if (qsa_status st = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim)) return st;
+  if (p->pool_head_dim < p->head_dim || (p->pool_head_dim % 8) != 0) return QSA_ERR_BAD_SHAPE;
+  if (!all_aligned16(p->q, p->o, p->kv_pool)) return QSA_ERR_BAD_SHAPE;
+  if (p->max_pages_per_seq > 4096) return QSA_ERR_UNSUPPORTED;
+  if (p->num_splits < 0 || p->num_splits > QSA_MAX_SPLITS) return QSA_ERR_BAD_SHAPE;
+  if ((int64_t)p->batch * p->num_kv_heads * QSA_MAX_SPLITS > (int64_t)INT32_MAX) return QSA_ERR_UNSUPPORTED;
+  if (!isfinite(p->attention_scale) || !(p->attention_scale > 0.f)) return QSA_ERR_BAD_SHAPE;
+  int splits = p->num_splits ? p->num_splits : default_splits(p->batch, p->num_kv_heads, p->top_k);
+  const int chunks = (p->top_k + 31) / 32;
+  const int per = (chunks + splits - 1) / splits;
+  splits = (chunks + per - 1) / per;  // drop splits that would get no slots
+  const int wpg = splits < qsa::kDecWaves ? splits : qsa::kDecWaves;
+  const int ngroups = (splits + wpg - 1) / wpg;
+  // more than one workgroup per (sequence, KV head): their partials meet in
+  // the caller's buffers
+  if (ngroups > 1 && (!p->partial_o || !p->partial_stats)) return QSA_ERR_NULL_POINTER;
+  if (ngroups > 1 && !aligned16(p->partial_o)) return QSA_ERR_BAD_SHAPE;
+  a = qsa::DecodeAttnArgs{};
+  a.q = static_cast<const uint16_t *>(p->q);
+  a.o = static_cast<uint16_t *>(p->o);
+  a.pool = static_cast<const uint16_t *>(p->kv_pool);
+  a.pt = p->page_table;
+  a.indices = p->indices;
+  a.ctx = p->context_lengths;
+  a.part_o = p->partial_o;
+  a.part_stats = p->partial_stats;
+  a.B = p->batch;
+  a.C = 1;
+  a.start = nullptr;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads;
+  a.PHD = p->pool_head_dim;
+  a.num_flat_pages = p->num_flat_pages;
+  a.max_pages = p->max_pages_per_seq;
+  a.top_k = p->top_k;
+  a.nsplits = splits;
+  a.split_slots = per * 32;
+  a.wpg = wpg;
+  a.ngroups = ngroups;
+  a.sl2 = p->attention_scale * qsa::kLog2e;
+  return QSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,51 +281,8 @@ qsa_status qsa_sparse_prefill(const qsa_sparse_prefill_params *p) {
 }
 
 qsa_status qsa_sparse_decode(const qsa_sparse_decode_params *p) {
-  if (!p || !p->q || !p->o || !p->kv_pool || !p->page_table || !p->indices || !p->context_lengths)
-    return QSA_ERR_NULL_POINTER;
-  if (!dtype_ok(p->dtype)) return QSA_ERR_UNSUPPORTED;
-  if (p->batch < 1 || p->top_k < 1 || p->num_flat_pages < 1 || p->max_pages_per_seq < 1) return QSA_ERR_BAD_SHAPE;
-  if (qsa_status st = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim)) return st;
-  if (p->pool_head_dim < p->head_dim || (p->pool_head_dim % 8) != 0) return QSA_ERR_BAD_SHAPE;
-  if (!all_aligned16(p->q, p->o, p->kv_pool)) return QSA_ERR_BAD_SHAPE;
-  if (p->max_pages_per_seq > 4096) return QSA_ERR_UNSUPPORTED;
-  if (p->num_splits < 0 || p->num_splits > QSA_MAX_SPLITS) return QSA_ERR_BAD_SHAPE;
-  if ((int64_t)p->batch * p->num_kv_heads * QSA_MAX_SPLITS > (int64_t)INT32_MAX) return QSA_ERR_UNSUPPORTED;
-  if (!isfinite(p->attention_scale) || !(p->attention_scale > 0.f)) return QSA_ERR_BAD_SHAPE;
-  int splits = p->num_splits ? p->num_splits : default_splits(p->batch, p->num_kv_heads, p->top_k);
-  const int chunks = (p->top_k + 31) / 32;
-  const int per = (chunks + splits - 1) / splits;
-  splits = (chunks + per - 1) / per;  // drop splits that would get no slots
-  const int wpg = splits < qsa::kDecWaves ? splits : qsa::kDecWaves;
-  const int ngroups = (splits + wpg - 1) / wpg;
-  // more than one workgroup per (sequence, KV head): their partials meet in
-  // the caller's buffers
-  if (ngroups > 1 && (!p->partial_o || !p->partial_stats)) return QSA_ERR_NULL_POINTER;
-  if (ngroups > 1 && !aligned16(p->partial_o)) return QSA_ERR_BAD_SHAPE;
-  qsa::DecodeAttnArgs a{};
-  a.q = static_cast<const uint16_t *>(p->q);
-  a.o = static_cast<uint16_t *>(p->o);
-  a.pool = static_cast<const uint16_t *>(p->kv_pool);
-  a.pt = p->page_table;
-  a.indices = p->indices;
-  a.ctx = p->context_lengths;
-  a.part_o = p->partial_o;
-  a.part_stats = p->partial_stats;
-  a.B = p->batch;
-  a.C = 1;
-  a.start = nullptr;
-  a.Hq = p->num_q_heads;
-  a.Hkv = p->num_kv_heads;
-  a.G = p->num_q_heads / p->num_kv_heads;
-  a.PHD = p->pool_head_dim;
-  a.num_flat_pages = p->num_flat_pages;
-  a.max_pages = p->max_pages_per_seq;
-  a.top_k = p->top_k;
-  a.nsplits = splits;
-  a.split_slots = per * 32;
-  a.wpg = wpg;
-  a.ngroups = ngroups;
-  a.sl2 = p->attention_scale * qsa::kLog2e;
+  qsa::DecodeAttnArgs a;
+  if (qsa_status st = decode_attn_args(p, a)) return st;
   return launched(qsa::launch_sparse_decode(a, p->head_dim, (int)p->dtype, (hipStream_t)p->stream));
 }
 
@@ -521,16 +528,12 @@ qsa_status qsa::check_indexer_decode(const qsa_indexer_decode_params *p) {
   return QSA_OK;
 }
 
-extern "C" {
+namespace {
 
-qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
-  if (qsa_status st = qsa::check_indexer_decode(p)) return st;
+// Decode B1 + B2 (one kernel) of a validated indexer decode call; the score
+// rows go to the workspace.
+hipError_t launch_dec_score(const qsa_indexer_decode_params *p) {
   const DecodeWs w = decode_ws(p->cfg, p->batch, p->max_pages_per_seq);
-  char *ws = static_cast<char *>(p->workspace);
-  const hipStream_t s = (hipStream_t)p->stream;
-  const int dt = (int)p->dtype;
-  const int gmax = p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio;
-
   qsa::IdxDecScoreArgs sa{};
   sa.idx_q = static_cast<const uint16_t *>(p->idx_q);
   sa.idx_k = static_cast<const uint16_t *>(p->idx_k);
@@ -539,7 +542,7 @@ qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
   sa.pool = static_cast<uint16_t *>(p->kv_pool);
   sa.pt = p->page_table;
   sa.ctx = p->context_lengths;
-  sa.scores = reinterpret_cast<float *>(ws + w.scores);
+  sa.scores = reinterpret_cast<float *>(static_cast<char *>(p->workspace) + w.scores);
   sa.B = p->batch;
   sa.Hi = p->cfg.num_heads;
   sa.hd = p->cfg.head_dim;
@@ -551,14 +554,24 @@ qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
   sa.num_flat_pages = p->num_flat_pages;
   sa.max_pages = p->max_pages_per_seq;
   sa.stride = w.stride;
-  sa.gmax = gmax;
+  sa.gmax = p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio;
   sa.theta = (double)p->cfg.rope_theta;
   sa.eps = (double)p->cfg.rms_eps;
-  sa.dt = dt;
-  if (qsa::launch_idx_dec_score(sa, dt, s) != hipSuccess) return QSA_ERR_LAUNCH;
+  sa.dt = (int)p->dtype;
+  return qsa::launch_idx_dec_score(sa, (int)p->dtype, (hipStream_t)p->stream);
+}
 
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
+  if (qsa_status st = qsa::check_indexer_decode(p)) return st;
+  if (launch_dec_score(p) != hipSuccess) return QSA_ERR_LAUNCH;
+  const DecodeWs w = decode_ws(p->cfg, p->batch, p->max_pages_per_seq);
+  const int gmax = p->max_pages_per_seq * QSA_PAGE_TOKENS / p->cfg.compress_ratio;
   qsa::IdxSelectArgs xa{};
-  xa.scores = sa.scores;
+  xa.scores = reinterpret_cast<const float *>(static_cast<const char *>(p->workspace) + w.scores);
   xa.row_stride = w.stride;
   xa.out = p->indices;
   xa.ctx = p->context_lengths;
@@ -569,7 +582,35 @@ qsa_status qsa_indexer_decode(const qsa_indexer_decode_params *p) {
   xa.ratio = p->cfg.compress_ratio;
   xa.decode = 1;
   xa.max_ctx = p->max_pages_per_seq * QSA_PAGE_TOKENS;
-  return launched(qsa::launch_idx_select(xa, gmax, s));
+  return launched(qsa::launch_idx_select(xa, gmax, (hipStream_t)p->stream));
+}
+
+qsa_status qsa_decode_step(const qsa_indexer_decode_params *ip, const qsa_sparse_decode_params *ap) {
+  if (!ip || !ap) return QSA_ERR_NULL_POINTER;
+  if (qsa_status st = qsa::check_indexer_decode(ip)) return st;
+  qsa::DecodeAttnArgs a;
+  if (qsa_status st = decode_attn_args(ap, a)) return st;
+  // both halves describe the same step
+  if (ap->indices != ip->indices || ap->context_lengths != ip->context_lengths || ap->kv_pool != ip->kv_pool ||
+      ap->page_table != ip->page_table || ap->batch != ip->batch || ap->num_kv_heads != ip->num_kv_heads ||
+      ap->head_dim != ip->head_dim || ap->pool_head_dim != ip->pool_head_dim ||
+      ap->num_flat_pages != ip->num_flat_pages || ap->max_pages_per_seq != ip->max_pages_per_seq ||
+      ap->top_k != ip->top_k || ap->dtype != ip->dtype || ap->stream != ip->stream)
+    return QSA_ERR_BAD_SHAPE;
+  const int gmax = ip->max_pages_per_seq * QSA_PAGE_TOKENS / ip->cfg.compress_ratio;
+  if (gmax > qsa::kStepMaxBlocks || a.ngroups != 1) {  // the two calls, one after the other
+    if (qsa_status st = qsa_indexer_decode(ip)) return st;
+    return launched(qsa::launch_sparse_decode(a, ap->head_dim, (int)ap->dtype, (hipStream_t)ap->stream));
+  }
+  if (launch_dec_score(ip) != hipSuccess) return QSA_ERR_LAUNCH;
+  const DecodeWs w = decode_ws(ip->cfg, ip->batch, ip->max_pages_per_seq);
+  a.scores = reinterpret_cast<const float *>(static_cast<const char *>(ip->workspace) + w.scores);
+  a.score_stride = w.stride;
+  a.gmax = gmax;
+  a.budget = ip->cfg.budget;
+  a.ratio = ip->cfg.compress_ratio;
+  a.lists_out = ip->indices;
+  return launched(qsa::launch_decode_select_attend(a, ap->head_dim, (int)ap->dtype, (hipStream_t)ap->stream));
 }
 
 }  // extern "C"

@@ -18,6 +18,7 @@
 
 #include "qsa_device.h"
 #include "qsa_launch.h"
+#include "select_core.h"
 
 namespace qsa {
 
@@ -427,37 +428,6 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Select + expand, shared pieces.  Scores are non-negative, so their fp32 bit
-// patterns (sign cleared) order like the values; an MSB-first radix select
-// over those keys narrows the cut down to one bin.  Every key above the bin
-// is kept, and of the bin's keys the lowest-index ones up to the budget.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t score_key(float s) { return __float_as_uint(s) & 0x7fffffffu; }
-
-// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts inside
-// each 16-lane row, then the row broadcasts of lanes 15 and 31.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return v;
-}
-
-// Radix histograms: the first window has 2048 bins, later ones 256; four pad
-// words per 32 bins keep reads of consecutive bins by consecutive lanes free
-// of bank conflicts.
-constexpr int kSelBins = 2048;
-__host__ __device__ constexpr int hpad(int d) { return d + ((d >> 5) << 2); }
-constexpr int kSelHistWords = kSelBins + (kSelBins >> 3);
-constexpr int kSelOddVecs = (hpad(255) + 4) >> 2;  // a padded 256-bin histogram in 16-byte words
-
-// Radix window of a pass: the first takes 11 bits below the bits shared by
-// every key, later ones 8.
-__device__ __forceinline__ int sel_window(int pass, int top) { return min(pass == 0 ? 11 : 8, top + 1); }
 
 // ---------------------------------------------------------------------------
 // Select + expand for prefill rows of up to 128*KPL blocks: NW = 1 wave per
@@ -480,10 +450,6 @@ __device__ __forceinline__ int sel_window(int pass, int top) { return min(pass =
 // (when the lists fit), and the row is stored with the causal tail and -1
 // padding in one coalesced pass.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int lanes_below(unsigned long long m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 template <int NW>
 __device__ __forceinline__ void row_sync() {
   if constexpr (NW == 1) __builtin_amdgcn_wave_barrier();
@@ -527,15 +493,12 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   uint32_t key[KPL];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
+    // unconditional loads (a load on one branch only is waited for alone
+    // where the branches join): slots past the row read its last scores
     const int i0 = base_i + 256 * g + 4 * lane;
-    if (i0 + 3 < nc) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + i0);
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + min((long long)i0, a.row_stride - 4));
 #pragma unroll
-      for (int c = 0; c < 4; ++c) key[4 * g + c] = score_key(v[c]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) key[4 * g + c] = i0 + c < nc ? score_key(srow[i0 + c]) : 0xffffffffu;
-    }
+    for (int c = 0; c < 4; ++c) key[4 * g + c] = i0 + c < nc ? score_key(v[c]) : 0xffffffffu;
   }
   uint32_t kmax = 0, kmin = 0x7fffffffu;
 #pragma unroll
@@ -718,51 +681,26 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
 
 // ---------------------------------------------------------------------------
 // Select + expand, one 1024-thread workgroup per row: decode rows (one per
-// sequence, up to 32768 blocks) and prefill rows over 8192 blocks.  Thread
-// j holds the KPT keys of blocks [j*KPT, (j+1)*KPT) in registers, so one
-// workgroup scan of per-thread counts places kept blocks in ascending order.
-// Passes as in the per-row kernel, over a workgroup histogram: a workgroup
-// scan of per-thread bin sums names the thread whose range holds the cut,
-// and that thread walks its own bins.  Two histograms alternate, so a pass
-// clears the next one's while it counts and takes three barriers.
+// sequence, up to 32768 blocks), prefill rows over 8192 blocks and chunk
+// rows.  Thread j holds the KPT keys of blocks [j*KPT, (j+1)*KPT) in
+// registers; the workgroup select (select_core.h) stages the kept block
+// indices in LDS, and the row is stored expanded, with the causal tail and
+// -1 padding, in one coalesced pass.
 // ---------------------------------------------------------------------------
 constexpr int kSelWgThreads = 1024;
 
-// Exclusive prefix sum of v over the workgroup in thread order, with one
-// barrier.  s_wt holds one int per wave and is read after that barrier, so
-// the caller puts another barrier between two calls.
-__device__ __forceinline__ int wg_exscan(int v, int *s_wt, int *total) {
-  constexpr int NW = kSelWgThreads / 64;
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(v);
-  if (lane == 63) s_wt[wv] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int x = s_wt[w];
-    before += w < wv ? x : 0;
-    all += x;
-  }
-  *total = all;
-  return before + incl - v;
-}
+template <int KPT>
+__global__ __launch_bounds__(kSelWgThreads) void idx_select_wg_kernel(IdxSelectArgs a) {
+  constexpr int NT = kSelWgThreads;
+  extern __shared__ uint16_t s_lb[];  // kept block indices [budget]
+  __shared__ WgSelLds<NT> s_sel;
+  const int tid = threadIdx.x;
 
-template <int KPT, bool STAGE>
-__global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
-  constexpr int NT = kSelWgThreads, NW = NT / 64;
-  extern __shared__ uint32_t s_dyn[];  // padded histogram | list
-  __shared__ u32x4 s_hodd[kSelOddVecs];  // histogram of the odd passes
-  __shared__ int s_wt[NW];
-  __shared__ uint32_t s_red[2 * NW];
-  __shared__ int s_res[3];
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
-
-  int b, t, live;
+  int t, live;
   int32_t *out;
   const float *srow;
   if (a.decode) {
-    b = blockIdx.x;
+    const int b = blockIdx.x;
     const int c = min(a.ctx[b], a.max_ctx);
     t = c - 1;
     live = c > 0;
@@ -770,7 +708,7 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
     srow = a.scores + (size_t)b * a.row_stride;
   } else {
     const int rw = a.row0 + blockIdx.x;  // longest rows first
-    b = rw % a.B;
+    const int b = rw % a.B;
     const int tl = a.S - 1 - rw / a.B;   // the row; its position is off + tl
     const int off = a.start ? a.start[b] : 0;
     t = off + tl;
@@ -788,143 +726,30 @@ __global__ __launch_bounds__(1024) void idx_select_wg_kernel(IdxSelectArgs a) {
     for (int i = tid; i < a.top_k; i += NT) out[i] = i <= t ? i : -1;
     return;
   }
-  int32_t *lst = STAGE ? reinterpret_cast<int32_t *>(s_dyn + kSelHistWords) : out;
-  // Pass p counts into s_dyn (even p) or s_hodd (odd p); both start cleared
-  // here, and pass p >= 1 clears the one pass p + 1 uses, which pass p - 1
-  // finished reading before its last barrier.
-  for (int j = tid; j < (kSelHistWords >> 2); j += NT) reinterpret_cast<u32x4 *>(s_dyn)[j] = u32x4{0u, 0u, 0u, 0u};
-  if (tid < kSelOddVecs) s_hodd[tid] = u32x4{0u, 0u, 0u, 0u};
-
+  wg_select_clear<NT>(s_sel);
   uint32_t key[KPT];
   const int i0 = tid * KPT;
 #pragma unroll
   for (int j = 0; j < KPT; j += 4) {
+    // unconditional loads, as in the per-row kernel
     const int i = i0 + j;
-    if (i + 3 < nc) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + i);
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + min((long long)i, a.row_stride - 4));
 #pragma unroll
-      for (int c = 0; c < 4; ++c) key[j + c] = score_key(v[c]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) key[j + c] = i + c < nc ? score_key(srow[i + c]) : 0xffffffffu;
-    }
+    for (int c = 0; c < 4; ++c) key[j + c] = i + c < nc ? score_key(v[c]) : 0xffffffffu;
   }
-  uint32_t kmax = 0, kmin = 0x7fffffffu;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if ((int)key[j] >= 0) {
-      kmax = max(kmax, key[j]);
-      kmin = min(kmin, key[j]);
-    }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-  }
-  if (lane == 0) {
-    s_red[wv] = kmax;
-    s_red[NW + wv] = kmin;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    kmax = max(kmax, s_red[w]);
-    kmin = min(kmin, s_red[NW + w]);
-  }
-  const uint32_t diff = kmax ^ kmin;
-  int top = diff ? 31 - __clz((int)diff) : -1;  // highest differing bit (< 31)
-  uint32_t pmask = top < 0 ? 0xffffffffu : ~((2u << top) - 1u);
-  uint32_t prefix = kmax & pmask;
-  int remaining = a.budget;
-  for (int pass = 0; top >= 0; ++pass) {
-    const int w = sel_window(pass, top), shift = top + 1 - w;
-    const uint32_t dmask = (1u << w) - 1u;
-    const int nb = 1 << w;
-    uint32_t *hist = (pass & 1) ? reinterpret_cast<uint32_t *>(s_hodd) : s_dyn;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint32_t k = key[j];
-      if ((k & pmask) == prefix) atomicAdd(&hist[hpad((int)((k >> shift) & dmask))], 1u);
-    }
-    if (pass > 0 && tid < kSelOddVecs)  // later windows take at most 8 bits
-      ((pass & 1) ? reinterpret_cast<u32x4 *>(s_dyn) : s_hodd)[tid] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    // thread j sums bins [nb - per*(j+1), nb - per*j): thread 0 the top digits
-    const int per = nb > NT ? nb / NT : 1;
-    const int lo = nb - per * (tid + 1);
-    int lsum = 0;
-    if (lo >= 0)
-      for (int j = 0; j < per; ++j) lsum += (int)hist[hpad(lo + j)];
-    int tot;
-    const int excl = wg_exscan(lsum, s_wt, &tot);
-    if (lsum > 0 && excl < remaining && excl + lsum >= remaining) {  // exactly one thread
-      int acc = excl;
-      for (int j = per - 1; j >= 0; --j) {
-        const int h = (int)hist[hpad(lo + j)];
-        if (acc + h >= remaining) {
-          s_res[0] = lo + j;
-          s_res[1] = acc;
-          s_res[2] = h;
-          break;
-        }
-        acc += h;
-      }
-    }
-    __syncthreads();
-    const int dsel = __builtin_amdgcn_readfirstlane(s_res[0]);
-    const int above = __builtin_amdgcn_readfirstlane(s_res[1]);
-    const int cnt = __builtin_amdgcn_readfirstlane(s_res[2]);
-    prefix |= (uint32_t)dsel << shift;
-    pmask |= dmask << shift;
-    remaining -= above;
-    if (cnt == remaining) break;  // the whole bin is kept
-    top = shift - 1;
-  }
-
-  // Keys with (k & pmask) > prefix are kept; of those == prefix, the first
-  // `remaining` in index order (all of them when the loop kept a whole bin).
-  // Each pass's scan is followed by the s_res barrier, so this scan may
-  // reuse s_wt.  Bit j of gt_bits / eq_bits: key j above / equal to the cut.
-  uint32_t gt_bits = 0u, eq_bits = 0u;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t m = key[j] & pmask;
-    gt_bits |= ((int)key[j] >= 0 && m > prefix) ? 1u << j : 0u;
-    eq_bits |= m == prefix ? 1u << j : 0u;
-  }
-  const int n_gt = __builtin_popcount(gt_bits), n_eq = __builtin_popcount(eq_bits);
-  // One scan of both counts (n_gt in the high half: fewer than budget < nc
-  // <= 32768 keys are above the cut, so neither half overflows).  The keys
-  // equal to the cut before this thread's take min(eq_before, remaining)
-  // slots, which is also right when the whole bin is kept.
-  int tot;
-  const int both = wg_exscan(n_eq | (n_gt << 16), s_wt, &tot);
-  const int eq_before = both & 0xffff;
-  const int take_eq = min(n_eq, max(0, remaining - eq_before));
-  int pos = (both >> 16) + min(eq_before, remaining);
-  // kept keys: those above the cut and the lowest take_eq equal ones; the
-  // emission visits set bits only (a thread keeps few of its KPT keys)
-  uint32_t keep = gt_bits;
-  for (int e = 0; e < take_eq; ++e) {
-    keep |= eq_bits & (0u - eq_bits);
-    eq_bits &= eq_bits - 1u;
-  }
-  while (keep != 0u) {
-    const int j = __builtin_ctz(keep);
-    keep &= keep - 1u;
-    const int blk = r * (i0 + j);
-    if (STAGE && r == 4) {
-      *reinterpret_cast<int4 *>(lst + 4 * pos) = make_int4(blk, blk + 1, blk + 2, blk + 3);
-    } else {
-      for (int q = 0; q < r; ++q) lst[r * pos + q] = blk + q;
-    }
-    ++pos;
-  }
-  __syncthreads();
+  wg_select_blocks<NT, KPT>(key, a.budget, s_sel, s_lb);
   const int head = r * a.budget;
   const int len = head + (t + 1) - r * nc;
-  for (int i = (STAGE ? 0 : head) + tid; i < a.top_k; i += NT)
-    out[i] = i < head ? lst[i] : (i < len ? r * nc + (i - head) : -1);
+  for (int i = tid; i < a.top_k; i += NT) {
+    int v;
+    if (i < head) {
+      const int j = r == 4 ? i >> 2 : i / r;
+      v = r * (int)s_lb[j] + (i - r * j);
+    } else {
+      v = i < len ? r * nc + (i - head) : -1;
+    }
+    out[i] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1162,14 +987,12 @@ static void launch_select_wg(IdxSelectArgs a, int row0, unsigned rows, hipStream
   if (rows == 0) return;
   a.row0 = row0;
   a.nrows = (int)rows;
-  const int list_words = (a.budget * a.ratio + 3) & ~3;
-  const bool stage = list_words <= 16384;
-  const size_t lds = (size_t)(kSelHistWords + (stage ? list_words : 0)) * sizeof(uint32_t);
-  const void *fn = stage ? reinterpret_cast<const void *>(&idx_select_wg_kernel<KPT, true>)
-                         : reinterpret_cast<const void *>(&idx_select_wg_kernel<KPT, false>);
-  if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (stage) hipLaunchKernelGGL((idx_select_wg_kernel<KPT, true>), dim3(rows), dim3(kSelWgThreads), lds, s, a);
-  else hipLaunchKernelGGL((idx_select_wg_kernel<KPT, false>), dim3(rows), dim3(kSelWgThreads), lds, s, a);
+  // the kept block list: fewer than QSA_MAX_BLOCKS entries of 16 bits
+  const size_t lds = (size_t)std::min(a.budget, QSA_MAX_BLOCKS) * sizeof(uint16_t);
+  const void *fn = reinterpret_cast<const void *>(&idx_select_wg_kernel<KPT>);
+  if (lds + sizeof(WgSelLds<kSelWgThreads>) > 65536)
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((idx_select_wg_kernel<KPT>), dim3(rows), dim3(kSelWgThreads), lds, s, a);
 }
 
 static void launch_select_wg_for(const IdxSelectArgs &a, int nc_max, int row0, unsigned rows, hipStream_t s) {

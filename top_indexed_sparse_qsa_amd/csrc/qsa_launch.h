@@ -43,6 +43,12 @@ struct DecodeAttnArgs {
   int nsplits, split_slots;  // split s covers list slots [s*split_slots, (s+1)*split_slots)
   int wpg, ngroups;          // splits (waves) per workgroup, workgroups per (sequence, KV head)
   float sl2;
+  // decode step only (select and attention in one kernel): the rows' block
+  // scores [B][score_stride] (gmax live width), the select's budget and
+  // ratio, and where the rows' lists are stored
+  const float *scores;
+  int score_stride, gmax, budget, ratio;
+  int32_t *lists_out;
 };
 
 // Decode: waves (splits) per workgroup, merged in LDS; splits beyond that
@@ -154,6 +160,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStream_t s);
 hipError_t launch_sparse_decode(const DecodeAttnArgs &a, int D, int dt, hipStream_t s);
+// Decode step select + attention (one workgroup of kDecWaves splits per
+// (sequence, KV head)); gmax <= kStepMaxBlocks.
+constexpr int kStepMaxBlocks = 64 * kDecWaves * 32;
+hipError_t launch_decode_select_attend(const DecodeAttnArgs &a, int D, int dt, hipStream_t s);
 hipError_t launch_idx_prep(const IdxPrepArgs &a, hipStream_t s);
 // prefill -> decode handoff into the pool tails (no-op when a.pool is null)
 hipError_t launch_idx_handoff(const IdxPrepArgs &a, hipStream_t s);

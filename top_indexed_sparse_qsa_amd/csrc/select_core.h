@@ -1,0 +1,256 @@
+// Top-k block selection pieces shared by the indexer's select kernels and
+// the fused decode step (gfx950, wave64).
+//
+// The selection is the indexer's fused step 2 (TensorRT-Edge-LLM, Qsa
+// Attention Plugin, class description; decode B3): keep the `budget`
+// highest-scoring complete blocks of a row, ties going to the lower block
+// index.  Scores are non-negative, so their fp32 bit patterns (sign cleared)
+// order like the values; an MSB-first radix select over those keys narrows
+// the cut down to one bin.  Every key above the bin is kept, and of the
+// bin's keys the lowest-index ones up to the budget.
+#pragma once
+
+#include "qsa_device.h"
+
+namespace qsa {
+
+__device__ __forceinline__ uint32_t score_key(float s) { return __float_as_uint(s) & 0x7fffffffu; }
+
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts inside
+// each 16-lane row, then the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Radix histograms: the first window has 2048 bins, later ones 256; four pad
+// words per 32 bins keep reads of consecutive bins by consecutive lanes free
+// of bank conflicts.
+constexpr int kSelBins = 2048;
+__host__ __device__ constexpr int hpad(int d) { return d + ((d >> 5) << 2); }
+constexpr int kSelHistWords = kSelBins + (kSelBins >> 3);
+constexpr int kSelOddVecs = (hpad(255) + 4) >> 2;  // a padded 256-bin histogram in 16-byte words
+
+// Radix window of a pass: the first takes 11 bits below the bits shared by
+// every key, later ones 8.
+__device__ __forceinline__ int sel_window(int pass, int top) { return min(pass == 0 ? 11 : 8, top + 1); }
+
+// Lanes below this one whose bit is set in m.
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Inclusive scan of v over the 64 lanes of a wave under a commutative,
+// associative op with identity id (DPP as wave_incl_scan); lane 63 ends
+// with the op over the whole wave.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_op(uint32_t v, uint32_t id, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xa, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup select: NT threads, thread j holding the KPT keys of blocks
+// [j*KPT, (j+1)*KPT) in registers (slots past the row hold 0xffffffff: real
+// keys have bit 31 clear), so one workgroup scan of per-thread counts
+// places kept blocks in ascending order.
+//
+// The cut is narrowed over key ranges [lo, hi) rather than bit prefixes.
+// Zero scores (every head's relu zero) are left out of the first range:
+// they are kept only when fewer than `budget` keys are non-zero, and then
+// the non-zero keys are all kept and the zeros tie.  The first range is
+// [smallest non-zero key, largest key], split into at most 2048 bins of
+// 2^s keys each; later passes split the cut bin into at most 256.  Scores
+// sit in a few binades, so a range that starts at the smallest non-zero key
+// spreads them over far more bins than a window aligned to the bits all
+// keys share would, and four passes always reach single keys.  A pass is
+// one barrier: the keys count into an LDS histogram (plain atomic
+// increments), and then every wave reads the whole histogram and finds the
+// cut bin for itself (DPP scans over lane sums of bins, then within the one
+// lane's range that holds it), so nothing is broadcast.  Each pass has a
+// histogram of its own, all cleared at the start.
+// ---------------------------------------------------------------------------
+constexpr int kSelSmallWords = ((hpad(255) + 4 + 3) / 4) * 4;  // a padded 256-bin histogram
+
+template <int NT>
+struct alignas(16) WgSelLds {
+  static constexpr int NW = NT / 64;
+  uint32_t hist[kSelHistWords];         // pass 0 (up to 2048 bins)
+  uint32_t small[3][kSelSmallWords];    // passes 1..3 (up to 256 bins)
+  uint32_t red[3 * NW];                 // per wave: largest key, smallest non-zero key, non-zero count
+  int wt[NW];                           // the emission scan
+};
+
+// Exclusive prefix sum of v over the workgroup in thread order, with one
+// barrier.  s_wt holds one int per wave and is read after that barrier, so
+// the caller puts another barrier between two calls.
+template <int NT>
+__device__ __forceinline__ int wg_exscan(int v, int *s_wt, int *total) {
+  constexpr int NW = NT / 64;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) s_wt[wv] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = s_wt[w];
+    before += w < wv ? x : 0;
+    all += x;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// Clears every histogram; call before the keys are needed, so that the
+// stores overlap their loads.  wg_select_blocks reads them after its first
+// barrier.
+template <int NT>
+__device__ __forceinline__ void wg_select_clear(WgSelLds<NT> &S) {
+  constexpr int kVecs = (kSelHistWords + 3 * kSelSmallWords) / 4;
+  static_assert(sizeof(S.hist) + sizeof(S.small) == 16 * kVecs, "histograms are whole 16-byte words");
+  u32x4 *h = reinterpret_cast<u32x4 *>(S.hist);
+  for (int j = threadIdx.x; j < kVecs; j += NT) h[j] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// The cut bin of one pass, found by one wave from the histogram H of nb
+// bins (a multiple of 256; bins past the pass's range are empty): dsel, the
+// bin holding the remaining-th largest key; above, the keys in bins above
+// it; cnt, the keys in it.
+__device__ __forceinline__ void sel_find_cut(const uint32_t *H, int nb, int remaining, int &dsel, int &above,
+                                             int &cnt) {
+  const int lane = lane_id();
+  // lane l sums bins [nb - per*(l+1), nb - per*l): lane 0 holds the top bins
+  const int per = nb >> 6;  // a multiple of 4
+  const int lo = nb - per * (lane + 1);
+  int lsum = 0;
+  for (int j = 0; j < per; j += 4) {
+    const u32x4 hv = *reinterpret_cast<const u32x4 *>(H + hpad(lo + j));
+    lsum += (int)(hv[0] + hv[1] + hv[2] + hv[3]);
+  }
+  const int incl = wave_incl_scan(lsum);
+  const int src = __ffsll((long long)__ballot(incl >= remaining)) - 1;
+  const int above0 = __builtin_amdgcn_readlane(incl - lsum, src);
+  // inside lane src's range, top bin first
+  const int hb = lane < per ? (int)H[hpad(nb - 1 - (src * per + lane))] : 0;
+  const int incl2 = above0 + wave_incl_scan(hb);
+  const int js = __ffsll((long long)__ballot(incl2 >= remaining)) - 1;
+  dsel = nb - 1 - (src * per + js);
+  above = __builtin_amdgcn_readlane(incl2 - hb, js);
+  cnt = __builtin_amdgcn_readlane(hb, js);
+}
+
+// Keeps `budget` (< the number of real keys) of the workgroup's keys and
+// writes the kept block indices (thread j's key i is block j*KPT + i) to
+// lb[0, budget) in ascending order.  The histograms must have been cleared
+// by wg_select_clear.  Ends with a barrier: lb is complete on return.
+template <int NT, int KPT>
+__device__ void wg_select_blocks(const uint32_t (&key)[KPT], int budget, WgSelLds<NT> &S, uint16_t *lb) {
+  constexpr int NW = NT / 64;
+  static_assert(KPT <= 32, "per-thread key masks are 32 bits");
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  const int i0 = tid * KPT;
+  uint32_t kmax = 0u, kmin = 0xffffffffu, nnz = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t k = key[j];
+    const bool nz = (int)k > 0;  // real and non-zero
+    kmax = (int)k >= 0 ? max(kmax, k) : kmax;
+    kmin = nz ? min(kmin, k) : kmin;
+    nnz += nz ? 1u : 0u;
+  }
+  kmax = wave_incl_op(kmax, 0u, [](uint32_t x, uint32_t y) { return max(x, y); });
+  kmin = wave_incl_op(kmin, 0xffffffffu, [](uint32_t x, uint32_t y) { return min(x, y); });
+  nnz = wave_incl_op(nnz, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+  if (lane == 63) {
+    S.red[wv] = kmax;
+    S.red[NW + wv] = kmin;
+    S.red[2 * NW + wv] = nnz;
+  }
+  __syncthreads();
+  kmax = 0u;
+  kmin = 0xffffffffu;
+  nnz = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    kmax = max(kmax, S.red[w]);
+    kmin = min(kmin, S.red[NW + w]);
+    nnz += S.red[2 * NW + w];
+  }
+  // keys in [lo, hi) are still open; those >= hi are kept
+  uint32_t lo, hi;
+  int remaining = budget;
+  if ((int)nnz < budget) {  // every non-zero key, then the first zeros
+    lo = 0u;
+    hi = 1u;
+    remaining = budget - (int)nnz;
+  } else {
+    lo = kmin;
+    hi = kmax + 1u;
+    for (int pass = 0; pass < 4; ++pass) {
+      const uint32_t range = hi - lo;
+      const int bl = range > 1u ? 32 - __clz((int)(range - 1u)) : 0;
+      const int s = max(0, bl - (pass == 0 ? 11 : 8));
+      const int nb = (((int)((range - 1u) >> s) >> 8) + 1) << 8;  // bins in use, rounded up to 256
+      uint32_t *H = pass == 0 ? S.hist : S.small[pass - 1];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const uint32_t k = key[j];
+        if (k >= lo && k < hi) atomicAdd(&H[hpad((int)((k - lo) >> s))], 1u);
+      }
+      __syncthreads();
+      int dsel, above, cnt;
+      sel_find_cut(H, nb, remaining, dsel, above, cnt);
+      remaining -= above;
+      lo += (uint32_t)dsel << s;
+      hi = min(hi, lo + (1u << s));
+      if (cnt == remaining || s == 0) break;
+    }
+  }
+
+  // Keys >= hi are kept; of those in [lo, hi), the first `remaining` in
+  // index order (all of them when the cut bin is kept whole).  Bit j of
+  // gt_bits / eq_bits: key j above / inside the cut bin.
+  uint32_t gt_bits = 0u, eq_bits = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t k = key[j];
+    gt_bits |= ((int)k >= 0 && k >= hi) ? 1u << j : 0u;
+    eq_bits |= (k >= lo && k < hi) ? 1u << j : 0u;
+  }
+  const int n_gt = __builtin_popcount(gt_bits), n_eq = __builtin_popcount(eq_bits);
+  // One scan of both counts (n_gt in the high half: fewer than budget < nc
+  // <= 32768 keys are above the cut, so neither half overflows).  The keys
+  // in the cut bin before this thread's take min(eq_before, remaining)
+  // slots, which is also right when the whole bin is kept.
+  int tot;
+  const int both = wg_exscan<NT>(n_eq | (n_gt << 16), S.wt, &tot);
+  const int eq_before = both & 0xffff;
+  const int take_eq = min(n_eq, max(0, remaining - eq_before));
+  int pos = (both >> 16) + min(eq_before, remaining);
+  // kept keys: those above the cut and the lowest take_eq in it; the
+  // emission visits set bits only (a thread keeps few of its KPT keys)
+  uint32_t keep = gt_bits;
+  for (int e = 0; e < take_eq; ++e) {
+    keep |= eq_bits & (0u - eq_bits);
+    eq_bits &= eq_bits - 1u;
+  }
+  while (keep != 0u) {
+    const int j = __builtin_ctz(keep);
+    keep &= keep - 1u;
+    lb[pos++] = (uint16_t)(i0 + j);
+  }
+  __syncthreads();
+}
+
+}  // namespace qsa

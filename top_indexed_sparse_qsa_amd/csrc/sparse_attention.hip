@@ -34,10 +34,12 @@
 // columns (see "Tiles" below).
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "qsa_device.h"
 #include "qsa_launch.h"
+#include "select_core.h"
 
 namespace qsa {
 
@@ -241,9 +243,11 @@ __device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf
 
 // Runs the online softmax over list slots [32 * c0, n_slots), with chunk c0
 // already issued into fa and id_b holding the ids of chunk c0 + 1.
-// Processing stops at the first 32-slot chunk that holds no usable id.
-template <int D, int DT, class KV>
-__device__ void run_chunks(const int32_t *__restrict__ list, int n_slots, const KV &kv,
+// Processing stops at the first 32-slot chunk that holds no usable id.  The
+// list is a pointer to the ids in memory or a KeptList (ids made from kept
+// blocks in LDS); both are read as list[slot].
+template <int D, int DT, class KV, class L>
+__device__ void run_chunks(L list, int n_slots, const KV &kv,
                            const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
                            f32x4 (&acc)[8], u32x4 *ktile, int c0, Frag<D> &fa, int id_b) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
@@ -287,8 +291,12 @@ __device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV
                          f32x4 (&acc)[8], u32x4 *ktile, int c0 = 0) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int s = (c0 << 5) + (lane & 31);
-  const int id_a = s < n_slots ? list[s] : -1;
-  const int id_b = s + 32 < n_slots ? list[s + 32] : -1;
+  // unconditional loads (clamped to the list): a load on one branch only
+  // would be waited for on its own
+  const int raw_a = list[min(s, n_slots - 1)];
+  const int raw_b = list[min(s + 32, n_slots - 1)];
+  const int id_a = s < n_slots ? raw_a : -1;
+  const int id_b = s + 32 < n_slots ? raw_b : -1;
   if (!wave_any((unsigned)id_a < (unsigned)kv.limit)) return;
   Frag<D> fa;
   issue_chunk<D, DT>(fa, id_a, kv, q4, r16);
@@ -297,8 +305,8 @@ __device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV
 
 // run_chunks over a list from slot 0, with the raw ids of its first two
 // chunks already loaded (slots past n_slots read as -1).
-template <int D, int DT, class KV>
-__device__ void run_list_ids(const int32_t *__restrict__ list, int n_slots, const KV &kv,
+template <int D, int DT, class KV, class L>
+__device__ void run_list_ids(L list, int n_slots, const KV &kv,
                              const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
                              f32x4 (&acc)[8], u32x4 *ktile, int id_a, int id_b) {
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
@@ -308,11 +316,15 @@ __device__ void run_list_ids(const int32_t *__restrict__ list, int n_slots, cons
   run_chunks<D, DT>(list, n_slots, kv, qf, sl2, m_run, l_run, acc, ktile, 0, fa, id_b);
 }
 
+// Q rows of the GQA group as MFMA B fragments (columns past G are zero).
+// The loads are unconditional (a clamped row), so that none waits alone.
 template <int D>
 __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhead0, int G, int q4, int r16) {
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = (r16 < G) ? ld16(qhead0 + (size_t)r16 * D + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const u32x4 v = ld16(qhead0 + (size_t)min(r16, G - 1) * D + 32 * ks + 8 * q4);
+    qf[ks] = r16 < G ? v : u32x4{0u, 0u, 0u, 0u};
+  }
 }
 
 // Tiles.  Where a row's list covers a large part of its causal prefix —
@@ -586,10 +598,15 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, Tile
     // Q after the mask build, so that it does not stay live through it
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      const uint16_t *qh = a.q + (((size_t)b * a.S + t0 + r_col[u]) * a.Hq + (size_t)kvh * a.G + h) * D;
+      // unconditional loads: a dead column (past the sequence, or a head
+      // past G) reads a clamped row and head of this KV head's group
+      const uint16_t *qh =
+          a.q + (((size_t)b * a.S + min(t0 + r_col[u], a.S - 1)) * a.Hq + (size_t)kvh * a.G + min(h, a.G - 1)) * D;
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        qp[u][ks] = col_live[u] ? ld16(qh + 32 * ks + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const u32x4 v = ld16(qh + 32 * ks + 8 * q4);
+        qp[u][ks] = col_live[u] ? v : u32x4{0u, 0u, 0u, 0u};
+      }
     }
     const int srow = tid >> 4, piece = tid & 15;
     // dead columns (zero Q) get no key: with no key seen, a column's
@@ -961,6 +978,10 @@ struct DecLds {
   __device__ float *l(int w) const { return m(nw) + 16 * w; }
 };
 
+template <int D, int DT>
+__device__ __forceinline__ void decode_merge_store(const DecodeAttnArgs &a, const DecLds<D> &mg, int pair, int group,
+                                                   int br, int kvh, float m_run, float l_run, const f32x4 (&acc)[8]);
+
 // Lane (q, r) of wave w merges row r, dims [d0, d0 + D/16).
 template <int D, int DT>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_decode_kernel(DecodeAttnArgs a) {
@@ -980,10 +1001,14 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   // one round trip precedes the first gathers.
   const int s0 = split * a.split_slots;
   const int n_slots = split < a.nsplits ? min(a.top_k - s0, a.split_slots) : 0;
-  const int32_t *list = a.indices + (size_t)br * a.top_k + s0;
+  const int32_t *row_ids = a.indices + (size_t)br * a.top_k;
+  const int32_t *list = row_ids + s0;
   const int sl = lane & 31;
-  const int id_a = sl < n_slots ? list[sl] : -1;
-  const int id_b = sl + 32 < n_slots ? list[sl + 32] : -1;
+  // unconditional loads of the first two chunks' ids (clamped to the row)
+  const int raw_a = row_ids[min(s0 + sl, a.top_k - 1)];
+  const int raw_b = row_ids[min(s0 + sl + 32, a.top_k - 1)];
+  const int id_a = sl < n_slots ? raw_a : -1;
+  const int id_b = sl + 32 < n_slots ? raw_b : -1;
   u32x4 qf[D / 32];
   load_q<D>(qf, a.q + ((size_t)br * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
   const int ctx_in = a.ctx[b];
@@ -995,10 +1020,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     for (int i0 = threadIdx.x; i0 < npt; i0 += U * (int)blockDim.x) {
       int v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * (int)blockDim.x;
-        v[u] = i < npt ? ptb[i] : 0;
-      }
+      for (int u = 0; u < U; ++u) v[u] = ptb[min(i0 + u * (int)blockDim.x, npt - 1)];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u * (int)blockDim.x;
@@ -1023,6 +1045,17 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     kv.limit = ctx;
     run_list_ids<D, DT>(list, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile(wv), id_a, id_b);
   }
+  decode_merge_store<D, DT>(a, mg, pair, group, br, kvh, m_run, l_run, acc);
+}
+
+// The workgroup's splits (one per wave: m_run, l_run, acc) merged in split
+// order, then stored as output rows (one workgroup per pair) or as the
+// workgroup's partial.
+template <int D, int DT>
+__device__ __forceinline__ void decode_merge_store(const DecodeAttnArgs &a, const DecLds<D> &mg, int pair, int group,
+                                                   int br, int kvh, float m_run, float l_run, const f32x4 (&acc)[8]) {
+  const int wv = threadIdx.x >> 6, nw = mg.nw;
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   __syncthreads();  // every K tile is dead before the merge scratch is written
   float l = l_run + shfl_xor_f(l_run, 16);
   l += shfl_xor_f(l, 32);
@@ -1042,7 +1075,8 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 
   // Merge the workgroup's splits in split order.  The head dims form 16
   // slices of D/16; lane (q, r) of wave w takes row r and slices w*4+q,
-  // w*4+q + 4*nw, ...
+  // w*4+q + 4*nw, ...  The sums are explicit fmas, so that every kernel
+  // that inlines this merge (whatever it knows of nw) rounds them alike.
   constexpr int ND = D / 16;
   float M = -INFINITY;
   for (int w = 0; w < nw; ++w) M = fmaxf(M, mg.m(w)[r16]);
@@ -1051,7 +1085,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   for (int w = 0; w < kDecWaves; ++w) {
     const float mw = w < nw ? mg.m(w)[r16] : -INFINITY;
     sc[w] = mw == -INFINITY ? 0.f : exp2f(mw - M);
-    L += w < nw ? mg.l(w)[r16] * sc[w] : 0.f;
+    L = __builtin_fmaf(w < nw ? mg.l(w)[r16] : 0.f, sc[w], L);
   }
   if (r16 >= a.G) return;
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -1064,7 +1098,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     for (int w = 0; w < nw; ++w) {
       const float *src = mg.acc(w) + r16 * DecLds<D>::RS + d0;
 #pragma unroll
-      for (int j = 0; j < ND; ++j) o[j] += src[j] * sc[w];
+      for (int j = 0; j < ND; ++j) o[j] = __builtin_fmaf(src[j], sc[w], o[j]);
     }
     if (a.ngroups == 1) {
       uint16_t *out = a.o + ((size_t)br * a.Hq + (size_t)kvh * a.G + r16) * D + d0;
@@ -1123,6 +1157,139 @@ __global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs 
       w[k] = pack2<DT>(o[j + 2 * k] * inv, o[j + 2 * k + 1] * inv);
     st16(out + j, w);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Decode step: the indexer's select (decode B3) and the sparse decode in one
+// kernel.  One workgroup of kDecWaves waves per (sequence, KV head) reads
+// the sequence's block scores, runs the workgroup select (select_core.h) --
+// the workgroups of all KV heads of a sequence run the same select, so the
+// list never has to reach memory before the walk -- and walks that list
+// straight from LDS.  The workgroup of KV head 0 also stores the list, as
+// the indexer would.  The scores of the whole row width go out with the
+// context length, Q and the page-table rows (masked once the length is
+// known), so one round trip precedes the select and one more the first
+// gathers.  Splits, walk and merge are those of sparse_decode_kernel with
+// one workgroup per pair, so the output is the same bit for bit.
+// ---------------------------------------------------------------------------
+
+// The list of one decode row, made from its kept blocks lb (ascending):
+// slot i < head is token r*lb[i/r] + i%r, then the causal tail i + tail0
+// below len, then -1; s0 offsets the slots (a split's first slot).  With
+// head = 0 the list is 0..len-1.
+struct KeptList {
+  const uint16_t *lb;
+  int s0, r, head, len, tail0;
+  __device__ int operator[](int slot) const {
+    const int i = s0 + slot;
+    if (i < head) {
+      const int j = r == 4 ? i >> 2 : i / r;
+      return r * (int)lb[j] + (i - r * j);
+    }
+    return i < len ? i + tail0 : -1;
+  }
+};
+
+// LDS of the decode step: the select's histograms share the front with the
+// walk's tiles and merge scratch (the select ends before the walk starts),
+// then both page-table rows, then the kept blocks.
+template <int D>
+__host__ __device__ constexpr size_t step_front_bytes() {
+  return DecLds<D>::bytes(kDecWaves) > sizeof(WgSelLds<64 * kDecWaves>) ? DecLds<D>::bytes(kDecWaves)
+                                                                         : sizeof(WgSelLds<64 * kDecWaves>);
+}
+
+template <int D, int DT, int KPT>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_select_attend_kernel(
+    DecodeAttnArgs a) {
+  constexpr int NT = 64 * kDecWaves;
+  extern __shared__ __align__(16) unsigned char s_raw[];
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const DecLds<D> mg{s_raw, kDecWaves};
+  WgSelLds<NT> &sel = *reinterpret_cast<WgSelLds<NT> *>(s_raw);
+  int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + step_front_bytes<D>());  // [2][max_pages]
+  uint16_t *s_lb = reinterpret_cast<uint16_t *>(s_pt + 2 * a.max_pages);
+  const int pair = blockIdx.x;  // (sequence, KV head)
+  const int b = pair / a.Hkv, kvh = pair % a.Hkv;
+  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
+
+  const int ctx_in = a.ctx[b];
+  const float *srow = a.scores + (size_t)b * a.score_stride;
+  // Every load is unconditional (a load on one branch only makes the
+  // compiler wait for it where the branches join, one load at a time):
+  // slots past the row width read the row's last four scores and are
+  // masked once the context length is known.
+  const int i0 = tid * KPT;
+  float sv[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; j += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + min(i0 + j, a.score_stride - 4));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sv[j + c] = v[c];
+  }
+  u32x4 qf[D / 32];
+  load_q<D>(qf, a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
+  wg_select_clear<NT>(sel);
+  {
+    const int32_t *ptb = a.pt + (size_t)b * 2 * a.max_pages;  // rows 0 and 1 are contiguous
+    const int npt = 2 * a.max_pages;
+    constexpr int U = 4;
+    for (int k0 = tid; k0 < npt; k0 += U * NT) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ptb[min(k0 + u * NT, npt - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + u * NT;
+        if (k < npt) s_pt[k] = v[u];
+      }
+    }
+  }
+  __syncthreads();
+
+  // the row's list, as the indexer's decode select makes it
+  const int c = min(ctx_in, a.max_pages * 128);
+  const int r = a.ratio;
+  const int nc = c > 0 ? c / r : 0;
+  KeptList list{s_lb, 0, r, 0, c > 0 ? c : 0, 0};
+  if (nc > a.budget) {  // uniform over the workgroup
+    uint32_t key[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = i0 + j < nc ? score_key(sv[j]) : 0xffffffffu;
+    wg_select_blocks<NT, KPT>(key, a.budget, sel, s_lb);
+    list.head = r * a.budget;
+    list.len = list.head + c - r * nc;
+    list.tail0 = r * nc - list.head;
+  }
+  if (kvh == 0) {
+    int32_t *out = a.lists_out + (size_t)b * a.top_k;
+    for (int i = tid; i < a.top_k; i += NT) out[i] = list[i];
+  }
+
+  const int s0 = wv * a.split_slots;
+  const int n_slots = wv < a.nsplits ? min(a.top_k - s0, a.split_slots) : 0;
+  KeptList mine = list;
+  mine.s0 = s0;
+  const int sl = lane & 31;
+  const int raw_a = mine[sl], raw_b = mine[sl + 32];  // LDS reads, any slot
+  const int id_a = sl < n_slots ? raw_a : -1;
+  const int id_b = sl + 32 < n_slots ? raw_b : -1;
+  const int ctx = min(max(ctx_in, 0), a.max_pages * 128);
+  f32x4 acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  if (ctx > 0 && n_slots > 0) {
+    PagedKV kv;
+    kv.pool = a.pool + (size_t)kvh * a.PHD;
+    kv.pk = s_pt;
+    kv.pv = s_pt + a.max_pages;
+    kv.row_stride = (size_t)a.Hkv * a.PHD;
+    kv.num_flat_pages = a.num_flat_pages;
+    kv.limit = ctx;
+    run_list_ids<D, DT>(mine, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile(wv), id_a, id_b);
+  }
+  decode_merge_store<D, DT>(a, mg, pair, 0, b, kvh, m_run, l_run, acc);
 }
 
 // Tiles take rows t with t + 1 <= kTileRangeX2 / 2 * top_k * R / 16 (R rows
@@ -1262,6 +1429,31 @@ static hipError_t launch_decode_t(const DecodeAttnArgs &a, hipStream_t s) {
 hipError_t launch_sparse_decode(const DecodeAttnArgs &a, int D, int dt, hipStream_t s) {
   if (D == 128) return dt == DT_F16 ? launch_decode_t<128, DT_F16>(a, s) : launch_decode_t<128, DT_BF16>(a, s);
   return dt == DT_F16 ? launch_decode_t<64, DT_F16>(a, s) : launch_decode_t<64, DT_BF16>(a, s);
+}
+
+template <int D, int DT, int KPT>
+static hipError_t launch_step_t(const DecodeAttnArgs &a, hipStream_t s) {
+  // the kept-block list: the select runs only when budget < nc <= gmax
+  const size_t lb_bytes = ((size_t)std::min(a.budget, a.gmax) * sizeof(uint16_t) + 15) & ~(size_t)15;
+  const size_t lds = step_front_bytes<D>() + (size_t)2 * a.max_pages * sizeof(int32_t) + lb_bytes;
+  const void *fn = reinterpret_cast<const void *>(&decode_select_attend_kernel<D, DT, KPT>);
+  if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((decode_select_attend_kernel<D, DT, KPT>), dim3((unsigned)((long long)a.B * a.Hkv)),
+                     dim3(64 * kDecWaves), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int DT>
+static hipError_t launch_step_d(const DecodeAttnArgs &a, hipStream_t s) {
+  // thread j holds the scores of blocks [j*KPT, (j+1)*KPT)
+  if (a.gmax <= 64 * kDecWaves * 16) return launch_step_t<D, DT, 16>(a, s);
+  return launch_step_t<D, DT, 32>(a, s);
+}
+
+hipError_t launch_decode_select_attend(const DecodeAttnArgs &a, int D, int dt, hipStream_t s) {
+  if (a.gmax > kStepMaxBlocks || a.ngroups != 1 || a.wpg > kDecWaves) return hipErrorInvalidValue;
+  if (D == 128) return dt == DT_F16 ? launch_step_d<128, DT_F16>(a, s) : launch_step_d<128, DT_BF16>(a, s);
+  return dt == DT_F16 ? launch_step_d<64, DT_F16>(a, s) : launch_step_d<64, DT_BF16>(a, s);
 }
 
 }  // namespace qsa
