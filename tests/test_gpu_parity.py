@@ -568,6 +568,18 @@ def test_decode_small(case):
     decode_parity(inp, "decode small", splits=(0, 1, 2, 3, 4, 5, 8, 13, 16))
 
 
+@pytest.mark.parametrize("B", [512, 513])
+def test_decode_large_batch(B):
+    """Up to 512 sequences the decode scoring deals the batch's tiles out in
+    equal ranges over the chip; past that it takes a workgroup per 128
+    blocks of each sequence.  Both against the oracle on every row."""
+    rng = np.random.default_rng(B)
+    ctx = rng.integers(1, 3000, size=B)
+    ctx[:8] = [0, 1, 3, 4, 2048, 2051, 2052, 2999]
+    inp = syn.make_decode(14, ctx=ctx, B=B, Hq=8, Hkv=2, D=64, dtype="bf16", max_pages=24)
+    decode_parity(inp, f"decode batch {B}", splits=(0,))
+
+
 def test_sparse_decode_largest_page_table():
     """max_pages_per_seq = 4096, the largest the attention boundary accepts:
     the page-table copy in LDS takes the workgroup past 64 KB of LDS.  Lists

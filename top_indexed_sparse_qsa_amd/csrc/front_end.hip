@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void front_end_kernel(FrontEndArgs a) {
       const int b = (int)(r / a.S), t = (int)(r % a.S);
       const double pos = (double)((a.start ? a.start[b] : 0) + t);
       double sn, cs;
-      sincos(pos * a.freq[lane], &sn, &cs);
+      sincos_angle(pos * a.freq[lane], &sn, &cs);
       s_cs[wv][lane][0] = cs;
       s_cs[wv][lane][1] = sn;
     }
@@ -84,8 +84,7 @@ __global__ __launch_bounds__(256) void front_end_kernel(FrontEndArgs a) {
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < E; ++e) ss += x[e] * x[e];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    ss = wave_sum_f64(ss);
     const double den = sqrt(ss / (double)D + a.eps);
     double y[E];
 #pragma unroll

@@ -42,13 +42,13 @@ __device__ __forceinline__ Rope2 rope_at(double pos, const double *s_freq, int r
   Rope2 r{1.0, 0.0, 1.0, 0.0};
   const int d0 = lane, d1 = lane + 64;
   const int i0 = d0 < half ? d0 : d0 - half, i1 = d1 < half ? d1 : d1 - half;
-  if (d0 < rot) sincos(pos * s_freq[i0], &r.s0, &r.c0);
+  if (d0 < rot) sincos_angle(pos * s_freq[i0], &r.s0, &r.c0);
   if (d1 < rot) {
     if (d0 < rot && i1 == i0) {
       r.c1 = r.c0;
       r.s1 = r.s0;
     } else {
-      sincos(pos * s_freq[i1], &r.s1, &r.c1);
+      sincos_angle(pos * s_freq[i1], &r.s1, &r.c1);
     }
   }
   return r;
@@ -57,9 +57,7 @@ __device__ __forceinline__ Rope2 rope_at(double pos, const double *s_freq, int r
 // (o0, o1) = RoPE(x / sqrt(mean(x^2) + eps) * (1 + w)) for the lane's two dims.
 __device__ __forceinline__ void norm_rope2(double x0, double x1, double w0, double w1, double eps, int rot,
                                            const Rope2 &r, double &o0, double &o1) {
-  double ss = x0 * x0 + x1 * x1;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  const double ss = wave_sum_f64(x0 * x0 + x1 * x1);
   const double den = sqrt(ss / 128.0 + eps);
   const double y0 = x0 / den * (1.0 + w0), y1 = x1 / den * (1.0 + w1);
   const int lane = lane_id(), half = rot >> 1;
@@ -682,7 +680,7 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
 // ---------------------------------------------------------------------------
 // Select + expand, one 1024-thread workgroup per row: decode rows (one per
 // sequence, up to 32768 blocks), prefill rows over 8192 blocks and chunk
-// rows.  Thread j holds the KPT keys of blocks [j*KPT, (j+1)*KPT) in
+// rows.  Thread j holds four keys per round (blocks 4*1024*r + 4j + c) in
 // registers; the workgroup select (select_core.h) stages the kept block
 // indices in LDS, and the row is stored expanded, with the causal tail and
 // -1 padding, in one coalesced pass.
@@ -727,17 +725,17 @@ __global__ __launch_bounds__(kSelWgThreads) void idx_select_wg_kernel(IdxSelectA
     return;
   }
   wg_select_clear<NT>(s_sel);
+  // thread j's keys of round r: blocks 4*NT*r + 4j + c (unconditional loads,
+  // as in the per-row kernel)
   uint32_t key[KPT];
-  const int i0 = tid * KPT;
 #pragma unroll
-  for (int j = 0; j < KPT; j += 4) {
-    // unconditional loads, as in the per-row kernel
-    const int i = i0 + j;
+  for (int r = 0; r < KPT / 4; ++r) {
+    const int i = 4 * NT * r + 4 * tid;
     const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + min((long long)i, a.row_stride - 4));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) key[j + c] = i + c < nc ? score_key(v[c]) : 0xffffffffu;
+    for (int c = 0; c < 4; ++c) key[4 * r + c] = i + c < nc ? score_key(v[c]) : 0xffffffffu;
   }
-  wg_select_blocks<NT, KPT>(key, a.budget, s_sel, s_lb);
+  wg_select_blocks<NT, KPT>(key, nc, a.budget, s_sel, s_lb);
   const int head = r * a.budget;
   const int len = head + (t + 1) - r * nc;
   for (int i = tid; i < a.top_k; i += NT) {
@@ -777,7 +775,8 @@ __global__ __launch_bounds__(kSelWgThreads) void idx_select_wg_kernel(IdxSelectA
 constexpr int kDecScoreWaves = QSA_DEC_SCORE_WAVES;
 
 template <int DT>
-__global__ __launch_bounds__(64 * kDecScoreWaves) void idx_dec_score_kernel(IdxDecScoreArgs a) {
+__global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_per_eu(5))) void idx_dec_score_kernel(
+    IdxDecScoreArgs a) {
   constexpr int NP = QSplit<DT>::NP;
   constexpr int TPW = kScoreTilesPerWave;
   __shared__ __align__(16) float s_q[4][128];

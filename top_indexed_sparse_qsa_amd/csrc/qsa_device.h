@@ -110,4 +110,49 @@ __device__ __forceinline__ uint32_t u4_at(const u32x4 &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// ---------------------------------------------------------------------------
+// fp64 helpers of the query / key preparation (RMSNorm and RoPE in fp64).
+// ---------------------------------------------------------------------------
+// sin and cos of an angle |x| < 2^24 (positions below 2^24 times
+// frequencies <= 1): x - k*pi/2 with pi/2 split into parts of 29, 25 and 53
+// significant bits (so k*P1 and k*P2 are exact for |k| < 2^24; the reduced
+// argument is within ~1e-16 of the exact one), then the library sincos on
+// |r| <= pi/4 and the quadrant k mod 4.  This keeps the library's reduction
+// of large arguments (a table walk) off the query prep's critical path.
+__device__ __forceinline__ void sincos_angle(double x, double *s, double *c) {
+  constexpr double kTwoOverPi = 0.6366197723675814;
+  const double P1 = 0x1.921fb54p+0, P2 = 0x1.10b461p-30, P3 = 0x1.a62633145c06ep-58;
+  const double k = rint(x * kTwoOverPi);
+  const double r = ((x - k * P1) - k * P2) - k * P3;
+  double sr, cr;
+  sincos(r, &sr, &cr);
+  const int q = (int)k & 3;
+  *s = q == 0 ? sr : q == 1 ? cr : q == 2 ? -sr : -cr;
+  *c = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
+}
+
+// One DPP step of a wave scan on a double (both 32-bit halves move).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWMASK, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWMASK, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Sum of v over the wave, in every lane: an inclusive DPP scan (row shifts,
+// then the row broadcasts of lanes 15 and 31), and lane 63's total.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_f64<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_f64<0x142, 0xa>(v);  // row_bcast:15
+  v += dpp_f64<0x143, 0xc>(v);  // row_bcast:31
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 }  // namespace qsa

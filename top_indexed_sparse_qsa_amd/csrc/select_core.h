@@ -60,10 +60,11 @@ __device__ __forceinline__ uint32_t wave_incl_op(uint32_t v, uint32_t id, Op op)
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup select: NT threads, thread j holding the KPT keys of blocks
-// [j*KPT, (j+1)*KPT) in registers (slots past the row hold 0xffffffff: real
-// keys have bit 31 clear), so one workgroup scan of per-thread counts
-// places kept blocks in ascending order.
+// Workgroup select over the keys of one row: NT threads, thread j holding in
+// round r the four keys of blocks 4*NT*r + 4j + c (c < 4; KPT/4 rounds; one
+// float4 load each, coalesced across the workgroup).  Slots past the row
+// hold 0xffffffff (real keys have bit 31 clear); a wave skips the rounds
+// that start past the row.
 //
 // The cut is narrowed over key ranges [lo, hi) rather than bit prefixes.
 // Zero scores (every head's relu zero) are left out of the first range:
@@ -75,20 +76,31 @@ __device__ __forceinline__ uint32_t wave_incl_op(uint32_t v, uint32_t id, Op op)
 // spreads them over far more bins than a window aligned to the bits all
 // keys share would, and four passes always reach single keys.  A pass is
 // one barrier: the keys count into an LDS histogram (plain atomic
-// increments), and then every wave reads the whole histogram and finds the
-// cut bin for itself (DPP scans over lane sums of bins, then within the one
-// lane's range that holds it), so nothing is broadcast.  Each pass has a
-// histogram of its own, all cleared at the start.
+// increments, under a wave-uniform branch; lanes whose key is outside the
+// range add to one of 32 spare words instead, so no lane is masked off), and
+// then every wave reads the whole histogram and finds the cut bin for itself
+// (DPP scans over lane sums of bins, then within the one lane's range that
+// holds it), so nothing is broadcast.  Each pass has a histogram of its own,
+// all cleared at the start.
+//
+// Emission: every lane stores one byte per round, its four blocks' "above
+// the cut" bits in the low nibble and "in the cut bin" bits in the high one;
+// after a barrier thread j turns bytes [8j, 8j+8) into the two 32-bit masks
+// of blocks [32j, 32j+32), and one workgroup scan of their counts places the
+// kept blocks in ascending order (those above the cut, then the lowest-index
+// ones of the cut bin up to the budget).
 // ---------------------------------------------------------------------------
 constexpr int kSelSmallWords = ((hpad(255) + 4 + 3) / 4) * 4;  // a padded 256-bin histogram
+constexpr int kSelTrash = 32;                                    // spare words after each histogram
 
 template <int NT>
 struct alignas(16) WgSelLds {
   static constexpr int NW = NT / 64;
-  uint32_t hist[kSelHistWords];         // pass 0 (up to 2048 bins)
-  uint32_t small[3][kSelSmallWords];    // passes 1..3 (up to 256 bins)
-  uint32_t red[3 * NW];                 // per wave: largest key, smallest non-zero key, non-zero count
-  int wt[NW];                           // the emission scan
+  uint32_t hist[kSelHistWords + kSelTrash];         // pass 0 (up to 2048 bins)
+  uint32_t small[3][kSelSmallWords + kSelTrash];    // passes 1..3 (up to 256 bins)
+  uint32_t red[3 * NW];   // per wave: largest key, smallest non-zero key, non-zero count
+  int wt[NW];             // the emission scan
+  uint8_t flags[8 * NT];  // per 4 blocks: above-cut bits | in-cut-bin bits << 4
 };
 
 // Exclusive prefix sum of v over the workgroup in thread order, with one
@@ -117,10 +129,20 @@ __device__ __forceinline__ int wg_exscan(int v, int *s_wt, int *total) {
 // barrier.
 template <int NT>
 __device__ __forceinline__ void wg_select_clear(WgSelLds<NT> &S) {
-  constexpr int kVecs = (kSelHistWords + 3 * kSelSmallWords) / 4;
-  static_assert(sizeof(S.hist) + sizeof(S.small) == 16 * kVecs, "histograms are whole 16-byte words");
+  constexpr int kVecs = (sizeof(S.hist) + sizeof(S.small)) / 16;
+  static_assert(sizeof(S.hist) % 16 == 0 && sizeof(S.small) % 16 == 0, "histograms are whole 16-byte words");
   u32x4 *h = reinterpret_cast<u32x4 *>(S.hist);
   for (int j = threadIdx.x; j < kVecs; j += NT) h[j] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Eight bytes (little-endian in v) -> the 32-bit word of their low nibbles
+// in order (byte j's nibble at bits 4j..4j+3).
+__device__ __forceinline__ uint32_t low_nibbles(unsigned long long v) {
+  v &= 0x0F0F0F0F0F0F0F0Full;
+  v = (v | (v >> 4)) & 0x00FF00FF00FF00FFull;
+  v = (v | (v >> 8)) & 0x0000FFFF0000FFFFull;
+  v = (v | (v >> 16)) & 0x00000000FFFFFFFFull;
+  return (uint32_t)v;
 }
 
 // The cut bin of one pass, found by one wave from the histogram H of nb
@@ -150,24 +172,31 @@ __device__ __forceinline__ void sel_find_cut(const uint32_t *H, int nb, int rema
   cnt = __builtin_amdgcn_readlane(hb, js);
 }
 
-// Keeps `budget` (< the number of real keys) of the workgroup's keys and
-// writes the kept block indices (thread j's key i is block j*KPT + i) to
-// lb[0, budget) in ascending order.  The histograms must have been cleared
-// by wg_select_clear.  Ends with a barrier: lb is complete on return.
+// Keeps `budget` (< the number of real keys, nc the row length) of the
+// workgroup's keys and writes the kept block indices to lb[0, budget) in
+// ascending order.  The histograms must have been cleared by
+// wg_select_clear.  Ends with a barrier: lb is complete on return.
 template <int NT, int KPT>
-__device__ void wg_select_blocks(const uint32_t (&key)[KPT], int budget, WgSelLds<NT> &S, uint16_t *lb) {
-  constexpr int NW = NT / 64;
-  static_assert(KPT <= 32, "per-thread key masks are 32 bits");
+__device__ void wg_select_blocks(const uint32_t (&key)[KPT], int nc, int budget, WgSelLds<NT> &S, uint16_t *lb) {
+  constexpr int NW = NT / 64, R = KPT / 4;
+  static_assert(KPT % 4 == 0 && NT * KPT <= 8 * NT * 4, "four keys per round, at most 32 per thread");
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
-  const int i0 = tid * KPT;
+  // rounds this wave holds real keys in (wave-uniform)
+  const int nrw = __builtin_amdgcn_readfirstlane(
+      nc > 256 * wv ? min(R, (nc - 256 * wv + 4 * NT - 1) / (4 * NT)) : 0);
   uint32_t kmax = 0u, kmin = 0xffffffffu, nnz = 0u;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t k = key[j];
-    const bool nz = (int)k > 0;  // real and non-zero
-    kmax = (int)k >= 0 ? max(kmax, k) : kmax;
-    kmin = nz ? min(kmin, k) : kmin;
-    nnz += nz ? 1u : 0u;
+  for (int r = 0; r < R; ++r) {
+    if (r < nrw) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t k = key[4 * r + c];
+        const bool nz = (int)k > 0;  // real and non-zero
+        kmax = (int)k >= 0 ? max(kmax, k) : kmax;
+        kmin = nz ? min(kmin, k) : kmin;
+        nnz += nz ? 1u : 0u;
+      }
+    }
   }
   kmax = wave_incl_op(kmax, 0u, [](uint32_t x, uint32_t y) { return max(x, y); });
   kmin = wave_incl_op(kmin, 0xffffffffu, [](uint32_t x, uint32_t y) { return min(x, y); });
@@ -203,10 +232,17 @@ __device__ void wg_select_blocks(const uint32_t (&key)[KPT], int budget, WgSelLd
       const int s = max(0, bl - (pass == 0 ? 11 : 8));
       const int nb = (((int)((range - 1u) >> s) >> 8) + 1) << 8;  // bins in use, rounded up to 256
       uint32_t *H = pass == 0 ? S.hist : S.small[pass - 1];
+      uint32_t *spare = H + (pass == 0 ? kSelHistWords : kSelSmallWords) + (lane & (kSelTrash - 1));
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const uint32_t k = key[j];
-        if (k >= lo && k < hi) atomicAdd(&H[hpad((int)((k - lo) >> s))], 1u);
+      for (int r = 0; r < R; ++r) {
+        if (r < nrw) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t k = key[4 * r + c];
+            const bool in = k >= lo && k < hi;
+            if (__ballot(in) != 0ull) atomicAdd(in ? &H[hpad((int)((k - lo) >> s))] : spare, 1u);
+          }
+        }
       }
       __syncthreads();
       int dsel, above, cnt;
@@ -218,15 +254,28 @@ __device__ void wg_select_blocks(const uint32_t (&key)[KPT], int budget, WgSelLd
     }
   }
 
-  // Keys >= hi are kept; of those in [lo, hi), the first `remaining` in
-  // index order (all of them when the cut bin is kept whole).  Bit j of
-  // gt_bits / eq_bits: key j above / inside the cut bin.
-  uint32_t gt_bits = 0u, eq_bits = 0u;
+  // Per round a byte per lane: bit c = block 4*NT*r + 4*tid + c above the
+  // cut (>= hi), bit 4 + c = inside the cut bin ([lo, hi)).  Every round is
+  // stored (past the row both nibbles are 0), so the bytes of [0, NT*KPT)
+  // are all written.
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t k = key[j];
-    gt_bits |= ((int)k >= 0 && k >= hi) ? 1u << j : 0u;
-    eq_bits |= (k >= lo && k < hi) ? 1u << j : 0u;
+  for (int r = 0; r < R; ++r) {
+    uint32_t byte = 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t k = key[4 * r + c];
+      byte |= ((int)k >= 0 && k >= hi) ? 1u << c : 0u;
+      byte |= (k >= lo && k < hi) ? 16u << c : 0u;
+    }
+    S.flags[NT * r + tid] = (uint8_t)byte;
+  }
+  __syncthreads();
+  // thread j: blocks [32j, 32j+32), bytes [8j, 8j+8)
+  uint32_t gt_bits = 0u, eq_bits = 0u;
+  if (32 * tid < NT * KPT) {
+    const unsigned long long v = *reinterpret_cast<const unsigned long long *>(&S.flags[8 * tid]);
+    gt_bits = low_nibbles(v);
+    eq_bits = low_nibbles(v >> 4);
   }
   const int n_gt = __builtin_popcount(gt_bits), n_eq = __builtin_popcount(eq_bits);
   // One scan of both counts (n_gt in the high half: fewer than budget < nc
@@ -238,8 +287,7 @@ __device__ void wg_select_blocks(const uint32_t (&key)[KPT], int budget, WgSelLd
   const int eq_before = both & 0xffff;
   const int take_eq = min(n_eq, max(0, remaining - eq_before));
   int pos = (both >> 16) + min(eq_before, remaining);
-  // kept keys: those above the cut and the lowest take_eq in it; the
-  // emission visits set bits only (a thread keeps few of its KPT keys)
+  // kept: above the cut, and the lowest take_eq of the cut bin
   uint32_t keep = gt_bits;
   for (int e = 0; e < take_eq; ++e) {
     keep |= eq_bits & (0u - eq_bits);
@@ -248,7 +296,7 @@ __device__ void wg_select_blocks(const uint32_t (&key)[KPT], int budget, WgSelLd
   while (keep != 0u) {
     const int j = __builtin_ctz(keep);
     keep &= keep - 1u;
-    lb[pos++] = (uint16_t)(i0 + j);
+    lb[pos++] = (uint16_t)(32 * tid + j);
   }
   __syncthreads();
 }

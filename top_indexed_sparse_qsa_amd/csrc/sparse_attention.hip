@@ -1219,13 +1219,13 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   // compiler wait for it where the branches join, one load at a time):
   // slots past the row width read the row's last four scores and are
   // masked once the context length is known.
-  const int i0 = tid * KPT;
+  // Thread j's keys of round r are blocks 4*NT*r + 4j + c (select_core.h).
   float sv[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; j += 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + min(i0 + j, a.score_stride - 4));
+  for (int r = 0; r < KPT / 4; ++r) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + min(4 * NT * r + 4 * tid, a.score_stride - 4));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sv[j + c] = v[c];
+    for (int c = 0; c < 4; ++c) sv[4 * r + c] = v[c];
   }
   u32x4 qf[D / 32];
   load_q<D>(qf, a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
@@ -1255,8 +1255,8 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   if (nc > a.budget) {  // uniform over the workgroup
     uint32_t key[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = i0 + j < nc ? score_key(sv[j]) : 0xffffffffu;
-    wg_select_blocks<NT, KPT>(key, a.budget, sel, s_lb);
+    for (int j = 0; j < KPT; ++j) key[j] = 4 * NT * (j >> 2) + 4 * tid + (j & 3) < nc ? score_key(sv[j]) : 0xffffffffu;
+    wg_select_blocks<NT, KPT>(key, nc, a.budget, sel, s_lb);
     list.head = r * a.budget;
     list.len = list.head + c - r * nc;
     list.tail0 = r * nc - list.head;
