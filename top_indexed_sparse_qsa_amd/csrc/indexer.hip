@@ -433,20 +433,21 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
 // row per 128-thread workgroup: half the keys and registers per wave, so
 // long rows run at higher occupancy and half the latency).  Wave h holds
 // the keys of blocks h*64*KPL + 256g + 4l + c (lane l, g < KPL/4, c < 4),
-// loaded as float4s; slots past the row hold 0xffffffff, which no radix
-// prefix matches (real keys have bit 31 clear).  All keys lie in
-// [kmin, kmax] and share the bits above the highest bit where those two
-// differ; the first radix window (11 bits) starts there, later windows take
-// 8 bits.  The row's histogram lives in LDS (plain atomic increments: the
-// adaptive window spreads the digits); the first wave finds the cut bin with
-// DPP scans of per-lane bin sums, then inside the one lane range that holds
-// it.  The select stops as soon as the cut bin holds exactly the keys still
-// needed (the usual case); otherwise it refines until all 32 bits are fixed
-// and keeps the lowest-index keys equal to the cut.  Emission keeps index
-// order: per 256-block group, ballots of the kept slots and mbcnt give each
-// lane its positions.  Each wave stages its kept blocks in its own LDS list
-// (when the lists fit), and the row is stored with the causal tail and -1
-// padding in one coalesced pass.
+// loaded as float4s; slots past the row hold 0xffffffff (real keys have
+// bit 31 clear).  The cut is narrowed over key ranges as in the workgroup
+// select (select_core.h): the first range runs from the smallest non-zero
+// key to the largest in up to 2048 bins, later ones split the cut bin into
+// up to 256; the row's histogram lives in LDS (plain atomic increments under
+// a wave-uniform branch, keys outside the range into spare words), and
+// every wave of the row finds the cut bin itself with DPP scans of per-lane
+// bin sums, then inside the one lane range that holds it.  The select stops
+// as soon as the cut bin holds exactly the keys still needed (the usual
+// case); otherwise it refines to single keys and keeps the lowest-index
+// keys equal to the cut.  Emission keeps index order: per 256-block group,
+// ballots of the kept slots and mbcnt give each lane its positions.  Each
+// wave stages its kept blocks in its own LDS list (when the lists fit), and
+// the row is stored with the causal tail and -1 padding in one coalesced
+// pass.
 // ---------------------------------------------------------------------------
 template <int NW>
 __device__ __forceinline__ void row_sync() {
@@ -484,7 +485,8 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   // Staged lists hold the kept block indices (16 bits: blocks < QSA_MAX_BLOCKS),
   // a.list_words words per wave.  One wave: the list overlays the histogram;
   // two waves: [hist | list0 | list1].  Unstaged: expanded ids go straight out.
-  uint16_t *lb0 = reinterpret_cast<uint16_t *>(region + (NW == 1 ? 0 : kSelHistWords));
+  uint16_t *lb0 =
+      reinterpret_cast<uint16_t *>(region + (NW == 1 ? 0 : kSelHistWords + kSelTrash + kSelSmallWords + kSelTrash));
   uint16_t *lb = lb0 + 2 * h * a.list_words;
   const float *srow = a.scores + ((size_t)b * a.S + t) * a.row_stride;
   const int base_i = h * SPAN;
@@ -498,111 +500,101 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) key[4 * g + c] = i0 + c < nc ? score_key(v[c]) : 0xffffffffu;
   }
-  uint32_t kmax = 0, kmin = 0x7fffffffu;
+  // Largest key, smallest non-zero key and the non-zero count (groups of
+  // 256 blocks that start past the row hold no real key: skipped).
+  uint32_t kmax = 0u, kmin = 0xffffffffu, nnz = 0u;
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
+  for (int g = 0; g < NG; ++g) {
+    if (base_i + 256 * g < nc) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t k = key[4 * g + c];
-      if ((int)k >= 0) {
-        kmax = max(kmax, k);
-        kmin = min(kmin, k);
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t k = key[4 * g + c];
+        const bool nz = (int)k > 0;
+        kmax = (int)k >= 0 ? max(kmax, k) : kmax;
+        kmin = nz ? min(kmin, k) : kmin;
+        nnz += nz ? 1u : 0u;
       }
     }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
   }
+  kmax = __builtin_amdgcn_readlane(wave_incl_op(kmax, 0u, [](uint32_t x, uint32_t y) { return max(x, y); }), 63);
+  kmin = __builtin_amdgcn_readlane(
+      wave_incl_op(kmin, 0xffffffffu, [](uint32_t x, uint32_t y) { return min(x, y); }), 63);
+  nnz = __builtin_amdgcn_readlane(wave_incl_op(nnz, 0u, [](uint32_t x, uint32_t y) { return x + y; }), 63);
   if constexpr (NW == 2) {
     if (lane == 0) {
       s_x[wv][0] = (int)kmax;
       s_x[wv][1] = (int)kmin;
+      s_x[wv][2] = (int)nnz;
     }
     __syncthreads();
     kmax = max((uint32_t)s_x[0][0], (uint32_t)s_x[1][0]);
     kmin = min((uint32_t)s_x[0][1], (uint32_t)s_x[1][1]);
+    nnz = (uint32_t)(s_x[0][2] + s_x[1][2]);
   }
-  const uint32_t diff = kmax ^ kmin;
-  int top = diff ? 31 - __clz((int)diff) : -1;  // highest differing bit (< 31)
-  uint32_t pmask = top < 0 ? 0xffffffffu : ~((2u << top) - 1u);
-  uint32_t prefix = kmax & pmask;
+  // The cut is narrowed over key ranges [lo, hi) as in the workgroup select
+  // (select_core.h): zeros are left out of the first range unless fewer than
+  // `budget` keys are non-zero; the first pass takes up to 2048 bins, later
+  // ones 256.  Keys outside the range count into spare words (no lane is
+  // masked off); two-wave rows alternate two histograms, so a wave may clear
+  // the next pass's while the other still reads this one's.
+  uint32_t lo, hi;
   int remaining = a.budget;
   bool whole_bin = false;
-  for (int pass = 0; top >= 0; ++pass) {
-    const int w = sel_window(pass, top), shift = top + 1 - w;
-    const uint32_t dmask = (1u << w) - 1u;
-    const int nb = 1 << w;
-    const int nvec = (hpad(nb - 1) + 4) >> 2;
-    for (int j = tid; j < nvec; j += nthr) reinterpret_cast<u32x4 *>(hist)[j] = u32x4{0u, 0u, 0u, 0u};
-    row_sync<NW>();
+  if ((int)nnz < a.budget) {  // every non-zero key, then the first zeros
+    lo = 0u;
+    hi = 1u;
+    remaining = a.budget - (int)nnz;
+  } else {
+    lo = kmin;
+    hi = kmax + 1u;
+    for (int pass = 0; pass < 4; ++pass) {
+      const uint32_t range = hi - lo;
+      const int bl = range > 1u ? 32 - __clz((int)(range - 1u)) : 0;
+      const int s = max(0, bl - (pass == 0 ? 11 : 8));
+      const int nb = (((int)((range - 1u) >> s) >> 8) + 1) << 8;  // bins in use, rounded up to 256
+      uint32_t *H = NW == 2 && (pass & 1) ? region + kSelHistWords + kSelTrash : hist;
+      uint32_t *spare = H + (H == hist ? kSelHistWords : kSelSmallWords) + (lane & (kSelTrash - 1));
+      const int nvec = (hpad(nb - 1) + 4) >> 2;
+      for (int j = tid; j < nvec; j += nthr) reinterpret_cast<u32x4 *>(H)[j] = u32x4{0u, 0u, 0u, 0u};
+      row_sync<NW>();
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (base_i + 256 * g < nc) {
+      for (int g = 0; g < NG; ++g) {
+        if (base_i + 256 * g < nc) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t k = key[4 * g + c];
-          if ((k & pmask) == prefix) atomicAdd(&hist[hpad((int)((k >> shift) & dmask))], 1u);
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t k = key[4 * g + c];
+            const bool in = k >= lo && k < hi;
+            if (__ballot(in) != 0ull) atomicAdd(in ? &H[hpad((int)((k - lo) >> s))] : spare, 1u);
+          }
         }
       }
-    }
-    row_sync<NW>();
-    int dsel = 0, above = 0, cnt = 0;
-    if (h == 0) {
-      // lane l sums bins [nb - per*(l+1), nb - per*l): lane 0 holds the top digits
-      const int per = (nb + 63) >> 6;
-      const int lo = nb - per * (lane + 1);
-      int lsum = 0;
-      if (per >= 4) {
-        for (int j = 0; j < per; j += 4) {
-          const u32x4 hv = *reinterpret_cast<const u32x4 *>(hist + hpad(lo + j));
-          lsum += (int)(hv[0] + hv[1] + hv[2] + hv[3]);
-        }
-      } else if (lo >= 0) {
-        for (int j = 0; j < per; ++j) lsum += (int)hist[hpad(lo + j)];
+      row_sync<NW>();
+      int dsel, above, cnt;
+      sel_find_cut(H, nb, remaining, dsel, above, cnt);  // every wave of the row
+      remaining -= above;
+      lo += (uint32_t)dsel << s;
+      hi = min(hi, lo + (1u << s));
+      if (cnt == remaining) {  // the whole bin is kept
+        whole_bin = true;
+        break;
       }
-      const int incl = wave_incl_scan(lsum);
-      const int src = __ffsll((long long)__ballot(incl - lsum < remaining && incl >= remaining)) - 1;
-      const int above0 = __builtin_amdgcn_readlane(incl - lsum, src);
-      // inside lane src's range, top digit first
-      const int hb = lane < per ? (int)hist[hpad(nb - 1 - (src * per + lane))] : 0;
-      const int incl2 = above0 + wave_incl_scan(hb);
-      const int js = __ffsll((long long)__ballot(incl2 - hb < remaining && incl2 >= remaining)) - 1;
-      dsel = nb - 1 - (src * per + js);
-      above = __builtin_amdgcn_readlane(incl2 - hb, js);
-      cnt = __builtin_amdgcn_readlane(hb, js);
-      if (NW == 2 && lane == 0) {
-        s_x[2][0] = dsel;
-        s_x[2][1] = above;
-        s_x[2][2] = cnt;
-      }
+      if (s == 0) break;  // single keys: the lowest-index ones of the cut key are kept
     }
-    if constexpr (NW == 2) {
-      __syncthreads();
-      dsel = __builtin_amdgcn_readfirstlane(s_x[2][0]);
-      above = __builtin_amdgcn_readfirstlane(s_x[2][1]);
-      cnt = __builtin_amdgcn_readfirstlane(s_x[2][2]);
-    }
-    prefix |= (uint32_t)dsel << shift;
-    pmask |= dmask << shift;
-    remaining -= above;
-    if (cnt == remaining) {  // the whole bin is kept
-      whole_bin = true;
-      break;
-    }
-    top = shift - 1;
   }
 
-  // Keys with (k & pmask) > prefix are kept; of those == prefix, the first
-  // `remaining` in index order (all of them when whole_bin).  Masked keys
-  // compare as signed: the empty-slot marker has bit 31 set, real ones not.
+  // Keys >= hi are kept; of those in [lo, hi), the first `remaining` in
+  // index order (all of them when whole_bin).  The empty-slot marker
+  // (0xffffffff) is above every range and never counts as real.
   int eq_seen = 0;
-  if (NW == 2 && !whole_bin) {  // the second wave's equal keys follow the first's
+  if (NW == 2 && !whole_bin) {  // the second wave's cut-bin keys follow the first's
     int ec = 0;
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) ec += __popcll(__ballot((key[4 * g + c] & pmask) == prefix));
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t k = key[4 * g + c];
+        ec += __popcll(__ballot(k >= lo && k < hi));
+      }
     if (lane == 0) s_x[wv][3] = ec;
     __syncthreads();
     eq_seen = h == 1 ? s_x[0][3] : 0;
@@ -614,16 +606,16 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
       bool kc[4];
       if (whole_bin) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kc[c] = (int)(key[4 * g + c] & pmask) >= (int)prefix;
+        for (int c = 0; c < 4; ++c) kc[c] = (int)key[4 * g + c] >= 0 && key[4 * g + c] >= lo;
       } else {
         bool eq[4];
         unsigned long long em[4];
         int er = eq_seen;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t m = key[4 * g + c] & pmask;
-          kc[c] = (int)m > (int)prefix;
-          eq[c] = m == prefix;
+          const uint32_t k = key[4 * g + c];
+          kc[c] = (int)k >= 0 && k >= hi;
+          eq[c] = k >= lo && k < hi;
           em[c] = __ballot(eq[c]);
           er += lanes_below(em[c]);
         }
@@ -963,13 +955,13 @@ static void launch_select_rows(IdxSelectArgs a, int row0, int nrows, hipStream_t
   if (NW == 1) {  // lists staged over the histogram when they fit, else written straight out
     stage = list_words <= kSelHistWords;
     a.list_words = list_words;
-    a.wave_words = kSelHistWords;
+    a.wave_words = kSelHistWords + kSelTrash;
     grid = (unsigned)((nrows + 3) / 4);
     block = 256;
-  } else {        // the launcher only picks two waves when both lists fit
+  } else {        // [histogram | second histogram | list0 | list1]; two waves only when both lists fit
     stage = true;
     a.list_words = list_words;
-    a.wave_words = kSelHistWords + 2 * list_words;
+    a.wave_words = kSelHistWords + kSelTrash + kSelSmallWords + kSelTrash + 2 * list_words;
     grid = (unsigned)nrows;
     block = 128;
   }
