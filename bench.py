@@ -52,7 +52,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_prefill_traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "top_indexed_sparse_qsa_amd", "csrc", "sparse_attention.hip")
+# the code the prefill attention kernels are built from
+KERNEL_SRCS = [os.path.join(ROOT, "top_indexed_sparse_qsa_amd", "csrc", f)
+               for f in ("sparse_attention.hip", "attention_core.h", "qsa_device.h")]
 METRIC = "sparse prefill tokens/s + decode seqs/s (topK 2051); % HBM roofline"
 PREFILL_WORKLOADS = (1, 2, 3, 5)
 DECODE_WORKLOAD = 4
@@ -519,16 +521,18 @@ def attach_ceiling_fracs(line, ceil):
 # ---------------------------------------------------------------------------
 # HBM counter figures
 # ---------------------------------------------------------------------------
-def kernel_code_sha256(path=None):
-    """sha256 of the attention kernel source with its comments and blank
-    space removed, so that the counter figures survive comment edits but
-    not code changes."""
+def kernel_code_sha256(paths=None):
+    """sha256 of the prefill attention kernels' sources with their comments
+    and blank space removed, so that the counter figures survive comment
+    edits but not code changes."""
     import hashlib
     import re
-    with open(path or KERNEL_SRC) as f:
-        text = re.sub(r"//[^\n]*|/\*.*?\*/", "", f.read(), flags=re.S)
-    code = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
-    return hashlib.sha256(code.encode()).hexdigest()
+    code = []
+    for path in paths or KERNEL_SRCS:
+        with open(path) as f:
+            text = re.sub(r"//[^\n]*|/\*.*?\*/", "", f.read(), flags=re.S)
+        code.append("\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip()))
+    return hashlib.sha256("\n\f\n".join(code).encode()).hexdigest()
 
 
 def measured_traffic(wl):

@@ -260,14 +260,18 @@ def test_bench_counter_figures_follow_kernel_code(tmp_path):
     code is unchanged: a comment or whitespace edit keeps the key, a code
     edit changes it."""
     import bench
-    src = open(bench.KERNEL_SRC).read()
+    src = open(bench.KERNEL_SRCS[0]).read()
+    rest = bench.KERNEL_SRCS[1:]
     base = bench.kernel_code_sha256()
     edited = tmp_path / "comments.hip"
     edited.write_text("// a new comment\n" + src.replace("\n", "\n\n", 3) + "\n/* trailing */\n")
-    assert bench.kernel_code_sha256(str(edited)) == base
+    assert bench.kernel_code_sha256([str(edited)] + rest) == base
     changed = tmp_path / "code.hip"
     changed.write_text(src.replace("kTileRangeX2 = QSA_TILE_RANGE_X2", "kTileRangeX2 = QSA_TILE_RANGE_X2 + 1", 1))
-    assert bench.kernel_code_sha256(str(changed)) != base
+    assert bench.kernel_code_sha256([str(changed)] + rest) != base
+    # the shared chunk machinery counts too; the decode kernels do not
+    assert any(p.endswith("attention_core.h") for p in rest)
+    assert not any(p.endswith("decode_attention.hip") for p in bench.KERNEL_SRCS)
 
 
 def test_product_path_and_oracle_are_separate():

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqsa.so")
-SOURCES = ["api.cpp", "indexer.hip", "sparse_attention.hip", "noalloc.hip", "front_end.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "sparse_attention.hip", "decode_attention.hip", "noalloc.hip", "front_end.hip"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -29,7 +29,7 @@ COMMON = [
 ]
 # The kernels take finite inputs: without NaN semantics a max (softmax,
 # relu) needs no quieting of MFMA results.
-EXTRA = {"sparse_attention.hip": ["-fno-honor-nans"], "indexer.hip": ["-fno-honor-nans"],
+EXTRA = {"sparse_attention.hip": ["-fno-honor-nans"], "decode_attention.hip": ["-fno-honor-nans"], "indexer.hip": ["-fno-honor-nans"],
          "front_end.hip": ["-fno-honor-nans"]}
 
 

@@ -1,331 +1,22 @@
-// Sparse GQA attention over index lists: prefill (dense BSND K/V) and
-// single-token split-K decode (paged pool).
-//
-// Contract: TensorRT-Edge-LLM "Cute Dsl Qsa Sparse Runner", structs
-// QsaSparsePrefillParams and QsaSparseDecodeParams -- lists of distinct ids,
-// -1 padded on the right, no positional mask, zero rows past the live
-// length, only pool columns [0, headDim) read, V page ids pre-offset.
-//
-// Work split: one wave per (query row, KV head) in prefill and per (sequence,
-// KV head, split) in decode.  The GQA head group of one KV head (up to 16
-// query heads) is the 16-wide MFMA tile.  Per chunk of 32 list slots a wave
-//   * gathers the 32 K rows and the 32 V rows with each 16-lane group
-//     reading whole 256-byte rows (a row per 16 lanes is ~3x the L1
-//     throughput of spreading one load instruction over 16 rows), so lane
-//     (q, c) holds dims 8c..8c+7 of eight keys ("key slots") of K and of V,
-//   * writes its K rows to a per-wave LDS tile (16-byte pieces XOR-swizzled
-//     by row) and reads them back as MFMA A fragments, both conflict-free,
-//   * computes S^T = K Q^T (two 16-key tiles), so every lane ends up owning
-//     the scores of one query head m = lane % 16 for its eight key slots,
-//   * runs the fp32 online softmax in the exp2 domain,
-//   * feeds those eight probabilities, unchanged in place, as the B operand
-//     of O^T += V^T P^T; the V^T A-operand is an in-register 8x8 transpose of
-//     16-bit values (v_perm) because a lane already holds eight keys x eight
-//     dims of V.  Output dim d = 8*row + e, so lane (q, m) accumulates the 32
-//     contiguous dims [32q, 32q+32) of head m.
-// The next chunk's gathers are in flight while the current one computes, and
-// ids run two chunks ahead.
+// Sparse GQA attention over index lists, prefill (dense BSND K/V): the list
+// walk and the list tiles.  The per-chunk machinery shared with decode is in
+// attention_core.h.
 //
 // Prefill rows whose lists cover most of their causal prefix (all of them
-// before the budget fills) run as list tiles instead: a workgroup of four
-// waves takes several consecutive rows of one KV head, turns their lists
-// into a per-row key mask in LDS, and walks the keys of the prefix densely,
-// each 32-key chunk of K and V staged once in LDS for all its (row, head)
-// columns (see "Tiles" below).
+// before the budget fills) run as list tiles instead of the list walk: a
+// workgroup of four waves takes several consecutive rows of one KV head,
+// turns their lists into a per-row key mask in LDS, and walks the keys of the
+// prefix densely, each 32-key chunk of K and V staged once in LDS for all its
+// (row, head) columns (see "Tiles" below).
 #include <math.h>
 
-#include <algorithm>
 #include <atomic>
 
+#include "attention_core.h"
 #include "qsa_device.h"
 #include "qsa_launch.h"
-#include "select_core.h"
 
 namespace qsa {
-
-template <int D>
-struct Frag {
-  static constexpr int NKS = D / 32;
-  u32x4 kf[8];       // K rows of the lane's eight key slots, dims 8c..8c+7
-  u32x4 vf[8];       // V rows of the lane's eight key slots, dims 8c..8c+7
-  uint32_t valid;    // bit i: key slot i of this lane is usable
-  bool full;         // every key slot of the wave is usable (wave-uniform)
-};
-
-// Key slot i of lane group q: keys 4q+i (i < 4) and 16+4q+(i-4) (i >= 4).
-__device__ __forceinline__ int slot_of(int q4, int i) { return i < 4 ? 4 * q4 + i : 12 + 4 * q4 + i; }
-
-// Dense K/V of one sequence and KV head.  The bases are wave-uniform (scalar
-// registers) and a token's 16-byte piece is a 32-bit byte offset shared by
-// the K and V loads (the host keeps one sequence's K/V under 4 GiB).
-struct DenseKV {
-  const char *k, *v;      // row 0 of this sequence, this KV head
-  uint32_t row_bytes;     // bytes between consecutive tokens
-  int limit;              // ids in [0, limit) are usable
-  __device__ void load(int id, int r16, u32x4 &kd, u32x4 &vd) const {
-    // ids < 2^24 and row_bytes < 2^24: one full-rate 24-bit multiply
-    const uint32_t off = __umul24((uint32_t)id, row_bytes) + 16u * (uint32_t)r16;
-    kd = ld16(k + off);
-    vd = ld16(v + off);
-  }
-};
-
-struct PagedKV {
-  const uint16_t *pool;   // pool + kvh * PHD
-  const int32_t *pk, *pv; // LDS copies of the sequence's page-table rows
-  size_t row_stride;      // Hkv * PHD
-  int num_flat_pages;
-  int limit;
-  __device__ const uint16_t *row(const int32_t *pt, int id) const {
-    int pg = pt[id >> 7];
-    if ((unsigned)pg >= (unsigned)num_flat_pages) pg = 0;
-    return pool + ((size_t)pg * 128 + (id & 127)) * row_stride;
-  }
-  __device__ void load(int id, int r16, u32x4 &kd, u32x4 &vd) const {
-    kd = ld16(row(pk, id) + 8 * r16);
-    vd = ld16(row(pv, id) + 8 * r16);
-  }
-};
-
-// Lanes l and l + 32 hold the id of list slot l % 32; invalid ids become 0
-// (a harmless row to load) and are masked by the validity bits.
-template <int D, int DT, class KV>
-__device__ __forceinline__ void issue_chunk(Frag<D> &f, int idv, const KV &kv, int q4, int r16) {
-  const bool ok = (unsigned)idv < (unsigned)kv.limit;
-  const int sidv = ok ? idv : 0;
-  const uint32_t bal = (uint32_t)__ballot(ok);  // bit s: list slot s is usable
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int id = shfl_i(sidv, slot_of(q4, i));
-    if (D == 128 || r16 < D / 8) {
-      kv.load(id, r16, f.kf[i], f.vf[i]);
-    } else {
-      f.kf[i] = u32x4{0u, 0u, 0u, 0u};
-      f.vf[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // key slots 0-3 are list slots 4q.., 4-7 are 16+4q..
-  f.valid = ((bal >> (4 * q4)) & 0xfu) | (((bal >> (16 + 4 * q4)) & 0xfu) << 4);
-  f.full = bal == 0xffffffffu;
-}
-
-// Online-softmax bookkeeping.  m_run is the reference the probabilities are
-// taken against; it is raised only when a chunk's max exceeds it by more
-// than 2^kLazyLog2 (in the exp2 domain), so most chunks skip the rescale of
-// the accumulators, and a probability is at most 2^kLazyLog2.  The row sum
-// adds the same 16-bit rounded probabilities the PV product uses, two at a
-// time with packed dot products against (1, 1).
-constexpr float kLazyLog2 = 8.f;
-
-// Max with lane l ^ 16 / l ^ 32 by the gfx950 lane swaps (no LDS round
-// trip): one of the two swapped copies holds the partner, the other the
-// lane itself.
-__device__ __forceinline__ float max_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
-}
-__device__ __forceinline__ float max_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
-}
-
-template <int DT>
-__device__ __forceinline__ float add_pair(uint32_t p2, float acc) {
-  if constexpr (DT == DT_F16)
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p2), __builtin_bit_cast(f16x2_t, 0x3C003C00u), acc,
-                                  false);
-  else
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p2),
-                                           __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
-}
-
-// Per-wave LDS tile for one chunk of K: 32 rows of 256 B, 16-byte pieces
-// XOR-swizzled by row so that both the row writes and the fragment reads are
-// free of bank conflicts.  sl2 (scale * log2 e) is positive, so the max of
-// the unscaled scores, times sl2, is the max of the scaled ones.
-// Probabilities of one chunk for the lane's column: the column max over the
-// 32 scores (8 per lane, lanes l, l ^ 16, l ^ 32, l ^ 48), the lazy rescale,
-// exp2 and the 16-bit packing that is the B operand of the PV product.
-// MAYBE_EMPTY: a column may have had no key yet (m_run = -inf, masked
-// scores -inf); its probabilities must then be exp2(-inf) = 0 rather than
-// exp2(-inf + inf).
-template <int DT, bool MAYBE_EMPTY = false>
-__device__ __forceinline__ u32x4 chunk_probs(const float (&x)[8], float sl2, float &m_run, float &l_run,
-                                             f32x4 (&acc)[8]) {
-  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  mx = max_xor16(mx);
-  mx = max_xor32(mx);
-  mx *= sl2;
-  if (wave_any(mx > m_run + kLazyLog2)) {
-    // m_new is finite on every lane of the list walk (every column sees >= 1
-    // usable key by its first chunk); a masked column with no key yet keeps
-    // -inf and alpha = 0 on its zero accumulators
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-    m_run = m_new;
-  }
-  const float m_ref = MAYBE_EMPTY && m_run == -INFINITY ? 0.f : m_run;
-  u32x4 bop;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    bop[w] = pack2<DT>(__builtin_amdgcn_exp2f(fmaf(x[2 * w], sl2, -m_ref)),
-                       __builtin_amdgcn_exp2f(fmaf(x[2 * w + 1], sl2, -m_ref)));
-    l_run = add_pair<DT>(bop[w], l_run);
-  }
-  return bop;
-}
-
-// A operand of the PV product for accumulator e: V^T built in registers
-// from the lane's eight key-slot pieces.
-__device__ __forceinline__ u32x4 v_operand(const u32x4 (&vf)[8], int e) {
-  u32x4 a;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t lo = u4_at(vf[2 * w], e >> 1), hi = u4_at(vf[2 * w + 1], e >> 1);
-    a[w] = (e & 1) ? pack_hi_hi(lo, hi) : pack_lo_lo(lo, hi);
-  }
-  return a;
-}
-
-// Scores of one chunk for one 16-column tile: S^T = K Q^T as two 16-key
-// tiles; x[i] is key slot slot_of(q4, i) of column r16.
-template <int D, int DT>
-__device__ __forceinline__ void chunk_scores(const u32x4 *ktile, const u32x4 (&qf)[D / 32], float (&x)[8]) {
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < Frag<D>::NKS; ++ks) {
-    const u32x4 k0 = ktile[r16 * 16 + ((4 * ks + q4) ^ r16)];
-    const u32x4 k1 = ktile[(16 + r16) * 16 + ((4 * ks + q4) ^ r16)];
-    s0 = mfma16x16x32<DT>(k0, qf[ks], s0);
-    s1 = mfma16x16x32<DT>(k1, qf[ks], s1);
-  }
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = s0[i];
-    x[4 + i] = s1[i];
-  }
-}
-
-// chunk_math: scores, online softmax and PV for one chunk whose K rows sit
-// in an LDS tile and whose V rows (the lane's eight key slots) are in vf.
-template <int D, int DT>
-__device__ __forceinline__ void chunk_math(const u32x4 *ktile, const u32x4 (&vf)[8], uint32_t valid, bool full,
-                                           const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
-                                           f32x4 (&acc)[8]) {
-  float x[8];
-  chunk_scores<D, DT>(ktile, qf, x);
-  if (!full) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = ((valid >> i) & 1u) ? x[i] : -INFINITY;
-  }
-  const u32x4 bop = chunk_probs<DT>(x, sl2, m_run, l_run, acc);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = mfma16x16x32<DT>(v_operand(vf, e), bop, acc[e]);
-}
-
-template <int D, int DT>
-__device__ __forceinline__ void consume_chunk(const Frag<D> &f, const u32x4 (&qf)[D / 32], float sl2,
-                                              float &m_run, float &l_run, f32x4 (&acc)[8], u32x4 *ktile) {
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = slot_of(q4, i);
-    if (D == 128 || r16 < D / 8) ktile[row * 16 + (r16 ^ (row & 15))] = f.kf[i];
-  }
-  __builtin_amdgcn_wave_barrier();
-  chunk_math<D, DT>(ktile, f.vf, f.valid, f.full, qf, sl2, m_run, l_run, acc);
-}
-
-// Runs the online softmax over list slots [32 * c0, n_slots), with chunk c0
-// already issued into fa and id_b holding the ids of chunk c0 + 1.
-// Processing stops at the first 32-slot chunk that holds no usable id.  The
-// list is a pointer to the ids in memory or a KeptList (ids made from kept
-// blocks in LDS); both are read as list[slot].
-template <int D, int DT, class KV, class L>
-__device__ void run_chunks(L list, int n_slots, const KV &kv,
-                           const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
-                           f32x4 (&acc)[8], u32x4 *ktile, int c0, Frag<D> &fa, int id_b) {
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  // Every load here is unconditional: a load issued on one path only would
-  // make the compiler count the wait for the chunk being consumed as if
-  // nothing were in flight after it, so that each consume would also wait
-  // for the chunk just issued.  Past the end, ids read slot n_slots - 1 and
-  // chunks read key 0, and both are dropped.  A chunk's ids are loaded ahead
-  // of the gathers issued before its turn and kept raw (range-masked only
-  // when used): loads retire in order, so waiting on an id loaded after a
-  // chunk's gathers would wait for those gathers too.
-  auto load_id = [&](int c) -> int { return list[min((c << 5) + (lane & 31), n_slots - 1)]; };
-  auto in_list = [&](int c, int idv) -> int { return (c << 5) + (lane & 31) < n_slots ? idv : -1; };
-  auto usable = [&](int idv) { return wave_any((unsigned)idv < (unsigned)kv.limit); };
-
-  Frag<D> fb;
-  int id_c = load_id(c0 + 2);
-  for (int c = c0;; c += 2) {
-    // fa holds chunk c; id_b / id_c are the raw ids of chunks c+1 / c+2.
-    const int ib = in_list(c + 1, id_b);
-    const bool b_ok = usable(ib);
-    const int id_d = load_id(c + 3);
-    issue_chunk<D, DT>(fb, ib, kv, q4, r16);
-    consume_chunk<D, DT>(fa, qf, sl2, m_run, l_run, acc, ktile);
-    if (!b_ok) break;
-    const int ic = in_list(c + 2, id_c);
-    const bool c_ok = usable(ic);
-    const int id_e = load_id(c + 4);
-    issue_chunk<D, DT>(fa, ic, kv, q4, r16);
-    consume_chunk<D, DT>(fb, qf, sl2, m_run, l_run, acc, ktile);
-    if (!c_ok) break;
-    id_b = id_d;
-    id_c = id_e;
-  }
-}
-
-// run_chunks from chunk c0, issuing that chunk first.
-template <int D, int DT, class KV>
-__device__ void run_list(const int32_t *__restrict__ list, int n_slots, const KV &kv,
-                         const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
-                         f32x4 (&acc)[8], u32x4 *ktile, int c0 = 0) {
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  const int s = (c0 << 5) + (lane & 31);
-  // unconditional loads (clamped to the list): a load on one branch only
-  // would be waited for on its own
-  const int raw_a = list[min(s, n_slots - 1)];
-  const int raw_b = list[min(s + 32, n_slots - 1)];
-  const int id_a = s < n_slots ? raw_a : -1;
-  const int id_b = s + 32 < n_slots ? raw_b : -1;
-  if (!wave_any((unsigned)id_a < (unsigned)kv.limit)) return;
-  Frag<D> fa;
-  issue_chunk<D, DT>(fa, id_a, kv, q4, r16);
-  run_chunks<D, DT>(list, n_slots, kv, qf, sl2, m_run, l_run, acc, ktile, c0, fa, id_b);
-}
-
-// run_chunks over a list from slot 0, with the raw ids of its first two
-// chunks already loaded (slots past n_slots read as -1).
-template <int D, int DT, class KV, class L>
-__device__ void run_list_ids(L list, int n_slots, const KV &kv,
-                             const u32x4 (&qf)[D / 32], float sl2, float &m_run, float &l_run,
-                             f32x4 (&acc)[8], u32x4 *ktile, int id_a, int id_b) {
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  if (!wave_any((unsigned)id_a < (unsigned)kv.limit)) return;
-  Frag<D> fa;
-  issue_chunk<D, DT>(fa, id_a, kv, q4, r16);
-  run_chunks<D, DT>(list, n_slots, kv, qf, sl2, m_run, l_run, acc, ktile, 0, fa, id_b);
-}
-
-// Q rows of the GQA group as MFMA B fragments (columns past G are zero).
-// The loads are unconditional (a clamped row), so that none waits alone.
-template <int D>
-__device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t *qhead0, int G, int q4, int r16) {
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    const u32x4 v = ld16(qhead0 + (size_t)min(r16, G - 1) * D + 32 * ks + 8 * q4);
-    qf[ks] = r16 < G ? v : u32x4{0u, 0u, 0u, 0u};
-  }
-}
 
 // Tiles.  Where a row's list covers a large part of its causal prefix —
 // before the budget fills (t < top_k) it is the whole prefix, and at short
@@ -947,351 +638,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   walk_row<D, DT>(a, b, t, kvh, s_ktile[wv]);
 }
 
-// Decode: one wave per (sequence, KV head, split); the waves of a workgroup
-// (up to four) take consecutive splits of the same (sequence, KV head),
-// share its page-table row in LDS, and merge their partial softmax states in
-// LDS in split order.  When a (sequence, KV head) needs more splits than one
-// workgroup holds, each workgroup stores its merged partial (unnormalised O,
-// running max, running sum) and a second small kernel merges the workgroup
-// partials, again in a fixed order.  The order never depends on timing, so
-// results are deterministic.  No cross-workgroup flags are used: on this
-// part each XCD has its own L2, and a kernel boundary is the cheap place to
-// make one workgroup's stores visible to another.
-
-// LDS of a decode workgroup of nw waves, sized to nw: per wave a K tile
-// (32 rows of 256 B) during the walk; once every wave has finished its list
-// (a workgroup barrier separates the two uses) the merge scratch -- per wave
-// 16 rows of D + 4 floats of O, then the running max and sum of each row --
-// overlays the K tiles.  The page-table rows follow.
-template <int D>
-struct DecLds {
-  static constexpr int RS = D + 4;  // padded row stride (floats)
-  static constexpr size_t kTile = 32 * 16 * sizeof(u32x4);
-  static constexpr size_t kMerge = (16 * RS + 2 * 16) * sizeof(float);
-  static constexpr size_t per_wave = kTile > kMerge ? kTile : kMerge;
-  static __host__ __device__ size_t bytes(int nw) { return per_wave * nw; }
-  unsigned char *base;
-  int nw;
-  __device__ u32x4 *ktile(int w) const { return reinterpret_cast<u32x4 *>(base + kTile * w); }
-  __device__ float *acc(int w) const { return reinterpret_cast<float *>(base) + (size_t)16 * RS * w; }
-  __device__ float *m(int w) const { return reinterpret_cast<float *>(base) + (size_t)16 * RS * nw + 16 * w; }
-  __device__ float *l(int w) const { return m(nw) + 16 * w; }
-};
-
-template <int D, int DT>
-__device__ __forceinline__ void decode_merge_store(const DecodeAttnArgs &a, const DecLds<D> &mg, int pair, int group,
-                                                   int br, int kvh, float m_run, float l_run, const f32x4 (&acc)[8]);
-
-// Lane (q, r) of wave w merges row r, dims [d0, d0 + D/16).
-template <int D, int DT>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_decode_kernel(DecodeAttnArgs a) {
-  extern __shared__ __align__(16) unsigned char s_raw[];
-  const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const DecLds<D> mg{s_raw, nw};
-  int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + DecLds<D>::bytes(nw));  // [2][max_pages]
-  const int group = blockIdx.x % a.ngroups;
-  const int pair = blockIdx.x / a.ngroups;  // (query row, KV head)
-  const int br = pair / a.Hkv, kvh = pair % a.Hkv;
-  const int b = br / a.C, row = br % a.C;
-  const int split = group * a.wpg + wv;
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  // Everything the walk needs first is issued at once -- the first two
-  // chunks' ids, Q, the context length and both page-table rows (whole
-  // rows, so that the copy does not wait for the context length) -- so that
-  // one round trip precedes the first gathers.
-  const int s0 = split * a.split_slots;
-  const int n_slots = split < a.nsplits ? min(a.top_k - s0, a.split_slots) : 0;
-  const int32_t *row_ids = a.indices + (size_t)br * a.top_k;
-  const int32_t *list = row_ids + s0;
-  const int sl = lane & 31;
-  // unconditional loads of the first two chunks' ids (clamped to the row)
-  const int raw_a = row_ids[min(s0 + sl, a.top_k - 1)];
-  const int raw_b = row_ids[min(s0 + sl + 32, a.top_k - 1)];
-  const int id_a = sl < n_slots ? raw_a : -1;
-  const int id_b = sl + 32 < n_slots ? raw_b : -1;
-  u32x4 qf[D / 32];
-  load_q<D>(qf, a.q + ((size_t)br * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
-  const int ctx_in = a.ctx[b];
-  const int pos = a.start ? a.start[b] + row : ctx_in - 1;  // the row's position
-  {
-    const int32_t *ptb = a.pt + (size_t)b * 2 * a.max_pages;  // rows 0 and 1 are contiguous
-    const int npt = 2 * a.max_pages;
-    constexpr int U = 4;
-    for (int i0 = threadIdx.x; i0 < npt; i0 += U * (int)blockDim.x) {
-      int v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = ptb[min(i0 + u * (int)blockDim.x, npt - 1)];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * (int)blockDim.x;
-        if (i < npt) s_pt[i] = v[u];
-      }
-    }
-  }
-  __syncthreads();
-  const int ctx = min(max(ctx_in, 0), a.max_pages * 128);
-
-  f32x4 acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  if (ctx > 0 && n_slots > 0 && pos >= 0 && pos < ctx_in) {
-    PagedKV kv;
-    kv.pool = a.pool + (size_t)kvh * a.PHD;
-    kv.pk = s_pt;
-    kv.pv = s_pt + a.max_pages;
-    kv.row_stride = (size_t)a.Hkv * a.PHD;
-    kv.num_flat_pages = a.num_flat_pages;
-    kv.limit = ctx;
-    run_list_ids<D, DT>(list, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile(wv), id_a, id_b);
-  }
-  decode_merge_store<D, DT>(a, mg, pair, group, br, kvh, m_run, l_run, acc);
-}
-
-// The workgroup's splits (one per wave: m_run, l_run, acc) merged in split
-// order, then stored as output rows (one workgroup per pair) or as the
-// workgroup's partial.
-template <int D, int DT>
-__device__ __forceinline__ void decode_merge_store(const DecodeAttnArgs &a, const DecLds<D> &mg, int pair, int group,
-                                                   int br, int kvh, float m_run, float l_run, const f32x4 (&acc)[8]) {
-  const int wv = threadIdx.x >> 6, nw = mg.nw;
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  __syncthreads();  // every K tile is dead before the merge scratch is written
-  float l = l_run + shfl_xor_f(l_run, 16);
-  l += shfl_xor_f(l, 32);
-  if (32 * q4 < D) {
-    float *dst = mg.acc(wv) + r16 * DecLds<D>::RS + 32 * q4;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      *reinterpret_cast<f32x4 *>(dst + 8 * rr) = f32x4{acc[0][rr], acc[1][rr], acc[2][rr], acc[3][rr]};
-      *reinterpret_cast<f32x4 *>(dst + 8 * rr + 4) = f32x4{acc[4][rr], acc[5][rr], acc[6][rr], acc[7][rr]};
-    }
-  }
-  if (q4 == 0) {
-    mg.m(wv)[r16] = m_run;
-    mg.l(wv)[r16] = l;
-  }
-  __syncthreads();
-
-  // Merge the workgroup's splits in split order.  The head dims form 16
-  // slices of D/16; lane (q, r) of wave w takes row r and slices w*4+q,
-  // w*4+q + 4*nw, ...  The sums are explicit fmas, so that every kernel
-  // that inlines this merge (whatever it knows of nw) rounds them alike.
-  constexpr int ND = D / 16;
-  float M = -INFINITY;
-  for (int w = 0; w < nw; ++w) M = fmaxf(M, mg.m(w)[r16]);
-  float L = 0.f, sc[kDecWaves];
-#pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) {
-    const float mw = w < nw ? mg.m(w)[r16] : -INFINITY;
-    sc[w] = mw == -INFINITY ? 0.f : exp2f(mw - M);
-    L = __builtin_fmaf(w < nw ? mg.l(w)[r16] : 0.f, sc[w], L);
-  }
-  if (r16 >= a.G) return;
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const size_t slot = (size_t)pair * kDecMaxGroups + group;
-  for (int sl = wv * 4 + q4; sl < 16; sl += 4 * nw) {
-    const int d0 = sl * ND;
-    float o[ND];
-#pragma unroll
-    for (int j = 0; j < ND; ++j) o[j] = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float *src = mg.acc(w) + r16 * DecLds<D>::RS + d0;
-#pragma unroll
-      for (int j = 0; j < ND; ++j) o[j] = __builtin_fmaf(src[j], sc[w], o[j]);
-    }
-    if (a.ngroups == 1) {
-      uint16_t *out = a.o + ((size_t)br * a.Hq + (size_t)kvh * a.G + r16) * D + d0;
-#pragma unroll
-      for (int j = 0; j < ND; j += 2)
-        *reinterpret_cast<uint32_t *>(out + j) =
-            pack2<DT>(o[j] * inv, o[j + 1] * inv);
-    } else {
-      float *po = a.part_o + (slot * 16 + r16) * D + d0;
-#pragma unroll
-      for (int j = 0; j < ND; j += 4) *reinterpret_cast<f32x4 *>(po + j) = f32x4{o[j], o[j + 1], o[j + 2], o[j + 3]};
-    }
-  }
-  if (a.ngroups > 1 && wv == 0 && q4 == 0) {
-    a.part_stats[slot * 32 + r16] = M;
-    a.part_stats[slot * 32 + 16 + r16] = L;
-  }
-}
-
-// Merges the workgroup partials of one (sequence, KV head) in group order.
-template <int D, int DT>
-__global__ __launch_bounds__(64) void sparse_decode_merge_kernel(DecodeAttnArgs a) {
-  const int pair = blockIdx.x;  // (query row, KV head)
-  const int br = pair / a.Hkv, kvh = pair % a.Hkv;
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-  if (r16 >= a.G) return;
-  constexpr int NDL = D / 4;  // dims per lane
-  const int d0 = q4 * NDL;
-  const size_t slot0 = (size_t)pair * kDecMaxGroups;
-  float M = -INFINITY;
-  for (int g = 0; g < a.ngroups; ++g) M = fmaxf(M, a.part_stats[(slot0 + g) * 32 + r16]);
-  float L = 0.f, o[NDL];
-#pragma unroll
-  for (int j = 0; j < NDL; ++j) o[j] = 0.f;
-  for (int g = 0; g < a.ngroups; ++g) {
-    const float mg = a.part_stats[(slot0 + g) * 32 + r16];
-    const float sc = mg == -INFINITY ? 0.f : exp2f(mg - M);
-    L += a.part_stats[(slot0 + g) * 32 + 16 + r16] * sc;
-    const float *src = a.part_o + ((slot0 + g) * 16 + r16) * D + d0;
-#pragma unroll
-    for (int j = 0; j < NDL; j += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(src + j);
-      o[j] += v[0] * sc;
-      o[j + 1] += v[1] * sc;
-      o[j + 2] += v[2] * sc;
-      o[j + 3] += v[3] * sc;
-    }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t *out = a.o + ((size_t)br * a.Hq + (size_t)kvh * a.G + r16) * D + d0;
-#pragma unroll
-  for (int j = 0; j < NDL; j += 8) {
-    u32x4 w;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = pack2<DT>(o[j + 2 * k] * inv, o[j + 2 * k + 1] * inv);
-    st16(out + j, w);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Decode step: the indexer's select (decode B3) and the sparse decode in one
-// kernel.  One workgroup of kDecWaves waves per (sequence, KV head) reads
-// the sequence's block scores, runs the workgroup select (select_core.h) --
-// the workgroups of all KV heads of a sequence run the same select, so the
-// list never has to reach memory before the walk -- and walks that list
-// straight from LDS.  The workgroup of KV head 0 also stores the list, as
-// the indexer would.  The scores of the whole row width go out with the
-// context length, Q and the page-table rows (masked once the length is
-// known), so one round trip precedes the select and one more the first
-// gathers.  Splits, walk and merge are those of sparse_decode_kernel with
-// one workgroup per pair, so the output is the same bit for bit.
-// ---------------------------------------------------------------------------
-
-// The list of one decode row, made from its kept blocks lb (ascending):
-// slot i < head is token r*lb[i/r] + i%r, then the causal tail i + tail0
-// below len, then -1; s0 offsets the slots (a split's first slot).  With
-// head = 0 the list is 0..len-1.
-struct KeptList {
-  const uint16_t *lb;
-  int s0, r, head, len, tail0;
-  __device__ int operator[](int slot) const {
-    const int i = s0 + slot;
-    if (i < head) {
-      const int j = r == 4 ? i >> 2 : i / r;
-      return r * (int)lb[j] + (i - r * j);
-    }
-    return i < len ? i + tail0 : -1;
-  }
-};
-
-// LDS of the decode step: the select's histograms share the front with the
-// walk's tiles and merge scratch (the select ends before the walk starts),
-// then both page-table rows, then the kept blocks.
-template <int D>
-__host__ __device__ constexpr size_t step_front_bytes() {
-  return DecLds<D>::bytes(kDecWaves) > sizeof(WgSelLds<64 * kDecWaves>) ? DecLds<D>::bytes(kDecWaves)
-                                                                         : sizeof(WgSelLds<64 * kDecWaves>);
-}
-
-template <int D, int DT, int KPT>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_select_attend_kernel(
-    DecodeAttnArgs a) {
-  constexpr int NT = 64 * kDecWaves;
-  extern __shared__ __align__(16) unsigned char s_raw[];
-  const int tid = threadIdx.x, wv = tid >> 6;
-  const DecLds<D> mg{s_raw, kDecWaves};
-  WgSelLds<NT> &sel = *reinterpret_cast<WgSelLds<NT> *>(s_raw);
-  int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + step_front_bytes<D>());  // [2][max_pages]
-  uint16_t *s_lb = reinterpret_cast<uint16_t *>(s_pt + 2 * a.max_pages);
-  const int pair = blockIdx.x;  // (sequence, KV head)
-  const int b = pair / a.Hkv, kvh = pair % a.Hkv;
-  const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
-
-  const int ctx_in = a.ctx[b];
-  const float *srow = a.scores + (size_t)b * a.score_stride;
-  // Every load is unconditional (a load on one branch only makes the
-  // compiler wait for it where the branches join, one load at a time):
-  // slots past the row width read the row's last four scores and are
-  // masked once the context length is known.
-  // Thread j's keys of round r are blocks 4*NT*r + 4j + c (select_core.h).
-  float sv[KPT];
-#pragma unroll
-  for (int r = 0; r < KPT / 4; ++r) {
-    const f32x4 v = *reinterpret_cast<const f32x4 *>(srow + min(4 * NT * r + 4 * tid, a.score_stride - 4));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) sv[4 * r + c] = v[c];
-  }
-  u32x4 qf[D / 32];
-  load_q<D>(qf, a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G) * D, a.G, q4, r16);
-  wg_select_clear<NT>(sel);
-  {
-    const int32_t *ptb = a.pt + (size_t)b * 2 * a.max_pages;  // rows 0 and 1 are contiguous
-    const int npt = 2 * a.max_pages;
-    constexpr int U = 4;
-    for (int k0 = tid; k0 < npt; k0 += U * NT) {
-      int v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = ptb[min(k0 + u * NT, npt - 1)];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = k0 + u * NT;
-        if (k < npt) s_pt[k] = v[u];
-      }
-    }
-  }
-  __syncthreads();
-
-  // the row's list, as the indexer's decode select makes it
-  const int c = min(ctx_in, a.max_pages * 128);
-  const int r = a.ratio;
-  const int nc = c > 0 ? c / r : 0;
-  KeptList list{s_lb, 0, r, 0, c > 0 ? c : 0, 0};
-  if (nc > a.budget) {  // uniform over the workgroup
-    uint32_t key[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = 4 * NT * (j >> 2) + 4 * tid + (j & 3) < nc ? score_key(sv[j]) : 0xffffffffu;
-    wg_select_blocks<NT, KPT>(key, nc, a.budget, sel, s_lb);
-    list.head = r * a.budget;
-    list.len = list.head + c - r * nc;
-    list.tail0 = r * nc - list.head;
-  }
-  if (kvh == 0) {
-    int32_t *out = a.lists_out + (size_t)b * a.top_k;
-    for (int i = tid; i < a.top_k; i += NT) out[i] = list[i];
-  }
-
-  const int s0 = wv * a.split_slots;
-  const int n_slots = wv < a.nsplits ? min(a.top_k - s0, a.split_slots) : 0;
-  KeptList mine = list;
-  mine.s0 = s0;
-  const int sl = lane & 31;
-  const int raw_a = mine[sl], raw_b = mine[sl + 32];  // LDS reads, any slot
-  const int id_a = sl < n_slots ? raw_a : -1;
-  const int id_b = sl + 32 < n_slots ? raw_b : -1;
-  const int ctx = min(max(ctx_in, 0), a.max_pages * 128);
-  f32x4 acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  if (ctx > 0 && n_slots > 0) {
-    PagedKV kv;
-    kv.pool = a.pool + (size_t)kvh * a.PHD;
-    kv.pk = s_pt;
-    kv.pv = s_pt + a.max_pages;
-    kv.row_stride = (size_t)a.Hkv * a.PHD;
-    kv.num_flat_pages = a.num_flat_pages;
-    kv.limit = ctx;
-    run_list_ids<D, DT>(mine, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile(wv), id_a, id_b);
-  }
-  decode_merge_store<D, DT>(a, mg, pair, 0, b, kvh, m_run, l_run, acc);
-}
-
 // Tiles take rows t with t + 1 <= kTileRangeX2 / 2 * top_k * R / 16 (R rows
 // per tile, kTileRangeX2 / 2 = 3.5).  At R = 16 a dense walk of a 32-key chunk costs a row ~1/2.6 of
 // what gathering 32 listed keys costs the list walk (workload 2: all 4096
@@ -1410,50 +756,6 @@ static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
 hipError_t launch_sparse_prefill(const PrefillAttnArgs &a, int D, int dt, hipStream_t s) {
   if (D == 128) return dt == DT_F16 ? launch_prefill_t<128, DT_F16>(a, s) : launch_prefill_t<128, DT_BF16>(a, s);
   return dt == DT_F16 ? launch_prefill_t<64, DT_F16>(a, s) : launch_prefill_t<64, DT_BF16>(a, s);
-}
-
-template <int D, int DT>
-static hipError_t launch_decode_t(const DecodeAttnArgs &a, hipStream_t s) {
-  const unsigned pairs = (unsigned)((long long)a.B * a.C * a.Hkv);
-  const size_t lds = DecLds<D>::bytes(a.wpg) + (size_t)2 * a.max_pages * sizeof(int32_t);
-  if (lds > 65536)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_decode_kernel<D, DT>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((sparse_decode_kernel<D, DT>), dim3(pairs * a.ngroups), dim3(64 * a.wpg), lds, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.ngroups == 1) return e;
-  hipLaunchKernelGGL((sparse_decode_merge_kernel<D, DT>), dim3(pairs), dim3(64), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_sparse_decode(const DecodeAttnArgs &a, int D, int dt, hipStream_t s) {
-  if (D == 128) return dt == DT_F16 ? launch_decode_t<128, DT_F16>(a, s) : launch_decode_t<128, DT_BF16>(a, s);
-  return dt == DT_F16 ? launch_decode_t<64, DT_F16>(a, s) : launch_decode_t<64, DT_BF16>(a, s);
-}
-
-template <int D, int DT, int KPT>
-static hipError_t launch_step_t(const DecodeAttnArgs &a, hipStream_t s) {
-  // the kept-block list: the select runs only when budget < nc <= gmax
-  const size_t lb_bytes = ((size_t)std::min(a.budget, a.gmax) * sizeof(uint16_t) + 15) & ~(size_t)15;
-  const size_t lds = step_front_bytes<D>() + (size_t)2 * a.max_pages * sizeof(int32_t) + lb_bytes;
-  const void *fn = reinterpret_cast<const void *>(&decode_select_attend_kernel<D, DT, KPT>);
-  if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((decode_select_attend_kernel<D, DT, KPT>), dim3((unsigned)((long long)a.B * a.Hkv)),
-                     dim3(64 * kDecWaves), lds, s, a);
-  return hipGetLastError();
-}
-
-template <int D, int DT>
-static hipError_t launch_step_d(const DecodeAttnArgs &a, hipStream_t s) {
-  // thread j holds the scores of blocks [j*KPT, (j+1)*KPT)
-  if (a.gmax <= 64 * kDecWaves * 16) return launch_step_t<D, DT, 16>(a, s);
-  return launch_step_t<D, DT, 32>(a, s);
-}
-
-hipError_t launch_decode_select_attend(const DecodeAttnArgs &a, int D, int dt, hipStream_t s) {
-  if (a.gmax > kStepMaxBlocks || a.ngroups != 1 || a.wpg > kDecWaves) return hipErrorInvalidValue;
-  if (D == 128) return dt == DT_F16 ? launch_step_d<128, DT_F16>(a, s) : launch_step_d<128, DT_BF16>(a, s);
-  return dt == DT_F16 ? launch_step_d<64, DT_F16>(a, s) : launch_step_d<64, DT_BF16>(a, s);
 }
 
 }  // namespace qsa
