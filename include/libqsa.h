@@ -381,8 +381,9 @@ qsa_status qsa_decode_step(const qsa_indexer_decode_params *indexer, const qsa_s
  * keys of the chunk's tokens of the trailing incomplete block in their K-row
  * tails, and leaves the rest of the pool bit-unchanged -- so the tails then
  * hold what a prefill of context_lengths[b] tokens leaves.  workspace: at
- * least qsa_indexer_chunk_workspace_bytes() bytes, 256-byte aligned (fp32
- * queries, kbar of every block, fp32 score rows).  Pool, page table and
+ * least qsa_indexer_chunk_workspace_bytes() bytes, 256-byte aligned (the
+ * fp32 queries as 16-bit scoring pieces, kbar of every block, fp32 score
+ * rows).  Pool, page table and
  * sizes as for qsa_indexer_decode.
  * qsa_sparse_chunk: q, o [batch, chunk_len, num_q_heads, head_dim]; the
  * attention of every live row over its list, K/V read through the page

@@ -43,7 +43,8 @@ int64_t min_top_k(const qsa_indexer_config &c) {
   return (int64_t)c.budget * c.compress_ratio + c.compress_ratio - 1;
 }
 
-// Prefill indexer workspace: fp32 queries | 16-bit kbar | fp32 score rows.
+// Prefill indexer workspace: queries (fp32 values as up to three 16-bit
+// scoring pieces each) | 16-bit kbar | fp32 score rows.
 struct PrefillWs {
   size_t qhat, kbar, scores, total;
   int gmax, stride;
@@ -53,7 +54,7 @@ PrefillWs prefill_ws(const qsa_indexer_config &c, int32_t B, int32_t S) {
   w.gmax = S / c.compress_ratio;
   w.stride = (int)round16((size_t)(w.gmax > 0 ? w.gmax : 1));
   w.qhat = 0;
-  w.kbar = align_up((size_t)B * S * c.num_heads * c.head_dim * 4);
+  w.kbar = align_up((size_t)B * S * c.num_heads * c.head_dim * 2 * qsa::kQPiecesMax);
   w.scores = w.kbar + align_up((size_t)B * (w.gmax > 0 ? w.gmax : 1) * c.head_dim * 2);
   w.total = w.scores + align_up((size_t)B * S * w.stride * 4);
   return w;
@@ -73,7 +74,7 @@ DecodeWs decode_ws(const qsa_indexer_config &c, int32_t B, int32_t max_pages) {
   return w;
 }
 
-// Chunk indexer workspace: fp32 queries | 16-bit kbar of every block a
+// Chunk indexer workspace: queries (as scoring pieces) | 16-bit kbar of every block a
 // sequence may hold | fp32 score rows.
 struct ChunkWs {
   size_t qhat, kbar, scores, total;
@@ -84,7 +85,7 @@ ChunkWs chunk_ws(const qsa_indexer_config &c, int32_t B, int32_t C, int32_t max_
   w.gmax = max_pages * QSA_PAGE_TOKENS / c.compress_ratio;
   w.stride = (int)round16((size_t)(w.gmax > 0 ? w.gmax : 1));
   w.qhat = 0;
-  w.kbar = align_up((size_t)B * C * c.num_heads * c.head_dim * 4);
+  w.kbar = align_up((size_t)B * C * c.num_heads * c.head_dim * 2 * qsa::kQPiecesMax);
   w.scores = w.kbar + align_up((size_t)B * w.gmax * c.head_dim * 2);
   w.total = w.scores + align_up((size_t)B * C * w.stride * 4);
   return w;
@@ -370,7 +371,7 @@ qsa_status qsa_indexer_chunk(const qsa_indexer_chunk_params *p) {
   pa.pt = p->page_table;
   pa.ctx = p->context_lengths;
   pa.start = p->start_positions;
-  pa.qhat = reinterpret_cast<float *>(ws + w.qhat);
+  pa.qhat = reinterpret_cast<uint16_t *>(ws + w.qhat);
   pa.kbar = reinterpret_cast<uint16_t *>(ws + w.kbar);
   pa.B = p->batch;
   pa.C = p->chunk_len;
@@ -451,7 +452,7 @@ qsa_status qsa_indexer_prefill(const qsa_indexer_prefill_params *p) {
   pa.wq = p->q_norm_w;
   pa.wk = p->k_norm_w;
   pa.ctx = p->context_lengths;
-  pa.qhat = reinterpret_cast<float *>(ws + w.qhat);
+  pa.qhat = reinterpret_cast<uint16_t *>(ws + w.qhat);
   pa.kbar = reinterpret_cast<uint16_t *>(ws + w.kbar);
   pa.B = p->batch;
   pa.S = p->seq_len;

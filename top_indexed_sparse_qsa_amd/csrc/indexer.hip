@@ -106,8 +106,10 @@ __global__ __launch_bounds__(256) void idx_prep_kernel(IdxPrepArgs a) {
         const size_t off = ((size_t)item * a.Hi + h) * 128;
         norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt), wq0, wq1,
                    a.eps, a.rot, r, o0, o1);
-        a.qhat[off + lane] = (float)o0;
-        a.qhat[off + 64 + lane] = (float)o1;
+        // q-hat rounded once to fp32, stored as the scoring's 16-bit pieces
+        uint16_t *qp = a.qhat + off * q_pieces(a.dt);
+        store_q_pieces_rt(qp + lane, (float)o0, a.dt);
+        store_q_pieces_rt(qp + 64 + lane, (float)o1, a.dt);
       }
     } else {
       const long long kk = item - nrows;
@@ -197,8 +199,9 @@ __global__ __launch_bounds__(256) void idx_chunk_prep_kernel(IdxChunkPrepArgs a)
       const size_t off = (((size_t)b * a.C + k) * a.Hi + h) * 128;
       norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
                  (double)a.wq[lane], (double)a.wq[lane + 64], a.eps, a.rot, rp, o0, o1);
-      a.qhat[off + lane] = (float)o0;
-      a.qhat[off + 64 + lane] = (float)o1;
+      uint16_t *qp = a.qhat + off * q_pieces(a.dt);
+      store_q_pieces_rt(qp + lane, (float)o0, a.dt);
+      store_q_pieces_rt(qp + 64 + lane, (float)o1, a.dt);
     }
     return;
   }
@@ -283,18 +286,20 @@ __device__ __forceinline__ void load8f(float (&x)[8], const float *p) {
 }
 
 // Prefill scoring.  A workgroup takes 32 consecutive rows and a run of up to
-// kScoreChunksPerGroup chunks of kScoreChunk complete blocks (rows' queries
-// are loaded and split once per run; short prefills take shorter runs so the
-// grid still fills the chip); runs of the last rows are dispatched first,
-// all runs of a row group on one XCD.  Per chunk the kbar rows are staged in LDS, 16-byte pieces
-// XOR-swizzled by row so that MFMA fragment reads are conflict-free; each wave
+// kScoreRunF16 / kScoreRunBf16 chunks of kScoreChunk complete blocks (the
+// rows' query pieces, prepared by the prep kernel, are loaded once per run;
+// short prefills take shorter runs so the grid still fills the chip); runs
+// of the last rows are dispatched first, all runs of a row group on one XCD.
+// Per chunk the kbar rows are staged in LDS, 16-byte pieces XOR-swizzled by
+// row so that MFMA fragment reads are conflict-free; each wave
 // computes 8 rows against the chunk.  The MFMA M tile is (row, head) with the
 // head fastest, so each 16-lane group ends with the four head dots of one row
 // and one block and sums their relus in-lane; a wave's two M tiles share every
 // kbar fragment.  The chunk's 32 x kScoreChunk scores are assembled in LDS and
 // stored as whole 512-byte row segments.
 template <int DT>
-__global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == DT_F16 ? 3 : 2))) void idx_score_kernel(
+    IdxScoreArgs a) {
   constexpr int NP = QSplit<DT>::NP;
   constexpr int CB = kScoreChunk;
   __shared__ __align__(16) uint32_t s_kb[CB * 64];     // CB rows x 256 B
@@ -348,23 +353,21 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreArgs a) {
   load_chunk(run_lo);  // in flight while the queries are loaded and split
 
   const int t0 = tg + 8 * wv;
+  // the rows' query pieces (written by the prep), zero for dead rows and
+  // heads; the loads are unconditional (a clamped row and head)
   u32x4 qa[2][NP][4];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int t = t0 + 4 * m + (r16 >> 2), h = r16 & 3;
     const bool ok = t < live && h < a.Hi;
+    const uint16_t *qp = a.qhat + (((size_t)b * a.S + min(t, a.S - 1)) * a.Hi + min(h, a.Hi - 1)) * NP * 128 + 8 * q4;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float x[8];
-      if (ok) load8f(x, a.qhat + (((size_t)b * a.S + t) * a.Hi + h) * 128 + 32 * ks + 8 * q4);
-      else
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = 0.f;
-      u32x4 pieces[NP];
-      split8<DT>(x, pieces);
-#pragma unroll
-      for (int p = 0; p < NP; ++p) qa[m][p][ks] = pieces[p];
-    }
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 v = ld16(qp + 128 * p + 32 * ks);
+        qa[m][p][ks] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
   }
   const int nc_wave = t0 < live ? (off + min(t0 + 7, live - 1) + 1) / a.ratio : 0;
   // score stores: thread tid owns columns 4 (tid % 32) .. +3 of rows tid / 32 + 8 j
@@ -933,7 +936,7 @@ hipError_t launch_idx_score(const IdxScoreArgs &a_in, int dt, hipStream_t s) {
   IdxScoreArgs a = a_in;
   const int chunks = max(1, (a.Gmax + kScoreChunk - 1) / kScoreChunk);
   const long long groups = (long long)a.B * ((a.S + 31) / 32);
-  int run = kScoreChunksPerGroup;  // halve runs until ~2048 workgroups (8 waves per CU)
+  int run = dt == DT_F16 ? kScoreRunF16 : kScoreRunBf16;  // halved until ~2048 workgroups (8 waves per CU)
   while (run > 1 && groups * ((chunks + run - 1) / run) < 2048) run >>= 1;
   a.run_chunks = run;
   a.nchunk = (chunks + run - 1) / run;

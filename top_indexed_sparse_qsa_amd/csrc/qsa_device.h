@@ -72,6 +72,28 @@ __device__ __forceinline__ uint32_t f32_to_bits_rt(float x, int dt) {
   return dt == DT_F16 ? f32_to_bits<DT_F16>(x) : f32_to_bits<DT_BF16>(x);
 }
 
+// An fp32 query value as the 16-bit pieces the block scoring multiplies
+// (MFMA takes 16-bit operands): piece 0 is x rounded to the dtype, each next
+// piece the rounded remainder; 2 pieces for fp16 (11 + 11 significant bits),
+// 3 for bf16 (8 + 8 + 8), at most kQPiecesMax.  Stored 128 elements apart.
+__host__ __device__ constexpr int q_pieces(int dt) { return dt == DT_F16 ? 2 : 3; }
+
+template <int DT>
+__device__ __forceinline__ void store_q_pieces(uint16_t *dst, float x) {
+  float r = x;
+#pragma unroll
+  for (int p = 0; p < q_pieces(DT); ++p) {
+    const uint32_t h = f32_to_bits<DT>(r);
+    r -= bits_to_f32_t<DT>(h);
+    dst[128 * p] = (uint16_t)h;
+  }
+}
+
+__device__ __forceinline__ void store_q_pieces_rt(uint16_t *dst, float x, int dt) {
+  if (dt == DT_F16) store_q_pieces<DT_F16>(dst, x);
+  else store_q_pieces<DT_BF16>(dst, x);
+}
+
 // double -> float rounded to odd: truncate, then force the last bit on when
 // the value was inexact.  Rounding that result to nearest-even in any format
 // with at least two fewer significant bits equals one direct rounding of the

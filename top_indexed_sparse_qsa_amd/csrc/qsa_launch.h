@@ -64,7 +64,7 @@ struct IdxPrepArgs {
   const uint16_t *idx_q, *idx_k;
   const float *wq, *wk;
   const int32_t *ctx;
-  float *qhat;      // [B,S,Hi,hd]
+  uint16_t *qhat;   // [B,S,Hi][pieces][hd]: the fp32 queries as 16-bit MFMA pieces
   uint16_t *kbar;   // [B,Gmax,hd]
   int B, S, Hi, hd, rot, ratio, Gmax;
   double theta, eps;
@@ -78,7 +78,7 @@ struct IdxPrepArgs {
 };
 
 struct IdxScoreArgs {
-  const float *qhat;
+  const uint16_t *qhat;  // [B,S,Hi][pieces][hd]
   const uint16_t *kbar;
   float *scores;    // [B,S,stride]
   const int32_t *ctx;
@@ -88,8 +88,14 @@ struct IdxScoreArgs {
   int run_chunks;   // chunks per run (set by the launcher)
 };
 
+constexpr int kQPiecesMax = 3;            // 16-bit pieces per prepared query value (bf16: 3)
 constexpr int kScoreChunk = 128;           // kbar rows staged at a time in prefill scoring
-constexpr int kScoreChunksPerGroup = 8;    // most chunks per prefill scoring workgroup
+// most chunks per prefill scoring workgroup: fp16 (three waves per SIMD)
+// balances best over short runs, bf16 (two waves per SIMD, 1.5x the query
+// pieces to load per run) over long ones (measured at S = 32768 fp16 and
+// B = 4 x 16384 bf16: 4 and 16 beat 2 and 8)
+constexpr int kScoreRunF16 = 4;
+constexpr int kScoreRunBf16 = 16;
 
 struct IdxSelectArgs {
   const float *scores;
@@ -129,7 +135,7 @@ struct IdxChunkPrepArgs {
   const float *wq, *wk;
   uint16_t *pool;
   const int32_t *pt, *ctx, *start;
-  float *qhat;                     // [B,C,Hi,hd]
+  uint16_t *qhat;                  // [B,C,Hi][pieces][hd]
   uint16_t *kbar;                  // [B,Gmax,hd]
   int B, C, Hi, hd, rot, ratio, Hkv, D, PHD, num_flat_pages, max_pages, Gmax;
   double theta, eps;
