@@ -565,9 +565,13 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
         if (base_i + 256 * g < nc) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const uint32_t k = key[4 * g + c];
-            const bool in = k >= lo && k < hi;
-            if (__ballot(in) != 0ull) atomicAdd(in ? &H[hpad((int)((k - lo) >> s))] : spare, 1u);
+            // k in [lo, hi) as one unsigned compare of k - lo
+            const uint32_t d = key[4 * g + c] - lo;
+            const bool in = d < range;
+            if (__ballot(in) != 0ull) {
+              const uint32_t bin = d >> s;
+              atomicAdd(in ? H + bin + ((bin >> 5) << 2) : spare, 1u);  // H[hpad(bin)]
+            }
           }
         }
       }
@@ -586,71 +590,84 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   }
 
   // Keys >= hi are kept; of those in [lo, hi), the first `remaining` in
-  // index order (all of them when whole_bin).  The empty-slot marker
-  // (0xffffffff) is above every range and never counts as real.
-  int eq_seen = 0;
-  if (NW == 2 && !whole_bin) {  // the second wave's cut-bin keys follow the first's
-    int ec = 0;
+  // index order (all of them when whole_bin).  A byte per lane and group
+  // (bit c: block 256 g + 4 lane + c at or above hi; bit 4 + c: in [lo,
+  // hi)), then lane l turns the bytes of blocks [32 j, 32 j + 32) of the
+  // wave's span, j = l + 64 u, into two 32-bit masks, and a wave scan of
+  // their counts places each mask's kept blocks in the wave's list.  A
+  // two-wave row's cut-bin keys in its first wave come before those in its
+  // second.  The flags overlay the histograms (past the staged list).
+  row_sync<NW>();  // every wave has read the histograms
+  uint8_t *fl = reinterpret_cast<uint8_t *>(NW == 1 ? region + (STAGE ? a.list_words : 0) : region + h * 16 * NG);
+  {
+    const uint32_t above = 0x80000000u - hi, range = hi - lo;  // real keys are below 2^31
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t k = key[4 * g + c];
-        ec += __popcll(__ballot(k >= lo && k < hi));
-      }
-    if (lane == 0) s_x[wv][3] = ec;
-    __syncthreads();
-    eq_seen = h == 1 ? s_x[0][3] : 0;
-  }
-  int kept = 0;
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    if (base_i + 256 * g < nc) {
-      bool kc[4];
-      if (whole_bin) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kc[c] = (int)key[4 * g + c] >= 0 && key[4 * g + c] >= lo;
-      } else {
-        bool eq[4];
-        unsigned long long em[4];
-        int er = eq_seen;
+    for (int g = 0; g < NG; ++g) {
+      if (base_i + 256 * g < nc) {
+        uint32_t byte = 0u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t k = key[4 * g + c];
-          kc[c] = (int)k >= 0 && k >= hi;
-          eq[c] = k >= lo && k < hi;
-          em[c] = __ballot(eq[c]);
-          er += lanes_below(em[c]);
+          byte |= k - hi < above ? 1u << c : 0u;
+          byte |= k - lo < range ? 16u << c : 0u;
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (eq[c]) {
-            kc[c] = er < remaining;
-            ++er;
-          }
-        eq_seen += __popcll(em[0]) + __popcll(em[1]) + __popcll(em[2]) + __popcll(em[3]);
+        fl[64 * g + lane] = (uint8_t)byte;
       }
-      unsigned long long km[4];
-      int pos = kept;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        km[c] = __ballot(kc[c]);
-        pos += lanes_below(km[c]);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (kc[c]) {
-          const int g_blk = base_i + 256 * g + 4 * lane + c;
-          if constexpr (STAGE) {
-            lb[pos] = (uint16_t)g_blk;
-          } else {
-            for (int j = 0; j < r; ++j) out[r * pos + j] = r * g_blk + j;
-          }
-          ++pos;
-        }
-      kept += __popcll(km[0]) + __popcll(km[1]) + __popcll(km[2]) + __popcll(km[3]);
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();  // a wave reads only its own flags (LDS is in order per wave)
+  constexpr int NU = (8 * NG + 63) / 64;        // masks per lane
+  const int jmax = min(8 * NG, max(0, (nc - base_i + 31) >> 5));  // masks holding blocks of the row
+  uint32_t gtm[NU], eqm[NU];
+  int ex[NU], tot[NU];
+  int eq_total = 0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int j = lane + 64 * u;
+    unsigned long long v = 0ull;
+    if (j < jmax) v = *reinterpret_cast<const unsigned long long *>(fl + 8 * j);
+    gtm[u] = low_nibbles(v);
+    eqm[u] = low_nibbles(v >> 4);
+    const int cnt = __builtin_popcount(eqm[u]) | (__builtin_popcount(gtm[u]) << 16);
+    const int inc = wave_incl_scan(cnt);
+    ex[u] = inc - cnt;
+    tot[u] = __builtin_amdgcn_readlane(inc, 63);
+    eq_total += tot[u] & 0xffff;
+  }
+  int eq_seen = 0;
+  if (NW == 2 && !whole_bin) {  // the second wave's cut-bin keys follow the first's
+    if (lane == 0) s_x[wv][3] = eq_total;
+    __syncthreads();
+    eq_seen = h == 1 ? s_x[0][3] : 0;
+  }
+  const int take_max = max(0, remaining - eq_seen);  // cut-bin keys this wave keeps at most
+  int gt_run = 0, eq_run = 0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int gt_b = gt_run + (ex[u] >> 16), eq_b = eq_run + (ex[u] & 0xffff);
+    const int take = min(__builtin_popcount(eqm[u]), max(0, take_max - eq_b));
+    int pos = gt_b + min(eq_b, take_max);
+    uint32_t keep = gtm[u], e = eqm[u];
+    for (int q = 0; q < take; ++q) {
+      keep |= e & (0u - e);
+      e &= e - 1u;
+    }
+    const int blk0 = base_i + 32 * (lane + 64 * u);
+    while (keep != 0u) {
+      const int g_blk = blk0 + __builtin_ctz(keep);
+      keep &= keep - 1u;
+      if constexpr (STAGE) {
+        lb[pos] = (uint16_t)g_blk;
+      } else {
+        for (int q = 0; q < r; ++q) out[r * pos + q] = r * g_blk + q;
+      }
+      ++pos;
+    }
+    gt_run += tot[u] >> 16;
+    eq_run += tot[u] & 0xffff;
+  }
+  const int kept = gt_run + min(eq_run, take_max);
   if constexpr (NW == 2) {
     if (lane == 0) s_x[wv][2] = kept;
   }
@@ -955,8 +972,8 @@ static void launch_select_rows(IdxSelectArgs a, int row0, int nrows, hipStream_t
   const int list_words = ((a.budget + 1) / 2 + 3) & ~3;
   bool stage;
   unsigned grid, block;
-  if (NW == 1) {  // lists staged over the histogram when they fit, else written straight out
-    stage = list_words <= kSelHistWords;
+  if (NW == 1) {  // lists staged over the histogram when they fit with the flags, else written straight out
+    stage = list_words + 16 * (KPL / 4) <= kSelHistWords;
     a.list_words = list_words;
     a.wave_words = kSelHistWords + kSelTrash;
     grid = (unsigned)((nrows + 3) / 4);

@@ -238,9 +238,13 @@ __device__ void wg_select_blocks(const uint32_t (&key)[KPT], int nc, int budget,
         if (r < nrw) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const uint32_t k = key[4 * r + c];
-            const bool in = k >= lo && k < hi;
-            if (__ballot(in) != 0ull) atomicAdd(in ? &H[hpad((int)((k - lo) >> s))] : spare, 1u);
+            // k in [lo, hi) as one unsigned compare of k - lo
+            const uint32_t d = key[4 * r + c] - lo;
+            const bool in = d < range;
+            if (__ballot(in) != 0ull) {
+              const uint32_t bin = d >> s;
+              atomicAdd(in ? H + bin + ((bin >> 5) << 2) : spare, 1u);  // H[hpad(bin)]
+            }
           }
         }
       }
@@ -258,14 +262,15 @@ __device__ void wg_select_blocks(const uint32_t (&key)[KPT], int nc, int budget,
   // cut (>= hi), bit 4 + c = inside the cut bin ([lo, hi)).  Every round is
   // stored (past the row both nibbles are 0), so the bytes of [0, NT*KPT)
   // are all written.
+  const uint32_t above = 0x80000000u - hi, range = hi - lo;  // real keys are below 2^31
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     uint32_t byte = 0u;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t k = key[4 * r + c];
-      byte |= ((int)k >= 0 && k >= hi) ? 1u << c : 0u;
-      byte |= (k >= lo && k < hi) ? 16u << c : 0u;
+      byte |= k - hi < above ? 1u << c : 0u;
+      byte |= k - lo < range ? 16u << c : 0u;
     }
     S.flags[NT * r + tid] = (uint8_t)byte;
   }
