@@ -504,25 +504,27 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
     for (int c = 0; c < 4; ++c) key[4 * g + c] = i0 + c < nc ? score_key(v[c]) : 0xffffffffu;
   }
   // Largest key, smallest non-zero key and the non-zero count (groups of
-  // 256 blocks that start past the row hold no real key: skipped).
-  uint32_t kmax = 0u, kmin = 0xffffffffu, nnz = 0u;
+  // 256 blocks that start past the row hold no real key: skipped).  As
+  // signed values the empty-slot marker is -1, below every key; k - 1 wraps
+  // a zero key past every real one; the count is taken by ballots.
+  int kmax_s = 0;
+  uint32_t kmin1 = 0xffffffffu, nnz = 0u;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     if (base_i + 256 * g < nc) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t k = key[4 * g + c];
-        const bool nz = (int)k > 0;
-        kmax = (int)k >= 0 ? max(kmax, k) : kmax;
-        kmin = nz ? min(kmin, k) : kmin;
-        nnz += nz ? 1u : 0u;
+        const uint32_t k = key[4 * g + c], km1 = k - 1u;
+        kmax_s = max(kmax_s, (int)k);
+        kmin1 = min(kmin1, km1);
+        nnz += (uint32_t)__popcll(__ballot(km1 < 0x7fffffffu));
       }
     }
   }
-  kmax = __builtin_amdgcn_readlane(wave_incl_op(kmax, 0u, [](uint32_t x, uint32_t y) { return max(x, y); }), 63);
-  kmin = __builtin_amdgcn_readlane(
-      wave_incl_op(kmin, 0xffffffffu, [](uint32_t x, uint32_t y) { return min(x, y); }), 63);
-  nnz = __builtin_amdgcn_readlane(wave_incl_op(nnz, 0u, [](uint32_t x, uint32_t y) { return x + y; }), 63);
+  uint32_t kmax = __builtin_amdgcn_readlane(
+      wave_incl_op((uint32_t)kmax_s, 0u, [](uint32_t x, uint32_t y) { return max(x, y); }), 63);
+  uint32_t kmin = __builtin_amdgcn_readlane(
+      wave_incl_op(kmin1, 0xffffffffu, [](uint32_t x, uint32_t y) { return min(x, y); }), 63);
   if constexpr (NW == 2) {
     if (lane == 0) {
       s_x[wv][0] = (int)kmax;
@@ -534,6 +536,7 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
     kmin = min((uint32_t)s_x[0][1], (uint32_t)s_x[1][1]);
     nnz = (uint32_t)(s_x[0][2] + s_x[1][2]);
   }
+  kmin += 1u;  // used only when some key is non-zero (then below 2^31)
   // The cut is narrowed over key ranges [lo, hi) as in the workgroup select
   // (select_core.h): zeros are left out of the first range unless fewer than
   // `budget` keys are non-zero; the first pass takes up to 2048 bins, later

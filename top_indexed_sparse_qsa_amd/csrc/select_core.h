@@ -184,23 +184,25 @@ __device__ void wg_select_blocks(const uint32_t (&key)[KPT], int nc, int budget,
   // rounds this wave holds real keys in (wave-uniform)
   const int nrw = __builtin_amdgcn_readfirstlane(
       nc > 256 * wv ? min(R, (nc - 256 * wv + 4 * NT - 1) / (4 * NT)) : 0);
-  uint32_t kmax = 0u, kmin = 0xffffffffu, nnz = 0u;
+  // As signed values the empty-slot marker is -1, below every key; k - 1
+  // wraps a zero key past every real one (kmin below is the smallest k - 1,
+  // plus one); the non-zero count is taken by ballots.
+  int kmax_s = 0;
+  uint32_t kmin = 0xffffffffu, nnz = 0u;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r < nrw) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t k = key[4 * r + c];
-        const bool nz = (int)k > 0;  // real and non-zero
-        kmax = (int)k >= 0 ? max(kmax, k) : kmax;
-        kmin = nz ? min(kmin, k) : kmin;
-        nnz += nz ? 1u : 0u;
+        const uint32_t k = key[4 * r + c], km1 = k - 1u;
+        kmax_s = max(kmax_s, (int)k);
+        kmin = min(kmin, km1);
+        nnz += (uint32_t)__popcll(__ballot(km1 < 0x7fffffffu));
       }
     }
   }
-  kmax = wave_incl_op(kmax, 0u, [](uint32_t x, uint32_t y) { return max(x, y); });
+  uint32_t kmax = wave_incl_op((uint32_t)kmax_s, 0u, [](uint32_t x, uint32_t y) { return max(x, y); });
   kmin = wave_incl_op(kmin, 0xffffffffu, [](uint32_t x, uint32_t y) { return min(x, y); });
-  nnz = wave_incl_op(nnz, 0u, [](uint32_t x, uint32_t y) { return x + y; });
   if (lane == 63) {
     S.red[wv] = kmax;
     S.red[NW + wv] = kmin;
@@ -216,6 +218,7 @@ __device__ void wg_select_blocks(const uint32_t (&key)[KPT], int nc, int budget,
     kmin = min(kmin, S.red[NW + w]);
     nnz += S.red[2 * NW + w];
   }
+  kmin += 1u;  // used only when some key is non-zero (then below 2^31)
   // keys in [lo, hi) are still open; those >= hi are kept
   uint32_t lo, hi;
   int remaining = budget;
