@@ -51,6 +51,7 @@ CASES = [
     dict(B=2, S=300, Hq=8, Hkv=2, D=128, dtype="fp16", ctx=[300, 171], rot=64),
     dict(B=2, S=200, Hq=16, Hkv=4, D=128, dtype="bf16", ctx=[133, 200], rot=128),
     dict(B=3, S=130, Hq=4, Hkv=4, D=64, dtype="bf16", ctx=[130, 1, 0], rot=34),   # odd half: partners across lanes
+    dict(B=2, S=70, Hq=4, Hkv=2, D=128, dtype="fp16", ctx=[70, 33], rot=34),      # odd half, two dims per lane
     dict(B=1, S=257, Hq=12, Hkv=3, D=64, dtype="fp16", ctx=[257], rot=0),
 ]
 

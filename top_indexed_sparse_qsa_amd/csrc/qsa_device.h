@@ -94,14 +94,18 @@ __device__ __forceinline__ void store_q_pieces_rt(uint16_t *dst, float x, int dt
   else store_q_pieces<DT_BF16>(dst, x);
 }
 
-// double -> float rounded to odd: truncate, then force the last bit on when
-// the value was inexact.  Rounding that result to nearest-even in any format
-// with at least two fewer significant bits equals one direct rounding of the
-// double.
+// double -> float rounded to odd: x itself when exact, else whichever of its
+// two float neighbours has its last bit set.  Rounding that result to
+// nearest-even in any format with at least two fewer significant bits equals
+// one direct rounding of the double.  From the nearest float f: f is that
+// neighbour when it is exact or odd; an even, inexact f is replaced by its
+// odd neighbour on x's side (one step away from or towards zero).
 __device__ __forceinline__ float f64_to_f32_odd(double x) {
-  float f = __double2float_rz(x);
-  if ((double)f != x) f = __uint_as_float(__float_as_uint(f) | 1u);
-  return f;
+  const float f = (float)x;
+  const double fd = (double)f;
+  const uint32_t b = __float_as_uint(f);
+  if (fd == x || (b & 1u)) return f;
+  return __uint_as_float(fabs(x) > fabs(fd) ? b + 1u : b - 1u);
 }
 
 // double -> 16-bit with a single round-to-nearest-even.
