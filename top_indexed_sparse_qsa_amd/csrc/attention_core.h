@@ -61,22 +61,27 @@ struct DenseKV {
   }
 };
 
+// Paged K/V of one sequence and KV head.  The sequence's page-table rows
+// are staged in LDS as byte offsets of the pages (page_bytes_of), so a
+// token's K and V pieces are one shared in-page offset plus one LDS read
+// each.
 struct PagedKV {
-  const uint16_t *pool;   // pool + kvh * PHD
-  const int32_t *pk, *pv; // LDS copies of the sequence's page-table rows
-  size_t row_stride;      // Hkv * PHD
-  int num_flat_pages;
+  const char *pool;           // the KV head's columns of pool row 0
+  const uint64_t *pk, *pv;    // LDS: byte offset of each page of the K / V plane rows
+  uint64_t row_bytes;         // Hkv * PHD * 2
   int limit;
-  __device__ const uint16_t *row(const int32_t *pt, int id) const {
-    int pg = pt[id >> 7];
-    if ((unsigned)pg >= (unsigned)num_flat_pages) pg = 0;
-    return pool + ((size_t)pg * 128 + (id & 127)) * row_stride;
-  }
   __device__ void load(int id, int r16, u32x4 &kd, u32x4 &vd) const {
-    kd = ld16(row(pk, id) + 8 * r16);
-    vd = ld16(row(pv, id) + 8 * r16);
+    const char *tok = pool + (uint64_t)(uint32_t)(id & 127) * row_bytes + 16u * (uint32_t)r16;
+    kd = ld16(tok + pk[id >> 7]);
+    vd = ld16(tok + pv[id >> 7]);
   }
 };
+
+// Byte offset of page-table entry pg (an entry out of [0, num_flat_pages)
+// reads page 0, harmlessly: only a list id past the context could use it).
+__device__ __forceinline__ uint64_t page_bytes_of(int pg, int num_flat_pages, uint64_t row_bytes) {
+  return (uint64_t)((unsigned)pg < (unsigned)num_flat_pages ? pg : 0) * (128u * row_bytes);
+}
 
 // Lanes l and l + 32 hold the id of list slot l % 32; invalid ids become 0
 // (a harmless row to load) and are masked by the validity bits.

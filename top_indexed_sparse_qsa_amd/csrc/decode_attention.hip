@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   extern __shared__ __align__(16) unsigned char s_raw[];
   const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const DecLds<D> mg{s_raw, nw};
-  int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + DecLds<D>::bytes(nw));  // [2][max_pages]
+  uint64_t *s_pb = reinterpret_cast<uint64_t *>(s_raw + DecLds<D>::bytes(nw));  // [2][max_pages] page byte offsets
   const int group = blockIdx.x % a.ngroups;
   const int pair = blockIdx.x / a.ngroups;  // (query row, KV head)
   const int br = pair / a.Hkv, kvh = pair % a.Hkv;
@@ -82,6 +82,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   {
     const int32_t *ptb = a.pt + (size_t)b * 2 * a.max_pages;  // rows 0 and 1 are contiguous
     const int npt = 2 * a.max_pages;
+    const uint64_t row_bytes = (uint64_t)a.Hkv * a.PHD * sizeof(uint16_t);
     constexpr int U = 4;
     for (int i0 = threadIdx.x; i0 < npt; i0 += U * (int)blockDim.x) {
       int v[U];
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u * (int)blockDim.x;
-        if (i < npt) s_pt[i] = v[u];
+        if (i < npt) s_pb[i] = page_bytes_of(v[u], a.num_flat_pages, row_bytes);
       }
     }
   }
@@ -103,11 +104,10 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   float m_run = -INFINITY, l_run = 0.f;
   if (ctx > 0 && n_slots > 0 && pos >= 0 && pos < ctx_in) {
     PagedKV kv;
-    kv.pool = a.pool + (size_t)kvh * a.PHD;
-    kv.pk = s_pt;
-    kv.pv = s_pt + a.max_pages;
-    kv.row_stride = (size_t)a.Hkv * a.PHD;
-    kv.num_flat_pages = a.num_flat_pages;
+    kv.pool = reinterpret_cast<const char *>(a.pool + (size_t)kvh * a.PHD);
+    kv.pk = s_pb;
+    kv.pv = s_pb + a.max_pages;
+    kv.row_bytes = (uint64_t)a.Hkv * a.PHD * sizeof(uint16_t);
     kv.limit = ctx;
     run_list_ids<D, DT>(list, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile(wv), id_a, id_b);
   }
@@ -273,8 +273,8 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   const int tid = threadIdx.x, wv = tid >> 6;
   const DecLds<D> mg{s_raw, kDecWaves};
   WgSelLds<NT> &sel = *reinterpret_cast<WgSelLds<NT> *>(s_raw);
-  int32_t *s_pt = reinterpret_cast<int32_t *>(s_raw + step_front_bytes<D>());  // [2][max_pages]
-  uint16_t *s_lb = reinterpret_cast<uint16_t *>(s_pt + 2 * a.max_pages);
+  uint64_t *s_pb = reinterpret_cast<uint64_t *>(s_raw + step_front_bytes<D>());  // [2][max_pages] page byte offsets
+  uint16_t *s_lb = reinterpret_cast<uint16_t *>(s_pb + 2 * a.max_pages);
   const int pair = blockIdx.x;  // (sequence, KV head)
   const int b = pair / a.Hkv, kvh = pair % a.Hkv;
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
@@ -299,6 +299,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   {
     const int32_t *ptb = a.pt + (size_t)b * 2 * a.max_pages;  // rows 0 and 1 are contiguous
     const int npt = 2 * a.max_pages;
+    const uint64_t row_bytes = (uint64_t)a.Hkv * a.PHD * sizeof(uint16_t);
     constexpr int U = 4;
     for (int k0 = tid; k0 < npt; k0 += U * NT) {
       int v[U];
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = k0 + u * NT;
-        if (k < npt) s_pt[k] = v[u];
+        if (k < npt) s_pb[k] = page_bytes_of(v[u], a.num_flat_pages, row_bytes);
       }
     }
   }
@@ -347,11 +348,10 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   float m_run = -INFINITY, l_run = 0.f;
   if (ctx > 0 && n_slots > 0) {
     PagedKV kv;
-    kv.pool = a.pool + (size_t)kvh * a.PHD;
-    kv.pk = s_pt;
-    kv.pv = s_pt + a.max_pages;
-    kv.row_stride = (size_t)a.Hkv * a.PHD;
-    kv.num_flat_pages = a.num_flat_pages;
+    kv.pool = reinterpret_cast<const char *>(a.pool + (size_t)kvh * a.PHD);
+    kv.pk = s_pb;
+    kv.pv = s_pb + a.max_pages;
+    kv.row_bytes = (uint64_t)a.Hkv * a.PHD * sizeof(uint16_t);
     kv.limit = ctx;
     run_list_ids<D, DT>(mine, n_slots, kv, qf, a.sl2, m_run, l_run, acc, mg.ktile(wv), id_a, id_b);
   }
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 template <int D, int DT>
 static hipError_t launch_decode_t(const DecodeAttnArgs &a, hipStream_t s) {
   const unsigned pairs = (unsigned)((long long)a.B * a.C * a.Hkv);
-  const size_t lds = DecLds<D>::bytes(a.wpg) + (size_t)2 * a.max_pages * sizeof(int32_t);
+  const size_t lds = DecLds<D>::bytes(a.wpg) + (size_t)2 * a.max_pages * sizeof(uint64_t);
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_decode_kernel<D, DT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -381,7 +381,7 @@ template <int D, int DT, int KPT>
 static hipError_t launch_step_t(const DecodeAttnArgs &a, hipStream_t s) {
   // the kept-block list: the select runs only when budget < nc <= gmax
   const size_t lb_bytes = ((size_t)std::min(a.budget, a.gmax) * sizeof(uint16_t) + 15) & ~(size_t)15;
-  const size_t lds = step_front_bytes<D>() + (size_t)2 * a.max_pages * sizeof(int32_t) + lb_bytes;
+  const size_t lds = step_front_bytes<D>() + (size_t)2 * a.max_pages * sizeof(uint64_t) + lb_bytes;
   const void *fn = reinterpret_cast<const void *>(&decode_select_attend_kernel<D, DT, KPT>);
   if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL((decode_select_attend_kernel<D, DT, KPT>), dim3((unsigned)((long long)a.B * a.Hkv)),
