@@ -276,7 +276,7 @@ __device__ bool list_tile(const PrefillAttnArgs &a, int b, int kvh, int t0, Tile
 
   bool fail = false;
   if (t_act > t0) {
-    const int W = (t_act + 31) >> 5, nch = W;  // 32-key chunks of [0, t_act), mask words per row
+    const int W = (t_act + 31) >> 5;  // 32-key chunks of [0, t_act), mask words per row
     const bool wave_bad = wave_any(build_key_mask(a, b, t0, t_act, live, W, s_mask, s_cnt));
     if (lane == 0) s_flag[wv] = wave_bad ? 1 : 0;
     __syncthreads();
