@@ -408,10 +408,27 @@ def chunk_bench(inp, args, Q, torch, syn):
     wq, wk = dev(inp.w_q), dev(inp.w_k)
     wsp = torch.empty(Q.qsa_indexer_prefill_workspace_bytes(cfg, B, P), dtype=torch.uint8, device="cuda")
     lp = torch.empty((B, P, icfg.top_k), dtype=torch.int32, device="cuda")
-    Q.qsa_indexer_prefill(iq_all[:, :P].contiguous(), ik_all[:, :P].contiguous(), wq, wk, start, lp, wsp, cfg,
+    iq_p, ik_p = iq_all[:, :P].contiguous(), ik_all[:, :P].contiguous()
+    Q.qsa_indexer_prefill(iq_p, ik_p, wq, wk, start, lp, wsp, cfg,
                           stream=stream, kv_pool=pool, page_table=ptd, head_dim=inp.D)
     torch.cuda.synchronize()
-    del wsp, lp
+
+    # the prefill -> decode handoff: the same indexer call without and with
+    # the pool (which adds the tail writes); rerunning it rewrites the same
+    # tails and lists
+    def prefill_pair(mark):
+        if mark:
+            mark(0)
+        Q.qsa_indexer_prefill(iq_p, ik_p, wq, wk, start, lp, wsp, cfg, stream=stream)
+        if mark:
+            mark(1)
+        Q.qsa_indexer_prefill(iq_p, ik_p, wq, wk, start, lp, wsp, cfg,
+                              stream=stream, kv_pool=pool, page_table=ptd, head_dim=inp.D)
+        if mark:
+            mark(2)
+
+    _, (plain_ms, with_pool_ms) = timed_loops(prefill_pair, max(3, args.steps // 4), 1, stream, torch, 3)
+    del wsp, lp, iq_p, ik_p
     iq, ik = iq_all[:, P:].contiguous(), ik_all[:, P:].contiguous()
     q = dev(np.ascontiguousarray(inp.q[:, P:]), inp.dtype)
     o = torch.empty_like(q)
@@ -435,6 +452,10 @@ def chunk_bench(inp, args, Q, torch, syn):
                        f"S=32768 Hq=32 Hkv=4 D=128 fp16) after {P} prefilled ones, topK 2051",
            "value": B * C / (wall / args.steps), "unit": "tokens/s", "ms_per_step": wall / args.steps * 1e3,
            "indexer_ms": idx_ms, "attention_ms": attn_ms,
+           "prefill_handoff": {"indexer_prefill_ms": plain_ms, "with_pool_tails_ms": with_pool_ms,
+                               "handoff_ms": with_pool_ms - plain_ms,
+                               "note": f"qsa_indexer_prefill over the first {P} tokens without and with the "
+                                       "pool (the decode indexer's tail state written as well)"},
            "attention": {"kernel": "qsa_sparse_chunk", "bound": "mfma",
                          "achieved": attn_flops / (attn_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": attn_flops / (attn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
