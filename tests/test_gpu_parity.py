@@ -229,6 +229,30 @@ def test_sparse_prefill_identity_prefix_lists_all_rows(case):
         TL.check_zero_rows(o[b, live:], f"b={b}")
 
 
+@pytest.mark.parametrize("mode", ["full", "dups"])
+def test_sparse_prefill_two_column_tiles_g8(mode):
+    """At G = 8 a launch with tiles for two rounds of two per CU (here
+    2 x 4 x 132 tiles of 16 rows) runs two 16-column MFMA tiles per wave;
+    sampled rows of every tile position (first, last, ragged end) match the
+    oracle, with lists the key mask holds and with repeated ids (the tile's
+    rows then go to the list walk)."""
+    TL.log(f"sparse_prefill two column tiles G=8 {mode}")
+    inp = syn.make_prefill(16, B=2, S=2100, Hq=32, Hkv=4, D=128, dtype="fp16", ctx=[2100, 1999], with_indexer=False)
+    lists = identity_lists(np.random.default_rng(16), inp.B, inp.S, inp.ctx, 2051, mode)
+    o = gpu_sparse_prefill(inp, lists)
+    got = TL.host_f64(o, inp.dtype)
+    rng = np.random.default_rng(17)
+    for b in range(inp.B):
+        live = min(int(inp.ctx[b]), inp.S)
+        rows = sorted(set([0, 1, 15, 16, 17, live - 1, live - 2, 2047, 2048, 2050, 2051]
+                          + list(rng.choice(live, 120, replace=False))))
+        rows = [r for r in rows if r < live]
+        ref = O.sparse_prefill(inp.q, inp.k, inp.v, lists, inp.ctx, inp.scale, inp.dtype, rows=[(b, r) for r in rows])
+        for t in rows:
+            TL.check_attention(got[b, t], ref[b, t], inp.dtype, f"b={b} t={t}")
+        TL.check_zero_rows(o[b, live:], f"b={b}")
+
+
 # ---------------------------------------------------------------------------
 # indexer prefill
 # ---------------------------------------------------------------------------

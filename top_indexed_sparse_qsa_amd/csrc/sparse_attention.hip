@@ -46,10 +46,13 @@ namespace qsa {
 __host__ __device__ constexpr int tile_heads(int G) { return G <= 4 ? 4 : G <= 8 ? 8 : 16; }
 // 16-column MFMA tiles per wave: one (128 VGPRs, four waves per SIMD),
 // except at Gp = 16 where a column tile is a single row and two per wave
-// (186 VGPRs, two waves per SIMD) keep eight rows per tile.
+// (186 VGPRs, two waves per SIMD) keep eight rows per tile.  At Gp = 8 the
+// launcher also takes two when the launch has tiles for several rounds
+// (two per wave read each K and V fragment once for both: half the LDS
+// traffic per column).
 __host__ __device__ constexpr int tile_nt(int G) { return tile_heads(G) == 16 ? 2 : 1; }
 // rows per tile: 4 * NT 16-column tiles of 16 / Gp rows each (G >= 4 only)
-__host__ __device__ constexpr int tile_rows_for(int G) { return 4 * tile_nt(G) * (16 / tile_heads(G)); }
+__host__ __device__ constexpr int tile_rows_nt(int G, int nt) { return 4 * nt * (16 / tile_heads(G)); }
 // key-mask words of a tile workgroup (rows x 32-key chunks of the tile
 // range), at most 16 KB of LDS, which bounds the tiled rows to
 // t < 32 * kTileMaskWords / rows per tile.  The launch sizes it to its tile
@@ -651,6 +654,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #define QSA_TILE_RANGE_X2 7
 #endif
 constexpr int kTileRangeX2 = QSA_TILE_RANGE_X2;
+// The same for two column tiles per wave at Gp = 8, with a key mask of up to
+// 32 KB (two workgroups per CU either way).
+#ifndef QSA_TILE_RANGE_X2_WIDE
+#define QSA_TILE_RANGE_X2_WIDE 8
+#endif
+constexpr int kTileRangeX2Wide = QSA_TILE_RANGE_X2_WIDE;
+constexpr int kTileMaskWordsWide = 8192;
 
 // CUs per XCD of the current device (its CU count / 8), or 0 when that is
 // not a whole number.  A read-only device property, looked up once per
@@ -677,11 +687,31 @@ static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
   // rows have kernels of their own (their register budgets differ: three
   // waves per SIMD for tiles, two for the walk).
   PrefillAttnArgs a = a0;
-  a.tile_rows = tile_rows_for(a.G);
-  long long tkl = (long long)kTileRangeX2 * a.top_k * (16 / tile_heads(a.G)) / 4;
-  if (tkl > a.S) tkl = a.S;
-  if (tkl > 32LL * kTileMaskWords / a.tile_rows) tkl = 32LL * kTileMaskWords / a.tile_rows;
-  const int tk = (int)tkl;
+  // the tiled rows t < tile_range(...): the range multiplier, capped so the
+  // key mask (rows per tile x 32-key words) fits its LDS
+  auto tile_range = [&](int x2, int rows_per_tile, int mask_words) {
+    long long r = (long long)x2 * a.top_k * (16 / tile_heads(a.G)) / 4;
+    r = std::min(r, (long long)a.S);
+    return (int)std::min(r, 32LL * mask_words / rows_per_tile);
+  };
+  // Two column tiles per wave at Gp = 8 (16 rows per tile, two waves per
+  // SIMD, so a larger key mask costs no occupancy and the tiles reach further)
+  // when the launch holds tiles for at least two rounds of two per CU: the
+  // long prefill (S = 32768, Hkv = 4) gains, while the 512 tiles of S = 4096,
+  // Hkv = 2 finish sooner as 1024 smaller ones (0.123 ms against 0.151 ms).
+  int nt = tile_nt(a.G), x2 = kTileRangeX2, mask_words = kTileMaskWords;
+  if (nt == 1 && tile_heads(a.G) == 8 && xcd_cus() > 0) {
+    const int r2 = tile_rows_nt(a.G, 2);
+    const long long tiles2 =
+        (long long)a.B * a.Hkv * ((tile_range(kTileRangeX2Wide, r2, kTileMaskWordsWide) + r2 - 1) / r2);
+    if (tiles2 >= 4LL * 8 * xcd_cus()) {
+      nt = 2;
+      x2 = kTileRangeX2Wide;
+      mask_words = kTileMaskWordsWide;
+    }
+  }
+  a.tile_rows = tile_rows_nt(a.G, nt);
+  const int tk = tile_range(x2, a.tile_rows, mask_words);
   const bool tiles_on = a.G >= 4 && a.top_k >= 4;
   a.tile_below = tk;
   a.tile_per_seq = (tk + a.tile_rows - 1) / a.tile_rows;
@@ -703,7 +733,7 @@ static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
     // rows of CUs within the XCD's share of the grid
     const size_t mask_bytes = (size_t)p.tile_rows * ((p.tile_below + 31) / 32) * sizeof(uint32_t);
     const size_t lds = sizeof(TileLds) + 36 * sizeof(int) + mask_bytes;
-    const int per_cu = tile_nt(a.G) == 1 ? (int)std::min<size_t>(4, (160 * 1024) / lds) : 2;
+    const int per_cu = nt == 1 ? (int)std::min<size_t>(4, (160 * 1024) / lds) : 2;
     p.tile_cus = xcd_cus();
     p.tile_snake = 0;
     if (p.tile_cus > 0 && (8 % a.Hkv) == 0) {
@@ -711,10 +741,14 @@ static hipError_t launch_prefill_t(const PrefillAttnArgs &a0, hipStream_t s) {
       const long long start = (long long)p.tile_cus * per_cu;
       p.tile_snake = (int)min(start, per_xcd / p.tile_cus * p.tile_cus);
     }
-    if (tile_nt(a.G) == 1)
+    if (nt == 1) {
       hipLaunchKernelGGL((sparse_prefill_tile_kernel<D, DT, 1>), dim3(tile_grid(p)), dim3(256), mask_bytes, s, p);
-    else
+    } else {
+      if (lds > 65536)  // the wide key mask
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_prefill_tile_kernel<D, DT, 2>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       hipLaunchKernelGGL((sparse_prefill_tile_kernel<D, DT, 2>), dim3(tile_grid(p)), dim3(256), mask_bytes, s, p);
+    }
     return hipGetLastError();
   };
   const int total = a.B * a.S, per = prefill_rows_per_launch(a, D);
