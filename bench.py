@@ -525,7 +525,14 @@ def attach_ceiling_fracs(line, ceil):
     if not ceil:
         return
     def prefill(att):
-        att["frac_of_measured_l2_gather"] = att["algorithmic_byte_rate_gbs"] / ceil["l2_gather_256B_gbs"]
+        f = att["algorithmic_byte_rate_gbs"] / ceil["l2_gather_256B_gbs"]
+        if f <= 1.0:
+            att["frac_of_measured_l2_gather"] = f
+        else:  # the listed ids' bytes are not what moves: list tiles stage each key chunk once for many rows
+            att["frac_of_measured_l2_gather"] = None
+            att["l2_gather_note"] = ("listed-id bytes above the measured L2 gather ceiling: these rows run as list "
+                                     "tiles, which stage each 32-key chunk once for all the tile's rows; see the "
+                                     "MFMA fraction")
     prefill(line["roofline"])
     for w in line["workloads"].values():
         if "algorithmic_byte_rate_gbs" in w["attention"]:
