@@ -192,10 +192,14 @@ typedef struct {
  * there are no more than `budget`; equal scores favour the lower block),
  * written in ascending block order as ratio consecutive ids each, then its
  * causal tail ratio*floor((t+1)/ratio) .. t, then -1.  Rows t >=
- * context_lengths[b] are all -1.  Scores are computed in fp32 from an exact
- * two- (fp16) or three-piece (bf16) split of the fp32 queries; the pages
- * call such scoring selection-equivalent, so a swap of blocks whose scores
- * sit within fp32 rounding of the cut can differ from a float64 reference.
+ * context_lengths[b] are all -1.  Scores are computed in fp32 from a
+ * two-piece fp16 split of the fp32 queries (22 significant bits) against
+ * kbar taken as fp16 (bf16 kbar converted: exact in fp16's normal range;
+ * RMSNorm bounds |kbar| by sqrt(128) * max|1 + w_k|, inside fp16's range
+ * while max|1 + w_k| < 5000);
+ * the pages call such scoring selection-equivalent, so a swap of blocks
+ * whose scores sit within that rounding of the cut can differ from a
+ * float64 reference.
  * workspace: device scratch of at least
  * qsa_indexer_prefill_workspace_bytes() bytes, 256-byte aligned.
  * Optional prefill -> decode handoff [Plugin: KV pool contract (widened

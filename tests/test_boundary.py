@@ -45,16 +45,16 @@ def test_status_strings():
 def test_workspace_sizes_follow_layout():
     cfg = Q.indexer_config()
     a = lambda x: (x + 255) // 256 * 256
-    # prefill: queries (three 16-bit pieces per value) | kbar | fp32 scores with a 16-rounded stride
+    # prefill: queries (two fp16 pieces per value) | kbar | fp32 scores with a 16-rounded stride
     B, S = 1, 32768
     g = S // 4
     assert Q.qsa_indexer_prefill_workspace_bytes(cfg, B, S) == \
-        a(B * S * 4 * 128 * 6) + a(B * g * 128 * 2) + a(B * S * g * 4)
+        a(B * S * 4 * 128 * 4) + a(B * g * 128 * 2) + a(B * S * g * 4)
     B, S = 4, 16383
     g = S // 4
     st = (g + 15) // 16 * 16
     assert Q.qsa_indexer_prefill_workspace_bytes(cfg, B, S) == \
-        a(B * S * 4 * 128 * 6) + a(B * g * 128 * 2) + a(B * S * st * 4)
+        a(B * S * 4 * 128 * 4) + a(B * g * 128 * 2) + a(B * S * st * 4)
     # decode: one fp32 score row per sequence, stride 128 * max_pages / ratio rounded to 16
     assert Q.qsa_indexer_decode_workspace_bytes(cfg, 32, 512) == a(32 * 16384 * 4)
     assert Q.qsa_indexer_decode_workspace_bytes(cfg, 3, 33) == a(3 * 1056 * 4)
@@ -366,6 +366,6 @@ def test_chunk_workspace_follows_layout():
     a = lambda x: (x + 255) // 256 * 256
     B, C, mp = 2, 100, 20
     g = mp * 128 // 4
-    assert Q.qsa_indexer_chunk_workspace_bytes(cfg, B, C, mp) == a(B * C * 4 * 128 * 6) + a(B * g * 128 * 2) + \
+    assert Q.qsa_indexer_chunk_workspace_bytes(cfg, B, C, mp) == a(B * C * 4 * 128 * 4) + a(B * g * 128 * 2) + \
         a(B * C * g * 4)
     assert Q.qsa_indexer_chunk_workspace_bytes(cfg, 0, C, mp) == 0

@@ -66,9 +66,9 @@ def gpu_indexer_prefill(inp, icfg, top_k):
 
 
 def kbar_from_workspace(ws, inp, icfg):
-    """The kbar region of the prefill workspace: after the queries (up to
-    three 16-bit scoring pieces per value)."""
-    qbytes = inp.B * inp.S * icfg.num_heads * icfg.head_dim * 6
+    """The kbar region of the prefill workspace: after the queries (two fp16
+    scoring pieces per value)."""
+    qbytes = inp.B * inp.S * icfg.num_heads * icfg.head_dim * 4
     off = (qbytes + 255) // 256 * 256
     gmax = inp.S // icfg.compress_ratio
     raw = ws[off:off + inp.B * gmax * icfg.head_dim * 2].view(torch.int16).cpu().numpy().view(np.uint16)

@@ -43,8 +43,8 @@ int64_t min_top_k(const qsa_indexer_config &c) {
   return (int64_t)c.budget * c.compress_ratio + c.compress_ratio - 1;
 }
 
-// Prefill indexer workspace: queries (fp32 values as up to three 16-bit
-// scoring pieces each) | 16-bit kbar | fp32 score rows.
+// Prefill indexer workspace: queries (fp32 values as two fp16 scoring
+// pieces each) | 16-bit kbar | fp32 score rows.
 struct PrefillWs {
   size_t qhat, kbar, scores, total;
   int gmax, stride;
@@ -54,7 +54,7 @@ PrefillWs prefill_ws(const qsa_indexer_config &c, int32_t B, int32_t S) {
   w.gmax = S / c.compress_ratio;
   w.stride = (int)round16((size_t)(w.gmax > 0 ? w.gmax : 1));
   w.qhat = 0;
-  w.kbar = align_up((size_t)B * S * c.num_heads * c.head_dim * 2 * qsa::kQPiecesMax);
+  w.kbar = align_up((size_t)B * S * c.num_heads * c.head_dim * 4);
   w.scores = w.kbar + align_up((size_t)B * (w.gmax > 0 ? w.gmax : 1) * c.head_dim * 2);
   w.total = w.scores + align_up((size_t)B * S * w.stride * 4);
   return w;
@@ -85,7 +85,7 @@ ChunkWs chunk_ws(const qsa_indexer_config &c, int32_t B, int32_t C, int32_t max_
   w.gmax = max_pages * QSA_PAGE_TOKENS / c.compress_ratio;
   w.stride = (int)round16((size_t)(w.gmax > 0 ? w.gmax : 1));
   w.qhat = 0;
-  w.kbar = align_up((size_t)B * C * c.num_heads * c.head_dim * 2 * qsa::kQPiecesMax);
+  w.kbar = align_up((size_t)B * C * c.num_heads * c.head_dim * 4);
   w.scores = w.kbar + align_up((size_t)B * w.gmax * c.head_dim * 2);
   w.total = w.scores + align_up((size_t)B * C * w.stride * 4);
   return w;

@@ -109,9 +109,9 @@ __global__ __launch_bounds__(256) void idx_prep_kernel(IdxPrepArgs a) {
         norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt), wq0, wq1,
                    a.eps, a.rot, r, o0, o1);
         // q-hat rounded once to fp32, stored as the scoring's 16-bit pieces
-        uint16_t *qp = a.qhat + off * q_pieces(a.dt);
-        store_q_pieces_rt(qp + lane, (float)o0, a.dt);
-        store_q_pieces_rt(qp + 64 + lane, (float)o1, a.dt);
+        uint16_t *qp = a.qhat + off * kQPieces;
+        store_q_pieces(qp + lane, (float)o0);
+        store_q_pieces(qp + 64 + lane, (float)o1);
       }
     } else {
       const long long kk = item - nrows;
@@ -201,9 +201,9 @@ __global__ __launch_bounds__(256) void idx_chunk_prep_kernel(IdxChunkPrepArgs a)
       const size_t off = (((size_t)b * a.C + k) * a.Hi + h) * 128;
       norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
                  (double)a.wq[lane], (double)a.wq[lane + 64], a.eps, a.rot, rp, o0, o1);
-      uint16_t *qp = a.qhat + off * q_pieces(a.dt);
-      store_q_pieces_rt(qp + lane, (float)o0, a.dt);
-      store_q_pieces_rt(qp + 64 + lane, (float)o1, a.dt);
+      uint16_t *qp = a.qhat + off * kQPieces;
+      store_q_pieces(qp + lane, (float)o0);
+      store_q_pieces(qp + 64 + lane, (float)o1);
     }
     return;
   }
@@ -258,27 +258,28 @@ __global__ __launch_bounds__(256) void idx_chunk_prep_kernel(IdxChunkPrepArgs a)
   }
 }
 
-// fp32 -> exact sum of NP 16-bit pieces (two fp16 or three bf16).
-template <int DT>
-struct QSplit {
-  static constexpr int NP = DT == DT_F16 ? 2 : 3;
-};
-
-template <int DT>
-__device__ __forceinline__ void split8(const float (&x)[8], u32x4 (&out)[QSplit<DT>::NP]) {
+// Eight fp32 query values -> their kQPieces fp16 pieces (as store_q_pieces).
+__device__ __forceinline__ void split8(const float (&x)[8], u32x4 (&out)[kQPieces]) {
   float r[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = x[i];
 #pragma unroll
-  for (int p = 0; p < QSplit<DT>::NP; ++p) {
+  for (int p = 0; p < kQPieces; ++p) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t h0 = f32_to_bits<DT>(r[2 * w]), h1 = f32_to_bits<DT>(r[2 * w + 1]);
-      r[2 * w] -= bits_to_f32_t<DT>(h0);
-      r[2 * w + 1] -= bits_to_f32_t<DT>(h1);
+      uint32_t h0 = f32_to_bits<DT_F16>(r[2 * w]), h1 = f32_to_bits<DT_F16>(r[2 * w + 1]);
+      r[2 * w] -= bits_to_f32_t<DT_F16>(h0);
+      r[2 * w + 1] -= bits_to_f32_t<DT_F16>(h1);
       out[p][w] = h0 | (h1 << 16);
     }
   }
+}
+
+// A kbar piece (eight 16-bit values) as the fp16 MFMA operand.
+template <int DT>
+__device__ __forceinline__ u32x4 kbar_operand(u32x4 v) {
+  if constexpr (DT == DT_F16) return v;
+  else return bf16x8_to_f16x8(v);
 }
 
 __device__ __forceinline__ void load8f(float (&x)[8], const float *p) {
@@ -300,9 +301,9 @@ __device__ __forceinline__ void load8f(float (&x)[8], const float *p) {
 // kbar fragment.  The chunk's 32 x kScoreChunk scores are assembled in LDS and
 // stored as whole 512-byte row segments.
 template <int DT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == DT_F16 ? 3 : 2))) void idx_score_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void idx_score_kernel(
     IdxScoreArgs a) {
-  constexpr int NP = QSplit<DT>::NP;
+  constexpr int NP = kQPieces;
   constexpr int CB = kScoreChunk;
   __shared__ __align__(16) uint32_t s_kb[CB * 64];     // CB rows x 256 B
   __shared__ __align__(16) float s_sc[32][CB + 4];    // scores of the chunk
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == DT_F1
     for (int u = 0; u < NV; ++u) {
       const int i = tid + 256 * u;
       const int row = i >> 4, pc = i & 15;
-      if (i < npiece) *reinterpret_cast<u32x4 *>(&s_kb[row * 64 + 4 * (pc ^ (row & 15))]) = v[u];
+      if (i < npiece) *reinterpret_cast<u32x4 *>(&s_kb[row * 64 + 4 * (pc ^ (row & 15))]) = kbar_operand<DT>(v[u]);
     }
   };
   load_chunk(run_lo);  // in flight while the queries are loaded and split
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == DT_F1
 #pragma unroll
         for (int p = 0; p < NP; ++p)
 #pragma unroll
-          for (int m = 0; m < 2; ++m) acc[m] = mfma16x16x32<DT>(qa[m][p][ks], kb[ks], acc[m]);
+          for (int m = 0; m < 2; ++m) acc[m] = mfma16x16x32<DT_F16>(qa[m][p][ks], kb[ks], acc[m]);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const f32x4 d = acc[m];
@@ -794,7 +795,7 @@ constexpr int kDecScoreWaves = QSA_DEC_SCORE_WAVES;
 template <int DT>
 __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_per_eu(5))) void idx_dec_score_kernel(
     IdxDecScoreArgs a) {
-  constexpr int NP = QSplit<DT>::NP;
+  constexpr int NP = kQPieces;
   constexpr int TPW = kScoreTilesPerWave;
   __shared__ __align__(16) float s_q[4][128];
   __shared__ __align__(16) uint16_t s_kb[128];
@@ -901,7 +902,7 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = 0.f;
     u32x4 pieces[NP];
-    split8<DT>(x, pieces);
+    split8(x, pieces);
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) qb[pp][ks] = pieces[pp];
   }
@@ -915,7 +916,7 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
     for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt)
-        accs[tt][ks & 1] = mfma16x16x32<DT>(kb[tt][ks], qb[pp][ks], accs[tt][ks & 1]);
+        accs[tt][ks & 1] = mfma16x16x32<DT_F16>(kbar_operand<DT>(kb[tt][ks]), qb[pp][ks], accs[tt][ks & 1]);
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const f32x4 acc = accs[tt][0] + accs[tt][1];

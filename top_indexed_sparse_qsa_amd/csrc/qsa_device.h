@@ -73,25 +73,30 @@ __device__ __forceinline__ uint32_t f32_to_bits_rt(float x, int dt) {
 }
 
 // An fp32 query value as the 16-bit pieces the block scoring multiplies
-// (MFMA takes 16-bit operands): piece 0 is x rounded to the dtype, each next
-// piece the rounded remainder; 2 pieces for fp16 (11 + 11 significant bits),
-// 3 for bf16 (8 + 8 + 8), at most kQPiecesMax.  Stored 128 elements apart.
-__host__ __device__ constexpr int q_pieces(int dt) { return dt == DT_F16 ? 2 : 3; }
+// (fp16 MFMA operands, for either activation dtype): piece 0 is x rounded to
+// fp16, piece 1 the rounded remainder (11 + 11 significant bits).  Stored
+// 128 elements apart.
+constexpr int kQPieces = 2;
 
-template <int DT>
 __device__ __forceinline__ void store_q_pieces(uint16_t *dst, float x) {
   float r = x;
 #pragma unroll
-  for (int p = 0; p < q_pieces(DT); ++p) {
-    const uint32_t h = f32_to_bits<DT>(r);
-    r -= bits_to_f32_t<DT>(h);
+  for (int p = 0; p < kQPieces; ++p) {
+    const uint32_t h = f32_to_bits<DT_F16>(r);
+    r -= bits_to_f32_t<DT_F16>(h);
     dst[128 * p] = (uint16_t)h;
   }
 }
 
-__device__ __forceinline__ void store_q_pieces_rt(uint16_t *dst, float x, int dt) {
-  if (dt == DT_F16) store_q_pieces<DT_F16>(dst, x);
-  else store_q_pieces<DT_BF16>(dst, x);
+// Two bf16 values (low, high halves) as two fp16 values: exact for
+// magnitudes in fp16's normal range [2^-14, 65504]; smaller ones round to
+// fp16's subnormal steps of 2^-24.  Block scoring takes bf16 kbar this way,
+// so that both dtypes score with the same fp16 MFMA and two query pieces.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  return pack2<DT_F16>(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+}
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  return u32x4{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]), bf16x2_to_f16x2(v[3])};
 }
 
 // double -> float rounded to odd: x itself when exact, else whichever of its

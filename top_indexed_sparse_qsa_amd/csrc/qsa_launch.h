@@ -88,7 +88,6 @@ struct IdxScoreArgs {
   int run_chunks;   // chunks per run (set by the launcher)
 };
 
-constexpr int kQPiecesMax = 3;            // 16-bit pieces per prepared query value (bf16: 3)
 constexpr int kScoreChunk = 128;           // kbar rows staged at a time in prefill scoring
 // most chunks per prefill scoring workgroup: fp16 (three waves per SIMD)
 // balances best over short runs, bf16 (two waves per SIMD, 1.5x the query
