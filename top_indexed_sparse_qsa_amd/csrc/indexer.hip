@@ -9,8 +9,8 @@
 //
 // Precision: pooling, RMSNorm and RoPE run in fp64 and round once (kbar to
 // the activation dtype, queries to fp32).  Scoring is an MFMA contraction of
-// the fp32 queries, split exactly into two fp16 or three bf16 pieces, against
-// the 16-bit kbar, accumulated in fp32.  Scores are kept unscaled by
+// the fp32 queries, split exactly into two fp16 pieces, against the kbar
+// taken as fp16 (bf16 kbar converted), accumulated in fp32.  Scores are kept unscaled by
 // 1/sqrt(hd): a positive factor does not change which blocks win.
 #include <math.h>
 
@@ -37,18 +37,34 @@ static void fill_freq(double *freq, int rot, double theta) {
   for (int i = 0; i < 64; ++i) freq[i] = i < (rot >> 1) ? pow(theta, (-2.0 * (double)i) / (double)rot) : 0.0;
 }
 
-__device__ __forceinline__ Rope2 rope_at(double pos, const double *s_freq, int rot) {
+// The lane's two frequencies, read once per kernel before any other load:
+// the table sits in the kernel arguments but is indexed per lane, so it is
+// a vector load, and one issued after a batch of loads waits for all of
+// them.
+struct RopeLane {
+  double f0, f1;
+  bool same;  // dims lane and lane + 64 share a frequency (rot = 128)
+};
+
+__device__ __forceinline__ RopeLane rope_lane(const double *freq, int rot) {
   const int lane = lane_id(), half = rot >> 1;
-  Rope2 r{1.0, 0.0, 1.0, 0.0};
   const int d0 = lane, d1 = lane + 64;
   const int i0 = d0 < half ? d0 : d0 - half, i1 = d1 < half ? d1 : d1 - half;
-  if (d0 < rot) sincos_angle(pos * s_freq[i0], &r.s0, &r.c0);
+  // indexes past the table (dims >= rot, which do not rotate) are clamped
+  return RopeLane{freq[min(max(i0, 0), 63)], freq[min(max(i1, 0), 63)], i1 == i0};
+}
+
+__device__ __forceinline__ Rope2 rope_at(double pos, const RopeLane &f, int rot) {
+  const int lane = lane_id();
+  Rope2 r{1.0, 0.0, 1.0, 0.0};
+  const int d0 = lane, d1 = lane + 64;
+  if (d0 < rot) sincos_angle(pos * f.f0, &r.s0, &r.c0);
   if (d1 < rot) {
-    if (d0 < rot && i1 == i0) {
+    if (d0 < rot && f.same) {
       r.c1 = r.c0;
       r.s1 = r.s0;
     } else {
-      sincos_angle(pos * s_freq[i1], &r.s1, &r.c1);
+      sincos_angle(pos * f.f1, &r.s1, &r.c1);
     }
   }
   return r;
@@ -85,48 +101,114 @@ __device__ __forceinline__ long long pool_row_off(const int32_t *ptrow, int toke
   return (((long long)pg * 128 + (token & 127)) * Hkv) * PHD;
 }
 
-// Items: B*S query rows, then B*Gmax blocks; a.per_wave consecutive items
+// Workgroups go round-robin over the eight XCDs.  For work whose cost
+// follows the item's sequence (item mod B, live lengths differ), the n-th set
+// of eight workgroups takes items 8n + ((x + n) mod 8) on XCD x: each XCD
+// cycles through every residue instead of keeping the ones that B ties to
+// its index.  Launches round the grid up to a multiple of eight and
+// bound-check the item.
+__device__ __forceinline__ int xcd_spread(int blk) {
+  const int n = blk >> 3;
+  return (n << 3) | (((blk & 7) + n) & 7);
+}
+
+// Items: B*S query rows, then B*Gmax blocks, a.per_wave consecutive items
 // per wave (up to kPrepItemsPerWave, fewer when that would leave the chip
-// short of waves), four waves per workgroup.
+// short of waves), four waves per workgroup; a wave holds rows only or
+// blocks only.  A wave issues every load of its next item before it works
+// on the current one.  (The item's stores could alias its loads as far as
+// the compiler knows, so loads written inside the per-head loop would each
+// wait for the previous head's stores: one memory round trip per head.)
 constexpr int kPrepItemsPerWave = 4;
 
+// One item's inputs, lane l's dims l and l + 64: a row's heads (slot h =
+// head h) or a block's raw keys (slot j = token j).  Slots past Hi (ratio)
+// repeat the last real one, so the loads are issued unconditionally.
+template <int N>
+struct PrepIn {
+  uint32_t x[N][2];
+  int ctx;
+};
+
+__device__ __forceinline__ void prep_row_loads(const IdxPrepArgs &a, long long item, int lane, PrepIn<4> &in) {
+  in.ctx = a.ctx[item / a.S];
+  const uint16_t *src = a.idx_q + (size_t)item * a.Hi * 128 + lane;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int hh = min(h, a.Hi - 1);
+    in.x[h][0] = src[hh * 128];
+    in.x[h][1] = src[hh * 128 + 64];
+  }
+}
+
+__device__ __forceinline__ void prep_block_loads(const IdxPrepArgs &a, long long kk, int lane, PrepIn<8> &in) {
+  const int b = (int)(kk / a.Gmax), g = (int)(kk % a.Gmax);
+  in.ctx = a.ctx[b];
+  const uint16_t *src = a.idx_k + ((size_t)b * a.S + (size_t)a.ratio * g) * 128 + lane;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int jj = min(j, a.ratio - 1);
+    in.x[j][0] = src[jj * 128];
+    in.x[j][1] = src[jj * 128 + 64];
+  }
+}
+
 __global__ __launch_bounds__(256) void idx_prep_kernel(IdxPrepArgs a) {
-  const double *s_freq = a.freq;
+  const RopeLane rl = rope_lane(a.freq, a.rot);
   const int lane = lane_id();
   const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const long long nrows = (long long)a.B * a.S, total = nrows + (long long)a.B * a.Gmax;
-  const double wq0 = a.wq[lane], wq1 = a.wq[lane + 64], wk0 = a.wk[lane], wk1 = a.wk[lane + 64];
-  for (int k = 0; k < a.per_wave; ++k) {
-    const long long item = wave * a.per_wave + k;
-    if (item >= total) break;
-    double o0, o1;
-    if (item < nrows) {
-      const int b = (int)(item / a.S), t = (int)(item % a.S);
-      if (t >= min(a.ctx[b], a.S)) continue;
-      const Rope2 r = rope_at((double)t, s_freq, a.rot);
-      for (int h = 0; h < a.Hi; ++h) {
-        const size_t off = ((size_t)item * a.Hi + h) * 128;
-        norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt), wq0, wq1,
-                   a.eps, a.rot, r, o0, o1);
-        // q-hat rounded once to fp32, stored as the scoring's 16-bit pieces
-        uint16_t *qp = a.qhat + off * kQPieces;
-        store_q_pieces(qp + lane, (float)o0);
-        store_q_pieces(qp + 64 + lane, (float)o1);
+  const long long nrows = (long long)a.B * a.S, nblocks = (long long)a.B * a.Gmax;
+  const long long row_waves = (nrows + a.per_wave - 1) / a.per_wave;
+  double o0, o1;
+  if (wave < row_waves) {
+    const long long first = wave * a.per_wave, end = min(first + a.per_wave, nrows);
+    const double w0 = a.wq[lane], w1 = a.wq[lane + 64];
+    PrepIn<4> cur;
+    prep_row_loads(a, first, lane, cur);
+    for (long long item = first; item < end; ++item) {
+      PrepIn<4> nxt;
+      prep_row_loads(a, min(item + 1, end - 1), lane, nxt);
+      const int t = (int)(item % a.S);
+      if (t < min(cur.ctx, a.S)) {
+        const Rope2 r = rope_at((double)t, rl, a.rot);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          if (h >= a.Hi) break;
+          norm_rope2(bits_to_f64(cur.x[h][0], a.dt), bits_to_f64(cur.x[h][1], a.dt), w0, w1, a.eps, a.rot, r, o0,
+                     o1);
+          // q-hat rounded once to fp32, stored as the scoring's 16-bit pieces
+          uint16_t *qp = a.qhat + ((size_t)item * a.Hi + h) * 128 * kQPieces;
+          store_q_pieces(qp + lane, (float)o0);
+          store_q_pieces(qp + 64 + lane, (float)o1);
+        }
       }
-    } else {
-      const long long kk = item - nrows;
-      const int b = (int)(kk / a.Gmax), g = (int)(kk % a.Gmax);
-      if (g >= min(a.ctx[b], a.S) / a.ratio) continue;
+      cur = nxt;
+    }
+    return;
+  }
+  const long long first = (wave - row_waves) * a.per_wave, end = min(first + a.per_wave, nblocks);
+  if (first >= end) return;
+  const double w0 = a.wk[lane], w1 = a.wk[lane + 64];
+  // one item's loads at a time here (blocks are a quarter of the items or
+  // fewer; a second buffer of eight slots would cost the row waves'
+  // occupancy as well)
+  for (long long kk = first; kk < end; ++kk) {
+    PrepIn<8> cur;
+    prep_block_loads(a, kk, lane, cur);
+    const int b = (int)(kk / a.Gmax), g = (int)(kk % a.Gmax);
+    if (g < min(cur.ctx, a.S) / a.ratio) {
+      // mean over the block's tokens, summed in token order from +0
       double m0 = 0.0, m1 = 0.0;
-      for (int j = 0; j < a.ratio; ++j) {
-        const size_t off = ((size_t)b * a.S + (size_t)a.ratio * g + j) * 128;
-        m0 += bits_to_f64(a.idx_k[off + lane], a.dt);
-        m1 += bits_to_f64(a.idx_k[off + 64 + lane], a.dt);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= a.ratio) break;
+        m0 += bits_to_f64(cur.x[j][0], a.dt);
+        m1 += bits_to_f64(cur.x[j][1], a.dt);
       }
       m0 /= (double)a.ratio;
       m1 /= (double)a.ratio;
-      const Rope2 r = rope_at((double)a.ratio * g, s_freq, a.rot);
-      norm_rope2(m0, m1, wk0, wk1, a.eps, a.rot, r, o0, o1);
+      const Rope2 r = rope_at((double)a.ratio * g, rl, a.rot);
+      norm_rope2(m0, m1, w0, w1, a.eps, a.rot, r, o0, o1);
       const size_t ob = ((size_t)b * a.Gmax + g) * 128;
       a.kbar[ob + lane] = (uint16_t)f64_to_bits(o0, a.dt);
       a.kbar[ob + 64 + lane] = (uint16_t)f64_to_bits(o1, a.dt);
@@ -178,7 +260,7 @@ __global__ __launch_bounds__(256) void idx_handoff_kernel(IdxPrepArgs a) {
 // The tails these items read (V rows of blocks complete before the chunk, K
 // rows of tokens before it) and those they write are disjoint.
 __global__ __launch_bounds__(256) void idx_chunk_prep_kernel(IdxChunkPrepArgs a) {
-  const double *s_freq = a.freq;
+  const RopeLane rl = rope_lane(a.freq, a.rot);
   const int lane = lane_id();
   const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long long per_seq = (long long)a.C + a.Gmax + 1;
@@ -196,7 +278,7 @@ __global__ __launch_bounds__(256) void idx_chunk_prep_kernel(IdxChunkPrepArgs a)
   if (k < a.C) {  // queries of row k
     const int pos = P + k;
     if (pos >= ctx) return;
-    const Rope2 rp = rope_at((double)pos, s_freq, a.rot);
+    const Rope2 rp = rope_at((double)pos, rl, a.rot);
     for (int h = 0; h < a.Hi; ++h) {
       const size_t off = (((size_t)b * a.C + k) * a.Hi + h) * 128;
       norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
@@ -237,7 +319,7 @@ __global__ __launch_bounds__(256) void idx_chunk_prep_kernel(IdxChunkPrepArgs a)
     }
     m0 /= (double)r;
     m1 /= (double)r;
-    const Rope2 rp = rope_at((double)(r * g), s_freq, a.rot);
+    const Rope2 rp = rope_at((double)(r * g), rl, a.rot);
     norm_rope2(m0, m1, (double)a.wk[lane], (double)a.wk[lane + 64], a.eps, a.rot, rp, o0, o1);
     const uint16_t k0 = (uint16_t)f64_to_bits(o0, a.dt), k1 = (uint16_t)f64_to_bits(o1, a.dt);
     kb[lane] = k0;
@@ -288,11 +370,12 @@ __device__ __forceinline__ void load8f(float (&x)[8], const float *p) {
   x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
 
-// Prefill scoring.  A workgroup takes 32 consecutive rows and a run of up to
-// kScoreRunF16 / kScoreRunBf16 chunks of kScoreChunk complete blocks (the
-// rows' query pieces, prepared by the prep kernel, are loaded once per run;
-// short prefills take shorter runs so the grid still fills the chip); runs
-// of the last rows are dispatched first, all runs of a row group on one XCD.
+// Prefill scoring.  A workgroup takes 32 consecutive rows and a run of
+// chunks of kScoreChunk complete blocks (whole rows or kScoreRun chunks, as
+// the launcher decides; the rows' query pieces, prepared by the prep kernel,
+// are loaded once per run; short prefills take shorter runs so the grid
+// still fills the chip); runs of the last rows are dispatched first, all
+// runs of a row group on one XCD.
 // Per chunk the kbar rows are staged in LDS, 16-byte pieces XOR-swizzled by
 // row so that MFMA fragment reads are conflict-free; each wave
 // computes 8 rows against the chunk.  The MFMA M tile is (row, head) with the
@@ -310,17 +393,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15, wv = threadIdx.x >> 6;
   const int tid = threadIdx.x;
   const int T32 = (a.S + 31) >> 5;
-  // Row group grp (= rows of sequence grp % B, last rows first) runs on XCD
-  // grp % 8 (workgroups go round-robin over the eight XCDs): its runs share
-  // the group's queries through that XCD's L2 instead of each XCD fetching
-  // them.
+  // Workgroups go round-robin over the eight XCDs.  All runs of a row group
+  // run on one XCD, so they share the group's queries through its L2.  The
+  // n-th group of XCD x is group level (n mod L8) * 8 + x (level 0 = the last
+  // 32 rows) of sequence n / L8, L8 = ceil(levels / 8): an XCD takes one
+  // sequence at a time (its kbar stays in the XCD's L2), longest rows first,
+  // and every XCD takes the same levels of every sequence, so ragged batches
+  // load the XCDs evenly.
   const int xcd = blockIdx.x & 7;
   const long long n = blockIdx.x >> 3;
   const int run = (int)(n % a.nchunk);
-  const long long grp = (n / a.nchunk) * 8 + xcd;
-  if (grp >= (long long)a.B * T32) return;
-  const int b = (int)(grp % a.B);
-  const int tg = 32 * (T32 - 1 - (int)(grp / a.B));
+  const long long k = n / a.nchunk;
+  const long long L8 = (T32 + 7) / 8;
+  const int b = (int)(k / L8);
+  const long long level = (k % L8) * 8 + xcd;
+  if (level >= T32) return;
+  const int tg = 32 * (T32 - 1 - (int)level);
   // row t sits at position off + t; rows [0, live) are live
   const int off = a.start ? a.start[b] : 0;
   // positions stay below Gmax * ratio, the blocks the kbar rows hold
@@ -470,7 +558,8 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   const int wv = threadIdx.x >> 6, lane = lane_id();
   const int h = NW == 1 ? 0 : wv;
   const int tid = NW == 1 ? lane : (int)threadIdx.x, nthr = 64 * NW;
-  const int row = a.row0 + (NW == 1 ? (int)blockIdx.x * 4 + wv : (int)blockIdx.x);
+  const int wg = xcd_spread((int)blockIdx.x);
+  const int row = a.row0 + (NW == 1 ? wg * 4 + wv : wg);
   if (row >= a.row0 + a.nrows) return;  // a two-wave workgroup holds one row
   const int b = row % a.B;
   const int t = a.S - 1 - row / a.B;  // longest rows first
@@ -723,7 +812,8 @@ __global__ __launch_bounds__(kSelWgThreads) void idx_select_wg_kernel(IdxSelectA
     out = a.out + (size_t)b * a.top_k;
     srow = a.scores + (size_t)b * a.row_stride;
   } else {
-    const int rw = a.row0 + blockIdx.x;  // longest rows first
+    const int rw = a.row0 + xcd_spread((int)blockIdx.x);  // longest rows first
+    if (rw >= a.row0 + a.nrows) return;  // the grid is rounded up to eight
     const int b = rw % a.B;
     const int tl = a.S - 1 - rw / a.B;   // the row; its position is off + tl
     const int off = a.start ? a.start[b] : 0;
@@ -799,7 +889,7 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
   constexpr int TPW = kScoreTilesPerWave;
   __shared__ __align__(16) float s_q[4][128];
   __shared__ __align__(16) uint16_t s_kb[128];
-  const double *s_freq = a.freq;
+  const RopeLane rl = rope_lane(a.freq, a.rot);
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x / a.wg_per_seq, wg = blockIdx.x % a.wg_per_seq;
@@ -843,7 +933,7 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
 
   // query head wv at position p
   if (wv < a.Hi) {
-    const Rope2 r = rope_at((double)p, s_freq, a.rot);
+    const Rope2 r = rope_at((double)p, rl, a.rot);
     const size_t off = ((size_t)b * a.Hi + wv) * 128;
     double o0, o1;
     norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
@@ -870,7 +960,7 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
     m1 += bits_to_f64(a.idx_k[(size_t)b * 128 + 64 + lane], a.dt);
     m0 /= (double)a.ratio;
     m1 /= (double)a.ratio;
-    const Rope2 r = rope_at((double)base, s_freq, a.rot);
+    const Rope2 r = rope_at((double)base, rl, a.rot);
     double o0, o1;
     norm_rope2(m0, m1, (double)a.wk[lane], (double)a.wk[lane + 64], a.eps, a.rot, r, o0, o1);
     const uint16_t k0 = (uint16_t)f64_to_bits(o0, a.dt), k1 = (uint16_t)f64_to_bits(o1, a.dt);
@@ -941,9 +1031,9 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
 hipError_t launch_idx_prep(const IdxPrepArgs &a_in, hipStream_t s) {
   IdxPrepArgs a = a_in;
   fill_freq(a.freq, a.rot, a.theta);
-  const long long items = (long long)a.B * a.S + (long long)a.B * a.Gmax;
-  a.per_wave = (int)std::min<long long>(kPrepItemsPerWave, std::max<long long>(1, items / 8192));
-  const long long waves = (items + a.per_wave - 1) / a.per_wave;
+  const long long nrows = (long long)a.B * a.S, nblocks = (long long)a.B * a.Gmax;
+  a.per_wave = (int)std::min<long long>(kPrepItemsPerWave, std::max<long long>(1, (nrows + nblocks) / 8192));
+  const long long waves = (nrows + a.per_wave - 1) / a.per_wave + (nblocks + a.per_wave - 1) / a.per_wave;
   hipLaunchKernelGGL(idx_prep_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -959,11 +1049,14 @@ hipError_t launch_idx_score(const IdxScoreArgs &a_in, int dt, hipStream_t s) {
   IdxScoreArgs a = a_in;
   const int chunks = max(1, (a.Gmax + kScoreChunk - 1) / kScoreChunk);
   const long long groups = (long long)a.B * ((a.S + 31) / 32);
-  int run = dt == DT_F16 ? kScoreRunF16 : kScoreRunBf16;  // halved until ~2048 workgroups (8 waves per CU)
+  int run = groups >= kScoreWholeRowGroups && chunks <= kScoreWholeRowChunks ? chunks : kScoreRun;
+  // halved until ~2048 workgroups (8 waves per CU)
   while (run > 1 && groups * ((chunks + run - 1) / run) < 2048) run >>= 1;
   a.run_chunks = run;
   a.nchunk = (chunks + run - 1) / run;
-  const unsigned grid = (unsigned)(8 * ((groups + 7) / 8) * a.nchunk);
+  // per XCD: B sequences x ceil(levels / 8) groups, nchunk runs each
+  const long long per_xcd = (long long)a.B * ((((a.S + 31) / 32) + 7) / 8);
+  const unsigned grid = (unsigned)(8 * per_xcd * a.nchunk);
   if (dt == DT_F16) hipLaunchKernelGGL(idx_score_kernel<DT_F16>, dim3(grid), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(idx_score_kernel<DT_BF16>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -982,13 +1075,13 @@ static void launch_select_rows(IdxSelectArgs a, int row0, int nrows, hipStream_t
     stage = list_words + 16 * (KPL / 4) <= kSelHistWords;
     a.list_words = list_words;
     a.wave_words = kSelHistWords + kSelTrash;
-    grid = (unsigned)((nrows + 3) / 4);
+    grid = (unsigned)(((nrows + 3) / 4 + 7) & ~7);  // whole sets of eight (xcd_spread)
     block = 256;
   } else {        // [histogram | second histogram | list0 | list1]; two waves only when both lists fit
     stage = true;
     a.list_words = list_words;
     a.wave_words = kSelHistWords + kSelTrash + kSelSmallWords + kSelTrash + 2 * list_words;
-    grid = (unsigned)nrows;
+    grid = (unsigned)((nrows + 7) & ~7);
     block = 128;
   }
   const size_t lds = (size_t)(NW == 1 ? 4 : 1) * a.wave_words * sizeof(uint32_t);
@@ -1009,7 +1102,10 @@ static void launch_select_wg(IdxSelectArgs a, int row0, unsigned rows, hipStream
   const void *fn = reinterpret_cast<const void *>(&idx_select_wg_kernel<KPT>);
   if (lds + sizeof(WgSelLds<kSelWgThreads>) > 65536)
     (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((idx_select_wg_kernel<KPT>), dim3(rows), dim3(kSelWgThreads), lds, s, a);
+  // decode: one workgroup per sequence; prefill and chunk rows: whole sets
+  // of eight workgroups (xcd_spread)
+  const unsigned grid = a.decode ? rows : ((rows + 7u) & ~7u);
+  hipLaunchKernelGGL((idx_select_wg_kernel<KPT>), dim3(grid), dim3(kSelWgThreads), lds, s, a);
 }
 
 static void launch_select_wg_for(const IdxSelectArgs &a, int nc_max, int row0, unsigned rows, hipStream_t s) {

@@ -89,12 +89,16 @@ struct IdxScoreArgs {
 };
 
 constexpr int kScoreChunk = 128;           // kbar rows staged at a time in prefill scoring
-// most chunks per prefill scoring workgroup: fp16 (three waves per SIMD)
-// balances best over short runs, bf16 (two waves per SIMD, 1.5x the query
-// pieces to load per run) over long ones (measured at S = 32768 fp16 and
-// B = 4 x 16384 bf16: 4 and 16 beat 2 and 8)
-constexpr int kScoreRunF16 = 4;
-constexpr int kScoreRunBf16 = 16;
+// Chunks per prefill scoring workgroup (a run).  Whole rows when there are
+// at least kScoreWholeRowGroups row groups and a row holds at most
+// kScoreWholeRowChunks chunks: the longest run then stays below the average
+// work per workgroup slot, so longest-first dispatch finishes evenly, and each
+// group loads its queries once.  Otherwise runs of kScoreRun chunks, which
+// keep the last runs short.  (Measured over nine shapes from 1 x 8192 to
+// 4 x 32768 rows; runs of 8 to 16 chunks were never the fastest.)
+constexpr int kScoreRun = 4;
+constexpr int kScoreWholeRowGroups = 2048;
+constexpr int kScoreWholeRowChunks = 32;
 
 struct IdxSelectArgs {
   const float *scores;
