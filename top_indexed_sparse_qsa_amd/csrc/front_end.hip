@@ -109,10 +109,10 @@ __global__ __launch_bounds__(256) void front_end_kernel(FrontEndArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) ss += x[e] * x[e];
     ss = wave_sum_f64(ss);
-    // one division per lane (the same for every lane) instead of one per
-    // element: x * (1 / den) and x / den differ by an fp64 ulp at most,
-    // far below the 16-bit rounding that follows
-    const double inv = 1.0 / sqrt(ss / (double)D + a.eps);
+    // one inverse square root per lane (the same for every lane) instead of
+    // a division per element: x * (1 / den) and x / den differ by about an
+    // fp64 ulp, far below the 16-bit rounding that follows
+    const double inv = inv_sqrt_f64(ss / (double)D + a.eps);
     double y[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) y[e] = x[e] * inv * (double)(is_q ? gq[e] : gk[e]);

@@ -74,9 +74,9 @@ __device__ __forceinline__ Rope2 rope_at(double pos, const RopeLane &f, int rot)
 __device__ __forceinline__ void norm_rope2(double x0, double x1, double w0, double w1, double eps, int rot,
                                            const Rope2 &r, double &o0, double &o1) {
   const double ss = wave_sum_f64(x0 * x0 + x1 * x1);
-  // one division per lane: x * (1 / den) and x / den differ by an fp64 ulp
-  // at most, far below the one rounding at the end
-  const double inv = 1.0 / sqrt(ss / 128.0 + eps);
+  // one inverse square root per lane: x * (1 / den) and x / den differ by
+  // about an fp64 ulp, far below the one rounding at the end
+  const double inv = inv_sqrt_f64(ss / 128.0 + eps);
   const double y0 = x0 * inv * (1.0 + w0), y1 = x1 * inv * (1.0 + w1);
   const int lane = lane_id(), half = rot >> 1;
   const int d0 = lane, d1 = lane + 64;

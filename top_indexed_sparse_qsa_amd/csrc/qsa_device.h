@@ -113,6 +113,22 @@ __device__ __forceinline__ float f64_to_f32_odd(double x) {
   return __uint_as_float(fabs(x) > fabs(fd) ? b + 1u : b - 1u);
 }
 
+// 1 / sqrt(v) for a normal v > 0: the hardware estimate (about 23 correct
+// bits) refined by two Newton steps r += r (1 - v r^2) / 2, within about an
+// fp64 ulp of the correctly rounded value (a correctly rounded sqrt and
+// divide take ~26 instructions; this takes 9).  Every use rounds the
+// normalised value once more, to fp32 or 16 bits, where an fp64 ulp decides
+// the rounding only for values within ~2^-29 (fp32) of a tie.
+__device__ __forceinline__ double inv_sqrt_f64(double v) {
+  double r = __builtin_amdgcn_rsq(v);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const double e = fma(-(v * r), r, 1.0);
+    r = fma(0.5 * r, e, r);
+  }
+  return r;
+}
+
 // double -> 16-bit with a single round-to-nearest-even.
 __device__ __forceinline__ uint32_t f64_to_bits(double x, int dt) {
   return f32_to_bits_rt(f64_to_f32_odd(x), dt);
