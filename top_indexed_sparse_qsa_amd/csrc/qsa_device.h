@@ -178,27 +178,45 @@ __device__ __forceinline__ void sincos_angle(double x, double *s, double *c) {
   *c = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
 }
 
-// One DPP step of a wave scan on a double (both 32-bit halves move).
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ double dpp_f64(double v) {
+// One in-row DPP shift of a double (both 32-bit halves move); a source lane
+// outside the row reads 0 (bound_ctrl), so no zero fill precedes the moves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_row_shr_f64(double v) {
   const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWMASK, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWMASK, 0xf, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xf, 0xf, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, true);
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
-// Sum of v over the wave, in every lane: an inclusive DPP scan (row shifts,
-// then the row broadcasts of lanes 15 and 31), and lane 63's total.
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
-  v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
-  v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
-  v += dpp_f64<0x118, 0xf>(v);  // row_shr:8
-  v += dpp_f64<0x142, 0xa>(v);  // row_bcast:15
-  v += dpp_f64<0x143, 0xc>(v);  // row_bcast:31
+// v + v[lane ^ 16] (X16) or v + v[lane ^ 32]: the gfx950 lane swap hands
+// every lane its own value and its partner's, one in each output, so their
+// sum is the pair's sum whichever output holds which.
+template <bool X16>
+__device__ __forceinline__ double add_swapped_f64(double v) {
   const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+  const auto l = X16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                     : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h = X16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                     : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const double d0 = __longlong_as_double((long long)(((unsigned long long)h[0] << 32) | l[0]));
+  const double d1 = __longlong_as_double((long long)(((unsigned long long)h[1] << 32) | l[1]));
+  return d0 + d1;
+}
+
+// Sum of v over the wave, in every lane: an inclusive scan within each row
+// of 16 lanes (lane 16r + 15 ends with row r's sum), the rows' sums added
+// across lanes l ^ 32 and then l ^ 16, and lane 15's total read back.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_row_shr_f64<0x111>(v);  // row_shr:1
+  v += dpp_row_shr_f64<0x112>(v);  // row_shr:2
+  v += dpp_row_shr_f64<0x114>(v);  // row_shr:4
+  v += dpp_row_shr_f64<0x118>(v);  // row_shr:8
+  v = add_swapped_f64<false>(v);   // rows 0 + 2, 1 + 3
+  v = add_swapped_f64<true>(v);    // all four
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 15);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 15);
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
