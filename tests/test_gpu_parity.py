@@ -401,6 +401,48 @@ def test_indexer_prefill_long_rows_workgroup_select(classes):
         TL.log(f"  boundary swaps used: {swaps}")
 
 
+RAGGED_BATCHES = [
+    # every row: three sequences (B does not divide the eight XCDs' order)
+    dict(B=3, S=1300, dtype="fp16", ctx=[1300, 0, 777], budget=12, rows="all"),
+    # every row: eight sequences with empty, one-token and near-full lengths
+    dict(B=8, S=600, dtype="bf16", ctx=[600, 1, 599, 333, 0, 64, 450, 2], budget=9, rows="all"),
+    # sampled rows: the two-wave select class in three sequences
+    dict(B=3, S=17000, dtype="fp16", ctx=[17000, 16500, 9000], budget=64, rows=12),
+    # sampled rows: 2048 row groups of <= 32 chunks, so scoring takes whole
+    # rows per workgroup; ragged lengths across eight sequences
+    dict(B=8, S=8192, dtype="bf16", ctx=[8192, 8000, 100, 8192, 5000, 0, 7777, 4096], budget=512, rows=6),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED_BATCHES, ids=lambda c: f"B{c['B']}S{c['S']}{c['dtype']}k{c['budget']}")
+def test_indexer_prefill_ragged_batches(case):
+    """Batches of several sequences of different lengths: scoring deals row
+    groups to the XCDs sequence by sequence and the selects spread rows over
+    them; every list (or a sample of rows of every sequence, plus every row's
+    closed-form invariants) must match the oracle."""
+    icfg = syn.IndexerCfg(budget=case["budget"])
+    TL.log(f"indexer_prefill ragged {case}")
+    inp = syn.make_prefill(21, B=case["B"], S=case["S"], Hq=2, Hkv=1, D=64, dtype=case["dtype"], ctx=case["ctx"],
+                           icfg=icfg)
+    out, _ = gpu_indexer_prefill(inp, icfg, icfg.top_k)
+    out_np = out.cpu().numpy()
+    if case["rows"] == "all":
+        rows = [(b, t) for b in range(inp.B) for t in range(inp.S)]
+    else:
+        rng = np.random.default_rng(21)
+        rows = set()
+        for b in range(inp.B):
+            live = min(int(inp.ctx[b]), inp.S)
+            rows |= {(b, int(t)) for t in rng.integers(0, max(live, 1), case["rows"])}
+            rows |= {(b, max(live - 1, 0)), (b, inp.S - 1)}
+        rows = sorted(rows)
+        n_rows = TL.check_list_invariants_all_rows(out_np, inp.ctx, icfg, "ragged")
+        TL.log(f"  list invariants hold on all {n_rows} live rows")
+    lists = {r: out_np[r] for r in rows}
+    _, swaps, _ = compare_lists(lists, inp, icfg, icfg.top_k, rows, "ragged")
+    TL.log(f"  rows {len(rows)}, boundary swaps used: {swaps}")
+
+
 # ---------------------------------------------------------------------------
 # the prefill workloads at full size (bench launch configuration)
 # ---------------------------------------------------------------------------
