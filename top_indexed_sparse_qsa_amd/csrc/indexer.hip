@@ -9,9 +9,10 @@
 //
 // Precision: pooling, RMSNorm and RoPE run in fp64 and round once (kbar to
 // the activation dtype, queries to fp32).  Scoring is an MFMA contraction of
-// the fp32 queries, split exactly into two fp16 pieces, against the kbar
-// taken as fp16 (bf16 kbar converted), accumulated in fp32.  Scores are kept unscaled by
-// 1/sqrt(hd): a positive factor does not change which blocks win.
+// the fp32 queries, split into two fp16 pieces (hi + lo: about 22 of their
+// 24 significant bits), against the kbar taken as fp16 (bf16 kbar
+// converted), accumulated in fp32.  Scores are kept unscaled by 1/sqrt(hd):
+// a positive factor does not change which blocks win.
 #include <math.h>
 
 #include <algorithm>
