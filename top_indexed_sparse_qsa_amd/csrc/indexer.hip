@@ -898,12 +898,19 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
   const int g_begin = wg_begin + wv * TPW * 16;
   const int32_t *ptk = a.pt + (size_t)b * 2 * a.max_pages;
   const int32_t *ptv = ptk + a.max_pages;
-  // the page-table entries of this wave's blocks go out with the context
-  // length (one round trip before the tail loads instead of two)
+  // Loads in the order they are needed (they return in order): the context
+  // length; the page-table entries of this wave's blocks (one round trip
+  // before the tail loads instead of two); the inputs of query head wv, which
+  // the fp64 prep below works on while the tails are in flight (issued after
+  // the tails, the prep would wait for all of them).
+  const int ctx_raw = a.ctx[b];
   int pte[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) pte[tt] = ptv[min((a.ratio * (g_begin + tt * 16 + r16)) >> 7, a.max_pages - 1)];
-  const int ctx = min(a.ctx[b], a.max_pages * 128);
+  const size_t qoff = ((size_t)b * a.Hi + min(wv, a.Hi - 1)) * 128;
+  const uint32_t qx0 = a.idx_q[qoff + lane], qx1 = a.idx_q[qoff + 64 + lane];
+  const float wq0 = a.wq[lane], wq1 = a.wq[lane + 64];
+  const int ctx = min(ctx_raw, a.max_pages * 128);
   if (ctx <= 0) return;
   const int p = ctx - 1;
   const int nc = ctx / a.ratio;
@@ -935,10 +942,8 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
   // query head wv at position p
   if (wv < a.Hi) {
     const Rope2 r = rope_at((double)p, rl, a.rot);
-    const size_t off = ((size_t)b * a.Hi + wv) * 128;
     double o0, o1;
-    norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
-               (double)a.wq[lane], (double)a.wq[lane + 64], a.eps, a.rot, r, o0, o1);
+    norm_rope2(bits_to_f64(qx0, a.dt), bits_to_f64(qx1, a.dt), (double)wq0, (double)wq1, a.eps, a.rot, r, o0, o1);
     s_q[wv][lane] = (float)o0;
     s_q[wv][lane + 64] = (float)o1;
   }
