@@ -279,12 +279,24 @@ __global__ __launch_bounds__(256) void idx_chunk_prep_kernel(IdxChunkPrepArgs a)
   if (k < a.C) {  // queries of row k
     const int pos = P + k;
     if (pos >= ctx) return;
+    // every head's inputs loaded before the first store (as in the prefill
+    // prep: a store may alias a later head's input as far as the compiler
+    // knows, so per-head loads would each wait for the previous stores)
+    const size_t row_off = ((size_t)b * a.C + k) * a.Hi * 128;
+    uint32_t x[4][2];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const size_t off = row_off + (size_t)min(h, a.Hi - 1) * 128;
+      x[h][0] = a.idx_q[off + lane];
+      x[h][1] = a.idx_q[off + 64 + lane];
+    }
+    const double w0 = a.wq[lane], w1 = a.wq[lane + 64];
     const Rope2 rp = rope_at((double)pos, rl, a.rot);
-    for (int h = 0; h < a.Hi; ++h) {
-      const size_t off = (((size_t)b * a.C + k) * a.Hi + h) * 128;
-      norm_rope2(bits_to_f64(a.idx_q[off + lane], a.dt), bits_to_f64(a.idx_q[off + 64 + lane], a.dt),
-                 (double)a.wq[lane], (double)a.wq[lane + 64], a.eps, a.rot, rp, o0, o1);
-      uint16_t *qp = a.qhat + off * kQPieces;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      if (h >= a.Hi) break;
+      norm_rope2(bits_to_f64(x[h][0], a.dt), bits_to_f64(x[h][1], a.dt), w0, w1, a.eps, a.rot, rp, o0, o1);
+      uint16_t *qp = a.qhat + (row_off + (size_t)h * 128) * kQPieces;
       store_q_pieces(qp + lane, (float)o0);
       store_q_pieces(qp + 64 + lane, (float)o1);
     }
