@@ -161,3 +161,75 @@ def test_chunk_long_prefill_tail():
     got_o = TL.host_f64(o, inp.dtype)
     for j, t in enumerate(rows):
         TL.check_attention(got_o[0, t], ref_o[0, j], inp.dtype, f"long chunk row {t}")
+
+
+def test_chunk_ragged_starts():
+    """Three sequences whose chunks start and end at different positions (one
+    from position 0, one ending a few rows into the chunk, one past a page
+    boundary): every list against the oracle (margin rule), the tails bit for
+    bit, the attention of rows whose lists agree, the padding rows, and the
+    same lists as the one-shot prefill of each sequence."""
+    B, S = 3, 900
+    start = np.array([100, 0, 641], dtype=np.int32)
+    ctx = np.array([700, 351, 900], dtype=np.int32)
+    C = int((ctx - start).max()) + 2
+    icfg = syn.IndexerCfg(budget=16)
+    TL.log(f"chunk ragged starts {start.tolist()} ctx {ctx.tolist()} C={C}")
+    inp = syn.make_prefill(77, B=B, S=S, Hq=8, Hkv=2, D=64, dtype="bf16", ctx=ctx, icfg=icfg)
+    rng = np.random.default_rng(77)
+    max_pages = (S + 127) // 128 + 1
+    pool, pt = paged_state(rng, inp, S, max_pages)
+    O.apply_tail_writes(pool, O.prefill_state_writes(inp.idx_k, inp.w_k, start, pt, icfg, inp.D, inp.dtype), inp.D)
+
+    def rows_from(a):  # each sequence's C rows from its own start, zero past S
+        out = np.zeros((B, C) + a.shape[2:], dtype=a.dtype)
+        for b in range(B):
+            n = min(C, S - int(start[b]))
+            out[b, :n] = a[b, start[b]:start[b] + n]
+        return out
+    iq, ik, q = rows_from(inp.idx_q), rows_from(inp.idx_k), rows_from(inp.q)
+    cfg = TL.idx_cfg_struct(icfg)
+    ws = torch.empty(Q.qsa_indexer_chunk_workspace_bytes(cfg, B, C, max_pages), dtype=torch.uint8, device="cuda")
+    lists = torch.full((B, C, icfg.top_k), -7, dtype=torch.int32, device="cuda")
+    pool_dev = TL.dev(pool, inp.dtype)
+    Q.qsa_indexer_chunk(TL.dev(iq, inp.dtype), TL.dev(ik, inp.dtype), TL.dev(inp.w_q), TL.dev(inp.w_k), pool_dev,
+                        TL.dev(pt), TL.dev(start), TL.dev(ctx), lists, ws, cfg, inp.D)
+    q_dev = TL.dev(q, inp.dtype)
+    o = torch.full_like(q_dev, float("nan"))
+    Q.qsa_sparse_chunk(q_dev, o, pool_dev, TL.dev(pt), lists, TL.dev(start), TL.dev(ctx), inp.scale, head_dim=inp.D)
+    torch.cuda.synchronize()
+    got = lists.cpu().numpy()
+    writes, ref, scores = O.indexer_chunk(iq, ik, inp.w_q, inp.w_k, pool, pt, start, ctx, icfg, inp.D, inp.dtype,
+                                          icfg.top_k, return_scores=True)
+    same, swaps = [], 0
+    for b in range(B):
+        live = int(ctx[b] - start[b])
+        for t in range(C):
+            if t >= live:
+                assert np.all(got[b, t] == -1), f"b={b}: padding row {t}"
+                continue
+            used = TL.check_list(got[b, t], ref[b, t], scores.get((b, t)), int(start[b]) + t, icfg, f"ragged b={b}")
+            swaps += used
+            if not used:
+                same.append((b, t))
+    TL.log(f"  boundary swaps used: {swaps}")
+    expect = pool.copy()
+    O.apply_tail_writes(expect, writes, inp.D)
+    assert torch.equal(pool_dev.view(torch.int16), TL.dev(expect, inp.dtype).view(torch.int16)), "pool after chunk"
+    ref_o = O.sparse_chunk(q, pool, pt, ref, start, ctx, inp.scale, inp.D, inp.dtype)
+    got_o = TL.host_f64(o, inp.dtype)
+    for (b, t) in same:
+        TL.check_attention(got_o[b, t], ref_o[b, t], inp.dtype, f"ragged chunk attention b={b} t={t}")
+    for b in range(B):
+        TL.check_zero_rows(o[b, int(ctx[b] - start[b]):], f"ragged chunk b={b} padding rows")
+    # the one-shot prefill of each sequence selects the same lists
+    wsp = torch.empty(Q.qsa_indexer_prefill_workspace_bytes(cfg, B, S), dtype=torch.uint8, device="cuda")
+    one = torch.full((B, S, icfg.top_k), -7, dtype=torch.int32, device="cuda")
+    Q.qsa_indexer_prefill(TL.dev(inp.idx_q, inp.dtype), TL.dev(inp.idx_k, inp.dtype), TL.dev(inp.w_q),
+                          TL.dev(inp.w_k), TL.dev(ctx), one, wsp, cfg)
+    torch.cuda.synchronize()
+    one = one.cpu().numpy()
+    for b in range(B):
+        for t in range(int(ctx[b] - start[b])):
+            assert np.array_equal(np.sort(got[b, t]), np.sort(one[b, start[b] + t])), \
+                f"b={b}: chunk row {t} vs one-shot row {start[b] + t}"
