@@ -233,3 +233,64 @@ def test_chunk_ragged_starts():
         for t in range(int(ctx[b] - start[b])):
             assert np.array_equal(np.sort(got[b, t]), np.sort(one[b, start[b] + t])), \
                 f"b={b}: chunk row {t} vs one-shot row {start[b] + t}"
+
+
+def test_chunk_rows_across_select_classes():
+    """Chunk rows on both sides of 8192 complete blocks (the pool holds
+    longer rows, so the per-row kernel and the workgroup kernel both run over
+    the chunk and split its rows): every list against the oracle (margin
+    rule), the tails bit for bit, and the one-shot prefill's lists."""
+    B, S = 2, 33300
+    start = np.array([32700, 32000], dtype=np.int32)
+    ctx = np.array([33300, 32800], dtype=np.int32)
+    C = int((ctx - start).max()) + 1
+    icfg = syn.IndexerCfg()
+    TL.log(f"chunk across select classes: starts {start.tolist()} ctx {ctx.tolist()} C={C}")
+    inp = syn.make_prefill(78, B=B, S=S, Hq=2, Hkv=1, D=64, dtype="fp16", ctx=ctx, icfg=icfg)
+    rng = np.random.default_rng(78)
+    max_pages = (S + 127) // 128 + 1
+    pool, pt = paged_state(rng, inp, S, max_pages)
+    O.apply_tail_writes(pool, O.prefill_state_writes(inp.idx_k, inp.w_k, start, pt, icfg, inp.D, inp.dtype), inp.D)
+
+    def rows_from(a):
+        out = np.zeros((B, C) + a.shape[2:], dtype=a.dtype)
+        for b in range(B):
+            n = min(C, S - int(start[b]))
+            out[b, :n] = a[b, start[b]:start[b] + n]
+        return out
+    iq, ik = rows_from(inp.idx_q), rows_from(inp.idx_k)
+    cfg = TL.idx_cfg_struct(icfg)
+    ws = torch.empty(Q.qsa_indexer_chunk_workspace_bytes(cfg, B, C, max_pages), dtype=torch.uint8, device="cuda")
+    lists = torch.full((B, C, icfg.top_k), -7, dtype=torch.int32, device="cuda")
+    pool_dev = TL.dev(pool, inp.dtype)
+    Q.qsa_indexer_chunk(TL.dev(iq, inp.dtype), TL.dev(ik, inp.dtype), TL.dev(inp.w_q), TL.dev(inp.w_k), pool_dev,
+                        TL.dev(pt), TL.dev(start), TL.dev(ctx), lists, ws, cfg, inp.D)
+    torch.cuda.synchronize()
+    got = lists.cpu().numpy()
+    writes, ref, scores = O.indexer_chunk(iq, ik, inp.w_q, inp.w_k, pool, pt, start, ctx, icfg, inp.D, inp.dtype,
+                                          icfg.top_k, return_scores=True)
+    swaps, long_rows = 0, 0
+    for b in range(B):
+        live = int(ctx[b] - start[b])
+        for t in range(C):
+            if t >= live:
+                assert np.all(got[b, t] == -1), f"b={b}: padding row {t}"
+                continue
+            long_rows += (int(start[b]) + t + 1) // icfg.compress_ratio > 8192
+            swaps += TL.check_list(got[b, t], ref[b, t], scores.get((b, t)), int(start[b]) + t, icfg, f"b={b}")
+    TL.log(f"  rows past 8192 blocks: {long_rows}; boundary swaps used: {swaps}")
+    assert long_rows > 0 and long_rows < int((ctx - start).sum()), "the chunk must span both select classes"
+    expect = pool.copy()
+    O.apply_tail_writes(expect, writes, inp.D)
+    assert torch.equal(pool_dev.view(torch.int16), TL.dev(expect, inp.dtype).view(torch.int16)), "pool after chunk"
+    del ws
+    wsp = torch.empty(Q.qsa_indexer_prefill_workspace_bytes(cfg, B, S), dtype=torch.uint8, device="cuda")
+    one = torch.full((B, S, icfg.top_k), -7, dtype=torch.int32, device="cuda")
+    Q.qsa_indexer_prefill(TL.dev(inp.idx_q, inp.dtype), TL.dev(inp.idx_k, inp.dtype), TL.dev(inp.w_q),
+                          TL.dev(inp.w_k), TL.dev(ctx), one, wsp, cfg)
+    torch.cuda.synchronize()
+    one_np = one[:, 32000:].cpu().numpy()
+    for b in range(B):
+        for t in range(int(ctx[b] - start[b])):
+            assert np.array_equal(np.sort(got[b, t]), np.sort(one_np[b, start[b] + t - 32000])), \
+                f"b={b}: chunk row {t} vs one-shot row {start[b] + t}"

@@ -575,15 +575,19 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   const int row = a.row0 + (NW == 1 ? wg * 4 + wv : wg);
   if (row >= a.row0 + a.nrows) return;  // a two-wave workgroup holds one row
   const int b = row % a.B;
-  const int t = a.S - 1 - row / a.B;  // longest rows first
-  const bool live = t < min(a.ctx[b], a.S);
-  int32_t *out = a.out + ((size_t)b * a.S + t) * a.top_k;
+  const int tl = a.S - 1 - row / a.B;  // longest rows first; the row's position is off + tl
+  const int t = (a.start ? a.start[b] : 0) + tl;
+  const bool live = t >= 0 && t < min(a.ctx[b], a.max_ctx);
+  int32_t *out = a.out + ((size_t)b * a.S + tl) * a.top_k;
   if (!live) {
     for (int i = tid; i < a.top_k; i += nthr) out[i] = -1;
     return;
   }
   const int r = a.ratio;
   const int nc = (t + 1) / r;
+  // chunk rows reach every launch (their lengths are device data): a row
+  // longer than this kernel holds is the workgroup select's
+  if (a.start && nc > NW * SPAN) return;
   if (nc <= a.budget) {
     for (int i = tid; i < a.top_k; i += nthr) out[i] = i <= t ? i : -1;
     return;
@@ -596,7 +600,7 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   uint16_t *lb0 =
       reinterpret_cast<uint16_t *>(region + (NW == 1 ? 0 : kSelHistWords + kSelTrash + kSelSmallWords + kSelTrash));
   uint16_t *lb = lb0 + 2 * h * a.list_words;
-  const float *srow = a.scores + ((size_t)b * a.S + t) * a.row_stride;
+  const float *srow = a.scores + ((size_t)b * a.S + tl) * a.row_stride;
   const int base_i = h * SPAN;
   uint32_t key[KPL];
 #pragma unroll
@@ -832,6 +836,9 @@ __global__ __launch_bounds__(kSelWgThreads) void idx_select_wg_kernel(IdxSelectA
     const int off = a.start ? a.start[b] : 0;
     t = off + tl;
     live = t >= 0 && t < min(a.ctx[b], a.max_ctx);
+    // chunk rows of up to wg_min_nc blocks, dead ones included, are the
+    // per-row kernel's (launched over the same rows)
+    if (a.wg_min_nc > 0 && (!live || (t + 1) / a.ratio <= a.wg_min_nc)) return;
     out = a.out + ((size_t)b * a.S + tl) * a.top_k;
     srow = a.scores + ((size_t)b * a.S + tl) * a.row_stride;
   }
@@ -1141,9 +1148,24 @@ hipError_t launch_idx_select(const IdxSelectArgs &a, int nc_max, hipStream_t s) 
     return hipGetLastError();
   }
   if (a.start) {
-    // chunk rows: their positions are device data, so the rows cannot be
-    // sorted into length classes on the host; one workgroup each
-    launch_select_wg_for(a, nc_max, 0, (unsigned)((long long)a.B * a.S), s);
+    // Chunk rows: their positions are device data, so the host cannot sort
+    // them into length classes.  The two-wave per-row kernel runs over every
+    // row and takes those of up to 8192 blocks; when the pool can hold
+    // longer rows, the workgroup kernel runs over every row as well and
+    // takes only those.
+    const int total = (int)((long long)a.B * a.S);
+    const int list_words = (a.budget * a.ratio + 3) & ~3;
+    constexpr int kTwoWaveBlocks = 2 * 64 * 64;
+    if (list_words <= 4096) {
+      launch_select_rows<64, 2>(a, 0, total, s);
+      if (nc_max > kTwoWaveBlocks) {
+        IdxSelectArgs w = a;
+        w.wg_min_nc = kTwoWaveBlocks;
+        launch_select_wg_for(w, nc_max, 0, (unsigned)total, s);
+      }
+    } else {
+      launch_select_wg_for(a, nc_max, 0, (unsigned)total, s);
+    }
     return hipGetLastError();
   }
   // Prefill rows go longest first (row = (S - 1 - t) * B + b), so rows whose

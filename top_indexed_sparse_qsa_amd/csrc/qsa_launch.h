@@ -113,6 +113,7 @@ struct IdxSelectArgs {
   int wave_words;      // per-row kernels: LDS words per row region (set by the launcher)
   int list_words;      // two-wave kernel: LDS words of each wave's list (set by the launcher)
   int row0, nrows;     // prefill: this launch covers rows [row0, row0 + nrows) (set by the launcher)
+  int wg_min_nc;       // chunk rows, workgroup kernel: skip rows of at most this many blocks (0: none)
 };
 
 // Indexer decode B1 + B2 (one kernel): query prep, the pool-tail update and
