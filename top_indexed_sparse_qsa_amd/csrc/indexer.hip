@@ -353,34 +353,11 @@ __global__ __launch_bounds__(256) void idx_chunk_prep_kernel(IdxChunkPrepArgs a)
   }
 }
 
-// Eight fp32 query values -> their kQPieces fp16 pieces (as store_q_pieces).
-__device__ __forceinline__ void split8(const float (&x)[8], u32x4 (&out)[kQPieces]) {
-  float r[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = x[i];
-#pragma unroll
-  for (int p = 0; p < kQPieces; ++p) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t h0 = f32_to_bits<DT_F16>(r[2 * w]), h1 = f32_to_bits<DT_F16>(r[2 * w + 1]);
-      r[2 * w] -= bits_to_f32_t<DT_F16>(h0);
-      r[2 * w + 1] -= bits_to_f32_t<DT_F16>(h1);
-      out[p][w] = h0 | (h1 << 16);
-    }
-  }
-}
-
 // A kbar piece (eight 16-bit values) as the fp16 MFMA operand.
 template <int DT>
 __device__ __forceinline__ u32x4 kbar_operand(u32x4 v) {
   if constexpr (DT == DT_F16) return v;
   else return bf16x8_to_f16x8(v);
-}
-
-__device__ __forceinline__ void load8f(float (&x)[8], const float *p) {
-  f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
-  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
-  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
 
 // Prefill scoring.  A workgroup takes 32 consecutive rows and a run of
@@ -907,7 +884,7 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
     IdxDecScoreArgs a) {
   constexpr int NP = kQPieces;
   constexpr int TPW = kScoreTilesPerWave;
-  __shared__ __align__(16) float s_q[4][128];
+  __shared__ __align__(16) uint16_t s_qp[4][kQPieces][128];  // query heads as fp16 scoring pieces
   __shared__ __align__(16) uint16_t s_kb[128];
   const RopeLane rl = rope_lane(a.freq, a.rot);
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
@@ -963,8 +940,10 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
     const Rope2 r = rope_at((double)p, rl, a.rot);
     double o0, o1;
     norm_rope2(bits_to_f64(qx0, a.dt), bits_to_f64(qx1, a.dt), (double)wq0, (double)wq1, a.eps, a.rot, r, o0, o1);
-    s_q[wv][lane] = (float)o0;
-    s_q[wv][lane + 64] = (float)o1;
+    // rounded once to fp32 and split into the pieces here, once per head
+    // (every wave reads every head's pieces below)
+    store_q_pieces(&s_qp[wv][0][lane], (float)o0);
+    store_q_pieces(&s_qp[wv][0][lane + 64], (float)o1);
   }
   // the block this step completes, when this workgroup holds it
   const int g_new = nc - 1;
@@ -1009,18 +988,15 @@ __global__ __launch_bounds__(64 * kDecScoreWaves) __attribute__((amdgpu_waves_pe
   }
 
   u32x4 qb[NP][4];
+  const bool head_ok = r16 < a.Hi;
+  const int hq = min(r16, a.Hi - 1);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    float x[8];
-    if (r16 < a.Hi) load8f(x, &s_q[r16][32 * ks + 8 * q4]);
-    else
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
-    u32x4 pieces[NP];
-    split8(x, pieces);
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) qb[pp][ks] = pieces[pp];
-  }
+    for (int pp = 0; pp < NP; ++pp) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&s_qp[hq][pp][32 * ks + 8 * q4]);
+      qb[pp][ks] = head_ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
   float *srow = a.scores + (size_t)b * a.stride;
   f32x4 accs[TPW][2];
 #pragma unroll
