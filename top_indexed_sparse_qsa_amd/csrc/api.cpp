@@ -176,7 +176,7 @@ const char *qsa_status_string(qsa_status s) {
     case QSA_OK: return "ok";
     case QSA_ERR_NULL_POINTER: return "null pointer argument";
     case QSA_ERR_BAD_SHAPE: return "invalid shape or size argument";
-    case QSA_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case QSA_ERR_UNSUPPORTED: return "configuration not supported by the library";
     case QSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case QSA_ERR_LAUNCH: return "HIP kernel launch failed";
     default: break;
