@@ -539,6 +539,16 @@ __device__ __forceinline__ void row_sync() {
   else __syncthreads();
 }
 
+// First-pass bits of the per-row select: 11 (2048 bins), or 10 for the
+// one-wave kernels of up to 32 keys per lane (rows of up to 2048 blocks),
+// whose 62-64 registers allow eight waves per SIMD but whose four 2048-bin
+// histograms per workgroup would allow only four.  Ten first-pass bits and
+// three passes of eight still reach single keys.
+__host__ __device__ constexpr int sel_rows_first_bits(int KPL, int NW) { return NW == 1 && KPL <= 32 ? 10 : 11; }
+__host__ __device__ constexpr int sel_rows_hist_words(int KPL, int NW) {
+  return (1 << sel_rows_first_bits(KPL, NW)) + ((1 << sel_rows_first_bits(KPL, NW)) >> 3);
+}
+
 template <int KPL, int NW, bool STAGE>
 __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   constexpr int NG = KPL / 4;
@@ -642,10 +652,10 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
     for (int pass = 0; pass < 4; ++pass) {
       const uint32_t range = hi - lo;
       const int bl = range > 1u ? 32 - __clz((int)(range - 1u)) : 0;
-      const int s = max(0, bl - (pass == 0 ? 11 : 8));
+      const int s = max(0, bl - (pass == 0 ? sel_rows_first_bits(KPL, NW) : 8));
       const int nb = (((int)((range - 1u) >> s) >> 8) + 1) << 8;  // bins in use, rounded up to 256
       uint32_t *H = NW == 2 && (pass & 1) ? region + kSelHistWords + kSelTrash : hist;
-      uint32_t *spare = H + (H == hist ? kSelHistWords : kSelSmallWords) + (lane & (kSelTrash - 1));
+      uint32_t *spare = H + (H == hist ? sel_rows_hist_words(KPL, NW) : kSelSmallWords) + (lane & (kSelTrash - 1));
       const int nvec = (hpad(nb - 1) + 4) >> 2;
       for (int j = tid; j < nvec; j += nthr) reinterpret_cast<u32x4 *>(H)[j] = u32x4{0u, 0u, 0u, 0u};
       row_sync<NW>();
@@ -1073,9 +1083,9 @@ static void launch_select_rows(IdxSelectArgs a, int row0, int nrows, hipStream_t
   bool stage;
   unsigned grid, block;
   if (NW == 1) {  // lists staged over the histogram when they fit with the flags, else written straight out
-    stage = list_words + 16 * (KPL / 4) <= kSelHistWords;
+    stage = list_words + 16 * (KPL / 4) <= sel_rows_hist_words(KPL, 1);
     a.list_words = list_words;
-    a.wave_words = kSelHistWords + kSelTrash;
+    a.wave_words = sel_rows_hist_words(KPL, 1) + kSelTrash;
     grid = (unsigned)(((nrows + 3) / 4 + 7) & ~7);  // whole sets of eight (xcd_spread)
     block = 256;
   } else {        // [histogram | second histogram | list0 | list1]; two waves only when both lists fit
