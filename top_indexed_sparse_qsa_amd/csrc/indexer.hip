@@ -520,7 +520,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
 // loaded as float4s; slots past the row hold 0xffffffff (real keys have
 // bit 31 clear).  The cut is narrowed over key ranges as in the workgroup
 // select (select_core.h): the first range runs from the smallest non-zero
-// key to the largest in up to 2048 bins, later ones split the cut bin into
+// key to the largest in up to 2048 bins (1024 in the one-wave kernels of up
+// to 32 keys per lane), later ones split the cut bin into
 // up to 256; the row's histogram lives in LDS (plain atomic increments under
 // a wave-uniform branch, keys outside the range into spare words), and
 // every wave of the row finds the cut bin itself with DPP scans of per-lane
@@ -635,8 +636,8 @@ __global__ __launch_bounds__(256) void idx_select_rows_kernel(IdxSelectArgs a) {
   kmin += 1u;  // used only when some key is non-zero (then below 2^31)
   // The cut is narrowed over key ranges [lo, hi) as in the workgroup select
   // (select_core.h): zeros are left out of the first range unless fewer than
-  // `budget` keys are non-zero; the first pass takes up to 2048 bins, later
-  // ones 256.  Keys outside the range count into spare words (no lane is
+  // `budget` keys are non-zero; the first pass takes up to 2048 bins (1024,
+  // sel_rows_first_bits), later ones 256.  Keys outside the range count into spare words (no lane is
   // masked off); two-wave rows alternate two histograms, so a wave may clear
   // the next pass's while the other still reads this one's.
   uint32_t lo, hi;
