@@ -520,8 +520,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
 // loaded as float4s; slots past the row hold 0xffffffff (real keys have
 // bit 31 clear).  The cut is narrowed over key ranges as in the workgroup
 // select (select_core.h): the first range runs from the smallest non-zero
-// key to the largest in up to 2048 bins (1024 in the one-wave kernels of up
-// to 32 keys per lane), later ones split the cut bin into
+// key to the largest in up to 2048 bins (1024 in the one-wave kernels),
+// later ones split the cut bin into
 // up to 256; the row's histogram lives in LDS (plain atomic increments under
 // a wave-uniform branch, keys outside the range into spare words), and
 // every wave of the row finds the cut bin itself with DPP scans of per-lane
@@ -540,12 +540,14 @@ __device__ __forceinline__ void row_sync() {
   else __syncthreads();
 }
 
-// First-pass bits of the per-row select: 11 (2048 bins), or 10 for the
-// one-wave kernels of up to 32 keys per lane (rows of up to 2048 blocks),
-// whose 62-64 registers allow eight waves per SIMD but whose four 2048-bin
-// histograms per workgroup would allow only four.  Ten first-pass bits and
-// three passes of eight still reach single keys.
-__host__ __device__ constexpr int sel_rows_first_bits(int KPL, int NW) { return NW == 1 && KPL <= 32 ? 10 : 11; }
+// First-pass bits of the per-row select: 11 (2048 bins) for two-wave rows,
+// 10 for the one-wave kernels (rows of up to 4096 blocks).  One wave's
+// histogram clear and first cut search halve; at up to 32 keys per lane
+// (62-64 registers, eight waves per SIMD) four 2048-bin histograms per
+// workgroup would also have held the kernel at four waves per SIMD by LDS.
+// Two-wave rows (8192 keys) measured no faster with 1024 bins.  Ten
+// first-pass bits and three passes of eight still reach single keys.
+__host__ __device__ constexpr int sel_rows_first_bits(int KPL, int NW) { return NW == 1 && KPL <= 64 ? 10 : 11; }
 __host__ __device__ constexpr int sel_rows_hist_words(int KPL, int NW) {
   return (1 << sel_rows_first_bits(KPL, NW)) + ((1 << sel_rows_first_bits(KPL, NW)) >> 3);
 }
