@@ -34,11 +34,6 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 constexpr int kSelBins = 2048;
 __host__ __device__ constexpr int hpad(int d) { return d + ((d >> 5) << 2); }
 constexpr int kSelHistWords = kSelBins + (kSelBins >> 3);
-constexpr int kSelOddVecs = (hpad(255) + 4) >> 2;  // a padded 256-bin histogram in 16-byte words
-
-// Radix window of a pass: the first takes 11 bits below the bits shared by
-// every key, later ones 8.
-__device__ __forceinline__ int sel_window(int pass, int top) { return min(pass == 0 ? 11 : 8, top + 1); }
 
 // Lanes below this one whose bit is set in m.
 __device__ __forceinline__ int lanes_below(unsigned long long m) {
