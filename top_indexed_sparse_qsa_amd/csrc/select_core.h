@@ -35,11 +35,6 @@ constexpr int kSelBins = 2048;
 __host__ __device__ constexpr int hpad(int d) { return d + ((d >> 5) << 2); }
 constexpr int kSelHistWords = kSelBins + (kSelBins >> 3);
 
-// Lanes below this one whose bit is set in m.
-__device__ __forceinline__ int lanes_below(unsigned long long m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 // Inclusive scan of v over the 64 lanes of a wave under a commutative,
 // associative op with identity id (DPP as wave_incl_scan); lane 63 ends
 // with the op over the whole wave.
